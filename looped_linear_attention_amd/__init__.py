@@ -1,0 +1,281 @@
+"""Python binding of libgdnloop: the looped gated-delta-rule (GDN) mixer on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgdnloop.so`` (built by ``looped_linear_attention_amd.build``).
+PyTorch supplies device memory and the stream.  Functions carry the names of
+the C entry points declared in ``include/gdnloop.h`` and take torch tensors in
+place of pointers; each tensor's dtype, device, contiguity and element count
+are checked against the descriptor on the host before the call, so a
+mismatched buffer raises instead of reaching a kernel.
+
+The library fails loudly: importing works without a GPU, but any entry point
+raises ``GdnError`` if the shared library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
+    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
+    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GdnError", "gdn_desc", "make_desc", "lib_path",
+    "load", "EXPORTED", "workspace",
+    "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
+    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
+    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_attach",
+    "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
+]
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT = range(5)
+GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE = range(4)
+
+# Every symbol the header declares (checked by the CPU test suite).
+EXPORTED = [
+    "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
+    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
+    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_attach",
+    "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdnloop.so")
+_lib = None
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+class gdn_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("chunk", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("alpha_lo", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+    @property
+    def act_dtype(self) -> torch.dtype:
+        return torch.float32 if self.act == GDN_F32 else torch.bfloat16
+
+
+def make_desc(B: int, L: int, H: int, dk: int, dv: int, T: int = 4, act=GDN_BF16,
+              alpha_lo: float = 0.0, norm_eps: float = 1e-6, chunk: int = 64) -> gdn_desc:
+    if isinstance(act, str):
+        act = GDN_F32 if act == "f32" else GDN_BF16
+    return gdn_desc(B, L, H, dk, dv, H * dv, T, chunk, act, alpha_lo, norm_eps)
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdnloop.so (raises GdnError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise GdnError(f"{_LIB_PATH} is missing: run `python -m looped_linear_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, D, S, I = ctypes.c_void_p, ctypes.POINTER(gdn_desc), ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "gdn_weights_packed_bytes": [D, ctypes.POINTER(S)],
+        "gdn_weights_pack": [D, P, P, P, P, P, P, P],
+        "gdn_workspace_bytes": [D, I, ctypes.POINTER(S)],
+        "gdn_project": [D, P, P, P, P, P, P, P, P],
+        "gdn_scan_prefill": [D, P, P, P, P, P, P, P, P, P, S, P],
+        "gdn_scan_decode": [D, P, P, P, P, P, P, P, P],
+        "gdn_loop_prefill": [D, P, P, P, P, P, P, P, S, P],
+        "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
+        "gdn_timer_create": [I, I, ctypes.POINTER(P)],
+        "gdn_timer_attach": [P],
+        "gdn_timer_detach": [],
+        "gdn_timer_reset": [P],
+        "gdn_timer_read": [P, ctypes.POINTER(I), ctypes.POINTER(ctypes.c_double)],
+        "gdn_timer_destroy": [P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        raise GdnError(f"{lib.gdn_status_string(status).decode()} -- {lib.gdn_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype], numel: int,
+         optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise GdnError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise GdnError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise GdnError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise GdnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.numel() != numel:
+        raise GdnError(f"{name} has {t.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise GdnError("ws must be a contiguous device tensor")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def gdn_status_string(status: int) -> str:
+    return load().gdn_status_string(status).decode()
+
+
+def gdn_last_error() -> str:
+    return load().gdn_last_error().decode()
+
+
+def gdn_version() -> str:
+    return load().gdn_version().decode()
+
+
+def gdn_weights_packed_bytes(desc: gdn_desc) -> int:
+    n = ctypes.c_size_t()
+    _check(load().gdn_weights_packed_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def gdn_workspace_bytes(desc: gdn_desc, op: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().gdn_workspace_bytes(ctypes.byref(desc), op, ctypes.byref(n)))
+    return n.value
+
+
+def workspace(desc: gdn_desc, op: int, device="cuda") -> torch.Tensor:
+    """Allocate the device workspace `op` needs (torch owns the memory)."""
+    return torch.empty(max(gdn_workspace_bytes(desc, op), 256), dtype=torch.uint8, device=device)
+
+
+def gdn_weights_pack(desc, Wq, Wk, Wv, wa, wb, Wpack, stream=None):
+    a, d, H, dk, dv = desc.act_dtype, desc.d, desc.H, desc.dk, desc.dv
+    pb = gdn_weights_packed_bytes(desc)
+    _check(load().gdn_weights_pack(
+        ctypes.byref(desc), _ptr(Wq, "Wq", a, d * H * dk), _ptr(Wk, "Wk", a, d * H * dk),
+        _ptr(Wv, "Wv", a, d * H * dv), _ptr(wa, "wa", a, d * H), _ptr(wb, "wb", a, d * H),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)), _stream(stream)))
+
+
+def gdn_project(desc, x, Wpack, q, k, v, alpha, beta, stream=None):
+    a, M, H, D = desc.act_dtype, desc.B * desc.L, desc.H, desc.dk
+    pb = gdn_weights_packed_bytes(desc)
+    _check(load().gdn_project(
+        ctypes.byref(desc), _ptr(x, "x", a, M * desc.d),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)),
+        _ptr(q, "q", a, M * H * D), _ptr(k, "k", a, M * H * D), _ptr(v, "v", a, M * H * D),
+        _ptr(alpha, "alpha", torch.float32, M * H), _ptr(beta, "beta", torch.float32, M * H),
+        _stream(stream)))
+
+
+def gdn_scan_prefill(desc, q, k, v, alpha, beta, s_init, o, s_final, ws, stream=None):
+    a, BL, H, D = desc.act_dtype, desc.B * desc.L, desc.H, desc.dk
+    st = desc.B * H * D * D
+    wp, wn = _ws(ws)
+    _check(load().gdn_scan_prefill(
+        ctypes.byref(desc), _ptr(q, "q", a, BL * H * D), _ptr(k, "k", a, BL * H * D),
+        _ptr(v, "v", a, BL * H * D), _ptr(alpha, "alpha", torch.float32, BL * H),
+        _ptr(beta, "beta", torch.float32, BL * H),
+        _ptr(s_init, "s_init", torch.float32, st, optional=True),
+        _ptr(o, "o", torch.float32, BL * H * D),
+        _ptr(s_final, "s_final", torch.float32, st, optional=True), wp, wn, _stream(stream)))
+
+
+def gdn_scan_decode(desc, q, k, v, alpha, beta, states, o, stream=None):
+    a, N, H, D = desc.act_dtype, desc.B, desc.H, desc.dk
+    _check(load().gdn_scan_decode(
+        ctypes.byref(desc), _ptr(q, "q", a, N * H * D), _ptr(k, "k", a, N * H * D),
+        _ptr(v, "v", a, N * H * D), _ptr(alpha, "alpha", torch.float32, N * H),
+        _ptr(beta, "beta", torch.float32, N * H),
+        _ptr(states, "states", torch.float32, N * H * D * D),
+        _ptr(o, "o", torch.float32, N * H * D), _stream(stream)))
+
+
+def gdn_loop_prefill(desc, h0, Wpack, rho, h_out, states_out, h_loops, ws, stream=None):
+    a, BL, d, T = desc.act_dtype, desc.B * desc.L, desc.d, desc.T
+    pb = gdn_weights_packed_bytes(desc)
+    wp, wn = _ws(ws)
+    _check(load().gdn_loop_prefill(
+        ctypes.byref(desc), _ptr(h0, "h0", a, BL * d),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)),
+        _ptr(rho, "rho", torch.float32, T * d), _ptr(h_out, "h_out", torch.float32, BL * d),
+        _ptr(states_out, "states_out", torch.float32, T * desc.B * desc.H * desc.dk * desc.dv,
+             optional=True),
+        _ptr(h_loops, "h_loops", torch.float32, T * BL * d, optional=True), wp, wn,
+        _stream(stream)))
+
+
+def gdn_loop_decode(desc, h_t, Wpack, rho, states, h_out, ws, stream=None):
+    a, N, d, T = desc.act_dtype, desc.B, desc.d, desc.T
+    pb = gdn_weights_packed_bytes(desc)
+    wp, wn = _ws(ws)
+    _check(load().gdn_loop_decode(
+        ctypes.byref(desc), _ptr(h_t, "h_t", a, N * d),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)),
+        _ptr(rho, "rho", torch.float32, T * d),
+        _ptr(states, "states", torch.float32, T * N * desc.H * desc.dk * desc.dv),
+        _ptr(h_out, "h_out", torch.float32, N * d), wp, wn, _stream(stream)))
+
+
+# ---- timers ------------------------------------------------------------------
+def gdn_timer_create(stage: int, capacity: int) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load().gdn_timer_create(stage, capacity, ctypes.byref(h)))
+    return h
+
+
+def gdn_timer_attach(timer) -> None:
+    _check(load().gdn_timer_attach(timer))
+
+
+def gdn_timer_detach() -> None:
+    _check(load().gdn_timer_detach())
+
+
+def gdn_timer_reset(timer) -> None:
+    _check(load().gdn_timer_reset(timer))
+
+
+def gdn_timer_read(timer):
+    n, ms = ctypes.c_int(), ctypes.c_double()
+    _check(load().gdn_timer_read(timer, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+def gdn_timer_destroy(timer) -> None:
+    _check(load().gdn_timer_destroy(timer))

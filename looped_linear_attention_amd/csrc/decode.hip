@@ -1,0 +1,135 @@
+// decode.hip -- one recurrent token of the gated delta rule per sequence, gfx950.
+//
+// LT2: Linear-Time Looped Transformers, related-work paragraph on linear
+// attention: inference is a recurrent state update at constant cost per step.
+// Per (sequence n, head h), with the state S [dk x dv] read once and written once:
+//     a = S^T k,   b = S^T q                    (one pass over S)
+//     u = beta (v - alpha a)
+//     o = S'^T q = alpha b + (k.q) u            (S' the updated state)
+//     S' = alpha S + k u^T
+// which is S' = alpha (I - beta k k^T) S + beta k v^T, o = S'^T q.
+// The kernel is HBM-bound: one workgroup per (n, h) streams the state with
+// 16-byte accesses (each wave touches whole 512-byte rows).
+#include "gdn_device.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void k_decode(const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                const TIn *__restrict__ v,
+                                                const float *__restrict__ alpha,
+                                                const float *__restrict__ beta, float *states,
+                                                float *__restrict__ o, const void *__restrict__ h_prev,
+                                                int h_prev_bf16, const float *__restrict__ rho,
+                                                float *__restrict__ h_out, bf16 *__restrict__ x_next,
+                                                int H) {
+    constexpr int CG = D / 4;       // float4 column groups
+    constexpr int RG = 256 / CG;    // row groups
+    constexpr int RPT = D / RG;     // rows per thread
+    __shared__ float ks[D], qs[D], vs[D];
+    __shared__ __attribute__((aligned(16))) float4 pa[RG][CG], pb[RG][CG];
+    __shared__ float kq_s;
+
+    const int t = threadIdx.x;
+    const int nh = blockIdx.x;  // n * H + h
+    const int h = nh % H;
+    const int64_t vec = (int64_t)nh * D;
+    if (t < D) {
+        ks[t] = to_f32(k[vec + t]);
+        qs[t] = to_f32(q[vec + t]);
+        vs[t] = to_f32(v[vec + t]);
+    }
+    const float al = alpha[nh], be = beta[nh];
+    const int cg = t % CG, rg = t / CG;
+    float4 *S = reinterpret_cast<float4 *>(states + (int64_t)nh * D * D);
+    float4 sr[RPT];
+#pragma unroll
+    for (int ii = 0; ii < RPT; ++ii) sr[ii] = S[(rg + RG * ii) * CG + cg];
+    __syncthreads();
+    if (t < 64) {
+        float p = 0.f;
+        for (int i = t; i < D; i += 64) p += ks[i] * qs[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
+        if (t == 0) kq_s = p;
+    }
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bq = a;
+#pragma unroll
+    for (int ii = 0; ii < RPT; ++ii) {
+        const int i = rg + RG * ii;
+        const float ki = ks[i], qi = qs[i];
+        a.x += ki * sr[ii].x; a.y += ki * sr[ii].y; a.z += ki * sr[ii].z; a.w += ki * sr[ii].w;
+        bq.x += qi * sr[ii].x; bq.y += qi * sr[ii].y; bq.z += qi * sr[ii].z; bq.w += qi * sr[ii].w;
+    }
+    pa[rg][cg] = a;
+    pb[rg][cg] = bq;
+    __syncthreads();
+    float4 at = pa[0][cg], bt = pb[0][cg];
+#pragma unroll
+    for (int r = 1; r < RG; ++r) {
+        const float4 x = pa[r][cg], y = pb[r][cg];
+        at.x += x.x; at.y += x.y; at.z += x.z; at.w += x.w;
+        bt.x += y.x; bt.y += y.y; bt.z += y.z; bt.w += y.w;
+    }
+    const float kq = kq_s;
+    const int j0 = 4 * cg;
+    float u[4], ov[4];
+    const float av[4] = {at.x, at.y, at.z, at.w}, bv[4] = {bt.x, bt.y, bt.z, bt.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u[c] = be * (vs[j0 + c] - al * av[c]);
+        ov[c] = al * bv[c] + kq * u[c];
+    }
+    if (rg == 0) {
+        if (h_out) {
+            const int d = H * D;
+            const int64_t n = nh / H;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t hi = n * d + (int64_t)h * D + j0 + c;
+                const float hp = h_prev_bf16 ? (float)reinterpret_cast<const bf16 *>(h_prev)[hi]
+                                             : reinterpret_cast<const float *>(h_prev)[hi];
+                const float hn = ov[c] + rho[h * D + j0 + c] * hp;
+                h_out[hi] = hn;
+                if (x_next) x_next[hi] = (bf16)hn;
+            }
+        } else {
+            *reinterpret_cast<float4 *>(o + vec + j0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        }
+    }
+#pragma unroll
+    for (int ii = 0; ii < RPT; ++ii) {
+        const float ki = ks[rg + RG * ii];
+        float4 s = sr[ii];
+        s.x = al * s.x + ki * u[0];
+        s.y = al * s.y + ki * u[1];
+        s.z = al * s.z + ki * u[2];
+        s.w = al * s.w + ki * u[3];
+        S[(rg + RG * ii) * CG + cg] = s;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(bool f32, int N, int H, int D, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *states, float *o,
+                         const void *h_prev, bool h_prev_bf16, const float *rho, float *h_out,
+                         bf16 *x_next, hipStream_t s) {
+    dim3 grid((unsigned)((int64_t)N * H));
+#define DEC(DD, T)                                                                                 \
+    hipLaunchKernelGGL((k_decode<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,      \
+                       (const T *)v, alpha, beta, states, o, h_prev, h_prev_bf16 ? 1 : 0, rho,    \
+                       h_out, x_next, H)
+    if (f32) {
+        if (D == 128) DEC(128, float); else DEC(64, float);
+    } else {
+        if (D == 128) DEC(128, bf16); else DEC(64, bf16);
+    }
+#undef DEC
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,75 @@
+// gdn_device.h -- device helpers shared by the gfx950 kernels of the looped
+// gated-delta-rule mixer (bf16 conversion, MFMA fragment types, split-bf16).
+//
+// MFMA lane layouts used throughout (CDNA4 matrix cores, 64-lane wavefront):
+//   v_mfma_f32_16x16x32_bf16: A lane l holds row l%16, k = 8*(l/16) + i (i<8);
+//                             B lane l holds col l%16, k = 8*(l/16) + i;
+//                             C lane l holds col l%16, rows 4*(l/16) + i (i<4).
+//   v_mfma_f32_16x16x16_bf16: as above with k = 4*(l/16) + i (i<4); its B
+//                             k-slots coincide with the C rows of a lane, so an
+//                             accumulator tile can feed the next product as B.
+//   v_mfma_f32_32x32x16_bf16: A row l%32, k = 8*(l/32) + i; B col l%32;
+//                             C col l%32, rows 8*(i/4) + 4*(l/32) + i%4 (i<16).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
+template <int N>
+__device__ __forceinline__ void split_bf16(const float (&x)[N], __bf16 (&hi)[N], __bf16 (&lo)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        hi[i] = (bf16)x[i];
+        lo[i] = (bf16)(x[i] - (float)hi[i]);
+    }
+}
+
+__device__ __forceinline__ bf16x8 pack8(const __bf16 (&v)[8]) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = v[i];
+    return r;
+}
+__device__ __forceinline__ bf16x4 pack4(const __bf16 (&v)[4]) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i];
+    return r;
+}
+
+// Workgroup barrier that waits only for LDS traffic (outstanding global loads
+// issued for a later step stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+}  // namespace gdn

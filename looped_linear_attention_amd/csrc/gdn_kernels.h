@@ -1,0 +1,60 @@
+// gdn_kernels.h -- host-side launchers of the gfx950 kernels (internal).
+// Shapes are validated by the C ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+
+// Rows of the packed weight matrix: per head q|k|v (3*D rows), zero rows up to
+// a multiple of 128 (qkv_rows_padded), then one 128-row tile holding wa (H
+// rows) and wb (H rows) followed by zero rows.
+__host__ __device__ inline int64_t qkv_rows_padded(int H, int D) { return ((int64_t)H * 3 * D + 127) / 128 * 128; }
+__host__ __device__ inline int64_t packed_rows(int H, int D) { return qkv_rows_padded(H, D) + 128; }
+
+// Wpack[n][c] = W_src[c][col(n)]  (transpose into K-contiguous rows).
+hipError_t launch_pack_weights(bool f32, int d, int H, int D, const void *Wq, const void *Wk,
+                               const void *Wv, const void *wa, const void *wb, void *Wpack,
+                               hipStream_t s);
+
+// X[M, d] x Wpack^T with the fused per-head epilogue (L2 norm of q and k,
+// gates alpha/beta, dtype conversion of q/k/v).
+hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
+                          void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
+                          float eps, hipStream_t s);
+
+// Chunk preparation: per (b, h, chunk) decay products, the UT-transform
+// inverse and the derived matrices W [D x 64], M [64 x 64], gamma [64].
+struct ChunkWs {
+    float *W;   // [B*H*Nc][D][64]
+    float *M;   // [B*H*Nc][64][64]
+    float *g;   // [B*H*Nc][64]
+};
+hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
+                            const float *alpha, const float *beta, ChunkWs ws, hipStream_t s);
+
+// Inter-chunk state carry plus outputs.  Either `o` (scan form) or the loop
+// residual h_out = o + rho (.) h_prev with an optional bf16 copy x_next.
+struct CarryOut {
+    float *o;              // [B, L, H, D] or nullptr
+    const void *h_prev;    // [B, L, H*D] (bf16 if h_prev_bf16, else fp32) or nullptr
+    bool h_prev_bf16;
+    const float *rho;      // [H*D]
+    float *h_out;          // [B, L, H*D]
+    bf16 *x_next;          // [B, L, H*D] or nullptr
+};
+hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k,
+                             const void *v, ChunkWs ws, const float *s_init, float *s_final,
+                             CarryOut out, hipStream_t s);
+
+// One recurrent token per sequence; states updated in place.  With
+// h_out != nullptr the loop residual is applied as in CarryOut.
+hipError_t launch_decode(bool f32, int N, int H, int D, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *states, float *o,
+                         const void *h_prev, bool h_prev_bf16, const float *rho, float *h_out,
+                         bf16 *x_next, hipStream_t s);
+
+}  // namespace gdn

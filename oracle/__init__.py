@@ -108,14 +108,24 @@ def round_f32(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def round_bf16(x) -> np.ndarray:
+def round_bf16(x, jitter=None) -> np.ndarray:
     """fp64 -> fp32 -> bf16 with round-to-nearest-even, returned as fp64.
 
     bf16 keeps the upper 16 bits of the fp32 bit pattern.  Rounding to
     nearest even adds 0x7FFF plus the lowest kept bit before truncating
     (finite inputs; overflow correctly rounds to infinity).
+
+    ``jitter`` (a numpy Generator, default None) first moves every fp32 value
+    one fp32 ulp up or down at random.  It models an implementation whose
+    fp32 arithmetic summed in another order: its bf16 rounding decisions are
+    equally valid, and the spread of results under jitter measures how far
+    two valid bf16 implementations can drift apart.
     """
     f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if jitter is not None:
+        up = jitter.random(f.shape) < 0.5
+        f = np.where(up, np.nextafter(f, np.float32(np.inf)),
+                     np.nextafter(f, np.float32(-np.inf))).astype(np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
     u = (u + np.uint64(0x7FFF) + keep_lsb) & np.uint64(0xFFFF0000)
@@ -153,36 +163,49 @@ def scan(q, k, v, alpha, beta, s_init=None, want_state: bool = True):
 # per-loop projections, normalisation and gates (numpy fp64)
 # ---------------------------------------------------------------------------
 def project(x, Wq, Wk, Wv, wa, wb, H: int, dk: int, dv: int, alpha_lo: float,
-            act: str, eps: float = 1e-6):
+            act: str, eps: float = 1e-6, jitter=None, fp32_sum: bool = False):
     """Projections of one loop for token rows x [M, d] (already at operand precision).
 
     q = x Wq, k = x Wk, v = x Wv (head j owns columns [j*dk, (j+1)*dk)),
     a = x wa, b = x wb (one column per head).  q and k are L2-normalised per
     head; alpha = alpha_lo + (1 - alpha_lo) / (1 + e^a); beta = 1 / (1 + e^-b).
     For act == "bf16", q/k/v are then rounded fp64->fp32->bf16 and alpha, beta
-    to fp32 (the precision they are stored in).
+    to fp32 (the precision they are stored in).  ``jitter``: see round_bf16.
+    ``fp32_sum`` forms the q/k/v dot products with a float32 library matmul
+    and normalises q/k in float32 (another valid fp32 implementation of the
+    same values; the gates stay fp64).
     """
     x = _f64(x)
     M = x.shape[0]
     Wq, Wk, Wv, wa, wb = map(_f64, (Wq, Wk, Wv, wa, wb))
-    q = (x @ Wq).reshape(M, H, dk)
-    k = (x @ Wk).reshape(M, H, dk)
-    v = (x @ Wv).reshape(M, H, dv)
     a = x @ wa
     b = x @ wb
-    q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
-    k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    if fp32_sum:
+        f32 = np.float32
+        xf = x.astype(f32)
+        q = (xf @ Wq.astype(f32)).reshape(M, H, dk)
+        k = (xf @ Wk.astype(f32)).reshape(M, H, dk)
+        v = (xf @ Wv.astype(f32)).reshape(M, H, dv).astype(np.float64)
+        q = (q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True, dtype=f32) + f32(eps))).astype(np.float64)
+        k = (k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True, dtype=f32) + f32(eps))).astype(np.float64)
+    else:
+        q = (x @ Wq).reshape(M, H, dk)
+        k = (x @ Wk).reshape(M, H, dk)
+        v = (x @ Wv).reshape(M, H, dv)
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
     alpha = alpha_lo + (1.0 - alpha_lo) / (1.0 + np.exp(a))
     beta = 1.0 / (1.0 + np.exp(-b))
     if act == "bf16":
-        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+        q, k, v = round_bf16(q, jitter), round_bf16(k, jitter), round_bf16(v, jitter)
         alpha, beta = round_f32(alpha), round_f32(beta)
     return q, k, v, alpha, beta
 
 
 def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
                  alpha_lo: float, act: str, eps: float = 1e-6,
-                 keep_loops: bool = False, keep_states: bool = False):
+                 keep_loops: bool = False, keep_states: bool = False, jitter=None,
+                 fp32_sum: bool = False):
     """T weight-tied loops of the GDN mixer with the per-loop residual gate.
 
     h^(0) = h0 [B, L, d]; for tau = 1..T:
@@ -193,6 +216,8 @@ def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
         h^(tau) = o.reshape(B, L, H*dv) + rho[tau-1] (.) h^(tau-1)
     Returns dict(h=h^(T) [B,L,d], loops=[h^(1..T)] or None,
     states=[S_final per loop, each [B,H,dk,dv]] or None).  fp64.
+    ``jitter``: see round_bf16 (applies to every bf16 rounding point);
+    ``fp32_sum``: see project.
     """
     h = _f64(h0)
     rho = _f64(rho)
@@ -201,9 +226,9 @@ def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
     assert H * dv == d, "the mixer output must have the width of the residual stream"
     loops, states = [], []
     for tau in range(T):
-        x = round_bf16(h) if act == "bf16" else h
+        x = round_bf16(h, jitter) if act == "bf16" else h
         q, k, v, al, be = project(x.reshape(B * L, d), Wq, Wk, Wv, wa, wb, H, dk, dv,
-                                  alpha_lo, act, eps)
+                                  alpha_lo, act, eps, jitter, fp32_sum)
         o, s = scan(q.reshape(B, L, H, dk), k.reshape(B, L, H, dk), v.reshape(B, L, H, dv),
                     al.reshape(B, L, H), be.reshape(B, L, H), None, want_state=keep_states)
         h = o.reshape(B, L, d) + rho[tau][None, None, :] * h
@@ -216,7 +241,7 @@ def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
 
 
 def loop_decode_step(h_t, Wq, Wk, Wv, wa, wb, rho, states, H: int, dk: int, dv: int,
-                     alpha_lo: float, act: str, eps: float = 1e-6):
+                     alpha_lo: float, act: str, eps: float = 1e-6, jitter=None):
     """One generated token per sequence through T loops (recurrent form).
 
     h_t [N, d] is the token's input; states [T, N, H, dk, dv] holds each loop's
@@ -230,8 +255,8 @@ def loop_decode_step(h_t, Wq, Wk, Wv, wa, wb, rho, states, H: int, dk: int, dv: 
     N, d = h.shape
     T = rho.shape[0]
     for tau in range(T):
-        x = round_bf16(h) if act == "bf16" else h
-        q, k, v, al, be = project(x, Wq, Wk, Wv, wa, wb, H, dk, dv, alpha_lo, act, eps)
+        x = round_bf16(h, jitter) if act == "bf16" else h
+        q, k, v, al, be = project(x, Wq, Wk, Wv, wa, wb, H, dk, dv, alpha_lo, act, eps, jitter)
         o, s = scan(q.reshape(N, 1, H, dk), k.reshape(N, 1, H, dk), v.reshape(N, 1, H, dv),
                     al.reshape(N, 1, H), be.reshape(N, 1, H), st[tau])
         st[tau] = s

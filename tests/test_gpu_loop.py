@@ -1,0 +1,225 @@
+"""GPU parity of the projection stage and of the whole looped mixer (prefill and decode) against the oracle.
+
+Workloads are the seeded synthetic ones of ``synth``: the tiny fp32 case (1e-4 bar), and the 16-head,
+width-2048 bf16 cases (3e-3 bar) -- in full for the 4096-token prompt, and for the 8192x4 and 32768-token
+prompts in the same launch configuration as the benchmark with the oracle on prefixes (every loop is causal,
+so the first tokens of a full-size run must equal a run over just those tokens).
+
+What is unique is gated at the bar: each stage on identical inputs (the scans in test_gpu_scan.py; the
+projection here, whose bf16 outputs may differ from the oracle's only by the fp32 summation error bound
+plus one bf16 step), and the fp32 loop end to end.  The bf16 loop end to end is not unique: bf16 rounding
+decisions of values within fp32 summation error of a boundary go either way in any valid implementation
+and propagate through the loops.  Its bar is the fixed one or twice the oracle's own spread under one-ulp
+perturbations of its rounding inputs (tests/helpers.py, loop_envelope), whichever is larger.
+"""
+import numpy as np
+import pytest
+import torch
+
+import looped_linear_attention_amd as gl
+import oracle
+import synth
+from helpers import (TOL_BF16, TOL_F32, bf16_ulp, dev, envelope_bar, loop_envelope, norm_err, rel_err,
+                     say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack(w, x):
+    desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = torch.empty(gl.gdn_weights_packed_bytes(desc) // (4 if w.act == "f32" else 2),
+                     dtype=desc.act_dtype, device="cuda")
+    gl.gdn_weights_pack(desc, dev(x["Wq"]), dev(x["Wk"]), dev(x["Wv"]), dev(x["wa"]), dev(x["wb"]), Wp)
+    return Wp
+
+
+def _loop_gpu(w, x, B, L, keep=True):
+    desc = gl.make_desc(B, L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = _pack(w, x)
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL)
+    h_out = torch.empty(B, L, w.d, device="cuda")
+    states = torch.empty(w.T, B, w.H, w.dk, w.dv, device="cuda") if keep else None
+    loops = torch.empty(w.T, B, L, w.d, device="cuda") if keep else None
+    gl.gdn_loop_prefill(desc, dev(x["h0"][:B, :L]), Wp, dev(x["rho"]), h_out, states, loops, ws)
+    torch.cuda.synchronize()
+    return h_out.cpu(), (states.cpu() if keep else None), (loops.cpu() if keep else None)
+
+
+def _oracle_loop(w, x, B, L, keep=True):
+    return oracle.loop_prefill(x["h0"][:B, :L], x["Wq"], x["Wk"], x["Wv"], x["wa"], x["wb"], x["rho"],
+                               w.H, w.dk, w.dv, w.alpha_lo, w.act, keep_loops=keep, keep_states=keep)
+
+
+# ---------------------------------------------------------------------------
+# projection stage
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,M", [("tiny_f32", 256), ("prefill_b1_l4096", 300), ("prefill_b1_l4096", 1)])
+def test_project_parity(name, M):
+    w = synth.workload(name)
+    say(f"[project] {name} M={M}")
+    x = synth.prefill_inputs(w, L=min(M, w.L))
+    xin = x["h0"].reshape(-1, w.d)[:M].contiguous()
+    desc = gl.make_desc(M, 1, w.H, w.dk, w.dv, T=1, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = _pack(w, x)
+    a = desc.act_dtype
+    q = torch.empty(M, w.H, w.dk, dtype=a, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty(M, w.H, w.dv, dtype=a, device="cuda")
+    al = torch.empty(M, w.H, device="cuda")
+    be = torch.empty(M, w.H, device="cuda")
+    gl.gdn_project(desc, dev(xin), Wp, q, k, v, al, be)
+    torch.cuda.synchronize()
+    rq, rk, rv, ra, rb = oracle.project(xin, x["Wq"], x["Wk"], x["Wv"], x["wa"], x["wb"], w.H, w.dk, w.dv,
+                                        w.alpha_lo, w.act)
+    if w.act == "f32":
+        for g, r in ((q, rq), (k, rk), (v, rv), (al, ra), (be, rb)):
+            assert rel_err(g.cpu(), r) < 1e-5
+    else:
+        # bf16-stored values: the GPU's fp32 dot products differ from the exact ones by at most the standard
+        # recursive-summation bound gamma_K * sum|x||w| (K = d terms, u = 2^-24); after rounding to bf16 the
+        # two results may additionally sit one bf16 step apart.  q and k carry their norm's error as well.
+        K = w.d
+        gam = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+        xa = np.abs(xin.double().numpy())
+        for g, r, W, normed in ((q, rq, x["Wq"], True), (k, rk, x["Wk"], True), (v, rv, x["Wv"], False)):
+            Wd = W.double().numpy()
+            p = (xin.double().numpy() @ Wd).reshape(M, w.H, -1)
+            mag = (xa @ np.abs(Wd)).reshape(M, w.H, -1)
+            if normed:
+                nrm = np.sqrt(np.sum(p * p, -1, keepdims=True) + 1e-6)
+                bound = 2 * gam * (mag + np.abs(p)) / nrm
+            else:
+                bound = 2 * gam * mag
+            gg = g.cpu().double().numpy()
+            diff = np.abs(gg - r)
+            step = bf16_ulp(np.maximum(np.abs(r), np.abs(gg)))
+            assert np.all(diff <= bound + step * 1.0001), float((diff - bound - step).max())
+            assert np.mean(diff > 0) < 0.01
+        assert rel_err(al.cpu(), ra) < 1e-5 and rel_err(be.cpu(), rb) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# looped prefill
+# ---------------------------------------------------------------------------
+def _check_loop(w, x, B, L, tol, gpu=None, Lcmp=None):
+    """Compare GPU loop outputs (first Lcmp tokens) with the oracle; bf16 uses the spread envelope."""
+    g_h, g_s, g_l = gpu if gpu is not None else _loop_gpu(w, x, B, L)
+    Lc = L if Lcmp is None else Lcmp
+    if w.act == "f32":
+        r = _oracle_loop(w, x, B, Lc)
+        el = [rel_err(g_l[t][:, :Lc], r["loops"][t]) for t in range(w.T)]
+        eh = rel_err(g_h[:, :Lc], r["h"])
+        say(f"    h^(T) err {eh:.2e}; per-loop {[f'{e:.1e}' for e in el]}")
+        assert eh <= tol and max(el) <= tol
+        if g_s is not None and Lc == L:
+            assert max(rel_err(g_s[t], r["states"][t]) for t in range(w.T)) <= tol
+        return g_h, g_s, r
+    r, smax, snorm, sst = loop_envelope(w, x, B, Lc)
+    for t in range(w.T):
+        em, en = rel_err(g_l[t][:, :Lc], r["loops"][t]), norm_err(g_l[t][:, :Lc], r["loops"][t])
+        bm, bn = envelope_bar(smax[t], tol), envelope_bar(snorm[t], 1e-4)
+        say(f"    loop {t + 1}: max-rel {em:.2e} (bar {bm:.2e}, spread {smax[t]:.2e}); "
+            f"normwise {en:.2e} (bar {bn:.2e}, spread {snorm[t]:.2e})")
+        assert em <= bm and en <= bn
+        if g_s is not None and Lc == L:
+            es = rel_err(g_s[t], r["states"][t])
+            say(f"       state max-rel {es:.2e} (bar {envelope_bar(sst[t], tol):.2e})")
+            assert es <= envelope_bar(sst[t], tol)
+    assert rel_err(g_h[:, :Lc], r["h"]) <= envelope_bar(smax[-1], tol)
+    return g_h, g_s, r
+
+
+def test_loop_prefill_tiny_f32():
+    w = synth.workload("tiny_f32")
+    say("[loop_prefill] tiny_f32 full")
+    x = synth.prefill_inputs(w)
+    _check_loop(w, x, w.B, w.L, TOL_F32)
+
+
+@pytest.mark.parametrize("L", [1, 63, 65, 200])
+def test_loop_prefill_bf16_ragged(L):
+    w = synth.workload("prefill_b1_l4096")
+    say(f"[loop_prefill] 16 heads bf16 L={L}")
+    x = synth.prefill_inputs(w, L=L)
+    _check_loop(w, x, 1, L, TOL_BF16)
+
+
+def test_loop_prefill_b1_l4096_full():
+    w = synth.workload("prefill_b1_l4096")
+    say("[loop_prefill] prefill_b1_l4096 full size (three oracle runs, ~1 min)")
+    x = synth.prefill_inputs(w)
+    _check_loop(w, x, w.B, w.L, TOL_BF16)
+
+
+@pytest.mark.parametrize("name,prefix", [("prefill_b4_l8192", 512), ("prefill_b1_l32768", 1024)])
+def test_loop_prefill_full_size_prefix(name, prefix):
+    """Full-size launch (as benchmarked); the oracle checks every batch row's first `prefix` tokens."""
+    w = synth.workload(name)
+    say(f"[loop_prefill] {name} full launch, oracle on {prefix}-token prefix")
+    x = synth.prefill_inputs(w)
+    g_h, g_s, g_l = _loop_gpu(w, x, w.B, w.L, keep=True)
+    assert np.isfinite(g_h.numpy()).all() and np.isfinite(g_s.numpy()).all()
+    _check_loop(w, x, w.B, w.L, TOL_BF16, gpu=(g_h, None, g_l), Lcmp=prefix)
+
+
+def test_loop_prefill_deterministic_and_no_aliasing_effects():
+    w = synth.workload("prefill_b1_l4096")
+    say("[loop_prefill] determinism, with and without per-loop outputs")
+    x = synth.prefill_inputs(w, L=700)
+    h1, _, _ = _loop_gpu(w, x, 1, 700, keep=True)
+    h2, _, _ = _loop_gpu(w, x, 1, 700, keep=False)
+    h3, _, _ = _loop_gpu(w, x, 1, 700, keep=False)
+    assert torch.equal(h1, h2) and torch.equal(h2, h3)
+
+
+def test_loop_prefill_zero_values_closed_form():
+    """Wv = 0 makes every mixer output zero, so h^(T) = (prod rho) (.) h^(0) (up to fp32 products)."""
+    w = synth.workload("prefill_b1_l4096")
+    say("[loop_prefill] Wv = 0 closed form")
+    x = synth.prefill_inputs(w, L=130)
+    x["Wv"] = torch.zeros_like(x["Wv"])
+    g_h, _, _ = _loop_gpu(w, x, 1, 130, keep=False)
+    ref = torch.prod(x["rho"].double(), 0)[None, None] * x["h0"].double()
+    assert rel_err(g_h, ref) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# looped decode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,N,L0,steps", [("tiny_f32", 1, 100, 3), ("prefill_b1_l4096", 3, 70, 3)])
+def test_loop_decode_after_prefill(name, N, L0, steps):
+    """GPU prefill over L0 tokens, then GPU decode of the next tokens, equals the oracle over L0+steps."""
+    w = synth.workload(name)
+    say(f"[loop_decode] {name} N={N} prefill {L0} then {steps} steps")
+    xb = synth.prefill_inputs(w)
+    # N sequences: reuse the drawn stream's rows as separate sequences
+    h0 = xb["h0"].reshape(-1, w.d)[: N * (L0 + steps)].reshape(N, L0 + steps, w.d).contiguous()
+    x = dict(xb)
+    x["h0"] = h0
+    desc_p = gl.make_desc(N, L0, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = _pack(w, x)
+    ws = gl.workspace(desc_p, gl.GDN_OP_LOOP_PREFILL)
+    h_out = torch.empty(N, L0, w.d, device="cuda")
+    states = torch.empty(w.T, N, w.H, w.dk, w.dv, device="cuda")
+    gl.gdn_loop_prefill(desc_p, dev(h0[:, :L0]), Wp, dev(x["rho"]), h_out, states, None, ws)
+    desc_d = gl.make_desc(N, 1, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    wsd = gl.workspace(desc_d, gl.GDN_OP_LOOP_DECODE)
+    outs = []
+    for s in range(steps):
+        ho = torch.empty(N, w.d, device="cuda")
+        gl.gdn_loop_decode(desc_d, dev(h0[:, L0 + s]), Wp, dev(x["rho"]), states, ho, wsd)
+        outs.append(ho)
+    torch.cuda.synchronize()
+    if w.act == "f32":
+        r = _oracle_loop(w, x, N, L0 + steps, keep=False)
+        for s in range(steps):
+            e = rel_err(outs[s].cpu(), r["h"][:, L0 + s])
+            say(f"    step {s}: err {e:.2e}")
+            assert e <= TOL_F32
+        return
+    r, smax, snorm, _ = loop_envelope(w, x, N, L0 + steps)
+    for s in range(steps):
+        g, rr = outs[s].cpu(), r["h"][:, L0 + s]
+        em, en = rel_err(g, rr), norm_err(g, rr)
+        say(f"    step {s}: max-rel {em:.2e} normwise {en:.2e} (loop-{w.T} spread {smax[-1]:.2e}/{snorm[-1]:.2e})")
+        assert em <= envelope_bar(smax[-1], TOL_BF16) and en <= envelope_bar(snorm[-1], 1e-4)

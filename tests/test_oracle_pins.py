@@ -351,3 +351,40 @@ def test_generators_deterministic():
     x2 = synth.scan_inputs(3, 1, 10, 2, 8, 8)
     assert all(torch.equal(x1[k], x2[k]) for k in x1)
     assert torch.allclose(x1["q"].float().norm(dim=-1), torch.ones(1, 10, 2), atol=1e-2)
+
+
+def test_round_bf16_jitter_moves_one_fp32_ulp():
+    """With a jitter generator, each result is the bf16 rounding of the fp32 value one ulp above or below."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(50000) * 10.0 ** rng.integers(-6, 6, 50000)
+    f = x.astype(np.float32)
+    up = oracle.round_bf16(np.nextafter(f, np.float32(np.inf)).astype(np.float64))
+    dn = oracle.round_bf16(np.nextafter(f, np.float32(-np.inf)).astype(np.float64))
+    j = oracle.round_bf16(x, np.random.default_rng(4))
+    assert np.all((j == up) | (j == dn))
+    assert np.mean(j != oracle.round_bf16(x)) < 0.01
+    # exact midpoints of the bf16 grid: the one-ulp move decides the rounding either way
+    ties = ((np.arange(1, 20001, dtype=np.uint32) << 16) | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    jt = oracle.round_bf16(ties, np.random.default_rng(5))
+    assert 0.3 < np.mean(jt != oracle.round_bf16(ties)) < 0.7
+    # fp32 workloads have no bf16 rounding point: jitter leaves the loop unchanged
+    xx, s = _tiny_loop_inputs(7)
+    a = oracle.loop_prefill(**xx, **s, alpha_lo=0.0, act="f32")
+    b = oracle.loop_prefill(**xx, **s, alpha_lo=0.0, act="f32", jitter=np.random.default_rng(0))
+    assert np.array_equal(a["h"], b["h"])
+
+
+def test_project_fp32_sum_is_a_float32_summation():
+    """fp32_sum forms the dot products in float32: v equals a float32 matmul; all within fp32 error of fp64."""
+    rng = np.random.default_rng(13)
+    d, H, D = 256, 2, 32
+    W = [rng.standard_normal((d, H * D)) / 16 for _ in range(3)]
+    wa, wb = rng.standard_normal((d, H)), rng.standard_normal((d, H))
+    x = rng.standard_normal((20, d))
+    a = oracle.project(x, *W, wa, wb, H, D, D, 0.0, "f32")
+    b = oracle.project(x, *W, wa, wb, H, D, D, 0.0, "f32", fp32_sum=True)
+    ref_v = (x.astype(np.float32) @ W[2].astype(np.float32)).astype(np.float64).reshape(20, H, D)
+    assert np.array_equal(b[2], ref_v)
+    assert np.abs(b[2] - a[2]).max() < 1e-4 and np.abs(b[2] - a[2]).max() > 0
+    assert np.abs(b[0] - a[0]).max() < 1e-5 and np.abs(b[1] - a[1]).max() < 1e-5
+    assert np.array_equal(b[3], a[3]) and np.array_equal(b[4], a[4])  # gates stay fp64
