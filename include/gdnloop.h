@@ -186,10 +186,11 @@ enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
 
 /* While a timer is attached, every launch of its stage is bracketed by a
  * pair of HIP events recorded on the stream that launch runs on (at most
- * `capacity` launches are recorded).  Attaching is process-wide and meant
- * for profiling runs; it is not thread-safe.  gdn_timer_read waits for the
- * recorded events and returns the number of bracketed launches and their
- * summed duration in milliseconds. */
+ * `capacity` launches are recorded).  One timer per stage can be attached at
+ * a time (attaching replaces that stage's timer; detach removes all).
+ * Attaching is process-wide and meant for profiling runs; it is not
+ * thread-safe.  gdn_timer_read waits for the recorded events and returns the
+ * number of bracketed launches and their summed duration in milliseconds. */
 typedef struct gdn_timer gdn_timer;
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out);
 gdn_status gdn_timer_attach(gdn_timer *t);

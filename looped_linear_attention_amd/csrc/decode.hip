@@ -22,9 +22,9 @@ __global__ __launch_bounds__(256) void k_decode(const TIn *__restrict__ q, const
                                                 const TIn *__restrict__ v,
                                                 const float *__restrict__ alpha,
                                                 const float *__restrict__ beta, float *states,
-                                                float *__restrict__ o, const void *__restrict__ h_prev,
+                                                float *__restrict__ o, const void *h_prev,
                                                 int h_prev_bf16, const float *__restrict__ rho,
-                                                float *__restrict__ h_out, bf16 *__restrict__ x_next,
+                                                float *h_out, bf16 *x_next,
                                                 int H) {
     constexpr int CG = D / 4;       // float4 column groups
     constexpr int RG = 256 / CG;    // row groups

@@ -133,12 +133,13 @@ struct gdn_timer {
 
 namespace {
 
-gdn_timer *g_timer = nullptr;
+constexpr int N_STAGES = GDN_STAGE_DECODE + 1;
+gdn_timer *g_timers[N_STAGES] = {nullptr, nullptr, nullptr, nullptr};
 
 // Runs `launch` bracketed by timer events when a timer for `stage` is attached.
 template <typename F>
 hipError_t timed(int stage, hipStream_t s, F &&launch) {
-    gdn_timer *tm = g_timer;
+    gdn_timer *tm = g_timers[stage];
     if (!tm || tm->stage != stage || tm->used >= tm->capacity) return launch();
     hipError_t e = hipEventRecord(tm->start[tm->used], s);
     if (e != hipSuccess) return e;
@@ -381,12 +382,12 @@ gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
 
 gdn_status gdn_timer_attach(gdn_timer *t) {
     if (!t) return fail(GDN_ERR_NULL, "timer is NULL");
-    g_timer = t;
+    g_timers[t->stage] = t;
     return GDN_OK;
 }
 
 gdn_status gdn_timer_detach(void) {
-    g_timer = nullptr;
+    for (auto &t : g_timers) t = nullptr;
     return GDN_OK;
 }
 
@@ -414,7 +415,7 @@ gdn_status gdn_timer_read(gdn_timer *t, int *launches, double *total_ms) {
 
 gdn_status gdn_timer_destroy(gdn_timer *t) {
     if (!t) return GDN_OK;
-    if (g_timer == t) g_timer = nullptr;
+    if (g_timers[t->stage] == t) g_timers[t->stage] = nullptr;
     for (int i = 0; i < t->capacity; ++i) {
         (void)hipEventDestroy(t->start[i]);
         (void)hipEventDestroy(t->stop[i]);

@@ -344,8 +344,8 @@ __global__ __launch_bounds__(256) void k_scan_carry(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H,
     int Nc, const float *__restrict__ W, const float *__restrict__ M, const float *__restrict__ g,
     const float *__restrict__ s_init, float *__restrict__ s_final, float *__restrict__ o,
-    const void *__restrict__ h_prev, int h_prev_bf16, const float *__restrict__ rho,
-    float *__restrict__ h_out, bf16 *__restrict__ x_next) {
+    const void *h_prev, int h_prev_bf16, const float *__restrict__ rho,
+    float *h_out, bf16 *x_next) {
     constexpr bool F32 = In<TIn>::f32;
     constexpr int NT = D / 64, RW = D / 4;
     constexpr int KW = (D == 128) ? 8 : 4;

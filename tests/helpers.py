@@ -41,34 +41,38 @@ def norm_err(g, r) -> float:
     return float(np.linalg.norm(g - r) / (nr if nr > 0 else 1.0))
 
 
-def loop_envelope(w, x, B, L, runs: int = 2):
+def loop_envelope(w, x, B, L, runs: int = 3):
     """Oracle loop run plus the spread of valid bf16 implementations around it.
 
     For bf16 workloads the looped result is not unique: every bf16 rounding of an fp32 intermediate that
     lies within fp32 summation error of a rounding boundary may go either way, and the loops propagate those
     decisions.  The oracle is re-run as other valid implementations would compute it -- once with the q/k/v
-    dot products summed in fp32 by a library matmul, and with its rounding inputs moved by one fp32 ulp
-    (seeded) -- and the largest per-loop deviation from the reference run (max-relative and normwise) is the
-    spread.  Returns (reference dict, spread_max[T], spread_norm[T], spread_state_max[T]).
+    dot products summed and normalised in fp32 by a library matmul, and with its rounding inputs moved by
+    one fp32 ulp (seeded) -- and the largest per-loop deviation from the reference run is the spread.
+    Returns (reference dict, spread dict) with per-loop lists "h_max", "h_norm", "s_max", "s_norm".
     """
     import oracle
     args = (x["h0"][:B, :L], x["Wq"], x["Wk"], x["Wv"], x["wa"], x["wb"], x["rho"], w.H, w.dk, w.dv,
             w.alpha_lo, w.act)
     ref = oracle.loop_prefill(*args, keep_loops=True, keep_states=True)
-    smax = [0.0] * w.T
-    snorm = [0.0] * w.T
-    sst = [0.0] * w.T
+    sp = {k: [0.0] * w.T for k in ("h_max", "h_norm", "s_max", "s_norm")}
     variants = [dict(fp32_sum=True)] + [dict(jitter=np.random.default_rng(9000 + i)) for i in range(runs - 1)]
     for kw in variants:
         j = oracle.loop_prefill(*args, keep_loops=True, keep_states=True, **kw)
         for t in range(w.T):
-            smax[t] = max(smax[t], rel_err(j["loops"][t], ref["loops"][t]))
-            snorm[t] = max(snorm[t], norm_err(j["loops"][t], ref["loops"][t]))
-            sst[t] = max(sst[t], rel_err(j["states"][t], ref["states"][t]))
-    return ref, smax, snorm, sst
+            sp["h_max"][t] = max(sp["h_max"][t], rel_err(j["loops"][t], ref["loops"][t]))
+            sp["h_norm"][t] = max(sp["h_norm"][t], norm_err(j["loops"][t], ref["loops"][t]))
+            sp["s_max"][t] = max(sp["s_max"][t], rel_err(j["states"][t], ref["states"][t]))
+            sp["s_norm"][t] = max(sp["s_norm"][t], norm_err(j["states"][t], ref["states"][t]))
+    return ref, sp
 
 
-def envelope_bar(spread: float, floor: float, factor: float = 2.0) -> float:
+# Envelope factors: normwise deviations are stable across valid implementations (2x); the max-relative
+# statistic is decided by a handful of flipped elements and is heavy-tailed (4x).
+ENV_NORM, ENV_MAX = 2.0, 4.0
+
+
+def envelope_bar(spread: float, floor: float, factor: float) -> float:
     """Bar for a non-unique bf16 loop result: the fixed bar, or `factor` times the spread if larger."""
     return max(floor, factor * spread)
 

@@ -9,8 +9,9 @@ What is unique is gated at the bar: each stage on identical inputs (the scans in
 projection here, whose bf16 outputs may differ from the oracle's only by the fp32 summation error bound
 plus one bf16 step), and the fp32 loop end to end.  The bf16 loop end to end is not unique: bf16 rounding
 decisions of values within fp32 summation error of a boundary go either way in any valid implementation
-and propagate through the loops.  Its bar is the fixed one or twice the oracle's own spread under one-ulp
-perturbations of its rounding inputs (tests/helpers.py, loop_envelope), whichever is larger.
+and propagate through the loops.  Its bars are the fixed ones or a multiple of the oracle's own spread when
+it is recomputed as other valid fp32 implementations would (tests/helpers.py, loop_envelope), whichever is
+larger: 2x for normwise errors, 4x for the heavy-tailed max-relative statistic.
 """
 import numpy as np
 import pytest
@@ -19,8 +20,8 @@ import torch
 import looped_linear_attention_amd as gl
 import oracle
 import synth
-from helpers import (TOL_BF16, TOL_F32, bf16_ulp, dev, envelope_bar, loop_envelope, norm_err, rel_err,
-                     say)
+from helpers import (ENV_MAX, ENV_NORM, TOL_BF16, TOL_F32, bf16_ulp, dev, envelope_bar, loop_envelope,
+                     norm_err, rel_err, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,18 +115,19 @@ def _check_loop(w, x, B, L, tol, gpu=None, Lcmp=None):
         if g_s is not None and Lc == L:
             assert max(rel_err(g_s[t], r["states"][t]) for t in range(w.T)) <= tol
         return g_h, g_s, r
-    r, smax, snorm, sst = loop_envelope(w, x, B, Lc)
+    r, sp = loop_envelope(w, x, B, Lc)
     for t in range(w.T):
         em, en = rel_err(g_l[t][:, :Lc], r["loops"][t]), norm_err(g_l[t][:, :Lc], r["loops"][t])
-        bm, bn = envelope_bar(smax[t], tol), envelope_bar(snorm[t], 1e-4)
-        say(f"    loop {t + 1}: max-rel {em:.2e} (bar {bm:.2e}, spread {smax[t]:.2e}); "
-            f"normwise {en:.2e} (bar {bn:.2e}, spread {snorm[t]:.2e})")
+        bm, bn = envelope_bar(sp["h_max"][t], tol, ENV_MAX), envelope_bar(sp["h_norm"][t], 1e-4, ENV_NORM)
+        say(f"    loop {t + 1}: h max-rel {em:.2e} (spread {sp['h_max'][t]:.2e}, bar {bm:.2e}); "
+            f"normwise {en:.2e} (spread {sp['h_norm'][t]:.2e}, bar {bn:.2e})")
         assert em <= bm and en <= bn
         if g_s is not None and Lc == L:
-            es = rel_err(g_s[t], r["states"][t])
-            say(f"       state max-rel {es:.2e} (bar {envelope_bar(sst[t], tol):.2e})")
-            assert es <= envelope_bar(sst[t], tol)
-    assert rel_err(g_h[:, :Lc], r["h"]) <= envelope_bar(smax[-1], tol)
+            es, esn = rel_err(g_s[t], r["states"][t]), norm_err(g_s[t], r["states"][t])
+            bs, bsn = envelope_bar(sp["s_max"][t], tol, ENV_MAX), envelope_bar(sp["s_norm"][t], 1e-4, ENV_NORM)
+            say(f"       state max-rel {es:.2e} (spread {sp['s_max'][t]:.2e}, bar {bs:.2e}); "
+                f"normwise {esn:.2e} (spread {sp['s_norm'][t]:.2e}, bar {bsn:.2e})")
+            assert es <= bs and esn <= bsn
     return g_h, g_s, r
 
 
@@ -217,9 +219,11 @@ def test_loop_decode_after_prefill(name, N, L0, steps):
             say(f"    step {s}: err {e:.2e}")
             assert e <= TOL_F32
         return
-    r, smax, snorm, _ = loop_envelope(w, x, N, L0 + steps)
+    r, sp = loop_envelope(w, x, N, L0 + steps)
     for s in range(steps):
         g, rr = outs[s].cpu(), r["h"][:, L0 + s]
         em, en = rel_err(g, rr), norm_err(g, rr)
-        say(f"    step {s}: max-rel {em:.2e} normwise {en:.2e} (loop-{w.T} spread {smax[-1]:.2e}/{snorm[-1]:.2e})")
-        assert em <= envelope_bar(smax[-1], TOL_BF16) and en <= envelope_bar(snorm[-1], 1e-4)
+        say(f"    step {s}: max-rel {em:.2e} normwise {en:.2e} "
+            f"(loop-{w.T} spread {sp['h_max'][-1]:.2e}/{sp['h_norm'][-1]:.2e})")
+        assert em <= envelope_bar(sp["h_max"][-1], TOL_BF16, ENV_MAX)
+        assert en <= envelope_bar(sp["h_norm"][-1], 1e-4, ENV_NORM)

@@ -57,6 +57,20 @@ def test_scan_prefill_parity(B, L, H, D, act, ar, br, ws):
     assert eo <= tol and es <= tol
 
 
+@pytest.mark.parametrize("B,L,H,ar", [(1, 4096, 16, (0.9, 1.0)), (4, 8192, 16, (0.0, 1.0)),
+                                      (1, 32768, 16, (0.95, 1.0))])
+def test_scan_prefill_long_full_size(B, L, H, ar):
+    """Scan-level parity at the prompts' full lengths and head counts (identical bf16 inputs on both sides), so
+    any error the carry accumulates over hundreds of chunks is measured against the 3e-3 bar."""
+    say(f"[scan_prefill] long: B={B} L={L} H={H} alpha={ar}")
+    x = synth.scan_inputs(40 + B, B, L, H, 128, 128, act="bf16", alpha_range=ar)
+    o, sf = _scan_gpu(x, "bf16")
+    ro, rs = oracle.scan(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+    eo, es = rel_err(o, ro), rel_err(sf, rs)
+    say(f"    o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 def test_scan_prefill_identity_and_decay():
     """alpha = 1, beta = 0 keeps S_0 (o_t = S_0^T q_t); beta = 0 alone gives pure decay of S_0."""
     say("[scan_prefill] invariants alpha=1,beta=0 and beta=0")
