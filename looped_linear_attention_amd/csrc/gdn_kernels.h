@@ -29,9 +29,9 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
 // Chunk preparation: per (b, h, chunk) decay products, the UT-transform
 // inverse and the derived matrices W [D x 64], M [64 x 64], gamma [64].
 struct ChunkWs {
-    float *W;   // [B*H*Nc][D][64]
-    float *M;   // [B*H*Nc][64][64]
-    float *g;   // [B*H*Nc][64]
+    float *W;   // per chunk: bf16 hi plane [D][64] then bf16 lo plane [D][64] (D*64*4 bytes)
+    float *M;   // per chunk: bf16 hi plane [64][64] then bf16 lo plane [64][64]
+    float *g;   // per chunk: gamma [64] fp32
 };
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
                             const float *alpha, const float *beta, ChunkWs ws, hipStream_t s);
