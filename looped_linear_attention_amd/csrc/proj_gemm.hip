@@ -8,7 +8,7 @@
 // caption: gating plus the delta rule): alpha = alpha_lo + (1 - alpha_lo)
 // sigmoid(-a), beta = sigmoid(b), a = x.wa, b = x.wb.
 //
-// bf16 path: 128x128x64 block tiles, 4 waves of 64x64 (2x2 MFMA 32x32x16
+// bf16 path: 256x128x64 block tiles, 4 waves of 128x64 (4x2 MFMA 32x32x16
 // tiles), double-buffered LDS with a 16-byte XOR swizzle, fp32 accumulation.
 // The packed weight puts each head's q|k|v rows in whole 128-row tiles, so one
 // output tile always holds complete head sections for the normalisation.
@@ -112,107 +112,178 @@ __device__ __forceinline__ void proj_epilogue(const float *Cs, float *red, int m
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM: C[m][n] = sum_c X[m][c] * Wp[n][c]
 // ---------------------------------------------------------------------------
-constexpr int BM_BF = 128, BK_BF = 64;
-constexpr int TILE_ELEMS = BM_BF * BK_BF;  // bf16 elements per operand tile (both are 128 x 64)
+// Block tile 256 (tokens) x 128 (packed output columns) x 64 (channels); four
+// waves in a 2 x 2 arrangement each own 128 x 64 of the tile as 4 x 2 MFMA
+// 32x32x16 accumulator tiles (128 fp32 per lane).  Operand tiles move from
+// global memory straight into LDS (global_load_lds_dwordx4: lane i of a wave
+// instruction fills the 16 bytes at the wave's LDS base + 16 i), three k-blocks
+// deep, so two k-blocks are in flight while one is multiplied.  The LDS tiles
+// are XOR-swizzled by choosing, for each lane, the global 16-byte chunk that
+// belongs at its LDS position.  Gate tiles (the 2H gate columns) come first in
+// the grid and only run the MFMAs of the columns they use, so they finish
+// early instead of adding a round.
+constexpr int BM_BF = 256, BK_BF = 64, STAGES = 3;
+constexpr int A_ELEMS = BM_BF * BK_BF;  // bf16 elements of the A tile (32 KB)
+constexpr int B_ELEMS = BN * BK_BF;     // bf16 elements of the B tile (16 KB)
+constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
 
-// 16-byte chunk `ch` (0..7) of row `r` of a 128x64 bf16 tile, XOR-swizzled by row.
-__device__ __forceinline__ int swz(int r, int ch) { return r * BK_BF + ((ch ^ (r & 7)) << 3); }
+// 16-byte chunk `ch` (0..7) of row `r` of a 64-wide bf16 tile, XOR-swizzled by
+// row.  A 128-byte row covers half of the 64 LDS banks, so rows of equal parity
+// share a bank half; keying the swizzle on r / 2 makes 16 consecutive rows
+// reading the same chunk land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz(int r, int ch) { return r * BK_BF + ((ch ^ swz_key(r)) << 3); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issues the direct loads of k-block starting at channel k0 into one stage.
+// A: 2048 chunks, wave w instruction i covers LDS chunks [(4 i + w) 64, +64);
+// B: 1024 chunks likewise with i < 4.  LDS chunk p holds row p / 8, logical
+// chunk (p % 8) ^ swz_key(row) of the tile.
+__device__ __forceinline__ void gemm_issue(bf16 *stage, const bf16 *__restrict__ x,
+                                           const bf16 *__restrict__ Wp, int lane, int wave, int m0,
+                                           int n0, int M, int K, int b_rows, int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int base = (4 * i + wave) * 64, p = base + lane;
+        const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
+        const int m = min(m0 + r, M - 1);   // tail rows re-read the last row; never stored
+        __builtin_amdgcn_global_load_lds(x + (int64_t)m * K + k0 + ch * 8,
+                                         (lds_void *)(stage + base * 8), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int base = (4 * i + wave) * 64, p = base + lane;
+        const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
+        const int rr = min(r, b_rows - 1);   // gate tile: unused rows repeat a used one
+        __builtin_amdgcn_global_load_lds(Wp + (int64_t)(n0 + rr) * K + k0 + ch * 8,
+                                         (lds_void *)(stage + A_ELEMS + base * 8), 16, 0, 0);
+    }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The k-loop of one tile.  GATE: only the 32-column MFMA tiles holding used
+// gate columns are computed (a wave-uniform condition outside the hot path).
+template <bool GATE>
+__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, const bf16 *__restrict__ x,
+                                           const bf16 *__restrict__ Wp, int lane, int wave, int wm,
+                                           int wn, int m0, int n0, int M, int K, int b_rows,
+                                           int gate_cols) {
+    const int nkb = K / BK_BF;   // >= 1
+    gemm_issue(stages, x, Wp, lane, wave, m0, n0, M, K, b_rows, 0);
+    if (nkb > 1) gemm_issue(stages + STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, BK_BF);
+    const bool tn_on[2] = {!GATE || wn * 64 < gate_cols, !GATE || wn * 64 + 32 < gate_cols};
+    for (int kb = 0; kb < nkb; ++kb) {
+        // this wave's loads of k-block kb are done once at most the 12 of kb+1 remain
+        if (kb + 1 < nkb) wait_vmcnt<12>();
+        else wait_vmcnt<0>();
+        lds_barrier();   // every wave's loads of kb landed; every wave finished k-block kb-1
+        if (kb + 2 < nkb)
+            gemm_issue(stages + ((kb + 2) % STAGES) * STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K,
+                       b_rows, (kb + 2) * BK_BF);
+        if (GATE && !tn_on[0] && !tn_on[1]) continue;
+        const bf16 *Ab = stages + (kb % STAGES) * STAGE_ELEMS;
+        const bf16 *Bb = Ab + A_ELEMS;
+        // fragments double-buffered across the 4 k-steps: step s+1 is read from LDS
+        // while step s is multiplied
+        bf16x8 af[2][4], bfr[2][2];
+        auto frag = [&](int s, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
+            const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+                a[tm] = *reinterpret_cast<const bf16x8 *>(Ab + swz(wm * 128 + tm * 32 + (lane & 31), ch));
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+                b[tn] = *reinterpret_cast<const bf16x8 *>(Bb + swz(wn * 64 + tn * 32 + (lane & 31), ch));
+        };
+        frag(0, af[0], bfr[0]);
+#pragma unroll
+        for (int s = 0; s < BK_BF / 16; ++s) {
+            if (s + 1 < BK_BF / 16) frag(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+            const int cur = s & 1;
+            if constexpr (!GATE) {
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+                        acc[tm][tn] = mfma32x32x16(af[cur][tm], bfr[cur][tn], acc[tm][tn]);
+            } else {
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+                    if (tn_on[tn])
+#pragma unroll
+                        for (int tm = 0; tm < 4; ++tm)
+                            acc[tm][tn] = mfma32x32x16(af[cur][tm], bfr[cur][tn], acc[tm][tn]);
+            }
+        }
+    }
+}
+
+// One workgroup per CU (the three LDS stages take 144 KB), i.e. one wave per
+// SIMD: the compiler may use the whole register file for latency hiding.
 template <int D>
-__global__ __launch_bounds__(256) void k_proj_bf16(const bf16 *__restrict__ x,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_proj_bf16(const bf16 *__restrict__ x,
                                                    const bf16 *__restrict__ Wp, int M, int K, int H,
-                                                   bf16 *q, bf16 *k, bf16 *v, float *alpha,
-                                                   float *beta, float alpha_lo, float eps) {
-    constexpr int LDS_MAIN = 2 * 2 * TILE_ELEMS * 2;      // A,B double-buffered, bytes
-    constexpr int LDS_EPI = BM_BF * CS_LD * 4 + 2 * BM_BF * 4;
+                                                   int m_tiles, int n_main, bf16 *q, bf16 *k, bf16 *v,
+                                                   float *alpha, float *beta, float alpha_lo,
+                                                   float eps) {
+    constexpr int LDS_MAIN = STAGES * STAGE_ELEMS * 2;          // bytes
+    constexpr int LDS_EPI = 128 * CS_LD * 4 + 2 * 128 * 4;      // one 128-row half of the tile
     constexpr int LDS_BYTES = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-    bf16 *As = reinterpret_cast<bf16 *>(smem);
-    bf16 *Bs = As + 2 * TILE_ELEMS;
+    bf16 *stages = reinterpret_cast<bf16 *>(smem);
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM_BF;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
+    // tile order: m_tiles gate tiles, then the main tiles m-fastest
+    const int id = blockIdx.x;
+    const bool gate = id < m_tiles;
+    const int m_tile = gate ? id : (id - m_tiles) % m_tiles;
+    const int n_tile = gate ? n_main : (id - m_tiles) / m_tiles;
+    const int m0 = m_tile * BM_BF, n0 = n_tile * BN;
+    const int gate_cols = 2 * H;          // used columns of the gate tile
+    const int b_rows = gate ? ((gate_cols + 31) / 32) * 32 : BN;
 
-    // global -> register staging: each thread moves 4 chunks of A and 4 of B per k-block
-    uint4 ra[4], rb[4];
-    auto gload = [&](int kb) {
-        const int k0 = kb * BK_BF;
+    f32x16 acc[4][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = t + 256 * i, r = c >> 3, ch = c & 7;
-            const int m = m0 + r;
-            if (m < M) ra[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k0 + ch * 8);
-            else ra[i] = make_uint4(0, 0, 0, 0);
-            rb[i] = *reinterpret_cast<const uint4 *>(Wp + (int64_t)(n0 + r) * K + k0 + ch * 8);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = t + 256 * i, r = c >> 3, ch = c & 7;
-            *reinterpret_cast<uint4 *>(As + buf * TILE_ELEMS + swz(r, ch)) = ra[i];
-            *reinterpret_cast<uint4 *>(Bs + buf * TILE_ELEMS + swz(r, ch)) = rb[i];
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    if (gate) gemm_kloop<true>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
+    else gemm_kloop<false>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
+    __syncthreads();   // all waves done reading the operand stages
 
-    const int nkb = K / BK_BF;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkb) gload(kb + 1);
-        const bf16 *Ab = As + buf * TILE_ELEMS;
-        const bf16 *Bb = Bs + buf * TILE_ELEMS;
+    // epilogue in two 128-row halves through an fp32 tile in LDS (reuses the operand buffers)
+    float *Cs = reinterpret_cast<float *>(smem);
+    float *red = Cs + 128 * CS_LD;
 #pragma unroll
-        for (int s = 0; s < BK_BF / 16; ++s) {
-            const int ch = 2 * s + (lane >> 5);
-            bf16x8 af[2], bfr[2];
+    for (int half = 0; half < 2; ++half) {
+        if (wm == half) {
 #pragma unroll
-            for (int tm = 0; tm < 2; ++tm) {
-                const int r = wm * 64 + tm * 32 + (lane & 31);
-                af[tm] = *reinterpret_cast<const bf16x8 *>(Ab + swz(r, ch));
-            }
+            for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < 2; ++tn) {
-                const int r = wn * 64 + tn * 32 + (lane & 31);
-                bfr[tn] = *reinterpret_cast<const bf16x8 *>(Bb + swz(r, ch));
-            }
+                for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = mfma32x32x16(af[tm], bfr[tn], acc[tm][tn]);
-        }
-        if (kb + 1 < nkb) {
-            sstore(buf ^ 1);
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const int c = wn * 64 + tn * 32 + (lane & 31);
+                        Cs[r * CS_LD + c] = acc[tm][tn][e];
+                    }
         }
         __syncthreads();
+        proj_epilogue<D, 128, bf16>(Cs, red, m0 + half * 128, n0, M, H, q, k, v, alpha, beta, alpha_lo,
+                                    eps);
+        __syncthreads();
     }
-
-    // accumulators -> fp32 tile in LDS (reuses the operand buffers)
-    float *Cs = reinterpret_cast<float *>(smem);
-    float *red = Cs + BM_BF * CS_LD;
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int c = wn * 64 + tn * 32 + (lane & 31);
-                Cs[r * CS_LD + c] = acc[tm][tn][e];
-            }
-    __syncthreads();
-    proj_epilogue<D, BM_BF, bf16>(Cs, red, m0, n0, M, H, q, k, v, alpha, beta, alpha_lo, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -307,15 +378,17 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
                                (const float *)Wpack, M, d, H, (float *)q, (float *)k, (float *)v,
                                alpha, beta, alpha_lo, eps);
     } else {
-        dim3 grid(ntiles, (M + BM_BF - 1) / BM_BF);
+        const int m_tiles = (M + BM_BF - 1) / BM_BF;
+        const int n_main = (int)(qkv_rows_padded(H, D) / BN);   // the gate tile is n_main
+        dim3 grid(m_tiles * (n_main + 1));
         if (D == 128)
             hipLaunchKernelGGL(k_proj_bf16<128>, grid, dim3(256), 0, s, (const bf16 *)x,
-                               (const bf16 *)Wpack, M, d, H, (bf16 *)q, (bf16 *)k, (bf16 *)v,
-                               alpha, beta, alpha_lo, eps);
+                               (const bf16 *)Wpack, M, d, H, m_tiles, n_main, (bf16 *)q, (bf16 *)k,
+                               (bf16 *)v, alpha, beta, alpha_lo, eps);
         else
             hipLaunchKernelGGL(k_proj_bf16<64>, grid, dim3(256), 0, s, (const bf16 *)x,
-                               (const bf16 *)Wpack, M, d, H, (bf16 *)q, (bf16 *)k, (bf16 *)v,
-                               alpha, beta, alpha_lo, eps);
+                               (const bf16 *)Wpack, M, d, H, m_tiles, n_main, (bf16 *)q, (bf16 *)k,
+                               (bf16 *)v, alpha, beta, alpha_lo, eps);
     }
     return hipGetLastError();
 }
