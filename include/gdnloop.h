@@ -184,8 +184,9 @@ const char *gdn_version(void);
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
        GDN_STAGE_DECODE = 3 };
 
-/* While a timer is attached, every launch of its stage is bracketed by a
- * pair of HIP events recorded on the stream that launch runs on (at most
+/* While a timer is attached, every launch of its stage carries a pair of HIP
+ * events on its dispatch (hipExtLaunchKernel start/stop events), so each pair
+ * spans that kernel's execution on its stream and nothing else (at most
  * `capacity` launches are recorded).  One timer per stage can be attached at
  * a time (attaching replaces that stage's timer; detach removes all).
  * Attaching is process-wide and meant for profiling runs; it is not

@@ -120,7 +120,7 @@ hipError_t launch_decode(bool f32, int N, int H, int D, const void *q, const voi
                          bf16 *x_next, hipStream_t s) {
     dim3 grid((unsigned)((int64_t)N * H));
 #define DEC(DD, T)                                                                                 \
-    hipLaunchKernelGGL((k_decode<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,      \
+    launch_kernel((k_decode<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,      \
                        (const T *)v, alpha, beta, states, o, h_prev, h_prev_bf16 ? 1 : 0, rho,    \
                        h_out, x_next, H)
     if (f32) {

@@ -1,6 +1,7 @@
 // gdn_kernels.h -- host-side launchers of the gfx950 kernels (internal).
 // Shapes are validated by the C ABI layer before any of these is called.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,23 @@
 namespace gdn {
 
 typedef __bf16 bf16;
+
+// Events that the next kernel launch of this thread stamps with its own start
+// and end (they ride on the dispatch packet, so they time the kernel alone, not
+// the gap before it).  The stage timer arms them for one launch; null otherwise.
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+LaunchEvents &launch_events();
+
+// Every kernel of the library is launched through here; the caller reads the
+// launch status with hipGetLastError().
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t s, Args... args) {
+    LaunchEvents &ev = launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u, args...);
+    ev = LaunchEvents{nullptr, nullptr};
+}
 
 // Rows of the packed weight matrix: per head q|k|v (3*D rows), zero rows up to
 // a multiple of 128 (qkv_rows_padded), then one 128-row tile holding wa (H

@@ -134,23 +134,26 @@ struct gdn_timer {
 namespace {
 
 constexpr int N_STAGES = GDN_STAGE_DECODE + 1;
+thread_local LaunchEvents t_launch_events{nullptr, nullptr};
 gdn_timer *g_timers[N_STAGES] = {nullptr, nullptr, nullptr, nullptr};
 
-// Runs `launch` bracketed by timer events when a timer for `stage` is attached.
+// Runs `launch` (exactly one kernel launch) with the stage timer's next event
+// pair armed, when a timer for `stage` is attached.
 template <typename F>
 hipError_t timed(int stage, hipStream_t s, F &&launch) {
     gdn_timer *tm = g_timers[stage];
     if (!tm || tm->stage != stage || tm->used >= tm->capacity) return launch();
-    hipError_t e = hipEventRecord(tm->start[tm->used], s);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(tm->stop[tm->used], s);
+    (void)s;
+    launch_events() = LaunchEvents{tm->start[tm->used], tm->stop[tm->used]};
+    hipError_t e = launch();
+    launch_events() = LaunchEvents{nullptr, nullptr};
     if (e == hipSuccess) tm->used++;
     return e;
 }
 
 }  // namespace
+
+LaunchEvents &gdn::launch_events() { return t_launch_events; }
 
 extern "C" {
 

@@ -353,11 +353,11 @@ hipError_t launch_pack_weights(bool f32, int d, int H, int D, const void *Wq, co
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     if (f32)
-        hipLaunchKernelGGL(k_pack<float>, dim3((unsigned)blocks), dim3(threads), 0, s, d, H, D,
+        launch_kernel(k_pack<float>, dim3((unsigned)blocks), dim3(threads), 0, s, d, H, D,
                            (const float *)Wq, (const float *)Wk, (const float *)Wv,
                            (const float *)wa, (const float *)wb, (float *)Wpack, total);
     else
-        hipLaunchKernelGGL(k_pack<bf16>, dim3((unsigned)blocks), dim3(threads), 0, s, d, H, D,
+        launch_kernel(k_pack<bf16>, dim3((unsigned)blocks), dim3(threads), 0, s, d, H, D,
                            (const bf16 *)Wq, (const bf16 *)Wk, (const bf16 *)Wv, (const bf16 *)wa,
                            (const bf16 *)wb, (bf16 *)Wpack, total);
     return hipGetLastError();
@@ -370,11 +370,11 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
     if (f32) {
         dim3 grid(ntiles, (M + BM_F - 1) / BM_F);
         if (D == 128)
-            hipLaunchKernelGGL(k_proj_f32<128>, grid, dim3(256), 0, s, (const float *)x,
+            launch_kernel(k_proj_f32<128>, grid, dim3(256), 0, s, (const float *)x,
                                (const float *)Wpack, M, d, H, (float *)q, (float *)k, (float *)v,
                                alpha, beta, alpha_lo, eps);
         else
-            hipLaunchKernelGGL(k_proj_f32<64>, grid, dim3(256), 0, s, (const float *)x,
+            launch_kernel(k_proj_f32<64>, grid, dim3(256), 0, s, (const float *)x,
                                (const float *)Wpack, M, d, H, (float *)q, (float *)k, (float *)v,
                                alpha, beta, alpha_lo, eps);
     } else {
@@ -382,11 +382,11 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
         const int n_main = (int)(qkv_rows_padded(H, D) / BN);   // the gate tile is n_main
         dim3 grid(m_tiles * (n_main + 1));
         if (D == 128)
-            hipLaunchKernelGGL(k_proj_bf16<128>, grid, dim3(256), 0, s, (const bf16 *)x,
+            launch_kernel(k_proj_bf16<128>, grid, dim3(256), 0, s, (const bf16 *)x,
                                (const bf16 *)Wpack, M, d, H, m_tiles, n_main, (bf16 *)q, (bf16 *)k,
                                (bf16 *)v, alpha, beta, alpha_lo, eps);
         else
-            hipLaunchKernelGGL(k_proj_bf16<64>, grid, dim3(256), 0, s, (const bf16 *)x,
+            launch_kernel(k_proj_bf16<64>, grid, dim3(256), 0, s, (const bf16 *)x,
                                (const bf16 *)Wpack, M, d, H, m_tiles, n_main, (bf16 *)q, (bf16 *)k,
                                (bf16 *)v, alpha, beta, alpha_lo, eps);
     }

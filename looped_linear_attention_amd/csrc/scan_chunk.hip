@@ -623,7 +623,7 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
     const int Nc = (L + C - 1) / C;
     dim3 grid(Nc, H, B);
 #define PREP(DD, T)                                                                                \
-    hipLaunchKernelGGL((k_scan_prep<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,   \
+    launch_kernel((k_scan_prep<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,   \
                        alpha, beta, L, H, Nc, ws.W, ws.M, ws.g)
     if (f32) {
         if (D == 128) PREP(128, float); else PREP(64, float);
@@ -641,7 +641,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
     dim3 grid(H, D / 16, B);
     const int res = out.h_out == nullptr ? 0 : (out.h_prev_bf16 ? 2 : 1);
 #define CARRY(DD, T, R)                                                                            \
-    hipLaunchKernelGGL((k_scan_carry<DD, T, R>), grid, dim3(256), 0, s, (const T *)q,             \
+    launch_kernel((k_scan_carry<DD, T, R>), grid, dim3(256), 0, s, (const T *)q,             \
                        (const T *)k, (const T *)v, L, H, Nc, ws.W, ws.M, ws.g, s_init, s_final,   \
                        out.o, out.h_prev, out.rho, out.h_out, out.x_next)
 #define CARRY_R(DD, T)                                                                             \
