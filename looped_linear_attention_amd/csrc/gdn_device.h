@@ -72,4 +72,47 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS load of 16 bytes per active lane: lane i of the wave
+// writes the 16 bytes at wave_base + 16 i (wave_base must be wave-uniform).
+// Completion is tracked by the vector-memory counter only (wait_vmcnt).
+__device__ __forceinline__ void dma16(const void *g, void *wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)wave_base, 16, 0, 0);
+}
+
+// The same direct load, issued so that the compiler's wait-count tracking does
+// not see it.  For the builtin form the compiler makes every later LDS access
+// it cannot prove disjoint wait for all outstanding direct loads, which would
+// stall each chunk on the prefetch of the next one.  Callers order the loaded
+// data themselves: wait_vmcnt until the loads are done, then a workgroup
+// barrier, before any lane reads the destination.  The instruction writes no
+// register (the data goes to LDS), and the leading s_nop covers the one wait
+// state an LDS direct load needs after M0 is written by a scalar instruction.
+__device__ __forceinline__ void dma16_async(const void *g, void *wave_base) {
+    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(lds_void *)wave_base);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0;
+// the gfx9-family format word).  Stores whose byte range does not lie inside
+// [0, bytes) are dropped by the hardware, so a tail can be masked without a
+// branch around the store instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at max).
+// The builtin is visible to the compiler's own wait tracking; the empty asm
+// statements on both sides keep memory operations from being scheduled across
+// it (the builtin alone does not order them), so the count refers to exactly
+// the operations issued before it in program order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace gdn

@@ -134,8 +134,6 @@ constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
 __device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz(int r, int ch) { return r * BK_BF + ((ch ^ swz_key(r)) << 3); }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Issues the direct loads of k-block starting at channel k0 into one stage.
 // A: 2048 chunks, wave w instruction i covers LDS chunks [(4 i + w) 64, +64);
 // B: 1024 chunks likewise with i < 4.  LDS chunk p holds row p / 8, logical
@@ -159,13 +157,6 @@ __device__ __forceinline__ void gemm_issue(bf16 *stage, const bf16 *__restrict__
         __builtin_amdgcn_global_load_lds(Wp + (int64_t)(n0 + rr) * K + k0 + ch * 8,
                                          (lds_void *)(stage + A_ELEMS + base * 8), 16, 0, 0);
     }
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // The k-loop of one tile.  GATE: only the 32-column MFMA tiles holding used

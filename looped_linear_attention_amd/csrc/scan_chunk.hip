@@ -25,13 +25,14 @@
 //   workspace.
 // k_scan_carry: one workgroup per (b, h, 16 columns of S); the columns of S
 //   never mix, so column slices are independent scans.  Each of the 4 waves
-//   keeps D/4 rows of the fp32 state slice in registers (MFMA accumulator
-//   layout) and, per chunk, forms its share of K.S and Q.S, exchanges the
-//   partial sums through LDS (one barrier per chunk, double-buffered), then
-//   computes E, S' = gamma_C S + W E (its own rows) and O for 16 tokens.  The
-//   products use split-bf16 operands (x = hi + lo, ~16 significant bits) with
-//   fp32 accumulation; operands that are exact bf16 inputs are not split.
-//   Next-chunk operands are prefetched into registers during the current chunk.
+//   keeps D/4 rows of the fp32 state slice in registers, forms its share of
+//   K.S and Q.S, reduce-scatters them by token tile through LDS, all-gathers
+//   the E tiles, then updates its rows (S' = gamma_C S + W E) and writes O for
+//   its 16 tokens.  The products use split-bf16 operands (x = hi + lo, ~16
+//   significant bits) with fp32 accumulation; operands that are exact bf16
+//   inputs are not split.  Chunk operands are loaded a chunk ahead of use.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_kernels.h"
 
@@ -48,21 +49,24 @@ template <> struct In<bf16> { static constexpr bool f32 = false; };
 
 // Position of element (row, token c) of a per-chunk [R x 64] matrix (W: R = D
 // rows of S; M: R = 64 output tokens) in the carry's fragment order.  Rows are
-// split over the 4 waves (R/4 each, in 16-row tiles tt); the 64 tokens form
-// two 32-token k-steps s.  Lane l = lr + 16 lg of the wave holds row
-// 16 tt + lr and, in slot j of its 8-element fragment, token
-// 32 s + 4 lg + j (j < 4) or 32 s + 16 + 4 lg + (j - 4) (j >= 4).  Layout:
+// split over the 4 waves (RW = R/4 each, NT = RW/16 tiles of 16); row
+// RW w + 4 NT g + 4 tt + j (j < 4) is output row 4 g + j of the wave's tile tt
+// (for M, and for W with D = 64, this is simply row 16 tt + 4 g + j).  The 64
+// tokens form two 32-token k-steps s; lane l = lr + 16 lg of the wave holds
+// output row lr and, in slot jj of its 8-element fragment, token
+// 32 s + 4 lg + jj (jj < 4) or 32 s + 16 + 4 lg + (jj - 4) (jj >= 4).  Layout:
 // [wave][tt][s][part: hi, lo][lane][8] bf16, so each wave reads its fragments
 // with fully coalesced 16-byte loads.  The lo part sits 8 * 64 elements after
 // the hi part.
 template <int R>
 __device__ __forceinline__ int64_t frag_index(int row, int c) {
     constexpr int RW = R / 4, NT = RW / 16;
-    const int w = row / RW, rem = row % RW, tt = rem / 16, lr = rem % 16;
+    const int w = row / RW, rem = row % RW;
+    const int g = rem / (4 * NT), tt = (rem % (4 * NT)) / 4, lr = 4 * g + rem % 4;
     const int s = c / 32, o = c % 32;
-    const int lg = (o % 16) / 4, j = (o % 4) + (o >= 16 ? 4 : 0);
+    const int lg = (o % 16) / 4, jj = (o % 4) + (o >= 16 ? 4 : 0);
     const int lane = lr + 16 * lg;
-    return ((((int64_t)(w * NT + tt) * 2 + s) * 2) * 64 + lane) * 8 + j;
+    return ((((int64_t)(w * NT + tt) * 2 + s) * 2) * 64 + lane) * 8 + jj;
 }
 
 // ---------------------------------------------------------------------------
@@ -272,143 +276,139 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
 // ---------------------------------------------------------------------------
 // carry
 // ---------------------------------------------------------------------------
-// Per-wave operand fragments of one chunk (registers).  K and Q rows are the
-// A operand of K.S / Q.S over this wave's D/4 state rows; W and M rows (bf16
-// hi/lo parts from the workspace) are the A operand of W.E / M.E over the
-// chunk's 64 tokens.  For D == 128 the 32 state rows (and the 32 tokens of each
-// E k-step) are taken in the order {4g..4g+3, 16+4g..16+4g+3} for lane group g,
-// which is exactly the order in which an MFMA accumulator tile holds them, so S
-// and E feed the next product straight from registers.
-template <int D, typename TIn> struct Frags {
-    static constexpr int NT = D / 64, KW = (D == 128) ? 8 : 4;
-    TIn k[4][KW], q[4][KW];
-    __bf16 wh[NT][2][8], wl[NT][2][8], mh[2][8], ml[2][8];
+// One workgroup per (b, h, 16-column slice of S); wave w keeps RW = D/4 rows
+// of the fp32 state slice in registers.  Lane l = lr + 16 g holds column lr
+// and, in tile tt of its rows, the rows
+//     srow(w, g, tt, j) = RW w + 4 NT g + 4 tt + j,   j = 0..3,
+// so the KW rows a lane contributes to the K.S product are contiguous
+// (RW w + KW g .. + KW) and its K fragment is one contiguous run of a token
+// row.  Row order inside an MFMA output tile is free, so the W fragments that
+// update S (written by the prep kernel) put S row srow(w, g, tt, j) at output
+// row 4 g + j of tile tt.
+//
+// Per chunk the K and Q tiles, the V and h_prev slices and gamma are copied
+// global -> LDS with direct loads (coalesced 16-byte rows, XOR-swizzled so the
+// fragment reads are bank-conflict free), double-buffered where LDS allows, a
+// chunk ahead of use; the per-wave W and M fragments come straight into
+// registers, also a chunk ahead.  Exchange per chunk: each wave's partial K.S
+// and Q.S of the three token tiles it does not own go through LDS (reduce-
+// scatter; wave w owns tokens 16w..16w+15), then the E tile of each wave goes
+// through LDS to all waves (all-gather), since W.E and M.E contract over all
+// 64 tokens.
+template <int D, typename TIn> struct CarryCfg {
+    static constexpr int RW = D / 4;                     // state rows per wave
+    static constexpr int NT = RW / 16;                   // 16-row tiles per wave
+    static constexpr int KW = (D == 128) ? 8 : 4;        // k-width of the K.S MFMA
+    static constexpr int ES = (int)sizeof(TIn);
+    static constexpr int ROWB = D * ES;                  // bytes of a token row of K or Q
+    static constexpr int NCH = ROWB / 16;                // 16-byte chunks per row
+    static constexpr int SH = (ES == 4 && D == 128) ? 1 : 0;
+    static constexpr int TILE = C * ROWB;                // bytes of a K or Q chunk tile
+    static constexpr int KQ_STAGES = (4 * TILE <= 65536) ? 2 : 1;
+    static constexpr int KQ_INS = 2 * TILE / 1024;       // direct-load instructions for K and Q
+    static constexpr int VROWB = 16 * ES;                // bytes of a token row of the V slice
+    static constexpr int V_INS = C * VROWB / 1024;
 };
 
-template <typename T> __device__ __forceinline__ void load4(const T *p, T *dst);
-template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, bf16 *dst) {
-    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = v[i];
-}
-template <> __device__ __forceinline__ void load4<float>(const float *p, float *dst) {
-    const float4 v = *reinterpret_cast<const float4 *>(p);
-    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+// physical 16-byte chunk of logical chunk c in row r of a K/Q tile
+template <int D, typename TIn>
+__device__ __forceinline__ int kq_phys(int r, int c) {
+    using G = CarryCfg<D, TIn>;
+    return c ^ ((r << G::SH) & (G::NCH - 1));
 }
 
-template <int D, typename TIn>
-__device__ __forceinline__ void load_frags(Frags<D, TIn> &F, int chunk, int L, int H, int h,
-                                           int64_t tokb, const TIn *q, const TIn *k,
-                                           const float *W, const float *M, int64_t cidb) {
-    constexpr int NT = D / 64, RW = D / 4, KW = (D == 128) ? 8 : 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int c0 = chunk * C, sr0 = wave * RW;
-    // Tokens past the end of the sequence read the last token instead (no
-    // branch around the loads, so they stay in flight): the prep kernel gives
-    // padded tokens beta = 0, which zeroes their columns of W and M, and their
-    // outputs are never stored, so any finite value is harmless.
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        const int tok = min(c0 + 16 * tm + lr, L - 1);
-        const int64_t base = ((tokb + tok) * H + h) * D + sr0 + 4 * lg;
-#pragma unroll
-        for (int part = 0; part < KW / 4; ++part) {
-            load4<TIn>(k + base + 16 * part, &F.k[tm][4 * part]);
-            load4<TIn>(q + base + 16 * part, &F.q[tm][4 * part]);
-        }
-    }
-    const int64_t cid = cidb + chunk;
-    // W and M come in fragment order (see frag_index): one 16-byte load per part
+// Per-wave W and M fragments of one chunk (bf16 hi/lo, fragment order).
+template <int D> struct WMFrags {
+    static constexpr int NT = D / 64;
+    bf16x8 wh[NT][2], wl[NT][2], mh[2], ml[2];
+};
+
+template <int D>
+__device__ __forceinline__ void load_wm(WMFrags<D> &F, const float *W, const float *M, int64_t cid,
+                                        int wave, int lane) {
+    constexpr int NT = D / 64;
     const bf16x8 *Wf = reinterpret_cast<const bf16x8 *>(W + cid * D * C) + (int64_t)wave * NT * 4 * 64 + lane;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const bf16x8 hi = Wf[((tt * 2 + s) * 2 + 0) * 64];
-            const bf16x8 lo = Wf[((tt * 2 + s) * 2 + 1) * 64];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                F.wh[tt][s][i] = hi[i];
-                F.wl[tt][s][i] = lo[i];
-            }
+            F.wh[tt][s] = Wf[((tt * 2 + s) * 2 + 0) * 64];
+            F.wl[tt][s] = Wf[((tt * 2 + s) * 2 + 1) * 64];
         }
     const bf16x8 *Mf = reinterpret_cast<const bf16x8 *>(M + cid * C * C) + (int64_t)wave * 4 * 64 + lane;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        const bf16x8 hi = Mf[(s * 2 + 0) * 64];
-        const bf16x8 lo = Mf[(s * 2 + 1) * 64];
+        F.mh[s] = Mf[(s * 2 + 0) * 64];
+        F.ml[s] = Mf[(s * 2 + 1) * 64];
+    }
+}
+
+// Issues this wave's share of the direct loads of chunk `cc`: K and Q tiles
+// (into kq, when KQ is set), V slice and gamma (vs, gs) and, RES != 0, the
+// h_prev slice (hs).  Tokens past the end of the sequence re-read the last
+// token: the prep kernel gives them beta = 0, which zeroes their columns of W
+// and M, and their outputs are never stored, so any finite value is harmless.
+template <int D, typename TIn, int RES, bool KQ, bool REST>
+__device__ __forceinline__ void carry_issue(unsigned char *__restrict__ kq, unsigned char *__restrict__ vs,
+                                            float *__restrict__ gs, unsigned char *__restrict__ hs, int cc,
+                                            int L, int H, int h, int64_t tokb, int col0,
+                                            const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                            const TIn *__restrict__ v, const float *__restrict__ g,
+                                            int64_t cidb, const void *__restrict__ h_prev, int wave,
+                                            int lane) {
+    using G = CarryCfg<D, TIn>;
+    constexpr int EPC = 16 / G::ES;   // elements per 16-byte chunk
+    const int c0 = cc * C;
+    if constexpr (KQ) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            F.mh[s][i] = hi[i];
-            F.ml[s][i] = lo[i];
+        for (int n = 0; n < G::KQ_INS / 4; ++n) {
+            const int I = 4 * n + wave;
+            const int tensor = I / (G::KQ_INS / 2);
+            const int base = (I % (G::KQ_INS / 2)) * 64, p = base + lane;
+            const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
+            const int tok = min(c0 + r, L - 1);
+            const TIn *src = (tensor ? q : k) + ((tokb + tok) * H + h) * D + c * EPC;
+            dma16_async(src, kq + tensor * G::TILE + base * 16);
         }
     }
-}
-
-// Per-chunk data shared by the four waves: V slice [64 tokens x 16 columns],
-// gamma [64] and (loop form) the residual input h_prev [64 x 16].  Thread t
-// loads token t/4, columns 4(t%4)..+3, and gamma[4(t%16)..+3] in raw form;
-// conversion happens when the values are written to LDS, a chunk later, so the
-// loads stay in flight.  Padded tokens read the last token (see load_frags).
-template <typename TIn> struct VG {
-    uint4 v;         // 4 values of V, raw (bf16: .x, .y hold 4 packed values)
-    float4 g;
-    uint4 hp;        // 4 values of h_prev, raw (bf16: .x, .y)
-};
-
-template <typename T> __device__ __forceinline__ uint4 load4_raw(const T *p);
-template <> __device__ __forceinline__ uint4 load4_raw<bf16>(const bf16 *p) {
-    const uint2 r = *reinterpret_cast<const uint2 *>(p);
-    return make_uint4(r.x, r.y, 0u, 0u);
-}
-template <> __device__ __forceinline__ uint4 load4_raw<float>(const float *p) {
-    return *reinterpret_cast<const uint4 *>(p);
-}
-template <typename T> __device__ __forceinline__ void unpack4(const uint4 &r, float *dst);
-template <> __device__ __forceinline__ void unpack4<bf16>(const uint4 &r, float *dst) {
-    dst[0] = __uint_as_float(r.x << 16);
-    dst[1] = __uint_as_float(r.x & 0xFFFF0000u);
-    dst[2] = __uint_as_float(r.y << 16);
-    dst[3] = __uint_as_float(r.y & 0xFFFF0000u);
-}
-template <> __device__ __forceinline__ void unpack4<float>(const uint4 &r, float *dst) {
-    dst[0] = __uint_as_float(r.x);
-    dst[1] = __uint_as_float(r.y);
-    dst[2] = __uint_as_float(r.z);
-    dst[3] = __uint_as_float(r.w);
-}
-
-template <typename TIn, int RES>
-__device__ __forceinline__ void load_vg(VG<TIn> &X, int chunk, int L, int H, int h, int D, int64_t tokb,
-                                        int col0, const TIn *v, const float *g, int64_t cidb,
-                                        const void *h_prev) {
-    const int t = threadIdx.x;
-    const int tok = min(chunk * C + (t >> 2), L - 1);
-    X.v = load4_raw<TIn>(v + ((tokb + tok) * H + h) * D + col0 + 4 * (t & 3));
-    X.g = *reinterpret_cast<const float4 *>(g + (cidb + chunk) * C + 4 * (t & 15));
-    if constexpr (RES != 0) {
-        const int64_t hi = (tokb + tok) * (int64_t)H * D + (int64_t)h * D + col0 + 4 * (t & 3);
-        if constexpr (RES == 2) X.hp = load4_raw<bf16>(reinterpret_cast<const bf16 *>(h_prev) + hi);
-        else X.hp = load4_raw<float>(reinterpret_cast<const float *>(h_prev) + hi);
+    if constexpr (REST) {
+        constexpr int LPR = G::VROWB / 16;   // lanes per V row
+        if (wave < G::V_INS) {
+            const int p = wave * 64 + lane, r = p / LPR, qq = p % LPR;
+            const int tok = min(c0 + r, L - 1);
+            dma16_async(v + ((tokb + tok) * H + h) * D + col0 + qq * EPC, vs + wave * 1024);
+        }
+        if constexpr (RES != 0) {
+            constexpr int HES = RES == 2 ? 2 : 4;
+            constexpr int HLPR = 16 * HES / 16, H_INS = C * 16 * HES / 1024;
+            if (wave < H_INS) {
+                const int p = wave * 64 + lane, r = p / HLPR, qq = p % HLPR;
+                const int tok = min(c0 + r, L - 1);
+                const int64_t off = (tokb + tok) * (int64_t)H * D + (int64_t)h * D + col0 + qq * (16 / HES);
+                dma16_async(static_cast<const unsigned char *>(h_prev) + off * HES, hs + wave * 1024);
+            }
+        }
+        if (wave == 3 && lane < C / 4) dma16_async(g + (cidb + cc) * C + 4 * lane, gs);
     }
 }
 
-template <typename TIn, int RES>
-__device__ __forceinline__ void store_vg(const VG<TIn> &X, float (*vl)[17], float *gl, float (*hl)[17]) {
-    const int t = threadIdx.x, r = t >> 2, c = 4 * (t & 3);
-    float f[4];
-    unpack4<TIn>(X.v, f);
+// K.S / Q.S A fragment (token row r, this lane's KW state rows) from a K/Q tile
+template <int D, typename TIn>
+__device__ __forceinline__ void kq_frag(const unsigned char *tile, int r, int wave, int lg,
+                                        TIn (&dst)[CarryCfg<D, TIn>::KW]) {
+    using G = CarryCfg<D, TIn>;
+    constexpr int BYTES = G::KW * G::ES;
+    const int b0 = (G::RW * wave + G::KW * lg) * G::ES;
+    const unsigned char *row = tile + r * G::ROWB;
+    if constexpr (BYTES >= 16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vl[r][c + i] = f[i];
-    if (t < 16) {
-        gl[4 * t] = X.g.x; gl[4 * t + 1] = X.g.y; gl[4 * t + 2] = X.g.z; gl[4 * t + 3] = X.g.w;
-    }
-    if constexpr (RES != 0) {
-        if constexpr (RES == 2) unpack4<bf16>(X.hp, f);
-        else unpack4<float>(X.hp, f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hl[r][c + i] = f[i];
+        for (int part = 0; part < BYTES / 16; ++part) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(row + kq_phys<D, TIn>(r, b0 / 16 + part) * 16);
+            __builtin_memcpy(&dst[part * (16 / G::ES)], &u, 16);
+        }
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2 *>(row + kq_phys<D, TIn>(r, b0 / 16) * 16 + b0 % 16);
+        __builtin_memcpy(&dst[0], &u, 8);
     }
 }
 
@@ -440,26 +440,39 @@ __device__ __forceinline__ f32x4 mma_a(const float (&a)[KW], const __bf16 (&bh)[
     c = mma_bf<KW>(ah, bl, c);
     return mma_bf<KW>(al, bh, c);
 }
-// ... or an A operand already given as hi/lo parts (3 passes)
-__device__ __forceinline__ f32x4 mma_hl(const __bf16 (&ah)[8], const __bf16 (&al)[8],
-                                        const __bf16 (&bh)[8], const __bf16 (&bl)[8], f32x4 c) {
-    c = mma_bf<8>(ah, bh, c);
-    c = mma_bf<8>(ah, bl, c);
-    return mma_bf<8>(al, bh, c);
+// c += a.b with both operands as hi/lo parts (3 passes)
+__device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, const bf16x8 &bh,
+                                        const bf16x8 &bl, f32x4 c) {
+    c = mfma16x16x32(ah, bh, c);
+    c = mfma16x16x32(ah, bl, c);
+    return mfma16x16x32(al, bh, c);
 }
 
-// One chunk of the carry for one wave: partial K.S / Q.S, exchange, E, S' and O.
-template <int D, typename TIn, int RES>
-__device__ __forceinline__ void carry_chunk(
-    const Frags<D, TIn> &F, float (&Sv)[D / 64][4], int chunk, int L, int H, int h, int64_t tokb,
-    int col, float rho_c, f32x4 (*red)[2][4][64], const float (*vl)[17], const float *gl,
-    const float (*hl)[17], float *o, float *h_out, bf16 *x_next) {
-    constexpr int NT = D / 64, KW = (D == 128) ? 8 : 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int d = H * D;
+// number of global stores one lane issues per full chunk (the wait for the
+// next chunk's direct loads lets exactly these stay in flight)
+template <int RES, bool XN> struct CarryStores {
+    static constexpr int N = RES == 0 ? 4 : (XN ? 8 : 4);
+};
 
-    // B operand of K.S / Q.S: this wave's state rows, split into bf16 hi/lo
+struct CarryLdsX {
+    f32x4 red[4][4][2][64];   // [source wave][token tile][K.S | Q.S][lane]
+    uint4 ex[4][64];          // [token tile][lane]: E hi (bf16x4) in .x .y, lo in .z .w
+};
+
+template <int D, typename TIn, int RES, bool XN, typename AfterB1>
+__device__ __forceinline__ void carry_chunk(
+    const WMFrags<D> &F, float (&Sv)[D / 64][4], int cc, int L, int H, int h, int64_t tokb, int col,
+    float rho_c, const unsigned char *__restrict__ kq, const unsigned char *__restrict__ vs,
+    const float *__restrict__ gs, const unsigned char *__restrict__ hs, CarryLdsX *__restrict__ Xp,
+    float *o, float *h_out, bf16 *x_next, AfterB1 &&after_b1) {
+    CarryLdsX &X = *Xp;
+    using G = CarryCfg<D, TIn>;
+    constexpr int NT = G::NT, KW = G::KW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+
+    // B operand of K.S / Q.S: this lane's KW contiguous state rows, hi/lo
     __bf16 sh[KW], sl[KW];
     {
         float sf[KW];
@@ -467,152 +480,201 @@ __device__ __forceinline__ void carry_chunk(
         for (int i = 0; i < KW; ++i) sf[i] = Sv[i / 4][i % 4];
         split_bf16(sf, sh, sl);
     }
+    f32x4 ks[4], qs[4];
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
-        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-        ks = mma_a<KW>(F.k[tm], sh, sl, ks);
-        qs = mma_a<KW>(F.q[tm], sh, sl, qs);
-        red[wave][0][tm][lane] = ks;
-        red[wave][1][tm][lane] = qs;
+        TIn ak[KW], aq[KW];
+        kq_frag<D, TIn>(kq, 16 * tm + lr, wave, lg, ak);
+        kq_frag<D, TIn>(kq + G::TILE, 16 * tm + lr, wave, lg, aq);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        ks[tm] = mma_a<KW>(ak, sh, sl, z);
+        qs[tm] = mma_a<KW>(aq, sh, sl, z);
     }
-    lds_barrier();
-
-    // E = V - diag(gamma) K S for all 64 tokens of this lane's column
-    float E[4][4];
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        f32x4 s4 = red[0][0][tm][lane];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-            const f32x4 p = red[w][0][tm][lane];
-            s4[0] += p[0]; s4[1] += p[1]; s4[2] += p[2]; s4[3] += p[3];
+    for (int tm = 0; tm < 4; ++tm)
+        if (tm != wave) {
+            X.red[wave][tm][0][lane] = ks[tm];
+            X.red[wave][tm][1][lane] = qs[tm];
         }
+    lds_barrier();   // (B1) partials visible; every wave done reading this chunk's K and Q
+    after_b1();      // single-buffered K/Q: the next chunk's tiles may now be loaded
+    // own token tile: sum of the four partials (wave-uniform selects keep tiles in registers)
+    f32x4 kt = ks[0], qt = qs[0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tm + 4 * lg + j;
-            E[tm][j] = vl[r][lr] - gl[r] * s4[j];
+    for (int tm = 1; tm < 4; ++tm)
+        if (tm == wave) { kt = ks[tm]; qt = qs[tm]; }
+#pragma unroll
+    for (int src = 0; src < 4; ++src)
+        if (src != wave) {
+            const f32x4 a = X.red[src][wave][0][lane], b = X.red[src][wave][1][lane];
+            kt += a;
+            qt += b;
         }
-    }
-    f32x4 qsum = red[0][1][wave][lane];
+    // E = V - diag(gamma) K S for tokens 16 wave + 4 lg + j
+    float e[4];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-        const f32x4 p = red[w][1][wave][lane];
-        qsum[0] += p[0]; qsum[1] += p[1]; qsum[2] += p[2]; qsum[3] += p[3];
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * wave + 4 * lg + j;
+        float vv;
+        if constexpr (G::ES == 2) vv = (float)reinterpret_cast<const bf16 *>(vs)[r * 16 + lr];
+        else vv = reinterpret_cast<const float *>(vs)[r * 16 + lr];
+        e[j] = vv - gs[r] * kt[j];
     }
-
-    // E as the B operand: k-step s covers accumulator tiles 2s and 2s+1
-    __bf16 eh[2][8], el[2][8];
+    {
+        __bf16 eh[4], el[4];
+        split_bf16(e, eh, el);
+        uint4 u;
+        __builtin_memcpy(&u.x, eh, 8);
+        __builtin_memcpy(&u.z, el, 8);
+        X.ex[wave][lane] = u;
+    }
+    lds_barrier();   // (B2) every E tile visible
+    // E as the B operand: k-step s covers the token tiles 2s and 2s+1
+    bf16x8 ebh[2], ebl[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        float ef[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ef[j] = E[2 * s][j];
-            ef[4 + j] = E[2 * s + 1][j];
-        }
-        split_bf16(ef, eh[s], el[s]);
+        const uint4 a = X.ex[2 * s][lane], b = X.ex[2 * s + 1][lane];
+        uint4 hi = make_uint4(a.x, a.y, b.x, b.y), lo = make_uint4(a.z, a.w, b.z, b.w);
+        __builtin_memcpy(&ebh[s], &hi, 16);
+        __builtin_memcpy(&ebl[s], &lo, 16);
     }
-    const float gC = gl[C - 1];
+    const float gC = gs[C - 1];
     // S' = gamma_C S + W E (this wave's rows)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
         f32x4 we = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 2; ++s) we = mma_hl(F.wh[tt][s], F.wl[tt][s], eh[s], el[s], we);
+        for (int s = 0; s < 2; ++s) we = mma_hl(F.wh[tt][s], F.wl[tt][s], ebh[s], ebl[s], we);
 #pragma unroll
         for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + we[j];
     }
-    // O = diag(gamma) Q S + M E for tokens 16*wave + 4lg + j
+    // O = diag(gamma) Q S + M E for tokens 16 wave + 4 lg + j
     f32x4 me = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) me = mma_hl(F.mh[s], F.ml[s], eh[s], el[s], me);
+    for (int s = 0; s < 2; ++s) me = mma_hl(F.mh[s], F.ml[s], ebh[s], ebl[s], me);
+    // Outputs through buffer stores whose range ends at the last token of the
+    // sequence: rows past it are dropped by the hardware, so every lane issues
+    // exactly CarryStores::N stores per chunk, with no branch around them (the
+    // wait for the next chunk's loads relies on that count).
+    const int d = H * D;
+    const int nvalid = min(C, L - cc * C);
+    const int64_t row0 = tokb + (int64_t)cc * C;
+    if constexpr (RES == 0) {
+        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(o + row0 * d, nvalid * d * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * wave + 4 * lg + j;
-        const int tok = chunk * C + r;
-        if (tok < L) {
-            const float ov = gl[r] * qsum[j] + me[j];
-            const int64_t row = tokb + tok;
-            if constexpr (RES == 0) {
-                o[(row * H + h) * D + col] = ov;
-            } else {
-                const int64_t hi = row * d + (int64_t)h * D + col;
-                const float hn = ov + rho_c * hl[r][lr];
-                h_out[hi] = hn;
-                if (x_next) x_next[hi] = (bf16)hn;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * wave + 4 * lg + j;
+            const float ov = gs[r] * qt[j] + me[j];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, ov), ro, (r * d + h * D + col) * 4, 0, 0);
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(h_out + row0 * d, nvalid * d * 4);
+        __amdgpu_buffer_rsrc_t rx;
+        if constexpr (XN) rx = buffer_rsrc(x_next + row0 * d, nvalid * d * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * wave + 4 * lg + j;
+            const float ov = gs[r] * qt[j] + me[j];
+            float hp;
+            if constexpr (RES == 2) hp = (float)reinterpret_cast<const bf16 *>(hs)[r * 16 + lr];
+            else hp = reinterpret_cast<const float *>(hs)[r * 16 + lr];
+            const float hn = ov + rho_c * hp;
+            const int e = r * d + h * D + col;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, hn), rh, e * 4, 0, 0);
+            if constexpr (XN)
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)hn), rx, e * 2, 0, 0);
         }
     }
 }
 
-template <int D, typename TIn, int RES>
+template <int D, typename TIn, int RES, bool XN>
 __global__ __launch_bounds__(256) void k_scan_carry(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H,
-    int Nc, const float *__restrict__ W, const float *__restrict__ M, const float *__restrict__ g,
+    int Nc, const float *W, const float *M, const float *__restrict__ g,
     const float *__restrict__ s_init, float *__restrict__ s_final, float *__restrict__ o,
     const void *h_prev, const float *__restrict__ rho, float *h_out, bf16 *x_next) {
-    constexpr int NT = D / 64, RW = D / 4;
-    __shared__ __attribute__((aligned(16))) f32x4 red[2][4][2][4][64];  // [buf][wave][KS|QS][tile][lane]
-    __shared__ float vls[2][C][17];
-    __shared__ float hls[RES ? 2 : 1][C][17];
-    __shared__ float gls[2][C];
+    // (W and M are not __restrict__: their loads must stay ordered with the
+    // wait_vmcnt fences, which a restrict pointer's loads may be moved across.)
+    using G = CarryCfg<D, TIn>;
+    constexpr int NT = G::NT, RW = G::RW;
+    constexpr int HB = RES == 0 ? 16 : C * 16 * (RES == 2 ? 2 : 4);
+    constexpr int NST = CarryStores<RES, XN>::N;
+    // every stage is an object of its own, so the compiler can tell the buffers
+    // a chunk reads from the ones the next chunk's direct loads write
+    __shared__ __attribute__((aligned(16))) unsigned char kq0_s[2 * G::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char kq1_s[G::KQ_STAGES == 2 ? 2 * G::TILE : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[C * G::VROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char h0_s[HB], h1_s[HB];
+    __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[C];
+    __shared__ CarryLdsX X;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lg = lane >> 4;
     // heads run along x so that the D/16 column slices of one head, which read the
     // same K, Q, W and M, get workgroup ids that are congruent mod 8 and share an XCD
     const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
-    const int col0 = slice * 16, col = col0 + lr;
-    const int sr0 = wave * RW;
+    const int col0 = slice * 16, col = col0 + (lane & 15);
     const int64_t tokb = (int64_t)b * L;
     const int64_t cidb = ((int64_t)b * H + h) * Nc;
     const float rho_c = RES ? rho[h * D + col] : 0.f;
-    float (*hl0)[17] = hls[0];
-    float (*hl1)[17] = hls[RES ? 1 : 0];
 
-    // state slice: Sv[tt][j] = S[sr0 + 16tt + 4lg + j][col]
+    // state slice: Sv[tt][j] = S[RW wave + 4 NT lg + 4 tt + j][col]
     float Sv[NT][4];
     const int64_t sbase = ((int64_t)b * H + h) * D * D;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            Sv[tt][j] = s_init ? s_init[sbase + (int64_t)(sr0 + 16 * tt + 4 * lg + j) * D + col] : 0.f;
+            Sv[tt][j] = s_init ? s_init[sbase + (int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] : 0.f;
+    // Nothing loaded before the loop may be pending inside it: otherwise the
+    // compiler's wait for these registers lands in the loop body (every chunk).
+    wait_vmcnt<0>();
 
-    Frags<D, TIn> fa, fb;
-    VG<TIn> vg;
-    load_frags<D, TIn>(fa, 0, L, H, h, tokb, q, k, W, M, cidb);
-    load_vg<TIn, RES>(vg, 0, L, H, h, D, tokb, col0, v, g, cidb, h_prev);
-    store_vg<TIn, RES>(vg, vls[0], gls[0], hl0);
-    __syncthreads();
+    WMFrags<D> fa, fb;
+    carry_issue<D, TIn, RES, true, true>(kq0_s, v0_s, g0_s, h0_s, 0, L, H, h, tokb, col0, q, k, v, g, cidb,
+                                         h_prev, wave, lane);
+    load_wm<D>(fa, W, M, cidb, wave, lane);
+    wait_vmcnt<0>();   // chunk 0's loads (the waits in the loop assume only stores are older)
 
-    // two chunks per iteration so the register sets swap roles without copies
-    for (int chunk = 0; chunk < Nc; chunk += 2) {
-        const bool has1 = chunk + 1 < Nc;
-        if (has1) {
-            load_frags<D, TIn>(fb, chunk + 1, L, H, h, tokb, q, k, W, M, cidb);
-            load_vg<TIn, RES>(vg, chunk + 1, L, H, h, D, tokb, col0, v, g, cidb, h_prev);
+    // One chunk step on LDS stage ST (= cc mod 2): wait for chunk cc's loads,
+    // issue chunk cc+1's into the other stage, compute cc.  Two steps per loop
+    // iteration so stages are compile-time constants and the W/M register sets
+    // swap roles without copies.
+    auto step = [&](auto stc, int cc, const WMFrags<D> &cur, WMFrags<D> &nxt) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stc)::value;
+        unsigned char *kq_cur = (G::KQ_STAGES == 1 || ST == 0) ? kq0_s : kq1_s;
+        unsigned char *kq_nxt = (G::KQ_STAGES == 1 || ST == 1) ? kq0_s : kq1_s;
+        unsigned char *v_cur = ST == 0 ? v0_s : v1_s, *v_nxt = ST == 0 ? v1_s : v0_s;
+        unsigned char *h_cur = ST == 0 ? h0_s : h1_s, *h_nxt = ST == 0 ? h1_s : h0_s;
+        float *g_cur = ST == 0 ? g0_s : g1_s, *g_nxt = ST == 0 ? g1_s : g0_s;
+        wait_vmcnt<NST>();   // only the previous chunk's stores may remain in flight
+        lds_barrier();            // (B0) chunk cc's direct loads of every wave have landed
+        const bool more = cc + 1 < Nc;
+        if (more) {
+            carry_issue<D, TIn, RES, G::KQ_STAGES == 2, true>(kq_nxt, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb,
+                                                            col0, q, k, v, g, cidb, h_prev, wave, lane);
+            load_wm<D>(nxt, W, M, cidb + cc + 1, wave, lane);
         }
-        carry_chunk<D, TIn, RES>(fa, Sv, chunk, L, H, h, tokb, col, rho_c, red[0], vls[0], gls[0], hl0,
-                                  o, h_out, x_next);
-        if (!has1) break;
-        // buffer 1 was last read before this chunk's barrier, which every wave has passed
-        store_vg<TIn, RES>(vg, vls[1], gls[1], hl1);
-        const bool has2 = chunk + 2 < Nc;
-        if (has2) {
-            load_frags<D, TIn>(fa, chunk + 2, L, H, h, tokb, q, k, W, M, cidb);
-            load_vg<TIn, RES>(vg, chunk + 2, L, H, h, D, tokb, col0, v, g, cidb, h_prev);
-        }
-        carry_chunk<D, TIn, RES>(fb, Sv, chunk + 1, L, H, h, tokb, col, rho_c, red[1], vls[1], gls[1],
-                                  hl1, o, h_out, x_next);
-        if (has2) store_vg<TIn, RES>(vg, vls[0], gls[0], hl0);
+        carry_chunk<D, TIn, RES, XN>(cur, Sv, cc, L, H, h, tokb, col, rho_c, kq_cur, v_cur, g_cur, h_cur, &X, o,
+                                     h_out, x_next, [&]() __attribute__((always_inline)) {
+                                         if constexpr (G::KQ_STAGES == 1)
+                                             if (more)
+                                                 carry_issue<D, TIn, RES, true, false>(
+                                                     kq0_s, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb, col0,
+                                                     q, k, v, g, cidb, h_prev, wave, lane);
+                                     });
+    };
+    for (int cc = 0; cc < Nc; cc += 2) {
+        step(std::integral_constant<int, 0>(), cc, fa, fb);
+        if (cc + 1 < Nc) step(std::integral_constant<int, 1>(), cc + 1, fb, fa);
     }
     if (s_final) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                s_final[sbase + (int64_t)(sr0 + 16 * tt + 4 * lg + j) * D + col] = Sv[tt][j];
+                s_final[sbase + (int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] = Sv[tt][j];
     }
 }
 
@@ -640,13 +702,16 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
     const int Nc = (L + C - 1) / C;
     dim3 grid(H, D / 16, B);
     const int res = out.h_out == nullptr ? 0 : (out.h_prev_bf16 ? 2 : 1);
-#define CARRY(DD, T, R)                                                                            \
-    launch_kernel((k_scan_carry<DD, T, R>), grid, dim3(256), 0, s, (const T *)q,             \
-                       (const T *)k, (const T *)v, L, H, Nc, ws.W, ws.M, ws.g, s_init, s_final,   \
-                       out.o, out.h_prev, out.rho, out.h_out, out.x_next)
+    const bool xn = out.h_out != nullptr && out.x_next != nullptr;
+#define CARRY(DD, T, R, X)                                                                         \
+    launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,  \
+                  (const T *)v, L, H, Nc, ws.W, ws.M, ws.g, s_init, s_final, out.o, out.h_prev,    \
+                  out.rho, out.h_out, out.x_next)
 #define CARRY_R(DD, T)                                                                             \
     do {                                                                                           \
-        if (res == 0) CARRY(DD, T, 0); else if (res == 1) CARRY(DD, T, 1); else CARRY(DD, T, 2);   \
+        if (res == 0) CARRY(DD, T, 0, false);                                                      \
+        else if (res == 1) { if (xn) CARRY(DD, T, 1, true); else CARRY(DD, T, 1, false); }         \
+        else { if (xn) CARRY(DD, T, 2, true); else CARRY(DD, T, 2, false); }                       \
     } while (0)
     if (f32) {
         if (D == 128) CARRY_R(128, float); else CARRY_R(64, float);
