@@ -47,8 +47,8 @@ template <typename T> struct In;
 template <> struct In<float> { static constexpr bool f32 = true; };
 template <> struct In<bf16> { static constexpr bool f32 = false; };
 
-// Position of element (row, token c) of a per-chunk [R x 64] matrix (W: R = D
-// rows of S; M: R = 64 output tokens) in the carry's fragment order.  Rows are
+// Fragment order of the per-chunk [R x 64] matrices W (R = D rows of S) and M
+// (R = 64 output tokens) that the prep kernel writes and the carry reads.  Rows are
 // split over the 4 waves (RW = R/4 each, NT = RW/16 tiles of 16); row
 // RW w + 4 NT g + 4 tt + j (j < 4) is output row 4 g + j of the wave's tile tt
 // (for M, and for W with D = 64, this is simply row 16 tt + 4 g + j).  The 64
@@ -58,20 +58,61 @@ template <> struct In<bf16> { static constexpr bool f32 = false; };
 // [wave][tt][s][part: hi, lo][lane][8] bf16, so each wave reads its fragments
 // with fully coalesced 16-byte loads.  The lo part sits 8 * 64 elements after
 // the hi part.
-template <int R>
-__device__ __forceinline__ int64_t frag_index(int row, int c) {
-    constexpr int RW = R / 4, NT = RW / 16;
-    const int w = row / RW, rem = row % RW;
-    const int g = rem / (4 * NT), tt = (rem % (4 * NT)) / 4, lr = 4 * g + rem % 4;
-    const int s = c / 32, o = c % 32;
-    const int lg = (o % 16) / 4, jj = (o % 4) + (o >= 16 ? 4 : 0);
-    const int lane = lr + 16 * lg;
-    return ((((int64_t)(w * NT + tt) * 2 + s) * 2) * 64 + lane) * 8 + jj;
-}
 
 // ---------------------------------------------------------------------------
 // prep
 // ---------------------------------------------------------------------------
+// One workgroup (4 waves) per (b, h, chunk).  Decay products come from the
+// chunk's log-cumsum lg_r = sum_{m<=r} log alpha_m, kept in fp64 so that
+// Gam_ri = exp(lg_r - lg_i) loses nothing to cancellation (alpha is clamped
+// above 0; a true zero gate gives a product below 1e-37 instead of 0).
+// K K^T and K Q^T run on MFMA.  T = (I + N)^{-1} is formed from the 16x16
+// diagonal blocks (forward substitution in registers) merged 16 -> 32 -> 64
+// with the block rule [A 0; B C]^{-1} = [A^{-1} 0; -C^{-1} B A^{-1}  C^{-1}]
+// (split-bf16 MFMA products).  W and M are computed transposed on MFMA so that
+// each lane holds 8 consecutive fragment slots of the carry's layout and
+// stores them with one 16-byte write per part.
+
+// A or B fragment (8 values along k) of a 16x16x32 product from a row-major
+// LDS tile of TIn: elements [row][k0 .. k0+8).
+template <typename TIn>
+__device__ __forceinline__ void row_frag8(const TIn *tile, int ld, int row, int k0, float (&f)[8]) {
+    if constexpr (sizeof(TIn) == 2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(tile + row * ld + k0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(tile + row * ld + k0);
+        const float4 b = *reinterpret_cast<const float4 *>(tile + row * ld + k0 + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+}
+
+// c += a.b on 16x16x32 bf16 MFMA, exact when both are bf16 values (EXACT),
+// else with both operands split into bf16 hi + lo (3 passes).
+template <bool EXACT>
+__device__ __forceinline__ f32x4 mma8(const float (&a)[8], const float (&b)[8], f32x4 c) {
+    __bf16 ah[8], al[8], bh[8], bl[8];
+    split_bf16(a, ah, al);
+    split_bf16(b, bh, bl);
+    c = mfma16x16x32(pack8(ah), pack8(bh), c);
+    if constexpr (!EXACT) {
+        c = mfma16x16x32(pack8(ah), pack8(bl), c);
+        c = mfma16x16x32(pack8(al), pack8(bh), c);
+    }
+    return c;
+}
+// c += a.b on 16x16x16 (k = 4 (l/16) + i), both fp32, split (3 passes)
+__device__ __forceinline__ f32x4 mma4s(const float (&a)[4], const float (&b)[4], f32x4 c) {
+    __bf16 ah[4], al[4], bh[4], bl[4];
+    split_bf16(a, ah, al);
+    split_bf16(b, bh, bl);
+    c = mfma16x16x16(pack4(ah), pack4(bh), c);
+    c = mfma16x16x16(pack4(ah), pack4(bl), c);
+    return mfma16x16x16(pack4(al), pack4(bh), c);
+}
+
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
                                                    const TIn *__restrict__ k,
@@ -81,196 +122,249 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
                                                    float *__restrict__ wsM,
                                                    float *__restrict__ wsg) {
     constexpr bool F32 = In<TIn>::f32;
-    constexpr int PADK = F32 ? 4 : 8;
-    constexpr int LDK = D + PADK;  // row stride (elements) of the K/Q tiles
+    constexpr int LDK = D + (F32 ? 4 : 8);   // row stride (elements) of the K tile
+    constexpr int LT = C + 4;                // row stride (floats) of the 64x64 N and T tiles
+    constexpr int KS = D / 32;               // k-steps of the D contractions
+    constexpr int RW = D / 4, NT = RW / 16;  // W rows per wave, 16-row tiles per wave
     __shared__ __attribute__((aligned(16))) TIn Ks[C * LDK];
-    __shared__ __attribute__((aligned(16))) TIn Qs[C * LDK];
-    __shared__ float Gm[C * LDP];   // Gm[r][i] = prod_{i<m<=r} alpha_m  (i <= r)
-    __shared__ float Ns[C * LDP];
-    __shared__ float Ps[C * LDP];
-    __shared__ float Ts[C * LDP];
-    __shared__ float Xs[16 * 49];
-    __shared__ float als[C], bes[C], gam[C];
+    __shared__ __attribute__((aligned(16))) float Ns[C * LT];
+    __shared__ __attribute__((aligned(16))) float Ts[C * LT];
+    __shared__ __attribute__((aligned(16))) f32x4 Ys[4][64];
+    __shared__ double lgs[C];
+    __shared__ float bes[C];
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int c0 = chunk * C;
     const int64_t tok0 = (int64_t)b * L + c0;
 
-    // (1) K, Q tiles (zero rows past the end of the sequence), alpha, beta
-    constexpr int VEC = 16 / sizeof(TIn);        // elements per 16-byte load
-    constexpr int CPR = D / VEC;                 // 16-byte chunks per row
+    // (1) K tile (zero rows past the end), the Q fragments of this wave's 16
+    // tokens (B operand of K Q^T), gates, and the fp64 log-cumsum of alpha
+    constexpr int VEC = 16 / sizeof(TIn);
+    constexpr int CPR = D / VEC;
     for (int idx = t; idx < C * CPR; idx += 256) {
         const int r = idx / CPR, ch = idx % CPR;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-        if (c0 + r < L) {
-            const int64_t off = ((tok0 + r) * H + h) * D + ch * VEC;
-            kv = *reinterpret_cast<const uint4 *>(k + off);
-            qv = *reinterpret_cast<const uint4 *>(q + off);
-        }
+        uint4 kv = make_uint4(0, 0, 0, 0);
+        if (c0 + r < L) kv = *reinterpret_cast<const uint4 *>(k + ((tok0 + r) * H + h) * D + ch * VEC);
         *reinterpret_cast<uint4 *>(Ks + r * LDK + ch * VEC) = kv;
-        *reinterpret_cast<uint4 *>(Qs + r * LDK + ch * VEC) = qv;
     }
-    if (t < C) {
-        const bool ok = c0 + t < L;
-        als[t] = ok ? alpha[(tok0 + t) * H + h] : 1.f;   // padded tokens: identity transition
-        bes[t] = ok ? beta[(tok0 + t) * H + h] : 0.f;
-    }
-    __syncthreads();
-
-    // (2) decay products
-    if (t < C) {
-        float p = 1.f;
-        for (int i = t; i >= 0; --i) {
-            Gm[t * LDP + i] = p;
-            p *= als[i];
-        }
-        gam[t] = p;
-    }
-    __syncthreads();
-
-    // (3) K K^T and Q K^T, lower block triangle; wave w owns rows [16w, 16w+16)
+    float qf[KS][8];
     {
-        const int r_a = 16 * wave + (lane & 15);
-        const int kq = 8 * (lane >> 4);
+        const int r = 16 * wave + lr;
+        const bool ok = c0 + r < L;
+        const TIn *src = q + ((tok0 + (ok ? r : 0)) * H + h) * D + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qf[s][i] = ok ? to_f32(src[32 * s + i]) : 0.f;
+    }
+    if (wave == 0) {
+        const bool ok = c0 + lane < L;
+        const float a = ok ? alpha[(tok0 + lane) * H + h] : 1.f;   // padded tokens: identity
+        double x = log((double)fmaxf(a, 1e-37f));
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        lgs[lane] = x;
+        bes[lane] = ok ? beta[(tok0 + lane) * H + h] : 0.f;
+    }
+    // the strictly upper 16x16 blocks of T are zero
+    for (int idx = t; idx < 6 * 256; idx += 256) {
+        const int blk = idx >> 8, e = idx & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
+    }
+    __syncthreads();
+
+    // (2) N = diag(beta) strict_lower(Gam (.) K K^T) for this wave's 16 rows;
+    // P^T tiles (m-tile mt, r-tile wave) = Gam (.) K Q^T, m <= r, in registers
+    float pv[4][4];
+    {
+        const int r_a = 16 * wave + lr;
+#pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
             if (tn <= wave) {
-                const int r_b = 16 * tn + (lane & 15);
+                const int r_b = 16 * tn + lr;
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                    const int kc = 32 * ks + kq;
-                    if constexpr (!F32) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Ks + r_a * LDK + kc);
-                        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(Qs + r_a * LDK + kc);
-                        const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(Ks + r_b * LDK + kc);
-                        kk = mfma16x16x32(a, bb, kk);
-                        qk = mfma16x16x32(aq, bb, qk);
-                    } else {
-                        float fa[8], fq[8], fb[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            fa[i] = Ks[r_a * LDK + kc + i];
-                            fq[i] = Qs[r_a * LDK + kc + i];
-                            fb[i] = Ks[r_b * LDK + kc + i];
-                        }
-                        __bf16 ah[8], al[8], qh[8], ql[8], bh[8], bl[8];
-                        split_bf16(fa, ah, al);
-                        split_bf16(fq, qh, ql);
-                        split_bf16(fb, bh, bl);
-                        kk = mfma16x16x32(pack8(ah), pack8(bh), kk);
-                        kk = mfma16x16x32(pack8(ah), pack8(bl), kk);
-                        kk = mfma16x16x32(pack8(al), pack8(bh), kk);
-                        qk = mfma16x16x32(pack8(qh), pack8(bh), qk);
-                        qk = mfma16x16x32(pack8(qh), pack8(bl), qk);
-                        qk = mfma16x16x32(pack8(ql), pack8(bh), qk);
-                    }
+                for (int s = 0; s < KS; ++s) {
+                    float a[8], bb[8];
+                    row_frag8<TIn>(Ks, LDK, r_a, 32 * s + 8 * lg, a);
+                    row_frag8<TIn>(Ks, LDK, r_b, 32 * s + 8 * lg, bb);
+                    kk = mma8<!F32>(a, bb, kk);          // K_r . K_i   (rows r of this wave)
+                    kq = mma8<!F32>(bb, qf[s], kq);      // K_m . Q_r   (rows m of tile tn)
                 }
             }
-            const int col = 16 * tn + (lane & 15);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = 16 * wave + 4 * (lane >> 4) + j;
-                const float g = (col <= row) ? Gm[row * LDP + col] : 0.f;
-                Ns[row * LDP + col] = (col < row) ? bes[row] * g * kk[j] : 0.f;
-                Ps[row * LDP + col] = (col <= row) ? g * qk[j] : 0.f;
+                const int row = 16 * wave + 4 * lg + j, col = 16 * tn + lr;   // N[row][col]
+                float nv = 0.f;
+                if (col < row) nv = bes[row] * __expf((float)(lgs[row] - lgs[col])) * kk[j];
+                if (tn <= wave) Ns[row * LT + col] = nv;
+                const int m = 16 * tn + 4 * lg + j, r = 16 * wave + lr;       // P[r][m]
+                pv[tn][j] = (tn <= wave && m <= r) ? __expf((float)(lgs[r] - lgs[m])) * kq[j] : 0.f;
             }
         }
     }
     __syncthreads();
 
-    // (4) T = (I + N)^{-1}: diagonal 16x16 blocks by forward substitution ...
-    for (int idx = t; idx < C * C; idx += 256) {  // zero everything above the block diagonal
-        const int r = idx / C, c = idx % C;
-        if ((c >> 4) > (r >> 4)) Ts[r * LDP + c] = 0.f;
-    }
-    if (t < C) {
-        const int blk = t >> 4, c = t & 15, base = 16 * blk, col = base + c;
-        for (int r = 0; r < 16; ++r) {
-            const int row = base + r;
-            float val;
-            if (r < c) val = 0.f;
-            else if (r == c) val = 1.f;
-            else {
-                val = 0.f;
-                for (int i = c; i < r; ++i) val -= Ns[row * LDP + base + i] * Ts[(base + i) * LDP + col];
-            }
-            Ts[row * LDP + col] = val;
+    // (3) diagonal block `wave` of T by forward substitution: lane column c = lr
+    {
+        float tv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tv[i] = (i == lr) ? 1.f : 0.f;
+        const float *nb = Ns + (16 * wave) * LT + 16 * wave;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc = fmaf(nb[r * LT + i], tv[i], acc);
+            if (r > lr) tv[r] = -acc;
+        }
+        if (lg == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ts[(16 * wave + r) * LT + 16 * wave + lr] = tv[r];
         }
     }
     __syncthreads();
-    // ... then block rows: T_ij = -T_ii sum_{m=j}^{i-1} N_im T_mj  (j < i)
-    for (int bi = 1; bi < 4; ++bi) {
-        for (int idx = t; idx < 256 * bi; idx += 256) {
-            const int bj = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
-            const int row = 16 * bi + r, col = 16 * bj + c;
-            float acc = 0.f;
-            for (int m = 16 * bj; m < 16 * bi; ++m) acc += Ns[row * LDP + m] * Ts[m * LDP + col];
-            Xs[r * 49 + 16 * bj + c] = acc;
-        }
-        __syncthreads();
-        for (int idx = t; idx < 256 * bi; idx += 256) {
-            const int bj = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
-            const int row = 16 * bi + r, col = 16 * bj + c;
-            float acc = 0.f;
-            for (int m = 0; m <= r; ++m) acc += Ts[row * LDP + 16 * bi + m] * Xs[m * 49 + 16 * bj + c];
-            Ts[row * LDP + col] = -acc;
-        }
-        __syncthreads();
-    }
 
-    // (5) Tb = T diag(beta)
-    for (int idx = t; idx < C * C; idx += 256) {
-        const int r = idx / C, c = idx % C;
-        Ts[r * LDP + c] *= bes[c];
+    // 16x16 block helpers on MFMA 16x16x16 (k = 4 lg + i): A rows from a
+    // row-major tile, B (k x col) from a row-major tile or a C-layout register
+    auto a_rows = [&](const float *tile, int row0, int col0, float (&f)[4]) {
+        const float4 v = *reinterpret_cast<const float4 *>(tile + (row0 + lr) * LT + col0 + 4 * lg);
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    };
+    auto b_cols = [&](const float *tile, int row0, int col0, float (&f)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = tile[(row0 + 4 * lg + i) * LT + col0 + lr];
+    };
+    // (4) T_{2i+1, 2i} = -T_{2i+1,2i+1} N_{2i+1,2i} T_{2i,2i}  (waves 0, 1)
+    if (wave < 2) {
+        const int bi = 2 * wave + 1, bj = 2 * wave;
+        float a[4], bb[4];
+        f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+        a_rows(Ns, 16 * bi, 16 * bj, a);
+        b_cols(Ts, 16 * bj, 16 * bj, bb);
+        y = mma4s(a, bb, y);
+        a_rows(Ts, 16 * bi, 16 * bi, a);
+        const float yb[4] = {y[0], y[1], y[2], y[3]};
+        z = mma4s(a, yb, z);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ts[(16 * bi + 4 * lg + j) * LT + 16 * bj + lr] = -z[j];
+    }
+    __syncthreads();
+    // (5) rows 32..63, cols 0..31: -T_BB (N_BA T_AA) on 16x16 blocks (p, qq)
+    const int p = wave >> 1, qq = wave & 1;
+    {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb < qq) continue;   // T_{kb, qq} = 0 above the diagonal
+            float a[4], bb[4];
+            a_rows(Ns, 16 * (2 + p), 16 * kb, a);
+            b_cols(Ts, 16 * kb, 16 * qq, bb);
+            y = mma4s(a, bb, y);
+        }
+        Ys[wave][lane] = y;
+    }
+    __syncthreads();
+    {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb > p) continue;   // T_BB is block lower triangular
+            float a[4];
+            a_rows(Ts, 16 * (2 + p), 16 * (2 + kb), a);
+            const f32x4 yv = Ys[2 * kb + qq][lane];
+            const float yb[4] = {yv[0], yv[1], yv[2], yv[3]};
+            z = mma4s(a, yb, z);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ts[(16 * (2 + p) + 4 * lg + j) * LT + 16 * qq + lr] = -z[j];
     }
     __syncthreads();
 
+    // (6) Tb^T fragments, A operand over k = token m (carry slot order):
+    // Tb[m][c] = T[m][c] beta_c; the W variant also carries gamma_C / gamma_m
     const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
-    // (6) W[i][c] = sum_r K[r][i] * (gamma_C / gamma_r) * Tb[r][c]
-    {
-        constexpr int IPT = D / 4;
-        const int c = t & 63, i0 = (t >> 6) * IPT;
-        float acc[IPT];
+    bf16 *dW = reinterpret_cast<bf16 *>(wsW + cid * D * C);
+    bf16 *dM = reinterpret_cast<bf16 *>(wsM + cid * C * C);
+    const double lgC = lgs[C - 1];
+    float am[4][2][8], aw[4][2][8];
 #pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) acc[ii] = 0.f;
-        for (int r = 0; r < C; ++r) {
-            const float g = Gm[(C - 1) * LDP + r] * Ts[r * LDP + c];
+    for (int ct = 0; ct < 4; ++ct) {
+        const int c = 16 * ct + lr;
+        const float bc = bes[c];
 #pragma unroll
-            for (int ii = 0; ii < IPT; ++ii) acc[ii] = fmaf(to_f32(Ks[r * LDK + i0 + ii]), g, acc[ii]);
-        }
-        // W ~= Wh + Wl (bf16 hi/lo) stored in the carry's fragment order
-        bf16 *dst = reinterpret_cast<bf16 *>(wsW + cid * D * C);
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) {
-            const bf16 hi = (bf16)acc[ii];
-            const int64_t at = frag_index<D>(i0 + ii, c);
-            dst[at] = hi;
-            dst[at + 8 * 64] = (bf16)(acc[ii] - (float)hi);
+            for (int jj = 0; jj < 8; ++jj) {
+                const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
+                const float tb = Ts[m * LT + c] * bc;
+                am[ct][s][jj] = tb;
+                aw[ct][s][jj] = tb * __expf((float)(lgC - lgs[m]));
+            }
+    }
+    // (7) W^T tiles: rows c (token), columns = this wave's S rows; lane column
+    // lr of tile tt is S row RW wave + 4 NT (lr / 4) + 4 tt + lr % 4
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        const int i = RW * wave + 4 * NT * (lr >> 2) + 4 * tt + (lr & 3);
+        float bk[2][8];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
+                bk[s][jj] = to_f32(Ks[m * LDK + i]);
+            }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {   // output k-step of the carry: c-tiles 2 s2, 2 s2 + 1
+            f32x4 acc[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) acc[h2] = mma8<false>(aw[2 * s2 + h2][s], bk[s], acc[h2]);
+            }
+            float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+            __bf16 vh[8], vl[8];
+            split_bf16(v, vh, vl);
+            bf16 *dst = dW + ((((int64_t)(wave * NT + tt) * 2 + s2) * 2) * 64 + lane) * 8;
+            *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
+            *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
         }
     }
-    // (7) M[r][c] = sum_m P[r][m] Tb[m][c]
-    {
-        const int c = t & 63, r0 = (t >> 6) * 16;
-        float acc[16];
+    // (8) M^T tiles: rows c, columns = output tokens 16 wave + lr; B = P^T from
+    // registers (k-step s covers the m-tiles 2s, 2s+1)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[rr] = 0.f;
-        for (int m = 0; m < C; ++m) {
-            const float tb = Ts[m * LDP + c];
+    for (int s2 = 0; s2 < 2; ++s2) {
+        f32x4 acc[2];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) acc[rr] = fmaf(Ps[(r0 + rr) * LDP + m], tb, acc[rr]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+            acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (2 * s > wave) continue;   // P[r][m] = 0 for m > r
+                const float bp[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
+                                     pv[2 * s + 1][0], pv[2 * s + 1][1], pv[2 * s + 1][2], pv[2 * s + 1][3]};
+                acc[h2] = mma8<false>(am[2 * s2 + h2][s], bp, acc[h2]);
+            }
         }
-        bf16 *dst = reinterpret_cast<bf16 *>(wsM + cid * C * C);
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const bf16 hi = (bf16)acc[rr];
-            const int at = frag_index<C>(r0 + rr, c);   // M rows: 16 per wave, like a D = 64 W
-            dst[at] = hi;
-            dst[at + 8 * 64] = (bf16)(acc[rr] - (float)hi);
-        }
+        float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+        __bf16 vh[8], vl[8];
+        split_bf16(v, vh, vl);
+        bf16 *dst = dM + ((((int64_t)wave * 2 + s2) * 2) * 64 + lane) * 8;
+        *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
+        *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
     }
-    // (8) gamma
-    if (t < C) wsg[cid * C + t] = gam[t];
+    // (9) gamma
+    if (t < C) wsg[cid * C + t] = __expf((float)lgs[t]);
 }
 
 // ---------------------------------------------------------------------------
@@ -459,12 +553,12 @@ struct CarryLdsX {
     uint4 ex[4][64];          // [token tile][lane]: E hi (bf16x4) in .x .y, lo in .z .w
 };
 
-template <int D, typename TIn, int RES, bool XN, typename AfterB1>
+template <int D, typename TIn, int RES, bool XN, typename AfterKS, typename AfterB1, typename AfterB2>
 __device__ __forceinline__ void carry_chunk(
     const WMFrags<D> &F, float (&Sv)[D / 64][4], int cc, int L, int H, int h, int64_t tokb, int col,
     float rho_c, const unsigned char *__restrict__ kq, const unsigned char *__restrict__ vs,
     const float *__restrict__ gs, const unsigned char *__restrict__ hs, CarryLdsX *__restrict__ Xp,
-    float *o, float *h_out, bf16 *x_next, AfterB1 &&after_b1) {
+    float *o, float *h_out, bf16 *x_next, AfterKS &&after_ks, AfterB1 &&after_b1, AfterB2 &&after_b2) {
     CarryLdsX &X = *Xp;
     using G = CarryCfg<D, TIn>;
     constexpr int NT = G::NT, KW = G::KW;
@@ -496,6 +590,8 @@ __device__ __forceinline__ void carry_chunk(
             X.red[wave][tm][0][lane] = ks[tm];
             X.red[wave][tm][1][lane] = qs[tm];
         }
+    after_ks();      // part of the next chunk's loads, spread over the chunk so that
+                     // issuing them does not stall the wave on a full memory pipeline
     lds_barrier();   // (B1) partials visible; every wave done reading this chunk's K and Q
     after_b1();      // single-buffered K/Q: the next chunk's tiles may now be loaded
     // own token tile: sum of the four partials (wave-uniform selects keep tiles in registers)
@@ -529,6 +625,7 @@ __device__ __forceinline__ void carry_chunk(
         X.ex[wave][lane] = u;
     }
     lds_barrier();   // (B2) every E tile visible
+    after_b2();
     // E as the B operand: k-step s covers the token tiles 2s and 2s+1
     bf16x8 ebh[2], ebl[2];
 #pragma unroll
@@ -651,19 +748,26 @@ __global__ __launch_bounds__(256) void k_scan_carry(
         wait_vmcnt<NST>();   // only the previous chunk's stores may remain in flight
         lds_barrier();            // (B0) chunk cc's direct loads of every wave have landed
         const bool more = cc + 1 < Nc;
-        if (more) {
-            carry_issue<D, TIn, RES, G::KQ_STAGES == 2, true>(kq_nxt, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb,
-                                                            col0, q, k, v, g, cidb, h_prev, wave, lane);
-            load_wm<D>(nxt, W, M, cidb + cc + 1, wave, lane);
-        }
-        carry_chunk<D, TIn, RES, XN>(cur, Sv, cc, L, H, h, tokb, col, rho_c, kq_cur, v_cur, g_cur, h_cur, &X, o,
-                                     h_out, x_next, [&]() __attribute__((always_inline)) {
-                                         if constexpr (G::KQ_STAGES == 1)
-                                             if (more)
-                                                 carry_issue<D, TIn, RES, true, false>(
-                                                     kq0_s, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb, col0,
-                                                     q, k, v, g, cidb, h_prev, wave, lane);
-                                     });
+        if constexpr (G::KQ_STAGES == 2)
+            if (more)
+                carry_issue<D, TIn, RES, true, false>(kq_nxt, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb, col0, q,
+                                                      k, v, g, cidb, h_prev, wave, lane);
+        carry_chunk<D, TIn, RES, XN>(
+            cur, Sv, cc, L, H, h, tokb, col, rho_c, kq_cur, v_cur, g_cur, h_cur, &X, o, h_out, x_next,
+            [&]() __attribute__((always_inline)) {
+                if (more) load_wm<D>(nxt, W, M, cidb + cc + 1, wave, lane);
+            },
+            [&]() __attribute__((always_inline)) {
+                if constexpr (G::KQ_STAGES == 1)
+                    if (more)
+                        carry_issue<D, TIn, RES, true, false>(kq0_s, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb,
+                                                              col0, q, k, v, g, cidb, h_prev, wave, lane);
+            },
+            [&]() __attribute__((always_inline)) {
+                if (more)
+                    carry_issue<D, TIn, RES, false, true>(kq_nxt, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb,
+                                                          col0, q, k, v, g, cidb, h_prev, wave, lane);
+            });
     };
     for (int cc = 0; cc < Nc; cc += 2) {
         step(std::integral_constant<int, 0>(), cc, fa, fb);
