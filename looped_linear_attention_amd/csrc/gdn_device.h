@@ -66,8 +66,15 @@ __device__ __forceinline__ bf16x4 pack4(const __bf16 (&v)[4]) {
 
 // Workgroup barrier that waits only for LDS traffic (outstanding global loads
 // issued for a later step stay in flight across it).
+// Built from the builtins (not inline asm) so that the compiler's own wait
+// tracking knows every LDS access has completed here and adds no wait of its
+// own for them later; the empty asm statements keep memory operations from
+// being scheduled across the barrier.
 __device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }

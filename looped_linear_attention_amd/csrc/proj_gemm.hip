@@ -134,86 +134,102 @@ constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
 __device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz(int r, int ch) { return r * BK_BF + ((ch ^ swz_key(r)) << 3); }
 
-// Issues the direct loads of k-block starting at channel k0 into one stage.
-// A: 2048 chunks, wave w instruction i covers LDS chunks [(4 i + w) 64, +64);
-// B: 1024 chunks likewise with i < 4.  LDS chunk p holds row p / 8, logical
-// chunk (p % 8) ^ swz_key(row) of the tile.
+// Direct loads of loads [I0, I1) of one k-block (starting at channel k0) into
+// one stage: loads 0..7 fill the A tile (2048 chunks; wave w's load i covers
+// LDS chunks [(4 i + w) 64, +64)), loads 8..11 the B tile (1024 chunks, same
+// rule).  LDS chunk p holds row p / 8, logical chunk (p % 8) ^ swz_key(row).
+template <int I0, int I1>
 __device__ __forceinline__ void gemm_issue(bf16 *stage, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int m0,
                                            int n0, int M, int K, int b_rows, int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int base = (4 * i + wave) * 64, p = base + lane;
-        const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
-        const int m = min(m0 + r, M - 1);   // tail rows re-read the last row; never stored
-        __builtin_amdgcn_global_load_lds(x + (int64_t)m * K + k0 + ch * 8,
-                                         (lds_void *)(stage + base * 8), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int base = (4 * i + wave) * 64, p = base + lane;
-        const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
-        const int rr = min(r, b_rows - 1);   // gate tile: unused rows repeat a used one
-        __builtin_amdgcn_global_load_lds(Wp + (int64_t)(n0 + rr) * K + k0 + ch * 8,
-                                         (lds_void *)(stage + A_ELEMS + base * 8), 16, 0, 0);
+    for (int i = I0; i < I1; ++i) {
+        if (i < 8) {
+            const int base = (4 * i + wave) * 64, p = base + lane;
+            const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
+            const int m = min(m0 + r, M - 1);   // tail rows re-read the last row; never stored
+            __builtin_amdgcn_global_load_lds(x + (int64_t)m * K + k0 + ch * 8,
+                                             (lds_void *)(stage + base * 8), 16, 0, 0);
+        } else {
+            const int base = (4 * (i - 8) + wave) * 64, p = base + lane;
+            const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
+            const int rr = min(r, b_rows - 1);   // gate tile: unused rows repeat a used one
+            __builtin_amdgcn_global_load_lds(Wp + (int64_t)(n0 + rr) * K + k0 + ch * 8,
+                                             (lds_void *)(stage + A_ELEMS + base * 8), 16, 0, 0);
+        }
     }
 }
 
-// The k-loop of one tile.  GATE: only the 32-column MFMA tiles holding used
-// gate columns are computed (a wave-uniform condition outside the hot path).
+// Operand fragments of one k-block (4 k-steps x (4 A + 2 B) 32x32x16 fragments).
+struct KFrags {
+    bf16x8 a[BK_BF / 16][4], b[BK_BF / 16][2];
+};
+
+__device__ __forceinline__ void read_frags_step(KFrags &F, const bf16 *stage, int s, int lane, int wm, int wn) {
+    const bf16 *Ab = stage, *Bb = stage + A_ELEMS;
+    const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+        F.a[s][tm] = *reinterpret_cast<const bf16x8 *>(Ab + swz(wm * 128 + tm * 32 + (lane & 31), ch));
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+        F.b[s][tn] = *reinterpret_cast<const bf16x8 *>(Bb + swz(wn * 64 + tn * 32 + (lane & 31), ch));
+}
+
+// The k-loop of one tile, software-pipelined over three LDS stages and two
+// fragment register sets.  Iteration kb: wait until k-block kb+1 has landed
+// (kb+2's loads may stay in flight), barrier, then per k-step: issue a quarter
+// of k-block kb+3's direct loads (into the stage that held kb, whose fragments
+// were read during the previous iteration), read k-block kb+1's fragments into
+// the idle register set, and run k-block kb's MFMAs from the other set.  The
+// direct loads go out in small groups between MFMAs so that issuing them never
+// fills the memory pipeline's queue, which would stall the wave's MFMA issue.
+// Past the end the loads re-read the last k-block into a free stage, so every
+// iteration has the same shape.  GATE: only the 32-column MFMA tiles holding
+// used gate columns are computed (a wave-uniform condition).
 template <bool GATE>
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int wm,
                                            int wn, int m0, int n0, int M, int K, int b_rows,
                                            int gate_cols) {
     const int nkb = K / BK_BF;   // >= 1
-    gemm_issue(stages, x, Wp, lane, wave, m0, n0, M, K, b_rows, 0);
-    if (nkb > 1) gemm_issue(stages + STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, BK_BF);
+    auto kblock = [&](int kb) { return min(kb, nkb - 1) * BK_BF; };
+    gemm_issue<0, 12>(stages, x, Wp, lane, wave, m0, n0, M, K, b_rows, 0);
+    gemm_issue<0, 12>(stages + STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(1));
+    gemm_issue<0, 12>(stages + 2 * STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(2));
+    wait_vmcnt<24>();   // k-block 0 landed
+    lds_barrier();
     const bool tn_on[2] = {!GATE || wn * 64 < gate_cols, !GATE || wn * 64 + 32 < gate_cols};
-    for (int kb = 0; kb < nkb; ++kb) {
-        // this wave's loads of k-block kb are done once at most the 12 of kb+1 remain
-        if (kb + 1 < nkb) wait_vmcnt<12>();
-        else wait_vmcnt<0>();
-        lds_barrier();   // every wave's loads of kb landed; every wave finished k-block kb-1
-        if (kb + 2 < nkb)
-            gemm_issue(stages + ((kb + 2) % STAGES) * STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K,
-                       b_rows, (kb + 2) * BK_BF);
-        if (GATE && !tn_on[0] && !tn_on[1]) continue;
-        const bf16 *Ab = stages + (kb % STAGES) * STAGE_ELEMS;
-        const bf16 *Bb = Ab + A_ELEMS;
-        // fragments double-buffered across the 4 k-steps: step s+1 is read from LDS
-        // while step s is multiplied
-        bf16x8 af[2][4], bfr[2][2];
-        auto frag = [&](int s, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
-            const int ch = 2 * s + (lane >> 5);
+    KFrags f0, f1;
 #pragma unroll
-            for (int tm = 0; tm < 4; ++tm)
-                a[tm] = *reinterpret_cast<const bf16x8 *>(Ab + swz(wm * 128 + tm * 32 + (lane & 31), ch));
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
-                b[tn] = *reinterpret_cast<const bf16x8 *>(Bb + swz(wn * 64 + tn * 32 + (lane & 31), ch));
-        };
-        frag(0, af[0], bfr[0]);
+    for (int s = 0; s < BK_BF / 16; ++s) read_frags_step(f0, stages, s, lane, wm, wn);
+
+    auto step = [&](int kb, const KFrags &cur, KFrags &nxt) __attribute__((always_inline)) {
+        wait_vmcnt<12>();   // k-block kb+1 landed (kb+2's 12 loads may remain)
+        lds_barrier();      // ... for every wave; every wave has read k-block kb's fragments
+        bf16 *ld_stage = stages + (kb % STAGES) * STAGE_ELEMS;           // receives kb+3
+        const bf16 *rd_stage = stages + ((kb + 1) % STAGES) * STAGE_ELEMS;
+        const int k3 = kblock(kb + 3);
 #pragma unroll
         for (int s = 0; s < BK_BF / 16; ++s) {
-            if (s + 1 < BK_BF / 16) frag(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-            const int cur = s & 1;
-            if constexpr (!GATE) {
+            if (s == 0) gemm_issue<0, 3>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 1) gemm_issue<3, 6>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 2) gemm_issue<6, 9>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 3) gemm_issue<9, 12>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            read_frags_step(nxt, rd_stage, s, lane, wm, wn);
 #pragma unroll
-                for (int tm = 0; tm < 4; ++tm)
+            for (int tn = 0; tn < 2; ++tn)
+                if (tn_on[tn])
 #pragma unroll
-                    for (int tn = 0; tn < 2; ++tn)
-                        acc[tm][tn] = mfma32x32x16(af[cur][tm], bfr[cur][tn], acc[tm][tn]);
-            } else {
-#pragma unroll
-                for (int tn = 0; tn < 2; ++tn)
-                    if (tn_on[tn])
-#pragma unroll
-                        for (int tm = 0; tm < 4; ++tm)
-                            acc[tm][tn] = mfma32x32x16(af[cur][tm], bfr[cur][tn], acc[tm][tn]);
-            }
+                    for (int tm = 0; tm < 4; ++tm)
+                        acc[tm][tn] = mfma32x32x16(cur.a[s][tm], cur.b[s][tn], acc[tm][tn]);
         }
+    };
+    for (int kb = 0; kb < nkb; kb += 2) {
+        step(kb, f0, f1);
+        if (kb + 1 < nkb) step(kb + 1, f1, f0);
     }
+    wait_vmcnt<0>();   // the re-reads past the end land before LDS is reused
 }
 
 // One workgroup per CU (the three LDS stages take 144 KB), i.e. one wave per
