@@ -100,7 +100,7 @@ def bench_prefill(args, w, torch, gl, synth):
     torch.cuda.synchronize()
 
     stages = {"project": gl.GDN_STAGE_PROJECT, "scan_prep": gl.GDN_STAGE_SCAN_PREP,
-              "scan_carry": gl.GDN_STAGE_SCAN_CARRY}
+              "scan_state": gl.GDN_STAGE_SCAN_CARRY, "scan_out": gl.GDN_STAGE_SCAN_OUT}
     timers = {k: gl.gdn_timer_create(v, args.steps * w.T) for k, v in stages.items()}
     for t in timers.values():
         gl.gdn_timer_attach(t)

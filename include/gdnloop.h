@@ -182,7 +182,7 @@ const char *gdn_version(void);
 
 /* Stages that a timer can bracket. */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
-       GDN_STAGE_DECODE = 3 };
+       GDN_STAGE_DECODE = 3, GDN_STAGE_SCAN_OUT = 4 };
 
 /* While a timer is attached, every launch of its stage carries a pair of HIP
  * events on its dispatch (hipExtLaunchKernel start/stop events), so each pair

@@ -85,7 +85,7 @@ gdn_status check_desc(const gdn_desc *d, bool decode) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, W = 0, M = 0, g = 0, x = 0, total = 0;
+    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, W = 0, M = 0, g = 0, sc = 0, x = 0, total = 0;
 };
 
 Layout layout(const gdn_desc *d, int op) {
@@ -114,6 +114,7 @@ Layout layout(const gdn_desc *d, int op) {
         lo.W = take(bh * Nc * D * CHUNK * 4);
         lo.M = take(bh * Nc * CHUNK * CHUNK * 4);
         lo.g = take(bh * Nc * CHUNK * 4);
+        lo.sc = take(carry_ws_bytes(d->act == GDN_F32, (int)D, bh * Nc));
     }
     lo.total = off;
     return lo;
@@ -133,9 +134,9 @@ struct gdn_timer {
 
 namespace {
 
-constexpr int N_STAGES = GDN_STAGE_DECODE + 1;
+constexpr int N_STAGES = GDN_STAGE_SCAN_OUT + 1;
 thread_local LaunchEvents t_launch_events{nullptr, nullptr};
-gdn_timer *g_timers[N_STAGES] = {nullptr, nullptr, nullptr, nullptr};
+gdn_timer *g_timers[N_STAGES] = {nullptr, nullptr, nullptr, nullptr, nullptr};
 
 // Runs `launch` (exactly one kernel launch) with the stage timer's next event
 // pair armed, when a timer for `stage` is attached.
@@ -223,15 +224,21 @@ static gdn_status scan_chunks(const gdn_desc *d, const void *q, const void *k, c
                               float *s_final, CarryOut out, void *ws, const Layout &lo,
                               hipStream_t s) {
     const bool f32 = d->act == GDN_F32;
-    ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g)};
+    const int64_t Nc = (d->L + CHUNK - 1) / CHUNK, heads = (int64_t)d->B * d->H;
+    // the E tiles follow the chunk-start states inside the sc region
+    const size_t sc_bytes = (size_t)heads * Nc * d->dk * d->dv * 4;
+    ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g),
+               (bf16 *)at(ws, lo.sc), (uint4 *)at(ws, lo.sc + sc_bytes)};
     hipError_t e = timed(GDN_STAGE_SCAN_PREP, s, [&] {
         return launch_scan_prep(f32, d->B, d->L, d->H, d->dk, q, k, alpha, beta, cw, s);
     });
     if (e != hipSuccess) return hip_fail(e, "chunk prep launch");
     e = timed(GDN_STAGE_SCAN_CARRY, s, [&] {
-        return launch_scan_carry(f32, d->B, d->L, d->H, d->dk, q, k, v, cw, s_init, s_final, out, s);
+        return launch_scan_state(f32, d->B, d->L, d->H, d->dk, k, v, cw, s_init, s_final, s);
     });
-    if (e != hipSuccess) return hip_fail(e, "state carry launch");
+    if (e != hipSuccess) return hip_fail(e, "state pass launch");
+    e = timed(GDN_STAGE_SCAN_OUT, s, [&] { return launch_scan_out(f32, d->B, d->L, d->H, d->dk, q, cw, out, s); });
+    if (e != hipSuccess) return hip_fail(e, "output pass launch");
     return GDN_OK;
 }
 
@@ -360,7 +367,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_DECODE || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_SCAN_OUT || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

@@ -154,11 +154,21 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
     {
         const int r = 16 * wave + lr;
         const bool ok = c0 + r < L;
-        const TIn *src = q + ((tok0 + (ok ? r : 0)) * H + h) * D + 8 * lg;
+        const TIn *src = q + ((tok0 + (ok ? r : 0)) * H + h) * D + 8 * lg;   // 16-byte aligned runs
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) {
+            if constexpr (F32) {
+                const float4 a = *reinterpret_cast<const float4 *>(src + 32 * s);
+                const float4 c = *reinterpret_cast<const float4 *>(src + 32 * s + 4);
+                const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qf[s][i] = ok ? to_f32(src[32 * s + i]) : 0.f;
+                for (int i = 0; i < 8; ++i) qf[s][i] = ok ? v[i] : 0.f;
+            } else {
+                const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src + 32 * s);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qf[s][i] = ok ? (float)v[i] : 0.f;
+            }
+        }
     }
     if (wave == 0) {
         const bool ok = c0 + lane < L;
@@ -368,58 +378,65 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// carry
+// carry: state pass (sequential over chunks) and output pass (parallel)
 // ---------------------------------------------------------------------------
-// One workgroup per (b, h, 16-column slice of S); wave w keeps RW = D/4 rows
-// of the fp32 state slice in registers.  Lane l = lr + 16 g holds column lr
-// and, in tile tt of its rows, the rows
+// State pass: one workgroup per (b, h, 16-column slice of S); the columns of S
+// never mix, so column slices are independent scans.  Wave w keeps RW = D/4
+// rows of the fp32 state slice in registers.  Lane l = lr + 16 g holds column
+// lr and, in tile tt of its rows, the rows
 //     srow(w, g, tt, j) = RW w + 4 NT g + 4 tt + j,   j = 0..3,
 // so the KW rows a lane contributes to the K.S product are contiguous
 // (RW w + KW g .. + KW) and its K fragment is one contiguous run of a token
 // row.  Row order inside an MFMA output tile is free, so the W fragments that
 // update S (written by the prep kernel) put S row srow(w, g, tt, j) at output
-// row 4 g + j of tile tt.
+// row 4 g + j of tile tt.  Per chunk: the wave's partial K.S over its rows,
+// reduce-scatter through LDS (wave w owns tokens 16w..16w+15), E = V -
+// diag(gamma) K S for its tokens, all-gather of the E tiles through LDS, then
+// S' = gamma_C S + W E on its rows.  The chunk-start state and the E tiles go
+// to the workspace in the exact register order in which the output pass uses
+// them as MFMA operands.  The K tile, the V slice and gamma are copied global
+// -> LDS with direct loads a chunk ahead (double-buffered); the wave's W
+// fragments come straight into registers, also a chunk ahead.
 //
-// Per chunk the K and Q tiles, the V and h_prev slices and gamma are copied
-// global -> LDS with direct loads (coalesced 16-byte rows, XOR-swizzled so the
-// fragment reads are bank-conflict free), double-buffered where LDS allows, a
-// chunk ahead of use; the per-wave W and M fragments come straight into
-// registers, also a chunk ahead.  Exchange per chunk: each wave's partial K.S
-// and Q.S of the three token tiles it does not own go through LDS (reduce-
-// scatter; wave w owns tokens 16w..16w+15), then the E tile of each wave goes
-// through LDS to all waves (all-gather), since W.E and M.E contract over all
-// 64 tokens.
+// Output pass: one workgroup per (b, h, chunk), computing
+//     O = diag(gamma) Q S_c + M E   (S_c the chunk-start state)
+// and either O itself or the loop residual h = O + rho (.) h_prev (with a bf16
+// copy for the next loop's projection).  Fully parallel over chunks.
 template <int D, typename TIn> struct CarryCfg {
     static constexpr int RW = D / 4;                     // state rows per wave
     static constexpr int NT = RW / 16;                   // 16-row tiles per wave
-    static constexpr int KW = (D == 128) ? 8 : 4;        // k-width of the K.S MFMA
+    static constexpr int KW = (D == 128) ? 8 : 4;        // k-width of the K.S / Q.S MFMA
+    static constexpr int NSL = D / 16;                   // column slices of S
     static constexpr int ES = (int)sizeof(TIn);
-    static constexpr int ROWB = D * ES;                  // bytes of a token row of K or Q
+    static constexpr int ROWB = D * ES;                  // bytes of a token row of K
     static constexpr int NCH = ROWB / 16;                // 16-byte chunks per row
     static constexpr int SH = (ES == 4 && D == 128) ? 1 : 0;
-    static constexpr int TILE = C * ROWB;                // bytes of a K or Q chunk tile
-    static constexpr int KQ_STAGES = (4 * TILE <= 65536) ? 2 : 1;
-    static constexpr int KQ_INS = 2 * TILE / 1024;       // direct-load instructions for K and Q
+    static constexpr int TILE = C * ROWB;                // bytes of a K chunk tile
+    static constexpr int K_INS = TILE / 1024;            // direct-load instructions for K
     static constexpr int VROWB = 16 * ES;                // bytes of a token row of the V slice
     static constexpr int V_INS = C * VROWB / 1024;
+    // workspace elements per (b, h, chunk): chunk-start state, hi and lo bf16
+    // planes as [slice][wave][part][lane][KW]; E tiles as [slice][tile][lane] of
+    // 16 bytes (4 bf16 hi then 4 bf16 lo)
+    static constexpr int64_t SC_ELEMS = (int64_t)NSL * 4 * 2 * 64 * KW;   // bf16
+    static constexpr int64_t E_BYTES = (int64_t)NSL * 4 * 64 * 16;
 };
 
-// physical 16-byte chunk of logical chunk c in row r of a K/Q tile
+// physical 16-byte chunk of logical chunk c in row r of a K tile
 template <int D, typename TIn>
-__device__ __forceinline__ int kq_phys(int r, int c) {
+__device__ __forceinline__ int k_phys(int r, int c) {
     using G = CarryCfg<D, TIn>;
     return c ^ ((r << G::SH) & (G::NCH - 1));
 }
 
-// Per-wave W and M fragments of one chunk (bf16 hi/lo, fragment order).
-template <int D> struct WMFrags {
+// Per-wave W fragments of one chunk (bf16 hi/lo, fragment order).
+template <int D> struct WFrags {
     static constexpr int NT = D / 64;
-    bf16x8 wh[NT][2], wl[NT][2], mh[2], ml[2];
+    bf16x8 wh[NT][2], wl[NT][2];
 };
 
 template <int D>
-__device__ __forceinline__ void load_wm(WMFrags<D> &F, const float *W, const float *M, int64_t cid,
-                                        int wave, int lane) {
+__device__ __forceinline__ void load_w(WFrags<D> &F, const float *W, int64_t cid, int wave, int lane) {
     constexpr int NT = D / 64;
     const bf16x8 *Wf = reinterpret_cast<const bf16x8 *>(W + cid * D * C) + (int64_t)wave * NT * 4 * 64 + lane;
 #pragma unroll
@@ -429,67 +446,40 @@ __device__ __forceinline__ void load_wm(WMFrags<D> &F, const float *W, const flo
             F.wh[tt][s] = Wf[((tt * 2 + s) * 2 + 0) * 64];
             F.wl[tt][s] = Wf[((tt * 2 + s) * 2 + 1) * 64];
         }
-    const bf16x8 *Mf = reinterpret_cast<const bf16x8 *>(M + cid * C * C) + (int64_t)wave * 4 * 64 + lane;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        F.mh[s] = Mf[(s * 2 + 0) * 64];
-        F.ml[s] = Mf[(s * 2 + 1) * 64];
-    }
 }
 
-// Issues this wave's share of the direct loads of chunk `cc`: K and Q tiles
-// (into kq, when KQ is set), V slice and gamma (vs, gs) and, RES != 0, the
-// h_prev slice (hs).  Tokens past the end of the sequence re-read the last
+// Issues this wave's share of the direct loads of chunk `cc`: the K tile, the
+// V slice and gamma.  Tokens past the end of the sequence re-read the last
 // token: the prep kernel gives them beta = 0, which zeroes their columns of W
-// and M, and their outputs are never stored, so any finite value is harmless.
-template <int D, typename TIn, int RES, bool KQ, bool REST>
-__device__ __forceinline__ void carry_issue(unsigned char *__restrict__ kq, unsigned char *__restrict__ vs,
-                                            float *__restrict__ gs, unsigned char *__restrict__ hs, int cc,
-                                            int L, int H, int h, int64_t tokb, int col0,
-                                            const TIn *__restrict__ q, const TIn *__restrict__ k,
-                                            const TIn *__restrict__ v, const float *__restrict__ g,
-                                            int64_t cidb, const void *__restrict__ h_prev, int wave,
-                                            int lane) {
+// and M, so any finite value is harmless.
+template <int D, typename TIn>
+__device__ __forceinline__ void state_issue(unsigned char *__restrict__ ks, unsigned char *__restrict__ vs,
+                                            float *__restrict__ gs, int cc, int L, int H, int h, int64_t tokb,
+                                            int col0, const TIn *__restrict__ k, const TIn *__restrict__ v,
+                                            const float *__restrict__ g, int64_t cidb, int wave, int lane) {
     using G = CarryCfg<D, TIn>;
     constexpr int EPC = 16 / G::ES;   // elements per 16-byte chunk
     const int c0 = cc * C;
-    if constexpr (KQ) {
 #pragma unroll
-        for (int n = 0; n < G::KQ_INS / 4; ++n) {
-            const int I = 4 * n + wave;
-            const int tensor = I / (G::KQ_INS / 2);
-            const int base = (I % (G::KQ_INS / 2)) * 64, p = base + lane;
-            const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
-            const int tok = min(c0 + r, L - 1);
-            const TIn *src = (tensor ? q : k) + ((tokb + tok) * H + h) * D + c * EPC;
-            dma16_async(src, kq + tensor * G::TILE + base * 16);
-        }
+    for (int n = 0; n < G::K_INS / 4; ++n) {
+        const int base = (4 * n + wave) * 64, p = base + lane;
+        const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
+        const int tok = min(c0 + r, L - 1);
+        dma16_async(k + ((tokb + tok) * H + h) * D + c * EPC, ks + base * 16);
     }
-    if constexpr (REST) {
-        constexpr int LPR = G::VROWB / 16;   // lanes per V row
-        if (wave < G::V_INS) {
-            const int p = wave * 64 + lane, r = p / LPR, qq = p % LPR;
-            const int tok = min(c0 + r, L - 1);
-            dma16_async(v + ((tokb + tok) * H + h) * D + col0 + qq * EPC, vs + wave * 1024);
-        }
-        if constexpr (RES != 0) {
-            constexpr int HES = RES == 2 ? 2 : 4;
-            constexpr int HLPR = 16 * HES / 16, H_INS = C * 16 * HES / 1024;
-            if (wave < H_INS) {
-                const int p = wave * 64 + lane, r = p / HLPR, qq = p % HLPR;
-                const int tok = min(c0 + r, L - 1);
-                const int64_t off = (tokb + tok) * (int64_t)H * D + (int64_t)h * D + col0 + qq * (16 / HES);
-                dma16_async(static_cast<const unsigned char *>(h_prev) + off * HES, hs + wave * 1024);
-            }
-        }
-        if (wave == 3 && lane < C / 4) dma16_async(g + (cidb + cc) * C + 4 * lane, gs);
+    constexpr int LPR = G::VROWB / 16;   // lanes per V row
+    if (wave < G::V_INS) {
+        const int p = wave * 64 + lane, r = p / LPR, qq = p % LPR;
+        const int tok = min(c0 + r, L - 1);
+        dma16_async(v + ((tokb + tok) * H + h) * D + col0 + qq * EPC, vs + wave * 1024);
     }
+    if (wave == 3 && lane < C / 4) dma16_async(g + (cidb + cc) * C + 4 * lane, gs);
 }
 
-// K.S / Q.S A fragment (token row r, this lane's KW state rows) from a K/Q tile
+// K.S A fragment (token row r, this lane's KW state rows) from a K tile
 template <int D, typename TIn>
-__device__ __forceinline__ void kq_frag(const unsigned char *tile, int r, int wave, int lg,
-                                        TIn (&dst)[CarryCfg<D, TIn>::KW]) {
+__device__ __forceinline__ void k_frag(const unsigned char *tile, int r, int wave, int lg,
+                                       TIn (&dst)[CarryCfg<D, TIn>::KW]) {
     using G = CarryCfg<D, TIn>;
     constexpr int BYTES = G::KW * G::ES;
     const int b0 = (G::RW * wave + G::KW * lg) * G::ES;
@@ -497,11 +487,11 @@ __device__ __forceinline__ void kq_frag(const unsigned char *tile, int r, int wa
     if constexpr (BYTES >= 16) {
 #pragma unroll
         for (int part = 0; part < BYTES / 16; ++part) {
-            const uint4 u = *reinterpret_cast<const uint4 *>(row + kq_phys<D, TIn>(r, b0 / 16 + part) * 16);
+            const uint4 u = *reinterpret_cast<const uint4 *>(row + k_phys<D, TIn>(r, b0 / 16 + part) * 16);
             __builtin_memcpy(&dst[part * (16 / G::ES)], &u, 16);
         }
     } else {
-        const uint2 u = *reinterpret_cast<const uint2 *>(row + kq_phys<D, TIn>(r, b0 / 16) * 16 + b0 % 16);
+        const uint2 u = *reinterpret_cast<const uint2 *>(row + k_phys<D, TIn>(r, b0 / 16) * 16 + b0 % 16);
         __builtin_memcpy(&dst[0], &u, 8);
     }
 }
@@ -542,179 +532,37 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
     return mfma16x16x32(al, bh, c);
 }
 
-// number of global stores one lane issues per full chunk (the wait for the
-// next chunk's direct loads lets exactly these stay in flight)
-template <int RES, bool XN> struct CarryStores {
-    static constexpr int N = RES == 0 ? 4 : (XN ? 8 : 4);
-};
+// global stores one lane issues per chunk in the state pass (chunk-start
+// state hi and lo, E tile), after the next chunk's loads: the wait for those
+// loads lets exactly these stay in flight
+constexpr int STATE_STORES = 3;
 
-struct CarryLdsX {
-    f32x4 red[4][4][2][64];   // [source wave][token tile][K.S | Q.S][lane]
-    uint4 ex[4][64];          // [token tile][lane]: E hi (bf16x4) in .x .y, lo in .z .w
-};
-
-template <int D, typename TIn, int RES, bool XN, typename AfterKS, typename AfterB1, typename AfterB2>
-__device__ __forceinline__ void carry_chunk(
-    const WMFrags<D> &F, float (&Sv)[D / 64][4], int cc, int L, int H, int h, int64_t tokb, int col,
-    float rho_c, const unsigned char *__restrict__ kq, const unsigned char *__restrict__ vs,
-    const float *__restrict__ gs, const unsigned char *__restrict__ hs, CarryLdsX *__restrict__ Xp,
-    float *o, float *h_out, bf16 *x_next, AfterKS &&after_ks, AfterB1 &&after_b1, AfterB2 &&after_b2) {
-    CarryLdsX &X = *Xp;
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void k_scan_state(
+    const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc, const float *W,
+    const float *__restrict__ g, const float *__restrict__ s_init, float *__restrict__ s_final,
+    bf16 *__restrict__ sc_ws, uint4 *__restrict__ e_ws) {
+    // (W is not __restrict__: its loads must stay ordered with the wait_vmcnt
+    // fences, which a restrict pointer's loads may be moved across.)
     using G = CarryCfg<D, TIn>;
-    constexpr int NT = G::NT, KW = G::KW;
+    constexpr int NT = G::NT, RW = G::RW, KW = G::KW;
+    // every stage is an object of its own, so the compiler can tell the buffers
+    // a chunk reads from the ones the next chunk's direct loads write
+    __shared__ __attribute__((aligned(16))) unsigned char k0_s[G::TILE], k1_s[G::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[C * G::VROWB];
+    __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[C];
+    __shared__ __attribute__((aligned(16))) f32x4 red[4][4][64];   // [source wave][token tile][lane]
+    __shared__ __attribute__((aligned(16))) uint4 ex[4][64];       // [token tile][lane]: E hi | lo
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-
-    // B operand of K.S / Q.S: this lane's KW contiguous state rows, hi/lo
-    __bf16 sh[KW], sl[KW];
-    {
-        float sf[KW];
-#pragma unroll
-        for (int i = 0; i < KW; ++i) sf[i] = Sv[i / 4][i % 4];
-        split_bf16(sf, sh, sl);
-    }
-    f32x4 ks[4], qs[4];
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        TIn ak[KW], aq[KW];
-        kq_frag<D, TIn>(kq, 16 * tm + lr, wave, lg, ak);
-        kq_frag<D, TIn>(kq + G::TILE, 16 * tm + lr, wave, lg, aq);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        ks[tm] = mma_a<KW>(ak, sh, sl, z);
-        qs[tm] = mma_a<KW>(aq, sh, sl, z);
-    }
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
-        if (tm != wave) {
-            X.red[wave][tm][0][lane] = ks[tm];
-            X.red[wave][tm][1][lane] = qs[tm];
-        }
-    after_ks();      // part of the next chunk's loads, spread over the chunk so that
-                     // issuing them does not stall the wave on a full memory pipeline
-    lds_barrier();   // (B1) partials visible; every wave done reading this chunk's K and Q
-    after_b1();      // single-buffered K/Q: the next chunk's tiles may now be loaded
-    // own token tile: sum of the four partials (wave-uniform selects keep tiles in registers)
-    f32x4 kt = ks[0], qt = qs[0];
-#pragma unroll
-    for (int tm = 1; tm < 4; ++tm)
-        if (tm == wave) { kt = ks[tm]; qt = qs[tm]; }
-#pragma unroll
-    for (int src = 0; src < 4; ++src)
-        if (src != wave) {
-            const f32x4 a = X.red[src][wave][0][lane], b = X.red[src][wave][1][lane];
-            kt += a;
-            qt += b;
-        }
-    // E = V - diag(gamma) K S for tokens 16 wave + 4 lg + j
-    float e[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * wave + 4 * lg + j;
-        float vv;
-        if constexpr (G::ES == 2) vv = (float)reinterpret_cast<const bf16 *>(vs)[r * 16 + lr];
-        else vv = reinterpret_cast<const float *>(vs)[r * 16 + lr];
-        e[j] = vv - gs[r] * kt[j];
-    }
-    {
-        __bf16 eh[4], el[4];
-        split_bf16(e, eh, el);
-        uint4 u;
-        __builtin_memcpy(&u.x, eh, 8);
-        __builtin_memcpy(&u.z, el, 8);
-        X.ex[wave][lane] = u;
-    }
-    lds_barrier();   // (B2) every E tile visible
-    after_b2();
-    // E as the B operand: k-step s covers the token tiles 2s and 2s+1
-    bf16x8 ebh[2], ebl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const uint4 a = X.ex[2 * s][lane], b = X.ex[2 * s + 1][lane];
-        uint4 hi = make_uint4(a.x, a.y, b.x, b.y), lo = make_uint4(a.z, a.w, b.z, b.w);
-        __builtin_memcpy(&ebh[s], &hi, 16);
-        __builtin_memcpy(&ebl[s], &lo, 16);
-    }
-    const float gC = gs[C - 1];
-    // S' = gamma_C S + W E (this wave's rows)
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        f32x4 we = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) we = mma_hl(F.wh[tt][s], F.wl[tt][s], ebh[s], ebl[s], we);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + we[j];
-    }
-    // O = diag(gamma) Q S + M E for tokens 16 wave + 4 lg + j
-    f32x4 me = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) me = mma_hl(F.mh[s], F.ml[s], ebh[s], ebl[s], me);
-    // Outputs through buffer stores whose range ends at the last token of the
-    // sequence: rows past it are dropped by the hardware, so every lane issues
-    // exactly CarryStores::N stores per chunk, with no branch around them (the
-    // wait for the next chunk's loads relies on that count).
-    const int d = H * D;
-    const int nvalid = min(C, L - cc * C);
-    const int64_t row0 = tokb + (int64_t)cc * C;
-    if constexpr (RES == 0) {
-        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(o + row0 * d, nvalid * d * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * wave + 4 * lg + j;
-            const float ov = gs[r] * qt[j] + me[j];
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, ov), ro, (r * d + h * D + col) * 4, 0, 0);
-        }
-    } else {
-        const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(h_out + row0 * d, nvalid * d * 4);
-        __amdgpu_buffer_rsrc_t rx;
-        if constexpr (XN) rx = buffer_rsrc(x_next + row0 * d, nvalid * d * 2);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * wave + 4 * lg + j;
-            const float ov = gs[r] * qt[j] + me[j];
-            float hp;
-            if constexpr (RES == 2) hp = (float)reinterpret_cast<const bf16 *>(hs)[r * 16 + lr];
-            else hp = reinterpret_cast<const float *>(hs)[r * 16 + lr];
-            const float hn = ov + rho_c * hp;
-            const int e = r * d + h * D + col;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, hn), rh, e * 4, 0, 0);
-            if constexpr (XN)
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)hn), rx, e * 2, 0, 0);
-        }
-    }
-}
-
-template <int D, typename TIn, int RES, bool XN>
-__global__ __launch_bounds__(256) void k_scan_carry(
-    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H,
-    int Nc, const float *W, const float *M, const float *__restrict__ g,
-    const float *__restrict__ s_init, float *__restrict__ s_final, float *__restrict__ o,
-    const void *h_prev, const float *__restrict__ rho, float *h_out, bf16 *x_next) {
-    // (W and M are not __restrict__: their loads must stay ordered with the
-    // wait_vmcnt fences, which a restrict pointer's loads may be moved across.)
-    using G = CarryCfg<D, TIn>;
-    constexpr int NT = G::NT, RW = G::RW;
-    constexpr int HB = RES == 0 ? 16 : C * 16 * (RES == 2 ? 2 : 4);
-    constexpr int NST = CarryStores<RES, XN>::N;
-    // every stage is an object of its own, so the compiler can tell the buffers
-    // a chunk reads from the ones the next chunk's direct loads write
-    __shared__ __attribute__((aligned(16))) unsigned char kq0_s[2 * G::TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char kq1_s[G::KQ_STAGES == 2 ? 2 * G::TILE : 16];
-    __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[C * G::VROWB];
-    __shared__ __attribute__((aligned(16))) unsigned char h0_s[HB], h1_s[HB];
-    __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[C];
-    __shared__ CarryLdsX X;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lg = lane >> 4;
     // heads run along x so that the D/16 column slices of one head, which read the
-    // same K, Q, W and M, get workgroup ids that are congruent mod 8 and share an XCD
+    // same K and W, get workgroup ids that are congruent mod 8 and share an XCD
     const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
-    const int col0 = slice * 16, col = col0 + (lane & 15);
+    const int col0 = slice * 16, col = col0 + lr;
     const int64_t tokb = (int64_t)b * L;
     const int64_t cidb = ((int64_t)b * H + h) * Nc;
-    const float rho_c = RES ? rho[h * D + col] : 0.f;
 
     // state slice: Sv[tt][j] = S[RW wave + 4 NT lg + 4 tt + j][col]
     float Sv[NT][4];
@@ -728,46 +576,96 @@ __global__ __launch_bounds__(256) void k_scan_carry(
     // compiler's wait for these registers lands in the loop body (every chunk).
     wait_vmcnt<0>();
 
-    WMFrags<D> fa, fb;
-    carry_issue<D, TIn, RES, true, true>(kq0_s, v0_s, g0_s, h0_s, 0, L, H, h, tokb, col0, q, k, v, g, cidb,
-                                         h_prev, wave, lane);
-    load_wm<D>(fa, W, M, cidb, wave, lane);
-    wait_vmcnt<0>();   // chunk 0's loads (the waits in the loop assume only stores are older)
+    WFrags<D> fa, fb;
+    state_issue<D, TIn>(k0_s, v0_s, g0_s, 0, L, H, h, tokb, col0, k, v, g, cidb, wave, lane);
+    load_w<D>(fa, W, cidb, wave, lane);
+    wait_vmcnt<0>();   // chunk 0's loads (the waits in the loop assume only stores are younger)
 
-    // One chunk step on LDS stage ST (= cc mod 2): wait for chunk cc's loads,
-    // issue chunk cc+1's into the other stage, compute cc.  Two steps per loop
-    // iteration so stages are compile-time constants and the W/M register sets
-    // swap roles without copies.
-    auto step = [&](auto stc, int cc, const WMFrags<D> &cur, WMFrags<D> &nxt) __attribute__((always_inline)) {
+    // One chunk step on LDS stage ST (= cc mod 2).  Two steps per loop iteration
+    // so stages are compile-time constants and the W register sets swap roles
+    // without copies.
+    auto step = [&](auto stc, int cc, const WFrags<D> &cur, WFrags<D> &nxt) __attribute__((always_inline)) {
         constexpr int ST = decltype(stc)::value;
-        unsigned char *kq_cur = (G::KQ_STAGES == 1 || ST == 0) ? kq0_s : kq1_s;
-        unsigned char *kq_nxt = (G::KQ_STAGES == 1 || ST == 1) ? kq0_s : kq1_s;
+        unsigned char *k_cur = ST == 0 ? k0_s : k1_s, *k_nxt = ST == 0 ? k1_s : k0_s;
         unsigned char *v_cur = ST == 0 ? v0_s : v1_s, *v_nxt = ST == 0 ? v1_s : v0_s;
-        unsigned char *h_cur = ST == 0 ? h0_s : h1_s, *h_nxt = ST == 0 ? h1_s : h0_s;
         float *g_cur = ST == 0 ? g0_s : g1_s, *g_nxt = ST == 0 ? g1_s : g0_s;
-        wait_vmcnt<NST>();   // only the previous chunk's stores may remain in flight
-        lds_barrier();            // (B0) chunk cc's direct loads of every wave have landed
+        wait_vmcnt<STATE_STORES>();   // only the previous chunk's stores may remain in flight
+        lds_barrier();                // (B0) chunk cc's direct loads of every wave have landed
         const bool more = cc + 1 < Nc;
-        if constexpr (G::KQ_STAGES == 2)
-            if (more)
-                carry_issue<D, TIn, RES, true, false>(kq_nxt, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb, col0, q,
-                                                      k, v, g, cidb, h_prev, wave, lane);
-        carry_chunk<D, TIn, RES, XN>(
-            cur, Sv, cc, L, H, h, tokb, col, rho_c, kq_cur, v_cur, g_cur, h_cur, &X, o, h_out, x_next,
-            [&]() __attribute__((always_inline)) {
-                if (more) load_wm<D>(nxt, W, M, cidb + cc + 1, wave, lane);
-            },
-            [&]() __attribute__((always_inline)) {
-                if constexpr (G::KQ_STAGES == 1)
-                    if (more)
-                        carry_issue<D, TIn, RES, true, false>(kq0_s, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb,
-                                                              col0, q, k, v, g, cidb, h_prev, wave, lane);
-            },
-            [&]() __attribute__((always_inline)) {
-                if (more)
-                    carry_issue<D, TIn, RES, false, true>(kq_nxt, v_nxt, g_nxt, h_nxt, cc + 1, L, H, h, tokb,
-                                                          col0, q, k, v, g, cidb, h_prev, wave, lane);
-            });
+        const int64_t cid = cidb + cc;
+        if (more) {
+            state_issue<D, TIn>(k_nxt, v_nxt, g_nxt, cc + 1, L, H, h, tokb, col0, k, v, g, cidb, wave, lane);
+            load_w<D>(nxt, W, cid + 1, wave, lane);   // before this chunk's stores, see STATE_STORES
+        }
+        // chunk-start state as the B operand of K.S (and of Q.S in the output pass)
+        __bf16 sh[KW], sl[KW];
+        {
+            float sf[KW];
+#pragma unroll
+            for (int i = 0; i < KW; ++i) sf[i] = Sv[i / 4][i % 4];
+            split_bf16(sf, sh, sl);
+            bf16 *dst = sc_ws + cid * G::SC_ELEMS + (((int64_t)slice * 4 + wave) * 2 * 64 + lane) * KW;
+            __builtin_memcpy(dst, sh, 2 * KW);
+            __builtin_memcpy(dst + 64 * KW, sl, 2 * KW);
+        }
+        f32x4 ks[4];
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            TIn ak[KW];
+            k_frag<D, TIn>(k_cur, 16 * tm + lr, wave, lg, ak);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            ks[tm] = mma_a<KW>(ak, sh, sl, z);
+        }
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+            if (tm != wave) red[wave][tm][lane] = ks[tm];
+        lds_barrier();   // (B1) partials visible
+        f32x4 kt = ks[0];
+#pragma unroll
+        for (int tm = 1; tm < 4; ++tm)
+            if (tm == wave) kt = ks[tm];
+#pragma unroll
+        for (int src = 0; src < 4; ++src)
+            if (src != wave) kt += red[src][wave][lane];
+        // E = V - diag(gamma) K S for tokens 16 wave + 4 lg + j
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * wave + 4 * lg + j;
+            float vv;
+            if constexpr (G::ES == 2) vv = (float)reinterpret_cast<const bf16 *>(v_cur)[r * 16 + lr];
+            else vv = reinterpret_cast<const float *>(v_cur)[r * 16 + lr];
+            e[j] = vv - g_cur[r] * kt[j];
+        }
+        {
+            __bf16 eh[4], el[4];
+            split_bf16(e, eh, el);
+            uint4 u;
+            __builtin_memcpy(&u.x, eh, 8);
+            __builtin_memcpy(&u.z, el, 8);
+            ex[wave][lane] = u;
+            e_ws[(cid * G::NSL + slice) * 4 * 64 + wave * 64 + lane] = u;
+        }
+        lds_barrier();   // (B2) every E tile visible
+        // E as the B operand: k-step s covers the token tiles 2s and 2s+1
+        bf16x8 ebh[2], ebl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 a = ex[2 * s][lane], c = ex[2 * s + 1][lane];
+            uint4 hi = make_uint4(a.x, a.y, c.x, c.y), lo = make_uint4(a.z, a.w, c.z, c.w);
+            __builtin_memcpy(&ebh[s], &hi, 16);
+            __builtin_memcpy(&ebl[s], &lo, 16);
+        }
+        const float gC = g_cur[C - 1];
+        // S' = gamma_C S + W E (this wave's rows)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 we = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) we = mma_hl(cur.wh[tt][s], cur.wl[tt][s], ebh[s], ebl[s], we);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + we[j];
+        }
     };
     for (int cc = 0; cc < Nc; cc += 2) {
         step(std::integral_constant<int, 0>(), cc, fa, fb);
@@ -779,6 +677,136 @@ __global__ __launch_bounds__(256) void k_scan_carry(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 s_final[sbase + (int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] = Sv[tt][j];
+    }
+}
+
+// Output pass.  The Q tile, the M fragments, gamma and the h_prev tile come
+// into LDS with coalesced 16-byte loads.  Wave w handles the column slices
+// [w SPW, (w+1) SPW) for all 64 tokens of the chunk: Q.S_c (B operand: the
+// stored chunk-start state, k-step ks = the state rows of state-pass wave ks)
+// and M.E (B operand: the stored E tiles), both split-bf16.  The results go
+// back through the LDS tile, which is then written out as whole 16-byte runs
+// of the output rows (fp32, plus the bf16 copy for the next loop).
+template <int D, typename TIn, int RES> struct OutCfg {
+    static constexpr int QROW = D + 16 / (int)sizeof(TIn);   // padded Q row (elements)
+    static constexpr int OROW = D + 4;                        // padded output row (floats)
+};
+
+template <int D, typename TIn, int RES, bool XN>
+__global__ __launch_bounds__(256) void k_scan_out(
+    const TIn *__restrict__ q, int L, int H, int Nc, const float *__restrict__ M,
+    const float *__restrict__ g, const bf16 *__restrict__ sc_ws, const uint4 *__restrict__ e_ws,
+    float *__restrict__ o, const void *h_prev, const float *__restrict__ rho, float *h_out,
+    bf16 *x_next) {
+    using G = CarryCfg<D, TIn>;
+    using OC = OutCfg<D, TIn, RES>;
+    constexpr int KW = G::KW, NKS = 4;                   // Q.S k-steps: one per state-pass wave
+    constexpr int SPW = G::NSL / 4;                      // slices per wave
+    __shared__ __attribute__((aligned(16))) TIn Qs[C * OC::QROW];
+    __shared__ __attribute__((aligned(16))) bf16x8 Ms[4 * 2 * 2 * 64];   // [tile][s][part][lane]
+    __shared__ __attribute__((aligned(16))) float Os[C * OC::OROW];      // h_prev in, result out
+    __shared__ float gs[C];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c0 = chunk * C, nvalid = min(C, L - c0);
+    const int64_t tokb = (int64_t)b * L;
+    const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
+    const int d = H * D;
+
+    // (1) cooperative loads (rows past the end of the sequence are left unset:
+    // they only feed results that are never stored)
+    {
+        constexpr int EPC = 16 / (int)sizeof(TIn), CPR = D / EPC;
+        for (int idx = t; idx < nvalid * CPR; idx += 256) {
+            const int r = idx / CPR, c = idx % CPR;
+            *reinterpret_cast<uint4 *>(Qs + r * OC::QROW + c * EPC) =
+                *reinterpret_cast<const uint4 *>(q + ((tokb + c0 + r) * H + h) * D + c * EPC);
+        }
+        const uint4 *Mg = reinterpret_cast<const uint4 *>(M + cid * C * C);
+        for (int idx = t; idx < 4 * 2 * 2 * 64; idx += 256) reinterpret_cast<uint4 *>(Ms)[idx] = Mg[idx];
+        if (t < C) gs[t] = g[cid * C + t];
+        if constexpr (RES != 0) {
+            constexpr int HEPC = RES == 2 ? 8 : 4, HCPR = D / HEPC;   // elements per 16 bytes
+            for (int idx = t; idx < nvalid * HCPR; idx += 256) {
+                const int r = idx / HCPR, c = idx % HCPR;
+                const int64_t off = (tokb + c0 + r) * (int64_t)d + (int64_t)h * D + c * HEPC;
+                float *dst = Os + r * OC::OROW + c * HEPC;
+                if constexpr (RES == 2) {
+                    const bf16x8 u = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(h_prev) + off);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) dst[i] = (float)u[i];
+                } else {
+                    *reinterpret_cast<float4 *>(dst) = *reinterpret_cast<const float4 *>(static_cast<const float *>(h_prev) + off);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int si = 0; si < SPW; ++si) {
+        const int slice = wave * SPW + si, col = slice * 16 + lr;
+        // chunk-start state and E B fragments (lane-contiguous, straight from the workspace)
+        __bf16 sh[NKS][KW], sl[NKS][KW];
+        const bf16 *scs = sc_ws + cid * G::SC_ELEMS + (int64_t)slice * 4 * 2 * 64 * KW + lane * KW;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            __builtin_memcpy(sh[ks], scs + (int64_t)(ks * 2 + 0) * 64 * KW, 2 * KW);
+            __builtin_memcpy(sl[ks], scs + (int64_t)(ks * 2 + 1) * 64 * KW, 2 * KW);
+        }
+        bf16x8 ebh[2], ebl[2];
+        const uint4 *es = e_ws + (cid * G::NSL + slice) * 4 * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 a = es[(2 * s) * 64], c = es[(2 * s + 1) * 64];
+            uint4 hi = make_uint4(a.x, a.y, c.x, c.y), lo = make_uint4(a.z, a.w, c.z, c.w);
+            __builtin_memcpy(&ebh[s], &hi, 16);
+            __builtin_memcpy(&ebl[s], &lo, 16);
+        }
+        const float rho_c = RES ? rho[h * D + col] : 0.f;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            f32x4 qs = {0.f, 0.f, 0.f, 0.f}, me = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                TIn qa[KW];
+                __builtin_memcpy(qa, Qs + (16 * tm + lr) * OC::QROW + G::RW * ks + KW * lg, KW * sizeof(TIn));
+                qs = mma_a<KW>(qa, sh[ks], sl[ks], qs);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                me = mma_hl(Ms[((tm * 2 + s) * 2 + 0) * 64 + lane], Ms[((tm * 2 + s) * 2 + 1) * 64 + lane],
+                            ebh[s], ebl[s], me);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * tm + 4 * lg + j;
+                const float ov = gs[r] * qs[j] + me[j];
+                float *cell = Os + r * OC::OROW + col;
+                if constexpr (RES == 0) *cell = ov;
+                else *cell = ov + rho_c * *cell;
+            }
+        }
+    }
+    __syncthreads();
+    // (3) whole rows out: fp32 result (o or h_out) and the bf16 copy
+    for (int idx = t; idx < nvalid * (D / 4); idx += 256) {
+        const int r = idx / (D / 4), c = idx % (D / 4);
+        const float4 v4 = *reinterpret_cast<const float4 *>(Os + r * OC::OROW + 4 * c);
+        const int64_t row = tokb + c0 + r;
+        if constexpr (RES == 0) {
+            *reinterpret_cast<float4 *>(o + (row * H + h) * D + 4 * c) = v4;
+        } else {
+            const int64_t hi = row * d + (int64_t)h * D + 4 * c;
+            *reinterpret_cast<float4 *>(h_out + hi) = v4;
+            if constexpr (XN) {
+                bf16x4 x4;
+                x4[0] = (bf16)v4.x; x4[1] = (bf16)v4.y; x4[2] = (bf16)v4.z; x4[3] = (bf16)v4.w;
+                *reinterpret_cast<bf16x4 *>(x_next + hi) = x4;
+            }
+        }
     }
 }
 
@@ -800,30 +828,57 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
     return hipGetLastError();
 }
 
-hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k,
-                             const void *v, ChunkWs ws, const float *s_init, float *s_final,
-                             CarryOut out, hipStream_t s) {
+size_t carry_ws_bytes(bool f32, int D, int64_t chunk_heads) {
+    int64_t sc = 0, e = 0;
+    if (f32) {
+        if (D == 128) { sc = CarryCfg<128, float>::SC_ELEMS; e = CarryCfg<128, float>::E_BYTES; }
+        else { sc = CarryCfg<64, float>::SC_ELEMS; e = CarryCfg<64, float>::E_BYTES; }
+    } else {
+        if (D == 128) { sc = CarryCfg<128, bf16>::SC_ELEMS; e = CarryCfg<128, bf16>::E_BYTES; }
+        else { sc = CarryCfg<64, bf16>::SC_ELEMS; e = CarryCfg<64, bf16>::E_BYTES; }
+    }
+    return (size_t)chunk_heads * (size_t)(sc * 2 + e);
+}
+
+hipError_t launch_scan_state(bool f32, int B, int L, int H, int D, const void *k, const void *v, ChunkWs ws,
+                             const float *s_init, float *s_final, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     dim3 grid(H, D / 16, B);
+#define STATE(DD, T)                                                                               \
+    launch_kernel((k_scan_state<DD, T>), grid, dim3(256), 0, s, (const T *)k, (const T *)v, L, H, Nc, \
+                  (const float *)ws.W, (const float *)ws.g, s_init, s_final, ws.sc, ws.e)
+    if (f32) {
+        if (D == 128) STATE(128, float); else STATE(64, float);
+    } else {
+        if (D == 128) STATE(128, bf16); else STATE(64, bf16);
+    }
+#undef STATE
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_out(bool f32, int B, int L, int H, int D, const void *q, ChunkWs ws, CarryOut out,
+                           hipStream_t s) {
+    const int Nc = (L + C - 1) / C;
+    dim3 grid(Nc, H, B);
     const int res = out.h_out == nullptr ? 0 : (out.h_prev_bf16 ? 2 : 1);
     const bool xn = out.h_out != nullptr && out.x_next != nullptr;
-#define CARRY(DD, T, R, X)                                                                         \
-    launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,  \
-                  (const T *)v, L, H, Nc, ws.W, ws.M, ws.g, s_init, s_final, out.o, out.h_prev,    \
-                  out.rho, out.h_out, out.x_next)
-#define CARRY_R(DD, T)                                                                             \
+#define OUT(DD, T, R, X)                                                                           \
+    launch_kernel((k_scan_out<DD, T, R, X>), grid, dim3(256), 0, s, (const T *)q, L, H, Nc,        \
+                  (const float *)ws.M, (const float *)ws.g, (const bf16 *)ws.sc, (const uint4 *)ws.e, \
+                  out.o, out.h_prev, out.rho, out.h_out, out.x_next)
+#define OUT_R(DD, T)                                                                               \
     do {                                                                                           \
-        if (res == 0) CARRY(DD, T, 0, false);                                                      \
-        else if (res == 1) { if (xn) CARRY(DD, T, 1, true); else CARRY(DD, T, 1, false); }         \
-        else { if (xn) CARRY(DD, T, 2, true); else CARRY(DD, T, 2, false); }                       \
+        if (res == 0) OUT(DD, T, 0, false);                                                        \
+        else if (res == 1) { if (xn) OUT(DD, T, 1, true); else OUT(DD, T, 1, false); }             \
+        else { if (xn) OUT(DD, T, 2, true); else OUT(DD, T, 2, false); }                           \
     } while (0)
     if (f32) {
-        if (D == 128) CARRY_R(128, float); else CARRY_R(64, float);
+        if (D == 128) OUT_R(128, float); else OUT_R(64, float);
     } else {
-        if (D == 128) CARRY_R(128, bf16); else CARRY_R(64, bf16);
+        if (D == 128) OUT_R(128, bf16); else OUT_R(64, bf16);
     }
-#undef CARRY_R
-#undef CARRY
+#undef OUT_R
+#undef OUT
     return hipGetLastError();
 }
 

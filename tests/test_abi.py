@@ -83,19 +83,21 @@ def test_decode_needs_single_token():
 
 
 def test_workspace_sizes():
-    """Prefill workspace: bf16 q/k/v, fp32 gates, per-chunk W [D x 64], M [64 x 64], gamma [64] and the bf16
-    GEMM operand for loops 2..T; every region rounded up to 256 bytes."""
+    """Prefill workspace: bf16 q/k/v, fp32 gates, per-chunk W [D x 64], M [64 x 64], gamma [64], the chunk-start
+    state [D x D] and E [64 x D] (both as bf16 hi/lo pairs, 4 bytes per element), and the bf16 GEMM operand
+    for loops 2..T; every region rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
     B, L, H, D, T = 2, 130, 3, 128, 4
     desc = gl.make_desc(B, L, H, D, D, T=T)
     st, n = _ws_status(desc)
     assert st == 0
     tok, Nc = B * L, (L + 63) // 64
-    exp = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2)
-    exp += up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+    chunks = (up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+              + up(B * H * Nc * (D * D + 64 * D) * 4))
+    exp = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2) + chunks
     assert n == exp
     st, n = _ws_status(desc, gl.GDN_OP_SCAN_PREFILL)
-    assert st == 0 and n == up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+    assert st == 0 and n == chunks
     st, n = _ws_status(gl.make_desc(64, 1, 16, 128, 128), gl.GDN_OP_SCAN_DECODE)
     assert st == 0 and n == 0
 
