@@ -182,7 +182,10 @@ const char *gdn_version(void);
 
 /* Stages that a timer can bracket. */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
-       GDN_STAGE_DECODE = 3, GDN_STAGE_SCAN_OUT = 4 };
+       GDN_STAGE_DECODE = 3, GDN_STAGE_SCAN_OUT = 4, GDN_STAGE_GATES = 5 };
+/* GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
+ * more tokens the gates alpha/beta leave the GEMM for a launch of their own,
+ * timed as GDN_STAGE_GATES (shorter inputs compute them inside the GEMM). */
 
 /* While a timer is attached, every launch of its stage carries a pair of HIP
  * events on its dispatch (hipExtLaunchKernel start/stop events), so each pair

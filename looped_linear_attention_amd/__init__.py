@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
     "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
-    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_SCAN_OUT", "GdnError", "gdn_desc", "make_desc", "lib_path",
+    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_SCAN_OUT", "GDN_STAGE_GATES", "GdnError", "gdn_desc", "make_desc", "lib_path",
     "load", "EXPORTED", "workspace",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
@@ -32,7 +32,7 @@ __all__ = [
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT = range(5)
-GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_SCAN_OUT = range(5)
+GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_SCAN_OUT, GDN_STAGE_GATES = range(6)
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [

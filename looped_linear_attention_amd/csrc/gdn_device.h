@@ -101,6 +101,14 @@ __device__ __forceinline__ void dma16_async(const void *g, void *wave_base) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// The same direct load with a wave-uniform base address (scalar registers)
+// and a per-lane 32-bit byte offset: one vector register per load instead of
+// a 64-bit address.
+__device__ __forceinline__ void dma16_async_s(const void *sbase, unsigned voff, void *wave_base) {
+    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(lds_void *)wave_base);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0;
 // the gfx9-family format word).  Stores whose byte range does not lie inside
 // [0, bytes) are dropped by the hardware, so a tail can be masked without a

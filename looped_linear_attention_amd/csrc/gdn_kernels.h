@@ -39,10 +39,15 @@ hipError_t launch_pack_weights(bool f32, int d, int H, int D, const void *Wq, co
                                hipStream_t s);
 
 // X[M, d] x Wpack^T with the fused per-head epilogue (L2 norm of q and k,
-// gates alpha/beta, dtype conversion of q/k/v).
+// gates alpha/beta, dtype conversion of q/k/v).  When project_separate_gates
+// is true, launch_project writes q, k, v only and launch_gates (an independent
+// launch: both read x) writes alpha and beta.
+bool project_separate_gates(bool f32, int M);
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
                           float eps, hipStream_t s);
+hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
+                        float *beta, float alpha_lo, hipStream_t s);
 
 // Chunk preparation: per (b, h, chunk) decay products, the UT-transform
 // inverse and the derived matrices W [D x 64], M [64 x 64], gamma [64].

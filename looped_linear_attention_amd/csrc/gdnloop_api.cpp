@@ -134,9 +134,9 @@ struct gdn_timer {
 
 namespace {
 
-constexpr int N_STAGES = GDN_STAGE_SCAN_OUT + 1;
+constexpr int N_STAGES = GDN_STAGE_GATES + 1;
 thread_local LaunchEvents t_launch_events{nullptr, nullptr};
-gdn_timer *g_timers[N_STAGES] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+gdn_timer *g_timers[N_STAGES] = {};
 
 // Runs `launch` (exactly one kernel launch) with the stage timer's next event
 // pair armed, when a timer for `stage` is attached.
@@ -149,6 +149,18 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
     hipError_t e = launch();
     launch_events() = LaunchEvents{nullptr, nullptr};
     if (e == hipSuccess) tm->used++;
+    return e;
+}
+
+// The projection of M tokens: the GEMM launch, plus the gate launch when the
+// GEMM leaves the gates to it.
+hipError_t project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
+                   void *v, float *al, float *be, float alpha_lo, float eps, hipStream_t s) {
+    hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
+        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, s);
+    });
+    if (e == hipSuccess && project_separate_gates(f32, M))
+        e = timed(GDN_STAGE_GATES, s, [&] { return launch_gates(M, d, H, D, x, Wpack, al, be, alpha_lo, s); });
     return e;
 }
 
@@ -212,10 +224,8 @@ gdn_status gdn_project(const gdn_desc *desc, const void *x, const void *Wpack, v
     REQUIRE_PTR(alpha); REQUIRE_PTR(beta);
     const hipStream_t s = (hipStream_t)stream;
     const int M = desc->B * desc->L;
-    hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
-        return launch_project(desc->act == GDN_F32, M, desc->d, desc->H, desc->dk, x, Wpack, q, k,
-                              v, alpha, beta, desc->alpha_lo, desc->norm_eps, s);
-    });
+    hipError_t e = project(desc->act == GDN_F32, M, desc->d, desc->H, desc->dk, x, Wpack, q, k, v, alpha,
+                           beta, desc->alpha_lo, desc->norm_eps, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "projection launch");
 }
 
@@ -301,10 +311,8 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
     for (int tau = 0; tau < desc->T; ++tau) {
         const bool last = tau == desc->T - 1;
         float *hdst = h_loops ? h_loops + tau * tokd : h_out;  // h^(tau+1), in place over h_out
-        hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
-            return launch_project(f32, M, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                                  desc->norm_eps, s);
-        });
+        hipError_t e = project(f32, M, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
+                               desc->norm_eps, s);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         CarryOut out{nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, hdst,
                      (!f32 && !last) ? xbuf : nullptr};
@@ -346,10 +354,8 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
     bool hprev_bf16 = !f32;
     for (int tau = 0; tau < desc->T; ++tau) {
         const bool last = tau == desc->T - 1;
-        hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
-            return launch_project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                                  desc->norm_eps, s);
-        });
+        hipError_t e = project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
+                               desc->norm_eps, s);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         e = timed(GDN_STAGE_DECODE, s, [&] {
             return launch_decode(f32, N, desc->H, D, q, k, v, al, be, states + tau * state_elems,
@@ -367,7 +373,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_SCAN_OUT || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_GATES || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

@@ -8,10 +8,14 @@
 // caption: gating plus the delta rule): alpha = alpha_lo + (1 - alpha_lo)
 // sigmoid(-a), beta = sigmoid(b), a = x.wa, b = x.wb.
 //
-// bf16 path: 256x128x64 block tiles, 4 waves of 128x64 (4x2 MFMA 32x32x16
-// tiles), double-buffered LDS with a 16-byte XOR swizzle, fp32 accumulation.
-// The packed weight puts each head's q|k|v rows in whole 128-row tiles, so one
-// output tile always holds complete head sections for the normalisation.
+// bf16 path, long inputs (>= 1024 tokens): k_proj_wide, 256 tokens x 384
+// packed columns (one head's q|k|v for D = 128) per workgroup, eight waves of
+// 128 x 96, and k_gates for the 2H gate columns.  Short inputs (decode steps):
+// k_proj_bf16, 256 x 128 tiles of four 128 x 64 waves with the gate columns as
+// one more tile.  Both stage operands through LDS with XOR-swizzled direct
+// loads and accumulate in fp32.  The packed weight puts each head's q|k|v rows
+// in whole 128-row sections, so every output tile holds complete head
+// sections for the normalisation.
 // fp32 path: a plain VALU tiled GEMM with the same epilogue.
 #include <type_traits>
 
@@ -294,6 +298,296 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// wide bf16 MFMA GEMM for long inputs
+// ---------------------------------------------------------------------------
+// Block tile 384 packed columns (q|k|v of one head for D = 128, of two heads for
+// D = 64) x 256 tokens x 32 channels.  Eight waves (two per SIMD) own 96
+// columns x 128 tokens each as 3 x 4 MFMA 32x32x16 tiles (192 fp32 accumulators
+// per lane).  Per flop this tile moves 45% fewer bytes from L2 into the CU than
+// a 256 x 128 tile, and each wave reads 22% fewer LDS bytes than with 128 x 64
+// wave tiles; the second wave on each SIMD covers the other's LDS latency.
+// The product is formed transposed (Wp rows as the A operand, tokens as B), so
+// that a lane holds, for one token, runs of four consecutive output columns:
+// the per-head norms then sum mostly inside the lane, and results leave as
+// 8-byte pieces of output rows through a staging tile in LDS.
+// With one head per column tile, a sequence of 4096 tokens and 16 heads is
+// exactly 256 tiles, one per CU.  The gate columns run in k_gates.
+constexpr int WM = 256, WN = 384, WK = 32, WSTAGES = 3;
+constexpr int WA = WM * WK, WB = WN * WK, WSTAGE = WA + WB;   // bf16 elements per stage
+constexpr int WOUT_LD = WN + 4;   // bf16 row stride of the output staging tile (776 bytes)
+constexpr int WCOLS = 96;         // columns per wave
+constexpr int W_LDS_MAIN = WSTAGES * WSTAGE * 2;
+constexpr int W_LDS_EPI = 64 * WOUT_LD * 2 + 4 * 6 * WM * 4;
+static_assert(W_LDS_EPI <= W_LDS_MAIN, "epilogue buffers reuse the operand stages");
+
+// 16-byte chunk `ch` (0..3) of row `r` of a 32-wide bf16 tile (64-byte rows),
+// XOR-swizzled by r / 4: 16 consecutive rows reading the same chunk then hit 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int wswz(int r, int ch) { return r * WK + ((ch ^ ((r >> 2) & 3)) << 3); }
+
+// Per-lane source offsets (bytes, relative to the k-block's first channel) of
+// the five direct loads a wave issues per k-block: loads 0..1 fill the token
+// tile (1024 16-byte chunks; wave w's load i covers LDS chunks [(8 i + w) 64,
+// +64)), loads 2..4 the column tile (1536 chunks).  LDS chunk p holds row p / 4,
+// logical chunk (p % 4) ^ ((row / 4) % 4).  Token rows past M re-read the last
+// token and column rows past the packed q|k|v rows re-read the last used one;
+// their results are never stored.
+struct WideSrc {
+    unsigned off[5];
+};
+__device__ __forceinline__ WideSrc wide_src(int lane, int wave, int m0, int M, int K, int n_rows) {
+    WideSrc s;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int base = (8 * (i < 2 ? i : i - 2) + wave) * 64, p = base + lane;
+        const int r = p >> 2, ch = (p & 3) ^ ((r >> 2) & 3);
+        const int row = i < 2 ? min(m0 + r, M - 1) - m0 : min(r, n_rows - 1);
+        s.off[i] = (unsigned)((row * K + ch * 8) * 2);
+    }
+    return s;
+}
+__device__ __forceinline__ void wide_issue(bf16 *stage, const WideSrc &src, const bf16 *xk, const bf16 *wk,
+                                           int wave) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        if (i < 2) dma16_async_s(xk, src.off[i], stage + (8 * i + wave) * 64 * 8);
+        else dma16_async_s(wk, src.off[i], stage + WA + (8 * (i - 2) + wave) * 64 * 8);
+    }
+}
+
+// Fragments of one k-step: 3 column tiles (A operand) and 4 token tiles (B).
+struct WFr {
+    bf16x8 a[3], b[4];
+};
+__device__ __forceinline__ void wide_read(WFr &F, const bf16 *stage, int ks, int lane, int wt, int wf) {
+    const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int ft = 0; ft < 3; ++ft)
+        F.a[ft] = *reinterpret_cast<const bf16x8 *>(stage + WA + wswz(wf * WCOLS + ft * 32 + (lane & 31), ch));
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+        F.b[tt] = *reinterpret_cast<const bf16x8 *>(stage + wswz(wt * 128 + tt * 32 + (lane & 31), ch));
+}
+__device__ __forceinline__ void wide_mma(f32x16 (&acc)[3][4], const WFr &F) {
+#pragma unroll
+    for (int ft = 0; ft < 3; ++ft)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[ft][tt] = mfma32x32x16(F.a[ft], F.b[tt], acc[ft][tt]);
+}
+
+// Epilogue of one wave.  WF (the wave's column quarter) is a template
+// parameter so that every section index is a compile-time constant; a tile
+// starts at a q section, so section s has kind s % 3.
+template <int D, int WF>
+__device__ __forceinline__ void wide_sumsq(const f32x16 (&acc)[3][4], float *red, int lane, int wt) {
+    constexpr int NSEC = WN / D;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        float ss[NSEC];
+#pragma unroll
+        for (int s = 0; s < NSEC; ++s) ss[s] = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 3; ++ft) {
+            const int sec = (WF * WCOLS + ft * 32) / D;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ss[sec] += acc[ft][tt][i] * acc[ft][tt][i];
+        }
+        const int tok = wt * 128 + tt * 32 + (lane & 31);
+#pragma unroll
+        for (int s = 0; s < NSEC; ++s) {
+            if (s % 3 == 2) continue;   // v sections: no norm
+            if (s * D >= (WF + 1) * WCOLS || (s + 1) * D <= WF * WCOLS) continue;   // not this wave's
+            const float tot = ss[s] + __shfl_xor(ss[s], 32);
+            if (lane < 32) red[(WF * 6 + s) * WM + tok] = tot;
+        }
+    }
+}
+// Scaled bf16 results of token tiles TT0, TT0+1 into the staging tile (64 rows).
+template <int D, int WF, int TT0>
+__device__ __forceinline__ void wide_stage(const f32x16 (&acc)[3][4], const float *red, bf16 *out_s, int lane,
+                                           int wt, float eps) {
+#pragma unroll
+    for (int tt = TT0; tt < TT0 + 2; ++tt) {
+        const int tok = wt * 128 + tt * 32 + (lane & 31);
+        const int row = (tt - TT0) * 32 + (lane & 31);
+#pragma unroll
+        for (int ft = 0; ft < 3; ++ft) {
+            const int f0 = WF * WCOLS + ft * 32, s = f0 / D;
+            float scale = 1.f;
+            if (s % 3 != 2) {   // q or k section: L2 norm over the section
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    if (s * D < (w + 1) * WCOLS && (s + 1) * D > w * WCOLS) tot += red[(w * 6 + s) * WM + tok];
+                scale = 1.f / sqrtf(tot + eps);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 pk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pk[j] = (bf16)(acc[ft][tt][4 * g + j] * scale);
+                *reinterpret_cast<bf16x4 *>(out_s + row * WOUT_LD + f0 + 8 * g + 4 * (lane >> 5)) = pk;
+            }
+        }
+    }
+}
+template <int D, int TT0>
+__device__ __forceinline__ void wide_stage_any(const f32x16 (&acc)[3][4], const float *red, bf16 *out_s,
+                                               int lane, int wt, int wf, float eps) {
+    switch (wf) {
+        case 0: wide_stage<D, 0, TT0>(acc, red, out_s, lane, wt, eps); break;
+        case 1: wide_stage<D, 1, TT0>(acc, red, out_s, lane, wt, eps); break;
+        case 2: wide_stage<D, 2, TT0>(acc, red, out_s, lane, wt, eps); break;
+        default: wide_stage<D, 3, TT0>(acc, red, out_s, lane, wt, eps); break;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_proj_wide(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ Wp, int M, int K, int H, int m_tiles, int n_tiles,
+    bf16 *q, bf16 *k, bf16 *v, float eps) {
+    __shared__ __attribute__((aligned(16))) char smem[W_LDS_MAIN];
+    bf16 *stages = reinterpret_cast<bf16 *>(smem);
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wt = wave >> 2, wf = wave & 3;
+    // Workgroup ids are dealt to the 8 XCDs round-robin; give each XCD a
+    // contiguous run of tiles (column-tile major) so that its L2 serves few
+    // column tiles.
+    const int ntot = m_tiles * n_tiles;
+    const int id = blockIdx.x;
+    const int tix = (ntot % 8 == 0) ? (id % 8) * (ntot / 8) + id / 8 : id;
+    const int n_tile = tix / m_tiles, m_tile = tix % m_tiles;
+    const int m0 = m_tile * WM, n0 = n_tile * WN;
+    const int qkv_rows = H * 3 * D;
+    const int n_rows = min(WN, qkv_rows - n0);
+
+    const WideSrc src = wide_src(lane, wave, m0, M, K, n_rows);
+    const bf16 *xb = x + (int64_t)m0 * K, *wb = Wp + (int64_t)n0 * K;
+    const int nkb = K / WK;
+    auto kblock = [&](int kb) { return min(kb, nkb - 1) * WK; };
+
+    f32x16 acc[3][4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // k-loop over three stages: k-block kb is multiplied while kb+1 and kb+2
+    // are in flight.  Step kb: wait for kb (kb+1's five loads may remain),
+    // barrier (every wave has also finished reading kb-1), issue kb+2 into
+    // kb-1's stage, then two k-steps of fragment reads and MFMAs.
+    wide_issue(stages, src, xb, wb, wave);
+    wide_issue(stages + WSTAGE, src, xb + kblock(1), wb + kblock(1), wave);
+    int s_cur = 0;
+    for (int kb = 0; kb < nkb; ++kb) {
+        wait_vmcnt<5>();
+        lds_barrier();
+        const int s_ld = s_cur == 0 ? 2 : s_cur - 1;
+        const int k2 = kblock(kb + 2);
+        wide_issue(stages + s_ld * WSTAGE, src, xb + k2, wb + k2, wave);
+        const bf16 *cur = stages + s_cur * WSTAGE;
+        WFr f0, f1;
+        wide_read(f0, cur, 0, lane, wt, wf);
+        wide_read(f1, cur, 1, lane, wt, wf);
+        wide_mma(acc, f0);
+        wide_mma(acc, f1);
+        s_cur = s_cur == 2 ? 0 : s_cur + 1;
+    }
+    wait_vmcnt<0>();   // the re-reads past the end land before LDS is reused
+    __syncthreads();
+
+    bf16 *out_s = stages;
+    float *red = reinterpret_cast<float *>(smem + 64 * WOUT_LD * 2);
+    switch (wf) {
+        case 0: wide_sumsq<D, 0>(acc, red, lane, wt); break;
+        case 1: wide_sumsq<D, 1>(acc, red, lane, wt); break;
+        case 2: wide_sumsq<D, 2>(acc, red, lane, wt); break;
+        default: wide_sumsq<D, 3>(acc, red, lane, wt); break;
+    }
+    __syncthreads();
+    // four passes of 64 tokens through the staging tile
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        if (wt == pass / 2) {
+            if (pass % 2 == 0) wide_stage_any<D, 0>(acc, red, out_s, lane, wt, wf, eps);
+            else wide_stage_any<D, 2>(acc, red, out_s, lane, wt, wf, eps);
+        }
+        __syncthreads();
+        constexpr int PIECES = WN / 8;   // 16-byte pieces per staged token row
+#pragma unroll 3
+        for (int u = t; u < 64 * PIECES; u += 512) {
+            const int r = u / PIECES, f = (u % PIECES) * 8;
+            const int m = m0 + pass * 64 + r;
+            const int n = n0 + f;
+            const int head = n / (3 * D), kind = (n % (3 * D)) / D, off = n % D;
+            const bf16 *srow = out_s + r * WOUT_LD + f;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(srow), hi = *reinterpret_cast<const uint2 *>(srow + 4);
+            if (m < M && head < H) {
+                bf16 *dst = (kind == 0 ? q : (kind == 1 ? k : v)) + ((int64_t)m * H + head) * D + off;
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Gates for long inputs: a = x.wa and b = x.wb for 16 tokens per workgroup.
+// Eight waves take the channel steps (32 channels each) round-robin, R per
+// round with every operand load of the round issued up front, as MFMA
+// 16x16x32 products (tokens x gate columns, operands straight from global
+// memory); the partial sums meet in LDS.  NG 16-column tiles cover the 2H gate
+// columns.
+template <int NG>
+__global__ __launch_bounds__(512) void k_gates(const bf16 *__restrict__ x, const bf16 *__restrict__ Wg, int M,
+                                               int K, int H, float *alpha, float *beta, float alpha_lo) {
+    constexpr int R = NG <= 2 ? 8 : 4;   // channel steps per wave and round
+    __shared__ float red[8][16][NG * 16 + 1];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m0 = blockIdx.x * 16;
+    const bf16 *xr = x + (int64_t)min(m0 + (lane & 15), M - 1) * K + 8 * (lane >> 4);
+    const bf16 *wr[NG];
+#pragma unroll
+    for (int c = 0; c < NG; ++c) wr[c] = Wg + (int64_t)min(c * 16 + (lane & 15), 2 * H - 1) * K + 8 * (lane >> 4);
+    f32x4 acc[NG];
+#pragma unroll
+    for (int c = 0; c < NG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nsteps = K / 32;
+    for (int j0 = wave; j0 < nsteps; j0 += 8 * R) {
+        bf16x8 a[R], b[R][NG];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int kk = min(j0 + 8 * i, nsteps - 1) * 32;
+            a[i] = *reinterpret_cast<const bf16x8 *>(xr + kk);
+#pragma unroll
+            for (int c = 0; c < NG; ++c) b[i][c] = *reinterpret_cast<const bf16x8 *>(wr[c] + kk);
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if (j0 + 8 * i < nsteps)
+#pragma unroll
+                for (int c = 0; c < NG; ++c) acc[c] = mfma16x16x32(a[i], b[i][c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][4 * (lane >> 4) + e][c * 16 + (lane & 15)] = acc[c][e];
+    __syncthreads();
+    for (int idx = t; idx < 16 * 2 * H; idx += 512) {
+        const int r = idx / (2 * H), c = idx % (2 * H), m = m0 + r;
+        if (m >= M) continue;
+        float z = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) z += red[w][r][c];
+        if (c < H) alpha[(int64_t)m * H + c] = alpha_lo + (1.f - alpha_lo) / (1.f + expf(z));
+        else beta[(int64_t)m * H + (c - H)] = 1.f / (1.f + expf(-z));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU GEMM (small fp32 workloads), 64x128x16 tiles
 // ---------------------------------------------------------------------------
 constexpr int BM_F = 64, BK_F = 16;
@@ -370,6 +664,27 @@ hipError_t launch_pack_weights(bool f32, int d, int H, int D, const void *Wq, co
     return hipGetLastError();
 }
 
+// bf16 inputs of at least this many tokens take the wide tiles (k_gates +
+// k_proj_wide); shorter ones (decode steps, short prompts) the 256 x 128 tiles,
+// which spread a short input over more workgroups.
+constexpr int WIDE_MIN_TOKENS = 1024;
+
+bool project_separate_gates(bool f32, int M) { return !f32 && M >= WIDE_MIN_TOKENS; }
+
+hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
+                        float *beta, float alpha_lo, hipStream_t s) {
+    const int ng = (2 * H + 15) / 16;
+    const bf16 *Wg = (const bf16 *)Wpack + qkv_rows_padded(H, D) * d;
+    const dim3 grid((M + 15) / 16);
+#define GATES(NG) launch_kernel(k_gates<NG>, grid, dim3(512), 0, s, (const bf16 *)x, Wg, M, d, H, alpha, beta, alpha_lo)
+    if (ng <= 1) GATES(1);
+    else if (ng <= 2) GATES(2);
+    else if (ng <= 4) GATES(4);
+    else GATES(8);
+#undef GATES
+    return hipGetLastError();
+}
+
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
                           float eps, hipStream_t s) {
@@ -384,6 +699,14 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
             launch_kernel(k_proj_f32<64>, grid, dim3(256), 0, s, (const float *)x,
                                (const float *)Wpack, M, d, H, (float *)q, (float *)k, (float *)v,
                                alpha, beta, alpha_lo, eps);
+    } else if (project_separate_gates(f32, M)) {
+        const int m_tiles = (M + WM - 1) / WM, n_tiles = (H * 3 * D + WN - 1) / WN;
+        if (D == 128)
+            launch_kernel(k_proj_wide<128>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x,
+                          (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps);
+        else
+            launch_kernel(k_proj_wide<64>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x,
+                          (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps);
     } else {
         const int m_tiles = (M + BM_BF - 1) / BM_BF;
         const int n_main = (int)(qkv_rows_padded(H, D) / BN);   // the gate tile is n_main

@@ -13,6 +13,7 @@ and propagate through the loops.  Its bars are the fixed ones or a multiple of t
 it is recomputed as other valid fp32 implementations would (tests/helpers.py, loop_envelope), whichever is
 larger: 2x for normwise errors, 4x for the heavy-tailed max-relative statistic.
 """
+import dataclasses
 import numpy as np
 import pytest
 import torch
@@ -54,9 +55,19 @@ def _oracle_loop(w, x, B, L, keep=True):
 # ---------------------------------------------------------------------------
 # projection stage
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name,M", [("tiny_f32", 256), ("prefill_b1_l4096", 300), ("prefill_b1_l4096", 1)])
+def _proj_workload(name):
+    # bf16 with 64-wide heads and an odd head count: a 384-column tile holds two
+    # heads' q|k|v, and the last tile only one
+    if name == "bf16_d64_h3":
+        return dataclasses.replace(synth.workload("prefill_b1_l4096"), name=name, H=3, dk=64, dv=64, d=192)
+    return synth.workload(name)
+
+
+# M >= 1024 bf16 tokens take the wide tiles (k_gates + k_proj_wide), shorter inputs the 256 x 128 tiles
+@pytest.mark.parametrize("name,M", [("tiny_f32", 256), ("prefill_b1_l4096", 300), ("prefill_b1_l4096", 1),
+                                    ("prefill_b1_l4096", 1100), ("bf16_d64_h3", 300), ("bf16_d64_h3", 1100)])
 def test_project_parity(name, M):
-    w = synth.workload(name)
+    w = _proj_workload(name)
     say(f"[project] {name} M={M}")
     x = synth.prefill_inputs(w, L=min(M, w.L))
     xin = x["h0"].reshape(-1, w.d)[:M].contiguous()
