@@ -101,11 +101,27 @@ __device__ __forceinline__ void dma16_async(const void *g, void *wave_base) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// The same direct load to an LDS byte address given as a number (see lds_addr).
+__device__ __forceinline__ void dma16_async_at(const void *g, unsigned lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+// LDS byte address of a __shared__ object, wave-uniform.  Taking it once from
+// the object itself (rather than from pointers derived later) lets the
+// compiler fold the address-space conversion.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(const lds_void *)p);
+}
+
 // The same direct load with a wave-uniform base address (scalar registers)
 // and a per-lane 32-bit byte offset: one vector register per load instead of
 // a 64-bit address.
 __device__ __forceinline__ void dma16_async_s(const void *sbase, unsigned voff, void *wave_base) {
     const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(lds_void *)wave_base);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
+// ... and with the LDS byte address given as a number (see lds_addr).
+__device__ __forceinline__ void dma16_async_s_at(const void *sbase, unsigned voff, unsigned lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 

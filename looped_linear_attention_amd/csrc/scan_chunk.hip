@@ -415,6 +415,9 @@ template <int D, typename TIn> struct CarryCfg {
     static constexpr int K_INS = TILE / 1024;            // direct-load instructions for K
     static constexpr int VROWB = 16 * ES;                // bytes of a token row of the V slice
     static constexpr int V_INS = C * VROWB / 1024;
+    static constexpr int W_BYTES = D * C * 4;            // W hi and lo parts of one chunk
+    static constexpr int W_INS = W_BYTES / 1024;
+    static constexpr int KVG_INS = K_INS + V_INS + 1;     // K tile, V slice, gamma
     // workspace elements per (b, h, chunk): chunk-start state, hi and lo bf16
     // planes as [slice][wave][part][lane][KW]; E tiles as [slice][tile][lane] of
     // 16 bytes (4 bf16 hi then 4 bf16 lo)
@@ -429,51 +432,77 @@ __device__ __forceinline__ int k_phys(int r, int c) {
     return c ^ ((r << G::SH) & (G::NCH - 1));
 }
 
-// Per-wave W fragments of one chunk (bf16 hi/lo, fragment order).
-template <int D> struct WFrags {
-    static constexpr int NT = D / 64;
-    bf16x8 wh[NT][2], wl[NT][2];
+// Direct loads of chunk `cc` into one LDS stage, all issued by the producer
+// wave.  state_produce_kvg: the K tile (16-byte chunks XOR-swizzled by row),
+// the V slice of the workgroup's 16 columns and gamma (KVG_INS instructions).
+// state_produce_w: the chunk's W fragments, a byte copy of their fragment-order
+// block (W_INS instructions).  Tokens past the end of the sequence re-read the
+// last token: the prep kernel gives them beta = 0, which zeroes their columns
+// of W, so any finite value is harmless.
+// Per-lane byte offsets of the K and V direct loads within a chunk's first
+// token row, computed once: full chunks then issue each load from a
+// wave-uniform base with no per-load vector arithmetic.
+template <int D, typename TIn> struct KvOffsets {
+    unsigned k[CarryCfg<D, TIn>::K_INS], v[CarryCfg<D, TIn>::V_INS];
 };
-
-template <int D>
-__device__ __forceinline__ void load_w(WFrags<D> &F, const float *W, int64_t cid, int wave, int lane) {
-    constexpr int NT = D / 64;
-    const bf16x8 *Wf = reinterpret_cast<const bf16x8 *>(W + cid * D * C) + (int64_t)wave * NT * 4 * 64 + lane;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            F.wh[tt][s] = Wf[((tt * 2 + s) * 2 + 0) * 64];
-            F.wl[tt][s] = Wf[((tt * 2 + s) * 2 + 1) * 64];
-        }
-}
-
-// Issues this wave's share of the direct loads of chunk `cc`: the K tile, the
-// V slice and gamma.  Tokens past the end of the sequence re-read the last
-// token: the prep kernel gives them beta = 0, which zeroes their columns of W
-// and M, so any finite value is harmless.
 template <int D, typename TIn>
-__device__ __forceinline__ void state_issue(unsigned char *__restrict__ ks, unsigned char *__restrict__ vs,
-                                            float *__restrict__ gs, int cc, int L, int H, int h, int64_t tokb,
-                                            int col0, const TIn *__restrict__ k, const TIn *__restrict__ v,
-                                            const float *__restrict__ g, int64_t cidb, int wave, int lane) {
+__device__ __forceinline__ KvOffsets<D, TIn> kv_offsets(int H, int lane) {
+    using G = CarryCfg<D, TIn>;
+    KvOffsets<D, TIn> o;
+    const unsigned rs = (unsigned)(H * D * G::ES);   // bytes per token row of q/k/v
+#pragma unroll
+    for (int n = 0; n < G::K_INS; ++n) {
+        const int p = n * 64 + lane;
+        const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
+        o.k[n] = r * rs + c * 16;
+    }
+    constexpr int LPR = G::VROWB / 16;   // lanes per V row
+#pragma unroll
+    for (int n = 0; n < G::V_INS; ++n) {
+        const int p = n * 64 + lane;
+        o.v[n] = (p / LPR) * rs + (p % LPR) * 16;
+    }
+    return o;
+}
+template <int D, typename TIn>
+__device__ __forceinline__ void state_produce_kvg(unsigned ks, unsigned vs, unsigned gs, int cc, int L, int H,
+                                                  int h, int64_t tokb, int col0, const TIn *__restrict__ k,
+                                                  const TIn *__restrict__ v, const float *g, int64_t cidb,
+                                                  int lane, const KvOffsets<D, TIn> &off) {
     using G = CarryCfg<D, TIn>;
     constexpr int EPC = 16 / G::ES;   // elements per 16-byte chunk
     const int c0 = cc * C;
+    if (c0 + C <= L) {
+        const TIn *kb = k + ((tokb + c0) * H + h) * D, *vb = v + ((tokb + c0) * H + h) * D + col0;
 #pragma unroll
-    for (int n = 0; n < G::K_INS / 4; ++n) {
-        const int base = (4 * n + wave) * 64, p = base + lane;
-        const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
-        const int tok = min(c0 + r, L - 1);
-        dma16_async(k + ((tokb + tok) * H + h) * D + c * EPC, ks + base * 16);
+        for (int n = 0; n < G::K_INS; ++n) dma16_async_s_at(kb, off.k[n], ks + n * 1024);
+#pragma unroll
+        for (int n = 0; n < G::V_INS; ++n) dma16_async_s_at(vb, off.v[n], vs + n * 1024);
+    } else {
+#pragma unroll
+        for (int n = 0; n < G::K_INS; ++n) {
+            const int p = n * 64 + lane;
+            const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
+            const int tok = min(c0 + r, L - 1);
+            dma16_async_at(k + ((tokb + tok) * H + h) * D + c * EPC, ks + n * 1024);
+        }
+        constexpr int LPR = G::VROWB / 16;   // lanes per V row
+#pragma unroll
+        for (int n = 0; n < G::V_INS; ++n) {
+            const int p = n * 64 + lane, r = p / LPR, qq = p % LPR;
+            const int tok = min(c0 + r, L - 1);
+            dma16_async_at(v + ((tokb + tok) * H + h) * D + col0 + qq * EPC, vs + n * 1024);
+        }
     }
-    constexpr int LPR = G::VROWB / 16;   // lanes per V row
-    if (wave < G::V_INS) {
-        const int p = wave * 64 + lane, r = p / LPR, qq = p % LPR;
-        const int tok = min(c0 + r, L - 1);
-        dma16_async(v + ((tokb + tok) * H + h) * D + col0 + qq * EPC, vs + wave * 1024);
-    }
-    if (wave == 3 && lane < C / 4) dma16_async(g + (cidb + cc) * C + 4 * lane, gs);
+    // one instruction with 16 active lanes (64 floats)
+    if (lane < C / 4) dma16_async_s_at(g + (cidb + cc) * C, lane * 16, gs);
+}
+template <int D, typename TIn>
+__device__ __forceinline__ void state_produce_w(unsigned ws, int cc, const float *W, int64_t cidb, int lane) {
+    using G = CarryCfg<D, TIn>;
+    const float *wsrc = W + (cidb + cc) * D * C;
+#pragma unroll
+    for (int n = 0; n < G::W_INS; ++n) dma16_async_s_at(wsrc + n * 256, lane * 16, ws + n * 1024);
 }
 
 // K.S A fragment (token row r, this lane's KW state rows) from a K tile
@@ -532,23 +561,34 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
     return mfma16x16x32(al, bh, c);
 }
 
-// global stores one lane issues per chunk in the state pass (chunk-start
-// state hi and lo, E tile), after the next chunk's loads: the wait for those
-// loads lets exactly these stay in flight
-constexpr int STATE_STORES = 3;
+// State pass.  Waves 0-3 compute; wave 4 only issues direct loads, so the
+// compute waves never stall behind the memory pipeline's issue queue.  Per
+// chunk cc, three workgroup barriers:
+//   B0  K, V, gamma of chunk cc have landed; the compute waves are done with
+//       chunk cc-1.  Compute: store the chunk-start state, K.S partials.
+//       Producer: issue K, V, gamma of chunk cc+1 into the other stage.
+//   B1  partials visible; W of chunk cc has landed.  Compute: reduce, form and
+//       store E, read W fragments.  Producer: issue W of chunk cc+1 into the
+//       other W stage (its last reader, chunk cc-1, passed B1 before B0).
+//   B2  E visible.  Compute: S = gamma_C S + W E.
+// So K, V, gamma get one chunk to land and W gets one chunk as well, shifted
+// by one barrier; the producer's two issue bursts overlap the compute phases
+// instead of delaying a barrier.  Past the last chunk the producer re-reads
+// the last chunk into the idle stages, so its wait counts never change, and
+// it drains its loads before it exits.
+constexpr int STATE_THREADS = 320;
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void k_scan_state(
+__global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
     const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc, const float *W,
-    const float *__restrict__ g, const float *__restrict__ s_init, float *__restrict__ s_final,
+    const float *g, const float *__restrict__ s_init, float *__restrict__ s_final,
     bf16 *__restrict__ sc_ws, uint4 *__restrict__ e_ws) {
-    // (W is not __restrict__: its loads must stay ordered with the wait_vmcnt
-    // fences, which a restrict pointer's loads may be moved across.)
     using G = CarryCfg<D, TIn>;
     constexpr int NT = G::NT, RW = G::RW, KW = G::KW;
     // every stage is an object of its own, so the compiler can tell the buffers
     // a chunk reads from the ones the next chunk's direct loads write
     __shared__ __attribute__((aligned(16))) unsigned char k0_s[G::TILE], k1_s[G::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char w0_s[G::W_BYTES], w1_s[G::W_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[C * G::VROWB];
     __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[C];
     __shared__ __attribute__((aligned(16))) f32x4 red[4][4][64];   // [source wave][token tile][lane]
@@ -564,6 +604,32 @@ __global__ __launch_bounds__(256) void k_scan_state(
     const int64_t tokb = (int64_t)b * L;
     const int64_t cidb = ((int64_t)b * H + h) * Nc;
 
+    if (wave == 4) {
+        // producer; two chunks per iteration so that the stages are compile-time choices
+        const unsigned lk[2] = {lds_addr(k0_s), lds_addr(k1_s)}, lv[2] = {lds_addr(v0_s), lds_addr(v1_s)};
+        const unsigned lgm[2] = {lds_addr(g0_s), lds_addr(g1_s)}, lw[2] = {lds_addr(w0_s), lds_addr(w1_s)};
+        const KvOffsets<D, TIn> off = kv_offsets<D, TIn>(H, lane);
+        auto pstep = [&](auto stc, int cc) __attribute__((always_inline)) {
+            constexpr int NX = 1 - decltype(stc)::value;   // stage that receives chunk cc+1
+            const int nx = min(cc + 1, Nc - 1);
+            wait_vmcnt<G::W_INS>();     // K, V, gamma of cc landed (W of cc may be in flight)
+            lds_barrier();              // B0
+            state_produce_kvg<D, TIn>(lk[NX], lv[NX], lgm[NX], nx, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
+            wait_vmcnt<G::KVG_INS>();   // W of cc landed (K, V, gamma of cc+1 may be in flight)
+            lds_barrier();              // B1
+            state_produce_w<D, TIn>(lw[NX], nx, W, cidb, lane);
+            __builtin_amdgcn_s_barrier();   // B2
+        };
+        state_produce_kvg<D, TIn>(lk[0], lv[0], lgm[0], 0, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
+        state_produce_w<D, TIn>(lw[0], 0, W, cidb, lane);
+        for (int cc = 0; cc < Nc; cc += 2) {
+            pstep(std::integral_constant<int, 0>(), cc);
+            if (cc + 1 < Nc) pstep(std::integral_constant<int, 1>(), cc + 1);
+        }
+        wait_vmcnt<0>();   // no direct load may still write this workgroup's LDS after it ends
+        return;
+    }
+
     // state slice: Sv[tt][j] = S[RW wave + 4 NT lg + 4 tt + j][col]
     float Sv[NT][4];
     const int64_t sbase = ((int64_t)b * H + h) * D * D;
@@ -573,30 +639,20 @@ __global__ __launch_bounds__(256) void k_scan_state(
         for (int j = 0; j < 4; ++j)
             Sv[tt][j] = s_init ? s_init[sbase + (int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] : 0.f;
     // Nothing loaded before the loop may be pending inside it: otherwise the
-    // compiler's wait for these registers lands in the loop body (every chunk).
+    // compiler's wait for these registers lands in the loop body, where it
+    // would also wait for every chunk's stores.
     wait_vmcnt<0>();
 
-    WFrags<D> fa, fb;
-    state_issue<D, TIn>(k0_s, v0_s, g0_s, 0, L, H, h, tokb, col0, k, v, g, cidb, wave, lane);
-    load_w<D>(fa, W, cidb, wave, lane);
-    wait_vmcnt<0>();   // chunk 0's loads (the waits in the loop assume only stores are younger)
-
     // One chunk step on LDS stage ST (= cc mod 2).  Two steps per loop iteration
-    // so stages are compile-time constants and the W register sets swap roles
-    // without copies.
-    auto step = [&](auto stc, int cc, const WFrags<D> &cur, WFrags<D> &nxt) __attribute__((always_inline)) {
+    // so that the stage is a compile-time constant.
+    auto step = [&](auto stc, int cc) __attribute__((always_inline)) {
         constexpr int ST = decltype(stc)::value;
-        unsigned char *k_cur = ST == 0 ? k0_s : k1_s, *k_nxt = ST == 0 ? k1_s : k0_s;
-        unsigned char *v_cur = ST == 0 ? v0_s : v1_s, *v_nxt = ST == 0 ? v1_s : v0_s;
-        float *g_cur = ST == 0 ? g0_s : g1_s, *g_nxt = ST == 0 ? g1_s : g0_s;
-        wait_vmcnt<STATE_STORES>();   // only the previous chunk's stores may remain in flight
-        lds_barrier();                // (B0) chunk cc's direct loads of every wave have landed
-        const bool more = cc + 1 < Nc;
+        const unsigned char *k_cur = ST == 0 ? k0_s : k1_s;
+        const unsigned char *v_cur = ST == 0 ? v0_s : v1_s;
+        const float *g_cur = ST == 0 ? g0_s : g1_s;
+        const bf16x8 *w_cur = reinterpret_cast<const bf16x8 *>(ST == 0 ? w0_s : w1_s) + wave * NT * 4 * 64 + lane;
+        lds_barrier();   // (B0) chunk cc's loads have landed; chunk cc-1's stage is free
         const int64_t cid = cidb + cc;
-        if (more) {
-            state_issue<D, TIn>(k_nxt, v_nxt, g_nxt, cc + 1, L, H, h, tokb, col0, k, v, g, cidb, wave, lane);
-            load_w<D>(nxt, W, cid + 1, wave, lane);   // before this chunk's stores, see STATE_STORES
-        }
         // chunk-start state as the B operand of K.S (and of Q.S in the output pass)
         __bf16 sh[KW], sl[KW];
         {
@@ -619,7 +675,7 @@ __global__ __launch_bounds__(256) void k_scan_state(
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)
             if (tm != wave) red[wave][tm][lane] = ks[tm];
-        lds_barrier();   // (B1) partials visible
+        lds_barrier();   // (B1) partials visible; W of chunk cc has landed
         f32x4 kt = ks[0];
 #pragma unroll
         for (int tm = 1; tm < 4; ++tm)
@@ -627,6 +683,15 @@ __global__ __launch_bounds__(256) void k_scan_state(
 #pragma unroll
         for (int src = 0; src < 4; ++src)
             if (src != wave) kt += red[src][wave][lane];
+        // W fragments of this wave's rows (read now, used after B2)
+        bf16x8 wh[NT][2], wl[NT][2];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                wh[tt][s] = w_cur[((tt * 2 + s) * 2 + 0) * 64];
+                wl[tt][s] = w_cur[((tt * 2 + s) * 2 + 1) * 64];
+            }
         // E = V - diag(gamma) K S for tokens 16 wave + 4 lg + j
         float e[4];
 #pragma unroll
@@ -662,14 +727,14 @@ __global__ __launch_bounds__(256) void k_scan_state(
         for (int tt = 0; tt < NT; ++tt) {
             f32x4 we = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) we = mma_hl(cur.wh[tt][s], cur.wl[tt][s], ebh[s], ebl[s], we);
+            for (int s = 0; s < 2; ++s) we = mma_hl(wh[tt][s], wl[tt][s], ebh[s], ebl[s], we);
 #pragma unroll
             for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + we[j];
         }
     };
     for (int cc = 0; cc < Nc; cc += 2) {
-        step(std::integral_constant<int, 0>(), cc, fa, fb);
-        if (cc + 1 < Nc) step(std::integral_constant<int, 1>(), cc + 1, fb, fa);
+        step(std::integral_constant<int, 0>(), cc);
+        if (cc + 1 < Nc) step(std::integral_constant<int, 1>(), cc + 1);
     }
     if (s_final) {
 #pragma unroll
@@ -845,7 +910,7 @@ hipError_t launch_scan_state(bool f32, int B, int L, int H, int D, const void *k
     const int Nc = (L + C - 1) / C;
     dim3 grid(H, D / 16, B);
 #define STATE(DD, T)                                                                               \
-    launch_kernel((k_scan_state<DD, T>), grid, dim3(256), 0, s, (const T *)k, (const T *)v, L, H, Nc, \
+    launch_kernel((k_scan_state<DD, T>), grid, dim3(STATE_THREADS), 0, s, (const T *)k, (const T *)v, L, H, Nc, \
                   (const float *)ws.W, (const float *)ws.g, s_init, s_final, ws.sc, ws.e)
     if (f32) {
         if (D == 128) STATE(128, float); else STATE(64, float);
