@@ -317,7 +317,7 @@ constexpr int WA = WM * WK, WB = WN * WK, WSTAGE = WA + WB;   // bf16 elements p
 constexpr int WOUT_LD = WN + 4;   // bf16 row stride of the output staging tile (776 bytes)
 constexpr int WCOLS = 96;         // columns per wave
 constexpr int W_LDS_MAIN = WSTAGES * WSTAGE * 2;
-constexpr int W_LDS_EPI = 64 * WOUT_LD * 2 + 4 * 6 * WM * 4;
+constexpr int W_LDS_EPI = 128 * WOUT_LD * 2;   // staging tile; the sums of squares (<= 24 KiB) come first
 static_assert(W_LDS_EPI <= W_LDS_MAIN, "epilogue buffers reuse the operand stages");
 
 // 16-byte chunk `ch` (0..3) of row `r` of a 32-wide bf16 tile (64-byte rows),
@@ -378,67 +378,113 @@ __device__ __forceinline__ void wide_mma(f32x16 (&acc)[3][4], const WFr &F) {
 // Epilogue of one wave.  WF (the wave's column quarter) is a template
 // parameter so that every section index is a compile-time constant; a tile
 // starts at a q section, so section s has kind s % 3.
+//   1. per-token sums of squares of each q/k section this wave touches (in-lane
+//      sums plus one exchange between lane halves) into LDS;
+//   2. the per-(token, section) scales 1/sqrt(sum + eps), once, in registers;
+//   3. two passes of 128 tokens (all eight waves stage 2 token tiles each) through
+//      a bf16 staging tile, then 16-byte stores of whole output row sections.
 template <int D, int WF>
-__device__ __forceinline__ void wide_sumsq(const f32x16 (&acc)[3][4], float *red, int lane, int wt) {
+__device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *smem, int lane, int wt, int t,
+                                              int m0, int n0, int M, int H, bf16 *q, bf16 *k, bf16 *v,
+                                              float eps) {
     constexpr int NSEC = WN / D;
+    constexpr int S0 = (WF * WCOLS) / D, S1 = (WF * WCOLS + WCOLS - 1) / D, NS = S1 - S0 + 1;
+    float *red = reinterpret_cast<float *>(smem);   // [4 column quarters][NSEC][WM tokens]
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        float ss[NSEC];
+        float ss[NS];
 #pragma unroll
-        for (int s = 0; s < NSEC; ++s) ss[s] = 0.f;
+        for (int i = 0; i < NS; ++i) ss[i] = 0.f;
 #pragma unroll
         for (int ft = 0; ft < 3; ++ft) {
-            const int sec = (WF * WCOLS + ft * 32) / D;
+            const int si = (WF * WCOLS + ft * 32) / D - S0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ss[sec] += acc[ft][tt][i] * acc[ft][tt][i];
+            for (int i = 0; i < 16; ++i) ss[si] += acc[ft][tt][i] * acc[ft][tt][i];
         }
         const int tok = wt * 128 + tt * 32 + (lane & 31);
 #pragma unroll
-        for (int s = 0; s < NSEC; ++s) {
-            if (s % 3 == 2) continue;   // v sections: no norm
-            if (s * D >= (WF + 1) * WCOLS || (s + 1) * D <= WF * WCOLS) continue;   // not this wave's
-            const float tot = ss[s] + __shfl_xor(ss[s], 32);
-            if (lane < 32) red[(WF * 6 + s) * WM + tok] = tot;
+        for (int i = 0; i < NS; ++i) {
+            if ((S0 + i) % 3 == 2) continue;   // v sections: no norm
+            const float tot = ss[i] + __shfl_xor(ss[i], 32);
+            if (lane < 32) red[(WF * NSEC + S0 + i) * WM + tok] = tot;
         }
     }
-}
-// Scaled bf16 results of token tiles TT0, TT0+1 into the staging tile (64 rows).
-template <int D, int WF, int TT0>
-__device__ __forceinline__ void wide_stage(const f32x16 (&acc)[3][4], const float *red, bf16 *out_s, int lane,
-                                           int wt, float eps) {
+    lds_barrier();
+    // scaled bf16 results, [ft][tt][g] = 4 consecutive columns of one token;
+    // the fp32 accumulators are dead from here on
+    bf16x4 res[3][4][4];
 #pragma unroll
-    for (int tt = TT0; tt < TT0 + 2; ++tt) {
+    for (int tt = 0; tt < 4; ++tt) {
         const int tok = wt * 128 + tt * 32 + (lane & 31);
-        const int row = (tt - TT0) * 32 + (lane & 31);
+        float sc[NS];
 #pragma unroll
-        for (int ft = 0; ft < 3; ++ft) {
-            const int f0 = WF * WCOLS + ft * 32, s = f0 / D;
-            float scale = 1.f;
+        for (int i = 0; i < NS; ++i) {
+            const int s = S0 + i;
+            sc[i] = 1.f;
             if (s % 3 != 2) {   // q or k section: L2 norm over the section
                 float tot = 0.f;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    if (s * D < (w + 1) * WCOLS && (s + 1) * D > w * WCOLS) tot += red[(w * 6 + s) * WM + tok];
-                scale = 1.f / sqrtf(tot + eps);
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 pk;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pk[j] = (bf16)(acc[ft][tt][4 * g + j] * scale);
-                *reinterpret_cast<bf16x4 *>(out_s + row * WOUT_LD + f0 + 8 * g + 4 * (lane >> 5)) = pk;
+                    if (s * D < (w + 1) * WCOLS && (s + 1) * D > w * WCOLS) tot += red[(w * NSEC + s) * WM + tok];
+                sc[i] = 1.f / sqrtf(tot + eps);
             }
         }
+#pragma unroll
+        for (int ft = 0; ft < 3; ++ft) {
+            const float scale = sc[(WF * WCOLS + ft * 32) / D - S0];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) res[ft][tt][g][j] = (bf16)(acc[ft][tt][4 * g + j] * scale);
+        }
     }
-}
-template <int D, int TT0>
-__device__ __forceinline__ void wide_stage_any(const f32x16 (&acc)[3][4], const float *red, bf16 *out_s,
-                                               int lane, int wt, int wf, float eps) {
-    switch (wf) {
-        case 0: wide_stage<D, 0, TT0>(acc, red, out_s, lane, wt, eps); break;
-        case 1: wide_stage<D, 1, TT0>(acc, red, out_s, lane, wt, eps); break;
-        case 2: wide_stage<D, 2, TT0>(acc, red, out_s, lane, wt, eps); break;
-        default: wide_stage<D, 3, TT0>(acc, red, out_s, lane, wt, eps); break;
+    lds_barrier();   // the staging tile below overwrites the sums
+    bf16 *out_s = reinterpret_cast<bf16 *>(smem);
+    constexpr int PIECES = WN / 8;   // 16-byte pieces per staged token row
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int tt = 2 * pass + h2;
+            const int row = wt * 64 + h2 * 32 + (lane & 31);
+#pragma unroll
+            for (int ft = 0; ft < 3; ++ft)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<bf16x4 *>(out_s + row * WOUT_LD + WF * WCOLS + ft * 32 + 8 * g +
+                                                4 * (lane >> 5)) = res[ft][tt][g];
+        }
+        lds_barrier();
+        // Staging row r holds token (r / 64) 128 + 64 pass + r % 64 of the tile.
+        // Threads 0..383 each own one 16-byte column piece of the rows and store
+        // 16 rows, 4 at a time; the destination row advances by a fixed stride.
+        if (t < 8 * PIECES) {
+            const int r0 = t / PIECES, f = (t % PIECES) * 8, n = n0 + f;
+            const int head = n / (3 * D), kind = (n % (3 * D)) / D, off = n % D;
+            const int64_t rs = (int64_t)H * D;   // elements between consecutive tokens
+            bf16 *dst = (kind == 0 ? q : (kind == 1 ? k : v)) + (int64_t)head * D + off +
+                        (int64_t)(m0 + pass * 64 + r0) * rs;
+            const bool col_ok = head < H;
+            const int mb = m0 + pass * 64 + r0;
+#pragma unroll
+            for (int i0 = 0; i0 < 16; i0 += 4) {
+                uint4 val[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = r0 + 8 * (i0 + i);
+                    const bf16 *srow = out_s + r * WOUT_LD + f;
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(srow);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(srow + 4);
+                    val[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ii = i0 + i, dm = (ii / 8) * 128 + 8 * (ii % 8);   // token offset of row r0 + 8 ii
+                    if (col_ok && mb + dm < M) *reinterpret_cast<uint4 *>(dst + dm * rs) = val[i];
+                }
+            }
+        }
+        if (pass == 0) lds_barrier();   // every staged row read before the second pass overwrites
     }
 }
 
@@ -478,8 +524,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // k-loop over three stages: k-block kb is multiplied while kb+1 and kb+2
     // are in flight.  Step kb: wait for kb (kb+1's five loads may remain),
-    // barrier (every wave has also finished reading kb-1), issue kb+2 into
-    // kb-1's stage, then two k-steps of fragment reads and MFMAs.
+    // barrier (every wave has also finished reading kb-1), read both k-steps'
+    // fragments, then the 24 MFMAs with the five direct loads of kb+2 (into
+    // kb-1's stage) spread between them.  Issuing the loads after the reads
+    // keeps them from delaying the first MFMAs: the eight waves' 40 loads per
+    // k-block take the CU's address path several hundred cycles to accept.
     wide_issue(stages, src, xb, wb, wave);
     wide_issue(stages + WSTAGE, src, xb + kblock(1), wb + kblock(1), wave);
     int s_cur = 0;
@@ -488,50 +537,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         lds_barrier();
         const int s_ld = s_cur == 0 ? 2 : s_cur - 1;
         const int k2 = kblock(kb + 2);
-        wide_issue(stages + s_ld * WSTAGE, src, xb + k2, wb + k2, wave);
+        bf16 *ld = stages + s_ld * WSTAGE;
         const bf16 *cur = stages + s_cur * WSTAGE;
         WFr f0, f1;
         wide_read(f0, cur, 0, lane, wt, wf);
         wide_read(f1, cur, 1, lane, wt, wf);
-        wide_mma(acc, f0);
-        wide_mma(acc, f1);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+            const WFr &F = i < 12 ? f0 : f1;
+            const int ft = (i % 12) / 4, tt = i % 4;
+            acc[ft][tt] = mfma32x32x16(F.a[ft], F.b[tt], acc[ft][tt]);
+            if (i % 5 == 1) {
+                const int n = i / 5;   // loads 0..4 after MFMAs 1, 6, 11, 16, 21
+                if (n < 2) dma16_async_s(xb + k2, src.off[n], ld + (8 * n + wave) * 64 * 8);
+                else dma16_async_s(wb + k2, src.off[n], ld + WA + (8 * (n - 2) + wave) * 64 * 8);
+            }
+        }
         s_cur = s_cur == 2 ? 0 : s_cur + 1;
     }
     wait_vmcnt<0>();   // the re-reads past the end land before LDS is reused
     __syncthreads();
 
-    bf16 *out_s = stages;
-    float *red = reinterpret_cast<float *>(smem + 64 * WOUT_LD * 2);
     switch (wf) {
-        case 0: wide_sumsq<D, 0>(acc, red, lane, wt); break;
-        case 1: wide_sumsq<D, 1>(acc, red, lane, wt); break;
-        case 2: wide_sumsq<D, 2>(acc, red, lane, wt); break;
-        default: wide_sumsq<D, 3>(acc, red, lane, wt); break;
-    }
-    __syncthreads();
-    // four passes of 64 tokens through the staging tile
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        if (wt == pass / 2) {
-            if (pass % 2 == 0) wide_stage_any<D, 0>(acc, red, out_s, lane, wt, wf, eps);
-            else wide_stage_any<D, 2>(acc, red, out_s, lane, wt, wf, eps);
-        }
-        __syncthreads();
-        constexpr int PIECES = WN / 8;   // 16-byte pieces per staged token row
-#pragma unroll 3
-        for (int u = t; u < 64 * PIECES; u += 512) {
-            const int r = u / PIECES, f = (u % PIECES) * 8;
-            const int m = m0 + pass * 64 + r;
-            const int n = n0 + f;
-            const int head = n / (3 * D), kind = (n % (3 * D)) / D, off = n % D;
-            const bf16 *srow = out_s + r * WOUT_LD + f;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(srow), hi = *reinterpret_cast<const uint2 *>(srow + 4);
-            if (m < M && head < H) {
-                bf16 *dst = (kind == 0 ? q : (kind == 1 ? k : v)) + ((int64_t)m * H + head) * D + off;
-                *reinterpret_cast<uint4 *>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-        }
-        __syncthreads();
+        case 0: wide_epilogue<D, 0>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
+        case 1: wide_epilogue<D, 1>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
+        case 2: wide_epilogue<D, 2>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
+        default: wide_epilogue<D, 3>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
     }
 }
 
