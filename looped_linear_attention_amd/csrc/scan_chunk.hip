@@ -141,20 +141,25 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
     const int64_t tok0 = (int64_t)b * L + c0;
 
     // (1) K tile (zero rows past the end), the Q fragments of this wave's 16
-    // tokens (B operand of K Q^T), gates, and the fp64 log-cumsum of alpha
+    // tokens (B operand of K Q^T), gates, and the fp64 log-cumsum of alpha.
+    // Every global load is issued before the first wait (rows past the end
+    // read the last row and are masked afterwards), so the phase costs one
+    // memory round trip instead of one per load.
     constexpr int VEC = 16 / sizeof(TIn);
     constexpr int CPR = D / VEC;
-    for (int idx = t; idx < C * CPR; idx += 256) {
-        const int r = idx / CPR, ch = idx % CPR;
-        uint4 kv = make_uint4(0, 0, 0, 0);
-        if (c0 + r < L) kv = *reinterpret_cast<const uint4 *>(k + ((tok0 + r) * H + h) * D + ch * VEC);
-        *reinterpret_cast<uint4 *>(Ks + r * LDK + ch * VEC) = kv;
+    constexpr int KPT = C * CPR / 256;   // K-tile chunks per thread
+    const int last = L - 1 - c0;         // last valid row of the chunk
+    uint4 kv[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = t + 256 * i, r = idx / CPR, ch = idx % CPR;
+        kv[i] = *reinterpret_cast<const uint4 *>(k + ((tok0 + min(r, last)) * H + h) * D + ch * VEC);
     }
     float qf[KS][8];
+    TIn qraw[KS][8];
+    const int rq = 16 * wave + lr;
     {
-        const int r = 16 * wave + lr;
-        const bool ok = c0 + r < L;
-        const TIn *src = q + ((tok0 + (ok ? r : 0)) * H + h) * D + 8 * lg;   // 16-byte aligned runs
+        const TIn *src = q + ((tok0 + min(rq, last)) * H + h) * D + 8 * lg;   // 16-byte aligned runs
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if constexpr (F32) {
@@ -162,17 +167,35 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
                 const float4 c = *reinterpret_cast<const float4 *>(src + 32 * s + 4);
                 const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) qf[s][i] = ok ? v[i] : 0.f;
+                for (int i = 0; i < 8; ++i) qraw[s][i] = v[i];
             } else {
                 const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src + 32 * s);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) qf[s][i] = ok ? (float)v[i] : 0.f;
+                for (int i = 0; i < 8; ++i) qraw[s][i] = v[i];
             }
         }
     }
+    float a_raw = 1.f, b_raw = 0.f;
     if (wave == 0) {
-        const bool ok = c0 + lane < L;
-        const float a = ok ? alpha[(tok0 + lane) * H + h] : 1.f;   // padded tokens: identity
+        const int64_t gi = (tok0 + min(lane, last)) * H + h;
+        a_raw = alpha[gi];
+        b_raw = beta[gi];
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = t + 256 * i, r = idx / CPR, ch = idx % CPR;
+        *reinterpret_cast<uint4 *>(Ks + r * LDK + ch * VEC) = r <= last ? kv[i] : make_uint4(0, 0, 0, 0);
+    }
+    {
+        const bool ok = rq <= last;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qf[s][i] = ok ? to_f32(qraw[s][i]) : 0.f;
+    }
+    if (wave == 0) {
+        const bool ok = lane <= last;
+        const float a = ok ? a_raw : 1.f;   // padded tokens: identity
         double x = log((double)fmaxf(a, 1e-37f));
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -180,7 +203,7 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
             if (lane >= off) x += y;
         }
         lgs[lane] = x;
-        bes[lane] = ok ? beta[(tok0 + lane) * H + h] : 0.f;
+        bes[lane] = ok ? b_raw : 0.f;
     }
     // the strictly upper 16x16 blocks of T are zero
     for (int idx = t; idx < 6 * 256; idx += 256) {
