@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // wide bf16 MFMA GEMM for long inputs
 // ---------------------------------------------------------------------------
 // Block tile 384 packed columns (q|k|v of one head for D = 128, of two heads for
-// D = 64) x 256 tokens x 32 channels.  Eight waves (two per SIMD) own 96
+// D = 64) x 256 tokens x 64 channels.  Eight waves (two per SIMD) own 96
 // columns x 128 tokens each as 3 x 4 MFMA 32x32x16 tiles (192 fp32 accumulators
 // per lane).  Per flop this tile moves 45% fewer bytes from L2 into the CU than
 // a 256 x 128 tile, and each wave reads 22% fewer LDS bytes than with 128 x 64
@@ -312,47 +312,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // 8-byte pieces of output rows through a staging tile in LDS.
 // With one head per column tile, a sequence of 4096 tokens and 16 heads is
 // exactly 256 tiles, one per CU.  The gate columns run in k_gates.
-constexpr int WM = 256, WN = 384, WK = 32, WSTAGES = 3;
+constexpr int WM = 256, WN = 384, WK = 64, WSTAGES = 2;
 constexpr int WA = WM * WK, WB = WN * WK, WSTAGE = WA + WB;   // bf16 elements per stage
 constexpr int WOUT_LD = WN + 4;   // bf16 row stride of the output staging tile (776 bytes)
 constexpr int WCOLS = 96;         // columns per wave
 constexpr int W_LDS_MAIN = WSTAGES * WSTAGE * 2;
 constexpr int W_LDS_EPI = 128 * WOUT_LD * 2;   // staging tile; the sums of squares (<= 24 KiB) come first
 static_assert(W_LDS_EPI <= W_LDS_MAIN, "epilogue buffers reuse the operand stages");
+// Direct loads per wave per k-block (10), of which the token tile's (4): wave w's
+// load i covers LDS chunks [(8 i + w) 64, +64) of its tile.  LDS chunk p holds row
+// p / 8, logical chunk (p % 8) ^ ((row / 2) % 8).  Token rows past M re-read the
+// last token and column rows past the packed q|k|v rows re-read the last used
+// one; their results are never stored.
+constexpr int WLOADS = (WA + WB) / 8 / 64 / 8;
+constexpr int WLOADS_A = WA / 8 / 64 / 8;
 
-// 16-byte chunk `ch` (0..3) of row `r` of a 32-wide bf16 tile (64-byte rows),
-// XOR-swizzled by r / 4: 16 consecutive rows reading the same chunk then hit 16
+// 16-byte chunk `ch` (0..7) of row `r` of a 64-wide bf16 tile (128-byte rows),
+// XOR-swizzled by r / 2: 16 consecutive rows reading the same chunk then hit 16
 // distinct 16-byte bank groups.
-__device__ __forceinline__ int wswz(int r, int ch) { return r * WK + ((ch ^ ((r >> 2) & 3)) << 3); }
+__device__ __forceinline__ int wswz(int r, int ch) { return r * WK + ((ch ^ ((r >> 1) & 7)) << 3); }
 
-// Per-lane source offsets (bytes, relative to the k-block's first channel) of
-// the five direct loads a wave issues per k-block: loads 0..1 fill the token
-// tile (1024 16-byte chunks; wave w's load i covers LDS chunks [(8 i + w) 64,
-// +64)), loads 2..4 the column tile (1536 chunks).  LDS chunk p holds row p / 4,
-// logical chunk (p % 4) ^ ((row / 4) % 4).  Token rows past M re-read the last
-// token and column rows past the packed q|k|v rows re-read the last used one;
-// their results are never stored.
 struct WideSrc {
-    unsigned off[5];
+    unsigned off[WLOADS];
 };
 __device__ __forceinline__ WideSrc wide_src(int lane, int wave, int m0, int M, int K, int n_rows) {
     WideSrc s;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int base = (8 * (i < 2 ? i : i - 2) + wave) * 64, p = base + lane;
-        const int r = p >> 2, ch = (p & 3) ^ ((r >> 2) & 3);
-        const int row = i < 2 ? min(m0 + r, M - 1) - m0 : min(r, n_rows - 1);
+    for (int i = 0; i < WLOADS; ++i) {
+        const int base = (8 * (i < WLOADS_A ? i : i - WLOADS_A) + wave) * 64, p = base + lane;
+        const int r = p >> 3, ch = (p & 7) ^ ((r >> 1) & 7);
+        const int row = i < WLOADS_A ? min(m0 + r, M - 1) - m0 : min(r, n_rows - 1);
         s.off[i] = (unsigned)((row * K + ch * 8) * 2);
     }
     return s;
 }
-__device__ __forceinline__ void wide_issue(bf16 *stage, const WideSrc &src, const bf16 *xk, const bf16 *wk,
-                                           int wave) {
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        if (i < 2) dma16_async_s(xk, src.off[i], stage + (8 * i + wave) * 64 * 8);
-        else dma16_async_s(wk, src.off[i], stage + WA + (8 * (i - 2) + wave) * 64 * 8);
-    }
+__device__ __forceinline__ void wide_load(int i, bf16 *stage, const WideSrc &src, const bf16 *xk, const bf16 *wk,
+                                          int wave) {
+    if (i < WLOADS_A) dma16_async_s(xk, src.off[i], stage + (8 * i + wave) * 64 * 8);
+    else dma16_async_s(wk, src.off[i], stage + WA + (8 * (i - WLOADS_A) + wave) * 64 * 8);
 }
 
 // Fragments of one k-step: 3 column tiles (A operand) and 4 token tiles (B).
@@ -367,12 +364,6 @@ __device__ __forceinline__ void wide_read(WFr &F, const bf16 *stage, int ks, int
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
         F.b[tt] = *reinterpret_cast<const bf16x8 *>(stage + wswz(wt * 128 + tt * 32 + (lane & 31), ch));
-}
-__device__ __forceinline__ void wide_mma(f32x16 (&acc)[3][4], const WFr &F) {
-#pragma unroll
-    for (int ft = 0; ft < 3; ++ft)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[ft][tt] = mfma32x32x16(F.a[ft], F.b[tt], acc[ft][tt]);
 }
 
 // Epilogue of one wave.  WF (the wave's column quarter) is a template
@@ -522,38 +513,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // k-loop over three stages: k-block kb is multiplied while kb+1 and kb+2
-    // are in flight.  Step kb: wait for kb (kb+1's five loads may remain),
-    // barrier (every wave has also finished reading kb-1), read both k-steps'
-    // fragments, then the 24 MFMAs with the five direct loads of kb+2 (into
-    // kb-1's stage) spread between them.  Issuing the loads after the reads
-    // keeps them from delaying the first MFMAs: the eight waves' 40 loads per
-    // k-block take the CU's address path several hundred cycles to accept.
-    wide_issue(stages, src, xb, wb, wave);
-    wide_issue(stages + WSTAGE, src, xb + kblock(1), wb + kblock(1), wave);
-    int s_cur = 0;
-    for (int kb = 0; kb < nkb; ++kb) {
-        wait_vmcnt<5>();
-        lds_barrier();
-        const int s_ld = s_cur == 0 ? 2 : s_cur - 1;
-        const int k2 = kblock(kb + 2);
-        bf16 *ld = stages + s_ld * WSTAGE;
-        const bf16 *cur = stages + s_cur * WSTAGE;
-        WFr f0, f1;
-        wide_read(f0, cur, 0, lane, wt, wf);
-        wide_read(f1, cur, 1, lane, wt, wf);
+    // k-loop over two stages of 64 channels: step kb waits for its own loads,
+    // barriers (every wave is also done with kb-1, whose stage takes kb+1), then
+    // runs four k-steps of 12 MFMAs, reading the next k-step's fragments into the
+    // other register set, with kb+1's ten direct loads spread between the MFMAs.
+    {
 #pragma unroll
-        for (int i = 0; i < 24; ++i) {
-            const WFr &F = i < 12 ? f0 : f1;
-            const int ft = (i % 12) / 4, tt = i % 4;
-            acc[ft][tt] = mfma32x32x16(F.a[ft], F.b[tt], acc[ft][tt]);
-            if (i % 5 == 1) {
-                const int n = i / 5;   // loads 0..4 after MFMAs 1, 6, 11, 16, 21
-                if (n < 2) dma16_async_s(xb + k2, src.off[n], ld + (8 * n + wave) * 64 * 8);
-                else dma16_async_s(wb + k2, src.off[n], ld + WA + (8 * (n - 2) + wave) * 64 * 8);
+        for (int i = 0; i < WLOADS; ++i) wide_load(i, stages, src, xb, wb, wave);
+    }
+    for (int kb = 0; kb < nkb; ++kb) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        const bf16 *cur = stages + (kb & 1) * WSTAGE;
+        bf16 *ld = stages + ((kb + 1) & 1) * WSTAGE;
+        const int k1 = kblock(kb + 1);
+        WFr fr[2];
+        wide_read(fr[0], cur, 0, lane, wt, wf);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) wide_read(fr[(s + 1) & 1], cur, s + 1, lane, wt, wf);
+#pragma unroll
+            for (int j = 0; j < 12; ++j) {
+                const int i = 12 * s + j, ft = j / 4, tt = j % 4;
+                acc[ft][tt] = mfma32x32x16(fr[s & 1].a[ft], fr[s & 1].b[tt], acc[ft][tt]);
+                if (i % 4 == 1 && i / 4 < WLOADS) wide_load(i / 4, ld, src, xb + k1, wb + k1, wave);
             }
         }
-        s_cur = s_cur == 2 ? 0 : s_cur + 1;
     }
     wait_vmcnt<0>();   // the re-reads past the end land before LDS is reused
     __syncthreads();
