@@ -2,8 +2,8 @@
 """Benchmark of the looped gated-delta-rule (GDN) mixer on one MI355X.
 
 One step = one gdn_loop_prefill call: T = 4 weight-tied loops, each running the projection GEMM with its
-fused epilogue and the gate launch, the chunk prep, the sequential state pass and the parallel output pass
-with the fused loop residual, over the 4096-token,
+fused epilogue and the gate launch, the chunk prep and the carry (the sequential state chain with the chunk
+outputs and the loop residual computed a chunk behind inside the same workgroups), over the 4096-token,
 16-head, width-2048 bf16 prompt (B=1, L=4096, H=16, dk=dv=128, T=4, alpha in (0.9, 1)).  Inputs are seeded
 synthetic draws (synth.prefill_inputs) resident in HBM before timing starts.
 
@@ -114,7 +114,7 @@ def bench_prefill(args, w, torch, gl, synth):
     torch.cuda.synchronize()
 
     stages = {"project": gl.GDN_STAGE_PROJECT, "gates": gl.GDN_STAGE_GATES, "scan_prep": gl.GDN_STAGE_SCAN_PREP,
-              "scan_state": gl.GDN_STAGE_SCAN_CARRY, "scan_out": gl.GDN_STAGE_SCAN_OUT}
+              "scan_carry": gl.GDN_STAGE_SCAN_CARRY}
 
     def timed_pass(names):
         """args.steps steps with the dispatch events of the named stages armed; (ms total, per-stage)."""

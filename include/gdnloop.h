@@ -183,7 +183,10 @@ const char *gdn_version(void);
 /* Stages that a timer can bracket. */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
        GDN_STAGE_DECODE = 3, GDN_STAGE_SCAN_OUT = 4, GDN_STAGE_GATES = 5 };
-/* GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
+/* GDN_STAGE_SCAN_CARRY times the carry kernel, which computes the chunk outputs
+ * (and the loop residual) as well; GDN_STAGE_SCAN_OUT names no launch any more
+ * and is kept so that stage numbers stay stable (a timer on it records none).
+ * GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
  * more tokens the gates alpha/beta leave the GEMM for a launch of their own,
  * timed as GDN_STAGE_GATES (shorter inputs compute them inside the GEMM). */
 

@@ -55,15 +55,11 @@ struct ChunkWs {
     float *W;    // per chunk: bf16 hi plane [D][64] then bf16 lo plane [D][64] (D*64*4 bytes)
     float *M;    // per chunk: bf16 hi plane [64][64] then bf16 lo plane [64][64]
     float *g;    // per chunk: gamma [64] fp32
-    bf16 *sc;    // per chunk: chunk-start state as bf16 hi/lo MFMA fragments (D*D*4 bytes)
-    uint4 *e;    // per chunk: E = V - diag(gamma) K S as bf16 hi/lo MFMA fragments (64*D*4 bytes)
 };
-// Bytes of the sc and e regions for `chunk_heads` (b, h, chunk) triples.
-size_t carry_ws_bytes(bool f32, int D, int64_t chunk_heads);
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
                             const float *alpha, const float *beta, ChunkWs ws, hipStream_t s);
 
-// Outputs of the output pass: either `o` (scan form) or the loop residual
+// Outputs of the carry: either `o` (scan form) or the loop residual
 // h_out = o + rho (.) h_prev with an optional bf16 copy x_next.
 struct CarryOut {
     float *o;              // [B, L, H, D] or nullptr
@@ -73,14 +69,12 @@ struct CarryOut {
     float *h_out;          // [B, L, H*D]
     bf16 *x_next;          // [B, L, H*D] or nullptr
 };
-// State pass: sequential over chunks per (b, h, 16-column slice of S); writes
-// the chunk-start states and E tiles to ws.sc / ws.e and the final state.
-hipError_t launch_scan_state(bool f32, int B, int L, int H, int D, const void *k, const void *v, ChunkWs ws,
-                             const float *s_init, float *s_final, hipStream_t s);
-// Output pass: parallel over (b, h, chunk): O = diag(gamma) Q S_c + M E and the
-// residual / output stores.
-hipError_t launch_scan_out(bool f32, int B, int L, int H, int D, const void *q, ChunkWs ws, CarryOut out,
-                           hipStream_t s);
+// Carry: sequential over chunks per (b, h, 16-column slice of S); the chain
+// updates the state, output waves of the same workgroup form
+// O = diag(gamma) Q S_c + M E a chunk behind and write `out`; final state to
+// s_final.
+hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,
+                             ChunkWs ws, const float *s_init, float *s_final, CarryOut out, hipStream_t s);
 
 // One recurrent token per sequence; states updated in place.  With
 // h_out != nullptr the loop residual is applied as in CarryOut.

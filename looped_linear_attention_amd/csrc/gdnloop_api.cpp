@@ -85,7 +85,7 @@ gdn_status check_desc(const gdn_desc *d, bool decode) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, W = 0, M = 0, g = 0, sc = 0, x = 0, total = 0;
+    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, W = 0, M = 0, g = 0, x = 0, total = 0;
 };
 
 Layout layout(const gdn_desc *d, int op) {
@@ -114,7 +114,6 @@ Layout layout(const gdn_desc *d, int op) {
         lo.W = take(bh * Nc * D * CHUNK * 4);
         lo.M = take(bh * Nc * CHUNK * CHUNK * 4);
         lo.g = take(bh * Nc * CHUNK * 4);
-        lo.sc = take(carry_ws_bytes(d->act == GDN_F32, (int)D, bh * Nc));
     }
     lo.total = off;
     return lo;
@@ -234,21 +233,15 @@ static gdn_status scan_chunks(const gdn_desc *d, const void *q, const void *k, c
                               float *s_final, CarryOut out, void *ws, const Layout &lo,
                               hipStream_t s) {
     const bool f32 = d->act == GDN_F32;
-    const int64_t Nc = (d->L + CHUNK - 1) / CHUNK, heads = (int64_t)d->B * d->H;
-    // the E tiles follow the chunk-start states inside the sc region
-    const size_t sc_bytes = (size_t)heads * Nc * d->dk * d->dv * 4;
-    ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g),
-               (bf16 *)at(ws, lo.sc), (uint4 *)at(ws, lo.sc + sc_bytes)};
+    ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g)};
     hipError_t e = timed(GDN_STAGE_SCAN_PREP, s, [&] {
         return launch_scan_prep(f32, d->B, d->L, d->H, d->dk, q, k, alpha, beta, cw, s);
     });
     if (e != hipSuccess) return hip_fail(e, "chunk prep launch");
     e = timed(GDN_STAGE_SCAN_CARRY, s, [&] {
-        return launch_scan_state(f32, d->B, d->L, d->H, d->dk, k, v, cw, s_init, s_final, s);
+        return launch_scan_carry(f32, d->B, d->L, d->H, d->dk, q, k, v, cw, s_init, s_final, out, s);
     });
-    if (e != hipSuccess) return hip_fail(e, "state pass launch");
-    e = timed(GDN_STAGE_SCAN_OUT, s, [&] { return launch_scan_out(f32, d->B, d->L, d->H, d->dk, q, cw, out, s); });
-    if (e != hipSuccess) return hip_fail(e, "output pass launch");
+    if (e != hipSuccess) return hip_fail(e, "carry launch");
     return GDN_OK;
 }
 

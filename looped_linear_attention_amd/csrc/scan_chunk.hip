@@ -401,30 +401,35 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// carry: state pass (sequential over chunks) and output pass (parallel)
+// carry: one kernel per loop, sequential over chunks
 // ---------------------------------------------------------------------------
-// State pass: one workgroup per (b, h, 16-column slice of S); the columns of S
-// never mix, so column slices are independent scans.  Wave w keeps RW = D/4
-// rows of the fp32 state slice in registers.  Lane l = lr + 16 g holds column
-// lr and, in tile tt of its rows, the rows
-//     srow(w, g, tt, j) = RW w + 4 NT g + 4 tt + j,   j = 0..3,
-// so the KW rows a lane contributes to the K.S product are contiguous
-// (RW w + KW g .. + KW) and its K fragment is one contiguous run of a token
-// row.  Row order inside an MFMA output tile is free, so the W fragments that
-// update S (written by the prep kernel) put S row srow(w, g, tt, j) at output
-// row 4 g + j of tile tt.  Per chunk: the wave's partial K.S over its rows,
-// reduce-scatter through LDS (wave w owns tokens 16w..16w+15), E = V -
-// diag(gamma) K S for its tokens, all-gather of the E tiles through LDS, then
-// S' = gamma_C S + W E on its rows.  The chunk-start state and the E tiles go
-// to the workspace in the exact register order in which the output pass uses
-// them as MFMA operands.  The K tile, the V slice and gamma are copied global
-// -> LDS with direct loads a chunk ahead (double-buffered); the wave's W
-// fragments come straight into registers, also a chunk ahead.
-//
-// Output pass: one workgroup per (b, h, chunk), computing
-//     O = diag(gamma) Q S_c + M E   (S_c the chunk-start state)
-// and either O itself or the loop residual h = O + rho (.) h_prev (with a bf16
-// copy for the next loop's projection).  Fully parallel over chunks.
+// One workgroup per (b, h, 16-column slice of S); the columns of S never mix,
+// so column slices are independent scans.  Nine waves:
+//   waves 0-3  the chain.  Wave w keeps RW = D/4 rows of the fp32 state slice in
+//              registers.  Lane l = lr + 16 g holds column lr and, in tile tt of
+//              its rows, the rows
+//                  srow(w, g, tt, j) = RW w + 4 NT g + 4 tt + j,   j = 0..3,
+//              so the KW rows a lane contributes to the K.S product are
+//              contiguous (RW w + KW g .. + KW) and its K fragment is one
+//              contiguous run of a token row.  Row order inside an MFMA output
+//              tile is free, so the W fragments that update S (written by the
+//              prep kernel) put S row srow(w, g, tt, j) at output row 4 g + j of
+//              tile tt.  Per chunk: the chunk-start state S_c (split) into LDS,
+//              the wave's partial K.S over its rows, reduce-scatter through LDS
+//              (wave w owns tokens 16w..16w+15), E = V - diag(gamma) K S_c for its
+//              tokens into LDS, then S' = gamma_C S + W E on its rows.
+//   wave 4     the producer: issues every direct load of the chain (K tile, V
+//              slice, gamma, W fragments) into double-buffered LDS stages.
+//   waves 5-8  the output: wave 5 + o computes, for tokens 16 o .. 16 o + 15 of
+//              chunk cc - 1 while the chain works on chunk cc,
+//                  O = diag(gamma) Q S_c + M E
+//              from S_c and E in LDS (both double-buffered) and Q, M, gamma,
+//              h_prev loaded a chunk ahead into registers, and writes O itself or
+//              the loop residual h = O + rho (.) h_prev (with a bf16 copy for the
+//              next loop's projection).
+// S_c and E never leave the CU.  The products use split-bf16 operands (x = hi
+// + lo, ~16 significant bits) with fp32 accumulation; exact bf16 inputs are not
+// split.
 template <int D, typename TIn> struct CarryCfg {
     static constexpr int RW = D / 4;                     // state rows per wave
     static constexpr int NT = RW / 16;                   // 16-row tiles per wave
@@ -441,11 +446,11 @@ template <int D, typename TIn> struct CarryCfg {
     static constexpr int W_BYTES = D * C * 4;            // W hi and lo parts of one chunk
     static constexpr int W_INS = W_BYTES / 1024;
     static constexpr int KVG_INS = K_INS + V_INS + 1;     // K tile, V slice, gamma
-    // workspace elements per (b, h, chunk): chunk-start state, hi and lo bf16
-    // planes as [slice][wave][part][lane][KW]; E tiles as [slice][tile][lane] of
-    // 16 bytes (4 bf16 hi then 4 bf16 lo)
-    static constexpr int64_t SC_ELEMS = (int64_t)NSL * 4 * 2 * 64 * KW;   // bf16
-    static constexpr int64_t E_BYTES = (int64_t)NSL * 4 * 64 * 16;
+    // one chunk-start state slice as [wave][part: hi, lo][lane][KW] bf16
+    static constexpr int SC_BYTES = 4 * 2 * 64 * KW * 2;
+    // LDS stages of the chain's operands: two when they fit beside the rest
+    static constexpr int STG = 2 * (TILE + W_BYTES + C * VROWB + C * 4) + 16384 + 2 * 4096 + 2 * SC_BYTES <=
+                                       160 * 1024 ? 2 : 1;
 };
 
 // physical 16-byte chunk of logical chunk c in row r of a K tile
@@ -584,38 +589,50 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
     return mfma16x16x32(al, bh, c);
 }
 
-// State pass.  Waves 0-3 compute; wave 4 only issues direct loads, so the
-// compute waves never stall behind the memory pipeline's issue queue.  Per
-// chunk cc, three workgroup barriers:
-//   B0  K, V, gamma of chunk cc have landed; the compute waves are done with
-//       chunk cc-1.  Compute: store the chunk-start state, K.S partials.
-//       Producer: issue K, V, gamma of chunk cc+1 into the other stage.
-//   B1  partials visible; W of chunk cc has landed.  Compute: reduce, form and
-//       store E, read W fragments.  Producer: issue W of chunk cc+1 into the
-//       other W stage (its last reader, chunk cc-1, passed B1 before B0).
-//   B2  E visible.  Compute: S = gamma_C S + W E.
-// So K, V, gamma get one chunk to land and W gets one chunk as well, shifted
-// by one barrier; the producer's two issue bursts overlap the compute phases
-// instead of delaying a barrier.  Past the last chunk the producer re-reads
-// the last chunk into the idle stages, so its wait counts never change, and
-// it drains its loads before it exits.
-constexpr int STATE_THREADS = 320;
+// Barrier schedule per chunk cc (all nine waves take part in each):
+//   B0  K, V, gamma of chunk cc have landed; the chain is done with chunk cc-1.
+//       Chain: S_c into LDS, K.S partials.  Producer (two stages): K, V, gamma of
+//       cc+1 into the other stage.  Output: loads of chunk cc into registers.
+//   B1  partials and S_c visible; W of chunk cc has landed.  Chain: reduce, E
+//       into LDS, W fragments.  Producer (two stages): W of cc+1 into the other W
+//       stage (its last reader, chunk cc-1, passed B1 before B0).  Output: chunk
+//       cc-1 from S_c, E of cc-1 and the registers loaded during cc-1, stores.
+//   B2  E visible.  Chain: S = gamma_C S + W E.  Producer (one stage): every
+//       load of chunk cc+1, into the stage chunk cc no longer reads.
+// With two stages, K, V, gamma get one chunk to land and W one chunk as well,
+// shifted by one barrier; past the last chunk the producer re-reads the last
+// chunk into the idle stages, so its wait counts never change, and it drains
+// its loads before it exits.  S_c of chunk cc is rewritten at chunk cc+2 (after
+// B0) and E at chunk cc+2 (after B1), after the output waves used them at cc+1.
+constexpr int CARRY_THREADS = 576;
 
-template <int D, typename TIn>
-__global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
-    const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc, const float *W,
-    const float *g, const float *__restrict__ s_init, float *__restrict__ s_final,
-    bf16 *__restrict__ sc_ws, uint4 *__restrict__ e_ws) {
+// Inputs of one output step held in registers: Q fragments of the wave's 16
+// tokens, M fragments, gamma of the lane's 4 tokens and h_prev at the lane's
+// 4 (token, column) cells.
+template <int D, typename TIn> struct OutIn {
+    TIn qa[4][CarryCfg<D, TIn>::KW];
+    bf16x8 mh[2], ml[2];
+    f32x4 gv;
+    float hp[4];
+};
+
+template <int D, typename TIn, int RES, bool XN>
+__global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc,
+    const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
+    float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
+    float *h_out, bf16 *x_next) {
     using G = CarryCfg<D, TIn>;
-    constexpr int NT = G::NT, RW = G::RW, KW = G::KW;
+    constexpr int NT = G::NT, RW = G::RW, KW = G::KW, STG = G::STG;
     // every stage is an object of its own, so the compiler can tell the buffers
     // a chunk reads from the ones the next chunk's direct loads write
-    __shared__ __attribute__((aligned(16))) unsigned char k0_s[G::TILE], k1_s[G::TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char w0_s[G::W_BYTES], w1_s[G::W_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[C * G::VROWB];
-    __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[C];
+    __shared__ __attribute__((aligned(16))) unsigned char k0_s[G::TILE], k1_s[STG == 2 ? G::TILE : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char w0_s[G::W_BYTES], w1_s[STG == 2 ? G::W_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[STG == 2 ? C * G::VROWB : 16];
+    __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[STG == 2 ? C : 4];
     __shared__ __attribute__((aligned(16))) f32x4 red[4][4][64];   // [source wave][token tile][lane]
-    __shared__ __attribute__((aligned(16))) uint4 ex[4][64];       // [token tile][lane]: E hi | lo
+    __shared__ __attribute__((aligned(16))) uint4 ex[2][4][64];    // [chunk parity][token tile][lane]: E hi | lo
+    __shared__ __attribute__((aligned(16))) unsigned char sc_s[2][G::SC_BYTES];   // [chunk parity] S_c
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -633,15 +650,24 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
         const unsigned lgm[2] = {lds_addr(g0_s), lds_addr(g1_s)}, lw[2] = {lds_addr(w0_s), lds_addr(w1_s)};
         const KvOffsets<D, TIn> off = kv_offsets<D, TIn>(H, lane);
         auto pstep = [&](auto stc, int cc) __attribute__((always_inline)) {
-            constexpr int NX = 1 - decltype(stc)::value;   // stage that receives chunk cc+1
+            constexpr int NX = STG == 2 ? 1 - decltype(stc)::value : 0;   // stage that receives chunk cc+1
             const int nx = min(cc + 1, Nc - 1);
-            wait_vmcnt<G::W_INS>();     // K, V, gamma of cc landed (W of cc may be in flight)
-            lds_barrier();              // B0
-            state_produce_kvg<D, TIn>(lk[NX], lv[NX], lgm[NX], nx, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
-            wait_vmcnt<G::KVG_INS>();   // W of cc landed (K, V, gamma of cc+1 may be in flight)
-            lds_barrier();              // B1
-            state_produce_w<D, TIn>(lw[NX], nx, W, cidb, lane);
-            __builtin_amdgcn_s_barrier();   // B2
+            if constexpr (STG == 2) {
+                wait_vmcnt<G::W_INS>();     // K, V, gamma of cc landed (W of cc may be in flight)
+                lds_barrier();              // B0
+                state_produce_kvg<D, TIn>(lk[NX], lv[NX], lgm[NX], nx, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
+                wait_vmcnt<G::KVG_INS>();   // W of cc landed (K, V, gamma of cc+1 may be in flight)
+                lds_barrier();              // B1
+                state_produce_w<D, TIn>(lw[NX], nx, W, cidb, lane);
+                lds_barrier();              // B2
+            } else {
+                wait_vmcnt<0>();            // every load of cc landed
+                lds_barrier();              // B0
+                lds_barrier();              // B1
+                lds_barrier();              // B2: chunk cc's stage is no longer read
+                state_produce_kvg<D, TIn>(lk[0], lv[0], lgm[0], nx, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
+                state_produce_w<D, TIn>(lw[0], nx, W, cidb, lane);
+            }
         };
         state_produce_kvg<D, TIn>(lk[0], lv[0], lgm[0], 0, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
         state_produce_w<D, TIn>(lw[0], 0, W, cidb, lane);
@@ -653,7 +679,97 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
         return;
     }
 
-    // state slice: Sv[tt][j] = S[RW wave + 4 NT lg + 4 tt + j][col]
+    if (wave >= 5) {
+        // output waves: tokens 16 ot .. 16 ot + 15 of each chunk, this slice's columns
+        const int ot = wave - 5;
+        const int d = H * D;
+        const float rho_c = RES ? rho[h * D + col] : 0.f;
+        // loads of chunk cc into registers (rows past the end of the sequence read
+        // the last row; their results are never stored)
+        auto load_in = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
+            const int c0 = cc * C, last = L - 1 - c0;
+            const int64_t cid = cidb + cc;
+            const TIn *qrow = q + ((tokb + c0 + min(16 * ot + lr, last)) * H + h) * D + KW * lg;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) __builtin_memcpy(in.qa[ks], qrow + RW * ks, KW * sizeof(TIn));
+            const bf16x8 *Mf = reinterpret_cast<const bf16x8 *>(M + cid * C * C) + lane;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                in.mh[s] = Mf[((ot * 2 + s) * 2 + 0) * 64];
+                in.ml[s] = Mf[((ot * 2 + s) * 2 + 1) * 64];
+            }
+            in.gv = *reinterpret_cast<const f32x4 *>(g + cid * C + 16 * ot + 4 * lg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                in.hp[j] = 0.f;
+                if constexpr (RES != 0) {
+                    const int64_t off = (tokb + c0 + min(16 * ot + 4 * lg + j, last)) * (int64_t)d + (int64_t)h * D + col;
+                    if constexpr (RES == 2) in.hp[j] = (float)static_cast<const bf16 *>(h_prev)[off];
+                    else in.hp[j] = static_cast<const float *>(h_prev)[off];
+                }
+            }
+        };
+        // output step of chunk cc from the LDS buffers of parity P
+        auto compute = [&](auto pc, const OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
+            const int c0 = cc * C;
+            const bf16 *scs = reinterpret_cast<const bf16 *>(sc_s[P]) + lane * KW;
+            f32x4 qs = {0.f, 0.f, 0.f, 0.f}, me = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                __bf16 sh[KW], sl[KW];
+                __builtin_memcpy(sh, scs + (ks * 2 + 0) * 64 * KW, 2 * KW);
+                __builtin_memcpy(sl, scs + (ks * 2 + 1) * 64 * KW, 2 * KW);
+                qs = mma_a<KW>(in.qa[ks], sh, sl, qs);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint4 a4 = ex[P][2 * s][lane], c4 = ex[P][2 * s + 1][lane];
+                const uint4 hi = make_uint4(a4.x, a4.y, c4.x, c4.y), lo = make_uint4(a4.z, a4.w, c4.z, c4.w);
+                bf16x8 ebh, ebl;
+                __builtin_memcpy(&ebh, &hi, 16);
+                __builtin_memcpy(&ebl, &lo, 16);
+                me = mma_hl(in.mh[s], in.ml[s], ebh, ebl, me);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ot + 4 * lg + j;
+                if (c0 + r >= L) continue;
+                const float ov = in.gv[j] * qs[j] + me[j];
+                const int64_t row = tokb + c0 + r;
+                if constexpr (RES == 0) {
+                    o[(row * H + h) * D + col] = ov;
+                } else {
+                    const float hv = ov + rho_c * in.hp[j];
+                    const int64_t hi = row * d + (int64_t)h * D + col;
+                    h_out[hi] = hv;
+                    if constexpr (XN) x_next[hi] = (bf16)hv;
+                }
+            }
+        };
+        OutIn<D, TIn> in0, in1;
+        // one chunk per step, two per iteration so that the register set and the
+        // LDS parity are compile-time choices
+        auto ostep = [&](auto pc, OutIn<D, TIn> &cur, const OutIn<D, TIn> &prev, int cc)
+            __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;   // parity of chunk cc
+            lds_barrier();   // B0
+            load_in(cur, cc);
+            lds_barrier();   // B1
+            if (cc > 0) compute(std::integral_constant<int, 1 - P>(), prev, cc - 1);
+            lds_barrier();   // B2
+        };
+        for (int cc = 0; cc < Nc; cc += 2) {
+            ostep(std::integral_constant<int, 0>(), in0, in1, cc);
+            if (cc + 1 < Nc) ostep(std::integral_constant<int, 1>(), in1, in0, cc + 1);
+        }
+        // the last chunk: its S_c and E stay in LDS, nobody rewrites them
+        if ((Nc - 1) & 1) compute(std::integral_constant<int, 1>(), in1, Nc - 1);
+        else compute(std::integral_constant<int, 0>(), in0, Nc - 1);
+        return;
+    }
+
+    // chain waves.  state slice: Sv[tt][j] = S[RW wave + 4 NT lg + 4 tt + j][col]
     float Sv[NT][4];
     const int64_t sbase = ((int64_t)b * H + h) * D * D;
 #pragma unroll
@@ -662,28 +778,27 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
         for (int j = 0; j < 4; ++j)
             Sv[tt][j] = s_init ? s_init[sbase + (int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] : 0.f;
     // Nothing loaded before the loop may be pending inside it: otherwise the
-    // compiler's wait for these registers lands in the loop body, where it
-    // would also wait for every chunk's stores.
+    // compiler's wait for these registers lands in the loop body.
     wait_vmcnt<0>();
 
-    // One chunk step on LDS stage ST (= cc mod 2).  Two steps per loop iteration
-    // so that the stage is a compile-time constant.
-    auto step = [&](auto stc, int cc) __attribute__((always_inline)) {
-        constexpr int ST = decltype(stc)::value;
+    // One chunk step on LDS stage ST (= cc mod 2 with two stages).  Two steps per
+    // loop iteration so that stage and parity are compile-time constants.
+    auto step = [&](auto pc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        constexpr int ST = STG == 2 ? P : 0;
         const unsigned char *k_cur = ST == 0 ? k0_s : k1_s;
         const unsigned char *v_cur = ST == 0 ? v0_s : v1_s;
         const float *g_cur = ST == 0 ? g0_s : g1_s;
         const bf16x8 *w_cur = reinterpret_cast<const bf16x8 *>(ST == 0 ? w0_s : w1_s) + wave * NT * 4 * 64 + lane;
         lds_barrier();   // (B0) chunk cc's loads have landed; chunk cc-1's stage is free
-        const int64_t cid = cidb + cc;
-        // chunk-start state as the B operand of K.S (and of Q.S in the output pass)
+        // chunk-start state as the B operand of K.S (and, in LDS, of Q.S for the output waves)
         __bf16 sh[KW], sl[KW];
         {
             float sf[KW];
 #pragma unroll
             for (int i = 0; i < KW; ++i) sf[i] = Sv[i / 4][i % 4];
             split_bf16(sf, sh, sl);
-            bf16 *dst = sc_ws + cid * G::SC_ELEMS + (((int64_t)slice * 4 + wave) * 2 * 64 + lane) * KW;
+            bf16 *dst = reinterpret_cast<bf16 *>(sc_s[P]) + (wave * 2 * 64 + lane) * KW;
             __builtin_memcpy(dst, sh, 2 * KW);
             __builtin_memcpy(dst + 64 * KW, sl, 2 * KW);
         }
@@ -698,7 +813,7 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)
             if (tm != wave) red[wave][tm][lane] = ks[tm];
-        lds_barrier();   // (B1) partials visible; W of chunk cc has landed
+        lds_barrier();   // (B1) partials and S_c visible; W of chunk cc has landed
         f32x4 kt = ks[0];
 #pragma unroll
         for (int tm = 1; tm < 4; ++tm)
@@ -725,26 +840,25 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
             else vv = reinterpret_cast<const float *>(v_cur)[r * 16 + lr];
             e[j] = vv - g_cur[r] * kt[j];
         }
+        const float gC = g_cur[C - 1];   // read before B2: with one stage the producer refills it after B2
         {
             __bf16 eh[4], el[4];
             split_bf16(e, eh, el);
             uint4 u;
             __builtin_memcpy(&u.x, eh, 8);
             __builtin_memcpy(&u.z, el, 8);
-            ex[wave][lane] = u;
-            e_ws[(cid * G::NSL + slice) * 4 * 64 + wave * 64 + lane] = u;
+            ex[P][wave][lane] = u;
         }
         lds_barrier();   // (B2) every E tile visible
         // E as the B operand: k-step s covers the token tiles 2s and 2s+1
         bf16x8 ebh[2], ebl[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const uint4 a = ex[2 * s][lane], c = ex[2 * s + 1][lane];
-            uint4 hi = make_uint4(a.x, a.y, c.x, c.y), lo = make_uint4(a.z, a.w, c.z, c.w);
+            const uint4 a4 = ex[P][2 * s][lane], c4 = ex[P][2 * s + 1][lane];
+            uint4 hi = make_uint4(a4.x, a4.y, c4.x, c4.y), lo = make_uint4(a4.z, a4.w, c4.z, c4.w);
             __builtin_memcpy(&ebh[s], &hi, 16);
             __builtin_memcpy(&ebl[s], &lo, 16);
         }
-        const float gC = g_cur[C - 1];
         // S' = gamma_C S + W E (this wave's rows)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -756,8 +870,8 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
         }
     };
     for (int cc = 0; cc < Nc; cc += 2) {
-        step(std::integral_constant<int, 0>(), cc);
-        if (cc + 1 < Nc) step(std::integral_constant<int, 1>(), cc + 1);
+        step(std::integral_constant<int, 0>());
+        if (cc + 1 < Nc) step(std::integral_constant<int, 1>());
     }
     if (s_final) {
 #pragma unroll
@@ -765,136 +879,6 @@ __global__ __launch_bounds__(STATE_THREADS) void k_scan_state(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 s_final[sbase + (int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] = Sv[tt][j];
-    }
-}
-
-// Output pass.  The Q tile, the M fragments, gamma and the h_prev tile come
-// into LDS with coalesced 16-byte loads.  Wave w handles the column slices
-// [w SPW, (w+1) SPW) for all 64 tokens of the chunk: Q.S_c (B operand: the
-// stored chunk-start state, k-step ks = the state rows of state-pass wave ks)
-// and M.E (B operand: the stored E tiles), both split-bf16.  The results go
-// back through the LDS tile, which is then written out as whole 16-byte runs
-// of the output rows (fp32, plus the bf16 copy for the next loop).
-template <int D, typename TIn, int RES> struct OutCfg {
-    static constexpr int QROW = D + 16 / (int)sizeof(TIn);   // padded Q row (elements)
-    static constexpr int OROW = D + 4;                        // padded output row (floats)
-};
-
-template <int D, typename TIn, int RES, bool XN>
-__global__ __launch_bounds__(256) void k_scan_out(
-    const TIn *__restrict__ q, int L, int H, int Nc, const float *__restrict__ M,
-    const float *__restrict__ g, const bf16 *__restrict__ sc_ws, const uint4 *__restrict__ e_ws,
-    float *__restrict__ o, const void *h_prev, const float *__restrict__ rho, float *h_out,
-    bf16 *x_next) {
-    using G = CarryCfg<D, TIn>;
-    using OC = OutCfg<D, TIn, RES>;
-    constexpr int KW = G::KW, NKS = 4;                   // Q.S k-steps: one per state-pass wave
-    constexpr int SPW = G::NSL / 4;                      // slices per wave
-    __shared__ __attribute__((aligned(16))) TIn Qs[C * OC::QROW];
-    __shared__ __attribute__((aligned(16))) bf16x8 Ms[4 * 2 * 2 * 64];   // [tile][s][part][lane]
-    __shared__ __attribute__((aligned(16))) float Os[C * OC::OROW];      // h_prev in, result out
-    __shared__ float gs[C];
-
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int lr = lane & 15, lg = lane >> 4;
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int c0 = chunk * C, nvalid = min(C, L - c0);
-    const int64_t tokb = (int64_t)b * L;
-    const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
-    const int d = H * D;
-
-    // (1) cooperative loads (rows past the end of the sequence are left unset:
-    // they only feed results that are never stored)
-    {
-        constexpr int EPC = 16 / (int)sizeof(TIn), CPR = D / EPC;
-        for (int idx = t; idx < nvalid * CPR; idx += 256) {
-            const int r = idx / CPR, c = idx % CPR;
-            *reinterpret_cast<uint4 *>(Qs + r * OC::QROW + c * EPC) =
-                *reinterpret_cast<const uint4 *>(q + ((tokb + c0 + r) * H + h) * D + c * EPC);
-        }
-        const uint4 *Mg = reinterpret_cast<const uint4 *>(M + cid * C * C);
-        for (int idx = t; idx < 4 * 2 * 2 * 64; idx += 256) reinterpret_cast<uint4 *>(Ms)[idx] = Mg[idx];
-        if (t < C) gs[t] = g[cid * C + t];
-        if constexpr (RES != 0) {
-            constexpr int HEPC = RES == 2 ? 8 : 4, HCPR = D / HEPC;   // elements per 16 bytes
-            for (int idx = t; idx < nvalid * HCPR; idx += 256) {
-                const int r = idx / HCPR, c = idx % HCPR;
-                const int64_t off = (tokb + c0 + r) * (int64_t)d + (int64_t)h * D + c * HEPC;
-                float *dst = Os + r * OC::OROW + c * HEPC;
-                if constexpr (RES == 2) {
-                    const bf16x8 u = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(h_prev) + off);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) dst[i] = (float)u[i];
-                } else {
-                    *reinterpret_cast<float4 *>(dst) = *reinterpret_cast<const float4 *>(static_cast<const float *>(h_prev) + off);
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int si = 0; si < SPW; ++si) {
-        const int slice = wave * SPW + si, col = slice * 16 + lr;
-        // chunk-start state and E B fragments (lane-contiguous, straight from the workspace)
-        __bf16 sh[NKS][KW], sl[NKS][KW];
-        const bf16 *scs = sc_ws + cid * G::SC_ELEMS + (int64_t)slice * 4 * 2 * 64 * KW + lane * KW;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            __builtin_memcpy(sh[ks], scs + (int64_t)(ks * 2 + 0) * 64 * KW, 2 * KW);
-            __builtin_memcpy(sl[ks], scs + (int64_t)(ks * 2 + 1) * 64 * KW, 2 * KW);
-        }
-        bf16x8 ebh[2], ebl[2];
-        const uint4 *es = e_ws + (cid * G::NSL + slice) * 4 * 64 + lane;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint4 a = es[(2 * s) * 64], c = es[(2 * s + 1) * 64];
-            uint4 hi = make_uint4(a.x, a.y, c.x, c.y), lo = make_uint4(a.z, a.w, c.z, c.w);
-            __builtin_memcpy(&ebh[s], &hi, 16);
-            __builtin_memcpy(&ebl[s], &lo, 16);
-        }
-        const float rho_c = RES ? rho[h * D + col] : 0.f;
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            f32x4 qs = {0.f, 0.f, 0.f, 0.f}, me = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                TIn qa[KW];
-                __builtin_memcpy(qa, Qs + (16 * tm + lr) * OC::QROW + G::RW * ks + KW * lg, KW * sizeof(TIn));
-                qs = mma_a<KW>(qa, sh[ks], sl[ks], qs);
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                me = mma_hl(Ms[((tm * 2 + s) * 2 + 0) * 64 + lane], Ms[((tm * 2 + s) * 2 + 1) * 64 + lane],
-                            ebh[s], ebl[s], me);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * tm + 4 * lg + j;
-                const float ov = gs[r] * qs[j] + me[j];
-                float *cell = Os + r * OC::OROW + col;
-                if constexpr (RES == 0) *cell = ov;
-                else *cell = ov + rho_c * *cell;
-            }
-        }
-    }
-    __syncthreads();
-    // (3) whole rows out: fp32 result (o or h_out) and the bf16 copy
-    for (int idx = t; idx < nvalid * (D / 4); idx += 256) {
-        const int r = idx / (D / 4), c = idx % (D / 4);
-        const float4 v4 = *reinterpret_cast<const float4 *>(Os + r * OC::OROW + 4 * c);
-        const int64_t row = tokb + c0 + r;
-        if constexpr (RES == 0) {
-            *reinterpret_cast<float4 *>(o + (row * H + h) * D + 4 * c) = v4;
-        } else {
-            const int64_t hi = row * d + (int64_t)h * D + 4 * c;
-            *reinterpret_cast<float4 *>(h_out + hi) = v4;
-            if constexpr (XN) {
-                bf16x4 x4;
-                x4[0] = (bf16)v4.x; x4[1] = (bf16)v4.y; x4[2] = (bf16)v4.z; x4[3] = (bf16)v4.w;
-                *reinterpret_cast<bf16x4 *>(x_next + hi) = x4;
-            }
-        }
     }
 }
 
@@ -916,57 +900,29 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
     return hipGetLastError();
 }
 
-size_t carry_ws_bytes(bool f32, int D, int64_t chunk_heads) {
-    int64_t sc = 0, e = 0;
-    if (f32) {
-        if (D == 128) { sc = CarryCfg<128, float>::SC_ELEMS; e = CarryCfg<128, float>::E_BYTES; }
-        else { sc = CarryCfg<64, float>::SC_ELEMS; e = CarryCfg<64, float>::E_BYTES; }
-    } else {
-        if (D == 128) { sc = CarryCfg<128, bf16>::SC_ELEMS; e = CarryCfg<128, bf16>::E_BYTES; }
-        else { sc = CarryCfg<64, bf16>::SC_ELEMS; e = CarryCfg<64, bf16>::E_BYTES; }
-    }
-    return (size_t)chunk_heads * (size_t)(sc * 2 + e);
-}
-
-hipError_t launch_scan_state(bool f32, int B, int L, int H, int D, const void *k, const void *v, ChunkWs ws,
-                             const float *s_init, float *s_final, hipStream_t s) {
+hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,
+                             ChunkWs ws, const float *s_init, float *s_final, CarryOut out, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     dim3 grid(H, D / 16, B);
-#define STATE(DD, T)                                                                               \
-    launch_kernel((k_scan_state<DD, T>), grid, dim3(STATE_THREADS), 0, s, (const T *)k, (const T *)v, L, H, Nc, \
-                  (const float *)ws.W, (const float *)ws.g, s_init, s_final, ws.sc, ws.e)
-    if (f32) {
-        if (D == 128) STATE(128, float); else STATE(64, float);
-    } else {
-        if (D == 128) STATE(128, bf16); else STATE(64, bf16);
-    }
-#undef STATE
-    return hipGetLastError();
-}
-
-hipError_t launch_scan_out(bool f32, int B, int L, int H, int D, const void *q, ChunkWs ws, CarryOut out,
-                           hipStream_t s) {
-    const int Nc = (L + C - 1) / C;
-    dim3 grid(Nc, H, B);
     const int res = out.h_out == nullptr ? 0 : (out.h_prev_bf16 ? 2 : 1);
     const bool xn = out.h_out != nullptr && out.x_next != nullptr;
-#define OUT(DD, T, R, X)                                                                           \
-    launch_kernel((k_scan_out<DD, T, R, X>), grid, dim3(256), 0, s, (const T *)q, L, H, Nc,        \
-                  (const float *)ws.M, (const float *)ws.g, (const bf16 *)ws.sc, (const uint4 *)ws.e, \
-                  out.o, out.h_prev, out.rho, out.h_out, out.x_next)
-#define OUT_R(DD, T)                                                                               \
+#define CARRY(DD, T, R, X)                                                                         \
+    launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(CARRY_THREADS), 0, s, (const T *)q, (const T *)k, \
+                  (const T *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
+                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next)
+#define CARRY_R(DD, T)                                                                             \
     do {                                                                                           \
-        if (res == 0) OUT(DD, T, 0, false);                                                        \
-        else if (res == 1) { if (xn) OUT(DD, T, 1, true); else OUT(DD, T, 1, false); }             \
-        else { if (xn) OUT(DD, T, 2, true); else OUT(DD, T, 2, false); }                           \
+        if (res == 0) CARRY(DD, T, 0, false);                                                      \
+        else if (res == 1) { if (xn) CARRY(DD, T, 1, true); else CARRY(DD, T, 1, false); }         \
+        else { if (xn) CARRY(DD, T, 2, true); else CARRY(DD, T, 2, false); }                       \
     } while (0)
     if (f32) {
-        if (D == 128) OUT_R(128, float); else OUT_R(64, float);
+        if (D == 128) CARRY_R(128, float); else CARRY_R(64, float);
     } else {
-        if (D == 128) OUT_R(128, bf16); else OUT_R(64, bf16);
+        if (D == 128) CARRY_R(128, bf16); else CARRY_R(64, bf16);
     }
-#undef OUT_R
-#undef OUT
+#undef CARRY_R
+#undef CARRY
     return hipGetLastError();
 }
 

@@ -92,8 +92,7 @@ def test_workspace_sizes():
     st, n = _ws_status(desc)
     assert st == 0
     tok, Nc = B * L, (L + 63) // 64
-    chunks = (up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
-              + up(B * H * Nc * (D * D + 64 * D) * 4))
+    chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
     exp = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2) + chunks
     assert n == exp
     st, n = _ws_status(desc, gl.GDN_OP_SCAN_PREFILL)
