@@ -424,7 +424,7 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
 //              chunk cc - 1 while the chain works on chunk cc,
 //                  O = diag(gamma) Q S_c + M E
 //              from S_c and E in LDS (both double-buffered) and Q, M, gamma,
-//              h_prev loaded a chunk ahead into registers, and writes O itself or
+//              h_prev loaded about a chunk ahead into registers, and writes O itself or
 //              the loop residual h = O + rho (.) h_prev (with a bf16 copy for the
 //              next loop's projection).
 // S_c and E never leave the CU.  The products use split-bf16 operands (x = hi
@@ -592,13 +592,18 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
 // Barrier schedule per chunk cc (all nine waves take part in each):
 //   B0  K, V, gamma of chunk cc have landed; the chain is done with chunk cc-1.
 //       Chain: S_c into LDS, K.S partials.  Producer (two stages): K, V, gamma of
-//       cc+1 into the other stage.  Output: loads of chunk cc into registers.
+//       cc+1 into the other stage.  Output: M, gamma, h_prev of chunk cc into
+//       registers.
 //   B1  partials and S_c visible; W of chunk cc has landed.  Chain: reduce, E
 //       into LDS, W fragments.  Producer (two stages): W of cc+1 into the other W
 //       stage (its last reader, chunk cc-1, passed B1 before B0).  Output: chunk
 //       cc-1 from S_c, E of cc-1 and the registers loaded during cc-1, stores.
 //   B2  E visible.  Chain: S = gamma_C S + W E.  Producer (one stage): every
-//       load of chunk cc+1, into the stage chunk cc no longer reads.
+//       load of chunk cc+1, into the stage chunk cc no longer reads.  Output:
+//       Q of chunk cc+1 (its M, gamma, h_prev follow after B0 of cc+1).
+// The CU's vector-memory address path is the shared resource: the output
+// waves' loads are split between the windows after B0 and after B2 so that
+// neither holds up the next barrier.
 // With two stages, K, V, gamma get one chunk to land and W one chunk as well,
 // shifted by one barrier; past the last chunk the producer re-reads the last
 // chunk into the idle stages, so its wait counts never change, and it drains
@@ -685,13 +690,16 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         const int d = H * D;
         const float rho_c = RES ? rho[h * D + col] : 0.f;
         // loads of chunk cc into registers (rows past the end of the sequence read
-        // the last row; their results are never stored)
-        auto load_in = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
+        // the last row; their results are never stored): Q, then the rest: Q, then the rest
+        auto load_q = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
             const int c0 = cc * C, last = L - 1 - c0;
-            const int64_t cid = cidb + cc;
             const TIn *qrow = q + ((tokb + c0 + min(16 * ot + lr, last)) * H + h) * D + KW * lg;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) __builtin_memcpy(in.qa[ks], qrow + RW * ks, KW * sizeof(TIn));
+        };
+        auto load_rest = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
+            const int c0 = cc * C, last = L - 1 - c0;
+            const int64_t cid = cidb + cc;
             const bf16x8 *Mf = reinterpret_cast<const bf16x8 *>(M + cid * C * C) + lane;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -750,15 +758,17 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         OutIn<D, TIn> in0, in1;
         // one chunk per step, two per iteration so that the register set and the
         // LDS parity are compile-time choices
-        auto ostep = [&](auto pc, OutIn<D, TIn> &cur, const OutIn<D, TIn> &prev, int cc)
+        auto ostep = [&](auto pc, OutIn<D, TIn> &cur, OutIn<D, TIn> &prev, int cc)
             __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;   // parity of chunk cc
             lds_barrier();   // B0
-            load_in(cur, cc);
+            load_rest(cur, cc);
             lds_barrier();   // B1
             if (cc > 0) compute(std::integral_constant<int, 1 - P>(), prev, cc - 1);
             lds_barrier();   // B2
+            if (cc + 1 < Nc) load_q(prev, cc + 1);
         };
+        load_q(in0, 0);
         for (int cc = 0; cc < Nc; cc += 2) {
             ostep(std::integral_constant<int, 0>(), in0, in1, cc);
             if (cc + 1 < Nc) ostep(std::integral_constant<int, 1>(), in1, in0, cc + 1);
