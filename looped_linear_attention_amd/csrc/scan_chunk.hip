@@ -690,7 +690,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         const int d = H * D;
         const float rho_c = RES ? rho[h * D + col] : 0.f;
         // loads of chunk cc into registers (rows past the end of the sequence read
-        // the last row; their results are never stored): Q, then the rest: Q, then the rest
+        // the last row; their results are never stored): Q, then the rest
         auto load_q = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
             const int c0 = cc * C, last = L - 1 - c0;
             const TIn *qrow = q + ((tokb + c0 + min(16 * ot + lr, last)) * H + h) * D + KW * lg;
