@@ -59,10 +59,12 @@ def proj_flops_per_token(w) -> int:
 
 
 def proj_gemm_kernel(w, tokens):
-    """(kernel name, algorithmic flops per token) of the projection GEMM launch: bf16 inputs of 1024 or more
-    tokens take k_proj_wide, which leaves the 2H gate columns to their own launch."""
+    """(kernel name, algorithmic flops per token) of the projection GEMM launch in the looped prefill: bf16
+    inputs of 1024 or more tokens take k_proj_wide, which also forms the 2H gate pre-activations (as partial
+    sums that the chunk preparation adds up) when 2H <= 32, and leaves them to their own launch otherwise."""
     if w.act == "bf16" and tokens >= 1024:
-        return "k_proj_wide", 2 * w.d * w.H * (2 * w.dk + w.dv)
+        gate_cols = 2 * w.H if 2 * w.H <= 32 else 0
+        return "k_proj_wide", 2 * w.d * (w.H * (2 * w.dk + w.dv) + gate_cols)
     return ("k_proj_bf16" if w.act == "bf16" else "k_proj_f32"), proj_flops_per_token(w)
 
 
@@ -135,7 +137,8 @@ def bench_prefill(args, w, torch, gl, synth):
         per_stage = {}
         for k, t in timers.items():
             n, ms = gl.gdn_timer_read(t)
-            per_stage[k] = dict(launches=n, avg_ms=ms / max(n, 1), share=ms / ms_total)
+            if n:   # the gate stage has no launch when the GEMM forms the gates
+                per_stage[k] = dict(launches=n, avg_ms=ms / n, share=ms / ms_total)
             gl.gdn_timer_destroy(t)
         return ms_total, wall, per_stage
 

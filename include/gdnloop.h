@@ -187,8 +187,11 @@ enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
  * (and the loop residual) as well; GDN_STAGE_SCAN_OUT names no launch any more
  * and is kept so that stage numbers stay stable (a timer on it records none).
  * GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
- * more tokens the gates alpha/beta leave the GEMM for a launch of their own,
- * timed as GDN_STAGE_GATES (shorter inputs compute them inside the GEMM). */
+ * more tokens the gates alpha/beta leave the GEMM's epilogue: gdn_project and
+ * gdn_loop_decode compute them in a launch of their own, timed as
+ * GDN_STAGE_GATES; gdn_loop_prefill with H <= 16 has the GEMM write partial
+ * gate pre-activations (in its workspace) that the chunk preparation sums,
+ * so no gate launch occurs.  Shorter inputs compute the gates inside the GEMM. */
 
 /* While a timer is attached, every launch of its stage carries a pair of HIP
  * events on its dispatch (hipExtLaunchKernel start/stop events), so each pair

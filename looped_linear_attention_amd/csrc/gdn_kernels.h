@@ -40,12 +40,16 @@ hipError_t launch_pack_weights(bool f32, int d, int H, int D, const void *Wq, co
 
 // X[M, d] x Wpack^T with the fused per-head epilogue (L2 norm of q and k,
 // gates alpha/beta, dtype conversion of q/k/v).  When project_separate_gates
-// is true, launch_project writes q, k, v only and launch_gates (an independent
-// launch: both read x) writes alpha and beta.
+// is true, launch_project writes q, k, v only, and the gates come either from
+// launch_gates (an independent launch: both read x), or, with zp != nullptr,
+// from the GEMM itself as gate_partials(...) fp32 partial pre-activations
+// zp[P][2H][M] (P = gate_partials, > 0 required), which the chunk preparation
+// sums and turns into alpha and beta.
 bool project_separate_gates(bool f32, int M);
+int gate_partials(bool f32, int M, int d, int H);
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
-                          float eps, hipStream_t s);
+                          float eps, float *zp, hipStream_t s);
 hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
                         float *beta, float alpha_lo, hipStream_t s);
 
@@ -56,8 +60,17 @@ struct ChunkWs {
     float *M;    // per chunk: bf16 hi plane [64][64] then bf16 lo plane [64][64]
     float *g;    // per chunk: gamma [64] fp32
 };
+// Gates of the chunk preparation: alpha/beta [B*L, H], or (zp != nullptr) the
+// P partial pre-activations zp[P][2H][B*L] of the projection, summed in order
+// p = 0..P-1, with alpha = lo + (1 - lo) sigmoid(-z_a), beta = sigmoid(z_b).
+struct GateSrc {
+    const float *alpha, *beta;
+    const float *zp;
+    int P;
+    float alpha_lo;
+};
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
-                            const float *alpha, const float *beta, ChunkWs ws, hipStream_t s);
+                            GateSrc gates, ChunkWs ws, hipStream_t s);
 
 // Outputs of the carry: either `o` (scan form) or the loop residual
 // h_out = o + rho (.) h_prev with an optional bf16 copy x_next.

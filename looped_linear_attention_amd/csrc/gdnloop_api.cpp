@@ -85,7 +85,8 @@ gdn_status check_desc(const gdn_desc *d, bool decode) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, W = 0, M = 0, g = 0, x = 0, total = 0;
+    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, total = 0;
+    int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
 
 Layout layout(const gdn_desc *d, int op) {
@@ -109,6 +110,10 @@ Layout layout(const gdn_desc *d, int op) {
         lo.alpha = take(tokens * d->H * 4);
         lo.beta = take(tokens * d->H * 4);
         if (d->act == GDN_BF16 && d->T > 1) lo.x = take(tokens * d->d * 2);
+        if (op == GDN_OP_LOOP_PREFILL) {
+            lo.P = gate_partials(d->act == GDN_F32, (int)tokens, d->d, d->H);
+            if (lo.P) lo.zp = take((size_t)lo.P * 2 * d->H * tokens * 4);
+        }
     }
     if (chunks) {
         lo.W = take(bh * Nc * D * CHUNK * 4);
@@ -152,13 +157,13 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
 }
 
 // The projection of M tokens: the GEMM launch, plus the gate launch when the
-// GEMM leaves the gates to it.
+// GEMM leaves the gates to it and does not write gate partials (zp).
 hipError_t project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
-                   void *v, float *al, float *be, float alpha_lo, float eps, hipStream_t s) {
+                   void *v, float *al, float *be, float alpha_lo, float eps, float *zp, hipStream_t s) {
     hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
-        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, s);
+        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, zp, s);
     });
-    if (e == hipSuccess && project_separate_gates(f32, M))
+    if (e == hipSuccess && !zp && project_separate_gates(f32, M))
         e = timed(GDN_STAGE_GATES, s, [&] { return launch_gates(M, d, H, D, x, Wpack, al, be, alpha_lo, s); });
     return e;
 }
@@ -224,18 +229,17 @@ gdn_status gdn_project(const gdn_desc *desc, const void *x, const void *Wpack, v
     const hipStream_t s = (hipStream_t)stream;
     const int M = desc->B * desc->L;
     hipError_t e = project(desc->act == GDN_F32, M, desc->d, desc->H, desc->dk, x, Wpack, q, k, v, alpha,
-                           beta, desc->alpha_lo, desc->norm_eps, s);
+                           beta, desc->alpha_lo, desc->norm_eps, nullptr, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "projection launch");
 }
 
 static gdn_status scan_chunks(const gdn_desc *d, const void *q, const void *k, const void *v,
-                              const float *alpha, const float *beta, const float *s_init,
-                              float *s_final, CarryOut out, void *ws, const Layout &lo,
-                              hipStream_t s) {
+                              GateSrc gates, const float *s_init, float *s_final, CarryOut out, void *ws,
+                              const Layout &lo, hipStream_t s) {
     const bool f32 = d->act == GDN_F32;
     ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g)};
     hipError_t e = timed(GDN_STAGE_SCAN_PREP, s, [&] {
-        return launch_scan_prep(f32, d->B, d->L, d->H, d->dk, q, k, alpha, beta, cw, s);
+        return launch_scan_prep(f32, d->B, d->L, d->H, d->dk, q, k, gates, cw, s);
     });
     if (e != hipSuccess) return hip_fail(e, "chunk prep launch");
     e = timed(GDN_STAGE_SCAN_CARRY, s, [&] {
@@ -258,7 +262,8 @@ gdn_status gdn_scan_prefill(const gdn_desc *desc, const void *q, const void *k, 
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
     if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
     CarryOut out{o, nullptr, false, nullptr, nullptr, nullptr};
-    return scan_chunks(desc, q, k, v, alpha, beta, s_init, s_final, out, ws, lo, (hipStream_t)stream);
+    return scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo}, s_init, s_final, out,
+                       ws, lo, (hipStream_t)stream);
 }
 
 gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k, const void *v,
@@ -295,6 +300,7 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
     const int64_t tokd = (int64_t)M * d;
     void *q = at(ws, lo.q), *k = at(ws, lo.k), *v = at(ws, lo.v);
     float *al = (float *)at(ws, lo.alpha), *be = (float *)at(ws, lo.beta);
+    float *zp = lo.P ? (float *)at(ws, lo.zp) : nullptr;   // gate partials, when the GEMM makes them
     bf16 *xbuf = f32 ? nullptr : (bf16 *)at(ws, lo.x);
     const int64_t state_elems = (int64_t)desc->B * desc->H * D * D;
 
@@ -305,11 +311,11 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
         const bool last = tau == desc->T - 1;
         float *hdst = h_loops ? h_loops + tau * tokd : h_out;  // h^(tau+1), in place over h_out
         hipError_t e = project(f32, M, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                               desc->norm_eps, s);
+                               desc->norm_eps, zp, s);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         CarryOut out{nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, hdst,
                      (!f32 && !last) ? xbuf : nullptr};
-        st = scan_chunks(desc, q, k, v, al, be, nullptr,
+        st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo}, nullptr,
                          states_out ? states_out + tau * state_elems : nullptr, out, ws, lo, s);
         if (st != GDN_OK) return st;
         hprev = hdst;
@@ -348,7 +354,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
     for (int tau = 0; tau < desc->T; ++tau) {
         const bool last = tau == desc->T - 1;
         hipError_t e = project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                               desc->norm_eps, s);
+                               desc->norm_eps, nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         e = timed(GDN_STAGE_DECODE, s, [&] {
             return launch_decode(f32, N, desc->H, D, q, k, v, al, be, states + tau * state_elems,

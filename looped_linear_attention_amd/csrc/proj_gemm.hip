@@ -311,7 +311,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // the per-head norms then sum mostly inside the lane, and results leave as
 // 8-byte pieces of output rows through a staging tile in LDS.
 // With one head per column tile, a sequence of 4096 tokens and 16 heads is
-// exactly 256 tiles, one per CU.  The gate columns run in k_gates.
+// exactly 256 tiles, one per CU.
+// Gate columns (GZ): the 2H <= 32 gate rows are one more 32-row A tile.  Column
+// tile j takes the gate product over channel blocks 2j and 2j+1 (d = H D gives
+// at most two blocks per column tile) and writes it as an fp32 partial
+// zp[j][2H][M]; the consumer sums the partials of a token in tile order.  The
+// k-loop of tile j starts at block 2j, so both gate blocks are in the two
+// stages after the prologue, where the gate MFMAs run before the main
+// accumulators are live.  Without GZ the gate columns run in k_gates.
 constexpr int WM = 256, WN = 384, WK = 64, WSTAGES = 2;
 constexpr int WA = WM * WK, WB = WN * WK, WSTAGE = WA + WB;   // bf16 elements per stage
 constexpr int WOUT_LD = WN + 4;   // bf16 row stride of the output staging tile (776 bytes)
@@ -479,10 +486,10 @@ __device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *s
     }
 }
 
-template <int D>
+template <int D, bool GZ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_proj_wide(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Wp, int M, int K, int H, int m_tiles, int n_tiles,
-    bf16 *q, bf16 *k, bf16 *v, float eps) {
+    bf16 *q, bf16 *k, bf16 *v, float eps, float *__restrict__ zp) {
     __shared__ __attribute__((aligned(16))) char smem[W_LDS_MAIN];
     bf16 *stages = reinterpret_cast<bf16 *>(smem);
 
@@ -503,7 +510,63 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const WideSrc src = wide_src(lane, wave, m0, M, K, n_rows);
     const bf16 *xb = x + (int64_t)m0 * K, *wb = Wp + (int64_t)n0 * K;
     const int nkb = K / WK;
-    auto kblock = [&](int kb) { return min(kb, nkb - 1) * WK; };
+    // channel offset of the i-th block of this tile's k order (blocks kb0,
+    // kb0+1, ... wrapping around); past the end it repeats the last one
+    const int kb0 = GZ ? 2 * n_tile : 0;
+    auto kblock = [&](int i) {
+        const int b = kb0 + min(i, nkb - 1);
+        return (b < nkb ? b : b - nkb) * WK;
+    };
+
+    // prologue: the first two blocks into the two stages
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i) wide_load(i, stages, src, xb + kblock(0), wb + kblock(0), wave);
+    if (nkb > 1) {
+#pragma unroll
+        for (int i = 0; i < WLOADS; ++i)
+            wide_load(i, stages + WSTAGE, src, xb + kblock(1), wb + kblock(1), wave);
+    }
+    if constexpr (GZ) {
+        // gate partial of this wave's 32 tokens (token tile wf of its half) over
+        // the tile's gate blocks: gate rows as A (8 fragments straight from
+        // global memory), the staged token tile as B
+        const bf16 *Wg = Wp + qkv_rows_padded(H, D) * K;   // 128-row gate tile
+        const bf16 *gsrc = Wg + (int64_t)(lane & 31) * K + kb0 * WK + 8 * (lane >> 5);
+        const bool two = kb0 + 1 < nkb;   // the tile's second gate block exists
+        bf16x8 ga[8];
+#pragma unroll
+        for (int gk = 0; gk < 8; ++gk)
+            ga[gk] = *reinterpret_cast<const bf16x8 *>(gsrc + 16 * (two ? gk : gk % 4));
+        wait_vmcnt<0>();
+        lds_barrier();
+        f32x16 gacc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) gacc[e] = 0.f;
+        auto gate_steps = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch = 2 * ks + (lane >> 5);
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(stages + st * WSTAGE +
+                                                                   wswz(wt * 128 + wf * 32 + (lane & 31), ch));
+                gacc = mfma32x32x16(ga[4 * st + ks], b, gacc);
+            }
+        };
+        gate_steps(0);
+        if (two) gate_steps(1);
+        // C lane layout: token (lane % 32), gate rows 8 (e / 4) + 4 (lane / 32) + e % 4
+        const int gh2 = 2 * H, tok = m0 + wt * 128 + wf * 32 + (lane & 31);
+        float *zdst = zp + (int64_t)n_tile * gh2 * M + tok;
+        if (tok < M) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = 8 * (e / 4) + 4 * (lane >> 5) + e % 4;
+                if (r < gh2) zdst[(int64_t)r * M] = gacc[e];
+            }
+        }
+    } else {
+        if (nkb > 1) wait_vmcnt<WLOADS>();   // the first stage's loads (the second may be in flight)
+        else wait_vmcnt<0>();
+    }
 
     f32x16 acc[3][4];
 #pragma unroll
@@ -513,20 +576,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // k-loop over two stages of 64 channels: step kb waits for its own loads,
-    // barriers (every wave is also done with kb-1, whose stage takes kb+1), then
-    // runs four k-steps of 12 MFMAs, reading the next k-step's fragments into the
-    // other register set, with kb+1's ten direct loads spread between the MFMAs.
-    {
-#pragma unroll
-        for (int i = 0; i < WLOADS; ++i) wide_load(i, stages, src, xb, wb, wave);
-    }
-    for (int kb = 0; kb < nkb; ++kb) {
-        wait_vmcnt<0>();
+    // k-loop over two stages of 64 channels: step i waits for its own loads,
+    // barriers (every wave is also done with step i-1, whose stage takes block
+    // i+1), then runs four k-steps of 12 MFMAs, reading the next k-step's
+    // fragments into the other register set, with block i+1's ten direct loads
+    // spread between the MFMAs.  Step 0 finds both stages loaded by the prologue.
+    auto kstep = [&](auto load_c, int it) __attribute__((always_inline)) {
+        constexpr bool LOAD = decltype(load_c)::value;
+        if constexpr (LOAD) wait_vmcnt<0>();
         lds_barrier();
-        const bf16 *cur = stages + (kb & 1) * WSTAGE;
-        bf16 *ld = stages + ((kb + 1) & 1) * WSTAGE;
-        const int k1 = kblock(kb + 1);
+        const bf16 *cur = stages + (it & 1) * WSTAGE;
+        bf16 *ld = stages + ((it + 1) & 1) * WSTAGE;
+        const int k1 = kblock(it + 1);
         WFr fr[2];
         wide_read(fr[0], cur, 0, lane, wt, wf);
 #pragma unroll
@@ -536,10 +597,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int j = 0; j < 12; ++j) {
                 const int i = 12 * s + j, ft = j / 4, tt = j % 4;
                 acc[ft][tt] = mfma32x32x16(fr[s & 1].a[ft], fr[s & 1].b[tt], acc[ft][tt]);
-                if (i % 4 == 1 && i / 4 < WLOADS) wide_load(i / 4, ld, src, xb + k1, wb + k1, wave);
+                if (LOAD && i % 4 == 1 && i / 4 < WLOADS) wide_load(i / 4, ld, src, xb + k1, wb + k1, wave);
             }
         }
-    }
+    };
+    kstep(std::false_type(), 0);
+    for (int it = 1; it < nkb; ++it) kstep(std::true_type(), it);
     wait_vmcnt<0>();   // the re-reads past the end land before LDS is reused
     __syncthreads();
 
@@ -701,9 +764,14 @@ hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *W
     return hipGetLastError();
 }
 
+int gate_partials(bool f32, int M, int d, int H) {
+    if (!project_separate_gates(f32, M) || 2 * H > 32) return 0;
+    return (d / WK + 1) / 2;
+}
+
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
-                          float eps, hipStream_t s) {
+                          float eps, float *zp, hipStream_t s) {
     const int ntiles = (int)(packed_rows(H, D) / BN);
     if (f32) {
         dim3 grid(ntiles, (M + BM_F - 1) / BM_F);
@@ -717,12 +785,15 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
                                alpha, beta, alpha_lo, eps);
     } else if (project_separate_gates(f32, M)) {
         const int m_tiles = (M + WM - 1) / WM, n_tiles = (H * 3 * D + WN - 1) / WN;
-        if (D == 128)
-            launch_kernel(k_proj_wide<128>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x,
-                          (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps);
-        else
-            launch_kernel(k_proj_wide<64>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x,
-                          (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps);
+#define WIDE(DD, GZ)                                                                               \
+    launch_kernel(k_proj_wide<DD, GZ>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x,   \
+                  (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps, zp)
+        if (zp) {
+            if (D == 128) WIDE(128, true); else WIDE(64, true);
+        } else {
+            if (D == 128) WIDE(128, false); else WIDE(64, false);
+        }
+#undef WIDE
     } else {
         const int m_tiles = (M + BM_BF - 1) / BM_BF;
         const int n_main = (int)(qkv_rows_padded(H, D) / BN);   // the gate tile is n_main

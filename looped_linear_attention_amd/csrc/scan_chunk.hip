@@ -113,11 +113,13 @@ __device__ __forceinline__ f32x4 mma4s(const float (&a)[4], const float (&b)[4],
     return mfma16x16x16(pack4(al), pack4(bh), c);
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, bool GP>
 __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
                                                    const TIn *__restrict__ k,
                                                    const float *__restrict__ alpha,
-                                                   const float *__restrict__ beta, int L, int H,
+                                                   const float *__restrict__ beta,
+                                                   const float *__restrict__ zp, int P, int Mtot,
+                                                   float alpha_lo, int L, int H,
                                                    int Nc, float *__restrict__ wsW,
                                                    float *__restrict__ wsM,
                                                    float *__restrict__ wsg) {
@@ -176,10 +178,22 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
         }
     }
     float a_raw = 1.f, b_raw = 0.f;
+    float za[GP ? 16 : 1], zb[GP ? 16 : 1];
     if (wave == 0) {
-        const int64_t gi = (tok0 + min(lane, last)) * H + h;
-        a_raw = alpha[gi];
-        b_raw = beta[gi];
+        if constexpr (GP) {
+            // partial pre-activations of the gates (P <= 16 of them), summed below
+            const float *src = zp + tok0 + min(lane, last);
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                const int64_t row = (int64_t)min(p, P - 1) * 2 * H + h;
+                za[p] = src[row * Mtot];
+                zb[p] = src[(row + H) * Mtot];
+            }
+        } else {
+            const int64_t gi = (tok0 + min(lane, last)) * H + h;
+            a_raw = alpha[gi];
+            b_raw = beta[gi];
+        }
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -194,6 +208,18 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
             for (int i = 0; i < 8; ++i) qf[s][i] = ok ? to_f32(qraw[s][i]) : 0.f;
     }
     if (wave == 0) {
+        if constexpr (GP) {
+            float sa = 0.f, sb = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                if (p < P) {
+                    sa += za[p];
+                    sb += zb[p];
+                }
+            }
+            a_raw = alpha_lo + (1.f - alpha_lo) / (1.f + expf(sa));
+            b_raw = 1.f / (1.f + expf(-sb));
+        }
         const bool ok = lane <= last;
         const float a = ok ? a_raw : 1.f;   // padded tokens: identity
         double x = log((double)fmaxf(a, 1e-37f));
@@ -895,16 +921,19 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 }  // namespace
 
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
-                            const float *alpha, const float *beta, ChunkWs ws, hipStream_t s) {
+                            GateSrc gs, ChunkWs ws, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     dim3 grid(Nc, H, B);
-#define PREP(DD, T)                                                                                \
-    launch_kernel((k_scan_prep<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,   \
-                       alpha, beta, L, H, Nc, ws.W, ws.M, ws.g)
+    if (gs.zp && (f32 || gs.P < 1 || gs.P > 16)) return hipErrorInvalidValue;
+#define PREP(DD, T, GP)                                                                            \
+    launch_kernel((k_scan_prep<DD, T, GP>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,     \
+                  gs.alpha, gs.beta, gs.zp, gs.P, B * L, gs.alpha_lo, L, H, Nc, ws.W, ws.M, ws.g)
     if (f32) {
-        if (D == 128) PREP(128, float); else PREP(64, float);
+        if (D == 128) PREP(128, float, false); else PREP(64, float, false);
+    } else if (gs.zp) {
+        if (D == 128) PREP(128, bf16, true); else PREP(64, bf16, true);
     } else {
-        if (D == 128) PREP(128, bf16); else PREP(64, bf16);
+        if (D == 128) PREP(128, bf16, false); else PREP(64, bf16, false);
     }
 #undef PREP
     return hipGetLastError();

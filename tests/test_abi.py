@@ -97,6 +97,20 @@ def test_workspace_sizes():
     assert n == exp
     st, n = _ws_status(desc, gl.GDN_OP_SCAN_PREFILL)
     assert st == 0 and n == chunks
+    # bf16 loop prefill of >= 1024 tokens with 2H <= 32: the projection GEMM leaves ceil(d / 128) fp32 partial
+    # gate pre-activations [P][2H][tokens] in the workspace
+    B, L, H, D = 1, 1100, 3, 64
+    desc = gl.make_desc(B, L, H, D, D, T=T)
+    tok, Nc, P = B * L, (L + 63) // 64, (H * D + 127) // 128
+    chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+    exp = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2) + up(P * 2 * H * tok * 4) + chunks
+    assert _ws_status(desc) == (0, exp)
+    # ... but not for 2H > 32, nor for the fp32 path
+    for H, act, eb in [(17, gl.GDN_BF16, 2), (3, gl.GDN_F32, 4)]:
+        desc = gl.make_desc(B, L, H, D, D, T=T, act=act)
+        chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+        exp = 3 * up(tok * H * D * eb) + 2 * up(tok * H * 4) + (up(tok * H * D * 2) if eb == 2 else 0) + chunks
+        assert _ws_status(desc) == (0, exp)
     st, n = _ws_status(gl.make_desc(64, 1, 16, 128, 128), gl.GDN_OP_SCAN_DECODE)
     assert st == 0 and n == 0
 

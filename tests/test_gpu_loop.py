@@ -175,6 +175,15 @@ def test_loop_prefill_full_size_prefix(name, prefix):
     _check_loop(w, x, w.B, w.L, TOL_BF16, gpu=(g_h, None, g_l), Lcmp=prefix)
 
 
+def test_loop_prefill_bf16_d64_h3_wide():
+    """1100 tokens of three 64-wide heads: the wide projection, whose two column tiles each leave a partial
+    gate pre-activation (the second over the single remaining 64-channel block) for the chunk preparation."""
+    w = _proj_workload("bf16_d64_h3")
+    say("[loop_prefill] bf16, 3 heads of 64, L=1100")
+    x = synth.prefill_inputs(w, L=1100)
+    _check_loop(w, x, 1, 1100, TOL_BF16)
+
+
 def test_loop_prefill_deterministic_and_no_aliasing_effects():
     w = synth.workload("prefill_b1_l4096")
     say("[loop_prefill] determinism, with and without per-loop outputs")
