@@ -141,6 +141,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void *base, int by
 // the operations issued before it in program order.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "the vector-memory counter holds 0..63");
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
     asm volatile("" ::: "memory");

@@ -444,15 +444,22 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
 //              the wave's partial K.S over its rows, reduce-scatter through LDS
 //              (wave w owns tokens 16w..16w+15), E = V - diag(gamma) K S_c for its
 //              tokens into LDS, then S' = gamma_C S + W E on its rows.
-//   wave 4     the producer: issues every direct load of the chain (K tile, V
-//              slice, gamma, W fragments) into double-buffered LDS stages.
+//   wave 4     the producer: issues every direct load of the workgroup's
+//              shared operands into LDS: the chain's K tile, V slice, gamma (two
+//              stages when they fit) and W fragments, and the output's Q tile, M
+//              fragments and gamma.
 //   waves 5-8  the output: wave 5 + o computes, for tokens 16 o .. 16 o + 15 of
 //              chunk cc - 1 while the chain works on chunk cc,
 //                  O = diag(gamma) Q S_c + M E
-//              from S_c and E in LDS (both double-buffered) and Q, M, gamma,
-//              h_prev loaded about a chunk ahead into registers, and writes O itself or
-//              the loop residual h = O + rho (.) h_prev (with a bf16 copy for the
-//              next loop's projection).
+//              from Q, M, gamma, S_c and E in LDS and h_prev loaded a chunk ahead
+//              into registers, and writes O itself or the loop residual
+//              h = O + rho (.) h_prev (with a bf16 copy for the next loop's
+//              projection).
+// Every operand that all 16-column slices of a head share (K, W, Q, M: about 80
+// KiB per chunk with bf16 inputs) arrives through direct global -> LDS loads of
+// whole 1 KiB runs: they take the CU's vector-memory path about a third of the
+// cycles per byte that 16-byte register loads of fragment-shaped pieces do, and
+// that path bounds the chunk step.
 // S_c and E never leave the CU.  The products use split-bf16 operands (x = hi
 // + lo, ~16 significant bits) with fp32 accumulation; exact bf16 inputs are not
 // split.
@@ -471,12 +478,18 @@ template <int D, typename TIn> struct CarryCfg {
     static constexpr int V_INS = C * VROWB / 1024;
     static constexpr int W_BYTES = D * C * 4;            // W hi and lo parts of one chunk
     static constexpr int W_INS = W_BYTES / 1024;
-    static constexpr int KVG_INS = K_INS + V_INS + 1;     // K tile, V slice, gamma
+    static constexpr int VG_INS = V_INS + 1;             // V slice, gamma
+    static constexpr int M_BYTES = C * C * 4;            // M hi and lo parts of one chunk
+    static constexpr int M_INS = M_BYTES / 1024;
+    static constexpr int QM_INS = K_INS + M_INS + 1;      // Q tile, M, gamma of the output
     // one chunk-start state slice as [wave][part: hi, lo][lane][KW] bf16
     static constexpr int SC_BYTES = 4 * 2 * 64 * KW * 2;
-    // LDS stages of the chain's operands: two when they fit beside the rest
-    static constexpr int STG = 2 * (TILE + W_BYTES + C * VROWB + C * 4) + 16384 + 2 * 4096 + 2 * SC_BYTES <=
-                                       160 * 1024 ? 2 : 1;
+    // LDS besides the W / V / gamma stages: the K tile, the output's Q / M /
+    // gamma, the K.S partials, E (two parities) and S_c (two parities)
+    static constexpr int FIXED = TILE + TILE + M_BYTES + C * 4 + 16384 + 2 * 4096 + 2 * SC_BYTES;
+    // stages of W, V, gamma: two when they fit
+    static constexpr int STG = 2 * (W_BYTES + C * VROWB + C * 4) + FIXED <= 160 * 1024 ? 2 : 1;
+    static_assert(STG * (W_BYTES + C * VROWB + C * 4) + FIXED <= 160 * 1024, "carry LDS");
 };
 
 // physical 16-byte chunk of logical chunk c in row r of a K tile
@@ -486,11 +499,11 @@ __device__ __forceinline__ int k_phys(int r, int c) {
     return c ^ ((r << G::SH) & (G::NCH - 1));
 }
 
-// Direct loads of chunk `cc` into one LDS stage, all issued by the producer
-// wave.  state_produce_kvg: the K tile (16-byte chunks XOR-swizzled by row),
-// the V slice of the workgroup's 16 columns and gamma (KVG_INS instructions).
-// state_produce_w: the chunk's W fragments, a byte copy of their fragment-order
-// block (W_INS instructions).  Tokens past the end of the sequence re-read the
+// Direct loads of chunk `cc` into LDS, all issued by the producer wave.
+// state_produce_k: the K tile (16-byte chunks XOR-swizzled by row, K_INS
+// instructions); state_produce_vg: the V slice of the workgroup's 16 columns
+// and gamma (VG_INS); state_produce_w: the chunk's W fragments, a byte copy of
+// their fragment-order block (W_INS).  Tokens past the end of the sequence re-read the
 // last token: the prep kernel gives them beta = 0, which zeroes their columns
 // of W, so any finite value is harmless.
 // Per-lane byte offsets of the K and V direct loads within a chunk's first
@@ -519,19 +532,15 @@ __device__ __forceinline__ KvOffsets<D, TIn> kv_offsets(int H, int lane) {
     return o;
 }
 template <int D, typename TIn>
-__device__ __forceinline__ void state_produce_kvg(unsigned ks, unsigned vs, unsigned gs, int cc, int L, int H,
-                                                  int h, int64_t tokb, int col0, const TIn *__restrict__ k,
-                                                  const TIn *__restrict__ v, const float *g, int64_t cidb,
-                                                  int lane, const KvOffsets<D, TIn> &off) {
+__device__ __forceinline__ void state_produce_k(unsigned ks, int cc, int L, int H, int h, int64_t tokb,
+                                                const TIn *__restrict__ k, int lane, const KvOffsets<D, TIn> &off) {
     using G = CarryCfg<D, TIn>;
     constexpr int EPC = 16 / G::ES;   // elements per 16-byte chunk
     const int c0 = cc * C;
     if (c0 + C <= L) {
-        const TIn *kb = k + ((tokb + c0) * H + h) * D, *vb = v + ((tokb + c0) * H + h) * D + col0;
+        const TIn *kb = k + ((tokb + c0) * H + h) * D;
 #pragma unroll
         for (int n = 0; n < G::K_INS; ++n) dma16_async_s_at(kb, off.k[n], ks + n * 1024);
-#pragma unroll
-        for (int n = 0; n < G::V_INS; ++n) dma16_async_s_at(vb, off.v[n], vs + n * 1024);
     } else {
 #pragma unroll
         for (int n = 0; n < G::K_INS; ++n) {
@@ -540,6 +549,20 @@ __device__ __forceinline__ void state_produce_kvg(unsigned ks, unsigned vs, unsi
             const int tok = min(c0 + r, L - 1);
             dma16_async_at(k + ((tokb + tok) * H + h) * D + c * EPC, ks + n * 1024);
         }
+    }
+}
+template <int D, typename TIn>
+__device__ __forceinline__ void state_produce_vg(unsigned vs, unsigned gs, int cc, int L, int H, int h,
+                                                 int64_t tokb, int col0, const TIn *__restrict__ v, const float *g,
+                                                 int64_t cidb, int lane, const KvOffsets<D, TIn> &off) {
+    using G = CarryCfg<D, TIn>;
+    constexpr int EPC = 16 / G::ES;
+    const int c0 = cc * C;
+    if (c0 + C <= L) {
+        const TIn *vb = v + ((tokb + c0) * H + h) * D + col0;
+#pragma unroll
+        for (int n = 0; n < G::V_INS; ++n) dma16_async_s_at(vb, off.v[n], vs + n * 1024);
+    } else {
         constexpr int LPR = G::VROWB / 16;   // lanes per V row
 #pragma unroll
         for (int n = 0; n < G::V_INS; ++n) {
@@ -549,6 +572,34 @@ __device__ __forceinline__ void state_produce_kvg(unsigned ks, unsigned vs, unsi
         }
     }
     // one instruction with 16 active lanes (64 floats)
+    if (lane < C / 4) dma16_async_s_at(g + (cidb + cc) * C, lane * 16, gs);
+}
+// The output's operands of chunk cc: the Q tile (laid out as the K tile), the
+// chunk's M fragments (a byte copy) and gamma (QM_INS instructions).
+template <int D, typename TIn>
+__device__ __forceinline__ void out_produce_qm(unsigned qs, unsigned ms, unsigned gs, int cc, int L, int H, int h,
+                                               int64_t tokb, const TIn *__restrict__ q, const float *M,
+                                               const float *g, int64_t cidb, int lane,
+                                               const KvOffsets<D, TIn> &off) {
+    using G = CarryCfg<D, TIn>;
+    constexpr int EPC = 16 / G::ES;
+    const int c0 = cc * C;
+    if (c0 + C <= L) {
+        const TIn *qb = q + ((tokb + c0) * H + h) * D;
+#pragma unroll
+        for (int n = 0; n < G::K_INS; ++n) dma16_async_s_at(qb, off.k[n], qs + n * 1024);
+    } else {
+#pragma unroll
+        for (int n = 0; n < G::K_INS; ++n) {
+            const int p = n * 64 + lane;
+            const int r = p / G::NCH, c = (p % G::NCH) ^ ((r << G::SH) & (G::NCH - 1));
+            const int tok = min(c0 + r, L - 1);
+            dma16_async_at(q + ((tokb + tok) * H + h) * D + c * EPC, qs + n * 1024);
+        }
+    }
+    const float *msrc = M + (cidb + cc) * C * C;
+#pragma unroll
+    for (int n = 0; n < G::M_INS; ++n) dma16_async_s_at(msrc + n * 256, lane * 16, ms + n * 1024);
     if (lane < C / 4) dma16_async_s_at(g + (cidb + cc) * C, lane * 16, gs);
 }
 template <int D, typename TIn>
@@ -616,34 +667,29 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
 }
 
 // Barrier schedule per chunk cc (all nine waves take part in each):
-//   B0  K, V, gamma of chunk cc have landed; the chain is done with chunk cc-1.
-//       Chain: S_c into LDS, K.S partials.  Producer (two stages): K, V, gamma of
-//       cc+1 into the other stage.  Output: M, gamma, h_prev of chunk cc into
-//       registers.
-//   B1  partials and S_c visible; W of chunk cc has landed.  Chain: reduce, E
-//       into LDS, W fragments.  Producer (two stages): W of cc+1 into the other W
-//       stage (its last reader, chunk cc-1, passed B1 before B0).  Output: chunk
-//       cc-1 from S_c, E of cc-1 and the registers loaded during cc-1, stores.
-//   B2  E visible.  Chain: S = gamma_C S + W E.  Producer (one stage): every
-//       load of chunk cc+1, into the stage chunk cc no longer reads.  Output:
-//       Q of chunk cc+1 (its M, gamma, h_prev follow after B0 of cc+1).
-// The CU's vector-memory address path is the shared resource: the output
-// waves' loads are split between the windows after B0 and after B2 so that
-// neither holds up the next barrier.
-// With two stages, K, V, gamma get one chunk to land and W one chunk as well,
-// shifted by one barrier; past the last chunk the producer re-reads the last
-// chunk into the idle stages, so its wait counts never change, and it drains
-// its loads before it exits.  S_c of chunk cc is rewritten at chunk cc+2 (after
-// B0) and E at chunk cc+2 (after B1), after the output waves used them at cc+1.
+//   B0  K, V, gamma and W of chunk cc have landed; the chain is done with chunk cc-1.
+//       Chain: S_c into LDS, K.S partials.  Producer (two stages): V, gamma of
+//       cc+1 into the other stage.  Output: h_prev of chunk cc into registers.
+//   B1  partials and S_c visible; the output operands of chunk cc-1 have
+//       landed; the K tile is no longer read.  Chain: reduce, E into LDS, W
+//       fragments.  Producer (two stages): W of cc+1 into the other W stage, then
+//       the K tile of cc+1 (one stage), both waited for before B0.  Output: chunk
+//       cc-1 from Q, M, gamma, S_c and E of cc-1 in LDS and h_prev in registers,
+//       stores.
+//   B2  E visible; the output operands are no longer read.  Chain:
+//       S = gamma_C S + W E.  Producer: the output operands of cc (one stage;
+//       with one stage of everything, all loads of cc+1 as well).
+// After the last chunk one more barrier (B3) makes the last output operands
+// visible for the output waves' final step.  With two stages the producer's
+// wait counts are the same every chunk: it issues one extra copy of chunk 0's
+// output operands up front, and past the last chunk it re-reads the last chunk
+// into the idle stages; it drains its loads before it exits.  S_c of chunk cc
+// is rewritten at chunk cc+2 (after B0) and E at chunk cc+2 (after B1), after
+// the output waves used them at cc+1.
 constexpr int CARRY_THREADS = 576;
 
-// Inputs of one output step held in registers: Q fragments of the wave's 16
-// tokens, M fragments, gamma of the lane's 4 tokens and h_prev at the lane's
-// 4 (token, column) cells.
-template <int D, typename TIn> struct OutIn {
-    TIn qa[4][CarryCfg<D, TIn>::KW];
-    bf16x8 mh[2], ml[2];
-    f32x4 gv;
+// h_prev at the lane's 4 (token, column) cells of one output step
+struct OutIn {
     float hp[4];
 };
 
@@ -657,13 +703,16 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     constexpr int NT = G::NT, RW = G::RW, KW = G::KW, STG = G::STG;
     // every stage is an object of its own, so the compiler can tell the buffers
     // a chunk reads from the ones the next chunk's direct loads write
-    __shared__ __attribute__((aligned(16))) unsigned char k0_s[G::TILE], k1_s[STG == 2 ? G::TILE : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char k_s[G::TILE];
     __shared__ __attribute__((aligned(16))) unsigned char w0_s[G::W_BYTES], w1_s[STG == 2 ? G::W_BYTES : 16];
     __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[STG == 2 ? C * G::VROWB : 16];
     __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[STG == 2 ? C : 4];
     __shared__ __attribute__((aligned(16))) f32x4 red[4][4][64];   // [source wave][token tile][lane]
     __shared__ __attribute__((aligned(16))) uint4 ex[2][4][64];    // [chunk parity][token tile][lane]: E hi | lo
     __shared__ __attribute__((aligned(16))) unsigned char sc_s[2][G::SC_BYTES];   // [chunk parity] S_c
+    // the output step's Q tile (K-tile layout), M fragments and gamma
+    __shared__ __attribute__((aligned(16))) unsigned char q_s[G::TILE], m_s[G::M_BYTES];
+    __shared__ __attribute__((aligned(16))) float go_s[C];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -677,36 +726,47 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 
     if (wave == 4) {
         // producer; two chunks per iteration so that the stages are compile-time choices
-        const unsigned lk[2] = {lds_addr(k0_s), lds_addr(k1_s)}, lv[2] = {lds_addr(v0_s), lds_addr(v1_s)};
+        const unsigned lk = lds_addr(k_s), lv[2] = {lds_addr(v0_s), lds_addr(v1_s)};
         const unsigned lgm[2] = {lds_addr(g0_s), lds_addr(g1_s)}, lw[2] = {lds_addr(w0_s), lds_addr(w1_s)};
+        const unsigned lq = lds_addr(q_s), lm = lds_addr(m_s), lgo = lds_addr(go_s);
         const KvOffsets<D, TIn> off = kv_offsets<D, TIn>(H, lane);
+        auto produce_qm = [&](int cc) __attribute__((always_inline)) {
+            out_produce_qm<D, TIn>(lq, lm, lgo, cc, L, H, h, tokb, q, M, g, cidb, lane, off);
+        };
         auto pstep = [&](auto stc, int cc) __attribute__((always_inline)) {
             constexpr int NX = STG == 2 ? 1 - decltype(stc)::value : 0;   // stage that receives chunk cc+1
             const int nx = min(cc + 1, Nc - 1);
             if constexpr (STG == 2) {
-                wait_vmcnt<G::W_INS>();     // K, V, gamma of cc landed (W of cc may be in flight)
+                wait_vmcnt<G::QM_INS>();    // V, gamma, W, K of cc landed (output operands of cc-1 in flight)
                 lds_barrier();              // B0
-                state_produce_kvg<D, TIn>(lk[NX], lv[NX], lgm[NX], nx, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
-                wait_vmcnt<G::KVG_INS>();   // W of cc landed (K, V, gamma of cc+1 may be in flight)
-                lds_barrier();              // B1
+                state_produce_vg<D, TIn>(lv[NX], lgm[NX], nx, L, H, h, tokb, col0, v, g, cidb, lane, off);
+                wait_vmcnt<G::VG_INS>();    // output operands of cc-1 landed (V, gamma of cc+1 in flight)
+                lds_barrier();              // B1: the K tile of cc is no longer read
                 state_produce_w<D, TIn>(lw[NX], nx, W, cidb, lane);
+                state_produce_k<D, TIn>(lk, nx, L, H, h, tokb, k, lane, off);
                 lds_barrier();              // B2
+                produce_qm(cc);
             } else {
-                wait_vmcnt<0>();            // every load of cc landed
+                wait_vmcnt<0>();            // every load of cc (and the output operands of cc-1) landed
                 lds_barrier();              // B0
                 lds_barrier();              // B1
-                lds_barrier();              // B2: chunk cc's stage is no longer read
-                state_produce_kvg<D, TIn>(lk[0], lv[0], lgm[0], nx, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
+                lds_barrier();              // B2: nothing loaded for chunk cc is read any more
+                state_produce_vg<D, TIn>(lv[0], lgm[0], nx, L, H, h, tokb, col0, v, g, cidb, lane, off);
+                state_produce_k<D, TIn>(lk, nx, L, H, h, tokb, k, lane, off);
                 state_produce_w<D, TIn>(lw[0], nx, W, cidb, lane);
+                produce_qm(cc);
             }
         };
-        state_produce_kvg<D, TIn>(lk[0], lv[0], lgm[0], 0, L, H, h, tokb, col0, k, v, g, cidb, lane, off);
+        state_produce_vg<D, TIn>(lv[0], lgm[0], 0, L, H, h, tokb, col0, v, g, cidb, lane, off);
         state_produce_w<D, TIn>(lw[0], 0, W, cidb, lane);
+        state_produce_k<D, TIn>(lk, 0, L, H, h, tokb, k, lane, off);
+        if constexpr (STG == 2) produce_qm(0);   // keeps the wait counts uniform; rewritten after B2 of chunk 0
         for (int cc = 0; cc < Nc; cc += 2) {
             pstep(std::integral_constant<int, 0>(), cc);
             if (cc + 1 < Nc) pstep(std::integral_constant<int, 1>(), cc + 1);
         }
-        wait_vmcnt<0>();   // no direct load may still write this workgroup's LDS after it ends
+        wait_vmcnt<0>();   // the last output operands landed; no direct load may write LDS after the end
+        lds_barrier();     // B3
         return;
     }
 
@@ -715,24 +775,10 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         const int ot = wave - 5;
         const int d = H * D;
         const float rho_c = RES ? rho[h * D + col] : 0.f;
-        // loads of chunk cc into registers (rows past the end of the sequence read
-        // the last row; their results are never stored): Q, then the rest
-        auto load_q = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
+        // h_prev of chunk cc into registers (rows past the end of the sequence
+        // read the last row; their results are never stored)
+        auto load_hp = [&](OutIn &in, int cc) __attribute__((always_inline)) {
             const int c0 = cc * C, last = L - 1 - c0;
-            const TIn *qrow = q + ((tokb + c0 + min(16 * ot + lr, last)) * H + h) * D + KW * lg;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) __builtin_memcpy(in.qa[ks], qrow + RW * ks, KW * sizeof(TIn));
-        };
-        auto load_rest = [&](OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
-            const int c0 = cc * C, last = L - 1 - c0;
-            const int64_t cid = cidb + cc;
-            const bf16x8 *Mf = reinterpret_cast<const bf16x8 *>(M + cid * C * C) + lane;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                in.mh[s] = Mf[((ot * 2 + s) * 2 + 0) * 64];
-                in.ml[s] = Mf[((ot * 2 + s) * 2 + 1) * 64];
-            }
-            in.gv = *reinterpret_cast<const f32x4 *>(g + cid * C + 16 * ot + 4 * lg);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 in.hp[j] = 0.f;
@@ -743,19 +789,23 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 }
             }
         };
-        // output step of chunk cc from the LDS buffers of parity P
-        auto compute = [&](auto pc, const OutIn<D, TIn> &in, int cc) __attribute__((always_inline)) {
+        // output step of chunk cc: S_c and E from the LDS buffers of parity P,
+        // Q, M and gamma from the output operand buffers
+        auto compute = [&](auto pc, const OutIn &in, int cc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;
             const int c0 = cc * C;
             const bf16 *scs = reinterpret_cast<const bf16 *>(sc_s[P]) + lane * KW;
             f32x4 qs = {0.f, 0.f, 0.f, 0.f}, me = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
+                TIn qa[KW];
+                k_frag<D, TIn>(q_s, 16 * ot + lr, ks, lg, qa);
                 __bf16 sh[KW], sl[KW];
                 __builtin_memcpy(sh, scs + (ks * 2 + 0) * 64 * KW, 2 * KW);
                 __builtin_memcpy(sl, scs + (ks * 2 + 1) * 64 * KW, 2 * KW);
-                qs = mma_a<KW>(in.qa[ks], sh, sl, qs);
+                qs = mma_a<KW>(qa, sh, sl, qs);
             }
+            const bf16x8 *mf = reinterpret_cast<const bf16x8 *>(m_s) + lane;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const uint4 a4 = ex[P][2 * s][lane], c4 = ex[P][2 * s + 1][lane];
@@ -763,13 +813,14 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 bf16x8 ebh, ebl;
                 __builtin_memcpy(&ebh, &hi, 16);
                 __builtin_memcpy(&ebl, &lo, 16);
-                me = mma_hl(in.mh[s], in.ml[s], ebh, ebl, me);
+                me = mma_hl(mf[((ot * 2 + s) * 2 + 0) * 64], mf[((ot * 2 + s) * 2 + 1) * 64], ebh, ebl, me);
             }
+            const f32x4 gv = *reinterpret_cast<const f32x4 *>(go_s + 16 * ot + 4 * lg);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * ot + 4 * lg + j;
                 if (c0 + r >= L) continue;
-                const float ov = in.gv[j] * qs[j] + me[j];
+                const float ov = gv[j] * qs[j] + me[j];
                 const int64_t row = tokb + c0 + r;
                 if constexpr (RES == 0) {
                     o[(row * H + h) * D + col] = ov;
@@ -781,24 +832,22 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 }
             }
         };
-        OutIn<D, TIn> in0, in1;
+        OutIn in0, in1;
         // one chunk per step, two per iteration so that the register set and the
         // LDS parity are compile-time choices
-        auto ostep = [&](auto pc, OutIn<D, TIn> &cur, OutIn<D, TIn> &prev, int cc)
-            __attribute__((always_inline)) {
+        auto ostep = [&](auto pc, OutIn &cur, OutIn &prev, int cc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;   // parity of chunk cc
             lds_barrier();   // B0
-            load_rest(cur, cc);
+            load_hp(cur, cc);
             lds_barrier();   // B1
             if (cc > 0) compute(std::integral_constant<int, 1 - P>(), prev, cc - 1);
             lds_barrier();   // B2
-            if (cc + 1 < Nc) load_q(prev, cc + 1);
         };
-        load_q(in0, 0);
         for (int cc = 0; cc < Nc; cc += 2) {
             ostep(std::integral_constant<int, 0>(), in0, in1, cc);
             if (cc + 1 < Nc) ostep(std::integral_constant<int, 1>(), in1, in0, cc + 1);
         }
+        lds_barrier();   // B3: the last chunk's output operands are visible
         // the last chunk: its S_c and E stay in LDS, nobody rewrites them
         if ((Nc - 1) & 1) compute(std::integral_constant<int, 1>(), in1, Nc - 1);
         else compute(std::integral_constant<int, 0>(), in0, Nc - 1);
@@ -822,7 +871,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     auto step = [&](auto pc) __attribute__((always_inline)) {
         constexpr int P = decltype(pc)::value;
         constexpr int ST = STG == 2 ? P : 0;
-        const unsigned char *k_cur = ST == 0 ? k0_s : k1_s;
+        const unsigned char *k_cur = k_s;
         const unsigned char *v_cur = ST == 0 ? v0_s : v1_s;
         const float *g_cur = ST == 0 ? g0_s : g1_s;
         const bf16x8 *w_cur = reinterpret_cast<const bf16x8 *>(ST == 0 ? w0_s : w1_s) + wave * NT * 4 * 64 + lane;
@@ -909,6 +958,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         step(std::integral_constant<int, 0>());
         if (cc + 1 < Nc) step(std::integral_constant<int, 1>());
     }
+    lds_barrier();   // B3 (the output waves' last step)
     if (s_final) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
