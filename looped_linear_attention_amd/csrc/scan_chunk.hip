@@ -668,14 +668,14 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
 
 // Barrier schedule per chunk cc (all nine waves take part in each):
 //   B0  K, V, gamma and W of chunk cc have landed; the chain is done with chunk cc-1.
-//       Chain: S_c into LDS, K.S partials.  Producer (two stages): V, gamma of
-//       cc+1 into the other stage.  Output: h_prev of chunk cc into registers.
+//       Chain: S_c into LDS, K.S partials.  Producer (two stages): V, gamma and
+//       W of cc+1 into the other stages (their last reader, chunk cc-1, passed
+//       B2 before).  Output: h_prev of chunk cc into registers.
 //   B1  partials and S_c visible; the output operands of chunk cc-1 have
 //       landed; the K tile is no longer read.  Chain: reduce, E into LDS, W
-//       fragments.  Producer (two stages): W of cc+1 into the other W stage, then
-//       the K tile of cc+1 (one stage), both waited for before B0.  Output: chunk
-//       cc-1 from Q, M, gamma, S_c and E of cc-1 in LDS and h_prev in registers,
-//       stores.
+//       fragments.  Producer: the K tile of cc+1 (one stage), waited for with V,
+//       gamma and W before B0.  Output: chunk cc-1 from Q, M, gamma, S_c and E of
+//       cc-1 in LDS and h_prev in registers, stores.
 //   B2  E visible; the output operands are no longer read.  Chain:
 //       S = gamma_C S + W E.  Producer: the output operands of cc (one stage;
 //       with one stage of everything, all loads of cc+1 as well).
@@ -740,9 +740,9 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 wait_vmcnt<G::QM_INS>();    // V, gamma, W, K of cc landed (output operands of cc-1 in flight)
                 lds_barrier();              // B0
                 state_produce_vg<D, TIn>(lv[NX], lgm[NX], nx, L, H, h, tokb, col0, v, g, cidb, lane, off);
-                wait_vmcnt<G::VG_INS>();    // output operands of cc-1 landed (V, gamma of cc+1 in flight)
-                lds_barrier();              // B1: the K tile of cc is no longer read
                 state_produce_w<D, TIn>(lw[NX], nx, W, cidb, lane);
+                wait_vmcnt<G::VG_INS + G::W_INS>();   // output operands of cc-1 landed (V, gamma, W of cc+1 in flight)
+                lds_barrier();              // B1: the K tile of cc is no longer read
                 state_produce_k<D, TIn>(lk, nx, L, H, h, tokb, k, lane, off);
                 lds_barrier();              // B2
                 produce_qm(cc);
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         state_produce_vg<D, TIn>(lv[0], lgm[0], 0, L, H, h, tokb, col0, v, g, cidb, lane, off);
         state_produce_w<D, TIn>(lw[0], 0, W, cidb, lane);
         state_produce_k<D, TIn>(lk, 0, L, H, h, tokb, k, lane, off);
-        if constexpr (STG == 2) produce_qm(0);   // keeps the wait counts uniform; rewritten after B2 of chunk 0
+        if constexpr (STG == 2) produce_qm(0);   // (V, gamma, W of chunk 0 precede K here: the same order as later)   // keeps the wait counts uniform; rewritten after B2 of chunk 0
         for (int cc = 0; cc < Nc; cc += 2) {
             pstep(std::integral_constant<int, 0>(), cc);
             if (cc + 1 < Nc) pstep(std::integral_constant<int, 1>(), cc + 1);
