@@ -795,7 +795,10 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
             constexpr int P = decltype(pc)::value;
             const int c0 = cc * C;
             const bf16 *scs = reinterpret_cast<const bf16 *>(sc_s[P]) + lane * KW;
-            f32x4 qs = {0.f, 0.f, 0.f, 0.f}, me = {0.f, 0.f, 0.f, 0.f};
+            // four independent accumulator chains (Q S_c over k-steps {0,2} and
+            // {1,3}, M E over the two k-steps), so the MFMAs overlap
+            f32x4 qs2[2], me2[2];
+            const bf16x8 *mf = reinterpret_cast<const bf16x8 *>(m_s) + lane;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 TIn qa[KW];
@@ -803,18 +806,20 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 __bf16 sh[KW], sl[KW];
                 __builtin_memcpy(sh, scs + (ks * 2 + 0) * 64 * KW, 2 * KW);
                 __builtin_memcpy(sl, scs + (ks * 2 + 1) * 64 * KW, 2 * KW);
-                qs = mma_a<KW>(qa, sh, sl, qs);
+                if (ks < 2) qs2[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+                qs2[ks & 1] = mma_a<KW>(qa, sh, sl, qs2[ks & 1]);
+                if (ks < 2) {
+                    const int s = ks;
+                    const uint4 a4 = ex[P][2 * s][lane], c4 = ex[P][2 * s + 1][lane];
+                    const uint4 hi = make_uint4(a4.x, a4.y, c4.x, c4.y), lo = make_uint4(a4.z, a4.w, c4.z, c4.w);
+                    bf16x8 ebh, ebl;
+                    __builtin_memcpy(&ebh, &hi, 16);
+                    __builtin_memcpy(&ebl, &lo, 16);
+                    me2[s] = mma_hl(mf[((ot * 2 + s) * 2 + 0) * 64], mf[((ot * 2 + s) * 2 + 1) * 64], ebh, ebl,
+                                    f32x4{0.f, 0.f, 0.f, 0.f});
+                }
             }
-            const bf16x8 *mf = reinterpret_cast<const bf16x8 *>(m_s) + lane;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint4 a4 = ex[P][2 * s][lane], c4 = ex[P][2 * s + 1][lane];
-                const uint4 hi = make_uint4(a4.x, a4.y, c4.x, c4.y), lo = make_uint4(a4.z, a4.w, c4.z, c4.w);
-                bf16x8 ebh, ebl;
-                __builtin_memcpy(&ebh, &hi, 16);
-                __builtin_memcpy(&ebl, &lo, 16);
-                me = mma_hl(mf[((ot * 2 + s) * 2 + 0) * 64], mf[((ot * 2 + s) * 2 + 1) * 64], ebh, ebl, me);
-            }
+            const f32x4 qs = qs2[0] + qs2[1], me = me2[0] + me2[1];
             const f32x4 gv = *reinterpret_cast<const f32x4 *>(go_s + 16 * ot + 4 * lg);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -944,15 +949,18 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
             __builtin_memcpy(&ebh[s], &hi, 16);
             __builtin_memcpy(&ebl[s], &lo, 16);
         }
-        // S' = gamma_C S + W E (this wave's rows)
+        // S' = gamma_C S + W E (this wave's rows); one accumulator chain per
+        // (row tile, k-step), so the MFMAs overlap
+        f32x4 we[NT][2];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 we = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) we = mma_hl(wh[tt][s], wl[tt][s], ebh[s], ebl[s], we);
+            for (int tt = 0; tt < NT; ++tt)
+                we[tt][s] = mma_hl(wh[tt][s], wl[tt][s], ebh[s], ebl[s], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + we[j];
-        }
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + (we[tt][0][j] + we[tt][1][j]);
     };
     for (int cc = 0; cc < Nc; cc += 2) {
         step(std::integral_constant<int, 0>());
