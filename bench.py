@@ -118,10 +118,12 @@ def bench_prefill(args, w, torch, gl, synth):
     stages = {"project": gl.GDN_STAGE_PROJECT, "gates": gl.GDN_STAGE_GATES, "scan_prep": gl.GDN_STAGE_SCAN_PREP,
               "scan_carry": gl.GDN_STAGE_SCAN_CARRY}
 
-    def timed_pass(names):
-        """args.steps steps with the dispatch events of the named stages armed; (ms total, per-stage)."""
+    def timed_pass(names, stride=1):
+        """args.steps steps with the dispatch events of the named stages armed on every stride-th launch;
+        (ms total, wall s, per-stage)."""
         timers = {k: gl.gdn_timer_create(stages[k], args.steps * w.T) for k in names}
         for t in timers.values():
+            gl.gdn_timer_set_stride(t, stride)
             gl.gdn_timer_attach(t)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -142,9 +144,11 @@ def bench_prefill(args, w, torch, gl, synth):
             gl.gdn_timer_destroy(t)
         return ms_total, wall, per_stage
 
-    # The timed region carries dispatch events on the projection GEMM only (each armed dispatch costs the GPU a
-    # few microseconds); the per-stage breakdown comes from a second pass with every stage armed.
-    ms_total, wall, timed_stages = timed_pass(["project"])
+    # The timed region carries dispatch events on every fifth projection GEMM launch only (each armed dispatch
+    # costs the GPU a few microseconds; 5 is coprime to the 4 loops, so the sample covers every loop evenly); the
+    # per-stage breakdown comes from a second pass with every launch of every stage armed.
+    stride = 5 if args.steps * w.T >= 20 else 1
+    ms_total, wall, timed_stages = timed_pass(["project"], stride)
     _, _, per_stage = timed_pass(list(stages))
     per_stage["project"] = timed_stages["project"]
     ms_step = ms_total / args.steps

@@ -200,9 +200,15 @@ enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
  * a time (attaching replaces that stage's timer; detach removes all).
  * Attaching is process-wide and meant for profiling runs; it is not
  * thread-safe.  gdn_timer_read waits for the recorded events and returns the
- * number of bracketed launches and their summed duration in milliseconds. */
+ * number of bracketed launches and their summed duration in milliseconds.
+ * Each armed dispatch costs the GPU a few microseconds; gdn_timer_set_stride
+ * (stride >= 1, default 1) arms only every stride-th launch of the stage made
+ * while the timer is attached, counted from the call (and from each reset),
+ * so that a long run can be sampled at a small cost.  gdn_timer_reset
+ * forgets the recorded launches. */
 typedef struct gdn_timer gdn_timer;
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out);
+gdn_status gdn_timer_set_stride(gdn_timer *t, int stride);
 gdn_status gdn_timer_attach(gdn_timer *t);
 gdn_status gdn_timer_detach(void);
 gdn_status gdn_timer_reset(gdn_timer *t);

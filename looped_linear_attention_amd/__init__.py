@@ -26,7 +26,7 @@ __all__ = [
     "load", "EXPORTED", "workspace",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
-    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_attach",
+    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
@@ -38,7 +38,7 @@ GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, 
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
-    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_attach",
+    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
@@ -92,6 +92,7 @@ def load():
         "gdn_loop_prefill": [D, P, P, P, P, P, P, P, S, P],
         "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
         "gdn_timer_create": [I, I, ctypes.POINTER(P)],
+        "gdn_timer_set_stride": [P, I],
         "gdn_timer_attach": [P],
         "gdn_timer_detach": [],
         "gdn_timer_reset": [P],
@@ -257,6 +258,10 @@ def gdn_timer_create(stage: int, capacity: int) -> ctypes.c_void_p:
     h = ctypes.c_void_p()
     _check(load().gdn_timer_create(stage, capacity, ctypes.byref(h)))
     return h
+
+
+def gdn_timer_set_stride(timer, stride: int) -> None:
+    _check(load().gdn_timer_set_stride(timer, stride))
 
 
 def gdn_timer_attach(timer) -> None:

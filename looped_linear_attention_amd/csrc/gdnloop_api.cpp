@@ -133,6 +133,8 @@ struct gdn_timer {
     int stage = 0;
     int capacity = 0;
     int used = 0;
+    int stride = 1;   // record launches stride-1, 2 stride-1, ... of the stage
+    int seen = 0;     // launches of the stage while attached
     std::vector<hipEvent_t> start, stop;
 };
 
@@ -148,6 +150,7 @@ template <typename F>
 hipError_t timed(int stage, hipStream_t s, F &&launch) {
     gdn_timer *tm = g_timers[stage];
     if (!tm || tm->stage != stage || tm->used >= tm->capacity) return launch();
+    if (++tm->seen % tm->stride != 0) return launch();
     (void)s;
     launch_events() = LaunchEvents{tm->start[tm->used], tm->stop[tm->used]};
     hipError_t e = launch();
@@ -406,9 +409,18 @@ gdn_status gdn_timer_detach(void) {
     return GDN_OK;
 }
 
+gdn_status gdn_timer_set_stride(gdn_timer *t, int stride) {
+    if (!t) return fail(GDN_ERR_NULL, "timer is NULL");
+    if (stride < 1) return fail(GDN_ERR_SHAPE, "timer stride must be >= 1 (got %d)", stride);
+    t->stride = stride;
+    t->seen = 0;
+    return GDN_OK;
+}
+
 gdn_status gdn_timer_reset(gdn_timer *t) {
     if (!t) return fail(GDN_ERR_NULL, "timer is NULL");
     t->used = 0;
+    t->seen = 0;
     return GDN_OK;
 }
 

@@ -171,6 +171,7 @@ def test_timer_validation(lib):
     assert lib.gdn_timer_destroy(None) == 0
     n, ms = ctypes.c_int(), ctypes.c_double()
     assert lib.gdn_timer_read(None, ctypes.byref(n), ctypes.byref(ms)) == -1
+    assert lib.gdn_timer_set_stride(None, 2) == -1
 
 
 @no_gpu

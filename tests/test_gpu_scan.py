@@ -146,3 +146,30 @@ def test_prefill_state_then_decode_matches_longer_prefill():
     torch.cuda.synchronize()
     ro, _ = oracle.scan(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
     assert rel_err(o.cpu(), ro[:, 128]) <= TOL_BF16
+
+
+def test_stage_timer_stride():
+    """A timer with stride 3 arms the 3rd and 6th of six launches of its stage, and only those."""
+    say("[timer] stride 3 over six decode launches")
+    N, H, D = 2, 2, 64
+    desc = gl.make_desc(N, 1, H, D, D, T=1, act="f32")
+    g = torch.Generator().manual_seed(7)
+    q, k, v = (torch.randn(N, H, D, generator=g).cuda() for _ in range(3))
+    al, be = torch.full((N, H), 0.9).cuda(), torch.full((N, H), 0.5).cuda()
+    S = torch.zeros(N, H, D, D).cuda()
+    o = torch.empty(N, H, D).cuda()
+    t = gl.gdn_timer_create(gl.GDN_STAGE_DECODE, 8)
+    try:
+        gl.gdn_timer_set_stride(t, 3)
+        gl.gdn_timer_attach(t)
+        for _ in range(6):
+            gl.gdn_scan_decode(desc, q, k, v, al, be, S, o)
+        torch.cuda.synchronize()
+        gl.gdn_timer_detach()
+        n, ms = gl.gdn_timer_read(t)
+        assert n == 2 and ms > 0
+        gl.gdn_timer_reset(t)
+        assert gl.gdn_timer_read(t)[0] == 0
+    finally:
+        gl.gdn_timer_detach()
+        gl.gdn_timer_destroy(t)
