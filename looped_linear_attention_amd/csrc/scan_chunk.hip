@@ -47,6 +47,67 @@ template <typename T> struct In;
 template <> struct In<float> { static constexpr bool f32 = true; };
 template <> struct In<bf16> { static constexpr bool f32 = false; };
 
+// A chunk tile of K or Q in LDS: 64 token rows of D elements, no padding, the
+// 16-byte chunks of row r permuted by an XOR with a row-dependent key, so that
+// 16 consecutive rows reading the same logical chunk hit distinct bank groups.
+// It arrives by direct loads of whole 1 KiB runs (tile_load).
+template <int D, typename TIn> struct KTile {
+    static constexpr int ES = (int)sizeof(TIn);
+    static constexpr int ROWB = D * ES;                  // bytes of a token row
+    static constexpr int NCH = ROWB / 16;                // 16-byte chunks per row
+    static constexpr int SH = (ES == 4 && D == 128) ? 1 : 0;
+    static constexpr int BYTES = C * ROWB;
+    static constexpr int INS = BYTES / 1024;             // direct-load instructions per tile
+    // physical 16-byte chunk of logical chunk c in row r
+    __device__ static int phys(int r, int c) { return c ^ ((r << SH) & (NCH - 1)); }
+};
+
+// Direct loads of the tile of `src` ([tokens][H][D]) for head h and the 64
+// tokens from row tok0 (rows past `last` re-read row `last`): instructions
+// n = n0, n0 + step, ... of the tile.
+template <int D, typename TIn>
+__device__ __forceinline__ void tile_load(unsigned char *tile, const TIn *src, int64_t tok0, int last, int H, int h,
+                                          int lane, int n0, int step) {
+    using T = KTile<D, TIn>;
+    constexpr int EPC = 16 / T::ES;
+    for (int n = n0; n < T::INS; n += step) {
+        const int p = n * 64 + lane;
+        const int r = p / T::NCH, c = T::phys(r, p % T::NCH);
+        dma16_async(src + ((tok0 + min(r, last)) * H + h) * D + c * EPC, tile + n * 1024);
+    }
+}
+
+// 8 consecutive elements [k0, k0 + 8) of row r of a tile (k0 a multiple of 8), as floats
+template <int D, typename TIn>
+__device__ __forceinline__ void tile_frag8(const unsigned char *tile, int r, int k0, float (&f)[8]) {
+    using T = KTile<D, TIn>;
+    const unsigned char *row = tile + r * T::ROWB;
+    if constexpr (T::ES == 2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(row + T::phys(r, k0 / 8) * 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(row + T::phys(r, k0 / 4) * 16);
+        const float4 b = *reinterpret_cast<const float4 *>(row + T::phys(r, k0 / 4 + 1) * 16);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+}
+// the same 8 elements as raw bf16 (bf16 tiles)
+template <int D>
+__device__ __forceinline__ bf16x8 tile_bf8(const unsigned char *tile, int r, int k0) {
+    using T = KTile<D, bf16>;
+    return *reinterpret_cast<const bf16x8 *>(tile + r * T::ROWB + T::phys(r, k0 / 8) * 16);
+}
+// element (r, i) of a tile, as a float
+template <int D, typename TIn>
+__device__ __forceinline__ float tile_elem(const unsigned char *tile, int r, int i) {
+    using T = KTile<D, TIn>;
+    constexpr int EPC = 16 / T::ES;
+    const TIn *e = reinterpret_cast<const TIn *>(tile + r * T::ROWB + T::phys(r, i / EPC) * 16) + i % EPC;
+    return to_f32(*e);
+}
+
 // Fragment order of the per-chunk [R x 64] matrices W (R = D rows of S) and M
 // (R = 64 output tokens) that the prep kernel writes and the carry reads.  Rows are
 // split over the 4 waves (RW = R/4 each, NT = RW/16 tiles of 16); row
@@ -72,22 +133,6 @@ template <> struct In<bf16> { static constexpr bool f32 = false; };
 // (split-bf16 MFMA products).  W and M are computed transposed on MFMA so that
 // each lane holds 8 consecutive fragment slots of the carry's layout and
 // stores them with one 16-byte write per part.
-
-// A or B fragment (8 values along k) of a 16x16x32 product from a row-major
-// LDS tile of TIn: elements [row][k0 .. k0+8).
-template <typename TIn>
-__device__ __forceinline__ void row_frag8(const TIn *tile, int ld, int row, int k0, float (&f)[8]) {
-    if constexpr (sizeof(TIn) == 2) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(tile + row * ld + k0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
-    } else {
-        const float4 a = *reinterpret_cast<const float4 *>(tile + row * ld + k0);
-        const float4 b = *reinterpret_cast<const float4 *>(tile + row * ld + k0 + 4);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    }
-}
 
 // c += a.b on 16x16x32 bf16 MFMA, exact when both are bf16 values (EXACT),
 // else with both operands split into bf16 hi + lo (3 passes).
@@ -124,11 +169,11 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
                                                    float *__restrict__ wsM,
                                                    float *__restrict__ wsg) {
     constexpr bool F32 = In<TIn>::f32;
-    constexpr int LDK = D + (F32 ? 4 : 8);   // row stride (elements) of the K tile
     constexpr int LT = C + 4;                // row stride (floats) of the 64x64 N and T tiles
     constexpr int KS = D / 32;               // k-steps of the D contractions
     constexpr int RW = D / 4, NT = RW / 16;  // W rows per wave, 16-row tiles per wave
-    __shared__ __attribute__((aligned(16))) TIn Ks[C * LDK];
+    using KT = KTile<D, TIn>;
+    __shared__ __attribute__((aligned(16))) unsigned char Ks[KT::BYTES], Qs[KT::BYTES];
     __shared__ __attribute__((aligned(16))) float Ns[C * LT];
     __shared__ __attribute__((aligned(16))) float Ts[C * LT];
     __shared__ __attribute__((aligned(16))) f32x4 Ys[4][64];
@@ -142,40 +187,17 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
     const int c0 = chunk * C;
     const int64_t tok0 = (int64_t)b * L + c0;
 
-    // (1) K tile (zero rows past the end), the Q fragments of this wave's 16
-    // tokens (B operand of K Q^T), gates, and the fp64 log-cumsum of alpha.
-    // Every global load is issued before the first wait (rows past the end
-    // read the last row and are masked afterwards), so the phase costs one
-    // memory round trip instead of one per load.
-    constexpr int VEC = 16 / sizeof(TIn);
-    constexpr int CPR = D / VEC;
-    constexpr int KPT = C * CPR / 256;   // K-tile chunks per thread
+    // (1) K and Q tiles into LDS by direct loads of whole 1 KiB runs (rows past
+    // the end of the sequence re-read the last row: beta = 0 makes their rows
+    // of T unit rows, so they meet only exact zeros in W, and the outputs of Q
+    // rows past the end are never stored), gates, and the fp64 log-cumsum of
+    // alpha.  Every global load is issued before the first wait.
+    // Waves 1-3 issue the tile loads and wave 0 only the gate loads, so the
+    // compiler's waits for the gates in wave 0 do not also wait for the tiles.
     const int last = L - 1 - c0;         // last valid row of the chunk
-    uint4 kv[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int idx = t + 256 * i, r = idx / CPR, ch = idx % CPR;
-        kv[i] = *reinterpret_cast<const uint4 *>(k + ((tok0 + min(r, last)) * H + h) * D + ch * VEC);
-    }
-    float qf[KS][8];
-    TIn qraw[KS][8];
-    const int rq = 16 * wave + lr;
-    {
-        const TIn *src = q + ((tok0 + min(rq, last)) * H + h) * D + 8 * lg;   // 16-byte aligned runs
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if constexpr (F32) {
-                const float4 a = *reinterpret_cast<const float4 *>(src + 32 * s);
-                const float4 c = *reinterpret_cast<const float4 *>(src + 32 * s + 4);
-                const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) qraw[s][i] = v[i];
-            } else {
-                const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src + 32 * s);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) qraw[s][i] = v[i];
-            }
-        }
+    if (wave > 0) {
+        tile_load<D, TIn>(Ks, k, tok0, last, H, h, lane, wave - 1, 3);
+        tile_load<D, TIn>(Qs, q, tok0, last, H, h, lane, wave - 1, 3);
     }
     float a_raw = 1.f, b_raw = 0.f;
     float za[GP ? 16 : 1], zb[GP ? 16 : 1];
@@ -194,18 +216,6 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
             a_raw = alpha[gi];
             b_raw = beta[gi];
         }
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int idx = t + 256 * i, r = idx / CPR, ch = idx % CPR;
-        *reinterpret_cast<uint4 *>(Ks + r * LDK + ch * VEC) = r <= last ? kv[i] : make_uint4(0, 0, 0, 0);
-    }
-    {
-        const bool ok = rq <= last;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qf[s][i] = ok ? to_f32(qraw[s][i]) : 0.f;
     }
     if (wave == 0) {
         if constexpr (GP) {
@@ -238,35 +248,77 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
         const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
         Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
     }
-    __syncthreads();
+    wait_vmcnt<0>();   // this wave's direct loads of the K and Q tiles landed
+    __syncthreads();   // ... and the other waves'.
 
     // (2) N = diag(beta) strict_lower(Gam (.) K K^T) for this wave's 16 rows;
     // P^T tiles (m-tile mt, r-tile wave) = Gam (.) K Q^T, m <= r, in registers
+    // Every LDS operand of the phase is read up front (one round trip).
     float pv[4][4];
     {
         const int r_a = 16 * wave + lr;
+        f32x4 kk[4], kq[4];
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) kk[tn] = kq[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!F32) {
+            bf16x8 ka[KS], qa[KS], kb[4][KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                ka[s] = tile_bf8<D>(Ks, r_a, 32 * s + 8 * lg);
+                qa[s] = tile_bf8<D>(Qs, r_a, 32 * s + 8 * lg);
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) kb[tn][s] = tile_bf8<D>(Ks, 16 * tn + lr, 32 * s + 8 * lg);
+            }
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+                if (tn <= wave) {
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        kk[tn] = mfma16x16x32(ka[s], kb[tn][s], kk[tn]);   // K_r . K_i   (rows r of this wave)
+                        kq[tn] = mfma16x16x32(kb[tn][s], qa[s], kq[tn]);   // K_m . Q_r   (rows m of tile tn)
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+                if (tn <= wave) {
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        float a[8], bb[8], qv[8];
+                        tile_frag8<D, TIn>(Ks, r_a, 32 * s + 8 * lg, a);
+                        tile_frag8<D, TIn>(Ks, 16 * tn + lr, 32 * s + 8 * lg, bb);
+                        tile_frag8<D, TIn>(Qs, r_a, 32 * s + 8 * lg, qv);
+                        kk[tn] = mma8<false>(a, bb, kk[tn]);
+                        kq[tn] = mma8<false>(bb, qv, kq[tn]);
+                    }
+                }
+        }
+        // decay factors: N[row][col] uses Gam(row, col), P[r][m] uses Gam(r, m)
+        double lrow[4], lcol[4], lm[4][4];
+        float brow[4];
+        const double lr_a = lgs[r_a];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lrow[j] = lgs[16 * wave + 4 * lg + j];
+            brow[j] = bes[16 * wave + 4 * lg + j];
+        }
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
-            if (tn <= wave) {
-                const int r_b = 16 * tn + lr;
+            lcol[tn] = lgs[16 * tn + lr];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    float a[8], bb[8];
-                    row_frag8<TIn>(Ks, LDK, r_a, 32 * s + 8 * lg, a);
-                    row_frag8<TIn>(Ks, LDK, r_b, 32 * s + 8 * lg, bb);
-                    kk = mma8<!F32>(a, bb, kk);          // K_r . K_i   (rows r of this wave)
-                    kq = mma8<!F32>(bb, qf[s], kq);      // K_m . Q_r   (rows m of tile tn)
-                }
-            }
+            for (int j = 0; j < 4; ++j) lm[tn][j] = lgs[16 * tn + 4 * lg + j];
+        }
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * wave + 4 * lg + j, col = 16 * tn + lr;   // N[row][col]
-                float nv = 0.f;
-                if (col < row) nv = bes[row] * __expf((float)(lgs[row] - lgs[col])) * kk[j];
+                const float gn = __expf((float)(lrow[j] - lcol[tn]));
+                const float nv = col < row ? brow[j] * gn * kk[tn][j] : 0.f;
                 if (tn <= wave) Ns[row * LT + col] = nv;
-                const int m = 16 * tn + 4 * lg + j, r = 16 * wave + lr;       // P[r][m]
-                pv[tn][j] = (tn <= wave && m <= r) ? __expf((float)(lgs[r] - lgs[m])) * kq[j] : 0.f;
+                const int m = 16 * tn + 4 * lg + j;                               // P[r_a][m]
+                const float gp = __expf((float)(lr_a - lm[tn][j]));
+                pv[tn][j] = (tn <= wave && m <= r_a) ? gp * kq[tn][j] : 0.f;
             }
         }
     }
@@ -354,19 +406,29 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
     bf16 *dW = reinterpret_cast<bf16 *>(wsW + cid * D * C);
     bf16 *dM = reinterpret_cast<bf16 *>(wsM + cid * C * C);
     const double lgC = lgs[C - 1];
+    // gamma_C / gamma_m for the lane's 16 token slots m, and beta of its 4 columns
+    float gw[2][8], bcs[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
+            gw[s][jj] = __expf((float)(lgC - lgs[m]));
+        }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) bcs[ct] = bes[16 * ct + lr];
     float am[4][2][8], aw[4][2][8];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         const int c = 16 * ct + lr;
-        const float bc = bes[c];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
-                const float tb = Ts[m * LT + c] * bc;
+                const float tb = Ts[m * LT + c] * bcs[ct];
                 am[ct][s][jj] = tb;
-                aw[ct][s][jj] = tb * __expf((float)(lgC - lgs[m]));
+                aw[ct][s][jj] = tb * gw[s][jj];
             }
     }
     // (7) W^T tiles: rows c (token), columns = this wave's S rows; lane column
@@ -380,7 +442,7 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
-                bk[s][jj] = to_f32(Ks[m * LDK + i]);
+                bk[s][jj] = tile_elem<D, TIn>(Ks, m, i);
             }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {   // output k-step of the carry: c-tiles 2 s2, 2 s2 + 1
@@ -470,8 +532,8 @@ template <int D, typename TIn> struct CarryCfg {
     static constexpr int NSL = D / 16;                   // column slices of S
     static constexpr int ES = (int)sizeof(TIn);
     static constexpr int ROWB = D * ES;                  // bytes of a token row of K
-    static constexpr int NCH = ROWB / 16;                // 16-byte chunks per row
-    static constexpr int SH = (ES == 4 && D == 128) ? 1 : 0;
+    static constexpr int NCH = KTile<D, TIn>::NCH;       // 16-byte chunks per row
+    static constexpr int SH = KTile<D, TIn>::SH;
     static constexpr int TILE = C * ROWB;                // bytes of a K chunk tile
     static constexpr int K_INS = TILE / 1024;            // direct-load instructions for K
     static constexpr int VROWB = 16 * ES;                // bytes of a token row of the V slice
@@ -495,8 +557,7 @@ template <int D, typename TIn> struct CarryCfg {
 // physical 16-byte chunk of logical chunk c in row r of a K tile
 template <int D, typename TIn>
 __device__ __forceinline__ int k_phys(int r, int c) {
-    using G = CarryCfg<D, TIn>;
-    return c ^ ((r << G::SH) & (G::NCH - 1));
+    return KTile<D, TIn>::phys(r, c);
 }
 
 // Direct loads of chunk `cc` into LDS, all issued by the producer wave.
