@@ -159,7 +159,7 @@ __device__ __forceinline__ f32x4 mma4s(const float (&a)[4], const float (&b)[4],
 }
 
 template <int D, typename TIn, bool GP>
-__global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scan_prep(const TIn *__restrict__ q,
                                                    const TIn *__restrict__ k,
                                                    const float *__restrict__ alpha,
                                                    const float *__restrict__ beta,
@@ -173,10 +173,21 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
     constexpr int KS = D / 32;               // k-steps of the D contractions
     constexpr int RW = D / 4, NT = RW / 16;  // W rows per wave, 16-row tiles per wave
     using KT = KTile<D, TIn>;
-    __shared__ __attribute__((aligned(16))) unsigned char Ks[KT::BYTES], Qs[KT::BYTES];
+    // LDS (52 KB with bf16 dk = 128, so three workgroups fit on a CU): the Q tile
+    // is read only by phase 2 and T is written from phase 3 on, so they share
+    // storage; the phase-5 exchange lives in the strictly upper 16x16 blocks of
+    // N, which are never written or read otherwise.
+    constexpr int TQ_FLOATS = C * LT > KT::BYTES / 4 ? C * LT : KT::BYTES / 4;
+    __shared__ __attribute__((aligned(16))) unsigned char Ks[KT::BYTES];
+    __shared__ __attribute__((aligned(16))) float TQs[TQ_FLOATS];
     __shared__ __attribute__((aligned(16))) float Ns[C * LT];
-    __shared__ __attribute__((aligned(16))) float Ts[C * LT];
-    __shared__ __attribute__((aligned(16))) f32x4 Ys[4][64];
+    unsigned char *const Qs = reinterpret_cast<unsigned char *>(TQs);
+    float *const Ts = TQs;
+    // exchange slot of (wave w, lane): upper block (0,1), (0,2), (0,3) or (1,2) of N
+    auto ys_slot = [&](int w, int ln) {
+        const int bi = w < 3 ? 0 : 1, bj = w < 3 ? w + 1 : 2;
+        return reinterpret_cast<f32x4 *>(Ns + (16 * bi + (ln >> 2)) * LT + 16 * bj + 4 * (ln & 3));
+    };
     __shared__ double lgs[C];
     __shared__ float bes[C];
 
@@ -240,13 +251,6 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
         }
         lgs[lane] = x;
         bes[lane] = ok ? b_raw : 0.f;
-    }
-    // the strictly upper 16x16 blocks of T are zero
-    for (int idx = t; idx < 6 * 256; idx += 256) {
-        const int blk = idx >> 8, e = idx & 255;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
     }
     wait_vmcnt<0>();   // this wave's direct loads of the K and Q tiles landed
     __syncthreads();   // ... and the other waves'.
@@ -324,6 +328,14 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
     }
     __syncthreads();
 
+    // the strictly upper 16x16 blocks of T are zero (T shares storage with the Q
+    // tile, which phase 2 was the last to read)
+    for (int idx = t; idx < 6 * 256; idx += 256) {
+        const int blk = idx >> 8, e = idx & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
+    }
     // (3) diagonal block `wave` of T by forward substitution: lane column c = lr
     {
         float tv[16];
@@ -381,7 +393,7 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
             b_cols(Ts, 16 * kb, 16 * qq, bb);
             y = mma4s(a, bb, y);
         }
-        Ys[wave][lane] = y;
+        *ys_slot(wave, lane) = y;
     }
     __syncthreads();
     {
@@ -391,7 +403,7 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
             if (kb > p) continue;   // T_BB is block lower triangular
             float a[4];
             a_rows(Ts, 16 * (2 + p), 16 * (2 + kb), a);
-            const f32x4 yv = Ys[2 * kb + qq][lane];
+            const f32x4 yv = *ys_slot(2 * kb + qq, lane);
             const float yb[4] = {yv[0], yv[1], yv[2], yv[3]};
             z = mma4s(a, yb, z);
         }
@@ -417,41 +429,52 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
         }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) bcs[ct] = bes[16 * ct + lr];
-    float am[4][2][8], aw[4][2][8];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const int c = 16 * ct + lr;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
-                const float tb = Ts[m * LT + c] * bcs[ct];
-                am[ct][s][jj] = tb;
-                aw[ct][s][jj] = tb * gw[s][jj];
-            }
-    }
-    // (7) W^T tiles: rows c (token), columns = this wave's S rows; lane column
-    // lr of tile tt is S row RW wave + 4 NT (lr / 4) + 4 tt + lr % 4
+    // K^T fragments of this wave's W rows (B operand of W^T, k = token m)
+    float bk[NT][2][8];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
         const int i = RW * wave + 4 * NT * (lr >> 2) + 4 * tt + (lr & 3);
-        float bk[2][8];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
-                bk[s][jj] = tile_elem<D, TIn>(Ks, m, i);
+                bk[tt][s][jj] = tile_elem<D, TIn>(Ks, m, i);
             }
+    }
+    // (7, 8) per output k-step s2 of the carry (c-tiles 2 s2, 2 s2 + 1): the Tb
+    // fragments of those two c-tiles, then the W^T tiles (rows c, columns = this
+    // wave's S rows; lane column lr of tile tt is S row RW wave + 4 NT (lr / 4) +
+    // 4 tt + lr % 4; Tb scaled by gamma_C / gamma_m) and the M^T tile (rows c,
+    // columns = output tokens 16 wave + lr; B = P^T from registers, k-step s
+    // covering the m-tiles 2s, 2s+1)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {   // output k-step of the carry: c-tiles 2 s2, 2 s2 + 1
+    for (int s2 = 0; s2 < 2; ++s2) {
+        float tb[2][2][8];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int ct = 2 * s2 + h2, c = 16 * ct + lr;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
+                    tb[h2][s][jj] = Ts[m * LT + c] * bcs[ct];
+                }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
             f32x4 acc[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 2; ++s) acc[h2] = mma8<false>(aw[2 * s2 + h2][s], bk[s], acc[h2]);
+                for (int s = 0; s < 2; ++s) {
+                    float aw[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) aw[jj] = tb[h2][s][jj] * gw[s][jj];
+                    acc[h2] = mma8<false>(aw, bk[tt][s], acc[h2]);
+                }
             }
             float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
             __bf16 vh[8], vl[8];
@@ -460,29 +483,26 @@ __global__ __launch_bounds__(256) void k_scan_prep(const TIn *__restrict__ q,
             *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
             *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
         }
-    }
-    // (8) M^T tiles: rows c, columns = output tokens 16 wave + lr; B = P^T from
-    // registers (k-step s covers the m-tiles 2s, 2s+1)
+        {
+            f32x4 acc[2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        f32x4 acc[2];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (2 * s > wave) continue;   // P[r][m] = 0 for m > r
-                const float bp[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
-                                     pv[2 * s + 1][0], pv[2 * s + 1][1], pv[2 * s + 1][2], pv[2 * s + 1][3]};
-                acc[h2] = mma8<false>(am[2 * s2 + h2][s], bp, acc[h2]);
+                for (int s = 0; s < 2; ++s) {
+                    if (2 * s > wave) continue;   // P[r][m] = 0 for m > r
+                    const float bp[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
+                                         pv[2 * s + 1][0], pv[2 * s + 1][1], pv[2 * s + 1][2], pv[2 * s + 1][3]};
+                    acc[h2] = mma8<false>(tb[h2][s], bp, acc[h2]);
+                }
             }
+            float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+            __bf16 vh[8], vl[8];
+            split_bf16(v, vh, vl);
+            bf16 *dst = dM + ((((int64_t)wave * 2 + s2) * 2) * 64 + lane) * 8;
+            *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
+            *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
         }
-        float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
-        __bf16 vh[8], vl[8];
-        split_bf16(v, vh, vl);
-        bf16 *dst = dM + ((((int64_t)wave * 2 + s2) * 2) * 64 + lane) * 8;
-        *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
-        *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
     }
     // (9) gamma
     if (t < C) wsg[cid * C + t] = __expf((float)lgs[t]);
