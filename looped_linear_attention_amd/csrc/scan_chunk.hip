@@ -159,7 +159,7 @@ __device__ __forceinline__ f32x4 mma4s(const float (&a)[4], const float (&b)[4],
 }
 
 template <int D, typename TIn, bool GP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scan_prep(const TIn *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_prep(const TIn *__restrict__ q,
                                                    const TIn *__restrict__ k,
                                                    const float *__restrict__ alpha,
                                                    const float *__restrict__ beta,
@@ -173,15 +173,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     constexpr int KS = D / 32;               // k-steps of the D contractions
     constexpr int RW = D / 4, NT = RW / 16;  // W rows per wave, 16-row tiles per wave
     using KT = KTile<D, TIn>;
-    // LDS (52 KB with bf16 dk = 128, so three workgroups fit on a CU): the Q tile
-    // is read only by phase 2 and T is written from phase 3 on, so they share
-    // storage; the phase-5 exchange lives in the strictly upper 16x16 blocks of
-    // N, which are never written or read otherwise.
+    // LDS (35 KB with bf16 dk = 128, so four workgroups fit on a CU): one array
+    // holds the Q tile until phase 2 has read it, then N, and T is formed in
+    // place over N (each block of N is read, by the wave that overwrites it or
+    // before a barrier, before T's block replaces it); the phase-5 exchange
+    // lives in the strictly upper 16x16 blocks, which are zeroed after it.
     constexpr int TQ_FLOATS = C * LT > KT::BYTES / 4 ? C * LT : KT::BYTES / 4;
     __shared__ __attribute__((aligned(16))) unsigned char Ks[KT::BYTES];
     __shared__ __attribute__((aligned(16))) float TQs[TQ_FLOATS];
-    __shared__ __attribute__((aligned(16))) float Ns[C * LT];
     unsigned char *const Qs = reinterpret_cast<unsigned char *>(TQs);
+    float *const Ns = TQs;
     float *const Ts = TQs;
     // exchange slot of (wave w, lane): upper block (0,1), (0,2), (0,3) or (1,2) of N
     auto ys_slot = [&](int w, int ln) {
@@ -265,21 +266,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) kk[tn] = kq[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (!F32) {
-            bf16x8 ka[KS], qa[KS], kb[4][KS];
+            bf16x8 ka[KS], qa[KS];
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 ka[s] = tile_bf8<D>(Ks, r_a, 32 * s + 8 * lg);
                 qa[s] = tile_bf8<D>(Qs, r_a, 32 * s + 8 * lg);
-#pragma unroll
-                for (int tn = 0; tn < 4; ++tn) kb[tn][s] = tile_bf8<D>(Ks, 16 * tn + lr, 32 * s + 8 * lg);
             }
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
                 if (tn <= wave) {
+                    bf16x8 kb[KS];
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) kb[s] = tile_bf8<D>(Ks, 16 * tn + lr, 32 * s + 8 * lg);
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
-                        kk[tn] = mfma16x16x32(ka[s], kb[tn][s], kk[tn]);   // K_r . K_i   (rows r of this wave)
-                        kq[tn] = mfma16x16x32(kb[tn][s], qa[s], kq[tn]);   // K_m . Q_r   (rows m of tile tn)
+                        kk[tn] = mfma16x16x32(ka[s], kb[s], kk[tn]);   // K_r . K_i   (rows r of this wave)
+                        kq[tn] = mfma16x16x32(kb[s], qa[s], kq[tn]);   // K_m . Q_r   (rows m of tile tn)
                     }
                 }
         } else {
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                     }
                 }
         }
+        __syncthreads();   // every wave has read the Q tile, which N overwrites
         // decay factors: N[row][col] uses Gam(row, col), P[r][m] uses Gam(r, m)
         double lrow[4], lcol[4], lm[4][4];
         float brow[4];
@@ -328,14 +331,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
     __syncthreads();
 
-    // the strictly upper 16x16 blocks of T are zero (T shares storage with the Q
-    // tile, which phase 2 was the last to read)
-    for (int idx = t; idx < 6 * 256; idx += 256) {
-        const int blk = idx >> 8, e = idx & 255;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
-    }
     // (3) diagonal block `wave` of T by forward substitution: lane column c = lr
     {
         float tv[16];
@@ -411,6 +406,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         for (int j = 0; j < 4; ++j) Ts[(16 * (2 + p) + 4 * lg + j) * LT + 16 * qq + lr] = -z[j];
     }
     __syncthreads();
+    // the strictly upper 16x16 blocks of T are zero (they held the exchange)
+    for (int idx = t; idx < 6 * 256; idx += 256) {
+        const int blk = idx >> 8, e = idx & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
+    }
+    __syncthreads();
 
     // (6) Tb^T fragments, A operand over k = token m (carry slot order):
     // Tb[m][c] = T[m][c] beta_c; the W variant also carries gamma_C / gamma_m
@@ -429,7 +432,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) bcs[ct] = bes[16 * ct + lr];
-    // K^T fragments of this wave's W rows (B operand of W^T, k = token m)
+    // K^T fragments of this wave's W rows (B operand of W^T, k = token m), each
+    // scaled by gamma_C / gamma_m of its token
     float bk[NT][2][8];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
@@ -439,70 +443,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
-                bk[tt][s][jj] = tile_elem<D, TIn>(Ks, m, i);
+                bk[tt][s][jj] = tile_elem<D, TIn>(Ks, m, i) * gw[s][jj];
             }
     }
-    // (7, 8) per output k-step s2 of the carry (c-tiles 2 s2, 2 s2 + 1): the Tb
-    // fragments of those two c-tiles, then the W^T tiles (rows c, columns = this
-    // wave's S rows; lane column lr of tile tt is S row RW wave + 4 NT (lr / 4) +
-    // 4 tt + lr % 4; Tb scaled by gamma_C / gamma_m) and the M^T tile (rows c,
+    // (7, 8) per output k-step s2 of the carry (c-tiles 2 s2, 2 s2 + 1) and per
+    // c-tile h2 of it: the Tb fragments of the c-tile, then its half of the W^T
+    // tiles (rows c, columns = this wave's S rows; lane column lr of tile tt is S
+    // row RW wave + 4 NT (lr / 4) + 4 tt + lr % 4) and of the M^T tile (rows c,
     // columns = output tokens 16 wave + lr; B = P^T from registers, k-step s
     // covering the m-tiles 2s, 2s+1)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-        float tb[2][2][8];
+        f32x4 aw_acc[NT][2], am_acc[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int ct = 2 * s2 + h2, c = 16 * ct + lr;
+            float tb[2][8];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     const int m = 32 * s + (jj < 4 ? 4 * lg + jj : 16 + 4 * lg + jj - 4);
-                    tb[h2][s][jj] = Ts[m * LT + c] * bcs[ct];
+                    tb[s][jj] = Ts[m * LT + c] * bcs[ct];
                 }
-        }
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 acc[2];
+            for (int tt = 0; tt < NT; ++tt) {
+                aw_acc[tt][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    float aw[8];
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) aw[jj] = tb[h2][s][jj] * gw[s][jj];
-                    acc[h2] = mma8<false>(aw, bk[tt][s], acc[h2]);
-                }
+                for (int s = 0; s < 2; ++s) aw_acc[tt][h2] = mma8<false>(tb[s], bk[tt][s], aw_acc[tt][h2]);
             }
+            am_acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (2 * s > wave) continue;   // P[r][m] = 0 for m > r
+                const float bp[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
+                                     pv[2 * s + 1][0], pv[2 * s + 1][1], pv[2 * s + 1][2], pv[2 * s + 1][3]};
+                am_acc[h2] = mma8<false>(tb[s], bp, am_acc[h2]);
+            }
+        }
+        auto store_pair = [&](const f32x4 (&acc)[2], bf16 *dst) __attribute__((always_inline)) {
             float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
             __bf16 vh[8], vl[8];
             split_bf16(v, vh, vl);
-            bf16 *dst = dW + ((((int64_t)(wave * NT + tt) * 2 + s2) * 2) * 64 + lane) * 8;
             *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
             *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
-        }
-        {
-            f32x4 acc[2];
+        };
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (2 * s > wave) continue;   // P[r][m] = 0 for m > r
-                    const float bp[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
-                                         pv[2 * s + 1][0], pv[2 * s + 1][1], pv[2 * s + 1][2], pv[2 * s + 1][3]};
-                    acc[h2] = mma8<false>(tb[h2][s], bp, acc[h2]);
-                }
-            }
-            float v[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
-            __bf16 vh[8], vl[8];
-            split_bf16(v, vh, vl);
-            bf16 *dst = dM + ((((int64_t)wave * 2 + s2) * 2) * 64 + lane) * 8;
-            *reinterpret_cast<bf16x8 *>(dst) = pack8(vh);
-            *reinterpret_cast<bf16x8 *>(dst + 8 * 64) = pack8(vl);
-        }
+        for (int tt = 0; tt < NT; ++tt)
+            store_pair(aw_acc[tt], dW + ((((int64_t)(wave * NT + tt) * 2 + s2) * 2) * 64 + lane) * 8);
+        store_pair(am_acc, dM + ((((int64_t)wave * 2 + s2) * 2) * 64 + lane) * 8);
     }
     // (9) gamma
     if (t < C) wsg[cid * C + t] = __expf((float)lgs[t]);
