@@ -41,7 +41,7 @@ def norm_err(g, r) -> float:
     return float(np.linalg.norm(g - r) / (nr if nr > 0 else 1.0))
 
 
-def loop_envelope(w, x, B, L, runs: int = 3):
+def loop_envelope(w, x, B, L, runs: int = 3, h_in=None, loops=None):
     """Oracle loop run plus the spread of valid bf16 implementations around it.
 
     For bf16 workloads the looped result is not unique: every bf16 rounding of an fp32 intermediate that
@@ -49,17 +49,21 @@ def loop_envelope(w, x, B, L, runs: int = 3):
     decisions.  The oracle is re-run as other valid implementations would compute it -- once with the q/k/v
     dot products summed and normalised in fp32 by a library matmul, and with its rounding inputs moved by
     one fp32 ulp (seeded) -- and the largest per-loop deviation from the reference run is the spread.
+    ``h_in`` (default: the workload's h0 rows) is the loop input and ``loops`` (default: all) a slice of
+    the loops whose residual gates are used, so that one loop can be run from a given h^(t-1).
     Returns (reference dict, spread dict) with per-loop lists "h_max", "h_norm", "s_max", "s_norm".
     """
     import oracle
-    args = (x["h0"][:B, :L], x["Wq"], x["Wk"], x["Wv"], x["wa"], x["wb"], x["rho"], w.H, w.dk, w.dv,
-            w.alpha_lo, w.act)
+    rho = x["rho"] if loops is None else x["rho"][loops]
+    h = x["h0"][:B, :L] if h_in is None else h_in
+    T = rho.shape[0]
+    args = (h, x["Wq"], x["Wk"], x["Wv"], x["wa"], x["wb"], rho, w.H, w.dk, w.dv, w.alpha_lo, w.act)
     ref = oracle.loop_prefill(*args, keep_loops=True, keep_states=True)
-    sp = {k: [0.0] * w.T for k in ("h_max", "h_norm", "s_max", "s_norm")}
+    sp = {k: [0.0] * T for k in ("h_max", "h_norm", "s_max", "s_norm")}
     variants = [dict(fp32_sum=True)] + [dict(jitter=np.random.default_rng(9000 + i)) for i in range(runs - 1)]
     for kw in variants:
         j = oracle.loop_prefill(*args, keep_loops=True, keep_states=True, **kw)
-        for t in range(w.T):
+        for t in range(T):
             sp["h_max"][t] = max(sp["h_max"][t], rel_err(j["loops"][t], ref["loops"][t]))
             sp["h_norm"][t] = max(sp["h_norm"][t], norm_err(j["loops"][t], ref["loops"][t]))
             sp["s_max"][t] = max(sp["s_max"][t], rel_err(j["states"][t], ref["states"][t]))
