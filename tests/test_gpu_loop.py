@@ -206,6 +206,49 @@ def test_loop_prefill_full_size_prefix(name, prefix):
     _check_loop(w, x, w.B, w.L, TOL_BF16, gpu=(g_h, None, g_l), Lcmp=prefix)
 
 
+def _forced_head(w, x, B, L, t, head, h_prev, x_in, **kw):
+    """Oracle loop t of one head from a given h^(t-1) (fp64 [B, L, d]) and its bf16 rounding x_in: the head's
+    q/k/v and gate columns only, its scan, its residual.  Returns (h^(t) columns [B, L, dv], S_final [B, dk, dv])."""
+    cq, cv = slice(head * w.dk, (head + 1) * w.dk), slice(head * w.dv, (head + 1) * w.dv)
+    q, k, v, al, be = oracle.project(x_in, x["Wq"][:, cq], x["Wk"][:, cq], x["Wv"][:, cv], x["wa"][:, head:head + 1],
+                                     x["wb"][:, head:head + 1], 1, w.dk, w.dv, w.alpha_lo, w.act, **kw)
+    o, st = oracle.scan(q.reshape(B, L, 1, w.dk), k.reshape(B, L, 1, w.dk), v.reshape(B, L, 1, w.dv),
+                        al.reshape(B, L, 1), be.reshape(B, L, 1))
+    rho = x["rho"][t].double().numpy()[cv]
+    return o.reshape(B, L, w.dv) + rho * h_prev[:, :, cv], st[:, 0]
+
+
+@pytest.mark.parametrize("name,head", [("prefill_b4_l8192", 0), ("prefill_b1_l32768", 15)])
+def test_loop_prefill_full_size_heads(name, head):
+    """Full-size launch (as benchmarked), every token of one head through all four loops, teacher-forced: loop t
+    of the head is rerun by the oracle from the GPU's own h^(t-1) (only that head's projection columns and scan
+    are needed) and the GPU's h^(t) columns and final states are held to that one loop's envelope (a library
+    fp32 matmul and a one-ulp jitter of every bf16 rounding; bars as in _check_forced)."""
+    w = synth.workload(name)
+    say(f"[loop_prefill] {name} full launch, head {head} teacher-forced over all {w.L} tokens")
+    x = synth.prefill_inputs(w)
+    B, L = w.B, w.L
+    _, g_s, g_l = _loop_gpu(w, x, B, L, keep=True)
+    cv = slice(head * w.dv, (head + 1) * w.dv)
+    for t in range(w.T):
+        h_prev = x["h0"].double().numpy() if t == 0 else g_l[t - 1].double().numpy()
+        flat = h_prev.reshape(B * L, w.d)
+        rh, rs = _forced_head(w, x, B, L, t, head, h_prev, oracle.round_bf16(flat))
+        runs = [_forced_head(w, x, B, L, t, head, h_prev, oracle.round_bf16(flat), fp32_sum=True),
+                _forced_head(w, x, B, L, t, head, h_prev, oracle.round_bf16(flat, np.random.default_rng(9100 + t)),
+                             jitter=np.random.default_rng(9200 + t))]
+        sp = dict(h_max=max(rel_err(a, rh) for a, _ in runs), h_norm=max(norm_err(a, rh) for a, _ in runs),
+                  s_max=max(rel_err(b, rs) for _, b in runs), s_norm=max(norm_err(b, rs) for _, b in runs))
+        gh, gs = g_l[t].double().numpy()[:, :, cv], g_s[t].double().numpy()[:, head]
+        em, en = rel_err(gh, rh), norm_err(gh, rh)
+        es, esn = rel_err(gs, rs), norm_err(gs, rs)
+        bm, bn = envelope_bar(sp["h_max"], TOL_BF16, ENV_MAX), envelope_bar(sp["h_norm"], 1e-4, ENV_NORM)
+        bs, bsn = envelope_bar(sp["s_max"], TOL_BF16, ENV_MAX), envelope_bar(sp["s_norm"], 1e-4, ENV_NORM)
+        say(f"    loop {t + 1}: h max-rel {em:.2e} (bar {bm:.2e}) normwise {en:.2e} (bar {bn:.2e}); "
+            f"state max-rel {es:.2e} (bar {bs:.2e}) normwise {esn:.2e} (bar {bsn:.2e})")
+        assert em <= bm and en <= bn and es <= bs and esn <= bsn
+
+
 def test_loop_prefill_bf16_d64_h3_wide():
     """1100 tokens of three 64-wide heads: the wide projection, whose two column tiles each leave a partial
     gate pre-activation (the second over the single remaining 64-channel block) for the chunk preparation."""
