@@ -44,10 +44,22 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
 // x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
 template <int N>
 __device__ __forceinline__ void split_bf16(const float (&x)[N], __bf16 (&hi)[N], __bf16 (&lo)[N]) {
+    static_assert(N % 2 == 0, "pairs");
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    // two elements per conversion; a bf16 value widens to fp32 by moving its
+    // bits to the upper half of the word
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        hi[i] = (bf16)x[i];
-        lo[i] = (bf16)(x[i] - (float)hi[i]);
+    for (int i = 0; i < N; i += 2) {
+        const bf16x2 h = __builtin_convertvector((f32x2{x[i], x[i + 1]}), bf16x2);
+        unsigned hu;
+        __builtin_memcpy(&hu, &h, 4);
+        const f32x2 r = {x[i] - __uint_as_float(hu << 16), x[i + 1] - __uint_as_float(hu & 0xffff0000u)};
+        const bf16x2 l = __builtin_convertvector(r, bf16x2);
+        hi[i] = h[0];
+        hi[i + 1] = h[1];
+        lo[i] = l[0];
+        lo[i + 1] = l[1];
     }
 }
 
