@@ -496,13 +496,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wt = wave >> 2, wf = wave & 3;
-    // Workgroup ids are dealt to the 8 XCDs round-robin; give each XCD a
-    // contiguous run of tiles (column-tile major) so that its L2 serves few
-    // column tiles.
+    // Workgroup ids are dealt to the 8 XCDs round-robin.  XCD x takes the
+    // column tiles x, x + 8, ... (each one's token tiles in order), so its L2
+    // serves few column tiles, and column tile n (one head for 128-wide heads)
+    // is written on XCD n mod 8, where the scan kernels of that head run.
+    // Otherwise each XCD takes a contiguous run of tiles, column-tile major.
     const int ntot = m_tiles * n_tiles;
     const int id = blockIdx.x;
-    const int tix = (ntot % 8 == 0) ? (id % 8) * (ntot / 8) + id / 8 : id;
-    const int n_tile = tix / m_tiles, m_tile = tix % m_tiles;
+    int n_tile, m_tile;
+    if (n_tiles % 8 == 0) {
+        const int kx = id / 8;
+        n_tile = id % 8 + 8 * (kx / m_tiles);
+        m_tile = kx % m_tiles;
+    } else {
+        const int tix = (ntot % 8 == 0) ? (id % 8) * (ntot / 8) + id / 8 : id;
+        n_tile = tix / m_tiles;
+        m_tile = tix % m_tiles;
+    }
     const int m0 = m_tile * WM, n0 = n_tile * WN;
     const int qkv_rows = H * 3 * D;
     const int n_rows = min(WN, qkv_rows - n0);

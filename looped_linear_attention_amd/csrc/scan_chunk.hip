@@ -195,7 +195,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // heads run fastest along x: with H a multiple of 8, head h runs on XCD
+    // h mod 8, where the projection wrote its q and k and its carry runs
+    const int h = blockIdx.x % H, chunk = blockIdx.x / H, b = blockIdx.y;
     const int c0 = chunk * C;
     const int64_t tok0 = (int64_t)b * L + c0;
 
@@ -1051,7 +1053,8 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
                             GateSrc gs, ChunkWs ws, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
-    dim3 grid(Nc, H, B);
+    if ((int64_t)Nc * H > INT32_MAX) return hipErrorInvalidValue;
+    dim3 grid((unsigned)(Nc * H), B);
     if (gs.zp && (f32 || gs.P < 1 || gs.P > 16)) return hipErrorInvalidValue;
 #define PREP(DD, T, GP)                                                                            \
     launch_kernel((k_scan_prep<DD, T, GP>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,     \
