@@ -313,10 +313,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // With one head per column tile, a sequence of 4096 tokens and 16 heads is
 // exactly 256 tiles, one per CU.
 // Gate columns (GZ): the 2H <= 32 gate rows are one more 32-row A tile.  Column
-// tile j takes the gate product over channel blocks 2j and 2j+1 (d = H D gives
-// at most two blocks per column tile) and writes it as an fp32 partial
+// tile j takes the gate product over one pair of channel blocks (2p, 2p+1;
+// d = H D gives at most two blocks per column tile, and the pairs p of the
+// column tiles are a permutation of all pairs) and writes it as an fp32 partial
 // zp[j][2H][M]; the consumer sums the partials of a token in tile order.  The
-// k-loop of tile j starts at block 2j, so both gate blocks are in the two
+// k-loop of tile j starts at block 2p, so both gate blocks are in the two
 // stages after the prologue, where the gate MFMAs run before the main
 // accumulators are live.  Without GZ the gate columns run in k_gates.
 constexpr int WM = 256, WN = 384, WK = 64, WSTAGES = 2;
@@ -503,8 +504,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Otherwise each XCD takes a contiguous run of tiles, column-tile major.
     const int ntot = m_tiles * n_tiles;
     const int id = blockIdx.x;
+    const bool x8 = n_tiles % 8 == 0;
     int n_tile, m_tile;
-    if (n_tiles % 8 == 0) {
+    if (x8) {
         const int kx = id / 8;
         n_tile = id % 8 + 8 * (kx / m_tiles);
         m_tile = kx % m_tiles;
@@ -521,8 +523,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16 *xb = x + (int64_t)m0 * K, *wb = Wp + (int64_t)n0 * K;
     const int nkb = K / WK;
     // channel offset of the i-th block of this tile's k order (blocks kb0,
-    // kb0+1, ... wrapping around); past the end it repeats the last one
-    const int kb0 = GZ ? 2 * n_tile : 0;
+    // kb0+1, ... wrapping around); past the end it repeats the last one.  The
+    // gate block pair of column tile n is pair n, or with the XCD dealing above
+    // pair r (n mod 8) + n / 8 (r = n_tiles / 8), so that the column tiles of
+    // one XCD start next to each other in k and share their token tile's lines
+    // in L2.
+    const int gpair = x8 ? (n_tiles / 8) * (n_tile % 8) + n_tile / 8 : n_tile;
+    const int kb0 = GZ ? 2 * gpair : 0;
     auto kblock = [&](int i) {
         const int b = kb0 + min(i, nkb - 1);
         return (b < nkb ? b : b - nkb) * WK;

@@ -24,8 +24,8 @@ import torch
 import looped_linear_attention_amd as gl
 import oracle
 import synth
-from helpers import (ENV_MAX, ENV_NORM, TOL_BF16, TOL_F32, bf16_ulp, dev, envelope_bar, loop_envelope,
-                     norm_err, rel_err, say)
+from helpers import (ENV_MAX, ENV_NORM, TOL_BF16, TOL_F32, bf16_ulp, dev, envelope_bar, fp32_blocked,
+                     loop_envelope, norm_err, rel_err, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -157,14 +157,15 @@ def _check_state(g, r, sp, t, tol):
 
 
 def _check_forced(w, x, B, L, tol, g_s, g_l):
-    """Teacher-forced check: loop t is rerun by the oracle (with its envelope) from the GPU's own fp32
-    h^(t-1), and the GPU's h^(t) and final state of loop t are held to that one loop's bars.
+    """Teacher-forced check: loop t is rerun by the oracle (with its envelope, including eight variants whose
+    q/k/v sums accumulate as an MFMA k-loop does) from the GPU's own fp32 h^(t-1), and the GPU's h^(t) and
+    final state of loop t are held to that one loop's bars.
 
     This gates what each loop computes, which is unique up to the one loop's bf16 rounding decisions; the
     free-running comparison also carries every earlier loop's valid rounding decisions, amplified."""
     for t in range(w.T):
         h_in = x["h0"][:B, :L] if t == 0 else g_l[t - 1].double().numpy()
-        r, sp = loop_envelope(w, x, B, L, h_in=h_in, loops=slice(t, t + 1))
+        r, sp = loop_envelope(w, x, B, L, h_in=h_in, loops=slice(t, t + 1), perms=8)
         em, en = rel_err(g_l[t], r["loops"][0]), norm_err(g_l[t], r["loops"][0])
         bm, bn = envelope_bar(sp["h_max"][0], tol, ENV_MAX), envelope_bar(sp["h_norm"][0], 1e-4, ENV_NORM)
         say(f"    loop {t + 1} from the GPU's h^({t}): h max-rel {em:.2e} (bar {bm:.2e}); "
@@ -206,12 +207,20 @@ def test_loop_prefill_full_size_prefix(name, prefix):
     _check_loop(w, x, w.B, w.L, TOL_BF16, gpu=(g_h, None, g_l), Lcmp=prefix)
 
 
-def _forced_head(w, x, B, L, t, head, h_prev, x_in, **kw):
+def _forced_head(w, x, B, L, t, head, h_prev, x_in, rot=None, **kw):
     """Oracle loop t of one head from a given h^(t-1) (fp64 [B, L, d]) and its bf16 rounding x_in: the head's
-    q/k/v and gate columns only, its scan, its residual.  Returns (h^(t) columns [B, L, dv], S_final [B, dk, dv])."""
+    q/k/v and gate columns only, its scan, its residual (``rot``: q/k/v summed as an MFMA k-loop does, see
+    helpers.fp32_blocked).  Returns (h^(t) columns [B, L, dv], S_final [B, dk, dv])."""
     cq, cv = slice(head * w.dk, (head + 1) * w.dk), slice(head * w.dv, (head + 1) * w.dv)
-    q, k, v, al, be = oracle.project(x_in, x["Wq"][:, cq], x["Wk"][:, cq], x["Wv"][:, cv], x["wa"][:, head:head + 1],
+    Wq, Wk, Wv = (x[n][:, c].double().numpy() for n, c in (("Wq", cq), ("Wk", cq), ("Wv", cv)))
+    q, k, v, al, be = oracle.project(x_in, Wq, Wk, Wv, x["wa"][:, head:head + 1],
                                      x["wb"][:, head:head + 1], 1, w.dk, w.dv, w.alpha_lo, w.act, **kw)
+    if rot is not None:
+        f32 = np.float32
+        qf, kf = fp32_blocked(x_in, Wq, rot), fp32_blocked(x_in, Wk, rot)
+        v = oracle.round_bf16(fp32_blocked(x_in, Wv, rot))
+        q = oracle.round_bf16(qf / np.sqrt(np.sum(qf * qf, axis=-1, keepdims=True, dtype=f32) + f32(1e-6)))
+        k = oracle.round_bf16(kf / np.sqrt(np.sum(kf * kf, axis=-1, keepdims=True, dtype=f32) + f32(1e-6)))
     o, st = oracle.scan(q.reshape(B, L, 1, w.dk), k.reshape(B, L, 1, w.dk), v.reshape(B, L, 1, w.dv),
                         al.reshape(B, L, 1), be.reshape(B, L, 1))
     rho = x["rho"][t].double().numpy()[cv]
@@ -223,7 +232,7 @@ def test_loop_prefill_full_size_heads(name, head):
     """Full-size launch (as benchmarked), every token of one head through all four loops, teacher-forced: loop t
     of the head is rerun by the oracle from the GPU's own h^(t-1) (only that head's projection columns and scan
     are needed) and the GPU's h^(t) columns and final states are held to that one loop's envelope (a library
-    fp32 matmul and a one-ulp jitter of every bf16 rounding; bars as in _check_forced)."""
+    fp32 matmul, a one-ulp jitter of every bf16 rounding and two MFMA-order sums; bars as in _check_forced)."""
     w = synth.workload(name)
     say(f"[loop_prefill] {name} full launch, head {head} teacher-forced over all {w.L} tokens")
     x = synth.prefill_inputs(w)
@@ -237,6 +246,8 @@ def test_loop_prefill_full_size_heads(name, head):
         runs = [_forced_head(w, x, B, L, t, head, h_prev, oracle.round_bf16(flat), fp32_sum=True),
                 _forced_head(w, x, B, L, t, head, h_prev, oracle.round_bf16(flat, np.random.default_rng(9100 + t)),
                              jitter=np.random.default_rng(9200 + t))]
+        x_ref = oracle.round_bf16(flat)
+        runs += [_forced_head(w, x, B, L, t, head, h_prev, x_ref, rot=r) for r in (0, w.d // 32)]
         sp = dict(h_max=max(rel_err(a, rh) for a, _ in runs), h_norm=max(norm_err(a, rh) for a, _ in runs),
                   s_max=max(rel_err(b, rs) for _, b in runs), s_norm=max(norm_err(b, rs) for _, b in runs))
         gh, gs = g_l[t].double().numpy()[:, :, cv], g_s[t].double().numpy()[:, head]
