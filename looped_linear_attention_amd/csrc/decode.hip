@@ -100,15 +100,15 @@ __global__ __launch_bounds__(256) void k_decode(const TIn *__restrict__ q, const
             *reinterpret_cast<float4 *>(o + vec + j0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
         }
     }
+    // the updated state is written with non-temporal stores: the next step of
+    // this loop comes after the other loops' states have streamed through
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int ii = 0; ii < RPT; ++ii) {
         const float ki = ks[rg + RG * ii];
-        float4 s = sr[ii];
-        s.x = al * s.x + ki * u[0];
-        s.y = al * s.y + ki * u[1];
-        s.z = al * s.z + ki * u[2];
-        s.w = al * s.w + ki * u[3];
-        S[(rg + RG * ii) * CG + cg] = s;
+        const float4 s = sr[ii];
+        const f32x4v sv = {al * s.x + ki * u[0], al * s.y + ki * u[1], al * s.z + ki * u[2], al * s.w + ki * u[3]};
+        __builtin_nontemporal_store(sv, reinterpret_cast<f32x4v *>(&S[(rg + RG * ii) * CG + cg]));
     }
 }
 
