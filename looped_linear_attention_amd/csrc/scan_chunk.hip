@@ -759,6 +759,10 @@ __device__ __forceinline__ f32x4 mma_hl(const bf16x8 &ah, const bf16x8 &al, cons
 // is rewritten at chunk cc+2 (after B0) and E at chunk cc+2 (after B1), after
 // the output waves used them at cc+1.
 constexpr int CARRY_THREADS = 576;
+// Chunks ahead of the output step that the output waves' L2 prefetch touches.
+// Where a loop's operands do not fit in the MALL (32k tokens: about 1.2 GB) the
+// direct loads otherwise wait on HBM latency.
+constexpr int PF_AHEAD = 3;
 
 // h_prev at the lane's 4 (token, column) cells of one output step
 struct OutIn {
@@ -912,10 +916,50 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         OutIn in0, in1;
         // one chunk per step, two per iteration so that the register set and the
         // LDS parity are compile-time choices
+        // L2 prefetch, PF_AHEAD chunks ahead: one load touching each 128-byte line of
+        // that chunk's K, Q, W, M, V, h_prev and gamma for this head, the lines dealt
+        // over the head's slice workgroups (which share an XCD's L2).  The loaded word
+        // is consumed two chunks later, long after it has arrived.
+        unsigned pfv[2] = {0u, 0u};
+        auto prefetch = [&](auto pc, int cc) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
+            constexpr int RL = G::ROWB / 128;
+            constexpr int KL = C * RL, WL = G::W_BYTES / 128, ML = G::M_BYTES / 128;
+            constexpr int HES = RES == 2 ? 2 : 4;
+            constexpr int HRL = RES ? D * HES / 128 : 0, HL = C * HRL, GL = C * 4 / 128;
+            constexpr int NL = 3 * KL + WL + ML + HL + GL;
+            asm volatile("" ::"v"(pfv[P]));
+            const int j = slice + G::NSL * (lane * 4 + ot);
+            if (j < NL) {
+                const int cp = min(cc + PF_AHEAD, Nc - 1), c0p = cp * C;
+                const char *p;
+                int jj = j;
+                auto row_tok = [&](int r) { return tokb + min(c0p + r, L - 1); };
+                if (jj < KL) {
+                    p = reinterpret_cast<const char *>(k + (row_tok(jj / RL) * H + h) * D) + (jj % RL) * 128;
+                } else if ((jj -= KL) < KL) {
+                    p = reinterpret_cast<const char *>(q + (row_tok(jj / RL) * H + h) * D) + (jj % RL) * 128;
+                } else if ((jj -= KL) < KL) {
+                    p = reinterpret_cast<const char *>(v + (row_tok(jj / RL) * H + h) * D) + (jj % RL) * 128;
+                } else if ((jj -= KL) < WL) {
+                    p = reinterpret_cast<const char *>(W + (cidb + cp) * D * C) + jj * 128;
+                } else if ((jj -= WL) < ML) {
+                    p = reinterpret_cast<const char *>(M + (cidb + cp) * C * C) + jj * 128;
+                } else if ((jj -= ML) < HL) {
+                    p = reinterpret_cast<const char *>(h_prev) +
+                        (row_tok(jj / HRL) * (int64_t)d + (int64_t)h * D) * HES + (jj % HRL) * 128;
+                } else {
+                    jj -= HL;
+                    p = reinterpret_cast<const char *>(g + (cidb + cp) * C) + jj * 128;
+                }
+                pfv[P] = *reinterpret_cast<const unsigned *>(p);
+            }
+        };
         auto ostep = [&](auto pc, OutIn &cur, OutIn &prev, int cc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;   // parity of chunk cc
             lds_barrier();   // B0
             load_hp(cur, cc);
+            prefetch(pc, cc);
             lds_barrier();   // B1
             if (cc > 0) compute(std::integral_constant<int, 1 - P>(), prev, cc - 1);
             lds_barrier();   // B2
@@ -924,6 +968,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
             ostep(std::integral_constant<int, 0>(), in0, in1, cc);
             if (cc + 1 < Nc) ostep(std::integral_constant<int, 1>(), in1, in0, cc + 1);
         }
+        asm volatile("" ::"v"(pfv[0]), "v"(pfv[1]));
         lds_barrier();   // B3: the last chunk's output operands are visible
         // the last chunk: its S_c and E stay in LDS, nobody rewrites them
         if ((Nc - 1) & 1) compute(std::integral_constant<int, 1>(), in1, Nc - 1);
