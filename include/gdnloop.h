@@ -72,7 +72,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   chunk  must be 64 (tokens per chunk of the chunkwise prefill)
  *   act    dtype of h0 / h_t, of the weights and of q, k, v: GDN_F32 or
  *          GDN_BF16.  alpha, beta, rho, states, o and h outputs are fp32.
- *   alpha_lo  lower bound of the decay gate, in [0, 1)
+ *   alpha_lo  lower bound of the decay gate, in [0, 1]; 1 makes alpha = 1 (the
+ *             delta rule without decay)
  *   norm_eps  epsilon of the q/k L2 normalisation, x / sqrt(sum x^2 + eps)
  */
 typedef struct {

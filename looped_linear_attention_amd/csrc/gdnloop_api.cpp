@@ -63,8 +63,8 @@ gdn_status check_desc(const gdn_desc *d, bool decode) {
     if ((int64_t)d->H * d->dv != d->d)
         return fail(GDN_ERR_SHAPE, "d must equal H*dv (d=%d H=%d dv=%d)", d->d, d->H, d->dv);
     if (decode && d->L != 1) return fail(GDN_ERR_SHAPE, "decode calls need L == 1 (got %d)", d->L);
-    if (!(d->alpha_lo >= 0.f && d->alpha_lo < 1.f))
-        return fail(GDN_ERR_SHAPE, "alpha_lo must be in [0, 1) (got %g)", (double)d->alpha_lo);
+    if (!(d->alpha_lo >= 0.f && d->alpha_lo <= 1.f))
+        return fail(GDN_ERR_SHAPE, "alpha_lo must be in [0, 1] (got %g)", (double)d->alpha_lo);
     if (!(d->norm_eps > 0.f) || !std::isfinite(d->norm_eps))
         return fail(GDN_ERR_SHAPE, "norm_eps must be positive and finite");
     // every tensor must be addressable with 64-bit offsets; keep element counts sane

@@ -60,7 +60,7 @@ def _ws_status(desc, op=gl.GDN_OP_LOOP_PREFILL):
 
 @pytest.mark.parametrize("field,value,code", [
     ("chunk", 32, -3), ("dk", 96, -3), ("dv", 64, -3), ("d", 1000, -2), ("B", 0, -2), ("L", 0, -2),
-    ("T", 0, -2), ("H", 0, -2), ("act", 7, -3), ("alpha_lo", 1.0, -2), ("alpha_lo", -0.1, -2),
+    ("T", 0, -2), ("H", 0, -2), ("act", 7, -3), ("alpha_lo", 1.01, -2), ("alpha_lo", -0.1, -2),
     ("norm_eps", 0.0, -2), ("norm_eps", float("nan"), -2),
 ])
 def test_descriptor_validation(field, value, code):
@@ -68,6 +68,13 @@ def test_descriptor_validation(field, value, code):
     setattr(desc, field, value)
     st, _ = _ws_status(desc)
     assert st == code, gl.gdn_last_error()
+
+
+@pytest.mark.parametrize("alpha_lo", [0.0, 0.9, 1.0])
+def test_alpha_lo_range_accepted(alpha_lo):
+    """alpha_lo = 1 is the delta rule without decay (alpha = 1 for every token)."""
+    desc = gl.make_desc(1, 128, 16, 128, 128, alpha_lo=alpha_lo)
+    assert _ws_status(desc)[0] == 0, gl.gdn_last_error()
 
 
 def test_too_many_heads():

@@ -281,6 +281,31 @@ def test_loop_prefill_b2_ragged_wide():
     _check_loop(w, x, 2, 700, TOL_BF16, forced=True)
 
 
+@pytest.mark.parametrize("name,L", [("prefill_b1_l4096", 300)])
+def test_loop_prefill_no_decay(name, L):
+    """alpha_lo = 1: every gate alpha is exactly 1, the loops run the delta rule without decay (DeltaNet).
+
+    bf16 only at the loop level: with fp32 inputs one scan without decay lands about 3e-5 from the oracle (the
+    split-bf16 products carry ~16 bits and no decay damps them; the fp32 scan-level cases with alpha = 1 pass the
+    1e-4 bar), and four loops compound that to 1.1e-4 on the 256-token fp32 workload."""
+    w = dataclasses.replace(synth.workload(name), alpha_lo=1.0)
+    say(f"[loop_prefill] {name} with alpha = 1, L={L}")
+    x = synth.prefill_inputs(w, L=L)
+    _check_loop(w, x, w.B, L, TOL_F32 if w.act == "f32" else TOL_BF16)
+
+
+def test_loop_prefill_d64_h16():
+    """16 heads of 64 (d = 1024) over 2048 tokens: eight 384-row column tiles of two heads each, so every XCD
+    takes one column tile and the gate block pairs stay in tile order.  States teacher-forced: already at loop 1
+    (identical inputs) the final states differ from the oracle's by the q/k/v roundings that the GEMM's fp32
+    sums flip, more than the free-running envelope's library-matmul variants flip."""
+    w = dataclasses.replace(synth.workload("prefill_b1_l4096"), name="bf16_d64_h16", dk=64, dv=64, d=1024)
+    say("[loop_prefill] bf16, 16 heads of 64, L=2048")
+    x = synth.prefill_inputs(w, L=2048)
+    assert tuple(x["h0"].shape) == (1, 2048, 1024)
+    _check_loop(w, x, 1, 2048, TOL_BF16, forced=True)
+
+
 def test_loop_prefill_deterministic_and_no_aliasing_effects():
     w = synth.workload("prefill_b1_l4096")
     say("[loop_prefill] determinism, with and without per-loop outputs")

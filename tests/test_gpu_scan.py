@@ -40,6 +40,8 @@ CASES = [
     (1, 130, 1, 64, "f32", (0.0, 1.0), (0.0, 1.0), True),
     (2, 96, 2, 128, "f32", (0.5, 1.0), (0.0, 1.0), True),
     (1, 300, 2, 128, "bf16", (0.0, 1.0), (0.0, 2.0), True),   # negative eigenvalues (beta up to 2)
+    (1, 300, 2, 128, "bf16", (1.0, 1.0), (0.0, 1.0), True),   # no decay (alpha = 1: DeltaNet)
+    (1, 200, 2, 64, "f32", (1.0, 1.0), (0.0, 2.0), True),     # no decay, beta up to 2
 ]
 
 
