@@ -140,15 +140,18 @@ __device__ __forceinline__ int swz(int r, int ch) { return r * BK_BF + ((ch ^ sw
 
 // Direct loads of loads [I0, I1) of one k-block (starting at channel k0) into
 // one stage: loads 0..7 fill the A tile (2048 chunks; wave w's load i covers
-// LDS chunks [(4 i + w) 64, +64)), loads 8..11 the B tile (1024 chunks, same
-// rule).  LDS chunk p holds row p / 8, logical chunk (p % 8) ^ swz_key(row).
-template <int I0, int I1>
+// LDS chunks [(4 i + w) 64, +64), i.e. rows 8 (4 i + w) .. + 7), loads 8..11 the
+// B tile (1024 chunks, same rule).  LDS chunk p holds row p / 8, logical chunk
+// (p % 8) ^ swz_key(row).  Only the first NA of the A loads are issued: with at
+// most 64 tokens (NA = 2) the rows they skip are all past M.
+template <int I0, int I1, int NA>
 __device__ __forceinline__ void gemm_issue(bf16 *stage, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int m0,
                                            int n0, int M, int K, int b_rows, int k0) {
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
         if (i < 8) {
+            if (i >= NA) continue;
             const int base = (4 * i + wave) * 64, p = base + lane;
             const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
             const int m = min(m0 + r, M - 1);   // tail rows re-read the last row; never stored
@@ -190,18 +193,27 @@ __device__ __forceinline__ void read_frags_step(KFrags &F, const bf16 *stage, in
 // fills the memory pipeline's queue, which would stall the wave's MFMA issue.
 // Past the end the loads re-read the last k-block into a free stage, so every
 // iteration has the same shape.  GATE: only the 32-column MFMA tiles holding
-// used gate columns are computed (a wave-uniform condition).
-template <bool GATE>
+// used gate columns are computed (a wave-uniform condition).  NA < 8: only the
+// tile's first 32 NA token rows can be valid; the other A rows are neither loaded
+// nor multiplied (their outputs are never stored), and the wait counts follow
+// the NA + 4 loads per k-block.
+template <bool GATE, int NA>
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int wm,
                                            int wn, int m0, int n0, int M, int K, int b_rows,
                                            int gate_cols) {
     const int nkb = K / BK_BF;   // >= 1
     auto kblock = [&](int kb) { return min(kb, nkb - 1) * BK_BF; };
-    gemm_issue<0, 12>(stages, x, Wp, lane, wave, m0, n0, M, K, b_rows, 0);
-    gemm_issue<0, 12>(stages + STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(1));
-    gemm_issue<0, 12>(stages + 2 * STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(2));
-    wait_vmcnt<24>();   // k-block 0 landed
+    constexpr int NL = NA + 4;          // direct loads per k-block
+    // 32-row A tiles a wave multiplies: each A load covers 8 rows in each of the
+    // 4 waves, so NA loads cover the rows of NA tiles
+    constexpr int TM = NA >= 8 ? 4 : NA;
+    static_assert(NA == 8 || NA <= 4, "NA < 8 covers rows of the first wave row (128 rows) only");
+    const bool rows_on = NA >= 8 || wm == 0;
+    gemm_issue<0, 12, NA>(stages, x, Wp, lane, wave, m0, n0, M, K, b_rows, 0);
+    gemm_issue<0, 12, NA>(stages + STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(1));
+    gemm_issue<0, 12, NA>(stages + 2 * STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(2));
+    wait_vmcnt<2 * NL>();   // k-block 0 landed
     lds_barrier();
     const bool tn_on[2] = {!GATE || wn * 64 < gate_cols, !GATE || wn * 64 + 32 < gate_cols};
     KFrags f0, f1;
@@ -209,23 +221,23 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, co
     for (int s = 0; s < BK_BF / 16; ++s) read_frags_step(f0, stages, s, lane, wm, wn);
 
     auto step = [&](int kb, const KFrags &cur, KFrags &nxt) __attribute__((always_inline)) {
-        wait_vmcnt<12>();   // k-block kb+1 landed (kb+2's 12 loads may remain)
+        wait_vmcnt<NL>();   // k-block kb+1 landed (kb+2's NL loads may remain)
         lds_barrier();      // ... for every wave; every wave has read k-block kb's fragments
         bf16 *ld_stage = stages + (kb % STAGES) * STAGE_ELEMS;           // receives kb+3
         const bf16 *rd_stage = stages + ((kb + 1) % STAGES) * STAGE_ELEMS;
         const int k3 = kblock(kb + 3);
 #pragma unroll
         for (int s = 0; s < BK_BF / 16; ++s) {
-            if (s == 0) gemm_issue<0, 3>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            if (s == 1) gemm_issue<3, 6>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            if (s == 2) gemm_issue<6, 9>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            if (s == 3) gemm_issue<9, 12>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 0) gemm_issue<0, 3, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 1) gemm_issue<3, 6, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 2) gemm_issue<6, 9, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
+            if (s == 3) gemm_issue<9, 12, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
             read_frags_step(nxt, rd_stage, s, lane, wm, wn);
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn)
-                if (tn_on[tn])
+                if (tn_on[tn] && rows_on)
 #pragma unroll
-                    for (int tm = 0; tm < 4; ++tm)
+                    for (int tm = 0; tm < TM; ++tm)
                         acc[tm][tn] = mfma32x32x16(cur.a[s][tm], cur.b[s][tn], acc[tm][tn]);
         }
     };
@@ -237,8 +249,9 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, co
 }
 
 // One workgroup per CU (the three LDS stages take 144 KB), i.e. one wave per
-// SIMD: the compiler may use the whole register file for latency hiding.
-template <int D>
+// SIMD: the compiler may use the whole register file for latency hiding.  NA:
+// A loads per k-block (8; 2 for at most 64 tokens, e.g. a decode batch).
+template <int D, int NA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_proj_bf16(const bf16 *__restrict__ x,
                                                    const bf16 *__restrict__ Wp, int M, int K, int H,
                                                    int m_tiles, int n_main, bf16 *q, bf16 *k, bf16 *v,
@@ -269,8 +282,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    if (gate) gemm_kloop<true>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
-    else gemm_kloop<false>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
+    if (gate) gemm_kloop<true, NA>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
+    else gemm_kloop<false, NA>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
     __syncthreads();   // all waves done reading the operand stages
 
     // epilogue in two 128-row halves through an fp32 tile in LDS (reuses the operand buffers)
@@ -278,6 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float *red = Cs + 128 * CS_LD;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+        if (m0 + half * 128 >= M) break;   // no valid row in this half (uniform)
         if (wm == half) {
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
@@ -815,14 +829,15 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
         const int m_tiles = (M + BM_BF - 1) / BM_BF;
         const int n_main = (int)(qkv_rows_padded(H, D) / BN);   // the gate tile is n_main
         dim3 grid(m_tiles * (n_main + 1));
-        if (D == 128)
-            launch_kernel(k_proj_bf16<128>, grid, dim3(256), 0, s, (const bf16 *)x,
-                               (const bf16 *)Wpack, M, d, H, m_tiles, n_main, (bf16 *)q, (bf16 *)k,
-                               (bf16 *)v, alpha, beta, alpha_lo, eps);
-        else
-            launch_kernel(k_proj_bf16<64>, grid, dim3(256), 0, s, (const bf16 *)x,
-                               (const bf16 *)Wpack, M, d, H, m_tiles, n_main, (bf16 *)q, (bf16 *)k,
-                               (bf16 *)v, alpha, beta, alpha_lo, eps);
+#define NARROW(DD, NA)                                                                            \
+    launch_kernel(k_proj_bf16<DD, NA>, grid, dim3(256), 0, s, (const bf16 *)x, (const bf16 *)Wpack, M, d, H, \
+                  m_tiles, n_main, (bf16 *)q, (bf16 *)k, (bf16 *)v, alpha, beta, alpha_lo, eps)
+        if (M <= 64) {
+            if (D == 128) NARROW(128, 2); else NARROW(64, 2);
+        } else {
+            if (D == 128) NARROW(128, 8); else NARROW(64, 8);
+        }
+#undef NARROW
     }
     return hipGetLastError();
 }

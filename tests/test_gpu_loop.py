@@ -67,7 +67,9 @@ def _proj_workload(name):
 
 
 # M >= 1024 bf16 tokens take the wide tiles (k_gates + k_proj_wide), shorter inputs the 256 x 128 tiles
+# (at most 64 tokens: only the first two 32-row tiles of each 256-token tile are loaded and multiplied)
 @pytest.mark.parametrize("name,M", [("tiny_f32", 256), ("prefill_b1_l4096", 300), ("prefill_b1_l4096", 1),
+                                    ("prefill_b1_l4096", 64), ("prefill_b1_l4096", 65), ("bf16_d64_h3", 40),
                                     ("prefill_b1_l4096", 1100), ("bf16_d64_h3", 300), ("bf16_d64_h3", 1100)])
 def test_project_parity(name, M):
     w = _proj_workload(name)
