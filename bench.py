@@ -253,8 +253,8 @@ def calib_copy(torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="prefill_b1_l4096")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
