@@ -185,3 +185,15 @@ def test_timer_validation(lib):
 def test_timer_without_device_reports_hip_error():
     with pytest.raises(gl.GdnError, match="GDN_ERR_HIP"):
         gl.gdn_timer_create(gl.GDN_STAGE_PROJECT, 4)
+
+
+@pytest.mark.parametrize("argv, env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "8"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """bench.py measures one GPU: a request for more exits with status 2 and says so, before it touches a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                       env={**os.environ, **env}, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
