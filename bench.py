@@ -1,18 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the looped gated-delta-rule (GDN) mixer on one MI355X.
 
-One step = one gdn_loop_prefill call: T = 4 weight-tied loops, each running the projection GEMM with its
-fused epilogue and the gate launch, the chunk prep and the carry (the sequential state chain with the chunk
-outputs and the loop residual computed a chunk behind inside the same workgroups), over the 4096-token,
-16-head, width-2048 bf16 prompt (B=1, L=4096, H=16, dk=dv=128, T=4, alpha in (0.9, 1)).  Inputs are seeded
-synthetic draws (synth.prefill_inputs) resident in HBM before timing starts.
+One step = one gdn_loop_prefill call: T = 4 weight-tied loops, each running the projection GEMM (which also
+forms the gate pre-activations), the chunk prep and the carry (the sequential state chain with the chunk
+outputs and the loop residual computed a chunk behind inside the same workgroups).  The headline workload is
+the largest single-GPU prompt: 4 sequences of 8192 tokens, 16 heads of 128, width 2048, bf16 inputs with an
+fp32 state (B=4, L=8192, T=4).  Inputs are seeded synthetic draws (synth.prefill_inputs) resident in HBM
+before timing starts.
 
-Printed (one JSON line on stdout): prefill tokens/s (tokens of the prompt per second, each token passing all
-4 loops), the roofline of the dominant kernel (the projection GEMM, bf16 MFMA) from the HIP start/stop events
-carried on its dispatches inside the timed region, the CPU oracle timed on the same workload, and a secondary
-measurement of batched decode (64 sequences x 256 generated tokens, 4 loop states each; HBM-bound).
+Printed (one JSON line on stdout):
+  value           prefill tokens/s of the headline workload (tokens of the prompts per second, each token
+                  passing all 4 loops), from W warm-up and K timed steps;
+  roofline        the dominant kernel (the projection GEMM, bf16 MFMA), from the HIP start/stop events
+                  carried on its dispatches inside the timed region;
+  roofline_carry  the carry against HBM (algorithmic bytes: q/k/v read, the previous h read, h and its bf16
+                  copy written), from a pass with every stage's dispatches timed;
+  whole_path      the step's algorithmic flops against the bf16 peak, and the per-stage times;
+  extra_workloads the 32768-token prompt and the 4096-token prompt, measured the same way;
+  decode          batched decode, 64 sequences x 256 generated tokens, 4 loop states each (the state step
+                  alone; HBM-bound);
+  loop_decode     the same 64 sequences through whole loops (projection, state step and residual per loop);
+  cpu_baseline    the oracle on a bounded sample of the headline workload, on the host's cores.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode]
+                       [--no-cpu-baseline]
        python bench.py --calib-copy          (plain 256 MiB device copy, for HBM counter calibration)
 Only one GPU is used: --gpus N with N > 1 exits with a message.
 """
@@ -78,6 +89,19 @@ def scan_flops_per_token(w, C=64) -> int:
     return w.H * (C * (3 * w.dk + 2 * w.dv) + 6 * w.dk * w.dv)
 
 
+def carry_bytes_per_step(w) -> int:
+    """Algorithmic HBM bytes of the T carry launches of one prefill step, per token: q, k, v read; the
+    previous loop's h read (loop 1: the bf16 h0, later loops fp32); h written in fp32 and, for loops 1..T-1,
+    its bf16 copy for the next loop's projection."""
+    ab = 2 if w.act == "bf16" else 4
+    qkv = w.H * (2 * w.dk + w.dv) * ab
+    total = 0
+    for tau in range(w.T):
+        h_prev = w.d * (ab if tau == 0 else 4)
+        total += qkv + h_prev + w.d * 4 + (w.d * 2 if (w.act == "bf16" and tau < w.T - 1) else 0)
+    return total
+
+
 def decode_bytes_per_launch(N, H, D, act_bytes=2) -> int:
     """Algorithmic HBM bytes of one decode launch: state read + write, q/k/v, alpha/beta, o."""
     return N * H * (2 * D * D * 4 + 3 * D * act_bytes + 2 * 4 + D * 4)
@@ -96,7 +120,7 @@ def traffic_for(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def bench_prefill(args, w, torch, gl, synth):
+def bench_prefill(args, w, torch, gl, synth, warmup):
     dev = lambda t: t.contiguous().to("cuda")
     x = synth.prefill_inputs(w)
     desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
@@ -111,7 +135,7 @@ def bench_prefill(args, w, torch, gl, synth):
     def step():
         gl.gdn_loop_prefill(desc, h0, Wp, rho, h_out, None, None, ws, stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -218,16 +242,77 @@ def bench_decode(args, torch, gl, synth):
     }
 
 
-def cpu_baseline(w, synth):
+def bench_loop_decode(args, torch, gl, synth, dw):
+    """64 sequences through whole loops, one gdn_loop_decode call (T loops: projection, state step, residual)
+    per generated token; the token inputs h_t are seeded N(0, 1) draws of width d, resident before timing, and
+    the weights those of the 4096-token prompt (same 16 x 128 heads, width 2048)."""
+    import numpy as np
+    w = synth.workload("prefill_b1_l4096")
+    steps = args.decode_steps
+    dev = lambda t: t.contiguous().to("cuda")
+    x = synth.prefill_inputs(w, L=1)
+    desc = gl.make_desc(dw.B, 1, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = torch.empty(gl.gdn_weights_packed_bytes(desc) // 2, dtype=desc.act_dtype, device="cuda")
+    gl.gdn_weights_pack(desc, dev(x["Wq"]), dev(x["Wk"]), dev(x["Wv"]), dev(x["wa"]), dev(x["wb"]), Wp)
+    rng = np.random.default_rng(dw.seed + 7)
+    hs = torch.from_numpy(rng.standard_normal((steps, dw.B, w.d), dtype=np.float32)).to(torch.bfloat16).to("cuda")
+    hts = list(hs.unbind(0))
+    rho = dev(x["rho"])
+    states = synth.decode_state_init(dw).to("cuda")
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_DECODE)
+    h_out = torch.empty(dw.B, w.d, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for s in range(steps):
+            gl.gdn_loop_decode(desc, hts[s], Wp, rho, states, h_out, ws, stream)
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for rep in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms_run = statistics.median(times)
+    tok_s = dw.B * steps / (ms_run * 1e-3)
+    # roofline: per generated token, the state traffic of the T loops plus each loop's weight stream shared
+    # by the batch
+    bytes_tok = decode_bytes_per_launch(dw.B, w.H, w.dk) * w.T / dw.B + w.T * proj_weight_bytes(w) / dw.B
+    roof = PEAK_HBM_GBS * 1e9 / bytes_tok
+    return {"workload": "decode_n64_s256 with projections", "sequences": dw.B, "steps": steps, "loops": w.T,
+            "value": tok_s, "unit": "tokens/s", "ms_per_run": ms_run,
+            "roofline": {"bound": "hbm", "bytes_per_token": bytes_tok, "roofline_tokens_per_s": roof,
+                         "frac": tok_s / roof}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, synth, sample_tokens=2048):
+    """The fp64 oracle on a bounded sample of the workload: the first `sample_tokens` tokens of sequence 0
+    through all T loops, repeated until at least 10 s of CPU work; tokens/s of the sample."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing: report OpenMP threads only
         blas_threads = 1
-    x = synth.prefill_inputs(w)
+    Ls = min(sample_tokens, w.L)
+    x = synth.prefill_inputs(w, L=Ls, B=1)
     runs, t0 = 0, time.perf_counter()
-    while True:   # whole runs of the full workload until at least 10 s of CPU work
+    while True:
         oracle.loop_prefill(x["h0"], x["Wq"], x["Wk"], x["Wv"], x["wa"], x["wb"], x["rho"], w.H, w.dk, w.dv,
                             w.alpha_lo, w.act)
         runs += 1
@@ -235,9 +320,10 @@ def cpu_baseline(w, synth):
         if dt >= 10.0:
             break
     cores = max(oracle.num_threads(), blas_threads)
-    return {"value": runs * w.B * w.L / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full {w.name} workload ({w.B * w.L} tokens x {w.T} loops), {runs} run(s) in "
-                      f"{dt:.1f} s (fp64: numpy/OpenBLAS projections, C/OpenMP recurrence)"}
+    return {"value": runs * Ls / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{w.name}: sequence 0, first {Ls} tokens, all {w.T} loops, {runs} run(s) in {dt:.1f} s "
+                      f"(fp64: numpy/OpenBLAS projections, C/OpenMP recurrence)"}
 
 
 def calib_copy(torch):
@@ -250,12 +336,48 @@ def calib_copy(torch):
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
 
 
+def prefill_record(w, pf):
+    """Rate, rooflines and per-stage times of one prefill workload."""
+    tokens = pf["tokens"]
+    st = pf["per_stage"]
+    proj = st["project"]
+    kname, kflops = proj_gemm_kernel(w, tokens)
+    flops_launch = kflops * tokens
+    achieved = flops_launch / (proj["avg_ms"] * 1e-3) / 1e12
+    total_flops = (proj_flops_per_token(w) + scan_flops_per_token(w)) * w.T * tokens
+    step_s = pf["ms_step"] * 1e-3
+    rec = {
+        "value": tokens / step_s, "unit": "tokens/s", "ms_per_step": pf["ms_step"],
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "H": w.H, "dk": w.dk, "dv": w.dv, "d": w.d,
+                   "T": w.T, "chunk": 64, "alpha_lo": w.alpha_lo},
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_for(kname, w.name), "flops_per_launch": flops_launch,
+                     "avg_launch_us": proj["avg_ms"] * 1e3},
+        "whole_path": {"algorithmic_tflops": total_flops / step_s / 1e12,
+                       "frac_of_bf16_peak": total_flops / step_s / 1e12 / PEAK_BF16_TFLOPS,
+                       "loop_tokens_per_s": w.T * tokens / step_s,
+                       "stages": {k: {"avg_launch_us": v["avg_ms"] * 1e3, "share_of_step": v["share"]}
+                                  for k, v in st.items()}},
+    }
+    if "scan_carry" in st:
+        bpl = carry_bytes_per_step(w) * tokens / w.T
+        gbs = bpl / (st["scan_carry"]["avg_ms"] * 1e-3) / 1e9
+        rec["roofline_carry"] = {"bound": "hbm", "kernel": "k_scan_carry", "achieved": gbs,
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                 "traffic": traffic_for("k_scan_carry", w.name), "bytes_per_launch": bpl,
+                                 "avg_launch_us": st["scan_carry"]["avg_ms"] * 1e3}
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="prefill_b1_l4096")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_b4_l8192")
+    ap.add_argument("--extra", default="prefill_b1_l32768,prefill_b1_l4096",
+                    help="comma-separated further prefill workloads reported under extra_workloads ('' for none)")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -277,40 +399,38 @@ def main():
     gl.load()
     w = synth.workload(args.workload)
     log(f"prefill: {w.name}, warmup {args.warmup}, steps {args.steps}")
-    pf = bench_prefill(args, w, torch, gl, synth)
-    proj = pf["per_stage"]["project"]
-    kname, kflops = proj_gemm_kernel(w, pf["tokens"])
-    flops_launch = kflops * pf["tokens"]
-    achieved = flops_launch / (proj["avg_ms"] * 1e-3) / 1e12
-    traffic = traffic_for(kname, w.name)
-    total_flops = (proj_flops_per_token(w) + scan_flops_per_token(w)) * w.T * pf["tokens"]
+    pf = bench_prefill(args, w, torch, gl, synth, args.warmup)
+    head = prefill_record(w, pf)
     out = {
         "metric": METRIC,
-        "value": pf["tokens"] / (pf["ms_step"] * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pf["ms_step"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.act,
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the workload's shape)",
-        "config": {"workload": w.name, "B": w.B, "L": w.L, "H": w.H, "dk": w.dk, "dv": w.dv, "d": w.d,
-                   "T": w.T, "chunk": 64, "alpha_lo": w.alpha_lo},
-        "roofline": {"bound": "mfma", "kernel": kname, "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "flops_per_launch": flops_launch,
-                     "avg_launch_us": proj["avg_ms"] * 1e3},
-        "whole_path": {"algorithmic_tflops": total_flops / (pf["ms_step"] * 1e-3) / 1e12,
-                       "frac_of_bf16_peak": total_flops / (pf["ms_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                       "loop_tokens_per_s": w.T * pf["tokens"] / (pf["ms_step"] * 1e-3),
-                       "stages": {k: {"avg_launch_us": v["avg_ms"] * 1e3, "share_of_step": v["share"]}
-                                  for k, v in pf["per_stage"].items()}},
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
+    for key in ("roofline_carry", "whole_path"):
+        if key in head:
+            out[key] = head[key]
+    extras = {}
+    for name in [n for n in args.extra.split(",") if n and n != w.name]:
+        we = synth.workload(name)
+        log(f"prefill (extra): {name}, warmup {max(args.warmup, 20)}, steps {args.steps}")
+        extras[name] = prefill_record(we, bench_prefill(args, we, torch, gl, synth, max(args.warmup, 20)))
+    if extras:
+        out["extra_workloads"] = extras
     if not args.no_decode:
         out["decode"] = bench_decode(args, torch, gl, synth)
+        log("loop decode: 64 sequences with projections ...")
+        out["loop_decode"] = bench_loop_decode(args, torch, gl, synth, synth.workload("decode_n64_s256"))
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(w, synth)

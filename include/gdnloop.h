@@ -106,6 +106,25 @@ enum { GDN_OP_LOOP_PREFILL = 0, GDN_OP_LOOP_DECODE = 1, GDN_OP_SCAN_PREFILL = 2,
 /* Device scratch bytes that operation `op` needs for `desc` (0 is valid). */
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes);
 
+/* Regions of the looped calls' workspace that hold a loop's projections
+ * (LT2 Section 2 "LT2" paragraph: q_t, k_t, v_t and the gates are per-token
+ * functions of h_t):
+ *   GDN_WS_Q, GDN_WS_K   [B*L, H, dk]  desc->act
+ *   GDN_WS_V             [B*L, H, dv]  desc->act
+ *   GDN_WS_ALPHA, GDN_WS_BETA  [B*L, H] fp32
+ * After gdn_loop_prefill or gdn_loop_decode has completed on its stream, these
+ * regions hold what the last loop (loop T) used: q and k after normalisation,
+ * v, and the gates alpha, beta.  A caller can thus inspect the operands of any
+ * loop tau by running the call with T = tau (loops 1..tau are computed
+ * identically for every T).  `op` must be GDN_OP_LOOP_PREFILL or
+ * GDN_OP_LOOP_DECODE; *offset is the region's byte offset from the start of
+ * the workspace and *bytes its length.  Errors: GDN_ERR_UNSUPPORTED for
+ * another op or an unknown region, the usual descriptor errors, GDN_ERR_NULL
+ * for a NULL output pointer. */
+enum { GDN_WS_Q = 0, GDN_WS_K = 1, GDN_WS_V = 2, GDN_WS_ALPHA = 3, GDN_WS_BETA = 4 };
+gdn_status gdn_workspace_region(const gdn_desc *desc, int op, int region, size_t *offset,
+                                size_t *bytes);
+
 /* ---- one loop's projection (P1 + fused epilogue) ------------------------- */
 
 /* Projects token rows x [B*L, d] (device, desc->act) with the packed weights:
@@ -121,6 +140,15 @@ gdn_status gdn_project(const gdn_desc *desc, const void *x, const void *Wpack,
 
 /* One chunkwise-parallel pass of the gated delta rule over given inputs
  * (q and k are used as given: no normalisation inside).
+ * Passage: LT2 Section 2 "LT2" paragraph (the mixer's recurrent state S_t in
+ * R^{dk x dv} updated from q_t, k_t, v_t) with the Gated DeltaNet mixer of
+ * Appendix C; the update is the rank-1 data-dependent transition of Appendix
+ * B.1 / Fig. 6 caption, read as the gated delta rule stated at the top of
+ * this header; o_t = S_t^T q_t.  The pages cite the chunkwise (WY/UT)
+ * rewrite as the fused chunkwise kernel of Section 3.2; the result equals the
+ * token recurrence up to rounding.
+ * Sequences of B are independent; each starts from s_init (or 0).  Errors:
+ * GDN_ERR_SHAPE also for B > 65535.
  *   q, k [B, L, H, dk], v [B, L, H, dv]   device, desc->act
  *   alpha, beta [B, L, H]                 device, fp32; alpha in (0, 1]
  *   s_init [B, H, dk, dv]                 device fp32, or NULL for S_0 = 0
@@ -135,6 +163,9 @@ gdn_status gdn_scan_prefill(const gdn_desc *desc, const void *q, const void *k,
 
 /* One recurrent step (one token per sequence) of the gated delta rule; the
  * state is read once and written once (in place).
+ * Passage: the same recurrence as gdn_scan_prefill, taken one token at a time
+ * (LT2 Section 3.2 measures decode throughput; the linear-time mixer decodes
+ * at constant cost per token from its state, Section 2 "LT2" paragraph).
  *   desc->L must be 1; B = number of sequences
  *   q, k [B, H, dk], v [B, H, dv]   device, desc->act
  *   alpha, beta [B, H]              device fp32
@@ -146,7 +177,13 @@ gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k,
 
 /* ---- the looped mixer --------------------------------------------------- */
 
-/* T weight-tied loops over a whole prompt (prefill):
+/* T weight-tied loops over a whole prompt (prefill).
+ * Passage: LT2 Section 2, "Looped Transformer (LT)" paragraph (the same block
+ * applied T times to the whole sequence) and "LT2" paragraph (per-loop
+ * residual gate h^(tau) = h~^(tau) + rho_tau (.) h^(tau-1)); Appendix C (T = 4,
+ * use_residual = true).  Each loop projects bf16(h^(tau-1)) (or h^(tau-1) for
+ * fp32 workloads) with the packed weights, normalises q and k, forms the
+ * gates, scans from S = 0 and applies the residual gate; h~^(tau) = o.
  *   h0 [B, L, d]                 device, desc->act (h^(0))
  *   Wpack                        from gdn_weights_pack
  *   rho [T, d]                   device fp32 (rho_1 .. rho_T)
@@ -160,7 +197,13 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
                             const float *rho, float *h_out, float *states_out,
                             float *h_loops, void *ws, size_t ws_bytes, void *stream);
 
-/* One generated token per sequence through the T loops (decode):
+/* One generated token per sequence through the T loops (decode).
+ * Passage: as gdn_loop_prefill, for one new token per sequence; each loop
+ * tau continues its own state (every loop scans the sequence from S = 0 in
+ * prefill, so decode keeps T states per sequence and head; the pages' looped
+ * cache grows with T, Section 3.2) with loop tau's projections of the token.
+ * The projection and residual are token-local, so the result equals the
+ * last row of gdn_loop_prefill over the prompt plus this token.
  *   desc->L must be 1; B = number of sequences
  *   h_t [B, d]                   device, desc->act
  *   rho [T, d]                   device fp32
@@ -181,13 +224,12 @@ const char *gdn_version(void);
 
 /* ---- optional device timing of one stage -------------------------------- */
 
-/* Stages that a timer can bracket. */
+/* Stages that a timer can bracket (4 is not a stage: it named a separate
+ * output pass that the carry now performs, and gdn_timer_create rejects it). */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
-       GDN_STAGE_DECODE = 3, GDN_STAGE_SCAN_OUT = 4, GDN_STAGE_GATES = 5 };
+       GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5 };
 /* GDN_STAGE_SCAN_CARRY times the carry kernel, which computes the chunk outputs
- * (and the loop residual) as well; GDN_STAGE_SCAN_OUT names no launch any more
- * and is kept so that stage numbers stay stable (a timer on it records none).
- * GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
+ * (and the loop residual) as well.  GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
  * more tokens the gates alpha/beta leave the GEMM's epilogue: gdn_project and
  * gdn_loop_decode compute them in a launch of their own, timed as
  * GDN_STAGE_GATES; gdn_loop_prefill with H <= 16 has the GEMM write partial

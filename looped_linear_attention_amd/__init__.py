@@ -22,8 +22,9 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
     "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
-    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_SCAN_OUT", "GDN_STAGE_GATES", "GdnError", "gdn_desc", "make_desc", "lib_path",
-    "load", "EXPORTED", "workspace",
+    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES", "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
+    "GDN_WS_ALPHA", "GDN_WS_BETA", "GdnError", "gdn_desc", "make_desc", "lib_path",
+    "load", "EXPORTED", "workspace", "workspace_view", "gdn_workspace_region",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
@@ -32,11 +33,12 @@ __all__ = [
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT = range(5)
-GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_SCAN_OUT, GDN_STAGE_GATES = range(6)
+GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_GATES = 0, 1, 2, 3, 5
+GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [
-    "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
+    "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
@@ -86,6 +88,7 @@ def load():
         "gdn_weights_packed_bytes": [D, ctypes.POINTER(S)],
         "gdn_weights_pack": [D, P, P, P, P, P, P, P],
         "gdn_workspace_bytes": [D, I, ctypes.POINTER(S)],
+        "gdn_workspace_region": [D, I, I, ctypes.POINTER(S), ctypes.POINTER(S)],
         "gdn_project": [D, P, P, P, P, P, P, P, P],
         "gdn_scan_prefill": [D, P, P, P, P, P, P, P, P, P, S, P],
         "gdn_scan_decode": [D, P, P, P, P, P, P, P, P],
@@ -182,6 +185,26 @@ def gdn_workspace_bytes(desc: gdn_desc, op: int) -> int:
 def workspace(desc: gdn_desc, op: int, device="cuda") -> torch.Tensor:
     """Allocate the device workspace `op` needs (torch owns the memory)."""
     return torch.empty(max(gdn_workspace_bytes(desc, op), 256), dtype=torch.uint8, device=device)
+
+
+def gdn_workspace_region(desc: gdn_desc, op: int, region: int):
+    """(byte offset, bytes) of a documented region of a looped call's workspace."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().gdn_workspace_region(ctypes.byref(desc), op, region, ctypes.byref(off), ctypes.byref(n)))
+    return off.value, n.value
+
+
+def workspace_view(ws: torch.Tensor, desc: gdn_desc, op: int, region: int) -> torch.Tensor:
+    """A typed view of a workspace region: q/k/v as [B*L, H, D] in the activation dtype, the gates as
+    [B*L, H] fp32 (the view shares the workspace's memory)."""
+    off, n = gdn_workspace_region(desc, op, region)
+    if ws.numel() * ws.element_size() < off + n:
+        raise GdnError("workspace is smaller than the region")
+    raw = ws.view(torch.uint8)[off:off + n]
+    tokens = desc.B * desc.L
+    if region in (GDN_WS_ALPHA, GDN_WS_BETA):
+        return raw.view(torch.float32).view(tokens, desc.H)
+    return raw.view(desc.act_dtype).view(tokens, desc.H, desc.dk)
 
 
 def gdn_weights_pack(desc, Wq, Wk, Wv, wa, wb, Wpack, stream=None):

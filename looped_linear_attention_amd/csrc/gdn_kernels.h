@@ -62,12 +62,15 @@ struct ChunkWs {
 };
 // Gates of the chunk preparation: alpha/beta [B*L, H], or (zp != nullptr) the
 // P partial pre-activations zp[P][2H][B*L] of the projection, summed in order
-// p = 0..P-1, with alpha = lo + (1 - lo) sigmoid(-z_a), beta = sigmoid(z_b).
+// p = 0..P-1, with alpha = lo + (1 - lo) sigmoid(-z_a), beta = sigmoid(z_b);
+// the gates formed from zp are stored to alpha_out/beta_out [B*L, H] when
+// those are given (so that a caller can read the gates the scan used).
 struct GateSrc {
     const float *alpha, *beta;
     const float *zp;
     int P;
     float alpha_lo;
+    float *alpha_out, *beta_out;
 };
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
                             GateSrc gates, ChunkWs ws, hipStream_t s);

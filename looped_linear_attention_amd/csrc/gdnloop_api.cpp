@@ -70,6 +70,22 @@ gdn_status check_desc(const gdn_desc *d, bool decode) {
     // every tensor must be addressable with 64-bit offsets; keep element counts sane
     const int64_t tokens = (int64_t)d->B * d->L;
     if (tokens * d->d > (int64_t)1 << 40) return fail(GDN_ERR_SHAPE, "problem too large");
+    // token counts are 32-bit inside the kernels
+    if (tokens > INT32_MAX) return fail(GDN_ERR_SHAPE, "B*L must be below 2^31 (got %lld)", (long long)tokens);
+    return GDN_OK;
+}
+
+// Launch-grid limits of the chunkwise prefill (checked before anything is
+// enqueued, so that no launch of a multi-kernel call can fail on its shape):
+// the chunk prep runs (chunk, head) pairs along x and sequences along y, the
+// carry sequences along z; both y and z hold at most 65535.
+gdn_status check_prefill_grid(const gdn_desc *d) {
+    if (d->B > 65535) return fail(GDN_ERR_SHAPE, "prefill calls take at most 65535 sequences (got %d)", d->B);
+    const int64_t nc = (d->L + 63) / 64;
+    if (nc * d->H > INT32_MAX) return fail(GDN_ERR_SHAPE, "too many (chunk, head) pairs per sequence");
+    // the fp32 projection runs 64-token row tiles along y
+    if (d->act == GDN_F32 && ((int64_t)d->B * d->L + 63) / 64 > 65535)
+        return fail(GDN_ERR_SHAPE, "fp32 projections take at most 65535 * 64 tokens");
     return GDN_OK;
 }
 
@@ -218,8 +234,30 @@ gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes) {
         return fail(GDN_ERR_UNSUPPORTED, "unknown op %d", op);
     gdn_status st = check_desc(desc, op == GDN_OP_LOOP_DECODE || op == GDN_OP_SCAN_DECODE);
     if (st != GDN_OK) return st;
+    if ((op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL) && (st = check_prefill_grid(desc)) != GDN_OK)
+        return st;
     if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
     *bytes = layout(desc, op).total;
+    return GDN_OK;
+}
+
+gdn_status gdn_workspace_region(const gdn_desc *desc, int op, int region, size_t *offset, size_t *bytes) {
+    if (op != GDN_OP_LOOP_PREFILL && op != GDN_OP_LOOP_DECODE)
+        return fail(GDN_ERR_UNSUPPORTED, "only the looped calls expose workspace regions (op %d)", op);
+    gdn_status st = check_desc(desc, op == GDN_OP_LOOP_DECODE);
+    if (st != GDN_OK) return st;
+    if (!offset || !bytes) return fail(GDN_ERR_NULL, "offset or bytes is NULL");
+    const Layout lo = layout(desc, op);
+    const size_t tokens = (size_t)desc->B * desc->L, H = desc->H;
+    const size_t qkv = tokens * H * desc->dk * act_bytes(desc), gate = tokens * H * 4;
+    switch (region) {
+        case GDN_WS_Q: *offset = lo.q; *bytes = qkv; break;
+        case GDN_WS_K: *offset = lo.k; *bytes = qkv; break;
+        case GDN_WS_V: *offset = lo.v; *bytes = qkv; break;
+        case GDN_WS_ALPHA: *offset = lo.alpha; *bytes = gate; break;
+        case GDN_WS_BETA: *offset = lo.beta; *bytes = gate; break;
+        default: return fail(GDN_ERR_UNSUPPORTED, "unknown workspace region %d", region);
+    }
     return GDN_OK;
 }
 
@@ -257,6 +295,7 @@ gdn_status gdn_scan_prefill(const gdn_desc *desc, const void *q, const void *k, 
                             float *s_final, void *ws, size_t ws_bytes, void *stream) {
     gdn_status st = check_desc(desc, false);
     if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
     REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(alpha); REQUIRE_PTR(beta);
     REQUIRE_PTR(o); OPTIONAL_PTR(s_init); OPTIONAL_PTR(s_final);
     if (s_init && s_init == s_final) return fail(GDN_ERR_SHAPE, "s_final may not alias s_init");
@@ -265,7 +304,8 @@ gdn_status gdn_scan_prefill(const gdn_desc *desc, const void *q, const void *k, 
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
     if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
     CarryOut out{o, nullptr, false, nullptr, nullptr, nullptr};
-    return scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo}, s_init, s_final, out,
+    return scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo, nullptr, nullptr}, s_init,
+                       s_final, out,
                        ws, lo, (hipStream_t)stream);
 }
 
@@ -289,6 +329,7 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
                             void *ws, size_t ws_bytes, void *stream) {
     gdn_status st = check_desc(desc, false);
     if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
     REQUIRE_PTR(h0); REQUIRE_PTR(Wpack); REQUIRE_PTR(rho); REQUIRE_PTR(h_out);
     OPTIONAL_PTR(states_out); OPTIONAL_PTR(h_loops);
     if ((const void *)h_out == h0) return fail(GDN_ERR_SHAPE, "h_out may not alias h0");
@@ -318,7 +359,10 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         CarryOut out{nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, hdst,
                      (!f32 && !last) ? xbuf : nullptr};
-        st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo}, nullptr,
+        // with gate partials the prep forms alpha and beta and stores them in the
+        // workspace's gate regions, where gdn_loop_prefill documents them
+        st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
+                         nullptr,
                          states_out ? states_out + tau * state_elems : nullptr, out, ws, lo, s);
         if (st != GDN_OK) return st;
         hprev = hdst;
@@ -375,7 +419,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_GATES || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_GATES || stage == 4 || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

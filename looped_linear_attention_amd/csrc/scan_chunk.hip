@@ -164,6 +164,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
                                                    const float *__restrict__ alpha,
                                                    const float *__restrict__ beta,
                                                    const float *__restrict__ zp, int P, int Mtot,
+                                                   float *__restrict__ alpha_out,
+                                                   float *__restrict__ beta_out,
                                                    float alpha_lo, int L, int H,
                                                    int Nc, float *__restrict__ wsW,
                                                    float *__restrict__ wsM,
@@ -243,6 +245,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             }
             a_raw = alpha_lo + (1.f - alpha_lo) / (1.f + expf(sa));
             b_raw = 1.f / (1.f + expf(-sb));
+            if (alpha_out && lane <= last) {
+                const int64_t gi = (tok0 + lane) * H + h;
+                alpha_out[gi] = a_raw;
+                beta_out[gi] = b_raw;
+            }
         }
         const bool ok = lane <= last;
         const float a = ok ? a_raw : 1.f;   // padded tokens: identity
@@ -1103,7 +1110,8 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
     if (gs.zp && (f32 || gs.P < 1 || gs.P > 16)) return hipErrorInvalidValue;
 #define PREP(DD, T, GP)                                                                            \
     launch_kernel((k_scan_prep<DD, T, GP>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,     \
-                  gs.alpha, gs.beta, gs.zp, gs.P, B * L, gs.alpha_lo, L, H, Nc, ws.W, ws.M, ws.g)
+                  gs.alpha, gs.beta, gs.zp, gs.P, B * L, gs.alpha_out, gs.beta_out, gs.alpha_lo, L, H, Nc, \
+                  ws.W, ws.M, ws.g)
     if (f32) {
         if (D == 128) PREP(128, float, false); else PREP(64, float, false);
     } else if (gs.zp) {

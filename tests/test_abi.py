@@ -90,9 +90,9 @@ def test_decode_needs_single_token():
 
 
 def test_workspace_sizes():
-    """Prefill workspace: bf16 q/k/v, fp32 gates, per-chunk W [D x 64], M [64 x 64], gamma [64], the chunk-start
-    state [D x D] and E [64 x D] (both as bf16 hi/lo pairs, 4 bytes per element), and the bf16 GEMM operand
-    for loops 2..T; every region rounded up to 256 bytes."""
+    """Prefill workspace: bf16 q/k/v, fp32 gates, the bf16 GEMM operand for loops 2..T, the projection's
+    partial gate pre-activations where it forms them, and per chunk W [D x 64], M [64 x 64] (each as bf16
+    hi and lo planes, 4 bytes per element) and gamma [64]; every region rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
     B, L, H, D, T = 2, 130, 3, 128, 4
     desc = gl.make_desc(B, L, H, D, D, T=T)
@@ -120,6 +120,46 @@ def test_workspace_sizes():
         assert _ws_status(desc) == (0, exp)
     st, n = _ws_status(gl.make_desc(64, 1, 16, 128, 128), gl.GDN_OP_SCAN_DECODE)
     assert st == 0 and n == 0
+
+
+@pytest.mark.parametrize("op", [gl.GDN_OP_LOOP_PREFILL, gl.GDN_OP_LOOP_DECODE])
+def test_workspace_regions(op):
+    """The documented regions (q, k, v, alpha, beta) lie in order at the start of the looped calls' workspace,
+    256-byte aligned, sized [B*L, H, D] in the activation dtype and [B*L, H] fp32, inside the workspace."""
+    up = lambda x: (x + 255) // 256 * 256
+    for B, L, H, D, act, eb in [(2, 130, 3, 128, gl.GDN_BF16, 2), (1, 1100, 16, 128, gl.GDN_BF16, 2),
+                                (3, 77, 1, 64, gl.GDN_F32, 4)]:
+        if op == gl.GDN_OP_LOOP_DECODE:
+            L = 1
+        desc = gl.make_desc(B, L, H, D, D, T=4, act=act)
+        total = gl.gdn_workspace_bytes(desc, op)
+        tok = B * L
+        expect = [(0, tok * H * D * eb), (up(tok * H * D * eb), tok * H * D * eb),
+                  (2 * up(tok * H * D * eb), tok * H * D * eb), (3 * up(tok * H * D * eb), tok * H * 4),
+                  (3 * up(tok * H * D * eb) + up(tok * H * 4), tok * H * 4)]
+        for reg, (off, n) in zip((gl.GDN_WS_Q, gl.GDN_WS_K, gl.GDN_WS_V, gl.GDN_WS_ALPHA, gl.GDN_WS_BETA), expect):
+            assert gl.gdn_workspace_region(desc, op, reg) == (off, n)
+            assert off + n <= total
+    desc = gl.make_desc(1, 64 if op == gl.GDN_OP_LOOP_PREFILL else 1, 2, 128, 128)
+    n, o = ctypes.c_size_t(), ctypes.c_size_t()
+    lib = gl.load()
+    assert lib.gdn_workspace_region(ctypes.byref(desc), op, 5, ctypes.byref(o), ctypes.byref(n)) == -3
+    assert lib.gdn_workspace_region(ctypes.byref(desc), gl.GDN_OP_SCAN_PREFILL, 0, ctypes.byref(o),
+                                    ctypes.byref(n)) == -3
+    assert lib.gdn_workspace_region(ctypes.byref(desc), op, 0, None, ctypes.byref(n)) in (-1, -2)
+
+
+def test_grid_limits_rejected_before_launch():
+    """Shapes whose launch grids or 32-bit token counts would not hold are refused on the host: more than
+    65535 sequences in a prefill call, or B*L of 2^31 tokens or more."""
+    for op in (gl.GDN_OP_LOOP_PREFILL, gl.GDN_OP_SCAN_PREFILL):
+        st, _ = _ws_status(gl.make_desc(65536, 1, 1, 64, 64), op)
+        assert st == -2 and "65535" in gl.gdn_last_error()
+        assert _ws_status(gl.make_desc(65535, 2, 1, 64, 64), op)[0] == 0
+    st, _ = _ws_status(gl.make_desc(4, 1 << 29, 1, 64, 64))
+    assert st == -2 and "2^31" in gl.gdn_last_error()
+    # decode calls run one workgroup per (sequence, head): many sequences are fine
+    assert _ws_status(gl.make_desc(100000, 1, 1, 64, 64), gl.GDN_OP_SCAN_DECODE)[0] == 0
 
 
 def test_packed_weight_bytes():
@@ -171,6 +211,7 @@ def test_binding_checks_tensor_sizes_on_host():
 def test_timer_validation(lib):
     h = ctypes.c_void_p()
     assert lib.gdn_timer_create(9, 4, ctypes.byref(h)) == -2
+    assert lib.gdn_timer_create(4, 4, ctypes.byref(h)) == -2   # not a stage
     assert lib.gdn_timer_create(0, 0, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(0, 4, None) == -1
     assert lib.gdn_timer_attach(None) == -1

@@ -11,21 +11,23 @@ import torch
 import looped_linear_attention_amd as gl
 import oracle
 import synth
-from helpers import TOL_BF16, TOL_F32, dev, rel_err, say
+from helpers import TOL_BF16, TOL_F32, canary_intact, dev, padded, poison_, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
 
 def _scan_gpu(x, act, s_init=None, want_state=True):
+    """gdn_scan_prefill on NaN-poisoned outputs and workspace, with canaries past the outputs."""
     q = x["q"]
     B, L, H, D = q.shape
     desc = gl.make_desc(B, L, H, D, D, T=1, act=act)
-    ws = gl.workspace(desc, gl.GDN_OP_SCAN_PREFILL)
-    o = torch.empty(B, L, H, D, device="cuda")
-    sf = torch.empty(B, H, D, D, device="cuda") if want_state else None
+    ws = poison_(gl.workspace(desc, gl.GDN_OP_SCAN_PREFILL))
+    o, ob = padded((B, L, H, D))
+    sf, sb = padded((B, H, D, D)) if want_state else (None, None)
     gl.gdn_scan_prefill(desc, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["alpha"]), dev(x["beta"]),
                         None if s_init is None else dev(s_init), o, sf, ws)
     torch.cuda.synchronize()
+    assert canary_intact(ob, o.numel()) and (sf is None or canary_intact(sb, sf.numel()))
     return o.cpu(), (sf.cpu() if sf is not None else None)
 
 
@@ -131,6 +133,43 @@ def test_scan_decode_parity(N, H, D, act, steps):
         eo, es = rel_err(o.cpu(), ro[:, 0]), rel_err(states.cpu(), rs)
         say(f"    step {t}: o err {eo:.2e} S err {es:.2e}")
         assert eo <= tol and es <= tol
+
+
+def test_scan_decode_full_generation():
+    """The batched-decode workload in full: 64 sequences x 16 heads of 128, 256 generated tokens, each token
+    advancing all 4 loop states (1,024 launches), inputs drawn by the workload's own generators.  Every o of
+    every (step, loop) and the final states are held to 3e-3 against the oracle run over the 256 tokens of
+    each loop state (the decode recurrence is the scan taken one token at a time)."""
+    w = synth.workload("decode_n64_s256")
+    N, H, D, T, steps = w.B, w.H, w.dk, w.T, w.steps
+    say(f"[scan_decode] {N} sequences x {steps} steps x {T} loop states")
+    S0 = synth.decode_state_init(w)
+    items = list(synth.decode_step_inputs(w, steps))
+    stack = lambda key, tau: torch.stack([items[s * T + tau][key] for s in range(steps)], 1)   # [N, steps, ...]
+    desc = gl.make_desc(N, 1, H, D, D, T=1, act=w.act)
+    states = dev(S0)
+    o_all = poison_(torch.empty(steps, T, N, H, D, device="cuda"))
+    dq = dev(torch.stack([it["q"] for it in items]))
+    dk = dev(torch.stack([it["k"] for it in items]))
+    dvv = dev(torch.stack([it["v"] for it in items]))
+    da = dev(torch.stack([it["alpha"] for it in items]))
+    db = dev(torch.stack([it["beta"] for it in items]))
+    for s in range(steps):
+        for tau in range(T):
+            i = s * T + tau
+            gl.gdn_scan_decode(desc, dq[i], dk[i], dvv[i], da[i], db[i], states[tau], o_all[s, tau])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o_all).all())
+    worst_o = worst_s = 0.0
+    for tau in range(T):
+        ro, rs = oracle.scan(stack("q", tau), stack("k", tau), stack("v", tau), stack("alpha", tau),
+                             stack("beta", tau), S0[tau])
+        g_o = o_all[:, tau].permute(1, 0, 2, 3).cpu()     # [N, steps, H, D]
+        eo = max(rel_err(g_o[:, s], ro[:, s]) for s in range(steps))
+        es = rel_err(states[tau].cpu(), rs)
+        say(f"    loop state {tau + 1}: worst per-step o err {eo:.2e}, final S err {es:.2e}")
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
 
 
 def test_prefill_state_then_decode_matches_longer_prefill():
