@@ -214,6 +214,21 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
                            const float *rho, float *states, float *h_out,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* The same decode step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments and results are those of
+ * gdn_loop_decode; the scratch is a library-held device array of
+ * GDN_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends, so the
+ * call allocates and frees nothing.  A step whose workspace
+ * (gdn_workspace_bytes with GDN_OP_LOOP_DECODE) exceeds that size returns
+ * GDN_ERR_WORKSPACE before anything is enqueued (bf16 at d = 2048: up to 508
+ * sequences).  Every call on one GPU uses the same array: calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller; calls on the same stream are ordered and safe. */
+#define GDN_NOALLOC_SCRATCH_BYTES (8u << 20)
+gdn_status gdn_loop_decode_noalloc(const gdn_desc *desc, const void *h_t, const void *Wpack,
+                                   const float *rho, float *states, float *h_out, void *stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 
 const char *gdn_status_string(gdn_status s);

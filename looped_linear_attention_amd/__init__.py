@@ -26,7 +26,7 @@ __all__ = [
     "GDN_WS_ALPHA", "GDN_WS_BETA", "GdnError", "gdn_desc", "make_desc", "lib_path",
     "load", "EXPORTED", "workspace", "workspace_view", "gdn_workspace_region",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
+    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
@@ -39,7 +39,7 @@ GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode",
+    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
@@ -94,6 +94,7 @@ def load():
         "gdn_scan_decode": [D, P, P, P, P, P, P, P, P],
         "gdn_loop_prefill": [D, P, P, P, P, P, P, P, S, P],
         "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
+        "gdn_loop_decode_noalloc": [D, P, P, P, P, P, P],
         "gdn_timer_create": [I, I, ctypes.POINTER(P)],
         "gdn_timer_set_stride": [P, I],
         "gdn_timer_attach": [P],
@@ -274,6 +275,18 @@ def gdn_loop_decode(desc, h_t, Wpack, rho, states, h_out, ws, stream=None):
         _ptr(rho, "rho", torch.float32, T * d),
         _ptr(states, "states", torch.float32, T * N * desc.H * desc.dk * desc.dv),
         _ptr(h_out, "h_out", torch.float32, N * d), wp, wn, _stream(stream)))
+
+
+def gdn_loop_decode_noalloc(desc, h_t, Wpack, rho, states, h_out, stream=None):
+    """gdn_loop_decode on the library's own device scratch (no workspace argument, nothing allocated)."""
+    a, N, d, T = desc.act_dtype, desc.B, desc.d, desc.T
+    pb = gdn_weights_packed_bytes(desc)
+    _check(load().gdn_loop_decode_noalloc(
+        ctypes.byref(desc), _ptr(h_t, "h_t", a, N * d),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)),
+        _ptr(rho, "rho", torch.float32, T * d),
+        _ptr(states, "states", torch.float32, T * N * desc.H * desc.dk * desc.dv),
+        _ptr(h_out, "h_out", torch.float32, N * d), _stream(stream)))
 
 
 # ---- timers ------------------------------------------------------------------

@@ -18,6 +18,10 @@ struct LaunchEvents {
 };
 LaunchEvents &launch_events();
 
+// Records `msg` as the calling thread's last error (gdn_last_error) and
+// returns `status` (a gdn_status).
+int set_last_error(int status, const char *msg);
+
 // Every kernel of the library is launched through here; the caller reads the
 // launch status with hipGetLastError().
 template <typename F, typename... Args>

@@ -191,6 +191,8 @@ hipError_t project(bool f32, int M, int d, int H, int D, const void *x, const vo
 
 LaunchEvents &gdn::launch_events() { return t_launch_events; }
 
+int gdn::set_last_error(int status, const char *msg) { return fail((gdn_status)status, "%s", msg); }
+
 extern "C" {
 
 const char *gdn_status_string(gdn_status s) {
