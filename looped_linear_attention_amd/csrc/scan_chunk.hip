@@ -1100,7 +1100,431 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     }
 }
 
+// ---------------------------------------------------------------------------
+// carry on 32-column slices (bf16 inputs, dk = dv = 128)
+// ---------------------------------------------------------------------------
+// One workgroup per (b, h, 32-column slice of S): half as many workgroups as
+// the 16-column carry, each bringing the chunk operands that all slices of a
+// head share (K, W, Q, M: 80 KiB per chunk) into its CU once for twice the
+// columns.  With 4 sequences of 16 heads this is 256 workgroups, one round on
+// the chip.  Nine waves:
+//   waves 0-3  the chain.  Wave w works on column tile ct = w / 2 (16 of the
+//              slice's columns) and row half rh = w % 2 (rows 64 rh .. 64 rh + 63
+//              of S).  Lane l = lr + 16 g keeps column 16 ct + lr and, in its
+//              tile tt (0..3), the rows
+//                  64 rh + 32 (tt / 2) + 8 g + 4 (tt % 2) + j,   j = 0..3,
+//              which are the rows that wave 2 rh + tt / 2 of the 16-column
+//              layout holds in its tile tt % 2: the prep's W fragments serve
+//              unchanged (rows of wave rh are fragments 4 rh .. 4 rh + 3).  Per
+//              chunk: S_c (split) into LDS, the partial K.S over its 64 rows for
+//              all 64 tokens, a pairwise exchange with the other row half (row
+//              half rh owns token tiles 2 rh and 2 rh + 1), E = V - diag(gamma) K S_c
+//              for its tiles into LDS, then S' = gamma_C S + W E on its rows.
+//   wave 4     the producer: every direct global -> LDS load of the workgroup.
+//   waves 5-8  the output: wave 5 + o handles tokens 16 o .. 16 o + 15 of both
+//              column tiles.  Q S_c of chunk cc in the window after B1 (S_c and
+//              Q of cc in LDS), then M E of cc, O = diag(gamma) Q S_c + M E, the
+//              loop residual and the stores in the window after B2 (E of cc in
+//              LDS).
+// Barrier schedule per chunk cc (all nine waves take part in each):
+//   B0  K, V, gamma, W of cc have landed.  Chain: S_c into LDS, K.S partials.
+//       Producer: V, gamma, W of cc+1 into the other stage, then M of cc.
+//       Output: h_prev of cc into registers, L2 prefetch.
+//   B1  partials and S_c visible; Q of cc has landed; the K tile is free.
+//       Chain: exchange, W fragments, E into LDS.  Producer: K of cc+1.
+//       Output: Q S_c.
+//   B2  E visible; M of cc has landed; Q is free.  Chain: S update.  Producer:
+//       Q of cc+1.  Output: M E, residual, stores.
+// M of cc is read after B2(cc) and rewritten after B0(cc+1), E after B1(cc+1)
+// and S_c after B0(cc+1), so each needs a single buffer; V, gamma and W have
+// two stages.  The producer's wait counts are the same every chunk (past the
+// last chunk it re-reads the last one into buffers nobody reads any more).
+struct CarryW {
+    static constexpr int D = 128;
+    static constexpr int SW = 32;                    // columns of S per workgroup
+    static constexpr int NSL = D / SW;               // slices per head
+    static constexpr int ROWB = D * 2;               // bytes of a token row of K or Q
+    static constexpr int TILE = C * ROWB;            // K or Q chunk tile (16 KiB)
+    static constexpr int T_INS = TILE / 1024;        // direct loads per tile
+    static constexpr int VROWB = SW * 2;             // bytes of a token row of the V slice
+    static constexpr int V_INS = C * VROWB / 1024;
+    static constexpr int W_BYTES = D * C * 4;        // W hi and lo parts of one chunk
+    static constexpr int W_INS = W_BYTES / 1024;
+    static constexpr int VGW_INS = V_INS + 1 + W_INS;
+    static constexpr int M_BYTES = C * C * 4;        // M hi and lo parts of one chunk
+    static constexpr int M_INS = M_BYTES / 1024;
+    static_assert(VGW_INS + M_INS < 64, "the vector-memory counter holds 0..63");
+};
+
+template <int RES, bool XN>
+__global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v, int L, int H, int Nc,
+    const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
+    float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
+    float *h_out, bf16 *x_next) {
+    using G = CarryW;
+    using KT = KTile<128, bf16>;
+    constexpr int D = G::D;
+    __shared__ __attribute__((aligned(16))) unsigned char k_s[G::TILE], q_s[G::TILE], m_s[G::M_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char w0_s[G::W_BYTES], w1_s[G::W_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v0_s[C * G::VROWB], v1_s[C * G::VROWB];
+    __shared__ __attribute__((aligned(16))) float g0_s[C], g1_s[C];
+    __shared__ __attribute__((aligned(16))) f32x4 red[4][2][64];   // [source wave][token tile of the partner][lane]
+    __shared__ __attribute__((aligned(16))) uint4 ex[2][4][64];    // [column tile][token tile][lane]: E hi | lo
+    __shared__ __attribute__((aligned(16))) uint4 sc[2][4][2][64]; // [column tile][k-step][hi, lo][lane]: S_c
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    // heads run along x, so the slices of one head get workgroup ids congruent
+    // mod 8 and share an XCD's L2
+    const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
+    const int col0 = slice * G::SW;
+    const int64_t tokb = (int64_t)b * L;
+    const int64_t cidb = ((int64_t)b * H + h) * Nc;
+
+    if (wave == 4) {
+        // ---- producer ----
+        const unsigned lk = lds_addr(k_s), lq = lds_addr(q_s), lm = lds_addr(m_s);
+        const unsigned lv[2] = {lds_addr(v0_s), lds_addr(v1_s)}, lgm[2] = {lds_addr(g0_s), lds_addr(g1_s)};
+        const unsigned lw[2] = {lds_addr(w0_s), lds_addr(w1_s)};
+        const unsigned rs = (unsigned)(H * D * 2);   // bytes per token row of q / k / v
+        unsigned toff[G::T_INS], voff[G::V_INS];
+#pragma unroll
+        for (int n = 0; n < G::T_INS; ++n) {
+            const int p = n * 64 + lane, r = p / KT::NCH;
+            toff[n] = r * rs + KT::phys(r, p % KT::NCH) * 16;
+        }
+        constexpr int LPR = G::VROWB / 16;   // lanes per V row
+#pragma unroll
+        for (int n = 0; n < G::V_INS; ++n) {
+            const int p = n * 64 + lane;
+            voff[n] = (p / LPR) * rs + (p % LPR) * 16;
+        }
+        // K or Q tile of chunk cc (rows past the end re-read the last row)
+        auto load_tile = [&](unsigned dst, const bf16 *src, int cc) __attribute__((always_inline)) {
+            const int c0 = cc * C;
+            if (c0 + C <= L) {
+                const bf16 *base = src + ((tokb + c0) * H + h) * D;
+#pragma unroll
+                for (int n = 0; n < G::T_INS; ++n) dma16_async_s_at(base, toff[n], dst + n * 1024);
+            } else {
+#pragma unroll
+                for (int n = 0; n < G::T_INS; ++n) {
+                    const int p = n * 64 + lane, r = p / KT::NCH;
+                    const int tok = min(c0 + r, L - 1);
+                    dma16_async_at(src + ((tokb + tok) * H + h) * D + KT::phys(r, p % KT::NCH) * 8, dst + n * 1024);
+                }
+            }
+        };
+        // V slice, gamma and W of chunk cc into stage st
+        auto load_vgw = [&](int st, int cc) __attribute__((always_inline)) {
+            const int c0 = cc * C;
+            if (c0 + C <= L) {
+                const bf16 *vb = v + ((tokb + c0) * H + h) * D + col0;
+#pragma unroll
+                for (int n = 0; n < G::V_INS; ++n) dma16_async_s_at(vb, voff[n], lv[st] + n * 1024);
+            } else {
+#pragma unroll
+                for (int n = 0; n < G::V_INS; ++n) {
+                    const int p = n * 64 + lane;
+                    const int tok = min(c0 + p / LPR, L - 1);
+                    dma16_async_at(v + ((tokb + tok) * H + h) * D + col0 + (p % LPR) * 8, lv[st] + n * 1024);
+                }
+            }
+            if (lane < C / 4) dma16_async_s_at(g + (cidb + cc) * C, lane * 16, lgm[st]);   // one instruction
+            const float *wsrc = W + (cidb + cc) * D * C;
+#pragma unroll
+            for (int n = 0; n < G::W_INS; ++n) dma16_async_s_at(wsrc + n * 256, lane * 16, lw[st] + n * 1024);
+        };
+        auto load_m = [&](int cc) __attribute__((always_inline)) {
+            const float *msrc = M + (cidb + cc) * C * C;
+#pragma unroll
+            for (int n = 0; n < G::M_INS; ++n) dma16_async_s_at(msrc + n * 256, lane * 16, lm + n * 1024);
+        };
+        auto pstep = [&](auto stc, int cc) __attribute__((always_inline)) {
+            constexpr int ST = decltype(stc)::value;   // stage of chunk cc
+            const int nx = min(cc + 1, Nc - 1);
+            wait_vmcnt<G::T_INS>();                    // K, V, gamma, W of cc landed (Q of cc in flight)
+            lds_barrier();                             // B0
+            load_vgw(1 - ST, nx);
+            load_m(cc);
+            wait_vmcnt<G::VGW_INS + G::M_INS>();       // Q of cc landed
+            lds_barrier();                             // B1
+            load_tile(lk, k, nx);
+            wait_vmcnt<G::T_INS>();                    // M of cc landed
+            lds_barrier();                             // B2
+            load_tile(lq, q, nx);
+        };
+        load_vgw(0, 0);
+        load_tile(lk, k, 0);
+        load_tile(lq, q, 0);
+        for (int cc = 0; cc < Nc; cc += 2) {
+            pstep(std::integral_constant<int, 0>(), cc);
+            if (cc + 1 < Nc) pstep(std::integral_constant<int, 1>(), cc + 1);
+        }
+        wait_vmcnt<0>();   // no direct load may write LDS after the workgroup ends
+        return;
+    }
+
+    if (wave < 4) {
+        // ---- chain ----
+        const int ct = wave >> 1, rh = wave & 1;
+        const int col = col0 + 16 * ct + lr;
+        const int64_t sbase = ((int64_t)b * H + h) * D * D;
+        auto srow = [&](int tt, int j) { return 64 * rh + 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1) + j; };
+        float Sv[4][4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sv[tt][j] = s_init ? s_init[sbase + (int64_t)srow(tt, j) * D + col] : 0.f;
+        // nothing loaded before the loop may be pending inside it
+        wait_vmcnt<0>();
+        const bf16x8 *wf0 = reinterpret_cast<const bf16x8 *>(w0_s) + rh * 16 * 64 + lane;
+        const bf16x8 *wf1 = reinterpret_cast<const bf16x8 *>(w1_s) + rh * 16 * 64 + lane;
+        auto step = [&](auto stc) __attribute__((always_inline)) {
+            constexpr int ST = decltype(stc)::value;
+            const bf16 *v_cur = reinterpret_cast<const bf16 *>(ST == 0 ? v0_s : v1_s);
+            const float *g_cur = ST == 0 ? g0_s : g1_s;
+            const bf16x8 *w_cur = ST == 0 ? wf0 : wf1;
+            lds_barrier();   // B0
+            // S_c as the B operand of K.S, local k-step kl = rows 64 rh + 32 kl ..; also into LDS for Q.S_c
+            bf16x8 sh[2], sl[2];
+#pragma unroll
+            for (int kl = 0; kl < 2; ++kl) {
+                const float sf[8] = {Sv[2 * kl][0], Sv[2 * kl][1], Sv[2 * kl][2], Sv[2 * kl][3],
+                                     Sv[2 * kl + 1][0], Sv[2 * kl + 1][1], Sv[2 * kl + 1][2], Sv[2 * kl + 1][3]};
+                __bf16 hh[8], ll[8];
+                split_bf16(sf, hh, ll);
+                sh[kl] = pack8(hh);
+                sl[kl] = pack8(ll);
+                __builtin_memcpy(&sc[ct][2 * rh + kl][0][lane], &sh[kl], 16);
+                __builtin_memcpy(&sc[ct][2 * rh + kl][1][lane], &sl[kl], 16);
+            }
+            f32x4 ks[4];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                ks[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kl = 0; kl < 2; ++kl) {
+                    const bf16x8 a = tile_bf8<D>(k_s, 16 * tm + lr, 64 * rh + 32 * kl + 8 * lg);
+                    ks[tm] = mfma16x16x32(a, sh[kl], ks[tm]);
+                    ks[tm] = mfma16x16x32(a, sl[kl], ks[tm]);
+                }
+            }
+            // the partner owns the other row half's token tiles
+            red[wave][0][lane] = rh ? ks[0] : ks[2];
+            red[wave][1][lane] = rh ? ks[1] : ks[3];
+            lds_barrier();   // B1
+            f32x4 kt[2];
+            kt[0] = (rh ? ks[2] : ks[0]) + red[wave ^ 1][0][lane];
+            kt[1] = (rh ? ks[3] : ks[1]) + red[wave ^ 1][1][lane];
+            // W fragments of this row half (read now, used after B2)
+            bf16x8 wh[4][2], wl[4][2];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    wh[tt][s2] = w_cur[((tt * 2 + s2) * 2 + 0) * 64];
+                    wl[tt][s2] = w_cur[((tt * 2 + s2) * 2 + 1) * 64];
+                }
+            // E = V - diag(gamma) K S_c for tokens 16 tm + 4 lg + j of the two owned tiles
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tm = 2 * rh + i;
+                float e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * tm + 4 * lg + j;
+                    e[j] = (float)v_cur[r * G::SW + 16 * ct + lr] - g_cur[r] * kt[i][j];
+                }
+                __bf16 eh[4], el[4];
+                split_bf16(e, eh, el);
+                uint4 u;
+                __builtin_memcpy(&u.x, eh, 8);
+                __builtin_memcpy(&u.z, el, 8);
+                ex[ct][tm][lane] = u;
+            }
+            const float gC = g_cur[C - 1];
+            lds_barrier();   // B2
+            // E of this column tile as the B operand: k-step s2 covers token tiles 2 s2, 2 s2 + 1
+            bf16x8 ebh[2], ebl[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const uint4 a4 = ex[ct][2 * s2][lane], c4 = ex[ct][2 * s2 + 1][lane];
+                const uint4 hi = make_uint4(a4.x, a4.y, c4.x, c4.y), lo = make_uint4(a4.z, a4.w, c4.z, c4.w);
+                __builtin_memcpy(&ebh[s2], &hi, 16);
+                __builtin_memcpy(&ebl[s2], &lo, 16);
+            }
+            // S' = gamma_C S + W E: one accumulator chain per (row tile, k-step)
+            f32x4 we[4][2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    we[tt][s2] = mma_hl(wh[tt][s2], wl[tt][s2], ebh[s2], ebl[s2], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Sv[tt][j] = gC * Sv[tt][j] + (we[tt][0][j] + we[tt][1][j]);
+        };
+        for (int cc = 0; cc < Nc; cc += 2) {
+            step(std::integral_constant<int, 0>());
+            if (cc + 1 < Nc) step(std::integral_constant<int, 1>());
+        }
+        if (s_final) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_final[sbase + (int64_t)srow(tt, j) * D + col] = Sv[tt][j];
+        }
+        return;
+    }
+
+    // ---- output (waves 5-8): tokens 16 ot .. 16 ot + 15, both column tiles ----
+    const int ot = wave - 5;
+    const int d = H * D;
+    float rho_c[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) rho_c[ct] = RES ? rho[h * D + col0 + 16 * ct + lr] : 0.f;
+    float hp[2][4];
+    // h_prev of chunk cc (rows past the end of the sequence read the last row; never stored)
+    auto load_hp = [&](int cc) __attribute__((always_inline)) {
+        const int c0 = cc * C, last = L - 1 - c0;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hp[ct][j] = 0.f;
+                if constexpr (RES != 0) {
+                    const int64_t off = (tokb + c0 + min(16 * ot + 4 * lg + j, last)) * (int64_t)d + (int64_t)h * D +
+                                        col0 + 16 * ct + lr;
+                    if constexpr (RES == 2) hp[ct][j] = (float)static_cast<const bf16 *>(h_prev)[off];
+                    else hp[ct][j] = static_cast<const float *>(h_prev)[off];
+                }
+            }
+    };
+    // L2 prefetch, PF_AHEAD chunks ahead: one load touching each 128-byte line of
+    // that chunk's K, Q, V, W, M, h_prev and gamma for this head, the lines dealt
+    // over the head's slice workgroups (which share an XCD's L2); the loaded word
+    // is consumed two chunks later.
+    unsigned pfv[2] = {0u, 0u};
+    auto prefetch = [&](auto pc, int cc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        constexpr int RL = G::ROWB / 128;
+        constexpr int KL = C * RL, WL = G::W_BYTES / 128, ML = G::M_BYTES / 128;
+        constexpr int HES = RES == 2 ? 2 : 4;
+        constexpr int HRL = RES ? D * HES / 128 : 0, HL = C * HRL;
+        constexpr int NL = 3 * KL + WL + ML + HL + 2;
+        asm volatile("" ::"v"(pfv[P]));
+        const int j = slice + G::NSL * (lane * 4 + ot);
+        if (j < NL) {
+            const int cp = min(cc + PF_AHEAD, Nc - 1), c0p = cp * C;
+            const char *p;
+            int jj = j;
+            auto row_tok = [&](int r) { return tokb + min(c0p + r, L - 1); };
+            if (jj < KL) {
+                p = reinterpret_cast<const char *>(k + (row_tok(jj / RL) * H + h) * D) + (jj % RL) * 128;
+            } else if ((jj -= KL) < KL) {
+                p = reinterpret_cast<const char *>(q + (row_tok(jj / RL) * H + h) * D) + (jj % RL) * 128;
+            } else if ((jj -= KL) < KL) {
+                p = reinterpret_cast<const char *>(v + (row_tok(jj / RL) * H + h) * D) + (jj % RL) * 128;
+            } else if ((jj -= KL) < WL) {
+                p = reinterpret_cast<const char *>(W + (cidb + cp) * D * C) + jj * 128;
+            } else if ((jj -= WL) < ML) {
+                p = reinterpret_cast<const char *>(M + (cidb + cp) * C * C) + jj * 128;
+            } else if ((jj -= ML) < HL) {
+                p = reinterpret_cast<const char *>(h_prev) +
+                    (row_tok(jj / HRL) * (int64_t)d + (int64_t)h * D) * HES + (jj % HRL) * 128;
+            } else {
+                jj -= HL;
+                p = reinterpret_cast<const char *>(g + (cidb + cp) * C) + jj * 128;
+            }
+            pfv[P] = *reinterpret_cast<const unsigned *>(p);
+        }
+    };
+    const bf16x8 *mf = reinterpret_cast<const bf16x8 *>(m_s) + lane;
+    auto ostep = [&](auto stc, int cc) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stc)::value;
+        const float *g_cur = ST == 0 ? g0_s : g1_s;
+        const int c0 = cc * C;
+        lds_barrier();   // B0
+        load_hp(cc);
+        prefetch(stc, cc);
+        lds_barrier();   // B1
+        // Q S_c for both column tiles: two accumulator chains each (k-steps {0,2}, {1,3})
+        f32x4 qa[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = tile_bf8<D>(q_s, 16 * ot + lr, 32 * ks + 8 * lg);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                bf16x8 bh, bl;
+                __builtin_memcpy(&bh, &sc[ct][ks][0][lane], 16);
+                __builtin_memcpy(&bl, &sc[ct][ks][1][lane], 16);
+                if (ks < 2) qa[ct][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+                qa[ct][ks & 1] = mfma16x16x32(a, bh, qa[ct][ks & 1]);
+                qa[ct][ks & 1] = mfma16x16x32(a, bl, qa[ct][ks & 1]);
+            }
+        }
+        lds_barrier();   // B2
+        f32x4 me[2][2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 mh = mf[((ot * 2 + s2) * 2 + 0) * 64], ml = mf[((ot * 2 + s2) * 2 + 1) * 64];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const uint4 a4 = ex[ct][2 * s2][lane], c4 = ex[ct][2 * s2 + 1][lane];
+                const uint4 hi = make_uint4(a4.x, a4.y, c4.x, c4.y), lo = make_uint4(a4.z, a4.w, c4.z, c4.w);
+                bf16x8 ebh, ebl;
+                __builtin_memcpy(&ebh, &hi, 16);
+                __builtin_memcpy(&ebl, &lo, 16);
+                me[ct][s2] = mma_hl(mh, ml, ebh, ebl, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+        }
+        const f32x4 gv = *reinterpret_cast<const f32x4 *>(g_cur + 16 * ot + 4 * lg);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x4 qs = qa[ct][0] + qa[ct][1], mev = me[ct][0] + me[ct][1];
+            const int col = col0 + 16 * ct + lr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ot + 4 * lg + j;
+                if (c0 + r >= L) continue;
+                const float ov = gv[j] * qs[j] + mev[j];
+                const int64_t row = tokb + c0 + r;
+                if constexpr (RES == 0) {
+                    o[(row * H + h) * D + col] = ov;
+                } else {
+                    const float hv = ov + rho_c[ct] * hp[ct][j];
+                    const int64_t hi = row * d + (int64_t)h * D + col;
+                    h_out[hi] = hv;
+                    if constexpr (XN) x_next[hi] = (bf16)hv;
+                }
+            }
+        }
+    };
+    for (int cc = 0; cc < Nc; cc += 2) {
+        ostep(std::integral_constant<int, 0>(), cc);
+        if (cc + 1 < Nc) ostep(std::integral_constant<int, 1>(), cc + 1);
+    }
+    asm volatile("" ::"v"(pfv[0]), "v"(pfv[1]));
+}
+
 }  // namespace
+
+// Compute units of the current device (looked up once per device).
+static int compute_units() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
 
 hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k,
                             GateSrc gs, ChunkWs ws, hipStream_t s) {
@@ -1126,9 +1550,25 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
 hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,
                              ChunkWs ws, const float *s_init, float *s_final, CarryOut out, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
-    dim3 grid(H, D / 16, B);
     const int res = out.h_out == nullptr ? 0 : (out.h_prev_bf16 ? 2 : 1);
     const bool xn = out.h_out != nullptr && out.x_next != nullptr;
+    // 32-column slices when 16-column ones would need more than one round of
+    // workgroups (one workgroup per CU: each holds most of the CU's LDS).  A
+    // 32-column chunk step takes nearly twice as long, so with one round of
+    // 16-column workgroups those are faster.
+    if (!f32 && D == 128 && (int64_t)B * H * (D / 16) > compute_units()) {
+        const dim3 gridw(H, D / CarryW::SW, B);
+#define CARRYW(R, X)                                                                               \
+    launch_kernel((k_scan_carry_w<R, X>), gridw, dim3(CARRY_THREADS), 0, s, (const bf16 *)q, (const bf16 *)k, \
+                  (const bf16 *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
+                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next)
+        if (res == 0) CARRYW(0, false);
+        else if (res == 1) { if (xn) CARRYW(1, true); else CARRYW(1, false); }
+        else { if (xn) CARRYW(2, true); else CARRYW(2, false); }
+#undef CARRYW
+        return hipGetLastError();
+    }
+    dim3 grid(H, D / 16, B);
 #define CARRY(DD, T, R, X)                                                                         \
     launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(CARRY_THREADS), 0, s, (const T *)q, (const T *)k, \
                   (const T *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \

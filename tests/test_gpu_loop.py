@@ -235,6 +235,15 @@ def test_loop_prefill_b2_ragged_wide():
     check_forced_loops(w, x, 2, 700)
 
 
+def test_loop_prefill_b3_ragged_wide_carry():
+    """Three sequences of 700 tokens with 16 heads: 384 (sequence, head, 16-column) slices are more than one
+    round of workgroups, so the carry takes 32-column slices; both sequences' ends fall in partial chunks."""
+    w = synth.workload("prefill_b4_l8192")
+    say("[loop_prefill] 16 heads bf16 B=3 L=700 (32-column carry), stage-forced")
+    x = synth.prefill_inputs(w, B=3, L=700)
+    check_forced_loops(w, x, 3, 700)
+
+
 @pytest.mark.parametrize("L", [300, 1500])
 def test_loop_prefill_no_decay(L):
     """alpha_lo = 1: every gate alpha is exactly 1, the loops run the delta rule without decay (DeltaNet),

@@ -44,6 +44,9 @@ CASES = [
     (1, 300, 2, 128, "bf16", (0.0, 1.0), (0.0, 2.0), True),   # negative eigenvalues (beta up to 2)
     (1, 300, 2, 128, "bf16", (1.0, 1.0), (0.0, 1.0), True),   # no decay (alpha = 1: DeltaNet)
     (1, 200, 2, 64, "f32", (1.0, 1.0), (0.0, 2.0), True),     # no decay, beta up to 2
+    # more (sequence, head) pairs than one round of 16-column workgroups: the 32-column carry
+    (3, 1000, 16, 128, "bf16", (0.0, 1.0), (0.0, 1.0), True),  # ragged: 15 chunks + 40 tokens
+    (5, 130, 16, 128, "bf16", (0.9, 1.0), (0.0, 2.0), True),   # 2 chunks + 2 tokens, beta up to 2
 ]
 
 
