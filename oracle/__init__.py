@@ -52,7 +52,7 @@ _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
 _lib = None
 
 __all__ = [
-    "build", "num_threads", "round_bf16", "round_f32", "scan", "project",
+    "build", "num_threads", "round_bf16", "round_f32", "scan", "scan_backward", "project",
     "loop_prefill", "loop_decode_step", "scan_chunkwise",
 ]
 
@@ -79,6 +79,8 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         lib.oracle_scan.argtypes = [ctypes.c_int] * 5 + [dp] * 8
         lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_scan_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14
+        lib.oracle_scan_backward.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -149,6 +151,29 @@ def scan(q, k, v, alpha, beta, s_init=None, want_state: bool = True):
     if rc != 0:
         raise MemoryError("oracle_scan could not allocate its state")
     return o, sf
+
+
+def scan_backward(q, k, v, alpha, beta, d_o, s_init=None, d_sfinal=None):
+    """Gradients of one scan pass (fp64, token by token in reverse; see gdn_scan_ref.c).
+
+    Given d_o = dL/do [B,L,H,dv] and d_sfinal = dL/dS_final [B,H,dk,dv] (None: zero) for the scan of
+    ``scan(q, k, v, alpha, beta, s_init)``, returns dict(dq, dk [B,L,H,dk], dv [B,L,H,dv], dalpha, dbeta
+    [B,L,H], ds_init [B,H,dk,dv]).  q and k are treated as given (no normalisation).
+    """
+    q, k, v, alpha, beta, d_o = map(_f64, (q, k, v, alpha, beta, d_o))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    si = None if s_init is None else _f64(s_init)
+    dsf = None if d_sfinal is None else _f64(d_sfinal)
+    out = dict(dq=np.zeros((B, L, H, dk)), dk=np.zeros((B, L, H, dk)), dv=np.zeros((B, L, H, dv)),
+               dalpha=np.zeros((B, L, H)), dbeta=np.zeros((B, L, H)), ds_init=np.zeros((B, H, dk, dv)))
+    rc = _load().oracle_scan_backward(B, L, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(si), _ptr(d_o), _ptr(dsf), _ptr(out["dq"]), _ptr(out["dk"]),
+                                      _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]),
+                                      _ptr(out["ds_init"]))
+    if rc != 0:
+        raise MemoryError("oracle_scan_backward could not allocate its scratch")
+    return out
 
 
 # ---------------------------------------------------------------------------

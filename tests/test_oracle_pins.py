@@ -351,3 +351,92 @@ def test_generators_deterministic():
     x2 = synth.scan_inputs(3, 1, 10, 2, 8, 8)
     assert all(torch.equal(x1[k], x2[k]) for k in x1)
     assert torch.allclose(x1["q"].float().norm(dim=-1), torch.ones(1, 10, 2), atol=1e-2)
+
+
+# ---------------------------------------------------------------------------
+# backward of the scan: pinned by finite differences of the (pinned) forward
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, B, L, H, dk, dv, beta_hi=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, L, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, L, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, L, H, dv))
+    al = rng.uniform(0.3, 1.0, (B, L, H))
+    be = rng.uniform(0.0, beta_hi, (B, L, H))
+    s0 = rng.standard_normal((B, H, dk, dv)) * 0.3
+    do = rng.standard_normal((B, L, H, dv))
+    dsf = rng.standard_normal((B, H, dk, dv))
+    return dict(q=q, k=k, v=v, alpha=al, beta=be, s_init=s0), do, dsf
+
+
+def _loss(x, do, dsf):
+    o, s = oracle.scan(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["s_init"])
+    return float(np.sum(o * do) + np.sum(s * dsf))
+
+
+@pytest.mark.parametrize("B,L,H,dk,dv,beta_hi", [(2, 7, 2, 4, 3, 1.0), (1, 9, 1, 5, 5, 2.0)])
+def test_scan_backward_equals_central_differences(B, L, H, dk, dv, beta_hi):
+    """Every gradient element against (L(x + e) - L(x - e)) / 2e of the forward oracle, L = <d_o, o> +
+    <d_S, S_final>; fp64 central differences are exact to O(e^2) (e = 1e-5 here, error ~1e-9)."""
+    x, do, dsf = _bwd_case(11 + L, B, L, H, dk, dv, beta_hi)
+    g = oracle.scan_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], do, x["s_init"], dsf)
+    names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "s_init": "ds_init"}
+    eps = 1e-5
+    for key, gk in names.items():
+        base = x[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            xp, xm = dict(x), dict(x)
+            xp[key] = base.copy(); xp[key][idx] += eps
+            xm[key] = base.copy(); xm[key][idx] -= eps
+            fd[idx] = (_loss(xp, do, dsf) - _loss(xm, do, dsf)) / (2 * eps)
+        err = np.max(np.abs(fd - g[gk])) / max(np.max(np.abs(fd)), 1e-12)
+        assert err < 1e-7, (key, err)
+
+
+def test_scan_backward_directional_long():
+    """Past the 64-token checkpoint blocks (L = 150): directional derivatives along random directions of
+    every input at once agree with central differences."""
+    x, do, dsf = _bwd_case(5, 1, 150, 2, 8, 6)
+    g = oracle.scan_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], do, x["s_init"], dsf)
+    rng = np.random.default_rng(6)
+    names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "s_init": "ds_init"}
+    for trial in range(3):
+        dirs = {key: rng.standard_normal(x[key].shape) for key in names}
+        eps = 1e-6
+        xp = {key: x[key] + eps * dirs[key] for key in names}
+        xm = {key: x[key] - eps * dirs[key] for key in names}
+        fd = (_loss(xp, do, dsf) - _loss(xm, do, dsf)) / (2 * eps)
+        an = sum(float(np.sum(g[gk] * dirs[key])) for key, gk in names.items())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
+def test_scan_backward_pure_decay_closed_form():
+    """beta = 0: S_t = gamma_t S_0 and o_t = gamma_t S_0^T q_t, so dq_t = gamma_t S_0 d_o_t, dk = dv = 0 and
+    dS_0 = sum_t gamma_t q_t d_o_t^T + gamma_L d_S (gamma_t the product of alpha up to t)."""
+    x, do, dsf = _bwd_case(21, 1, 70, 1, 6, 5)
+    x["beta"][:] = 0.0
+    g = oracle.scan_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], do, x["s_init"], dsf)
+    gam = np.cumprod(x["alpha"][0, :, 0])
+    S0 = x["s_init"][0, 0]
+    dq = gam[:, None] * (do[0, :, 0] @ S0.T)
+    assert np.allclose(g["dq"][0, :, 0], dq, rtol=1e-12, atol=1e-12)
+    assert np.all(g["dk"] == 0) and np.all(g["dv"] == 0)
+    ds0 = np.einsum("t,ti,tj->ij", gam, x["q"][0, :, 0], do[0, :, 0]) + gam[-1] * dsf[0, 0]
+    assert np.allclose(g["ds_init"][0, 0], ds0, rtol=1e-12, atol=1e-12)
+
+
+def test_scan_backward_split_chain_rule():
+    """Gradients through [0, m) then [m, L) (the second half's ds_init fed to the first half as dS_final)
+    equal the single pass's."""
+    x, do, dsf = _bwd_case(31, 1, 100, 2, 6, 4)
+    g = oracle.scan_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], do, x["s_init"], dsf)
+    m = 37
+    a = {key: (val[:, :m] if key != "s_init" else val) for key, val in x.items()}
+    _, s_m = oracle.scan(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s_init"])
+    b = {key: (val[:, m:] if key != "s_init" else s_m) for key, val in x.items()}
+    g2 = oracle.scan_backward(b["q"], b["k"], b["v"], b["alpha"], b["beta"], do[:, m:], b["s_init"], dsf)
+    g1 = oracle.scan_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], do[:, :m], a["s_init"], g2["ds_init"])
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
+        assert np.allclose(np.concatenate([g1[key], g2[key]], 1), g[key], rtol=1e-11, atol=1e-12), key
+    assert np.allclose(g1["ds_init"], g["ds_init"], rtol=1e-11, atol=1e-12)
