@@ -102,6 +102,14 @@ def carry_bytes_per_step(w) -> int:
     return total
 
 
+def carry_kernel(w) -> str:
+    """The carry the library launches: 32-column slices (k_scan_carry_w) for bf16 128-wide heads when
+    16-column slices would need more than one workgroup per CU, else k_scan_carry."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return "k_scan_carry_w" if (w.act == "bf16" and w.dk == 128 and w.B * w.H * (w.dk // 16) > cus) else "k_scan_carry"
+
+
 def decode_bytes_per_launch(N, H, D, act_bytes=2) -> int:
     """Algorithmic HBM bytes of one decode launch: state read + write, q/k/v, alpha/beta, o."""
     return N * H * (2 * D * D * 4 + 3 * D * act_bytes + 2 * 4 + D * 4)
@@ -363,9 +371,10 @@ def prefill_record(w, pf):
     if "scan_carry" in st:
         bpl = carry_bytes_per_step(w) * tokens / w.T
         gbs = bpl / (st["scan_carry"]["avg_ms"] * 1e-3) / 1e9
-        rec["roofline_carry"] = {"bound": "hbm", "kernel": "k_scan_carry", "achieved": gbs,
+        cname = carry_kernel(w)
+        rec["roofline_carry"] = {"bound": "hbm", "kernel": cname, "achieved": gbs,
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                 "traffic": traffic_for("k_scan_carry", w.name), "bytes_per_launch": bpl,
+                                 "traffic": traffic_for(cname, w.name), "bytes_per_launch": bpl,
                                  "avg_launch_us": st["scan_carry"]["avg_ms"] * 1e3}
     return rec
 
