@@ -101,7 +101,7 @@ gdn_status gdn_weights_pack(const gdn_desc *desc, const void *Wq, const void *Wk
 /* ---- workspace ---------------------------------------------------------- */
 
 enum { GDN_OP_LOOP_PREFILL = 0, GDN_OP_LOOP_DECODE = 1, GDN_OP_SCAN_PREFILL = 2,
-       GDN_OP_SCAN_DECODE = 3, GDN_OP_PROJECT = 4 };
+       GDN_OP_SCAN_DECODE = 3, GDN_OP_PROJECT = 4, GDN_OP_SCAN_BACKWARD = 5 };
 
 /* Device scratch bytes that operation `op` needs for `desc` (0 is valid). */
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes);
@@ -175,6 +175,27 @@ gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k,
                            const void *v, const float *alpha, const float *beta,
                            float *states, float *o, void *stream);
 
+/* Gradients of one gdn_scan_prefill pass (training: LT2 Appendix C trains
+ * every looped model through this mixer with bf16 mixed precision).  For a
+ * loss L of the scan's outputs o and final state S_final, given
+ *   d_o [B, L, H, dv]        device fp32, dL/do
+ *   d_sfinal [B, H, dk, dv]  device fp32 or NULL (zero), dL/dS_final
+ * and the forward inputs (q, k, v in desc->act, alpha, beta, s_init as for
+ * gdn_scan_prefill), it writes
+ *   dq, dk [B, L, H, dk], dv [B, L, H, dv], dalpha, dbeta [B, L, H]   device fp32
+ *   ds_init [B, H, dk, dv]   device fp32 or NULL
+ * The forward pass is recomputed (chunk-start states into the workspace);
+ * ws is gdn_workspace_bytes(GDN_OP_SCAN_BACKWARD).  The gradients are those
+ * of the token recurrence (the chunkwise form is exact up to rounding); q
+ * and k are treated as given (no normalisation).  alpha must be in (0, 1]:
+ * dalpha divides by alpha.  GDN_ERR_UNSUPPORTED for fp32 inputs with
+ * dk = 128.  Outputs must not alias inputs. */
+gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, const float *s_init,
+                             const float *d_o, const float *d_sfinal, float *dq, float *dk,
+                             float *dv, float *dalpha, float *dbeta, float *ds_init, void *ws,
+                             size_t ws_bytes, void *stream);
+
 /* ---- the looped mixer --------------------------------------------------- */
 
 /* T weight-tied loops over a whole prompt (prefill).
@@ -242,7 +263,12 @@ const char *gdn_version(void);
 /* Stages that a timer can bracket (4 is not a stage: it named a separate
  * output pass that the carry now performs, and gdn_timer_create rejects it). */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
-       GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5 };
+       GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5, GDN_STAGE_BWD_CARRY = 6, GDN_STAGE_BWD_CHUNK = 7,
+       GDN_STAGE_BWD_PREP = 8 };
+/* GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_CARRY and GDN_STAGE_BWD_CHUNK time the
+ * three kernels of gdn_scan_backward that follow its forward recomputation
+ * (whose prep and carry are timed as GDN_STAGE_SCAN_PREP and
+ * GDN_STAGE_SCAN_CARRY). */
 /* GDN_STAGE_SCAN_CARRY times the carry kernel, which computes the chunk outputs
  * (and the loop residual) as well.  GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
  * more tokens the gates alpha/beta leave the GEMM's epilogue: gdn_project and

@@ -21,25 +21,27 @@ import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
-    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
-    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES", "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
+    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
+    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES", "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_PREP",
+    "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
     "GDN_WS_ALPHA", "GDN_WS_BETA", "GdnError", "gdn_desc", "make_desc", "lib_path",
     "load", "EXPORTED", "workspace", "workspace_view", "gdn_workspace_region",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
+    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
-GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT = range(5)
+GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT, GDN_OP_SCAN_BACKWARD = range(6)
 GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_GATES = 0, 1, 2, 3, 5
+GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_PREP = 6, 7, 8
 GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
+    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
@@ -92,6 +94,7 @@ def load():
         "gdn_project": [D, P, P, P, P, P, P, P, P],
         "gdn_scan_prefill": [D, P, P, P, P, P, P, P, P, P, S, P],
         "gdn_scan_decode": [D, P, P, P, P, P, P, P, P],
+        "gdn_scan_backward": [D] + [P] * 15 + [S, P],
         "gdn_loop_prefill": [D, P, P, P, P, P, P, P, S, P],
         "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
         "gdn_loop_decode_noalloc": [D, P, P, P, P, P, P],
@@ -239,6 +242,21 @@ def gdn_scan_prefill(desc, q, k, v, alpha, beta, s_init, o, s_final, ws, stream=
         _ptr(s_init, "s_init", torch.float32, st, optional=True),
         _ptr(o, "o", torch.float32, BL * H * D),
         _ptr(s_final, "s_final", torch.float32, st, optional=True), wp, wn, _stream(stream)))
+
+
+def gdn_scan_backward(desc, q, k, v, alpha, beta, s_init, d_o, d_sfinal, dq, dk, dv, dalpha, dbeta, ds_init, ws,
+                      stream=None):
+    a, BL, H, D = desc.act_dtype, desc.B * desc.L, desc.H, desc.dk
+    st = desc.B * H * D * D
+    f = torch.float32
+    wp, wn = _ws(ws)
+    _check(load().gdn_scan_backward(
+        ctypes.byref(desc), _ptr(q, "q", a, BL * H * D), _ptr(k, "k", a, BL * H * D),
+        _ptr(v, "v", a, BL * H * D), _ptr(alpha, "alpha", f, BL * H), _ptr(beta, "beta", f, BL * H),
+        _ptr(s_init, "s_init", f, st, optional=True), _ptr(d_o, "d_o", f, BL * H * D),
+        _ptr(d_sfinal, "d_sfinal", f, st, optional=True), _ptr(dq, "dq", f, BL * H * D),
+        _ptr(dk, "dk", f, BL * H * D), _ptr(dv, "dv", f, BL * H * D), _ptr(dalpha, "dalpha", f, BL * H),
+        _ptr(dbeta, "dbeta", f, BL * H), _ptr(ds_init, "ds_init", f, st, optional=True), wp, wn, _stream(stream)))
 
 
 def gdn_scan_decode(desc, q, k, v, alpha, beta, states, o, stream=None):

@@ -101,7 +101,8 @@ gdn_status check_prefill_grid(const gdn_desc *d) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, total = 0;
+    size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, sc = 0, dse = 0, bm = 0;
+    size_t total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
 
@@ -118,7 +119,7 @@ Layout layout(const gdn_desc *d, int op) {
         return at;
     };
     const bool proj = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_LOOP_DECODE;
-    const bool chunks = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL;
+    const bool chunks = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD;
     if (proj) {
         lo.q = take(tokens * d->H * D * act_bytes(d));
         lo.k = take(tokens * d->H * D * act_bytes(d));
@@ -135,6 +136,11 @@ Layout layout(const gdn_desc *d, int op) {
         lo.W = take(bh * Nc * D * CHUNK * 4);
         lo.M = take(bh * Nc * CHUNK * CHUNK * 4);
         lo.g = take(bh * Nc * CHUNK * 4);
+    }
+    if (op == GDN_OP_SCAN_BACKWARD) {   // chunk-start states and the gradient at each chunk's end
+        lo.sc = take(bh * Nc * D * D * 4);
+        lo.dse = take(bh * Nc * D * D * 4);
+        lo.bm = take(bwd_mats_bytes(bh * Nc));
     }
     lo.total = off;
     return lo;
@@ -156,7 +162,7 @@ struct gdn_timer {
 
 namespace {
 
-constexpr int N_STAGES = GDN_STAGE_GATES + 1;
+constexpr int N_STAGES = GDN_STAGE_BWD_PREP + 1;
 thread_local LaunchEvents t_launch_events{nullptr, nullptr};
 gdn_timer *g_timers[N_STAGES] = {};
 
@@ -232,12 +238,15 @@ gdn_status gdn_weights_pack(const gdn_desc *desc, const void *Wq, const void *Wk
 }
 
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes) {
-    if (op < GDN_OP_LOOP_PREFILL || op > GDN_OP_PROJECT)
+    if (op < GDN_OP_LOOP_PREFILL || op > GDN_OP_SCAN_BACKWARD)
         return fail(GDN_ERR_UNSUPPORTED, "unknown op %d", op);
     gdn_status st = check_desc(desc, op == GDN_OP_LOOP_DECODE || op == GDN_OP_SCAN_DECODE);
     if (st != GDN_OK) return st;
-    if ((op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL) && (st = check_prefill_grid(desc)) != GDN_OK)
+    if ((op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD) &&
+        (st = check_prefill_grid(desc)) != GDN_OK)
         return st;
+    if (op == GDN_OP_SCAN_BACKWARD && desc->act == GDN_F32 && desc->dk == 128)
+        return fail(GDN_ERR_UNSUPPORTED, "the backward pass takes fp32 inputs with dk = 64 only");
     if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
     *bytes = layout(desc, op).total;
     return GDN_OK;
@@ -309,6 +318,48 @@ gdn_status gdn_scan_prefill(const gdn_desc *desc, const void *q, const void *k, 
     return scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo, nullptr, nullptr}, s_init,
                        s_final, out,
                        ws, lo, (hipStream_t)stream);
+}
+
+gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, const float *s_init, const float *d_o,
+                             const float *d_sfinal, float *dq, float *dk, float *dv, float *dalpha, float *dbeta,
+                             float *ds_init, void *ws, size_t ws_bytes, void *stream) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
+    if (desc->act == GDN_F32 && desc->dk == 128)
+        return fail(GDN_ERR_UNSUPPORTED, "the backward pass takes fp32 inputs with dk = 64 only");
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(alpha); REQUIRE_PTR(beta); REQUIRE_PTR(d_o);
+    REQUIRE_PTR(dq); REQUIRE_PTR(dk); REQUIRE_PTR(dv); REQUIRE_PTR(dalpha); REQUIRE_PTR(dbeta);
+    OPTIONAL_PTR(s_init); OPTIONAL_PTR(d_sfinal); OPTIONAL_PTR(ds_init);
+    const Layout lo = layout(desc, GDN_OP_SCAN_BACKWARD);
+    if (!ws || ws_bytes < lo.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
+    if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+    const hipStream_t s = (hipStream_t)stream;
+    const bool f32 = desc->act == GDN_F32;
+    const int B = desc->B, L = desc->L, H = desc->H, D = desc->dk;
+    // forward recomputation: the chunk matrices, then the state chain with the chunk-start states kept
+    float *sc = (float *)at(ws, lo.sc), *dse = (float *)at(ws, lo.dse);
+    CarryOut out{nullptr, nullptr, false, nullptr, nullptr, nullptr, sc};
+    st = scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo, nullptr, nullptr}, s_init,
+                     nullptr, out, ws, lo, s);
+    if (st != GDN_OK) return st;
+    float *bm = (float *)at(ws, lo.bm);
+    hipError_t e = timed(GDN_STAGE_BWD_PREP, s, [&] {
+        return launch_bwd_prep(f32, B, L, H, D, q, k, alpha, beta, bm, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+    e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
+        return launch_bwd_carry(f32, B, L, H, D, q, k, beta, d_o, d_sfinal, bm, dv, dse, ds_init, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "backward carry launch");
+    e = timed(GDN_STAGE_BWD_CHUNK, s, [&] {
+        return launch_bwd_chunk(f32, B, L, H, D, q, k, v, alpha, beta, d_o, dv, sc, dse, bm, dq, dk, dalpha, dbeta,
+                                s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "backward chunk launch");
+    return GDN_OK;
 }
 
 gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k, const void *v,
@@ -421,7 +472,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_GATES || stage == 4 || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BWD_PREP || stage == 4 || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

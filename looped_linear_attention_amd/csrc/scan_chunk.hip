@@ -781,7 +781,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc,
     const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
     float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
-    float *h_out, bf16 *x_next) {
+    float *h_out, bf16 *x_next, float *__restrict__ s_chunks) {
     using G = CarryCfg<D, TIn>;
     constexpr int NT = G::NT, RW = G::RW, KW = G::KW, STG = G::STG;
     // every stage is an object of its own, so the compiler can tell the buffers
@@ -911,7 +911,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 const float ov = gv[j] * qs[j] + me[j];
                 const int64_t row = tokb + c0 + r;
                 if constexpr (RES == 0) {
-                    o[(row * H + h) * D + col] = ov;
+                    if (o) o[(row * H + h) * D + col] = ov;
                 } else {
                     const float hv = ov + rho_c * in.hp[j];
                     const int64_t hi = row * d + (int64_t)h * D + col;
@@ -997,6 +997,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 
     // One chunk step on LDS stage ST (= cc mod 2 with two stages).  Two steps per
     // loop iteration so that stage and parity are compile-time constants.
+    int ccs = 0;   // chunk of the step
     auto step = [&](auto pc) __attribute__((always_inline)) {
         constexpr int P = decltype(pc)::value;
         constexpr int ST = STG == 2 ? P : 0;
@@ -1005,6 +1006,14 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         const float *g_cur = ST == 0 ? g0_s : g1_s;
         const bf16x8 *w_cur = reinterpret_cast<const bf16x8 *>(ST == 0 ? w0_s : w1_s) + wave * NT * 4 * 64 + lane;
         lds_barrier();   // (B0) chunk cc's loads have landed; chunk cc-1's stage is free
+        if (s_chunks) {   // chunk-start states for the backward pass
+            float *dst = s_chunks + (cidb + ccs) * D * D;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[(int64_t)(RW * wave + 4 * NT * lg + 4 * tt + j) * D + col] = Sv[tt][j];
+        }
+        ++ccs;
         // chunk-start state as the B operand of K.S (and, in LDS, of Q.S for the output waves)
         __bf16 sh[KW], sl[KW];
         {
@@ -1161,7 +1170,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v, int L, int H, int Nc,
     const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
     float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
-    float *h_out, bf16 *x_next) {
+    float *h_out, bf16 *x_next, float *__restrict__ s_chunks) {
     using G = CarryW;
     using KT = KTile<128, bf16>;
     constexpr int D = G::D;
@@ -1282,12 +1291,21 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
         wait_vmcnt<0>();
         const bf16x8 *wf0 = reinterpret_cast<const bf16x8 *>(w0_s) + rh * 16 * 64 + lane;
         const bf16x8 *wf1 = reinterpret_cast<const bf16x8 *>(w1_s) + rh * 16 * 64 + lane;
+        int ccs = 0;   // chunk of the step
         auto step = [&](auto stc) __attribute__((always_inline)) {
             constexpr int ST = decltype(stc)::value;
             const bf16 *v_cur = reinterpret_cast<const bf16 *>(ST == 0 ? v0_s : v1_s);
             const float *g_cur = ST == 0 ? g0_s : g1_s;
             const bf16x8 *w_cur = ST == 0 ? wf0 : wf1;
             lds_barrier();   // B0
+            if (s_chunks) {   // chunk-start states for the backward pass
+                float *dst = s_chunks + (cidb + ccs) * D * D;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dst[(int64_t)srow(tt, j) * D + col] = Sv[tt][j];
+            }
+            ++ccs;
             // S_c as the B operand of K.S, local k-step kl = rows 64 rh + 32 kl ..; also into LDS for Q.S_c
             bf16x8 sh[2], sl[2];
 #pragma unroll
@@ -1494,7 +1512,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
                 const float ov = gv[j] * qs[j] + mev[j];
                 const int64_t row = tokb + c0 + r;
                 if constexpr (RES == 0) {
-                    o[(row * H + h) * D + col] = ov;
+                    if (o) o[(row * H + h) * D + col] = ov;
                 } else {
                     const float hv = ov + rho_c[ct] * hp[ct][j];
                     const int64_t hi = row * d + (int64_t)h * D + col;
@@ -1561,7 +1579,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
 #define CARRYW(R, X)                                                                               \
     launch_kernel((k_scan_carry_w<R, X>), gridw, dim3(CARRY_THREADS), 0, s, (const bf16 *)q, (const bf16 *)k, \
                   (const bf16 *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
-                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next)
+                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks)
         if (res == 0) CARRYW(0, false);
         else if (res == 1) { if (xn) CARRYW(1, true); else CARRYW(1, false); }
         else { if (xn) CARRYW(2, true); else CARRYW(2, false); }
@@ -1572,7 +1590,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
 #define CARRY(DD, T, R, X)                                                                         \
     launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(CARRY_THREADS), 0, s, (const T *)q, (const T *)k, \
                   (const T *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
-                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next)
+                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks)
 #define CARRY_R(DD, T)                                                                             \
     do {                                                                                           \
         if (res == 0) CARRY(DD, T, 0, false);                                                      \

@@ -30,7 +30,7 @@ import torch
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "prefill_inputs", "scan_inputs",
-    "decode_state_init", "decode_step_inputs", "unit_rows",
+    "decode_state_init", "decode_step_inputs", "unit_rows", "grad_inputs",
 ]
 
 
@@ -182,3 +182,13 @@ def decode_step_inputs(w: Workload, steps: Optional[int] = None) -> Iterator[dic
             yield dict(step=s, tau=tau, q=_to_act(q, "bf16"), k=_to_act(k, "bf16"),
                        v=_to_act(v, "bf16"), alpha=torch.from_numpy(alpha),
                        beta=torch.from_numpy(beta))
+
+
+def grad_inputs(seed: int, B: int, L: int, H: int, dk: int, dv: int, with_state_grad: bool = True) -> dict:
+    """Incoming gradients for a backward pass, drawn in this order: d_o ~ N(0,1) [B,L,H,dv]; optionally
+    d_sfinal ~ N(0,1) [B,H,dk,dv]; both fp32 (the loss is taken as <d_o, o> + <d_sfinal, S_final>)."""
+    rng = np.random.default_rng(seed)
+    out = dict(d_o=torch.from_numpy(rng.standard_normal((B, L, H, dv), dtype=np.float32)))
+    if with_state_grad:
+        out["d_sfinal"] = torch.from_numpy(rng.standard_normal((B, H, dk, dv), dtype=np.float32))
+    return out

@@ -120,6 +120,15 @@ def test_workspace_sizes():
         assert _ws_status(desc) == (0, exp)
     st, n = _ws_status(gl.make_desc(64, 1, 16, 128, 128), gl.GDN_OP_SCAN_DECODE)
     assert st == 0 and n == 0
+    # backward: the chunk matrices plus the chunk-start states and the state gradients at chunk ends
+    B, L, H, D = 2, 130, 3, 128
+    Nc = (L + 63) // 64
+    chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+    mats = B * H * Nc * (3 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4)   # fp32 T, P, A; fp64 log-cumsum; gamma, c
+    assert _ws_status(gl.make_desc(B, L, H, D, D), gl.GDN_OP_SCAN_BACKWARD) == (
+        0, chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats))
+    st, _ = _ws_status(gl.make_desc(B, L, H, D, D, act=gl.GDN_F32), gl.GDN_OP_SCAN_BACKWARD)
+    assert st == -3   # fp32 inputs with 128-wide heads
 
 
 @pytest.mark.parametrize("op", [gl.GDN_OP_LOOP_PREFILL, gl.GDN_OP_LOOP_DECODE])
