@@ -20,10 +20,11 @@ Printed (one JSON line on stdout):
   decode          batched decode, 64 sequences x 256 generated tokens, 4 loop states each (the state step
                   alone; HBM-bound);
   loop_decode     the same 64 sequences through whole loops (projection, state step and residual per loop);
+  scan_backward   gradients of one scan pass at the 4096-token prompt's shape (gdn_scan_backward);
   cpu_baseline    the oracle on a bounded sample of the headline workload, on the host's cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode]
-                       [--no-cpu-baseline]
+                       [--no-backward] [--no-cpu-baseline]
        python bench.py --calib-copy          (plain 256 MiB device copy, for HBM counter calibration)
 Only one GPU is used: --gpus N with N > 1 exits with a message.
 """
@@ -44,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "looped-GDN prefill tokens/s (×T=4) and decode tokens/s; % MFMA / HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["proj_gemm.hip", "scan_chunk.hip", "decode.hip", "gdn_device.h"]
 
@@ -297,6 +299,70 @@ def bench_loop_decode(args, torch, gl, synth, dw):
                          "frac": tok_s / roof}}
 
 
+def bwd_kernel_flops_per_chunk(D, C=64) -> int:
+    """fp32 flops k_bwd_chunk performs per (b, h, chunk): per 16-column block K S, Q S, K dS' (3 C 16 D),
+    U = T diag(beta) E and P^T dO (2 C C 16), the dP and dTb sums (2 C C 16), the dQ and dK sums (3 C D 16);
+    then T^T dT, dN (2 C^3) and the four (Gam (.) dP / dA) products with K or Q (4 C C D); 2 flops a MAC."""
+    blocks = D // 16
+    per_block = 3 * C * 16 * D + 2 * C * C * 16 + 2 * C * C * 16 + 3 * C * D * 16
+    return 2 * (blocks * per_block + 2 * C ** 3 + 4 * C * C * D)
+
+
+def bench_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
+    """gdn_scan_backward on one scan pass of a prompt workload's shape (q/k/v of unit norm, alpha in
+    (alpha_lo, 1), beta in (0, 1), carried initial state, incoming gradients for o and the final state)."""
+    w = synth.workload(name)
+    B, L, H, D = w.B, w.L, w.H, w.dk
+    dev = lambda t: t.contiguous().to("cuda")
+    x = synth.scan_inputs(90, B, L, H, D, D, act=w.act, alpha_range=(max(w.alpha_lo, 0.05), 1.0), with_state=True)
+    g = synth.grad_inputs(91, B, L, H, D, D)
+    desc = gl.make_desc(B, L, H, D, D, T=1, act=w.act)
+    ws = gl.workspace(desc, gl.GDN_OP_SCAN_BACKWARD)
+    ins = [dev(x[k]) for k in ("q", "k", "v", "alpha", "beta", "s_init")] + [dev(g["d_o"]), dev(g["d_sfinal"])]
+    outs = [torch.empty(B, L, H, D, device="cuda") for _ in range(3)] + \
+           [torch.empty(B, L, H, device="cuda") for _ in range(2)] + [torch.empty(B, H, D, D, device="cuda")]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gl.gdn_scan_backward(desc, *ins, *outs, ws, stream)
+
+    for _ in range(max(args.warmup, 5)):
+        call()
+    torch.cuda.synchronize()
+    n = max(args.steps, 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    stages = {"fwd_prep": gl.GDN_STAGE_SCAN_PREP, "fwd_carry": gl.GDN_STAGE_SCAN_CARRY,
+              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
+              "bwd_chunk": gl.GDN_STAGE_BWD_CHUNK}
+    timers = {k: gl.gdn_timer_create(v, n) for k, v in stages.items()}
+    for t in timers.values():
+        gl.gdn_timer_attach(t)
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    gl.gdn_timer_detach()
+    per = {}
+    for k, t in timers.items():
+        cnt, tot = gl.gdn_timer_read(t)
+        per[k] = tot / max(cnt, 1)
+        gl.gdn_timer_destroy(t)
+    Nc = (L + 63) // 64
+    fl = bwd_kernel_flops_per_chunk(D) * B * H * Nc
+    ach = fl / (per["bwd_chunk"] * 1e-3) / 1e12
+    return {"workload": f"scan backward, {name} shape (B={B}, L={L}, H={H}, dk=dv={D}, {w.act} inputs)",
+            "value": B * L / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+            "stages_us": {k: v * 1e3 for k, v in per.items()},
+            "roofline": {"bound": "alu", "kernel": "k_bwd_chunk", "achieved": ach, "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32_TFLOPS, "flops_per_launch": fl,
+                         "avg_launch_us": per["bwd_chunk"] * 1e3}}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -389,6 +455,7 @@ def main():
                     help="comma-separated further prefill workloads reported under extra_workloads ('' for none)")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
@@ -436,6 +503,9 @@ def main():
         extras[name] = prefill_record(we, bench_prefill(args, we, torch, gl, synth, max(args.warmup, 20)))
     if extras:
         out["extra_workloads"] = extras
+    if not args.no_backward:
+        log("scan backward: the 4096-token prompt's shape ...")
+        out["scan_backward"] = bench_backward(args, torch, gl, synth)
     if not args.no_decode:
         out["decode"] = bench_decode(args, torch, gl, synth)
         log("loop decode: 64 sequences with projections ...")

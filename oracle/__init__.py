@@ -53,7 +53,7 @@ _lib = None
 
 __all__ = [
     "build", "num_threads", "round_bf16", "round_f32", "scan", "scan_backward", "project",
-    "loop_prefill", "loop_decode_step", "scan_chunkwise",
+    "loop_prefill", "loop_prefill_act", "loop_decode_step", "scan_chunkwise",
 ]
 
 
@@ -240,6 +240,48 @@ def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
             states.append(s)
     return dict(h=h, loops=loops if keep_loops else None,
                 states=states if keep_states else None)
+
+
+def loop_prefill_act(h0, Wq, Wk, Wv, wa, wb, rho, w_halt, b_halt: float, eps: float, H: int, dk: int, dv: int,
+                     alpha_lo: float, act: str, norm_eps: float = 1e-6, keep_loops: bool = False):
+    """T weight-tied loops with per-token adaptive halting (LT2 Appendix A, adaptive computation time).
+
+    As ``loop_prefill``, except that after each loop tau every position t that is still running draws a
+    halting probability p_t = sigmoid(w_halt . h_t^(tau) + b_halt) and adds it to its running sum R_t; once
+    R_t >= 1 - eps the position halts: its hidden state is frozen at h_t^(tau) and takes no further update.
+    Every position is still projected and scanned in later loops (its frozen state remains context for the
+    positions after it); only the residual update h = o + rho (.) h is withheld from halted positions.
+
+    The halting decision is an integer decided by floating point; it is taken here as the library takes it,
+    in fp32: the dot product w_halt . h_t is summed in fp32 (numpy, from the fp32 value of h), the sigmoid
+    and the running sum in fp32.  Returns dict(h [B,L,d] fp64, halt_loop [B,L] int (tau_t, or T if the sum
+    never reached the threshold), ponder [B,L] fp32 (R_t), loops [h^(1..T)] or None).
+    """
+    h = _f64(h0)
+    rho = _f64(rho)
+    B, L, d = h.shape
+    T = rho.shape[0]
+    w32 = np.asarray(_f64(w_halt), dtype=np.float32)
+    R = np.zeros((B, L), dtype=np.float32)
+    halt = np.zeros((B, L), dtype=np.int64)          # loop after which the position halted (0: running)
+    loops = []
+    thr = np.float32(1.0) - np.float32(eps)
+    for tau in range(T):
+        x = round_bf16(h) if act == "bf16" else h
+        q, k, v, al, be = project(x.reshape(B * L, d), Wq, Wk, Wv, wa, wb, H, dk, dv, alpha_lo, act, norm_eps)
+        o, _ = scan(q.reshape(B, L, H, dk), k.reshape(B, L, H, dk), v.reshape(B, L, H, dv),
+                    al.reshape(B, L, H), be.reshape(B, L, H), None, want_state=False)
+        running = halt == 0
+        h = np.where(running[..., None], o.reshape(B, L, d) + rho[tau][None, None, :] * h, h)
+        if keep_loops:
+            loops.append(h.copy())
+        z = (h.astype(np.float32) @ w32) + np.float32(b_halt)
+        p = (np.float32(1.0) / (np.float32(1.0) + np.exp(-z, dtype=np.float32))).astype(np.float32)
+        R = np.where(running, (R + p).astype(np.float32), R)
+        newly = running & (R >= thr)
+        halt = np.where(newly, tau + 1, halt)
+    halt_loop = np.where(halt == 0, T, halt)
+    return dict(h=h, halt_loop=halt_loop, ponder=R, loops=loops if keep_loops else None)
 
 
 def loop_decode_step(h_t, Wq, Wk, Wv, wa, wb, rho, states, H: int, dk: int, dv: int,

@@ -440,3 +440,56 @@ def test_scan_backward_split_chain_rule():
     for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
         assert np.allclose(np.concatenate([g1[key], g2[key]], 1), g[key], rtol=1e-11, atol=1e-12), key
     assert np.allclose(g1["ds_init"], g["ds_init"], rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# adaptive halting (ACT) in the loop driver
+# ---------------------------------------------------------------------------
+def _act_inputs(seed, B=2, L=40, H=2, D=8):
+    x, s = _tiny_loop_inputs(seed, B=B, L=L, H=H, dk=D, dv=D, T=4)
+    rng = np.random.default_rng(seed + 100)
+    w = rng.standard_normal(H * D) / np.sqrt(H * D)
+    return x, s, w
+
+
+def test_act_extremes_equal_plain_loops():
+    """b = +inf: every position halts after loop 1 (h = h^(1)); b = -inf: none halts (the plain T loops)."""
+    x, s, w = _act_inputs(41)
+    plain = oracle.loop_prefill(**x, **s, alpha_lo=0.0, act="f32", keep_loops=True)
+    r = oracle.loop_prefill_act(**x, w_halt=w, b_halt=60.0, eps=0.01, **s, alpha_lo=0.0, act="f32")
+    assert np.array_equal(r["h"], plain["loops"][0]) and np.all(r["halt_loop"] == 1)
+    r = oracle.loop_prefill_act(**x, w_halt=w, b_halt=-60.0, eps=0.01, **s, alpha_lo=0.0, act="f32")
+    assert np.array_equal(r["h"], plain["h"]) and np.all(r["halt_loop"] == x["rho"].shape[0])
+
+
+@pytest.mark.parametrize("pval,tau", [(0.5, 2), (0.3, 4), (0.995, 1)])
+def test_act_constant_probability_halts_at_the_threshold_loop(pval, tau):
+    """w = 0 gives every position p = sigmoid(b): the running sum first reaches 1 - 0.01 after
+    ceil(0.99 / p) loops (0.5 -> 2, 0.3 -> 4, 0.995 -> 1), and h equals that loop's h of the plain run."""
+    x, s, w = _act_inputs(42)
+    b = float(np.log(pval / (1 - pval)))
+    plain = oracle.loop_prefill(**x, **s, alpha_lo=0.0, act="f32", keep_loops=True)
+    r = oracle.loop_prefill_act(**x, w_halt=np.zeros_like(w), b_halt=b, eps=0.01, **s, alpha_lo=0.0, act="f32")
+    assert np.all(r["halt_loop"] == tau)
+    assert np.array_equal(r["h"], plain["loops"][tau - 1])
+    assert np.allclose(r["ponder"], tau * pval, rtol=1e-6)
+
+
+def test_act_frozen_position_is_context_but_not_updated():
+    """Only the last position can halt (its halting logit is raised by a large feature only it carries):
+    every earlier position is causally unaffected and equals the plain loop, and the last position stays at
+    its h^(tau_t) of the plain loop once halted."""
+    x, s, w = _act_inputs(43, B=1, L=30)
+    h0 = x["h0"].copy()
+    h0[0, -1, 0] = 1000.0                     # a feature only the last position carries,
+    x["h0"] = h0
+    x["rho"] = x["rho"].copy()
+    x["rho"][:, 0] = 0.5                      # kept by the residual gate of every loop
+    w = np.zeros_like(w)
+    w[0] = 1.0                                # logit = h[0] + b: very large only for the last position
+    plain = oracle.loop_prefill(**x, **s, alpha_lo=0.0, act="f32", keep_loops=True)
+    r = oracle.loop_prefill_act(**x, w_halt=w, b_halt=-20.0, eps=0.01, **s, alpha_lo=0.0, act="f32",
+                                keep_loops=True)
+    assert r["halt_loop"][0, -1] == 1 and np.all(r["halt_loop"][0, :-1] == x["rho"].shape[0])
+    assert np.array_equal(r["h"][0, :-1], plain["h"][0, :-1])
+    assert np.array_equal(r["h"][0, -1], plain["loops"][0][0, -1])
