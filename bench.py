@@ -20,11 +20,13 @@ Printed (one JSON line on stdout):
   decode          batched decode, 64 sequences x 256 generated tokens, 4 loop states each (the state step
                   alone; HBM-bound);
   loop_decode     the same 64 sequences through whole loops (projection, state step and residual per loop);
+  act             the headline workload through gdn_loop_prefill_act (per-token adaptive halting): rate,
+                  halting loops, share of position-loops projected;
   scan_backward   gradients of one scan pass at the 4096-token prompt's shape (gdn_scan_backward);
   cpu_baseline    the oracle on a bounded sample of the headline workload, on the host's cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode]
-                       [--no-backward] [--no-cpu-baseline]
+                       [--no-act] [--no-backward] [--no-cpu-baseline]
        python bench.py --calib-copy          (plain 256 MiB device copy, for HBM counter calibration)
 Only one GPU is used: --gpus N with N > 1 exits with a message.
 """
@@ -363,6 +365,50 @@ def bench_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
                          "avg_launch_us": per["bwd_chunk"] * 1e3}}
 
 
+def bench_act(args, torch, gl, synth, w):
+    """gdn_loop_prefill_act on the headline prompt workload: the looped mixer with per-token adaptive halting
+    (halting layer from synth.act_inputs).  Reports the throughput, the halting loops and the share of
+    position-loops whose projection ran (only positions that ran the previous loop are projected again)."""
+    dev = lambda t: t.contiguous().to("cuda")
+    x = synth.prefill_inputs(w)
+    a = synth.act_inputs(w)
+    desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = torch.empty(gl.gdn_weights_packed_bytes(desc) // (4 if w.act == "f32" else 2),
+                     dtype=desc.act_dtype, device="cuda")
+    gl.gdn_weights_pack(desc, dev(x["Wq"]), dev(x["Wk"]), dev(x["Wv"]), dev(x["wa"]), dev(x["wb"]), Wp)
+    h0, rho, wh = dev(x["h0"]), dev(x["rho"]), dev(a["w_halt"])
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL_ACT)
+    h_out = torch.empty(w.B, w.L, w.d, device="cuda")
+    hl = torch.empty(w.B, w.L, dtype=torch.int32, device="cuda")
+    pd = torch.empty(w.B, w.L, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gl.gdn_loop_prefill_act(desc, h0, Wp, rho, wh, a["b_halt"], a["eps"], h_out, hl, pd, ws, stream)
+
+    for _ in range(max(args.warmup, 5)):
+        call()
+    torch.cuda.synchronize()
+    n = max(args.steps, 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    loops = hl.cpu().numpy().ravel()
+    counts = [int((loops == t).sum()) for t in range(1, w.T + 1)]
+    M = w.B * w.L
+    # loop 1 projects every position; loop t > 1 those that ran loop t - 1 (not halted before it)
+    projected = M + sum(int((loops >= t - 1).sum()) for t in range(2, w.T + 1))
+    return {"workload": f"{w.name} with adaptive halting (w_halt ~ N(0, 1/d), b_halt {a['b_halt']}, "
+                        f"eps {a['eps']})",
+            "value": M / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+            "halting_loop_counts": counts, "mean_loops": float(loops.mean()),
+            "projected_share": projected / (M * w.T)}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -456,6 +502,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-act", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
@@ -503,6 +550,9 @@ def main():
         extras[name] = prefill_record(we, bench_prefill(args, we, torch, gl, synth, max(args.warmup, 20)))
     if extras:
         out["extra_workloads"] = extras
+    if not args.no_act:
+        log(f"adaptive halting: {w.name} ...")
+        out["act"] = bench_act(args, torch, gl, synth, w)
     if not args.no_backward:
         log("scan backward: the 4096-token prompt's shape ...")
         out["scan_backward"] = bench_backward(args, torch, gl, synth)

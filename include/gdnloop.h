@@ -101,7 +101,8 @@ gdn_status gdn_weights_pack(const gdn_desc *desc, const void *Wq, const void *Wk
 /* ---- workspace ---------------------------------------------------------- */
 
 enum { GDN_OP_LOOP_PREFILL = 0, GDN_OP_LOOP_DECODE = 1, GDN_OP_SCAN_PREFILL = 2,
-       GDN_OP_SCAN_DECODE = 3, GDN_OP_PROJECT = 4, GDN_OP_SCAN_BACKWARD = 5 };
+       GDN_OP_SCAN_DECODE = 3, GDN_OP_PROJECT = 4, GDN_OP_SCAN_BACKWARD = 5,
+       GDN_OP_LOOP_PREFILL_ACT = 6 };
 
 /* Device scratch bytes that operation `op` needs for `desc` (0 is valid). */
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes);
@@ -120,7 +121,7 @@ gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes);
  * GDN_OP_LOOP_DECODE; *offset is the region's byte offset from the start of
  * the workspace and *bytes its length.  Errors: GDN_ERR_UNSUPPORTED for
  * another op or an unknown region, the usual descriptor errors, GDN_ERR_NULL
- * for a NULL output pointer. */
+ * for a NULL output pointer.  GDN_OP_LOOP_PREFILL_ACT has the same regions. */
 enum { GDN_WS_Q = 0, GDN_WS_K = 1, GDN_WS_V = 2, GDN_WS_ALPHA = 3, GDN_WS_BETA = 4 };
 gdn_status gdn_workspace_region(const gdn_desc *desc, int op, int region, size_t *offset,
                                 size_t *bytes);
@@ -217,6 +218,29 @@ gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k,
 gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wpack,
                             const float *rho, float *h_out, float *states_out,
                             float *h_loops, void *ws, size_t ws_bytes, void *stream);
+
+/* T loops with per-token adaptive halting (ACT).
+ * Passage: LT2 Appendix A: after loop tau a linear layer with a sigmoid gives
+ * each position a halting probability p_t = sigmoid(w_halt . h_t^(tau) +
+ * b_halt); the probabilities accumulate over the loops, and once the running
+ * sum reaches 1 - eps (the pages use eps = 0.01) the position halts: its
+ * hidden state is frozen at h_t^(tau) and takes no further update.  Reading
+ * of the pages for this mixer: every position is still projected and scanned
+ * in every loop (a halted position's frozen state stays context for the
+ * positions after it); only the residual update is withheld.  The halting
+ * decision is taken in fp32.
+ *   h0, Wpack, rho               as for gdn_loop_prefill
+ *   w_halt [d]                   device fp32; b_halt, eps host floats (0 <= eps < 1)
+ *   h_out [B, L, d]              device fp32, written: each position's final state
+ *   halt_loop [B, L]             device int32 or NULL: the loop after which the
+ *                                position halted (T if it never did)
+ *   ponder [B, L]                device fp32 or NULL: the running sum of p
+ *   ws, ws_bytes                 gdn_workspace_bytes(GDN_OP_LOOP_PREFILL_ACT)
+ * h_out may not alias h0. */
+gdn_status gdn_loop_prefill_act(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,
+                                const float *w_halt, float b_halt, float eps, float *h_out,
+                                int32_t *halt_loop, float *ponder, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /* One generated token per sequence through the T loops (decode).
  * Passage: as gdn_loop_prefill, for one new token per sequence; each loop

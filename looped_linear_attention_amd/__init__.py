@@ -21,19 +21,20 @@ import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
-    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
+    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_OP_LOOP_PREFILL_ACT", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
     "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES", "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_PREP",
     "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
     "GDN_WS_ALPHA", "GDN_WS_BETA", "GdnError", "gdn_desc", "make_desc", "lib_path",
     "load", "EXPORTED", "workspace", "workspace_view", "gdn_workspace_region",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
+    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act", "gdn_loop_decode", "gdn_loop_decode_noalloc",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
-GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT, GDN_OP_SCAN_BACKWARD = range(6)
+(GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT, GDN_OP_SCAN_BACKWARD,
+ GDN_OP_LOOP_PREFILL_ACT) = range(7)
 GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_GATES = 0, 1, 2, 3, 5
 GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_PREP = 6, 7, 8
 GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
@@ -41,7 +42,7 @@ GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_decode", "gdn_loop_decode_noalloc",
+    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act", "gdn_loop_decode", "gdn_loop_decode_noalloc",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
@@ -97,6 +98,7 @@ def load():
         "gdn_scan_backward": [D] + [P] * 15 + [S, P],
         "gdn_loop_prefill": [D, P, P, P, P, P, P, P, S, P],
         "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
+        "gdn_loop_prefill_act": [D, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, P, P, S, P],
         "gdn_loop_decode_noalloc": [D, P, P, P, P, P, P],
         "gdn_timer_create": [I, I, ctypes.POINTER(P)],
         "gdn_timer_set_stride": [P, I],
@@ -281,6 +283,18 @@ def gdn_loop_prefill(desc, h0, Wpack, rho, h_out, states_out, h_loops, ws, strea
              optional=True),
         _ptr(h_loops, "h_loops", torch.float32, T * BL * d, optional=True), wp, wn,
         _stream(stream)))
+
+
+def gdn_loop_prefill_act(desc, h0, Wpack, rho, w_halt, b_halt, eps, h_out, halt_loop, ponder, ws, stream=None):
+    a, BL, d, T = desc.act_dtype, desc.B * desc.L, desc.d, desc.T
+    pb = gdn_weights_packed_bytes(desc)
+    wp, wn = _ws(ws)
+    _check(load().gdn_loop_prefill_act(
+        ctypes.byref(desc), _ptr(h0, "h0", a, BL * d),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)),
+        _ptr(rho, "rho", torch.float32, T * d), _ptr(w_halt, "w_halt", torch.float32, d), float(b_halt), float(eps),
+        _ptr(h_out, "h_out", torch.float32, BL * d), _ptr(halt_loop, "halt_loop", torch.int32, BL, optional=True),
+        _ptr(ponder, "ponder", torch.float32, BL, optional=True), wp, wn, _stream(stream)))
 
 
 def gdn_loop_decode(desc, h_t, Wpack, rho, states, h_out, ws, stream=None):

@@ -51,9 +51,13 @@ hipError_t launch_pack_weights(bool f32, int d, int H, int D, const void *Wq, co
 // sums and turns into alpha and beta.
 bool project_separate_gates(bool f32, int M);
 int gate_partials(bool f32, int M, int d, int H);
+// With rows != nullptr (bf16 wide projection with gate partials only) only the
+// tokens rows[0 .. *rows_count) are projected (count read on the device); the
+// other tokens' q, k, v and gate partials stay as they are.
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
-                          float eps, float *zp, hipStream_t s);
+                          float eps, float *zp, hipStream_t s, const int *rows = nullptr,
+                          const int *rows_count = nullptr);
 hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
                         float *beta, float alpha_lo, hipStream_t s);
 
@@ -89,7 +93,20 @@ struct CarryOut {
     float *h_out;          // [B, L, H*D]
     bf16 *x_next;          // [B, L, H*D] or nullptr
     float *s_chunks;       // [B, H, Nc, D, D] chunk-start states, or nullptr
+    const int *halted;     // [B * L]: nonzero marks a halted position (no residual update), or nullptr
 };
+
+// Adaptive halting of the loop driver: R (running halting sums) and halt
+// (the loop after which a position halted, 0 while it runs) start at zero;
+// after loop tau every running position adds p = sigmoid(w . h + b) (fp32) to
+// R and halts (halt = tau) once R >= thr.  After loop T the outputs get the
+// halting loop (T for positions that never halted) and R.
+hipError_t launch_act_init(int M, float *R, int *halt, hipStream_t s);
+hipError_t launch_act_halt(int M, int d, const float *h, const float *w, float b, float thr, int tau, int T, float *R,
+                           int *halt, int *halt_out, float *ponder_out, hipStream_t s);
+// The positions that ran loop tau (halt 0 or tau), in ascending order, and
+// their count: the rows whose projection input changed for loop tau + 1.
+hipError_t launch_act_rows(int M, const int *halt, int tau, int *rows, int *count, hipStream_t s);
 // Carry: sequential over chunks per (b, h, 16-column slice of S); the chain
 // updates the state, output waves of the same workgroup form
 // O = diag(gamma) Q S_c + M E a chunk behind and write `out`; final state to

@@ -102,7 +102,7 @@ gdn_status check_prefill_grid(const gdn_desc *d) {
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
     size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, sc = 0, dse = 0, bm = 0;
-    size_t total = 0;
+    size_t R = 0, halt = 0, rows = 0, rows_count = 0, total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
 
@@ -118,6 +118,8 @@ Layout layout(const gdn_desc *d, int op) {
         off += align_up(bytes);
         return at;
     };
+    const bool act = op == GDN_OP_LOOP_PREFILL_ACT;
+    if (act) op = GDN_OP_LOOP_PREFILL;   // the loop prefill's regions, then the halting state
     const bool proj = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_LOOP_DECODE;
     const bool chunks = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD;
     if (proj) {
@@ -141,6 +143,12 @@ Layout layout(const gdn_desc *d, int op) {
         lo.sc = take(bh * Nc * D * D * 4);
         lo.dse = take(bh * Nc * D * D * 4);
         lo.bm = take(bwd_mats_bytes(bh * Nc));
+    }
+    if (act) {
+        lo.R = take(tokens * 4);
+        lo.halt = take(tokens * 4);
+        lo.rows = take(tokens * 4);   // positions re-projected in the next loop, and their count
+        lo.rows_count = take(4);
     }
     lo.total = off;
     return lo;
@@ -184,9 +192,10 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
 // The projection of M tokens: the GEMM launch, plus the gate launch when the
 // GEMM leaves the gates to it and does not write gate partials (zp).
 hipError_t project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
-                   void *v, float *al, float *be, float alpha_lo, float eps, float *zp, hipStream_t s) {
+                   void *v, float *al, float *be, float alpha_lo, float eps, float *zp, hipStream_t s,
+                   const int *rows = nullptr, const int *rows_count = nullptr) {
     hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
-        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, zp, s);
+        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, zp, s, rows, rows_count);
     });
     if (e == hipSuccess && !zp && project_separate_gates(f32, M))
         e = timed(GDN_STAGE_GATES, s, [&] { return launch_gates(M, d, H, D, x, Wpack, al, be, alpha_lo, s); });
@@ -238,11 +247,12 @@ gdn_status gdn_weights_pack(const gdn_desc *desc, const void *Wq, const void *Wk
 }
 
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes) {
-    if (op < GDN_OP_LOOP_PREFILL || op > GDN_OP_SCAN_BACKWARD)
+    if (op < GDN_OP_LOOP_PREFILL || op > GDN_OP_LOOP_PREFILL_ACT)
         return fail(GDN_ERR_UNSUPPORTED, "unknown op %d", op);
     gdn_status st = check_desc(desc, op == GDN_OP_LOOP_DECODE || op == GDN_OP_SCAN_DECODE);
     if (st != GDN_OK) return st;
-    if ((op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD) &&
+    if ((op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD ||
+         op == GDN_OP_LOOP_PREFILL_ACT) &&
         (st = check_prefill_grid(desc)) != GDN_OK)
         return st;
     if (op == GDN_OP_SCAN_BACKWARD && desc->act == GDN_F32 && desc->dk == 128)
@@ -253,7 +263,7 @@ gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes) {
 }
 
 gdn_status gdn_workspace_region(const gdn_desc *desc, int op, int region, size_t *offset, size_t *bytes) {
-    if (op != GDN_OP_LOOP_PREFILL && op != GDN_OP_LOOP_DECODE)
+    if (op != GDN_OP_LOOP_PREFILL && op != GDN_OP_LOOP_DECODE && op != GDN_OP_LOOP_PREFILL_ACT)
         return fail(GDN_ERR_UNSUPPORTED, "only the looped calls expose workspace regions (op %d)", op);
     gdn_status st = check_desc(desc, op == GDN_OP_LOOP_DECODE);
     if (st != GDN_OK) return st;
@@ -377,6 +387,71 @@ gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k, c
     return e == hipSuccess ? GDN_OK : hip_fail(e, "decode launch");
 }
 
+// The halting of gdn_loop_prefill_act (nullptr for the plain loops).
+struct ActArgs {
+    const float *w;
+    float b, thr;
+    float *R;
+    int *halt;
+    int *rows, *rows_count;   // the positions re-projected in the next loop
+    int32_t *halt_out;
+    float *ponder;
+};
+
+static gdn_status loop_prefill_impl(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,
+                                    float *h_out, float *states_out, float *h_loops, void *ws, const Layout &lo,
+                                    hipStream_t s, const ActArgs *act) {
+    const bool f32 = desc->act == GDN_F32;
+    const int M = desc->B * desc->L, D = desc->dk, d = desc->d;
+    const int64_t tokd = (int64_t)M * d;
+    void *q = at(ws, lo.q), *k = at(ws, lo.k), *v = at(ws, lo.v);
+    float *al = (float *)at(ws, lo.alpha), *be = (float *)at(ws, lo.beta);
+    float *zp = lo.P ? (float *)at(ws, lo.zp) : nullptr;   // gate partials, when the GEMM makes them
+    bf16 *xbuf = f32 ? nullptr : (bf16 *)at(ws, lo.x);
+    const int64_t state_elems = (int64_t)desc->B * desc->H * D * D;
+    hipError_t e;
+    if (act && (e = launch_act_init(M, act->R, act->halt, s)) != hipSuccess) return hip_fail(e, "halting init launch");
+
+    const void *x = h0;            // GEMM operand of loop tau
+    const void *hprev = h0;        // h^(tau-1) for the residual
+    bool hprev_bf16 = !f32;
+    for (int tau = 0; tau < desc->T; ++tau) {
+        const bool last = tau == desc->T - 1;
+        float *hdst = h_loops ? h_loops + tau * tokd : h_out;  // h^(tau+1), in place over h_out
+        // Under halting a position that did not run the previous loop keeps its
+        // projection input, so its q, k, v and gates from then stand; with the
+        // row-list projection only the positions that ran it are projected again.
+        // (the row-list loads address x with 32-bit byte offsets)
+        const bool compact = act && tau > 0 && zp && (int64_t)M * d * 2 < (int64_t(1) << 32);
+        if (compact && (e = launch_act_rows(M, act->halt, tau, act->rows, act->rows_count, s)) != hipSuccess)
+            return hip_fail(e, "halting row list launch");
+        e = project(f32, M, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo, desc->norm_eps, zp, s,
+                    compact ? act->rows : nullptr, compact ? act->rows_count : nullptr);
+        if (e != hipSuccess) return hip_fail(e, "projection launch");
+        CarryOut out{nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, hdst, (!f32 && !last) ? xbuf : nullptr,
+                     nullptr, act ? act->halt : nullptr};
+        // with gate partials the prep forms alpha and beta and stores them in the
+        // workspace's gate regions, where gdn_loop_prefill documents them
+        gdn_status st = scan_chunks(desc, q, k, v,
+                                    GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
+                                    nullptr, states_out ? states_out + tau * state_elems : nullptr, out, ws, lo, s);
+        if (st != GDN_OK) return st;
+        if (act) {
+            e = launch_act_halt(M, d, hdst, act->w, act->b, act->thr, tau + 1, desc->T, act->R, act->halt,
+                                act->halt_out, act->ponder, s);
+            if (e != hipSuccess) return hip_fail(e, "halting launch");
+        }
+        hprev = hdst;
+        hprev_bf16 = false;
+        x = f32 ? (const void *)hdst : (const void *)xbuf;
+    }
+    if (h_loops) {
+        e = hipMemcpyAsync(h_out, h_loops + (desc->T - 1) * tokd, tokd * sizeof(float), hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "copy of h^(T)");
+    }
+    return GDN_OK;
+}
+
 gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wpack,
                             const float *rho, float *h_out, float *states_out, float *h_loops,
                             void *ws, size_t ws_bytes, void *stream) {
@@ -390,44 +465,27 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
     if (!ws || ws_bytes < lo.total)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
     if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+    return loop_prefill_impl(desc, h0, Wpack, rho, h_out, states_out, h_loops, ws, lo, (hipStream_t)stream, nullptr);
+}
 
-    const hipStream_t s = (hipStream_t)stream;
-    const bool f32 = desc->act == GDN_F32;
-    const int M = desc->B * desc->L, D = desc->dk, d = desc->d;
-    const int64_t tokd = (int64_t)M * d;
-    void *q = at(ws, lo.q), *k = at(ws, lo.k), *v = at(ws, lo.v);
-    float *al = (float *)at(ws, lo.alpha), *be = (float *)at(ws, lo.beta);
-    float *zp = lo.P ? (float *)at(ws, lo.zp) : nullptr;   // gate partials, when the GEMM makes them
-    bf16 *xbuf = f32 ? nullptr : (bf16 *)at(ws, lo.x);
-    const int64_t state_elems = (int64_t)desc->B * desc->H * D * D;
-
-    const void *x = h0;            // GEMM operand of loop tau
-    const void *hprev = h0;        // h^(tau-1) for the residual
-    bool hprev_bf16 = !f32;
-    for (int tau = 0; tau < desc->T; ++tau) {
-        const bool last = tau == desc->T - 1;
-        float *hdst = h_loops ? h_loops + tau * tokd : h_out;  // h^(tau+1), in place over h_out
-        hipError_t e = project(f32, M, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                               desc->norm_eps, zp, s);
-        if (e != hipSuccess) return hip_fail(e, "projection launch");
-        CarryOut out{nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, hdst,
-                     (!f32 && !last) ? xbuf : nullptr};
-        // with gate partials the prep forms alpha and beta and stores them in the
-        // workspace's gate regions, where gdn_loop_prefill documents them
-        st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
-                         nullptr,
-                         states_out ? states_out + tau * state_elems : nullptr, out, ws, lo, s);
-        if (st != GDN_OK) return st;
-        hprev = hdst;
-        hprev_bf16 = false;
-        x = f32 ? (const void *)hdst : (const void *)xbuf;
-    }
-    if (h_loops) {
-        hipError_t e = hipMemcpyAsync(h_out, h_loops + (desc->T - 1) * tokd, tokd * sizeof(float),
-                                      hipMemcpyDeviceToDevice, s);
-        if (e != hipSuccess) return hip_fail(e, "copy of h^(T)");
-    }
-    return GDN_OK;
+gdn_status gdn_loop_prefill_act(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,
+                                const float *w_halt, float b_halt, float eps, float *h_out, int32_t *halt_loop,
+                                float *ponder, void *ws, size_t ws_bytes, void *stream) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
+    REQUIRE_PTR(h0); REQUIRE_PTR(Wpack); REQUIRE_PTR(rho); REQUIRE_PTR(w_halt); REQUIRE_PTR(h_out);
+    OPTIONAL_PTR(halt_loop); OPTIONAL_PTR(ponder);
+    if ((const void *)h_out == h0) return fail(GDN_ERR_SHAPE, "h_out may not alias h0");
+    if (!(eps >= 0.f && eps < 1.f)) return fail(GDN_ERR_SHAPE, "eps must be in [0, 1) (got %g)", (double)eps);
+    if (!std::isfinite(b_halt)) return fail(GDN_ERR_SHAPE, "b_halt must be finite");
+    const Layout lo = layout(desc, GDN_OP_LOOP_PREFILL_ACT);
+    if (!ws || ws_bytes < lo.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
+    if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+    const ActArgs act{w_halt, b_halt, 1.0f - eps, (float *)at(ws, lo.R), (int *)at(ws, lo.halt),
+                      (int *)at(ws, lo.rows), (int *)at(ws, lo.rows_count), halt_loop, ponder};
+    return loop_prefill_impl(desc, h0, Wpack, rho, h_out, nullptr, nullptr, ws, lo, (hipStream_t)stream, &act);
 }
 
 gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wpack,

@@ -357,14 +357,20 @@ __device__ __forceinline__ int wswz(int r, int ch) { return r * WK + ((ch ^ ((r 
 struct WideSrc {
     unsigned off[WLOADS];
 };
-__device__ __forceinline__ WideSrc wide_src(int lane, int wave, int m0, int M, int K, int n_rows) {
+// With a row list (rows != nullptr) token row m of the tile is x row rows[m],
+// and the token offsets are taken from the start of x instead of the tile's
+// first row.
+__device__ __forceinline__ WideSrc wide_src(int lane, int wave, int m0, int M, int K, int n_rows,
+                                            const int *rows = nullptr) {
     WideSrc s;
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
         const int base = (8 * (i < WLOADS_A ? i : i - WLOADS_A) + wave) * 64, p = base + lane;
         const int r = p >> 3, ch = (p & 7) ^ ((r >> 1) & 7);
-        const int row = i < WLOADS_A ? min(m0 + r, M - 1) - m0 : min(r, n_rows - 1);
-        s.off[i] = (unsigned)((row * K + ch * 8) * 2);
+        int row;
+        if (i < WLOADS_A) row = rows ? rows[min(m0 + r, M - 1)] : min(m0 + r, M - 1) - m0;
+        else row = min(r, n_rows - 1);
+        s.off[i] = (unsigned)(((unsigned)row * (unsigned)K + ch * 8) * 2u);
     }
     return s;
 }
@@ -399,7 +405,7 @@ __device__ __forceinline__ void wide_read(WFr &F, const bf16 *stage, int ks, int
 template <int D, int WF>
 __device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *smem, int lane, int wt, int t,
                                               int m0, int n0, int M, int H, bf16 *q, bf16 *k, bf16 *v,
-                                              float eps) {
+                                              float eps, const int *rows) {
     constexpr int NSEC = WN / D;
     constexpr int S0 = (WF * WCOLS) / D, S1 = (WF * WCOLS + WCOLS - 1) / D, NS = S1 - S0 + 1;
     float *red = reinterpret_cast<float *>(smem);   // [4 column quarters][NSEC][WM tokens]
@@ -475,8 +481,8 @@ __device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *s
             const int r0 = t / PIECES, f = (t % PIECES) * 8, n = n0 + f;
             const int head = n / (3 * D), kind = (n % (3 * D)) / D, off = n % D;
             const int64_t rs = (int64_t)H * D;   // elements between consecutive tokens
-            bf16 *dst = (kind == 0 ? q : (kind == 1 ? k : v)) + (int64_t)head * D + off +
-                        (int64_t)(m0 + pass * 64 + r0) * rs;
+            bf16 *dst0 = (kind == 0 ? q : (kind == 1 ? k : v)) + (int64_t)head * D + off;
+            bf16 *dst = dst0 + (int64_t)(m0 + pass * 64 + r0) * rs;
             const bool col_ok = head < H;
             const int mb = m0 + pass * 64 + r0;
 #pragma unroll
@@ -493,7 +499,10 @@ __device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *s
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ii = i0 + i, dm = (ii / 8) * 128 + 8 * (ii % 8);   // token offset of row r0 + 8 ii
-                    if (col_ok && mb + dm < M) *reinterpret_cast<uint4 *>(dst + dm * rs) = val[i];
+                    if (col_ok && mb + dm < M) {
+                        bf16 *d2 = rows ? dst0 + (int64_t)rows[mb + dm] * rs : dst + dm * rs;
+                        *reinterpret_cast<uint4 *>(d2) = val[i];
+                    }
                 }
             }
         }
@@ -501,10 +510,15 @@ __device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *s
     }
 }
 
-template <int D, bool GZ>
+// ROWS: the tile's token rows are the entries m0 .. of the row list `rows`
+// (count in *rows_count, read on the device), gathered from x and scattered to
+// q, k, v and the gate partials; tiles past the count return at once.  M stays
+// the row stride of the gate partials.
+template <int D, bool GZ, bool ROWS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_proj_wide(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Wp, int M, int K, int H, int m_tiles, int n_tiles,
-    bf16 *q, bf16 *k, bf16 *v, float eps, float *__restrict__ zp) {
+    bf16 *q, bf16 *k, bf16 *v, float eps, float *__restrict__ zp, const int *__restrict__ rows,
+    const int *__restrict__ rows_count) {
     __shared__ __attribute__((aligned(16))) char smem[W_LDS_MAIN];
     bf16 *stages = reinterpret_cast<bf16 *>(smem);
 
@@ -534,9 +548,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int m0 = m_tile * WM, n0 = n_tile * WN;
     const int qkv_rows = H * 3 * D;
     const int n_rows = min(WN, qkv_rows - n0);
+    int Mv = M;   // rows of this launch
+    if constexpr (ROWS) {
+        Mv = *rows_count;
+        if (m0 >= Mv) return;   // uniform over the workgroup, before any barrier
+    }
 
-    const WideSrc src = wide_src(lane, wave, m0, M, K, n_rows);
-    const bf16 *xb = x + (int64_t)m0 * K, *wb = Wp + (int64_t)n0 * K;
+    const WideSrc src = wide_src(lane, wave, m0, Mv, K, n_rows, ROWS ? rows : nullptr);
+    const bf16 *xb = x + (ROWS ? (int64_t)0 : (int64_t)m0 * K), *wb = Wp + (int64_t)n0 * K;
     const int nkb = K / WK;
     // channel offset of the i-th block of this tile's k order (blocks kb0,
     // kb0+1, ... wrapping around); past the end it repeats the last one.  The
@@ -588,8 +607,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (two) gate_steps(1);
         // C lane layout: token (lane % 32), gate rows 8 (e / 4) + 4 (lane / 32) + e % 4
         const int gh2 = 2 * H, tok = m0 + wt * 128 + wf * 32 + (lane & 31);
-        float *zdst = zp + (int64_t)n_tile * gh2 * M + tok;
-        if (tok < M) {
+        if (tok < Mv) {
+            float *zdst = zp + (int64_t)n_tile * gh2 * M + (ROWS ? rows[tok] : tok);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = 8 * (e / 4) + 4 * (lane >> 5) + e % 4;
@@ -640,10 +659,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
 
     switch (wf) {
-        case 0: wide_epilogue<D, 0>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
-        case 1: wide_epilogue<D, 1>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
-        case 2: wide_epilogue<D, 2>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
-        default: wide_epilogue<D, 3>(acc, smem, lane, wt, t, m0, n0, M, H, q, k, v, eps); break;
+        case 0: wide_epilogue<D, 0>(acc, smem, lane, wt, t, m0, n0, Mv, H, q, k, v, eps, ROWS ? rows : nullptr); break;
+        case 1: wide_epilogue<D, 1>(acc, smem, lane, wt, t, m0, n0, Mv, H, q, k, v, eps, ROWS ? rows : nullptr); break;
+        case 2: wide_epilogue<D, 2>(acc, smem, lane, wt, t, m0, n0, Mv, H, q, k, v, eps, ROWS ? rows : nullptr); break;
+        default: wide_epilogue<D, 3>(acc, smem, lane, wt, t, m0, n0, Mv, H, q, k, v, eps, ROWS ? rows : nullptr); break;
     }
 }
 
@@ -804,7 +823,9 @@ int gate_partials(bool f32, int M, int d, int H) {
 
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
-                          float eps, float *zp, hipStream_t s) {
+                          float eps, float *zp, hipStream_t s, const int *rows, const int *rows_count) {
+    if (rows && (f32 || !project_separate_gates(f32, M) || !zp || (int64_t)M * d * 2 >= (int64_t(1) << 32)))
+        return hipErrorInvalidValue;
     const int ntiles = (int)(packed_rows(H, D) / BN);
     if (f32) {
         dim3 grid(ntiles, (M + BM_F - 1) / BM_F);
@@ -818,13 +839,16 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
                                alpha, beta, alpha_lo, eps);
     } else if (project_separate_gates(f32, M)) {
         const int m_tiles = (M + WM - 1) / WM, n_tiles = (H * 3 * D + WN - 1) / WN;
-#define WIDE(DD, GZ)                                                                               \
-    launch_kernel(k_proj_wide<DD, GZ>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x,   \
-                  (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps, zp)
-        if (zp) {
-            if (D == 128) WIDE(128, true); else WIDE(64, true);
+#define WIDE(DD, GZ, RW)                                                                           \
+    launch_kernel(k_proj_wide<DD, GZ, RW>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x, \
+                  (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps, zp, rows, \
+                  rows_count)
+        if (rows) {
+            if (D == 128) WIDE(128, true, true); else WIDE(64, true, true);
+        } else if (zp) {
+            if (D == 128) WIDE(128, true, false); else WIDE(64, true, false);
         } else {
-            if (D == 128) WIDE(128, false); else WIDE(64, false);
+            if (D == 128) WIDE(128, false, false); else WIDE(64, false, false);
         }
 #undef WIDE
     } else {

@@ -781,7 +781,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc,
     const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
     float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
-    float *h_out, bf16 *x_next, float *__restrict__ s_chunks) {
+    float *h_out, bf16 *x_next, float *__restrict__ s_chunks, const int *__restrict__ halted) {
     using G = CarryCfg<D, TIn>;
     constexpr int NT = G::NT, RW = G::RW, KW = G::KW, STG = G::STG;
     // every stage is an object of its own, so the compiler can tell the buffers
@@ -910,6 +910,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 if (c0 + r >= L) continue;
                 const float ov = gv[j] * qs[j] + me[j];
                 const int64_t row = tokb + c0 + r;
+                if (halted && halted[row] != 0) continue;   // a halted position keeps its state
                 if constexpr (RES == 0) {
                     if (o) o[(row * H + h) * D + col] = ov;
                 } else {
@@ -1170,7 +1171,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v, int L, int H, int Nc,
     const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
     float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
-    float *h_out, bf16 *x_next, float *__restrict__ s_chunks) {
+    float *h_out, bf16 *x_next, float *__restrict__ s_chunks, const int *__restrict__ halted) {
     using G = CarryW;
     using KT = KTile<128, bf16>;
     constexpr int D = G::D;
@@ -1511,6 +1512,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
                 if (c0 + r >= L) continue;
                 const float ov = gv[j] * qs[j] + mev[j];
                 const int64_t row = tokb + c0 + r;
+                if (halted && halted[row] != 0) continue;   // a halted position keeps its state
                 if constexpr (RES == 0) {
                     if (o) o[(row * H + h) * D + col] = ov;
                 } else {
@@ -1579,7 +1581,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
 #define CARRYW(R, X)                                                                               \
     launch_kernel((k_scan_carry_w<R, X>), gridw, dim3(CARRY_THREADS), 0, s, (const bf16 *)q, (const bf16 *)k, \
                   (const bf16 *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
-                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks)
+                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks, out.halted)
         if (res == 0) CARRYW(0, false);
         else if (res == 1) { if (xn) CARRYW(1, true); else CARRYW(1, false); }
         else { if (xn) CARRYW(2, true); else CARRYW(2, false); }
@@ -1590,7 +1592,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
 #define CARRY(DD, T, R, X)                                                                         \
     launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(CARRY_THREADS), 0, s, (const T *)q, (const T *)k, \
                   (const T *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
-                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks)
+                  s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks, out.halted)
 #define CARRY_R(DD, T)                                                                             \
     do {                                                                                           \
         if (res == 0) CARRY(DD, T, 0, false);                                                      \

@@ -30,8 +30,13 @@ import torch
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "prefill_inputs", "scan_inputs",
-    "decode_state_init", "decode_step_inputs", "unit_rows", "grad_inputs",
+    "decode_state_init", "decode_step_inputs", "unit_rows", "grad_inputs", "act_inputs", "ACT_BIAS", "ACT_EPS",
 ]
+
+# The halting layer of the adaptive-halting workloads: w ~ N(0, 1/d) and this bias, so that
+# sigmoid(w . h + b) spreads the positions' halting loops over 1..T; eps as on the pages (LT2 Appendix A).
+ACT_BIAS = -0.5
+ACT_EPS = 0.01
 
 
 @dataclasses.dataclass(frozen=True)
@@ -192,3 +197,11 @@ def grad_inputs(seed: int, B: int, L: int, H: int, dk: int, dv: int, with_state_
     if with_state_grad:
         out["d_sfinal"] = torch.from_numpy(rng.standard_normal((B, H, dk, dv), dtype=np.float32))
     return out
+
+
+def act_inputs(w: Workload, seed: int = 7) -> dict:
+    """Halting layer of an adaptive-halting loop: w_halt ~ N(0, 1/d) [d] fp32 (seeded), b_halt = ACT_BIAS,
+    eps = ACT_EPS."""
+    rng = np.random.default_rng(seed)
+    wh = rng.standard_normal(w.d, dtype=np.float32) * np.float32(1.0 / math.sqrt(w.d))
+    return dict(w_halt=torch.from_numpy(wh), b_halt=ACT_BIAS, eps=ACT_EPS)
