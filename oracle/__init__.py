@@ -53,7 +53,7 @@ _lib = None
 
 __all__ = [
     "build", "num_threads", "round_bf16", "round_f32", "scan", "scan_backward", "project",
-    "loop_prefill", "loop_prefill_act", "loop_decode_step", "scan_chunkwise",
+    "loop_prefill", "loop_prefill_act", "loop_backward", "loop_decode_step", "scan_chunkwise",
 ]
 
 
@@ -240,6 +240,77 @@ def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
             states.append(s)
     return dict(h=h, loops=loops if keep_loops else None,
                 states=states if keep_states else None)
+
+
+def loop_backward(h0, Wq, Wk, Wv, wa, wb, rho, loops, dh, H: int, dk: int, dv: int, alpha_lo: float, act: str,
+                  eps: float = 1e-6):
+    """Gradients of ``loop_prefill`` (T weight-tied loops, LT2 Section 2; trained through, Appendix C) for an
+    incoming gradient dh = dL/dh^(T) [B, L, d].
+
+    ``loops`` holds the forward's h^(1..T) (``keep_loops``; only h^(1..T-1), the inputs of loops 2..T, are
+    read).  Each loop tau = T..1 is recomputed from its input h^(tau-1) and then taken in reverse:
+        x                     = h^(tau-1), or bf16(fp32(h^(tau-1))) for bf16 workloads
+        qr, kr, v, a, b       = x Wq, x Wk, x Wv, x wa, x wb          (raw projections, per head)
+        q = qr / r_q, k = kr / r_k with r = sqrt(|raw|^2 + eps) per (token, head)
+        alpha = alpha_lo + (1 - alpha_lo) s, s = 1 / (1 + e^a);  beta = 1 / (1 + e^-b)
+        dq, dk, dv, dalpha, dbeta = scan_backward(q, k, v, alpha, beta, d_o = dh)   (from S = 0; the loop's
+                                    final state is not an output of the loss, so dS_final = 0)
+        dqr = (dq - q (q . dq)) / r_q, likewise dkr          (through the L2 normalisation)
+        da  = -dalpha (1 - alpha_lo) s (1 - s),  db = dbeta beta (1 - beta)
+        dW* += x^T d*r  (q, k, v, a, b)
+        drho_tau = sum over (b, l) of dh (.) h^(tau-1)
+        dh <- rho_tau (.) dh + dqr Wq^T + dkr Wk^T + dv Wv^T + da wa^T + db wb^T
+    For bf16 workloads the roundings of the forward (x, and q, k, v after normalisation) pass the gradient
+    through unchanged: the scan backward is evaluated at the rounded q, k, v, everything else at the unrounded
+    values.  Returns dict(dh0 [B,L,d], dWq, dWk [d,H*dk], dWv [d,H*dv], dwa, dwb [d,H], drho [T,d]).  fp64.
+    """
+    h0 = _f64(h0)
+    rho = _f64(rho)
+    B, L, d = h0.shape
+    T = rho.shape[0]
+    M = B * L
+    Wq, Wk, Wv, wa, wb = map(_f64, (Wq, Wk, Wv, wa, wb))
+    ins = [h0] + [_f64(h) for h in loops[:T - 1]]
+    g = _f64(dh).reshape(M, d)
+    out = dict(dWq=np.zeros_like(Wq), dWk=np.zeros_like(Wk), dWv=np.zeros_like(Wv), dwa=np.zeros_like(wa),
+               dwb=np.zeros_like(wb), drho=np.zeros((T, d)))
+    for tau in range(T - 1, -1, -1):
+        hp = ins[tau].reshape(M, d)
+        x = round_bf16(hp) if act == "bf16" else hp
+        qr = (x @ Wq).reshape(M, H, dk)
+        kr = (x @ Wk).reshape(M, H, dk)
+        vr = (x @ Wv).reshape(M, H, dv)
+        a, b = x @ wa, x @ wb
+        rq = np.sqrt(np.sum(qr * qr, axis=-1, keepdims=True) + eps)
+        rk = np.sqrt(np.sum(kr * kr, axis=-1, keepdims=True) + eps)
+        qn, kn = qr / rq, kr / rk
+        sg = 1.0 / (1.0 + np.exp(a))
+        alpha = alpha_lo + (1.0 - alpha_lo) * sg
+        beta = 1.0 / (1.0 + np.exp(-b))
+        if act == "bf16":
+            qs, ks, vs = round_bf16(qn), round_bf16(kn), round_bf16(vr)
+            als, bes = round_f32(alpha), round_f32(beta)
+        else:
+            qs, ks, vs, als, bes = qn, kn, vr, alpha, beta
+        gs = scan_backward(qs.reshape(B, L, H, dk), ks.reshape(B, L, H, dk), vs.reshape(B, L, H, dv),
+                           als.reshape(B, L, H), bes.reshape(B, L, H), g.reshape(B, L, H, dv))
+        dq = gs["dq"].reshape(M, H, dk)
+        dkn = gs["dk"].reshape(M, H, dk)
+        dqr = (dq - qn * np.sum(qn * dq, axis=-1, keepdims=True)) / rq
+        dkr = (dkn - kn * np.sum(kn * dkn, axis=-1, keepdims=True)) / rk
+        dvr = gs["dv"].reshape(M, H * dv)
+        da = -gs["dalpha"].reshape(M, H) * (1.0 - alpha_lo) * sg * (1.0 - sg)
+        db = gs["dbeta"].reshape(M, H) * beta * (1.0 - beta)
+        dqr, dkr = dqr.reshape(M, H * dk), dkr.reshape(M, H * dk)
+        out["dWq"] += x.T @ dqr
+        out["dWk"] += x.T @ dkr
+        out["dWv"] += x.T @ dvr
+        out["dwa"] += x.T @ da
+        out["dwb"] += x.T @ db
+        out["drho"][tau] = np.sum(g * hp, axis=0)
+        g = rho[tau][None, :] * g + dqr @ Wq.T + dkr @ Wk.T + dvr @ Wv.T + da @ wa.T + db @ wb.T
+    out["dh0"] = g.reshape(B, L, d)
+    return out
 
 
 def loop_prefill_act(h0, Wq, Wk, Wv, wa, wb, rho, w_halt, b_halt: float, eps: float, H: int, dk: int, dv: int,

@@ -493,3 +493,77 @@ def test_act_frozen_position_is_context_but_not_updated():
     assert r["halt_loop"][0, -1] == 1 and np.all(r["halt_loop"][0, :-1] == x["rho"].shape[0])
     assert np.array_equal(r["h"][0, :-1], plain["h"][0, :-1])
     assert np.array_equal(r["h"][0, -1], plain["loops"][0][0, -1])
+
+
+# ---------------------------------------------------------------------------
+# backward through the T loops
+# ---------------------------------------------------------------------------
+_LB_KEYS = ("h0", "Wq", "Wk", "Wv", "wa", "wb", "rho")
+_LB_GRADS = {"h0": "dh0", "Wq": "dWq", "Wk": "dWk", "Wv": "dWv", "wa": "dwa", "wb": "dwb", "rho": "drho"}
+
+
+def _loop_loss(x, s, dh, alpha_lo):
+    return float(np.sum(oracle.loop_prefill(**x, **s, alpha_lo=alpha_lo, act="f32")["h"] * dh))
+
+
+def _loop_grads(x, s, dh, alpha_lo, act="f32"):
+    fwd = oracle.loop_prefill(**x, **s, alpha_lo=alpha_lo, act=act, keep_loops=True)
+    return oracle.loop_backward(**x, loops=fwd["loops"], dh=dh, **s, alpha_lo=alpha_lo, act=act)
+
+
+@pytest.mark.parametrize("alpha_lo,T", [(0.0, 3), (0.6, 2)])
+def test_loop_backward_equals_central_differences(alpha_lo, T):
+    """Every element of dh0, dWq, dWk, dWv, dwa, dwb and drho against central differences of L = <dh, h^(T)>
+    through the fp64 forward loop (e = 1e-6; exact to O(e^2))."""
+    x, s = _tiny_loop_inputs(51 + T, B=2, L=6, H=2, dk=3, dv=3, T=T)
+    dh = np.random.default_rng(7).standard_normal(x["h0"].shape)
+    g = _loop_grads(x, s, dh, alpha_lo)
+    eps = 1e-6
+    for key in _LB_KEYS:
+        base = x[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            xp, xm = dict(x), dict(x)
+            xp[key] = base.copy(); xp[key][idx] += eps
+            xm[key] = base.copy(); xm[key][idx] -= eps
+            fd[idx] = (_loop_loss(xp, s, dh, alpha_lo) - _loop_loss(xm, s, dh, alpha_lo)) / (2 * eps)
+        err = np.max(np.abs(fd - g[_LB_GRADS[key]])) / max(np.max(np.abs(fd)), 1e-12)
+        assert err < 1e-6, (key, err)
+
+
+def test_loop_backward_directional_long():
+    """Past the scan's 64-token checkpoint blocks (L = 100, 2 sequences, 4 loops): directional derivatives along
+    random directions of every input at once agree with central differences."""
+    x, s = _tiny_loop_inputs(61, B=2, L=100, H=2, dk=4, dv=4, T=4)
+    rng = np.random.default_rng(62)
+    dh = rng.standard_normal(x["h0"].shape)
+    g = _loop_grads(x, s, dh, 0.3)
+    for trial in range(2):
+        dirs = {key: rng.standard_normal(x[key].shape) for key in _LB_KEYS}
+        eps = 1e-6
+        xp = {key: x[key] + eps * dirs[key] for key in _LB_KEYS}
+        xm = {key: x[key] - eps * dirs[key] for key in _LB_KEYS}
+        fd = (_loop_loss(xp, s, dh, 0.3) - _loop_loss(xm, s, dh, 0.3)) / (2 * eps)
+        an = sum(float(np.sum(g[_LB_GRADS[key]] * dirs[key])) for key in _LB_KEYS)
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_loop_backward_zero_values_closed_form(act):
+    """Wv = 0: h^(T) = (prod rho) (.) h0 whatever q, k and the gates are, so dh0 = (prod rho) (.) dh,
+    drho_tau = sum over positions of dh (.) h0 (.) prod_{sigma != tau} rho_sigma, and the gradients of Wq, Wk,
+    wa, wb vanish exactly (the state stays zero, so nothing downstream depends on them)."""
+    x, s = _tiny_loop_inputs(71, B=2, L=30, H=2, dk=4, dv=4, T=3)
+    x["Wv"] = np.zeros_like(x["Wv"])
+    if act == "bf16":
+        x["h0"] = oracle.round_bf16(x["h0"])
+    dh = np.random.default_rng(72).standard_normal(x["h0"].shape)
+    g = _loop_grads(x, s, dh, 0.2, act)
+    rho = x["rho"]
+    assert np.allclose(g["dh0"], np.prod(rho, 0)[None, None] * dh, rtol=1e-13, atol=1e-15)
+    for t in range(rho.shape[0]):
+        others = np.prod(np.delete(rho, t, axis=0), 0)
+        ref = np.sum(dh * x["h0"], axis=(0, 1)) * others
+        assert np.allclose(g["drho"][t], ref, rtol=1e-12, atol=1e-14)
+    for key in ("dWq", "dWk", "dwa", "dwb"):
+        assert np.all(g[key] == 0), key
