@@ -23,6 +23,7 @@ Printed (one JSON line on stdout):
   act             the headline workload through gdn_loop_prefill_act (per-token adaptive halting): rate,
                   halting loops, share of position-loops projected;
   scan_backward   gradients of one scan pass at the 4096-token prompt's shape (gdn_scan_backward);
+  loop_backward   gradients through the 4 loops of the 4096-token prompt (gdn_loop_backward);
   cpu_baseline    the oracle on a bounded sample of the headline workload, on the host's cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode]
@@ -409,6 +410,70 @@ def bench_act(args, torch, gl, synth, w):
             "projected_share": projected / (M * w.T)}
 
 
+def bench_loop_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
+    """gdn_loop_backward through the T loops of a prompt workload (the forward's h^(1..T-1) from
+    gdn_loop_prefill, a seeded N(0, 1) incoming gradient dL/dh^(T))."""
+    w = synth.workload(name)
+    B, L, H, D, d, T = w.B, w.L, w.H, w.dk, w.d, w.T
+    dev = lambda t: t.contiguous().to("cuda")
+    x = synth.prefill_inputs(w)
+    desc = gl.make_desc(B, L, H, D, D, T=T, act=w.act, alpha_lo=w.alpha_lo)
+    Wp = torch.empty(gl.gdn_weights_packed_bytes(desc) // (4 if w.act == "f32" else 2), dtype=desc.act_dtype,
+                     device="cuda")
+    gl.gdn_weights_pack(desc, dev(x["Wq"]), dev(x["Wk"]), dev(x["Wv"]), dev(x["wa"]), dev(x["wb"]), Wp)
+    h0, rho = dev(x["h0"]), dev(x["rho"])
+    h_out = torch.empty(B, L, d, device="cuda")
+    h_loops = torch.empty(T, B, L, d, device="cuda")
+    gl.gdn_loop_prefill(desc, h0, Wp, rho, h_out, None, h_loops, gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL))
+    dh = dev(synth.grad_inputs(92, B, L, H, D, D, with_state_grad=False)["d_o"].reshape(B, L, d))
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_BACKWARD)
+    f = dict(device="cuda")
+    outs = [torch.empty(B, L, d, **f), torch.empty(d, H * D, **f), torch.empty(d, H * D, **f),
+            torch.empty(d, H * D, **f), torch.empty(d, H, **f), torch.empty(d, H, **f), torch.empty(T, d, **f)]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gl.gdn_loop_backward(desc, h0, Wp, rho, h_loops, dh, *outs, ws, stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    n = max(min(args.steps, 10), 3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    stages = {"gemm": gl.GDN_STAGE_BWD_GEMM, "fwd_prep": gl.GDN_STAGE_SCAN_PREP, "fwd_carry": gl.GDN_STAGE_SCAN_CARRY,
+              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
+              "bwd_chunk": gl.GDN_STAGE_BWD_CHUNK}
+    timers = {k: gl.gdn_timer_create(v, 3 * n * T) for k, v in stages.items()}
+    for t in timers.values():
+        gl.gdn_timer_attach(t)
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    gl.gdn_timer_detach()
+    per, tot = {}, {}
+    for k, t in timers.items():
+        cnt, total = gl.gdn_timer_read(t)
+        per[k] = total / max(cnt, 1)
+        tot[k] = total / n
+        gl.gdn_timer_destroy(t)
+    M = B * L
+    P = (H * 3 * D + 127) // 128 * 128 + 128
+    gemm_flops = 3 * 2 * M * P * d     # per loop: projections recomputed, dY W, x^T dY (counted once each)
+    gemm_ach = gemm_flops * T / (tot["gemm"] * 1e-3) / 1e12
+    return {"workload": f"loop backward, {name} (B={B}, L={L}, H={H}, dk=dv={D}, d={d}, T={T}, {w.act} inputs)",
+            "value": M / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+            "stages_ms_per_call": tot, "stages_avg_launch_us": {k: v * 1e3 for k, v in per.items()},
+            "gemm": {"bound": "mfma", "kernel": "k_gemm_nt", "achieved": gemm_ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_ach / PEAK_BF16_TFLOPS,
+                     "note": "algorithmic 2MNK per product; fp32 operands run 2-3 bf16 passes"}}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -556,6 +621,8 @@ def main():
     if not args.no_backward:
         log("scan backward: the 4096-token prompt's shape ...")
         out["scan_backward"] = bench_backward(args, torch, gl, synth)
+        log("loop backward: the 4096-token prompt ...")
+        out["loop_backward"] = bench_loop_backward(args, torch, gl, synth)
     if not args.no_decode:
         out["decode"] = bench_decode(args, torch, gl, synth)
         log("loop decode: 64 sequences with projections ...")

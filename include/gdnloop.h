@@ -102,7 +102,7 @@ gdn_status gdn_weights_pack(const gdn_desc *desc, const void *Wq, const void *Wk
 
 enum { GDN_OP_LOOP_PREFILL = 0, GDN_OP_LOOP_DECODE = 1, GDN_OP_SCAN_PREFILL = 2,
        GDN_OP_SCAN_DECODE = 3, GDN_OP_PROJECT = 4, GDN_OP_SCAN_BACKWARD = 5,
-       GDN_OP_LOOP_PREFILL_ACT = 6 };
+       GDN_OP_LOOP_PREFILL_ACT = 6, GDN_OP_LOOP_BACKWARD = 7 };
 
 /* Device scratch bytes that operation `op` needs for `desc` (0 is valid). */
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes);
@@ -274,6 +274,39 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 gdn_status gdn_loop_decode_noalloc(const gdn_desc *desc, const void *h_t, const void *Wpack,
                                    const float *rho, float *states, float *h_out, void *stream);
 
+/* Gradients of gdn_loop_prefill through its T loops.
+ * Passage: LT2: Linear-Time Looped Transformers, Appendix C (every looped
+ * model is trained through this path with bf16 mixed precision); the
+ * forward is that of gdn_loop_prefill (Section 2, "Looped Transformer (LT)"
+ * and "LT2" paragraphs: weight tying and the per-loop residual gate).  For a
+ * loss L of h^(T), given dh = dL/dh^(T), each loop tau = T..1 is recomputed
+ * from its input h^(tau-1) (raw projections, L2 norm, gates; then the scan's
+ * chunk matrices and states) and taken in reverse: the scan backward with
+ * dO = dL/dh^(tau), the gradient through the normalisation and the gates,
+ *     dW += x^T dY,   drho_tau = sum over positions of dL/dh^(tau) (.) h^(tau-1),
+ *     dL/dh^(tau-1) = rho_tau (.) dL/dh^(tau) + dY W.
+ * The forward's bf16 roundings (the loop operand x = bf16(h), q/k/v) pass
+ * the gradient through unchanged.  Every loop's scan starts from S = 0 and
+ * its final state is not an input of L.
+ *   h0 [B, L, d]                 device, desc->act (as given to gdn_loop_prefill)
+ *   Wpack, rho [T, d]            as for gdn_loop_prefill
+ *   h_loops [T, B, L, d]         device fp32: h^(1..T) as gdn_loop_prefill's h_loops
+ *                                wrote them (slices 0..T-2 are read; NULL allowed when T == 1)
+ *   dh [B, L, d]                 device fp32, dL/dh^(T) (read only)
+ *   dh0 [B, L, d]                device fp32, written: dL/dh0
+ *   dWq, dWk [d, H*dk], dWv [d, H*dv], dwa, dwb [d, H]   device fp32, written: the
+ *                                gradients of the unpacked weights (gdn_weights_pack's inputs)
+ *   drho [T, d]                  device fp32, written
+ *   ws, ws_bytes                 gdn_workspace_bytes(GDN_OP_LOOP_BACKWARD)
+ * Products run on bf16 MFMA with fp32 operands split into two bf16 parts.
+ * alpha must stay above 0 (dalpha divides by it).  GDN_ERR_UNSUPPORTED for
+ * fp32 inputs with dk = 128; GDN_ERR_SHAPE beyond 65535 * 64 tokens or when dh0
+ * aliases dh. */
+gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,
+                             const float *h_loops, const float *dh, float *dh0, float *dWq, float *dWk,
+                             float *dWv, float *dwa, float *dwb, float *drho, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 
 const char *gdn_status_string(gdn_status s);
@@ -288,7 +321,10 @@ const char *gdn_version(void);
  * output pass that the carry now performs, and gdn_timer_create rejects it). */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
        GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5, GDN_STAGE_BWD_CARRY = 6, GDN_STAGE_BWD_CHUNK = 7,
-       GDN_STAGE_BWD_PREP = 8 };
+       GDN_STAGE_BWD_PREP = 8, GDN_STAGE_BWD_GEMM = 9 };
+/* GDN_STAGE_BWD_GEMM times the three products of each loop of
+ * gdn_loop_backward (the projections recomputed, the input gradient and the
+ * weight gradient). */
 /* GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_CARRY and GDN_STAGE_BWD_CHUNK time the
  * three kernels of gdn_scan_backward that follow its forward recomputation
  * (whose prep and carry are timed as GDN_STAGE_SCAN_PREP and

@@ -21,29 +21,29 @@ import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
-    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_OP_LOOP_PREFILL_ACT", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
+    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_OP_LOOP_PREFILL_ACT", "GDN_OP_LOOP_BACKWARD", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
     "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES", "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_PREP",
-    "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
+    "GDN_STAGE_BWD_GEMM", "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
     "GDN_WS_ALPHA", "GDN_WS_BETA", "GdnError", "gdn_desc", "make_desc", "lib_path",
     "load", "EXPORTED", "workspace", "workspace_view", "gdn_workspace_region",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act", "gdn_loop_decode", "gdn_loop_decode_noalloc",
-    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
+    "gdn_loop_backward", "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
 (GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT, GDN_OP_SCAN_BACKWARD,
- GDN_OP_LOOP_PREFILL_ACT) = range(7)
+ GDN_OP_LOOP_PREFILL_ACT, GDN_OP_LOOP_BACKWARD) = range(8)
 GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_GATES = 0, 1, 2, 3, 5
-GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_PREP = 6, 7, 8
+GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_GEMM = 6, 7, 8, 9
 GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act", "gdn_loop_decode", "gdn_loop_decode_noalloc",
-    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
+    "gdn_loop_backward", "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
     "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
@@ -100,6 +100,7 @@ def load():
         "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
         "gdn_loop_prefill_act": [D, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, P, P, S, P],
         "gdn_loop_decode_noalloc": [D, P, P, P, P, P, P],
+        "gdn_loop_backward": [D] + [P] * 13 + [S, P],
         "gdn_timer_create": [I, I, ctypes.POINTER(P)],
         "gdn_timer_set_stride": [P, I],
         "gdn_timer_attach": [P],
@@ -259,6 +260,20 @@ def gdn_scan_backward(desc, q, k, v, alpha, beta, s_init, d_o, d_sfinal, dq, dk,
         _ptr(d_sfinal, "d_sfinal", f, st, optional=True), _ptr(dq, "dq", f, BL * H * D),
         _ptr(dk, "dk", f, BL * H * D), _ptr(dv, "dv", f, BL * H * D), _ptr(dalpha, "dalpha", f, BL * H),
         _ptr(dbeta, "dbeta", f, BL * H), _ptr(ds_init, "ds_init", f, st, optional=True), wp, wn, _stream(stream)))
+
+
+def gdn_loop_backward(desc, h0, Wpack, rho, h_loops, dh, dh0, dWq, dWk, dWv, dwa, dwb, drho, ws, stream=None):
+    a, BL, d, T, H = desc.act_dtype, desc.B * desc.L, desc.d, desc.T, desc.H
+    pb = gdn_weights_packed_bytes(desc)
+    f = torch.float32
+    wp, wn = _ws(ws)
+    _check(load().gdn_loop_backward(
+        ctypes.byref(desc), _ptr(h0, "h0", a, BL * d),
+        _ptr(Wpack, "Wpack", a, pb // (4 if desc.act == GDN_F32 else 2)), _ptr(rho, "rho", f, T * d),
+        _ptr(h_loops, "h_loops", f, T * BL * d, optional=T == 1), _ptr(dh, "dh", f, BL * d),
+        _ptr(dh0, "dh0", f, BL * d), _ptr(dWq, "dWq", f, d * H * desc.dk), _ptr(dWk, "dWk", f, d * H * desc.dk),
+        _ptr(dWv, "dWv", f, d * H * desc.dv), _ptr(dwa, "dwa", f, d * H), _ptr(dwb, "dwb", f, d * H),
+        _ptr(drho, "drho", f, T * d), wp, wn, _stream(stream)))
 
 
 def gdn_scan_decode(desc, q, k, v, alpha, beta, states, o, stream=None):

@@ -104,6 +104,41 @@ struct CarryOut {
 hipError_t launch_act_init(int M, float *R, int *halt, hipStream_t s);
 hipError_t launch_act_halt(int M, int d, const float *h, const float *w, float b, float thr, int tau, int T, float *R,
                            int *halt, int *halt_out, float *ponder_out, hipStream_t s);
+// ---- token-local steps of the loop backward (loop_backward.hip) ----
+// x[i] = bf16(h[i]) (round to nearest even), n elements, 16-byte aligned.
+hipError_t launch_lb_round(int64_t n, const float *h, bf16 *x, hipStream_t s);
+// Y <- dL/dY from the scan gradients, in place.
+hipError_t launch_lb_epilogue_grad(int M, int H, int D, float *Y, int64_t P, int64_t qkvp, float eps, float alpha_lo,
+                                   const float *dq, const float *dk, const float *dv, const float *dalpha,
+                                   const float *dbeta, hipStream_t s);
+// drho[c] = sum_r dh[r][c] hp[r][c] through lb_drho_blocks(M) x d partials.
+int lb_drho_blocks(int M);
+hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp_f32, float *part, float *drho,
+                          hipStream_t s);
+// dWT [d][P] to dWq, dWk [d][H D], dWv [d][H D], dwa, dwb [d][H].
+hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, int64_t P, int64_t qkvp, float *dWq, float *dWk,
+                            float *dWv, float *dwa, float *dwb, hipStream_t s);
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
+
+// ---- products and transposes of the loop backward (gemm_nt.hip) ----
+// Operand modes: bf16 in memory; fp32 split into bf16 hi + lo; fp32 rounded to bf16.
+// (Named enums: an enumerator of an unnamed enum inside a kernel's template
+// signature is mangled differently by the host and device compilations.)
+enum GemmOperand : int { OPND_BF16 = 0, OPND_F32_SPLIT = 1, OPND_F32_ROUND = 2 };
+// Epilogues: C = acc; C += acc; C = acc + rho[n] * Dsrc[m][n].
+enum GemmEpilogue : int { EPI_STORE = 0, EPI_ACCUM = 1, EPI_RESID = 2 };
+// C[m][n] (op)= sum_k A[m][k] B[n][k] for m < M, n < N; A [M][lda], B [N][ldb]
+// K-contiguous, K, lda, ldb multiples of 8, 16-byte aligned bases.  Pairs
+// supported: (bf16, bf16), (round, bf16), (split, bf16), (split, split),
+// (bf16, split).
+hipError_t launch_gemm_nt(int mode_a, int mode_b, int epi, const void *A, int64_t lda, const void *B, int64_t ldb,
+                          int M, int N, int K, float *C, int64_t ldc, const float *rho, const float *Dsrc,
+                          int64_t ldd, hipStream_t s);
+// out[c][r] = in[r][c] (r < R, c < Cc; fp32 or bf16 either side, RNE to bf16),
+// and 0 for R <= r < Rp.
+hipError_t launch_transpose(bool in_f32, bool out_f32, const void *in, int64_t ldi, int R, int Cc, void *out,
+                            int64_t ldo, int Rp, hipStream_t s);
+
 // The positions that ran loop tau (halt 0 or tau), in ascending order, and
 // their count: the rows whose projection input changed for loop tau + 1.
 hipError_t launch_act_rows(int M, const int *halt, int tau, int *rows, int *count, hipStream_t s);

@@ -89,6 +89,14 @@ gdn_status check_prefill_grid(const gdn_desc *d) {
     return GDN_OK;
 }
 
+// Sizes the loop backward's products and row-block reductions can take.
+gdn_status check_loop_backward(const gdn_desc *d) {
+    const int64_t M = (int64_t)d->B * d->L, Mp = (M + 63) / 64 * 64;
+    if ((M + 127) / 128 > 65535 || Mp / 64 > 65535 || (packed_rows(d->H, d->dk) + 127) / 128 > 65535)
+        return fail(GDN_ERR_SHAPE, "the loop backward takes at most 65535 * 64 tokens");
+    return GDN_OK;
+}
+
 #define REQUIRE_PTR(p)                                                                             \
     do {                                                                                           \
         if (!(p)) return fail(GDN_ERR_NULL, "%s is NULL", #p);                                     \
@@ -102,7 +110,12 @@ gdn_status check_prefill_grid(const gdn_desc *d) {
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
     size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, sc = 0, dse = 0, bm = 0;
-    size_t R = 0, halt = 0, rows = 0, rows_count = 0, total = 0;
+    size_t R = 0, halt = 0, rows = 0, rows_count = 0;
+    // the loop backward: raw projections (then their gradient) [M][P] and its
+    // transpose [P][Mp], the loop input and the weights transposed, the scan
+    // gradients, two dh buffers, the weight-gradient accumulator [d][P], rho partials
+    size_t Y = 0, YT = 0, XT = 0, WT = 0, gq = 0, gk = 0, gv = 0, gal = 0, gbe = 0, dhA = 0, dhB = 0, dW = 0, part = 0;
+    size_t total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
 
@@ -120,8 +133,9 @@ Layout layout(const gdn_desc *d, int op) {
     };
     const bool act = op == GDN_OP_LOOP_PREFILL_ACT;
     if (act) op = GDN_OP_LOOP_PREFILL;   // the loop prefill's regions, then the halting state
-    const bool proj = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_LOOP_DECODE;
-    const bool chunks = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD;
+    const bool lbwd = op == GDN_OP_LOOP_BACKWARD;
+    const bool proj = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_LOOP_DECODE || lbwd;
+    const bool chunks = op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD || lbwd;
     if (proj) {
         lo.q = take(tokens * d->H * D * act_bytes(d));
         lo.k = take(tokens * d->H * D * act_bytes(d));
@@ -129,7 +143,7 @@ Layout layout(const gdn_desc *d, int op) {
         lo.alpha = take(tokens * d->H * 4);
         lo.beta = take(tokens * d->H * 4);
         if (d->act == GDN_BF16 && d->T > 1) lo.x = take(tokens * d->d * 2);
-        if (op == GDN_OP_LOOP_PREFILL) {
+        if (op == GDN_OP_LOOP_PREFILL || lbwd) {
             lo.P = gate_partials(d->act == GDN_F32, (int)tokens, d->d, d->H);
             if (lo.P) lo.zp = take((size_t)lo.P * 2 * d->H * tokens * 4);
         }
@@ -139,10 +153,26 @@ Layout layout(const gdn_desc *d, int op) {
         lo.M = take(bh * Nc * CHUNK * CHUNK * 4);
         lo.g = take(bh * Nc * CHUNK * 4);
     }
-    if (op == GDN_OP_SCAN_BACKWARD) {   // chunk-start states and the gradient at each chunk's end
+    if (op == GDN_OP_SCAN_BACKWARD || lbwd) {   // chunk-start states and the gradient at each chunk's end
         lo.sc = take(bh * Nc * D * D * 4);
         lo.dse = take(bh * Nc * D * D * 4);
         lo.bm = take(bwd_mats_bytes(bh * Nc));
+    }
+    if (lbwd) {
+        const int64_t P = packed_rows(d->H, d->dk), Mp = (tokens + 63) / 64 * 64, ab = act_bytes(d);
+        lo.Y = take(tokens * P * 4);
+        lo.YT = take(P * Mp * 4);
+        lo.XT = take(d->d * Mp * ab);
+        lo.WT = take(d->d * P * ab);
+        lo.gq = take(tokens * d->H * D * 4);
+        lo.gk = take(tokens * d->H * D * 4);
+        lo.gv = take(tokens * d->H * D * 4);
+        lo.gal = take(tokens * d->H * 4);
+        lo.gbe = take(tokens * d->H * 4);
+        lo.dhA = take(tokens * d->d * 4);
+        lo.dhB = take(tokens * d->d * 4);
+        lo.dW = take(d->d * P * 4);
+        lo.part = take((size_t)lb_drho_blocks((int)tokens) * d->d * 4);
     }
     if (act) {
         lo.R = take(tokens * 4);
@@ -170,7 +200,7 @@ struct gdn_timer {
 
 namespace {
 
-constexpr int N_STAGES = GDN_STAGE_BWD_PREP + 1;
+constexpr int N_STAGES = GDN_STAGE_BWD_GEMM + 1;
 thread_local LaunchEvents t_launch_events{nullptr, nullptr};
 gdn_timer *g_timers[N_STAGES] = {};
 
@@ -247,16 +277,17 @@ gdn_status gdn_weights_pack(const gdn_desc *desc, const void *Wq, const void *Wk
 }
 
 gdn_status gdn_workspace_bytes(const gdn_desc *desc, int op, size_t *bytes) {
-    if (op < GDN_OP_LOOP_PREFILL || op > GDN_OP_LOOP_PREFILL_ACT)
+    if (op < GDN_OP_LOOP_PREFILL || op > GDN_OP_LOOP_BACKWARD)
         return fail(GDN_ERR_UNSUPPORTED, "unknown op %d", op);
     gdn_status st = check_desc(desc, op == GDN_OP_LOOP_DECODE || op == GDN_OP_SCAN_DECODE);
     if (st != GDN_OK) return st;
     if ((op == GDN_OP_LOOP_PREFILL || op == GDN_OP_SCAN_PREFILL || op == GDN_OP_SCAN_BACKWARD ||
-         op == GDN_OP_LOOP_PREFILL_ACT) &&
+         op == GDN_OP_LOOP_PREFILL_ACT || op == GDN_OP_LOOP_BACKWARD) &&
         (st = check_prefill_grid(desc)) != GDN_OK)
         return st;
-    if (op == GDN_OP_SCAN_BACKWARD && desc->act == GDN_F32 && desc->dk == 128)
+    if ((op == GDN_OP_SCAN_BACKWARD || op == GDN_OP_LOOP_BACKWARD) && desc->act == GDN_F32 && desc->dk == 128)
         return fail(GDN_ERR_UNSUPPORTED, "the backward pass takes fp32 inputs with dk = 64 only");
+    if (op == GDN_OP_LOOP_BACKWARD && (st = check_loop_backward(desc)) != GDN_OK) return st;
     if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
     *bytes = layout(desc, op).total;
     return GDN_OK;
@@ -370,6 +401,110 @@ gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k,
     });
     if (e != hipSuccess) return hip_fail(e, "backward chunk launch");
     return GDN_OK;
+}
+
+gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,
+                             const float *h_loops, const float *dh, float *dh0, float *dWq, float *dWk, float *dWv,
+                             float *dwa, float *dwb, float *drho, void *ws, size_t ws_bytes, void *stream) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
+    if ((st = check_loop_backward(desc)) != GDN_OK) return st;
+    const bool f32 = desc->act == GDN_F32;
+    if (f32 && desc->dk == 128)
+        return fail(GDN_ERR_UNSUPPORTED, "the backward pass takes fp32 inputs with dk = 64 only");
+    REQUIRE_PTR(h0); REQUIRE_PTR(Wpack); REQUIRE_PTR(rho); REQUIRE_PTR(dh); REQUIRE_PTR(dh0);
+    REQUIRE_PTR(dWq); REQUIRE_PTR(dWk); REQUIRE_PTR(dWv); REQUIRE_PTR(dwa); REQUIRE_PTR(dwb); REQUIRE_PTR(drho);
+    if (desc->T > 1) REQUIRE_PTR(h_loops);
+    else OPTIONAL_PTR(h_loops);
+    if (dh0 == dh) return fail(GDN_ERR_SHAPE, "dh0 may not alias dh");
+    const Layout lo = layout(desc, GDN_OP_LOOP_BACKWARD);
+    if (!ws || ws_bytes < lo.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
+    if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+
+    const hipStream_t s = (hipStream_t)stream;
+    const int B = desc->B, L = desc->L, H = desc->H, D = desc->dk, d = desc->d, T = desc->T;
+    const int M = B * L, Mp = (M + 63) / 64 * 64;
+    float *zp = lo.P ? (float *)at(ws, lo.zp) : nullptr;   // gate partials, as in the forward
+    bf16 *xb = f32 ? nullptr : (bf16 *)at(ws, lo.x);
+    const int P = (int)packed_rows(H, D);
+    const int64_t qkvp = qkv_rows_padded(H, D);
+    void *q = at(ws, lo.q), *k = at(ws, lo.k), *v = at(ws, lo.v);
+    float *al = (float *)at(ws, lo.alpha), *be = (float *)at(ws, lo.beta);
+    float *Y = (float *)at(ws, lo.Y), *YT = (float *)at(ws, lo.YT), *dW = (float *)at(ws, lo.dW);
+    void *XT = at(ws, lo.XT), *WT = at(ws, lo.WT);
+    float *gq = (float *)at(ws, lo.gq), *gk = (float *)at(ws, lo.gk), *gv = (float *)at(ws, lo.gv);
+    float *gal = (float *)at(ws, lo.gal), *gbe = (float *)at(ws, lo.gbe), *part = (float *)at(ws, lo.part);
+    float *bufs[2] = {(float *)at(ws, lo.dhA), (float *)at(ws, lo.dhB)};
+    float *sc = (float *)at(ws, lo.sc), *dse = (float *)at(ws, lo.dse), *bm = (float *)at(ws, lo.bm);
+    const int wmode = f32 ? OPND_F32_SPLIT : OPND_BF16;
+    const int64_t tokd = (int64_t)M * d;
+
+    hipError_t e = launch_transpose(f32, f32, Wpack, d, P, d, WT, P, P, s);   // W^T [d][P]
+    if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
+    if ((e = launch_fill_zero(dW, (int64_t)d * P, s)) != hipSuccess) return hip_fail(e, "fill launch");
+    for (int tau = T - 1; tau >= 0; --tau) {
+        // loop tau + 1 of the forward: input h^(tau), incoming gradient dL/dh^(tau+1)
+        const bool hp_f32 = f32 || tau > 0;
+        const void *hp = tau == 0 ? h0 : (const void *)(h_loops + (int64_t)(tau - 1) * tokd);
+        const float *g_in = tau == T - 1 ? dh : bufs[(T - 2 - tau) & 1];
+        float *g_out = tau == 0 ? dh0 : bufs[(T - 1 - tau) & 1];
+        // The loop's operand (bf16(h) for bf16 workloads, rounded as the forward's carry rounds it) and its
+        // q, k, v and gates from the forward's own kernels, launched as gdn_loop_prefill launches them: the
+        // same values bit for bit, so this is the gradient of the forward that produced h_loops.
+        const void *x = hp;
+        if (!f32 && tau > 0) {
+            if ((e = launch_lb_round(tokd, (const float *)hp, xb, s)) != hipSuccess) return hip_fail(e, "round launch");
+            x = xb;
+        }
+        e = project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo, desc->norm_eps, zp, s);
+        if (e != hipSuccess) return hip_fail(e, "projection launch");
+        // the raw projections in fp32 (the normalisation's and the gates' gradients need them)
+        e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+            return launch_gemm_nt(f32 ? OPND_F32_SPLIT : OPND_BF16, wmode, EPI_STORE, x, d, Wpack, d, M, P, d, Y, P,
+                                  nullptr, nullptr, 0, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "projection recompute launch");
+        // the scan backward from S = 0 with dO = dL/dh^(tau+1) (the mixer output is h's width); with gate
+        // partials the prep forms alpha and beta into their workspace regions, as in the forward
+        CarryOut out{nullptr, nullptr, false, nullptr, nullptr, nullptr, sc};
+        st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
+                         nullptr, nullptr, out, ws, lo, s);
+        if (st != GDN_OK) return st;
+        e = timed(GDN_STAGE_BWD_PREP, s, [&] { return launch_bwd_prep(f32, B, L, H, D, q, k, al, be, bm, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+        e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
+            return launch_bwd_carry(f32, B, L, H, D, q, k, be, g_in, nullptr, bm, gv, dse, nullptr, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "backward carry launch");
+        e = timed(GDN_STAGE_BWD_CHUNK, s, [&] {
+            return launch_bwd_chunk(f32, B, L, H, D, q, k, v, al, be, g_in, gv, sc, dse, bm, gq, gk, gal, gbe, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "backward chunk launch");
+        // through the normalisation and the gates: Y <- dY
+        e = launch_lb_epilogue_grad(M, H, D, Y, P, qkvp, desc->norm_eps, desc->alpha_lo, gq, gk, gv, gal, gbe, s);
+        if (e != hipSuccess) return hip_fail(e, "epilogue gradient launch");
+        e = launch_lb_drho(M, d, g_in, hp, hp_f32, part, drho + (int64_t)tau * d, s);
+        if (e != hipSuccess) return hip_fail(e, "rho gradient launch");
+        // dL/dh^(tau) = rho_tau (.) dL/dh^(tau+1) + dY W
+        e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+            return launch_gemm_nt(OPND_F32_SPLIT, wmode, EPI_RESID, Y, P, WT, P, M, d, P, g_out, d,
+                                  rho + (int64_t)tau * d, g_in, d, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "input gradient launch");
+        // dW^T [d][P] += x^T dY
+        if ((e = launch_transpose(f32, f32, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess ||
+            (e = launch_transpose(true, true, Y, P, M, P, YT, Mp, Mp, s)) != hipSuccess)
+            return hip_fail(e, "transpose launch");
+        e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+            return launch_gemm_nt(f32 ? OPND_F32_SPLIT : OPND_BF16, OPND_F32_SPLIT, EPI_ACCUM, XT, Mp, YT, Mp, d, P,
+                                  Mp, dW, P, nullptr, nullptr, 0, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "weight gradient launch");
+    }
+    e = launch_lb_unpack(d, H, D, dW, P, qkvp, dWq, dWk, dWv, dwa, dwb, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "weight gradient unpack launch");
 }
 
 gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k, const void *v,
@@ -530,7 +665,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BWD_PREP || stage == 4 || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BWD_GEMM || stage == 4 || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

@@ -243,7 +243,7 @@ def loop_prefill(h0, Wq, Wk, Wv, wa, wb, rho, H: int, dk: int, dv: int,
 
 
 def loop_backward(h0, Wq, Wk, Wv, wa, wb, rho, loops, dh, H: int, dk: int, dv: int, alpha_lo: float, act: str,
-                  eps: float = 1e-6):
+                  eps: float = 1e-6, qkv=None):
     """Gradients of ``loop_prefill`` (T weight-tied loops, LT2 Section 2; trained through, Appendix C) for an
     incoming gradient dh = dL/dh^(T) [B, L, d].
 
@@ -262,7 +262,10 @@ def loop_backward(h0, Wq, Wk, Wv, wa, wb, rho, loops, dh, H: int, dk: int, dv: i
         dh <- rho_tau (.) dh + dqr Wq^T + dkr Wk^T + dv Wv^T + da wa^T + db wb^T
     For bf16 workloads the roundings of the forward (x, and q, k, v after normalisation) pass the gradient
     through unchanged: the scan backward is evaluated at the rounded q, k, v, everything else at the unrounded
-    values.  Returns dict(dh0 [B,L,d], dWq, dWk [d,H*dk], dWv [d,H*dv], dwa, dwb [d,H], drho [T,d]).  fp64.
+    values.  ``qkv``, if given, holds for each loop 1..T the rounded (q, k, v) ([B*L, H, dk] / [.., dv]) to use
+    there instead of this function's own roundings: a value within summation error of a bf16 rounding boundary
+    may round either way in a valid forward, and the gradient depends on the side it fell.  Returns
+    dict(dh0 [B,L,d], dWq, dWk [d,H*dk], dWv [d,H*dv], dwa, dwb [d,H], drho [T,d]).  fp64.
     """
     h0 = _f64(h0)
     rho = _f64(rho)
@@ -292,6 +295,8 @@ def loop_backward(h0, Wq, Wk, Wv, wa, wb, rho, loops, dh, H: int, dk: int, dv: i
             als, bes = round_f32(alpha), round_f32(beta)
         else:
             qs, ks, vs, als, bes = qn, kn, vr, alpha, beta
+        if qkv is not None:
+            qs, ks, vs = (_f64(t).reshape(M, H, -1) for t in qkv[tau])
         gs = scan_backward(qs.reshape(B, L, H, dk), ks.reshape(B, L, H, dk), vs.reshape(B, L, H, dv),
                            als.reshape(B, L, H), bes.reshape(B, L, H), g.reshape(B, L, H, dv))
         dq = gs["dq"].reshape(M, H, dk)

@@ -129,6 +129,24 @@ def test_workspace_sizes():
         0, chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats))
     st, _ = _ws_status(gl.make_desc(B, L, H, D, D, act=gl.GDN_F32), gl.GDN_OP_SCAN_BACKWARD)
     assert st == -3   # fp32 inputs with 128-wide heads
+    # loop backward: the loop prefill's regions (q, k, v, alpha, beta, the bf16 operand; gate partials from 1024
+    # tokens), the scan backward's, then the raw projections
+    # [M][P] and their transpose [P][Mp] (Mp = M rounded up to 64), x^T [d][Mp] and W^T [d][P] in the activation
+    # dtype, the scan gradients, two dh buffers, the weight-gradient accumulator [d][P] and the rho partials
+    for act, eb in [(gl.GDN_BF16, 2), (gl.GDN_F32, 4)]:
+        B, L, H, D = 2, 130, 3, (128 if act == gl.GDN_BF16 else 64)
+        d, tok, Nc = H * D, B * L, (L + 63) // 64
+        P = (H * 3 * D + 127) // 128 * 128 + 128
+        Mp = (tok + 63) // 64 * 64
+        chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+        mats = B * H * Nc * (3 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4)
+        xb = up(tok * d * 2) if act == gl.GDN_BF16 else 0   # the bf16 loop operand
+        exp = (3 * up(tok * H * D * eb) + 2 * up(tok * H * 4) + xb + chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats)
+               + up(tok * P * 4) + up(P * Mp * 4) + up(d * Mp * eb) + up(d * P * eb) + 3 * up(tok * H * D * 4)
+               + 2 * up(tok * H * 4) + 2 * up(tok * d * 4) + up(d * P * 4) + up(((tok + 127) // 128) * d * 4))
+        assert _ws_status(gl.make_desc(B, L, H, D, D, act=act), gl.GDN_OP_LOOP_BACKWARD) == (0, exp)
+    st, _ = _ws_status(gl.make_desc(B, L, H, 128, 128, act=gl.GDN_F32), gl.GDN_OP_LOOP_BACKWARD)
+    assert st == -3
 
 
 @pytest.mark.parametrize("op", [gl.GDN_OP_LOOP_PREFILL, gl.GDN_OP_LOOP_DECODE])
@@ -206,6 +224,17 @@ def test_alignment_and_workspace_rejected_before_launch(lib):
     assert st == -2  # s_final aliases s_init
     st = lib.gdn_loop_prefill(ctypes.byref(desc), good, good, good, good, None, None, None, 0, None)
     assert st == -2  # h_out aliases h0
+    # loop backward: h_loops required for T > 1, dh0 may not alias dh, then the workspace size
+    o = [ctypes.c_void_p(0x100000 + 0x1000 * i) for i in range(12)]
+    st = lib.gdn_loop_backward(ctypes.byref(desc), o[0], o[1], o[2], None, o[3], o[4], *o[5:11], good, 1 << 40, None)
+    assert st == -1 and "h_loops" in gl.gdn_last_error()
+    st = lib.gdn_loop_backward(ctypes.byref(desc), o[0], o[1], o[2], o[11], o[3], o[3], *o[5:11], good, 1 << 40, None)
+    assert st == -2 and "alias" in gl.gdn_last_error()
+    st = lib.gdn_loop_backward(ctypes.byref(desc), o[0], o[1], o[2], o[11], o[3], o[4], *o[5:11], good, 16, None)
+    assert st == -4 and "workspace" in gl.gdn_last_error()
+    st = lib.gdn_loop_backward(ctypes.byref(gl.make_desc(1, 64, 2, 128, 128, act=gl.GDN_F32)), o[0], o[1], o[2],
+                               o[11], o[3], o[4], *o[5:11], good, 1 << 40, None)
+    assert st == -3
 
 
 def test_binding_checks_tensor_sizes_on_host():
@@ -219,7 +248,7 @@ def test_binding_checks_tensor_sizes_on_host():
 
 def test_timer_validation(lib):
     h = ctypes.c_void_p()
-    assert lib.gdn_timer_create(9, 4, ctypes.byref(h)) == -2
+    assert lib.gdn_timer_create(10, 4, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(4, 4, ctypes.byref(h)) == -2   # not a stage
     assert lib.gdn_timer_create(0, 0, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(0, 4, None) == -1

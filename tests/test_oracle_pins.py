@@ -567,3 +567,26 @@ def test_loop_backward_zero_values_closed_form(act):
         assert np.allclose(g["drho"][t], ref, rtol=1e-12, atol=1e-14)
     for key in ("dWq", "dWk", "dwa", "dwb"):
         assert np.all(g[key] == 0), key
+
+
+def test_loop_backward_given_operands_are_used_for_the_scan():
+    """The rounded q, k, v handed in (per loop) replace the oracle's own: handing in its own roundings gives the
+    same gradients bit for bit, and handing in q, k, v moved by one bf16 step at one position changes them."""
+    x, s = _tiny_loop_inputs(81, B=1, L=20, H=2, dk=4, dv=4, T=2)
+    x["h0"] = oracle.round_bf16(x["h0"])
+    dh = np.random.default_rng(82).standard_normal(x["h0"].shape)
+    fwd = oracle.loop_prefill(**x, **s, alpha_lo=0.1, act="bf16", keep_loops=True)
+    ins = [x["h0"]] + fwd["loops"][:-1]
+    own = []
+    for h in ins:
+        q, k, v, _, _ = oracle.project(oracle.round_bf16(h.reshape(20, 8)), x["Wq"], x["Wk"], x["Wv"], x["wa"],
+                                       x["wb"], 2, 4, 4, 0.1, "bf16")
+        own.append((q, k, v))
+    base = oracle.loop_backward(**x, loops=fwd["loops"], dh=dh, **s, alpha_lo=0.1, act="bf16")
+    same = oracle.loop_backward(**x, loops=fwd["loops"], dh=dh, **s, alpha_lo=0.1, act="bf16", qkv=own)
+    for key in base:
+        assert np.array_equal(base[key], same[key]), key
+    moved = [tuple(t.copy() for t in o) for o in own]
+    moved[1][1][5, 0, 2] = moved[1][1][5, 0, 2] * (1 + 2.0 ** -7)   # k of loop 2, one element, one bf16 step
+    diff = oracle.loop_backward(**x, loops=fwd["loops"], dh=dh, **s, alpha_lo=0.1, act="bf16", qkv=moved)
+    assert not np.array_equal(diff["dWk"], base["dWk"])
