@@ -341,7 +341,7 @@ def bench_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     stages = {"fwd_prep": gl.GDN_STAGE_SCAN_PREP, "fwd_carry": gl.GDN_STAGE_SCAN_CARRY,
-              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
+              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_ops": gl.GDN_STAGE_BWD_OPS, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
               "bwd_chunk": gl.GDN_STAGE_BWD_CHUNK}
     timers = {k: gl.gdn_timer_create(v, n) for k, v in stages.items()}
     for t in timers.values():
@@ -447,7 +447,7 @@ def bench_loop_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     stages = {"gemm": gl.GDN_STAGE_BWD_GEMM, "fwd_prep": gl.GDN_STAGE_SCAN_PREP, "fwd_carry": gl.GDN_STAGE_SCAN_CARRY,
-              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
+              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_ops": gl.GDN_STAGE_BWD_OPS, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
               "bwd_chunk": gl.GDN_STAGE_BWD_CHUNK}
     timers = {k: gl.gdn_timer_create(v, 3 * n * T) for k, v in stages.items()}
     for t in timers.values():

@@ -321,12 +321,14 @@ const char *gdn_version(void);
  * output pass that the carry now performs, and gdn_timer_create rejects it). */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
        GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5, GDN_STAGE_BWD_CARRY = 6, GDN_STAGE_BWD_CHUNK = 7,
-       GDN_STAGE_BWD_PREP = 8, GDN_STAGE_BWD_GEMM = 9 };
+       GDN_STAGE_BWD_PREP = 8, GDN_STAGE_BWD_GEMM = 9, GDN_STAGE_BWD_OPS = 10 };
 /* GDN_STAGE_BWD_GEMM times the three products of each loop of
  * gdn_loop_backward (the projections recomputed, the input gradient and the
  * weight gradient). */
-/* GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_CARRY and GDN_STAGE_BWD_CHUNK time the
- * three kernels of gdn_scan_backward that follow its forward recomputation
+/* GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_OPS, GDN_STAGE_BWD_CARRY and
+ * GDN_STAGE_BWD_CHUNK time the four kernels of the scan backward (in
+ * gdn_scan_backward and in each loop of gdn_loop_backward) that follow its
+ * forward recomputation
  * (whose prep and carry are timed as GDN_STAGE_SCAN_PREP and
  * GDN_STAGE_SCAN_CARRY). */
 /* GDN_STAGE_SCAN_CARRY times the carry kernel, which computes the chunk outputs

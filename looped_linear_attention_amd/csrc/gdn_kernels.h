@@ -149,21 +149,24 @@ hipError_t launch_act_rows(int M, const int *halt, int tau, int *rows, int *coun
 hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,
                              ChunkWs ws, const float *s_init, float *s_final, CarryOut out, hipStream_t s);
 
-// Backward of the chunkwise scan (fp32 arithmetic).  launch_bwd_prep forms
-// per (b, h, chunk) T, P, A, the log-cumsum of alpha, gamma and c in `mats`
-// (bwd_mats_bytes for B*H*Nc chunks).  The reverse carry walks the chunks of
-// each (b, h, 16-column slice) backwards: dE = diag(beta) T^T (P^T dO + diag(c)
-// K dS') (written to dv), dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma)
-// dE, with each chunk's dS' kept in ds_end [B, H, Nc, D, D] and ds_init given
-// the final dS when non-null.  The chunk kernel then forms dq, dk, dalpha,
-// dbeta per (b, h, chunk) from the chunk-start states s_chunks and ds_end.
-// fp32 inputs need D = 64.
-size_t bwd_mats_bytes(int64_t chunks);
+// Backward of the chunkwise scan.  launch_bwd_prep forms per (b, h, chunk) T,
+// P, A, the log-cumsum of alpha, gamma and c in `mats` (bwd_mats_bytes for
+// B*H*Nc chunks of width D); launch_bwd_ops the reverse carry's operands from
+// them and dO: W^T = diag(beta) T^T diag(c) K (split bf16), K^T, Q^T (bf16) and
+// M^T dO = diag(beta) T^T P^T dO (fp32).  The reverse carry walks the chunks of
+// each (b, h, 16-column slice) backwards on MFMA: dE = M^T dO + W^T dS'
+// (written to dv), dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dE,
+// with each chunk's dS' kept in ds_end [B, H, Nc, D, D] and ds_init given the
+// final dS when non-null.  The chunk kernel then forms dq, dk, dalpha, dbeta
+// per (b, h, chunk) from the chunk-start states s_chunks and ds_end.  fp32
+// inputs need D = 64.
+size_t bwd_mats_bytes(int64_t chunks, int D);
 hipError_t launch_bwd_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *alpha,
                            const float *beta, float *mats, hipStream_t s);
-hipError_t launch_bwd_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
-                            const float *d_o, const float *d_sfinal, float *mats, float *dv, float *ds_end,
-                            float *ds_init, hipStream_t s);
+hipError_t launch_bwd_ops(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
+                          const float *d_o, float *mats, hipStream_t s);
+hipError_t launch_bwd_carry(bool f32, int B, int L, int H, int D, const float *d_o, const float *d_sfinal,
+                            float *mats, float *dv, float *ds_end, float *ds_init, hipStream_t s);
 hipError_t launch_bwd_chunk(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const float *d_o, const float *dv,
                             const float *s_chunks, const float *ds_end, float *mats, float *dq, float *dk,

@@ -156,7 +156,7 @@ Layout layout(const gdn_desc *d, int op) {
     if (op == GDN_OP_SCAN_BACKWARD || lbwd) {   // chunk-start states and the gradient at each chunk's end
         lo.sc = take(bh * Nc * D * D * 4);
         lo.dse = take(bh * Nc * D * D * 4);
-        lo.bm = take(bwd_mats_bytes(bh * Nc));
+        lo.bm = take(bwd_mats_bytes(bh * Nc, (int)D));
     }
     if (lbwd) {
         const int64_t P = packed_rows(d->H, d->dk), Mp = (tokens + 63) / 64 * 64, ab = act_bytes(d);
@@ -200,7 +200,7 @@ struct gdn_timer {
 
 namespace {
 
-constexpr int N_STAGES = GDN_STAGE_BWD_GEMM + 1;
+constexpr int N_STAGES = GDN_STAGE_BWD_OPS + 1;
 thread_local LaunchEvents t_launch_events{nullptr, nullptr};
 gdn_timer *g_timers[N_STAGES] = {};
 
@@ -391,8 +391,10 @@ gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k,
         return launch_bwd_prep(f32, B, L, H, D, q, k, alpha, beta, bm, s);
     });
     if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+    e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, beta, d_o, bm, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward carry operands launch");
     e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
-        return launch_bwd_carry(f32, B, L, H, D, q, k, beta, d_o, d_sfinal, bm, dv, dse, ds_init, s);
+        return launch_bwd_carry(f32, B, L, H, D, d_o, d_sfinal, bm, dv, dse, ds_init, s);
     });
     if (e != hipSuccess) return hip_fail(e, "backward carry launch");
     e = timed(GDN_STAGE_BWD_CHUNK, s, [&] {
@@ -474,8 +476,10 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         if (st != GDN_OK) return st;
         e = timed(GDN_STAGE_BWD_PREP, s, [&] { return launch_bwd_prep(f32, B, L, H, D, q, k, al, be, bm, s); });
         if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+        e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, be, g_in, bm, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward carry operands launch");
         e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
-            return launch_bwd_carry(f32, B, L, H, D, q, k, be, g_in, nullptr, bm, gv, dse, nullptr, s);
+            return launch_bwd_carry(f32, B, L, H, D, g_in, nullptr, bm, gv, dse, nullptr, s);
         });
         if (e != hipSuccess) return hip_fail(e, "backward carry launch");
         e = timed(GDN_STAGE_BWD_CHUNK, s, [&] {
@@ -665,7 +669,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BWD_GEMM || stage == 4 || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BWD_OPS || stage == 4 || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

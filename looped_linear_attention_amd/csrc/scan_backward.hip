@@ -44,15 +44,23 @@ namespace {
 constexpr int C = 64;
 
 // Per-chunk matrices of the backward, fp32: T, P, A [64][64] row-major, the
-// log-cumsum lg [64] (fp64), gamma = e^lg and c = e^(lg_last - lg) [64].
+// log-cumsum lg [64] (fp64), gamma = e^lg and c = e^(lg_last - lg) [64]; and
+// the operands of the reverse carry: W^T = diag(beta) T^T diag(c) K [64][D]
+// as bf16 hi and lo planes, K^T and Q^T [D][64] as bf16 hi (and, for fp32
+// inputs, lo) planes, and M^T dO = diag(beta) T^T P^T dO [64][D] fp32.
 struct BwdMats {
     float *T, *P, *A;
     double *lg;
     float *gam, *c;
+    bf16 *Wth, *Wtl, *Kth, *Ktl, *Qth, *Qtl;
+    float *MtdO;
 };
-constexpr size_t BWD_MATS_PER_CHUNK = 3 * C * C * 4 + C * 8 + 2 * C * 4;   // bytes per chunk
+// bytes per chunk
+__host__ __device__ constexpr size_t bwd_mats_per_chunk(int D) {
+    return 3 * C * C * 4 + C * 8 + 2 * C * 4 + (size_t)6 * D * C * 2 + (size_t)C * D * 4;
+}
 // The regions of a BwdMats block for `chunks` chunks, each array for all chunks in turn.
-BwdMats bwd_mats(float *base, int64_t chunks) {
+BwdMats bwd_mats(float *base, int64_t chunks, int D) {
     BwdMats m;
     m.T = base;
     m.P = m.T + chunks * C * C;
@@ -60,6 +68,15 @@ BwdMats bwd_mats(float *base, int64_t chunks) {
     m.lg = reinterpret_cast<double *>(m.A + chunks * C * C);
     m.gam = reinterpret_cast<float *>(m.lg + chunks * C);
     m.c = m.gam + chunks * C;
+    bf16 *b = reinterpret_cast<bf16 *>(m.c + chunks * C);
+    const int64_t plane = chunks * C * D;
+    m.Wth = b;
+    m.Wtl = b + plane;
+    m.Kth = b + 2 * plane;
+    m.Ktl = b + 3 * plane;
+    m.Qth = b + 4 * plane;
+    m.Qtl = b + 5 * plane;
+    m.MtdO = reinterpret_cast<float *>(b + 6 * plane);
     return m;
 }
 
@@ -147,96 +164,281 @@ __global__ __launch_bounds__(BP_THREADS) void k_bwd_prep(const TIn *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// reverse carry: one workgroup per (b, h, 16-column slice), chunks in reverse
+// carry operands: one workgroup per (b, h, chunk), in 32-column blocks
 // ---------------------------------------------------------------------------
-constexpr int BC_THREADS = 256;
+// W^T[m][i] = beta_m sum_{r >= m} T[r][m] c_r K[r][i], (P^T dO)[m][i] =
+// sum_{r >= m} P[r][m] dO[r][i], M^T dO[m][i] = beta_m sum_{r >= m} T[r][m]
+// (P^T dO)[r][i]; K^T and Q^T copied transposed.  Rows past the end of the
+// sequence are zero (beta = 0 there).
+constexpr int BO_THREADS = 256;
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(BC_THREADS) void k_bwd_carry(
-    const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ d_o,
-    BwdMats bm, const float *__restrict__ d_sfinal, int L, int H, int Nc, float *__restrict__ dv,
-    float *__restrict__ ds_end, float *__restrict__ ds_init) {
-    __shared__ float Tf[C][C + 1], Pf[C][C + 1];
-    __shared__ float Kf[C][D + 1], Qf[C][D + 1];
-    __shared__ float dOs[C][17], dUs[C][17], dEs[C][17], dSs[D][17];
-    __shared__ float gs[C], cs[C], bs[C];
+__global__ __launch_bounds__(BO_THREADS) void k_bwd_ops(const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                        const float *__restrict__ beta, const float *__restrict__ d_o,
+                                                        int L, int H, int Nc, BwdMats bm) {
+    constexpr bool SPLIT_KQ = sizeof(TIn) == 4;
+    __shared__ float Ts[C][C + 1], Ps[C][C + 1];
+    __shared__ float Kc[C][33], Kr[C][33], Qr[C][33], dOb[C][33], PdO[C][33];
+    __shared__ float bes[C];
     const int t = threadIdx.x;
+    const int h = blockIdx.x % H, chunk = blockIdx.x / H, b = blockIdx.y;
+    const int c0 = chunk * C, nvalid = min(C, L - c0);
+    const int64_t tok0 = (int64_t)b * L + c0;
+    const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
+    for (int n = t; n < C * C; n += BO_THREADS) {
+        Ts[n / C][n % C] = bm.T[cid * C * C + n];
+        Ps[n / C][n % C] = bm.P[cid * C * C + n];
+    }
+    if (t < C) bes[t] = t < nvalid ? beta[(tok0 + t) * H + h] : 0.f;
+    const int m = t >> 2, i8 = (t & 3) * 8;   // this thread's row and 8 columns of a block
+    for (int cb = 0; cb < D; cb += 32) {
+        __syncthreads();   // the previous block's readers are done
+        for (int n = t; n < C * 32; n += BO_THREADS) {
+            const int r = n >> 5, i = n & 31;
+            const bool ok = r < nvalid;
+            const int64_t off = ((tok0 + (ok ? r : 0)) * H + h) * D + cb + i;
+            const float kv = ok ? to_f32(k[off]) : 0.f;
+            Kr[r][i] = kv;
+            Kc[r][i] = kv * bm.c[cid * C + r];
+            Qr[r][i] = ok ? to_f32(q[off]) : 0.f;
+            dOb[r][i] = ok ? d_o[off] : 0.f;
+        }
+        __syncthreads();
+        float w[8] = {}, pd[8] = {};
+        for (int r = m; r < C; ++r) {
+            const float tr = Ts[r][m], pr = Ps[r][m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                w[e] = fmaf(tr, Kc[r][i8 + e], w[e]);
+                pd[e] = fmaf(pr, dOb[r][i8 + e], pd[e]);
+            }
+        }
+        const float bm_ = bes[m];
+        {
+            float wv[8];
+            bf16 hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wv[e] = bm_ * w[e];
+                PdO[m][i8 + e] = pd[e];
+            }
+            split_bf16<8>(wv, hi, lo);
+            const int64_t o = (cid * C + m) * D + cb + i8;
+            *reinterpret_cast<bf16x8 *>(bm.Wth + o) = pack8(hi);
+            *reinterpret_cast<bf16x8 *>(bm.Wtl + o) = pack8(lo);
+        }
+        // K^T, Q^T of the block: [i][m]
+        for (int n = t; n < 32 * C; n += BO_THREADS) {
+            const int i = n >> 6, r = n & 63;
+            const int64_t o = (cid * D + cb + i) * C + r;
+            if constexpr (SPLIT_KQ) {
+                const float kv[2] = {Kr[r][i], Qr[r][i]};
+                bf16 hi[2], lo[2];
+                split_bf16<2>(kv, hi, lo);
+                bm.Kth[o] = hi[0];
+                bm.Ktl[o] = lo[0];
+                bm.Qth[o] = hi[1];
+                bm.Qtl[o] = lo[1];
+            } else {
+                bm.Kth[o] = (bf16)Kr[r][i];
+                bm.Qth[o] = (bf16)Qr[r][i];
+            }
+        }
+        __syncthreads();
+        float mo[8] = {};
+        for (int r = m; r < C; ++r) {
+            const float tr = Ts[r][m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mo[e] = fmaf(tr, PdO[r][i8 + e], mo[e]);
+        }
+        float4 *dst = reinterpret_cast<float4 *>(bm.MtdO + (cid * C + m) * D + cb + i8);
+        dst[0] = float4{bm_ * mo[0], bm_ * mo[1], bm_ * mo[2], bm_ * mo[3]};
+        dst[1] = float4{bm_ * mo[4], bm_ * mo[5], bm_ * mo[6], bm_ * mo[7]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reverse carry: one workgroup (4 waves) per (b, h, 16-column slice), chunks in reverse
+// ---------------------------------------------------------------------------
+// The slice's state gradient dS' [D][16] lives in registers in the 16x16x32
+// MFMA output layout: wave w holds rows D/4 w .. D/4 (w+1) - 1, lane (lr, lg)
+// = (lane % 16, lane / 16) the rows 16 rt + 4 lg + jj of its row tiles rt at
+// column lr.  Per chunk:
+//   1. dS' (split) into LDS as [column][row]; dS' out to ds_end.   barrier A
+//   2. Y = W^T dS' (wave w: token rows 16 w ..; 3 passes), dE = M^T dO + Y
+//      out to dv; -gamma (.) dE and gamma (.) dO (split) into LDS as
+//      [column][token].                                            barrier B
+//   3. dS = gamma_C dS' + Q^T (gamma dO) - K^T (gamma dE) on the wave's rows.
+// The next chunk's operands (W^T, K^T, Q^T fragments, M^T dO, dO, gamma) are
+// loaded into registers one chunk ahead.
+constexpr int BC_THREADS = 256;
+
+template <int D, bool SPLIT_KQ>
+struct BwdCarryOps {
+    static constexpr int RT = D / 64;   // 16-row tiles of dS' per wave
+    static constexpr int KS = D / 32;   // k-steps of W^T dS'
+    bf16x8 wh[KS], wl[KS];              // W^T rows 16 w + lr, k = 32 s + 8 lg ..
+    bf16x8 kh[RT][2], qh[RT][2];        // K^T, Q^T rows of the wave, k = m = 32 s + 8 lg ..
+    bf16x8 kl[SPLIT_KQ ? RT : 1][2], ql[SPLIT_KQ ? RT : 1][2];
+    float mt[4], od[4], g[4];           // M^T dO, dO and gamma at token rows 16 w + 4 lg + jj, column lr
+    float gC;
+};
+
+template <int D, bool SPLIT_KQ>
+__device__ __forceinline__ void bwd_carry_load(BwdCarryOps<D, SPLIT_KQ> &o, const BwdMats &bm, const float *d_o,
+                                               int64_t cid, int64_t tok0, int nvalid, int H, int h, int col0,
+                                               int wave, int lr, int lg) {
+    using G = BwdCarryOps<D, SPLIT_KQ>;
+    const int mrow = 16 * wave + lr;
+#pragma unroll
+    for (int s = 0; s < G::KS; ++s) {
+        const int64_t off = (cid * C + mrow) * D + 32 * s + 8 * lg;
+        o.wh[s] = *reinterpret_cast<const bf16x8 *>(bm.Wth + off);
+        o.wl[s] = *reinterpret_cast<const bf16x8 *>(bm.Wtl + off);
+    }
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int i = (D / 4) * wave + 16 * rt + lr;
+            const int64_t off = (cid * D + i) * C + 32 * s + 8 * lg;
+            o.kh[rt][s] = *reinterpret_cast<const bf16x8 *>(bm.Kth + off);
+            o.qh[rt][s] = *reinterpret_cast<const bf16x8 *>(bm.Qth + off);
+            if constexpr (SPLIT_KQ) {
+                o.kl[rt][s] = *reinterpret_cast<const bf16x8 *>(bm.Ktl + off);
+                o.ql[rt][s] = *reinterpret_cast<const bf16x8 *>(bm.Qtl + off);
+            }
+        }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int m = 16 * wave + 4 * lg + jj;
+        o.mt[jj] = bm.MtdO[(cid * C + m) * D + col0 + lr];
+        o.od[jj] = m < nvalid ? d_o[((tok0 + m) * H + h) * D + col0 + lr] : 0.f;
+        o.g[jj] = bm.gam[cid * C + m];
+    }
+    o.gC = bm.gam[cid * C + C - 1];
+}
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(BC_THREADS) void k_bwd_carry(const float *__restrict__ d_o, BwdMats bm,
+                                                          const float *__restrict__ d_sfinal, int L, int H, int Nc,
+                                                          float *__restrict__ dv, float *__restrict__ ds_end,
+                                                          float *__restrict__ ds_init) {
+    constexpr bool SPLIT_KQ = sizeof(TIn) == 4;
+    using G = BwdCarryOps<D, SPLIT_KQ>;
+    constexpr int SLD = D + 8, MLD = C + 8;          // LDS row strides (bf16): 16-byte aligned rows
+    __shared__ bf16 dSh[16 * SLD], dSl[16 * SLD];    // dS' as [column][row]
+    __shared__ bf16 gEh[16 * MLD], gEl[16 * MLD];    // -gamma (.) dE as [column][token]
+    __shared__ bf16 gOh[16 * MLD], gOl[16 * MLD];    // gamma (.) dO as [column][token]
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 15, lg = lane >> 4;
     const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
     const int col0 = slice * 16;
     const int64_t tokb = (int64_t)b * L;
     const int64_t cidb = ((int64_t)b * H + h) * Nc;
     const int64_t sbase = ((int64_t)b * H + h) * D * D;
-    // this thread's state elements dS[i][j]: j = t % 16, i = t / 16 + 16 a
-    constexpr int RA = D / 16;
-    const int jc = t & 15, i0 = t >> 4;
-    float dS[RA];
-#pragma unroll
-    for (int a = 0; a < RA; ++a) dS[a] = d_sfinal ? d_sfinal[sbase + (int64_t)(i0 + 16 * a) * D + col0 + jc] : 0.f;
+    const int rbase = (D / 4) * wave;
 
-    for (int c = Nc - 1; c >= 0; --c) {
-        const int c0 = c * C, nvalid = min(C, L - c0);
+    f32x4 dS[G::RT];
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int i = rbase + 16 * rt + 4 * lg + jj;
+            dS[rt][jj] = d_sfinal ? d_sfinal[sbase + (int64_t)i * D + col0 + lr] : 0.f;
+        }
+
+    G ops[2];
+    auto load = [&](G &o, int c) {
+        bwd_carry_load<D, SPLIT_KQ>(o, bm, d_o, cidb + c, tokb + (int64_t)c * C, min(C, L - c * C), H, h, col0,
+                                    wave, lr, lg);
+    };
+    auto step = [&](const G &o, int c) {
         const int64_t cid = cidb + c;
-        // stage the chunk: T, P, gamma, c, beta, K, Q, the dO slice; dS' (the current state) to LDS and out
-        for (int n = t; n < C * C; n += BC_THREADS) {
-            Tf[n / C][n % C] = bm.T[cid * C * C + n];
-            Pf[n / C][n % C] = bm.P[cid * C * C + n];
-        }
-        for (int n = t; n < C * D; n += BC_THREADS) {
-            const int r = n / D, i = n % D;
-            const bool ok = r < nvalid;
-            const int64_t off = ((tokb + c0 + (ok ? r : 0)) * H + h) * D + i;
-            Kf[r][i] = ok ? to_f32(k[off]) : 0.f;
-            Qf[r][i] = ok ? to_f32(q[off]) : 0.f;
-        }
-        for (int n = t; n < C * 16; n += BC_THREADS) {
-            const int r = n / 16, j = n % 16;
-            dOs[r][j] = r < nvalid ? d_o[((tokb + c0 + r) * H + h) * D + col0 + j] : 0.f;
-        }
-        if (t < C) {
-            gs[t] = bm.gam[cid * C + t];
-            cs[t] = bm.c[cid * C + t];
-            bs[t] = t < nvalid ? beta[(tokb + c0 + t) * H + h] : 0.f;
-        }
+        const int c0 = c * C, nvalid = min(C, L - c0);
+        // 1. dS' into LDS (split, transposed) and out
 #pragma unroll
-        for (int a = 0; a < RA; ++a) {
-            const int i = i0 + 16 * a;
-            dSs[i][jc] = dS[a];
-            ds_end[(cid * D + i) * D + col0 + jc] = dS[a];
-        }
-        __syncthreads();
-        // dU = P^T dO + diag(c) K dS'   (64 x 16)
-        for (int n = t; n < C * 16; n += BC_THREADS) {
-            const int m = n / 16, j = n % 16;
-            float pd = 0.f, kd = 0.f;
-            for (int r = m; r < C; ++r) pd = fmaf(Pf[r][m], dOs[r][j], pd);
-            for (int i = 0; i < D; ++i) kd = fmaf(Kf[m][i], dSs[i][j], kd);
-            dUs[m][j] = fmaf(cs[m], kd, pd);
-        }
-        __syncthreads();
-        // dE = diag(beta) T^T dU   (= dV)
-        for (int n = t; n < C * 16; n += BC_THREADS) {
-            const int m = n / 16, j = n % 16;
-            float acc = 0.f;
-            for (int r = m; r < C; ++r) acc = fmaf(Tf[r][m], dUs[r][j], acc);
-            acc *= bs[m];
-            dEs[m][j] = acc;
-            if (m < nvalid) dv[((tokb + c0 + m) * H + h) * D + col0 + j] = acc;
-        }
-        __syncthreads();
-        // dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dE
-        const float gC = gs[C - 1];
+        for (int rt = 0; rt < G::RT; ++rt) {
+            const float v[4] = {dS[rt][0], dS[rt][1], dS[rt][2], dS[rt][3]};
+            bf16 hi[4], lo[4];
+            split_bf16<4>(v, hi, lo);
+            const int i = rbase + 16 * rt + 4 * lg;
+            *reinterpret_cast<bf16x4 *>(dSh + lr * SLD + i) = pack4(hi);
+            *reinterpret_cast<bf16x4 *>(dSl + lr * SLD + i) = pack4(lo);
 #pragma unroll
-        for (int a = 0; a < RA; ++a) {
-            const int i = i0 + 16 * a;
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) acc = fmaf(gs[r], Qf[r][i] * dOs[r][jc] - Kf[r][i] * dEs[r][jc], acc);
-            dS[a] = gC * dS[a] + acc;
+            for (int jj = 0; jj < 4; ++jj) ds_end[(cid * D + i + jj) * D + col0 + lr] = v[jj];
         }
-        __syncthreads();   // the next chunk restages every buffer
+        lds_barrier();
+        // 2. Y = W^T dS' for token rows 16 wave .., dE = M^T dO + Y
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(dSh + lr * SLD + 32 * s + 8 * lg);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(dSl + lr * SLD + 32 * s + 8 * lg);
+            y = mfma16x16x32(o.wh[s], bh, y);
+            y = mfma16x16x32(o.wh[s], bl, y);
+            y = mfma16x16x32(o.wl[s], bh, y);
+        }
+        {
+            float ge[4], go[4];
+            bf16 eh[4], el[4], oh[4], ol[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int m = 16 * wave + 4 * lg + jj;
+                const float de = o.mt[jj] + y[jj];
+                if (m < nvalid) dv[((tokb + c0 + m) * H + h) * D + col0 + lr] = de;
+                ge[jj] = -o.g[jj] * de;
+                go[jj] = o.g[jj] * o.od[jj];
+            }
+            split_bf16<4>(ge, eh, el);
+            split_bf16<4>(go, oh, ol);
+            const int m0 = 16 * wave + 4 * lg;
+            *reinterpret_cast<bf16x4 *>(gEh + lr * MLD + m0) = pack4(eh);
+            *reinterpret_cast<bf16x4 *>(gEl + lr * MLD + m0) = pack4(el);
+            *reinterpret_cast<bf16x4 *>(gOh + lr * MLD + m0) = pack4(oh);
+            *reinterpret_cast<bf16x4 *>(gOl + lr * MLD + m0) = pack4(ol);
+        }
+        lds_barrier();
+        // 3. dS = gamma_C dS' + Q^T (gamma dO) - K^T (gamma dE)
+#pragma unroll
+        for (int rt = 0; rt < G::RT; ++rt) {
+            f32x4 acc;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[jj] = o.gC * dS[rt][jj];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int mo = lr * MLD + 32 * s + 8 * lg;
+                const bf16x8 oh = *reinterpret_cast<const bf16x8 *>(gOh + mo);
+                const bf16x8 ol = *reinterpret_cast<const bf16x8 *>(gOl + mo);
+                const bf16x8 eh = *reinterpret_cast<const bf16x8 *>(gEh + mo);
+                const bf16x8 el = *reinterpret_cast<const bf16x8 *>(gEl + mo);
+                acc = mfma16x16x32(o.qh[rt][s], oh, acc);
+                acc = mfma16x16x32(o.qh[rt][s], ol, acc);
+                acc = mfma16x16x32(o.kh[rt][s], eh, acc);
+                acc = mfma16x16x32(o.kh[rt][s], el, acc);
+                if constexpr (SPLIT_KQ) {
+                    acc = mfma16x16x32(o.ql[rt][s], oh, acc);
+                    acc = mfma16x16x32(o.kl[rt][s], eh, acc);
+                }
+            }
+            dS[rt] = acc;
+        }
+    };
+
+    load(ops[0], Nc - 1);
+    for (int c = Nc - 1; c >= 0; c -= 2) {
+        if (c >= 1) load(ops[1], c - 1);
+        step(ops[0], c);
+        if (c >= 1) {
+            if (c >= 2) load(ops[0], c - 2);
+            step(ops[1], c - 1);
+        }
     }
     if (ds_init) {
 #pragma unroll
-        for (int a = 0; a < RA; ++a) ds_init[sbase + (int64_t)(i0 + 16 * a) * D + col0 + jc] = dS[a];
+        for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                ds_init[sbase + (int64_t)(rbase + 16 * rt + 4 * lg + jj) * D + col0 + lr] = dS[rt][jj];
     }
 }
 
@@ -538,7 +740,7 @@ hipError_t launch_bwd_prep(bool f32, int B, int L, int H, int D, const void *q, 
                            const float *beta, float *mats, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     const dim3 grid((unsigned)(Nc * H), B);
-    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc);
+    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc, D);
 #define BP(DD, T) launch_kernel((k_bwd_prep<DD, T>), grid, dim3(BP_THREADS), 0, s, (const T *)q, (const T *)k, alpha, beta, L, H, Nc, bm)
     if (f32) {
         if (D == 64) BP(64, float); else return hipErrorInvalidValue;
@@ -549,15 +751,28 @@ hipError_t launch_bwd_prep(bool f32, int B, int L, int H, int D, const void *q, 
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
-                            const float *d_o, const float *d_sfinal, float *mats, float *dv, float *ds_end,
-                            float *ds_init, hipStream_t s) {
+hipError_t launch_bwd_ops(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
+                          const float *d_o, float *mats, hipStream_t s) {
+    const int Nc = (L + C - 1) / C;
+    const dim3 grid((unsigned)(Nc * H), B);
+    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc, D);
+#define BO(DD, T) launch_kernel((k_bwd_ops<DD, T>), grid, dim3(BO_THREADS), 0, s, (const T *)q, (const T *)k, beta, d_o, L, H, Nc, bm)
+    if (f32) {
+        if (D == 64) BO(64, float); else return hipErrorInvalidValue;
+    } else {
+        if (D == 128) BO(128, bf16); else BO(64, bf16);
+    }
+#undef BO
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_carry(bool f32, int B, int L, int H, int D, const float *d_o, const float *d_sfinal,
+                            float *mats, float *dv, float *ds_end, float *ds_init, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     const dim3 grid(H, D / 16, B);
-    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc);
+    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc, D);
 #define BC(DD, T)                                                                                    \
-    launch_kernel((k_bwd_carry<DD, T>), grid, dim3(BC_THREADS), 0, s, (const T *)q, (const T *)k, beta, d_o, bm, \
-                  d_sfinal, L, H, Nc, dv, ds_end, ds_init)
+    launch_kernel((k_bwd_carry<DD, T>), grid, dim3(BC_THREADS), 0, s, d_o, bm, d_sfinal, L, H, Nc, dv, ds_end, ds_init)
     if (f32) {
         if (D == 64) BC(64, float); else return hipErrorInvalidValue;
     } else {
@@ -573,7 +788,7 @@ hipError_t launch_bwd_chunk(bool f32, int B, int L, int H, int D, const void *q,
                             float *dalpha, float *dbeta, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     const dim3 grid((unsigned)(Nc * H), B);
-    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc);
+    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc, D);
 #define BK(DD, T)                                                                                    \
     launch_kernel((k_bwd_chunk<DD, T>), grid, dim3(BK_THREADS), 0, s, (const T *)q, (const T *)k, (const T *)v, \
                   alpha, beta, d_o, dv, s_chunks, ds_end, bm, L, H, Nc, dq, dk, dalpha, dbeta)
@@ -586,6 +801,6 @@ hipError_t launch_bwd_chunk(bool f32, int B, int L, int H, int D, const void *q,
     return hipGetLastError();
 }
 
-size_t bwd_mats_bytes(int64_t chunks) { return (size_t)chunks * BWD_MATS_PER_CHUNK; }
+size_t bwd_mats_bytes(int64_t chunks, int D) { return (size_t)chunks * bwd_mats_per_chunk(D); }
 
 }  // namespace gdn
