@@ -54,6 +54,7 @@ _lib = None
 __all__ = [
     "build", "num_threads", "round_bf16", "round_f32", "scan", "scan_backward", "project",
     "loop_prefill", "loop_prefill_act", "loop_backward", "loop_decode_step", "scan_chunkwise",
+    "ffn_width", "rms_norm", "block_forward", "block_loop_prefill",
 ]
 
 
@@ -316,6 +317,77 @@ def loop_backward(h0, Wq, Wk, Wv, wa, wb, rho, loops, dh, H: int, dk: int, dv: i
         g = rho[tau][None, :] * g + dqr @ Wq.T + dkr @ Wk.T + dvr @ Wv.T + da @ wa.T + db @ wb.T
     out["dh0"] = g.reshape(B, L, d)
     return out
+
+
+# ---------------------------------------------------------------------------
+# the LT2 block around the mixer
+# ---------------------------------------------------------------------------
+def ffn_width(d: int, multiple: int = 256) -> int:
+    """Hidden width of the gated FFN: 8d/3 rounded up to a multiple of 256 (the training setup's "FFN
+    multiple-of 256", read as the usual SwiGLU sizing; 5632 at d = 2048, 2816 at d = 1024)."""
+    return multiple * ((8 * d // 3 + multiple - 1) // multiple)
+
+
+def rms_norm(x, g, eps: float = 1e-6):
+    """x / sqrt(mean(x^2) + eps) * g over the last axis (the pre-norm of each sub-layer)."""
+    x = _f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f64(g)
+
+
+def block_forward(h, wts: dict, H: int, dk: int, dv: int, alpha_lo: float, act: str, eps: float = 1e-6,
+                  keep: bool = False):
+    """One LT2 block F(h) (LT2 Section 2, "LT2" paragraph: the Transformer block of its Eq. (1) with the
+    attention sub-layer replaced by the linear mixer; pre-norm per sub-layer; the head-specific sigmoid
+    output gate of Gated Attention applied to the mixer output, as the attention-sink paragraph of Section 3
+    adds it inside the looped block):
+        x1 = rms_norm(h, g1)
+        q, k, v, alpha, beta = project(x1)             (the mixer's projections, as in loop_prefill)
+        o  = scan(q, k, v, alpha, beta) from S = 0
+        z  = o (.) sigmoid(x1 Wg)                       (Wg [d, H dv]: one gate per head channel)
+        h1 = h + z Wo                                   (Wo [H dv, d]; identity residual)
+        x2 = rms_norm(h1, g2)
+        u  = silu(x2 W1) (.) (x2 W3)                    (W1, W3 [d, F])
+        F(h) = h1 + u W2                                (W2 [F, d]; identity residual)
+    wts holds g1, Wq, Wk, Wv, wa, wb, Wg, Wo, g2, W1, W3, W2.  For bf16 workloads x1, q/k/v, z, x2 and u are
+    rounded to bf16 (the operands of the products), h, h1, o, the statistics and the gates stay fp32.
+    Returns F(h) [B, L, d] (fp64), or with keep a dict of every intermediate."""
+    h = _f64(h)
+    B, L, d = h.shape
+    M = B * L
+    rb = round_bf16 if act == "bf16" else (lambda t: t)
+    W = {k_: _f64(v_) for k_, v_ in wts.items()}
+    x1 = rb(rms_norm(h, W["g1"], eps)).reshape(M, d)
+    q, k, v, al, be = project(x1, W["Wq"], W["Wk"], W["Wv"], W["wa"], W["wb"], H, dk, dv, alpha_lo, act, eps)
+    o, _ = scan(q.reshape(B, L, H, dk), k.reshape(B, L, H, dk), v.reshape(B, L, H, dv), al.reshape(B, L, H),
+                be.reshape(B, L, H), None, want_state=False)
+    o = o.reshape(M, H * dv)
+    gate = 1.0 / (1.0 + np.exp(-(x1 @ W["Wg"])))
+    z = rb(o * gate)
+    h1 = h.reshape(M, d) + z @ W["Wo"]
+    x2 = rb(rms_norm(h1, W["g2"], eps))
+    a, b = x2 @ W["W1"], x2 @ W["W3"]
+    u = rb(a / (1.0 + np.exp(-a)) * b)
+    out = (h1 + u @ W["W2"]).reshape(B, L, d)
+    if keep:
+        return dict(out=out, x1=x1, q=q, k=k, v=v, alpha=al, beta=be, o=o, z=z, h1=h1, x2=x2, u=u)
+    return out
+
+
+def block_loop_prefill(h0, layers, rho, H: int, dk: int, dv: int, alpha_lo: float, act: str, eps: float = 1e-6,
+                       keep_loops: bool = False):
+    """T loops of an N-block LT2 stack (LT2 Section 2): h^(tau) = (F_N o ... o F_1)(h^(tau-1)) + rho_tau (.)
+    h^(tau-1), with the same N blocks (``layers``, a list of weight dicts) in every loop.  fp64."""
+    h = _f64(h0)
+    rho = _f64(rho)
+    loops = []
+    for tau in range(rho.shape[0]):
+        x = h
+        for wts in layers:
+            x = block_forward(x, wts, H, dk, dv, alpha_lo, act, eps)
+        h = x + rho[tau][None, None, :] * h
+        if keep_loops:
+            loops.append(h.copy())
+    return dict(h=h, loops=loops if keep_loops else None)
 
 
 def loop_prefill_act(h0, Wq, Wk, Wv, wa, wb, rho, w_halt, b_halt: float, eps: float, H: int, dk: int, dv: int,

@@ -590,3 +590,97 @@ def test_loop_backward_given_operands_are_used_for_the_scan():
     moved[1][1][5, 0, 2] = moved[1][1][5, 0, 2] * (1 + 2.0 ** -7)   # k of loop 2, one element, one bf16 step
     diff = oracle.loop_backward(**x, loops=fwd["loops"], dh=dh, **s, alpha_lo=0.1, act="bf16", qkv=moved)
     assert not np.array_equal(diff["dWk"], base["dWk"])
+
+
+# ---------------------------------------------------------------------------
+# the LT2 block around the mixer
+# ---------------------------------------------------------------------------
+def _block_weights(seed, d, H, dk, dv, F):
+    rng = np.random.default_rng(seed)
+    n = lambda *shape: rng.standard_normal(shape) / math.sqrt(shape[0])
+    return dict(g1=1.0 + 0.1 * rng.standard_normal(d), Wq=n(d, H * dk), Wk=n(d, H * dk), Wv=n(d, H * dv),
+                wa=n(d, H), wb=n(d, H), Wg=n(d, H * dv), Wo=n(H * dv, d), g2=1.0 + 0.1 * rng.standard_normal(d),
+                W1=n(d, F), W3=n(d, F), W2=n(F, d))
+
+
+def test_ffn_width_and_rms_norm_hand_values():
+    """8d/3 rounded up to 256: 2048 -> 5461.3 -> 5632, 1024 -> 2730.7 -> 2816; rms_norm([3, 4]) =
+    [3, 4] / sqrt(12.5) (hand-computed 0.848528.., 1.131370..) times the weight."""
+    assert oracle.ffn_width(2048) == 5632 and oracle.ffn_width(1024) == 2816 and oracle.ffn_width(96) == 256
+    r = oracle.rms_norm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), eps=0.0)
+    assert np.allclose(r, [0.8485281374238570, 2 * 1.1313708498984760], rtol=1e-14)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_block_zero_projections_is_identity(act):
+    """Wo = W2 = 0: both sub-layers add nothing, F(h) = h exactly; so T loops give prod(1 + rho_tau) (.) h0."""
+    d, H, D = 16, 2, 8
+    w = _block_weights(91, d, H, D, D, 256)
+    w["Wo"][:] = 0.0
+    w["W2"][:] = 0.0
+    h = oracle.round_bf16(np.random.default_rng(92).standard_normal((2, 20, d)))
+    assert np.array_equal(oracle.block_forward(h, w, H, D, D, 0.0, act), h)
+    rho = np.random.default_rng(93).random((3, d)) * 0.5
+    r = oracle.block_loop_prefill(h, [w, w], rho, H, D, D, 0.0, act)
+    assert np.allclose(r["h"], np.prod(1.0 + rho, 0)[None, None] * h, rtol=1e-14)
+
+
+def test_block_ffn_matches_library_rms_norm_and_silu():
+    """Wv = 0 makes the mixer output zero (F(h) = h + FFN(h)); the FFN sub-layer then equals torch's
+    rms_norm and silu composed by hand: (silu(x2 W1) * (x2 W3)) W2 with x2 = rms_norm(h; g2)."""
+    d, H, D, F = 24, 3, 8, 256
+    w = _block_weights(94, d, H, D, D, F)
+    w["Wv"][:] = 0.0
+    h = np.random.default_rng(95).standard_normal((1, 9, d))
+    got = oracle.block_forward(h, w, H, D, D, 0.2, "f32") - h
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    x2 = torch.nn.functional.rms_norm(t(h), (d,), weight=t(w["g2"]), eps=1e-6)
+    ref = (torch.nn.functional.silu(x2 @ t(w["W1"])) * (x2 @ t(w["W3"]))) @ t(w["W2"])
+    assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("zero_gate", [True, False])
+def test_block_mixer_sublayer_is_the_pinned_loop_through_the_gate(zero_gate):
+    """W2 = 0: F(h) = h + (o (.) sigmoid(x1 Wg)) Wo, where x1 = rms_norm(h; g1) (torch's routine) and o is the
+    mixer output of x1, i.e. one loop of the pinned loop_prefill with rho = 0 applied to x1.  With Wg = 0
+    every gate is sigmoid(0) = 1/2."""
+    d, H, D = 16, 2, 8
+    w = _block_weights(96, d, H, D, D, 256)
+    w["W2"][:] = 0.0
+    if zero_gate:
+        w["Wg"][:] = 0.0
+    h = np.random.default_rng(97).standard_normal((2, 70, d))
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    x1 = torch.nn.functional.rms_norm(t(h), (d,), weight=t(w["g1"]), eps=1e-6)
+    o = oracle.loop_prefill(x1.numpy(), w["Wq"], w["Wk"], w["Wv"], w["wa"], w["wb"], np.zeros((1, d)), H, D, D,
+                            0.3, "f32")["h"]
+    gate = torch.sigmoid(x1 @ t(w["Wg"])).numpy()
+    if zero_gate:
+        assert np.all(gate == 0.5)
+    got = oracle.block_forward(h, w, H, D, D, 0.3, "f32")
+    assert np.allclose(got, h + (o * gate) @ w["Wo"], rtol=1e-12, atol=1e-13)
+
+
+def test_block_loop_composes_blocks_and_the_loop_residual():
+    """h^(1) = F_2(F_1(h0)) + rho_1 (.) h0 and h^(2) = F_2(F_1(h^(1))) + rho_2 (.) h^(1), block by block."""
+    d, H, D = 16, 2, 8
+    w1, w2 = _block_weights(100, d, H, D, D, 256), _block_weights(101, d, H, D, D, 256)
+    h0 = np.random.default_rng(102).standard_normal((1, 40, d))
+    rho = np.random.default_rng(103).random((2, d)) * 0.5
+    f = lambda x: oracle.block_forward(oracle.block_forward(x, w1, H, D, D, 0.0, "f32"), w2, H, D, D, 0.0, "f32")
+    h1 = f(h0) + rho[0] * h0
+    h2 = f(h1) + rho[1] * h1
+    r = oracle.block_loop_prefill(h0, [w1, w2], rho, H, D, D, 0.0, "f32", keep_loops=True)
+    assert np.array_equal(r["loops"][0], h1) and np.array_equal(r["h"], h2)
+
+
+def test_block_is_causal_and_sequences_independent():
+    d, H, D = 16, 2, 8
+    w = _block_weights(98, d, H, D, D, 256)
+    h = np.random.default_rng(99).standard_normal((2, 30, d))
+    base = oracle.block_forward(h, w, H, D, D, 0.1, "f32")
+    h2 = h.copy()
+    h2[0, 20:] += 1.0
+    moved = oracle.block_forward(h2, w, H, D, D, 0.1, "f32")
+    assert np.array_equal(moved[0, :20], base[0, :20]) and np.array_equal(moved[1], base[1])
+    assert not np.allclose(moved[0, 20:], base[0, 20:])
