@@ -125,8 +125,13 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 // (Named enums: an enumerator of an unnamed enum inside a kernel's template
 // signature is mangled differently by the host and device compilations.)
 enum GemmOperand : int { OPND_BF16 = 0, OPND_F32_SPLIT = 1, OPND_F32_ROUND = 2 };
-// Epilogues: C = acc; C += acc; C = acc + rho[n] * Dsrc[m][n].
-enum GemmEpilogue : int { EPI_STORE = 0, EPI_ACCUM = 1, EPI_RESID = 2 };
+// Epilogues: C = acc; C += acc; C = acc + rho[n] D1[m][n]; C = acc + D1[m][n];
+// C = acc + D1[m][n] + rho[n] D2[m][n]; C = D1[m][n] sigmoid(acc); and
+// C[m][f] = silu(acc[m][64 g + r]) acc[m][64 g + 32 + r], f = 32 g + r (the
+// gated FFN with W1 and W3 rows interleaved in groups of 32).
+enum GemmEpilogue : int {
+    EPI_STORE = 0, EPI_ACCUM = 1, EPI_RESID = 2, EPI_ADD = 3, EPI_ADD_RESID = 4, EPI_GATE = 5, EPI_SWIGLU = 6
+};
 // C[m][n] (op)= sum_k A[m][k] B[n][k] for m < M, n < N; A [M][lda], B [N][ldb]
 // K-contiguous, K, lda, ldb multiples of 8, 16-byte aligned bases.  Pairs
 // supported: (bf16, bf16), (round, bf16), (split, bf16), (split, split),
@@ -134,6 +139,18 @@ enum GemmEpilogue : int { EPI_STORE = 0, EPI_ACCUM = 1, EPI_RESID = 2 };
 hipError_t launch_gemm_nt(int mode_a, int mode_b, int epi, const void *A, int64_t lda, const void *B, int64_t ldb,
                           int M, int N, int K, float *C, int64_t ldc, const float *rho, const float *Dsrc,
                           int64_t ldd, hipStream_t s);
+// The tiled bf16 product (gemm_tile.hip): C[m][n] = epi(sum_k A[m][k] B[n][k])
+// with A2 / B2 the optional lo planes of an fp32 operand split into bf16 hi +
+// lo (null when the operand is bf16).  K a multiple of 64, lda, ldb multiples
+// of 8 and >= K; C fp32 or bf16 (EPI_ACCUM fp32 only).
+hipError_t launch_gemm_tile(int epi, bool out_f32, const bf16 *A, const bf16 *A2, int64_t lda, const bf16 *B,
+                            const bf16 *B2, int64_t ldb, int M, int N, int K, void *C, int64_t ldc, const float *rho,
+                            const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s);
+// x ~ hi + lo, both bf16, elementwise over n values (16-byte aligned).
+hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream_t s);
+// hi[c][r] + lo[c][r] ~ in[r][c] (fp32 in [R][ldi]), zero for R <= r < Rp.
+hipError_t launch_transpose_split(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldo,
+                                  int Rp, hipStream_t s);
 // out[c][r] = in[r][c] (r < R, c < Cc; fp32 or bf16 either side, RNE to bf16),
 // and 0 for R <= r < Rp.
 hipError_t launch_transpose(bool in_f32, bool out_f32, const void *in, int64_t ldi, int R, int Cc, void *out,

@@ -115,6 +115,7 @@ struct Layout {
     // transpose [P][Mp], the loop input and the weights transposed, the scan
     // gradients, two dh buffers, the weight-gradient accumulator [d][P], rho partials
     size_t Y = 0, YT = 0, XT = 0, WT = 0, gq = 0, gk = 0, gv = 0, gal = 0, gbe = 0, dhA = 0, dhB = 0, dW = 0, part = 0;
+    size_t Yhl = 0;   // bf16 workloads: dY as bf16 hi and lo planes (the transpose's planes reuse YT)
     size_t total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
@@ -161,6 +162,7 @@ Layout layout(const gdn_desc *d, int op) {
     if (lbwd) {
         const int64_t P = packed_rows(d->H, d->dk), Mp = (tokens + 63) / 64 * 64, ab = act_bytes(d);
         lo.Y = take(tokens * P * 4);
+        if (d->act == GDN_BF16) lo.Yhl = take(tokens * P * 4);
         lo.YT = take(P * Mp * 4);
         lo.XT = take(d->d * Mp * ab);
         lo.WT = take(d->d * P * ab);
@@ -464,8 +466,11 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         // the raw projections in fp32 (the normalisation's and the gates' gradients need them)
         e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
-            return launch_gemm_nt(f32 ? OPND_F32_SPLIT : OPND_BF16, wmode, EPI_STORE, x, d, Wpack, d, M, P, d, Y, P,
-                                  nullptr, nullptr, 0, s);
+            if (f32)
+                return launch_gemm_nt(OPND_F32_SPLIT, wmode, EPI_STORE, x, d, Wpack, d, M, P, d, Y, P, nullptr,
+                                      nullptr, 0, s);
+            return launch_gemm_tile(EPI_STORE, true, (const bf16 *)x, nullptr, d, (const bf16 *)Wpack, nullptr, d, M,
+                                    P, d, Y, P, nullptr, nullptr, 0, nullptr, 0, s);
         });
         if (e != hipSuccess) return hip_fail(e, "projection recompute launch");
         // the scan backward from S = 0 with dO = dL/dh^(tau+1) (the mixer output is h's width); with gate
@@ -491,20 +496,38 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         if (e != hipSuccess) return hip_fail(e, "epilogue gradient launch");
         e = launch_lb_drho(M, d, g_in, hp, hp_f32, part, drho + (int64_t)tau * d, s);
         if (e != hipSuccess) return hip_fail(e, "rho gradient launch");
-        // dL/dh^(tau) = rho_tau (.) dL/dh^(tau+1) + dY W
-        e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
-            return launch_gemm_nt(OPND_F32_SPLIT, wmode, EPI_RESID, Y, P, WT, P, M, d, P, g_out, d,
-                                  rho + (int64_t)tau * d, g_in, d, s);
-        });
-        if (e != hipSuccess) return hip_fail(e, "input gradient launch");
-        // dW^T [d][P] += x^T dY
-        if ((e = launch_transpose(f32, f32, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess ||
-            (e = launch_transpose(true, true, Y, P, M, P, YT, Mp, Mp, s)) != hipSuccess)
-            return hip_fail(e, "transpose launch");
-        e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
-            return launch_gemm_nt(f32 ? OPND_F32_SPLIT : OPND_BF16, OPND_F32_SPLIT, EPI_ACCUM, XT, Mp, YT, Mp, d, P,
-                                  Mp, dW, P, nullptr, nullptr, 0, s);
-        });
+        // dL/dh^(tau) = rho_tau (.) dL/dh^(tau+1) + dY W, then dW^T [d][P] += x^T dY; dY enters the bf16
+        // products as two bf16 planes (hi + lo)
+        if (f32) {
+            e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                return launch_gemm_nt(OPND_F32_SPLIT, wmode, EPI_RESID, Y, P, WT, P, M, d, P, g_out, d,
+                                      rho + (int64_t)tau * d, g_in, d, s);
+            });
+            if (e != hipSuccess) return hip_fail(e, "input gradient launch");
+            if ((e = launch_transpose(f32, f32, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess ||
+                (e = launch_transpose(true, true, Y, P, M, P, YT, Mp, Mp, s)) != hipSuccess)
+                return hip_fail(e, "transpose launch");
+            e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                return launch_gemm_nt(OPND_F32_SPLIT, OPND_F32_SPLIT, EPI_ACCUM, XT, Mp, YT, Mp, d, P, Mp, dW, P,
+                                      nullptr, nullptr, 0, s);
+            });
+        } else {
+            bf16 *Yh = (bf16 *)at(ws, lo.Yhl), *Yl = Yh + (int64_t)M * P;
+            bf16 *YTh = (bf16 *)YT, *YTl = YTh + (int64_t)P * Mp;
+            if ((e = launch_split((int64_t)M * P, Y, Yh, Yl, s)) != hipSuccess) return hip_fail(e, "split launch");
+            e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                return launch_gemm_tile(EPI_RESID, true, Yh, Yl, P, (const bf16 *)WT, nullptr, P, M, d, P, g_out, d,
+                                        rho + (int64_t)tau * d, g_in, d, nullptr, 0, s);
+            });
+            if (e != hipSuccess) return hip_fail(e, "input gradient launch");
+            if ((e = launch_transpose(false, false, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess ||
+                (e = launch_transpose_split(Y, P, M, P, YTh, YTl, Mp, Mp, s)) != hipSuccess)
+                return hip_fail(e, "transpose launch");
+            e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                return launch_gemm_tile(EPI_ACCUM, true, (const bf16 *)XT, nullptr, Mp, YTh, YTl, Mp, d, P, Mp, dW,
+                                        P, nullptr, nullptr, 0, nullptr, 0, s);
+            });
+        }
         if (e != hipSuccess) return hip_fail(e, "weight gradient launch");
     }
     e = launch_lb_unpack(d, H, D, dW, P, qkvp, dWq, dWk, dWv, dwa, dwb, s);

@@ -189,6 +189,53 @@ __global__ __launch_bounds__(256) void k_transpose(const TI *__restrict__ in, in
     }
 }
 
+// hi[c][r] + lo[c][r] ~ in[r][c], the fp32 value split into two bf16 parts.
+__global__ __launch_bounds__(256) void k_transpose_split(const float *__restrict__ in, int64_t ldi, int R, int Cc,
+                                                         bf16 *__restrict__ hi, bf16 *__restrict__ lo, int64_t ldo,
+                                                         int Rp) {
+    __shared__ float tile[64][65];
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = r0 + ty + 4 * i, c = c0 + tx;
+        tile[ty + 4 * i][tx] = (r < R && c < Cc) ? in[(int64_t)r * ldi + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = c0 + ty + 4 * i, r = r0 + tx;
+        if (c < Cc && r < Rp) {
+            const float x[2] = {tile[tx][ty + 4 * i], 0.f};
+            bf16 h[2], l[2];
+            split_bf16<2>(x, h, l);
+            hi[(int64_t)c * ldo + r] = h[0];
+            lo[(int64_t)c * ldo + r] = l[0];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_split(const float *__restrict__ x, bf16 *__restrict__ hi,
+                                               bf16 *__restrict__ lo, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    if (i + 3 < n) {
+        const float4 v = *reinterpret_cast<const float4 *>(x + i);
+        const float a[4] = {v.x, v.y, v.z, v.w};
+        bf16 h[4], l[4];
+        split_bf16<4>(a, h, l);
+        *reinterpret_cast<bf16x4 *>(hi + i) = pack4(h);
+        *reinterpret_cast<bf16x4 *>(lo + i) = pack4(l);
+    } else {
+        for (int64_t j = i; j < n; ++j) {
+            const float a[2] = {x[j], 0.f};
+            bf16 h[2], l[2];
+            split_bf16<2>(a, h, l);
+            hi[j] = h[0];
+            lo[j] = l[0];
+        }
+    }
+}
+
 template <int MA, int MB>
 hipError_t gemm_launch(int epi, const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N, int K,
                        float *C, int64_t ldc, const float *rho, const float *Dsrc, int64_t ldd, hipStream_t s) {
@@ -221,6 +268,22 @@ hipError_t launch_gemm_nt(int mode_a, int mode_b, int epi, const void *A, int64_
     GEMM_CASE(OPND_BF16, OPND_F32_SPLIT)
 #undef GEMM_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t groups = (n + 3) / 4;
+    launch_kernel(k_split, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, hi, lo, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_split(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldo,
+                                  int Rp, hipStream_t s) {
+    if (R < 0 || Cc <= 0 || Rp < R || (Rp + 63) / 64 > 65535) return hipErrorInvalidValue;
+    if (Rp == 0) return hipSuccess;
+    launch_kernel(k_transpose_split, dim3((Cc + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s, in, ldi, R, Cc, hi, lo,
+                  ldo, Rp);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose(bool in_f32, bool out_f32, const void *in, int64_t ldi, int R, int Cc, void *out,

@@ -132,7 +132,7 @@ def test_workspace_sizes():
     st, _ = _ws_status(gl.make_desc(B, L, H, D, D, act=gl.GDN_F32), gl.GDN_OP_SCAN_BACKWARD)
     assert st == -3   # fp32 inputs with 128-wide heads
     # loop backward: the loop prefill's regions (q, k, v, alpha, beta, the bf16 operand; gate partials from 1024
-    # tokens), the scan backward's, then the raw projections
+    # tokens), the scan backward's, then the raw projections (and for bf16 their gradient as bf16 hi/lo planes)
     # [M][P] and their transpose [P][Mp] (Mp = M rounded up to 64), x^T [d][Mp] and W^T [d][P] in the activation
     # dtype, the scan gradients, two dh buffers, the weight-gradient accumulator [d][P] and the rho partials
     for act, eb in [(gl.GDN_BF16, 2), (gl.GDN_F32, 4)]:
@@ -144,7 +144,7 @@ def test_workspace_sizes():
         mats = B * H * Nc * (3 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4 + 6 * D * 64 * 2 + 64 * D * 4)
         xb = up(tok * d * 2) if act == gl.GDN_BF16 else 0   # the bf16 loop operand
         exp = (3 * up(tok * H * D * eb) + 2 * up(tok * H * 4) + xb + chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats)
-               + up(tok * P * 4) + up(P * Mp * 4) + up(d * Mp * eb) + up(d * P * eb) + 3 * up(tok * H * D * 4)
+               + up(tok * P * 4) + (up(tok * P * 4) if act == gl.GDN_BF16 else 0) + up(P * Mp * 4) + up(d * Mp * eb) + up(d * P * eb) + 3 * up(tok * H * D * 4)
                + 2 * up(tok * H * 4) + 2 * up(tok * d * 4) + up(d * P * 4) + up(((tok + 127) // 128) * d * 4))
         assert _ws_status(gl.make_desc(B, L, H, D, D, act=act), gl.GDN_OP_LOOP_BACKWARD) == (0, exp)
     st, _ = _ws_status(gl.make_desc(B, L, H, 128, 128, act=gl.GDN_F32), gl.GDN_OP_LOOP_BACKWARD)
