@@ -24,10 +24,11 @@ Printed (one JSON line on stdout):
                   halting loops, share of position-loops projected;
   scan_backward   gradients of one scan pass at the 4096-token prompt's shape (gdn_scan_backward);
   loop_backward   gradients through the 4 loops of the 4096-token prompt (gdn_loop_backward);
+  block           the headline workload through a one-block LT2 stack looped T times (gdn_block_loop_prefill);
   cpu_baseline    the oracle on a bounded sample of the headline workload, on the host's cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode]
-                       [--no-act] [--no-backward] [--no-cpu-baseline]
+                       [--no-act] [--no-block] [--no-backward] [--no-cpu-baseline]
        python bench.py --calib-copy          (plain 256 MiB device copy, for HBM counter calibration)
 Only one GPU is used: --gpus N with N > 1 exits with a message.
 """
@@ -474,6 +475,69 @@ def bench_loop_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
                      "note": "algorithmic 2MNK per product; fp32 operands run 2-3 bf16 passes"}}
 
 
+def bench_block(args, torch, gl, synth, name="prefill_b4_l8192", layers=1):
+    """gdn_block_loop_prefill: T loops of an LT2 block stack (pre-norm, the mixer, the sigmoid-gated output
+    projection, the SwiGLU FFN, identity residuals) on a prompt workload's shape."""
+    w = synth.workload(name)
+    B, L, H, D, d, T = w.B, w.L, w.H, w.dk, w.d, w.T
+    F = synth.block_ffn(w)
+    dev = lambda t: t.contiguous().to("cuda")
+    x = synth.prefill_inputs(w)
+    blocks = synth.block_inputs(w, layers)
+    desc = gl.make_desc(B, L, H, D, D, T=T, act=w.act, alpha_lo=w.alpha_lo)
+    n = gl.gdn_block_packed_bytes(desc, F)
+    Wb = torch.empty(layers * n, dtype=torch.uint8, device="cuda")
+    keys = ("g1", "Wq", "Wk", "Wv", "wa", "wb", "Wg", "Wo", "g2", "W1", "W3", "W2")
+    for i, blk in enumerate(blocks):
+        gl.gdn_block_pack(desc, F, *[dev(blk[k]) for k in keys], Wb[i * n:(i + 1) * n])
+    ws = gl.block_workspace(desc, F)
+    h0, rho = dev(x["h0"]), dev(x["rho"])
+    h_out = torch.empty(B, L, d, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gl.gdn_block_loop_prefill(desc, F, layers, h0, Wb, rho, h_out, ws, stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    nrep = max(min(args.steps, 10), 3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(nrep):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / nrep
+    stages = {"block_gemm": gl.GDN_STAGE_BLOCK_GEMM, "project": gl.GDN_STAGE_PROJECT,
+              "scan_prep": gl.GDN_STAGE_SCAN_PREP, "scan_carry": gl.GDN_STAGE_SCAN_CARRY}
+    timers = {k: gl.gdn_timer_create(v, 4 * nrep * T * layers) for k, v in stages.items()}
+    for t in timers.values():
+        gl.gdn_timer_attach(t)
+    for _ in range(nrep):
+        call()
+    torch.cuda.synchronize()
+    gl.gdn_timer_detach()
+    per, tot = {}, {}
+    for k, t in timers.items():
+        cnt, total = gl.gdn_timer_read(t)
+        per[k] = total / max(cnt, 1)
+        tot[k] = total / nrep
+        gl.gdn_timer_destroy(t)
+    M, HD = B * L, H * D
+    gemm_flops = 2 * M * (d * HD + HD * d + d * 2 * F + F * d)             # per block application
+    step_flops = T * layers * (gemm_flops + proj_flops_per_token(w) * M + scan_flops_per_token(w) * M)
+    gemm_ach = gemm_flops * T * layers / (tot["block_gemm"] * 1e-3) / 1e12
+    return {"workload": f"LT2 block stack, {name} shape (B={B}, L={L}, d={d}, H={H}, ffn={F}, layers={layers}, "
+                        f"T={T}, {w.act})",
+            "value": M / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+            "algorithmic_tflops": step_flops / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "stages_ms_per_call": tot, "stages_avg_launch_us": {k: v * 1e3 for k, v in per.items()},
+            "gemm": {"bound": "mfma", "kernel": "k_gemm_tile", "achieved": gemm_ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_ach / PEAK_BF16_TFLOPS}}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -568,6 +632,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-act", action="store_true")
+    ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
@@ -618,6 +683,9 @@ def main():
     if not args.no_act:
         log(f"adaptive halting: {w.name} ...")
         out["act"] = bench_act(args, torch, gl, synth, w)
+    if not args.no_block:
+        log(f"LT2 block stack: {w.name} ...")
+        out["block"] = bench_block(args, torch, gl, synth, w.name)
     if not args.no_backward:
         log("scan backward: the 4096-token prompt's shape ...")
         out["scan_backward"] = bench_backward(args, torch, gl, synth)

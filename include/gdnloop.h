@@ -307,6 +307,56 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
                              float *dWv, float *dwa, float *dwb, float *drho, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* ---- the LT2 block around the mixer ------------------------------------- */
+
+/* Passage: LT2: Linear-Time Looped Transformers, Section 2 ("Looped
+ * Transformer (LT)": a block is a token mixer and a position-wise FFN, each
+ * with an identity residual, pre-norm omitted from Eq. (1) for brevity, and
+ * the N blocks are reused for T iterations; "LT2": the mixer is the linear
+ * one and h^(tau) = (F_N o ... o F_1)(h^(tau-1)) + rho_tau (.) h^(tau-1)), and
+ * Section 3's attention-sink paragraph (the head-specific sigmoid output gate
+ * of Gated Attention, applied inside the looped block).  One block:
+ *     x1 = RMSNorm(h; g1)            [x / sqrt(mean(x^2) + norm_eps) * g]
+ *     o  = the gated-delta-rule mixer of x1 (projections, L2 norm, gates and
+ *          the scan from S = 0, exactly as one loop of gdn_loop_prefill)
+ *     z  = o (.) sigmoid(x1 Wg)       Wg [d, H*dv]: one gate per head channel
+ *     h1 = h + z Wo                   Wo [H*dv, d]
+ *     x2 = RMSNorm(h1; g2)
+ *     F(h) = h1 + (silu(x2 W1) (.) (x2 W3)) W2     W1, W3 [d, ffn], W2 [ffn, d]
+ * For bf16 workloads x1, q/k/v, z, x2 and silu(.)(.) are rounded to bf16 (the
+ * products' operands); h, h1, o, the norms' statistics and the gates stay
+ * fp32.  ffn must be a positive multiple of 64. */
+
+/* Bytes of one packed block (desc->act weights plus the fp32 norm weights). */
+gdn_status gdn_block_packed_bytes(const gdn_desc *desc, int ffn, size_t *bytes);
+/* Pack one block's weights (device pointers): g1, g2 [d] fp32; Wq, Wk [d, H*dk],
+ * Wv [d, H*dv], wa, wb [d, H] (as gdn_weights_pack), Wg [d, H*dv], Wo [H*dv, d],
+ * W1, W3 [d, ffn], W2 [ffn, d] in desc->act.  Wblock: gdn_block_packed_bytes,
+ * opaque, 256-byte aligned. */
+gdn_status gdn_block_pack(const gdn_desc *desc, int ffn, const float *g1, const void *Wq, const void *Wk,
+                          const void *Wv, const void *wa, const void *wb, const void *Wg, const void *Wo,
+                          const float *g2, const void *W1, const void *W3, const void *W2, void *Wblock,
+                          void *stream);
+/* Workspace of gdn_block_forward and gdn_block_loop_prefill. */
+gdn_status gdn_block_workspace_bytes(const gdn_desc *desc, int ffn, size_t *bytes);
+/* Regions of that workspace that hold, after gdn_block_forward (or after the
+ * last block of gdn_block_loop_prefill), that block's intermediates:
+ *   GDN_BWS_X1, GDN_BWS_X2 [B*L, d] desc->act; GDN_BWS_O [B*L, H*dv] fp32;
+ *   GDN_BWS_Z [B*L, H*dv] desc->act; GDN_BWS_H1 [B*L, d] fp32;
+ *   GDN_BWS_U [B*L, ffn] desc->act; GDN_WS_Q .. GDN_WS_BETA as for the loop. */
+enum { GDN_BWS_X1 = 16, GDN_BWS_O = 17, GDN_BWS_Z = 18, GDN_BWS_H1 = 19, GDN_BWS_X2 = 20, GDN_BWS_U = 21 };
+gdn_status gdn_block_workspace_region(const gdn_desc *desc, int ffn, int region, size_t *offset, size_t *bytes);
+/* One block on h [B, L, d] device fp32: out = F(h) [B, L, d] device fp32
+ * (desc->T is ignored).  out may not alias h. */
+gdn_status gdn_block_forward(const gdn_desc *desc, int ffn, const float *h, const void *Wblock, float *out,
+                             void *ws, size_t ws_bytes, void *stream);
+/* T loops of a stack of `layers` blocks (Wblocks: that many packed blocks
+ * back to back, each gdn_block_packed_bytes): h^(tau) = F_N(...F_1(h^(tau-1)))
+ * + rho_tau (.) h^(tau-1).  h0 [B, L, d] desc->act, rho [T, d] fp32, h_out
+ * [B, L, d] fp32 (may not alias h0). */
+gdn_status gdn_block_loop_prefill(const gdn_desc *desc, int ffn, int layers, const void *h0, const void *Wblocks,
+                                  const float *rho, float *h_out, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 
 const char *gdn_status_string(gdn_status s);
@@ -321,7 +371,10 @@ const char *gdn_version(void);
  * output pass that the carry now performs, and gdn_timer_create rejects it). */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
        GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5, GDN_STAGE_BWD_CARRY = 6, GDN_STAGE_BWD_CHUNK = 7,
-       GDN_STAGE_BWD_PREP = 8, GDN_STAGE_BWD_GEMM = 9, GDN_STAGE_BWD_OPS = 10 };
+       GDN_STAGE_BWD_PREP = 8, GDN_STAGE_BWD_GEMM = 9, GDN_STAGE_BWD_OPS = 10, GDN_STAGE_BLOCK_GEMM = 11 };
+/* GDN_STAGE_BLOCK_GEMM times the four products of an LT2 block around its
+ * mixer (the gate with o, the output projection, the FFN's up and down
+ * projections); the mixer's own launches keep their stages. */
 /* GDN_STAGE_BWD_GEMM times the three products of each loop of
  * gdn_loop_backward (the projections recomputed, the input gradient and the
  * weight gradient). */

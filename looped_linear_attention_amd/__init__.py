@@ -20,16 +20,19 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL",
-    "GDN_OP_SCAN_DECODE", "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_OP_LOOP_PREFILL_ACT", "GDN_OP_LOOP_BACKWARD", "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP",
-    "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES", "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_PREP",
-    "GDN_STAGE_BWD_GEMM", "GDN_STAGE_BWD_OPS", "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V",
-    "GDN_WS_ALPHA", "GDN_WS_BETA", "GdnError", "gdn_desc", "make_desc", "lib_path",
-    "load", "EXPORTED", "workspace", "workspace_view", "gdn_workspace_region",
-    "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act", "gdn_loop_decode", "gdn_loop_decode_noalloc",
-    "gdn_loop_backward", "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
-    "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
+    "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL", "GDN_OP_SCAN_DECODE",
+    "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_OP_LOOP_PREFILL_ACT", "GDN_OP_LOOP_BACKWARD",
+    "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP", "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES",
+    "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_PREP", "GDN_STAGE_BWD_GEMM", "GDN_STAGE_BWD_OPS",
+    "GDN_STAGE_BLOCK_GEMM", "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V", "GDN_WS_ALPHA", "GDN_WS_BETA", "GDN_BWS_X1",
+    "GDN_BWS_O", "GDN_BWS_Z", "GDN_BWS_H1", "GDN_BWS_X2", "GDN_BWS_U", "GdnError", "gdn_desc", "make_desc",
+    "lib_path", "load", "EXPORTED", "workspace", "workspace_view", "block_workspace", "block_workspace_view",
+    "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
+    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act",
+    "gdn_loop_decode", "gdn_loop_decode_noalloc", "gdn_loop_backward", "gdn_block_packed_bytes", "gdn_block_pack",
+    "gdn_block_workspace_bytes", "gdn_block_workspace_region", "gdn_block_forward", "gdn_block_loop_prefill",
+    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride",
+    "gdn_timer_attach", "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -37,14 +40,18 @@ GDN_F32, GDN_BF16 = 0, 1
  GDN_OP_LOOP_PREFILL_ACT, GDN_OP_LOOP_BACKWARD) = range(8)
 GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_GATES = 0, 1, 2, 3, 5
 GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_GEMM, GDN_STAGE_BWD_OPS = 6, 7, 8, 9, 10
+GDN_STAGE_BLOCK_GEMM = 11
 GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
+GDN_BWS_X1, GDN_BWS_O, GDN_BWS_Z, GDN_BWS_H1, GDN_BWS_X2, GDN_BWS_U = range(16, 22)
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
-    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act", "gdn_loop_decode", "gdn_loop_decode_noalloc",
-    "gdn_loop_backward", "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride", "gdn_timer_attach",
-    "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
+    "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act",
+    "gdn_loop_decode", "gdn_loop_decode_noalloc", "gdn_loop_backward", "gdn_block_packed_bytes", "gdn_block_pack",
+    "gdn_block_workspace_bytes", "gdn_block_workspace_region", "gdn_block_forward", "gdn_block_loop_prefill",
+    "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride",
+    "gdn_timer_attach", "gdn_timer_detach", "gdn_timer_reset", "gdn_timer_read", "gdn_timer_destroy",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +108,12 @@ def load():
         "gdn_loop_prefill_act": [D, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, P, P, S, P],
         "gdn_loop_decode_noalloc": [D, P, P, P, P, P, P],
         "gdn_loop_backward": [D] + [P] * 13 + [S, P],
+        "gdn_block_packed_bytes": [D, I, ctypes.POINTER(S)],
+        "gdn_block_pack": [D, I] + [P] * 14,
+        "gdn_block_workspace_bytes": [D, I, ctypes.POINTER(S)],
+        "gdn_block_workspace_region": [D, I, I, ctypes.POINTER(S), ctypes.POINTER(S)],
+        "gdn_block_forward": [D, I, P, P, P, P, S, P],
+        "gdn_block_loop_prefill": [D, I, I, P, P, P, P, P, S, P],
         "gdn_timer_create": [I, I, ctypes.POINTER(P)],
         "gdn_timer_set_stride": [P, I],
         "gdn_timer_attach": [P],
@@ -212,6 +225,77 @@ def workspace_view(ws: torch.Tensor, desc: gdn_desc, op: int, region: int) -> to
     if region in (GDN_WS_ALPHA, GDN_WS_BETA):
         return raw.view(torch.float32).view(tokens, desc.H)
     return raw.view(desc.act_dtype).view(tokens, desc.H, desc.dk)
+
+
+def gdn_block_packed_bytes(desc: gdn_desc, ffn: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().gdn_block_packed_bytes(ctypes.byref(desc), ffn, ctypes.byref(n)))
+    return n.value
+
+
+def gdn_block_workspace_bytes(desc: gdn_desc, ffn: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().gdn_block_workspace_bytes(ctypes.byref(desc), ffn, ctypes.byref(n)))
+    return n.value
+
+
+def block_workspace(desc: gdn_desc, ffn: int, device="cuda") -> torch.Tensor:
+    """Allocate the device workspace of the LT2 block calls (torch owns the memory)."""
+    return torch.empty(max(gdn_block_workspace_bytes(desc, ffn), 256), dtype=torch.uint8, device=device)
+
+
+def gdn_block_workspace_region(desc: gdn_desc, ffn: int, region: int):
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().gdn_block_workspace_region(ctypes.byref(desc), ffn, region, ctypes.byref(off), ctypes.byref(n)))
+    return off.value, n.value
+
+
+def block_workspace_view(ws: torch.Tensor, desc: gdn_desc, ffn: int, region: int) -> torch.Tensor:
+    """A typed view of a block workspace region ([B*L, width] in its dtype; q/k/v [B*L, H, D])."""
+    off, n = gdn_block_workspace_region(desc, ffn, region)
+    if ws.numel() * ws.element_size() < off + n:
+        raise GdnError("workspace is smaller than the region")
+    raw = ws.view(torch.uint8)[off:off + n]
+    tokens = desc.B * desc.L
+    if region in (GDN_WS_ALPHA, GDN_WS_BETA):
+        return raw.view(torch.float32).view(tokens, desc.H)
+    if region in (GDN_WS_Q, GDN_WS_K, GDN_WS_V):
+        return raw.view(desc.act_dtype).view(tokens, desc.H, desc.dk)
+    dt = torch.float32 if region in (GDN_BWS_O, GDN_BWS_H1) else desc.act_dtype
+    return raw.view(dt).view(tokens, -1)
+
+
+def gdn_block_pack(desc, ffn, g1, Wq, Wk, Wv, wa, wb, Wg, Wo, g2, W1, W3, W2, Wblock, stream=None):
+    a, d, H, dk, dv, f = desc.act_dtype, desc.d, desc.H, desc.dk, desc.dv, torch.float32
+    n = gdn_block_packed_bytes(desc, ffn)
+    if Wblock.numel() * Wblock.element_size() != n or Wblock.device.type != "cuda":
+        raise GdnError(f"Wblock must be a device buffer of {n} bytes")
+    _check(load().gdn_block_pack(
+        ctypes.byref(desc), ffn, _ptr(g1, "g1", f, d), _ptr(Wq, "Wq", a, d * H * dk), _ptr(Wk, "Wk", a, d * H * dk),
+        _ptr(Wv, "Wv", a, d * H * dv), _ptr(wa, "wa", a, d * H), _ptr(wb, "wb", a, d * H),
+        _ptr(Wg, "Wg", a, d * H * dv), _ptr(Wo, "Wo", a, H * dv * d), _ptr(g2, "g2", f, d),
+        _ptr(W1, "W1", a, d * ffn), _ptr(W3, "W3", a, d * ffn), _ptr(W2, "W2", a, ffn * d),
+        ctypes.c_void_p(Wblock.data_ptr()), _stream(stream)))
+
+
+def gdn_block_forward(desc, ffn, h, Wblock, out, ws, stream=None):
+    BL, d = desc.B * desc.L, desc.d
+    wp, wn = _ws(ws)
+    _check(load().gdn_block_forward(
+        ctypes.byref(desc), ffn, _ptr(h, "h", torch.float32, BL * d), ctypes.c_void_p(Wblock.data_ptr()),
+        _ptr(out, "out", torch.float32, BL * d), wp, wn, _stream(stream)))
+
+
+def gdn_block_loop_prefill(desc, ffn, layers, h0, Wblocks, rho, h_out, ws, stream=None):
+    BL, d, T = desc.B * desc.L, desc.d, desc.T
+    n = gdn_block_packed_bytes(desc, ffn) * layers
+    if Wblocks.numel() * Wblocks.element_size() != n or Wblocks.device.type != "cuda":
+        raise GdnError(f"Wblocks must be a device buffer of {n} bytes ({layers} packed blocks)")
+    wp, wn = _ws(ws)
+    _check(load().gdn_block_loop_prefill(
+        ctypes.byref(desc), ffn, layers, _ptr(h0, "h0", desc.act_dtype, BL * d), ctypes.c_void_p(Wblocks.data_ptr()),
+        _ptr(rho, "rho", torch.float32, T * d), _ptr(h_out, "h_out", torch.float32, BL * d), wp, wn,
+        _stream(stream)))
 
 
 def gdn_weights_pack(desc, Wq, Wk, Wv, wa, wb, Wpack, stream=None):

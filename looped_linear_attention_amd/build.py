@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libgdnloop.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["proj_gemm.hip", "scan_chunk.hip", "scan_backward.hip", "act.hip", "decode.hip",
-           "loop_decode_noalloc.hip", "gemm_nt.hip", "gemm_tile.hip", "loop_backward.hip", "gdnloop_api.cpp"]
+           "loop_decode_noalloc.hip", "gemm_nt.hip", "gemm_tile.hip", "loop_backward.hip", "block.hip", "gdnloop_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

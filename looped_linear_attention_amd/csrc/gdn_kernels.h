@@ -104,6 +104,16 @@ struct CarryOut {
 hipError_t launch_act_init(int M, float *R, int *halt, hipStream_t s);
 hipError_t launch_act_halt(int M, int d, const float *h, const float *w, float b, float thr, int tau, int T, float *R,
                            int *halt, int *halt_out, float *ponder_out, hipStream_t s);
+// ---- the LT2 block's token-local kernels (block.hip) ----
+// out = h / sqrt(mean(h^2) + eps) * g per row of d (d a multiple of 4).
+hipError_t launch_rmsnorm(bool in_f32, bool out_f32, int M, int d, const void *h, const float *g, float eps,
+                          void *out, hipStream_t s);
+// W13 [2F][d] from W1, W3 [d][F]: in each group of 64 packed rows, 32 columns
+// of W1 then the same 32 columns of W3.
+hipError_t launch_pack_w13(bool f32, int d, int F, const void *W1, const void *W3, void *W13, hipStream_t s);
+hipError_t launch_bf16_to_f32(const bf16 *src, float *dst, int64_t n, hipStream_t s);
+hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s);
+
 // ---- token-local steps of the loop backward (loop_backward.hip) ----
 // x[i] = bf16(h[i]) (round to nearest even), n elements, 16-byte aligned.
 hipError_t launch_lb_round(int64_t n, const float *h, bf16 *x, hipStream_t s);
@@ -151,6 +161,11 @@ hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream
 // hi[c][r] + lo[c][r] ~ in[r][c] (fp32 in [R][ldi]), zero for R <= r < Rp.
 hipError_t launch_transpose_split(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldo,
                                   int Rp, hipStream_t s);
+// The same product with every epilogue of launch_gemm_tile (C fp32 or bf16);
+// operand pairs (split, split) and (bf16, bf16).
+hipError_t launch_gemm_nt_ex(int mode_a, int mode_b, int epi, bool out_f32, const void *A, int64_t lda, const void *B,
+                             int64_t ldb, int M, int N, int K, void *C, int64_t ldc, const float *rho,
+                             const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s);
 // out[c][r] = in[r][c] (r < R, c < Cc; fp32 or bf16 either side, RNE to bf16),
 // and 0 for R <= r < Rp.
 hipError_t launch_transpose(bool in_f32, bool out_f32, const void *in, int64_t ldi, int R, int Cc, void *out,

@@ -202,7 +202,7 @@ struct gdn_timer {
 
 namespace {
 
-constexpr int N_STAGES = GDN_STAGE_BWD_OPS + 1;
+constexpr int N_STAGES = GDN_STAGE_BLOCK_GEMM + 1;
 thread_local LaunchEvents t_launch_events{nullptr, nullptr};
 gdn_timer *g_timers[N_STAGES] = {};
 
@@ -534,6 +534,251 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
     return e == hipSuccess ? GDN_OK : hip_fail(e, "weight gradient unpack launch");
 }
 
+// ---- the LT2 block ------------------------------------------------------------
+namespace {
+
+// Offsets (bytes) of a packed block: the mixer's packed weights, Wg^T [HD][d],
+// Wo^T [d][HD], W13 [2F][d] (interleaved), W2^T [d][F], g1, g2 [d] fp32.
+struct BlockPack {
+    size_t mix = 0, wg = 0, wo = 0, w13 = 0, w2 = 0, g1 = 0, g2 = 0, total = 0;
+};
+BlockPack block_pack_layout(const gdn_desc *d, int F) {
+    BlockPack b;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    const size_t ab = act_bytes(d), HD = (size_t)d->H * d->dv, D = d->d;
+    b.mix = take((size_t)packed_rows(d->H, d->dk) * D * ab);
+    b.wg = take(HD * D * ab);
+    b.wo = take(D * HD * ab);
+    b.w13 = take((size_t)2 * F * D * ab);
+    b.w2 = take(D * (size_t)F * ab);
+    b.g1 = take(D * 4);
+    b.g2 = take(D * 4);
+    b.total = off;
+    return b;
+}
+
+// The block's workspace: the loop prefill's (q, k, v, gates, gate partials,
+// chunk matrices), then X1, O, Z, H1, X2, U and the fp32 stream buffers of
+// the loop (its converted input, two loop outputs, two block outputs).
+struct BlockLayout {
+    Layout lo;
+    size_t x1 = 0, o = 0, z = 0, h1 = 0, x2 = 0, u = 0, hin = 0, lp[2] = {0, 0}, ch[2] = {0, 0}, total = 0;
+};
+BlockLayout block_layout(const gdn_desc *d, int F) {
+    BlockLayout b;
+    b.lo = layout(d, GDN_OP_LOOP_PREFILL);
+    size_t off = b.lo.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    const size_t M = (size_t)d->B * d->L, ab = act_bytes(d), HD = (size_t)d->H * d->dv, D = d->d;
+    b.x1 = take(M * D * ab);
+    b.o = take(M * HD * 4);
+    b.z = take(M * HD * ab);
+    b.h1 = take(M * D * 4);
+    b.x2 = take(M * D * ab);
+    b.u = take(M * (size_t)F * ab);
+    b.hin = take(M * D * 4);
+    b.lp[0] = take(M * D * 4);
+    b.lp[1] = take(M * D * 4);
+    b.ch[0] = take(M * D * 4);
+    b.ch[1] = take(M * D * 4);
+    b.total = off;
+    return b;
+}
+
+gdn_status check_block(const gdn_desc *desc, int ffn) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
+    if (ffn <= 0 || ffn % 64) return fail(GDN_ERR_SHAPE, "ffn must be a positive multiple of 64 (got %d)", ffn);
+    if ((int64_t)desc->B * desc->L * ffn > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "problem too large");
+    return GDN_OK;
+}
+
+// One product of the block: bf16 workloads on the tiled kernel, fp32 ones on
+// the split-operand kernel.
+hipError_t block_gemm(bool f32, int epi, bool out_f32, const void *A, int64_t lda, const void *B, int64_t ldb, int M,
+                      int N, int K, void *C, int64_t ldc, const float *rho, const float *D1, int64_t ldd1,
+                      const float *D2, int64_t ldd2, hipStream_t s) {
+    return timed(GDN_STAGE_BLOCK_GEMM, s, [&] {
+        if (f32)
+            return launch_gemm_nt_ex(OPND_F32_SPLIT, OPND_F32_SPLIT, epi, out_f32, A, lda, B, ldb, M, N, K, C, ldc,
+                                     rho, D1, ldd1, D2, ldd2, s);
+        return launch_gemm_tile(epi, out_f32, (const bf16 *)A, nullptr, lda, (const bf16 *)B, nullptr, ldb, M, N, K,
+                                C, ldc, rho, D1, ldd1, D2, ldd2, s);
+    });
+}
+
+// out = F(hin) (+ rho (.) hres when rho is given: the loop residual of the
+// stack's last block, fused into the down projection).
+gdn_status block_apply(const gdn_desc *desc, int F, const float *hin, const char *Wb, float *out, const float *rho,
+                       const float *hres, void *ws, const BlockLayout &bl, hipStream_t s) {
+    const bool f32 = desc->act == GDN_F32;
+    const int M = desc->B * desc->L, d = desc->d, H = desc->H, D = desc->dk, HD = desc->H * desc->dv;
+    const BlockPack bp = block_pack_layout(desc, F);
+    const Layout &lo = bl.lo;
+    void *x1 = at(ws, bl.x1), *z = at(ws, bl.z), *x2 = at(ws, bl.x2), *u = at(ws, bl.u);
+    float *o = (float *)at(ws, bl.o), *h1 = (float *)at(ws, bl.h1);
+    void *q = at(ws, lo.q), *k = at(ws, lo.k), *v = at(ws, lo.v);
+    float *al = (float *)at(ws, lo.alpha), *be = (float *)at(ws, lo.beta);
+    float *zp = lo.P ? (float *)at(ws, lo.zp) : nullptr;
+    const float *g1 = (const float *)(Wb + bp.g1), *g2 = (const float *)(Wb + bp.g2);
+    hipError_t e = launch_rmsnorm(true, f32, M, d, hin, g1, desc->norm_eps, x1, s);
+    if (e != hipSuccess) return hip_fail(e, "norm launch");
+    e = project(f32, M, d, H, D, x1, Wb + bp.mix, q, k, v, al, be, desc->alpha_lo, desc->norm_eps, zp, s);
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
+    CarryOut out_o{o, nullptr, false, nullptr, nullptr, nullptr, nullptr, nullptr};
+    gdn_status st = scan_chunks(desc, q, k, v,
+                                GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
+                                nullptr, nullptr, out_o, ws, lo, s);
+    if (st != GDN_OK) return st;
+    // z = o (.) sigmoid(x1 Wg); h1 = h + z Wo
+    if ((e = block_gemm(f32, EPI_GATE, f32, x1, d, Wb + bp.wg, d, M, HD, d, z, HD, nullptr, o, HD, nullptr, 0, s)) !=
+        hipSuccess)
+        return hip_fail(e, "gate product launch");
+    if ((e = block_gemm(f32, EPI_ADD, true, z, HD, Wb + bp.wo, HD, M, d, HD, h1, d, nullptr, hin, d, nullptr, 0, s)) !=
+        hipSuccess)
+        return hip_fail(e, "output projection launch");
+    // FFN: u = silu(x2 W1) (.) (x2 W3); out = h1 + u W2 (+ rho (.) hres)
+    if ((e = launch_rmsnorm(true, f32, M, d, h1, g2, desc->norm_eps, x2, s)) != hipSuccess)
+        return hip_fail(e, "norm launch");
+    if ((e = block_gemm(f32, EPI_SWIGLU, f32, x2, d, Wb + bp.w13, d, M, 2 * F, d, u, F, nullptr, nullptr, 0, nullptr,
+                        0, s)) != hipSuccess)
+        return hip_fail(e, "FFN up-projection launch");
+    e = block_gemm(f32, rho ? EPI_ADD_RESID : EPI_ADD, true, u, F, Wb + bp.w2, F, M, d, F, out, d, rho, h1, d, hres,
+                   d, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "FFN down-projection launch");
+}
+
+}  // namespace
+
+gdn_status gdn_block_packed_bytes(const gdn_desc *desc, int ffn, size_t *bytes) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if (ffn <= 0 || ffn % 64) return fail(GDN_ERR_SHAPE, "ffn must be a positive multiple of 64 (got %d)", ffn);
+    if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
+    *bytes = block_pack_layout(desc, ffn).total;
+    return GDN_OK;
+}
+
+gdn_status gdn_block_pack(const gdn_desc *desc, int ffn, const float *g1, const void *Wq, const void *Wk,
+                          const void *Wv, const void *wa, const void *wb, const void *Wg, const void *Wo,
+                          const float *g2, const void *W1, const void *W3, const void *W2, void *Wblock,
+                          void *stream) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if (ffn <= 0 || ffn % 64) return fail(GDN_ERR_SHAPE, "ffn must be a positive multiple of 64 (got %d)", ffn);
+    REQUIRE_PTR(g1); REQUIRE_PTR(Wq); REQUIRE_PTR(Wk); REQUIRE_PTR(Wv); REQUIRE_PTR(wa); REQUIRE_PTR(wb);
+    REQUIRE_PTR(Wg); REQUIRE_PTR(Wo); REQUIRE_PTR(g2); REQUIRE_PTR(W1); REQUIRE_PTR(W3); REQUIRE_PTR(W2);
+    REQUIRE_PTR(Wblock);
+    if (((uintptr_t)Wblock) % 256) return fail(GDN_ERR_ALIGN, "Wblock is not 256-byte aligned");
+    const hipStream_t s = (hipStream_t)stream;
+    const bool f32 = desc->act == GDN_F32;
+    const int d = desc->d, HD = desc->H * desc->dv;
+    const BlockPack bp = block_pack_layout(desc, ffn);
+    char *W = (char *)Wblock;
+    hipError_t e = launch_pack_weights(f32, d, desc->H, desc->dk, Wq, Wk, Wv, wa, wb, W + bp.mix, s);
+    if (e == hipSuccess) e = launch_transpose(f32, f32, Wg, HD, d, HD, W + bp.wg, d, d, s);     // [HD][d]
+    if (e == hipSuccess) e = launch_transpose(f32, f32, Wo, d, HD, d, W + bp.wo, HD, HD, s);    // [d][HD]
+    if (e == hipSuccess) e = launch_pack_w13(f32, d, ffn, W1, W3, W + bp.w13, s);
+    if (e == hipSuccess) e = launch_transpose(f32, f32, W2, d, ffn, d, W + bp.w2, ffn, ffn, s); // [d][F]
+    if (e == hipSuccess) e = launch_copy_f32(g1, (float *)(W + bp.g1), d, s);
+    if (e == hipSuccess) e = launch_copy_f32(g2, (float *)(W + bp.g2), d, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "block pack launch");
+}
+
+gdn_status gdn_block_workspace_bytes(const gdn_desc *desc, int ffn, size_t *bytes) {
+    gdn_status st = check_block(desc, ffn);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
+    *bytes = block_layout(desc, ffn).total;
+    return GDN_OK;
+}
+
+gdn_status gdn_block_workspace_region(const gdn_desc *desc, int ffn, int region, size_t *offset, size_t *bytes) {
+    gdn_status st = check_block(desc, ffn);
+    if (st != GDN_OK) return st;
+    if (!offset || !bytes) return fail(GDN_ERR_NULL, "offset or bytes is NULL");
+    const BlockLayout bl = block_layout(desc, ffn);
+    const size_t M = (size_t)desc->B * desc->L, ab = act_bytes(desc), HD = (size_t)desc->H * desc->dv;
+    const size_t D = desc->d, qkv = M * desc->H * desc->dk * ab, gate = M * desc->H * 4;
+    switch (region) {
+        case GDN_WS_Q: *offset = bl.lo.q; *bytes = qkv; break;
+        case GDN_WS_K: *offset = bl.lo.k; *bytes = qkv; break;
+        case GDN_WS_V: *offset = bl.lo.v; *bytes = qkv; break;
+        case GDN_WS_ALPHA: *offset = bl.lo.alpha; *bytes = gate; break;
+        case GDN_WS_BETA: *offset = bl.lo.beta; *bytes = gate; break;
+        case GDN_BWS_X1: *offset = bl.x1; *bytes = M * D * ab; break;
+        case GDN_BWS_O: *offset = bl.o; *bytes = M * HD * 4; break;
+        case GDN_BWS_Z: *offset = bl.z; *bytes = M * HD * ab; break;
+        case GDN_BWS_H1: *offset = bl.h1; *bytes = M * D * 4; break;
+        case GDN_BWS_X2: *offset = bl.x2; *bytes = M * D * ab; break;
+        case GDN_BWS_U: *offset = bl.u; *bytes = M * (size_t)ffn * ab; break;
+        default: return fail(GDN_ERR_UNSUPPORTED, "unknown block workspace region %d", region);
+    }
+    return GDN_OK;
+}
+
+gdn_status gdn_block_forward(const gdn_desc *desc, int ffn, const float *h, const void *Wblock, float *out,
+                             void *ws, size_t ws_bytes, void *stream) {
+    gdn_status st = check_block(desc, ffn);
+    if (st != GDN_OK) return st;
+    REQUIRE_PTR(h); REQUIRE_PTR(Wblock); REQUIRE_PTR(out);
+    if ((const void *)out == (const void *)h) return fail(GDN_ERR_SHAPE, "out may not alias h");
+    const BlockLayout bl = block_layout(desc, ffn);
+    if (!ws || ws_bytes < bl.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", bl.total, ws_bytes);
+    if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+    return block_apply(desc, ffn, h, (const char *)Wblock, out, nullptr, nullptr, ws, bl, (hipStream_t)stream);
+}
+
+gdn_status gdn_block_loop_prefill(const gdn_desc *desc, int ffn, int layers, const void *h0, const void *Wblocks,
+                                  const float *rho, float *h_out, void *ws, size_t ws_bytes, void *stream) {
+    gdn_status st = check_block(desc, ffn);
+    if (st != GDN_OK) return st;
+    if (layers < 1) return fail(GDN_ERR_SHAPE, "layers must be >= 1 (got %d)", layers);
+    REQUIRE_PTR(h0); REQUIRE_PTR(Wblocks); REQUIRE_PTR(rho); REQUIRE_PTR(h_out);
+    if ((const void *)h_out == h0) return fail(GDN_ERR_SHAPE, "h_out may not alias h0");
+    const BlockLayout bl = block_layout(desc, ffn);
+    if (!ws || ws_bytes < bl.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", bl.total, ws_bytes);
+    if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+    const hipStream_t s = (hipStream_t)stream;
+    const bool f32 = desc->act == GDN_F32;
+    const int64_t n = (int64_t)desc->B * desc->L * desc->d;
+    const size_t stride = block_pack_layout(desc, ffn).total;
+    // the loop stream is fp32: a bf16 h0 is widened once
+    const float *hin0 = (const float *)h0;
+    if (!f32) {
+        hipError_t e = launch_bf16_to_f32((const bf16 *)h0, (float *)at(ws, bl.hin), n, s);
+        if (e != hipSuccess) return hip_fail(e, "widen launch");
+        hin0 = (const float *)at(ws, bl.hin);
+    }
+    const int T = desc->T;
+    for (int tau = 0; tau < T; ++tau) {
+        const float *hp = tau == 0 ? hin0 : (const float *)at(ws, bl.lp[(tau - 1) & 1]);
+        float *loop_out = tau == T - 1 ? h_out : (float *)at(ws, bl.lp[tau & 1]);
+        const float *x = hp;
+        for (int l = 0; l < layers; ++l) {
+            const bool last = l == layers - 1;
+            float *dst = last ? loop_out : (float *)at(ws, bl.ch[l & 1]);
+            st = block_apply(desc, ffn, x, (const char *)Wblocks + (size_t)l * stride, dst,
+                             last ? rho + (int64_t)tau * desc->d : nullptr, last ? hp : nullptr, ws, bl, s);
+            if (st != GDN_OK) return st;
+            x = dst;
+        }
+    }
+    return GDN_OK;
+}
+
 gdn_status gdn_scan_decode(const gdn_desc *desc, const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta, float *states, float *o,
                            void *stream) {
@@ -692,7 +937,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BWD_OPS || stage == 4 || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BLOCK_GEMM || stage == 4 || capacity < 1 || capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

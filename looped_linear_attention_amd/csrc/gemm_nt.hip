@@ -19,6 +19,7 @@
 // the current one is multiplied.
 #include "gdn_device.h"
 #include "gdn_kernels.h"
+#include "gemm_epi.h"
 
 namespace gdn {
 
@@ -92,11 +93,11 @@ __device__ __forceinline__ void stage_store(const Stage<MODE> &st, bf16 *hi, bf1
     }
 }
 
-template <int MA, int MB, int EPI>
+template <int MA, int MB, int EPI, typename TOut>
 __global__ __launch_bounds__(256) void k_gemm_nt(const Elem<MA> *__restrict__ A, int64_t lda,
                                                  const Elem<MB> *__restrict__ B, int64_t ldb, int M, int N, int K,
-                                                 float *C, int64_t ldc, const float *__restrict__ rho,
-                                                 const float *Dsrc, int64_t ldd) {
+                                                 TOut *C, int64_t ldc, const float *__restrict__ rho,
+                                                 const float *D1, int64_t ldd1, const float *D2, int64_t ldd2) {
     constexpr bool SA = MA == OPND_F32_SPLIT, SB = MB == OPND_F32_SPLIT;
     __shared__ bf16 lds[(2 + SA + SB) * PLANE];
     bf16 *Ah = lds, *Bh = lds + PLANE;
@@ -153,18 +154,19 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const Elem<MA> *__restrict__ A,
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn + 32 * j + (lane & 31);
-            if (n >= N) continue;
-            const float r = EPI == EPI_RESID ? rho[n] : 0.f;
+        for (int e = 0; e < 16; ++e) {
+            const int m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m >= M) continue;
+            if constexpr (EPI == EPI_SWIGLU) {
+                // packed rows 64 g + r and 64 g + 32 + r are column r of W1 and W3 in group g
+                const int f = (n0 + wn) / 2 + (lane & 31);
+                if (f < N / 2) C[(int64_t)m * ldc + f] = from_f32<TOut>(swiglu(acc[i][0][e], acc[i][1][e]));
+            } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (m >= M) continue;
-                float *c = C + (int64_t)m * ldc + n;
-                if constexpr (EPI == EPI_STORE) *c = acc[i][j][e];
-                else if constexpr (EPI == EPI_ACCUM) *c += acc[i][j][e];
-                else *c = acc[i][j][e] + r * Dsrc[(int64_t)m * ldd + n];
+                for (int j = 0; j < 2; ++j) {
+                    const int n = n0 + wn + 32 * j + (lane & 31);
+                    if (n < N) epi_apply<EPI, TOut>(acc[i][j][e], m, n, C, ldc, rho, D1, ldd1, D2, ldd2);
+                }
             }
         }
 }
@@ -236,38 +238,65 @@ __global__ __launch_bounds__(256) void k_split(const float *__restrict__ x, bf16
     }
 }
 
-template <int MA, int MB>
-hipError_t gemm_launch(int epi, const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N, int K,
-                       float *C, int64_t ldc, const float *rho, const float *Dsrc, int64_t ldd, hipStream_t s) {
+template <int MA, int MB, int EPI, typename TOut>
+void gemm_launch(const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N, int K, void *C, int64_t ldc,
+                 const float *rho, const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s) {
     const dim3 grid((N + TN - 1) / TN, (M + TM - 1) / TM);
-    const auto *a = (const Elem<MA> *)A;
-    const auto *b = (const Elem<MB> *)B;
-    if (epi == EPI_STORE)
-        launch_kernel(k_gemm_nt<MA, MB, EPI_STORE>, grid, dim3(256), 0, s, a, lda, b, ldb, M, N, K, C, ldc, rho, Dsrc, ldd);
-    else if (epi == EPI_ACCUM)
-        launch_kernel(k_gemm_nt<MA, MB, EPI_ACCUM>, grid, dim3(256), 0, s, a, lda, b, ldb, M, N, K, C, ldc, rho, Dsrc, ldd);
-    else
-        launch_kernel(k_gemm_nt<MA, MB, EPI_RESID>, grid, dim3(256), 0, s, a, lda, b, ldb, M, N, K, C, ldc, rho, Dsrc, ldd);
+    launch_kernel(k_gemm_nt<MA, MB, EPI, TOut>, grid, dim3(256), 0, s, (const Elem<MA> *)A, lda, (const Elem<MB> *)B,
+                  ldb, M, N, K, (TOut *)C, ldc, rho, D1, ldd1, D2, ldd2);
+}
+
+template <int MA, int MB>
+hipError_t gemm_modes(int epi, bool out_f32, const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N,
+                      int K, void *C, int64_t ldc, const float *rho, const float *D1, int64_t ldd1, const float *D2,
+                      int64_t ldd2, hipStream_t s) {
+#define GL(E)                                                                                               \
+    do {                                                                                                    \
+        if (out_f32) gemm_launch<MA, MB, E, float>(A, lda, B, ldb, M, N, K, C, ldc, rho, D1, ldd1, D2, ldd2, s); \
+        else gemm_launch<MA, MB, E, bf16>(A, lda, B, ldb, M, N, K, C, ldc, rho, D1, ldd1, D2, ldd2, s);          \
+    } while (0)
+    switch (epi) {
+        case EPI_STORE: GL(EPI_STORE); break;
+        case EPI_ACCUM:
+            if (!out_f32) return hipErrorInvalidValue;
+            gemm_launch<MA, MB, EPI_ACCUM, float>(A, lda, B, ldb, M, N, K, C, ldc, rho, D1, ldd1, D2, ldd2, s);
+            break;
+        case EPI_RESID: GL(EPI_RESID); break;
+        case EPI_ADD: GL(EPI_ADD); break;
+        case EPI_ADD_RESID: GL(EPI_ADD_RESID); break;
+        case EPI_GATE: GL(EPI_GATE); break;
+        case EPI_SWIGLU: GL(EPI_SWIGLU); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef GL
     return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_gemm_nt_ex(int mode_a, int mode_b, int epi, bool out_f32, const void *A, int64_t lda, const void *B,
+                             int64_t ldb, int M, int N, int K, void *C, int64_t ldc, const float *rho,
+                             const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 8 || lda % 8 || ldb % 8 || (M + TM - 1) / TM > 65535)
+        return hipErrorInvalidValue;
+    const bool need_d1 = epi == EPI_RESID || epi == EPI_ADD || epi == EPI_ADD_RESID || epi == EPI_GATE;
+    if ((need_d1 && !D1) || ((epi == EPI_RESID || epi == EPI_ADD_RESID) && !rho) || (epi == EPI_ADD_RESID && !D2))
+        return hipErrorInvalidValue;
+    if (epi == EPI_SWIGLU && N % 64) return hipErrorInvalidValue;
+    if (mode_a == OPND_F32_SPLIT && mode_b == OPND_F32_SPLIT)
+        return gemm_modes<OPND_F32_SPLIT, OPND_F32_SPLIT>(epi, out_f32, A, lda, B, ldb, M, N, K, C, ldc, rho, D1,
+                                                          ldd1, D2, ldd2, s);
+    if (mode_a == OPND_BF16 && mode_b == OPND_BF16)
+        return gemm_modes<OPND_BF16, OPND_BF16>(epi, out_f32, A, lda, B, ldb, M, N, K, C, ldc, rho, D1, ldd1, D2,
+                                                ldd2, s);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm_nt(int mode_a, int mode_b, int epi, const void *A, int64_t lda, const void *B, int64_t ldb,
                           int M, int N, int K, float *C, int64_t ldc, const float *rho, const float *Dsrc,
                           int64_t ldd, hipStream_t s) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % 8 || lda % 8 || ldb % 8 || (M + TM - 1) / TM > 65535)
-        return hipErrorInvalidValue;
-    if (epi == EPI_RESID && (!rho || !Dsrc)) return hipErrorInvalidValue;
-#define GEMM_CASE(MA, MB) \
-    if (mode_a == MA && mode_b == MB) return gemm_launch<MA, MB>(epi, A, lda, B, ldb, M, N, K, C, ldc, rho, Dsrc, ldd, s);
-    GEMM_CASE(OPND_BF16, OPND_BF16)
-    GEMM_CASE(OPND_F32_ROUND, OPND_BF16)
-    GEMM_CASE(OPND_F32_SPLIT, OPND_BF16)
-    GEMM_CASE(OPND_F32_SPLIT, OPND_F32_SPLIT)
-    GEMM_CASE(OPND_BF16, OPND_F32_SPLIT)
-#undef GEMM_CASE
-    return hipErrorInvalidValue;
+    return launch_gemm_nt_ex(mode_a, mode_b, epi, true, A, lda, B, ldb, M, N, K, C, ldc, rho, Dsrc, ldd, nullptr, 0,
+                             s);
 }
 
 hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream_t s) {

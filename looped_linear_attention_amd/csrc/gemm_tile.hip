@@ -19,6 +19,7 @@
 // row of 32 features is one contiguous 128-byte (fp32) run.
 #include "gdn_device.h"
 #include "gdn_kernels.h"
+#include "gemm_epi.h"
 
 namespace gdn {
 
@@ -165,25 +166,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if constexpr (EPI == EPI_SWIGLU) {
                 // features 64 g + r and 64 g + 32 + r of the packed rows are column r of W1 and W3 in group g
                 const int f = (n0 + wn * 64) / 2 + (lane & 31);
-                if (f < N / 2) {
-                    const float a = acc[ti][0][e], b = acc[ti][1][e];
-                    C[(int64_t)m * ldc + f] = from_f32<TOut>(a / (1.f + expf(-a)) * b);
-                }
+                if (f < N / 2) C[(int64_t)m * ldc + f] = from_f32<TOut>(swiglu(acc[ti][0][e], acc[ti][1][e]));
             } else {
 #pragma unroll
                 for (int tj = 0; tj < 2; ++tj) {
                     const int n = nb + 32 * tj;
-                    if (n >= N) continue;
-                    const float x = acc[ti][tj][e];
-                    TOut *c = C + (int64_t)m * ldc + n;
-                    if constexpr (EPI == EPI_STORE) *c = from_f32<TOut>(x);
-                    else if constexpr (EPI == EPI_ACCUM) *c = from_f32<TOut>(to_f32(*c) + x);
-                    else if constexpr (EPI == EPI_RESID) *c = from_f32<TOut>(x + rho[n] * D1[(int64_t)m * ldd1 + n]);
-                    else if constexpr (EPI == EPI_ADD) *c = from_f32<TOut>(x + D1[(int64_t)m * ldd1 + n]);
-                    else if constexpr (EPI == EPI_ADD_RESID)
-                        *c = from_f32<TOut>(x + D1[(int64_t)m * ldd1 + n] + rho[n] * D2[(int64_t)m * ldd2 + n]);
-                    else if constexpr (EPI == EPI_GATE)
-                        *c = from_f32<TOut>(D1[(int64_t)m * ldd1 + n] / (1.f + expf(-x)));
+                    if (n < N) epi_apply<EPI, TOut>(acc[ti][tj][e], m, n, C, ldc, rho, D1, ldd1, D2, ldd2);
                 }
             }
         }

@@ -31,6 +31,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "workload", "prefill_inputs", "scan_inputs",
     "decode_state_init", "decode_step_inputs", "unit_rows", "grad_inputs", "act_inputs", "ACT_BIAS", "ACT_EPS",
+    "block_ffn", "block_inputs",
 ]
 
 # The halting layer of the adaptive-halting workloads: w ~ N(0, 1/d) and this bias, so that
@@ -205,3 +206,28 @@ def act_inputs(w: Workload, seed: int = 7) -> dict:
     rng = np.random.default_rng(seed)
     wh = rng.standard_normal(w.d, dtype=np.float32) * np.float32(1.0 / math.sqrt(w.d))
     return dict(w_halt=torch.from_numpy(wh), b_halt=ACT_BIAS, eps=ACT_EPS)
+
+
+def block_ffn(w: Workload) -> int:
+    """Hidden width of a block's gated FFN at the workload's width: 8d/3 rounded up to a multiple of 256
+    (5632 at d = 2048, 256 at d = 64)."""
+    return 256 * ((8 * w.d // 3 + 255) // 256)
+
+
+def block_inputs(w: Workload, layers: int, seed: int = 11) -> list:
+    """Weights of `layers` LT2 blocks, drawn per block in this order: g1 = 1 + 0.1 N(0,1) [d] fp32; Wq, Wk
+    ~ N(0,1/d) [d,H*dk]; Wv ~ N(0,1/d) [d,H*dv]; wa, wb ~ N(0,1/d) [d,H]; Wg ~ N(0,1/d) [d,H*dv]; Wo ~
+    N(0,1/(H dv)) [H*dv,d]; g2 as g1; W1, W3 ~ N(0,1/d) [d,F]; W2 ~ N(0,1/F) [F,d] (F = block_ffn).  Matrices
+    in the workload's activation dtype."""
+    rng = np.random.default_rng(seed)
+    d, HK, HV, F = w.d, w.H * w.dk, w.H * w.dv, block_ffn(w)
+    n = lambda rows, cols: _to_act(rng.standard_normal((rows, cols), dtype=np.float32)
+                                   * np.float32(1.0 / math.sqrt(rows)), w.act)
+    out = []
+    for _ in range(layers):
+        blk = dict(g1=torch.from_numpy(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32)))
+        blk.update(Wq=n(d, HK), Wk=n(d, HK), Wv=n(d, HV), wa=n(d, w.H), wb=n(d, w.H), Wg=n(d, HV), Wo=n(HV, d))
+        blk["g2"] = torch.from_numpy(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32))
+        blk.update(W1=n(d, F), W3=n(d, F), W2=n(F, d))
+        out.append(blk)
+    return out

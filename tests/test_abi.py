@@ -250,7 +250,7 @@ def test_binding_checks_tensor_sizes_on_host():
 
 def test_timer_validation(lib):
     h = ctypes.c_void_p()
-    assert lib.gdn_timer_create(11, 4, ctypes.byref(h)) == -2
+    assert lib.gdn_timer_create(12, 4, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(4, 4, ctypes.byref(h)) == -2   # not a stage
     assert lib.gdn_timer_create(0, 0, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(0, 4, None) == -1
@@ -278,3 +278,27 @@ def test_bench_refuses_more_than_one_gpu(argv, env):
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_block_sizes_and_rejections(lib):
+    """Packed block bytes: the mixer's packed weights, Wg^T, Wo^T, W13, W2^T in the activation dtype and the two
+    fp32 norm weights, each region rounded up to 256 bytes; ffn must be a positive multiple of 64."""
+    up = lambda x: (x + 255) // 256 * 256
+    for act, eb in [(gl.GDN_BF16, 2), (gl.GDN_F32, 4)]:
+        H, D = 4, 64
+        d = H * D
+        desc = gl.make_desc(1, 8, H, D, D, act=act)
+        P = (H * 3 * D + 127) // 128 * 128 + 128
+        F = 704
+        exp = up(P * d * eb) + 2 * up(d * d * eb) + up(2 * F * d * eb) + up(d * F * eb) + 2 * up(d * 4)
+        n = ctypes.c_size_t()
+        assert lib.gdn_block_packed_bytes(ctypes.byref(desc), F, ctypes.byref(n)) == 0 and n.value == exp
+        assert lib.gdn_block_packed_bytes(ctypes.byref(desc), 100, ctypes.byref(n)) == -2
+        assert lib.gdn_block_workspace_bytes(ctypes.byref(desc), 0, ctypes.byref(n)) == -2
+    desc = gl.make_desc(1, 64, 2, 128, 128)
+    good = ctypes.c_void_p(0x100000)
+    assert lib.gdn_block_forward(ctypes.byref(desc), 256, good, good, good, good, 1 << 40, None) == -2   # aliasing
+    assert lib.gdn_block_loop_prefill(ctypes.byref(desc), 256, 0, good, good, good, ctypes.c_void_p(0x200000),
+                                      good, 1 << 40, None) == -2   # no layers
+    st = lib.gdn_block_forward(ctypes.byref(desc), 256, good, good, ctypes.c_void_p(0x200000), good, 16, None)
+    assert st == -4 and "workspace" in gl.gdn_last_error()
