@@ -9,9 +9,10 @@
 // about 16 significant bits): the k-loop then runs over passes of the planes
 // (hi.hi, lo.hi and/or hi.lo), all accumulated in fp32.
 //
-// Tile 256 (m) x 256 (n) x 64 (k), eight waves of 128 x 64 (4 x 2 MFMA
-// 32x32x16 tiles, 128 fp32 accumulators per lane).  Operands go global -> LDS
-// with direct loads into two 64 KiB stages: block i+1 lands while block i is
+// Tile 384 (m) x 256 (n) x 64 (k), eight waves of 96 x 128 (3 x 4 MFMA
+// 32x32x16 tiles, 192 fp32 accumulators per lane; each k-step reads 7
+// fragments for 12 MFMAs).  Operands go global -> LDS with direct loads into
+// two 80 KiB stages (the whole LDS): block i+1 lands while block i is
 // multiplied, one wait and one barrier per 64 channels.  The LDS tile rows
 // are XOR-swizzled in 16-byte chunks by row / 2 so that the fragment reads of
 // 16 consecutive rows hit distinct bank groups.  A lane holds, for one
@@ -25,17 +26,17 @@ namespace gdn {
 
 namespace {
 
-constexpr int GM = 256, GN = 256, GK = 64;
+constexpr int GM = 384, GN = 256, GK = 64;
 constexpr int GSA = GM * GK, GSB = GN * GK, GSTAGE = GSA + GSB;   // bf16 elements
 constexpr int G_LDS = 2 * GSTAGE * 2;                             // bytes, two stages
-constexpr int GLOADS = (GSA + GSB) / 8 / 64 / 8;                  // direct loads per wave per block (8)
-constexpr int GLOADS_A = GSA / 8 / 64 / 8;                        // of which A's (4)
+constexpr int GLOADS = (GSA + GSB) / 8 / 64 / 8;                  // direct loads per wave per block (10)
+constexpr int GLOADS_A = GSA / 8 / 64 / 8;                        // of which A's (6)
 
 __device__ __forceinline__ int gswz(int r, int ch) { return r * GK + ((ch ^ ((r >> 1) & 7)) << 3); }
 
 // Per-lane byte offsets of the wave's direct loads, relative to the tile's
 // first row: wave w's load i covers LDS chunks [(8 i' + w) 64, +64) of its
-// operand tile (i' = i for A, i - 4 for B); LDS chunk p holds row p / 8 and
+// operand tile (i' = i for A, i - 6 for B); LDS chunk p holds row p / 8 and
 // logical chunk (p % 8) ^ ((row / 2) % 8).  Rows past the operand's end
 // re-read its last row (their results are never stored).
 struct TileSrc {
@@ -68,13 +69,14 @@ __device__ __forceinline__ void block_bases(const Planes &P, int pass, int kb, c
 template <int EPI, typename TOut>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_tile(
     const bf16 *__restrict__ A, const bf16 *__restrict__ A2, int64_t lda, const bf16 *__restrict__ B,
-    const bf16 *__restrict__ B2, int64_t ldb, int M, int N, int K, int m_tiles, int n_tiles, TOut *C, int64_t ldc,
-    const float *__restrict__ rho, const float *D1, int64_t ldd1, const float *D2, int64_t ldd2) {
+    const bf16 *__restrict__ B2, int64_t ldb, int M, int N, int K, int m_tiles, int n_tiles, TOut *__restrict__ C,
+    int64_t ldc, const float *__restrict__ rho, const float *__restrict__ D1, int64_t ldd1,
+    const float *__restrict__ D2, int64_t ldd2) {
     __shared__ __attribute__((aligned(16))) char smem[G_LDS];
     bf16 *stages = reinterpret_cast<bf16 *>(smem);
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 waves of 128 tokens x 64 features
+    const int wm = wave >> 1, wn = wave & 1;   // 4 x 2 waves of 96 tokens x 128 features
     // Workgroup ids go to the 8 XCDs round-robin; XCD x takes the tiles
     // x, x + 8, ... of the token-tile-major order, so one XCD's tiles share
     // token tiles (A rows) in its L2 as the features advance.
@@ -108,29 +110,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     wait_vmcnt<GLOADS>();   // block 0 has landed; block 1 may be in flight
 
-    f32x16 acc[4][2];
+    f32x16 acc[3][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     struct Fr {
-        bf16x8 a[4], b[2];
+        bf16x8 a[3], b[4];
     };
     auto read = [&](Fr &F, const bf16 *stage, int ks) __attribute__((always_inline)) {
         const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            F.a[i] = *reinterpret_cast<const bf16x8 *>(stage + gswz(wm * 128 + i * 32 + (lane & 31), ch));
+        for (int i = 0; i < 3; ++i)
+            F.a[i] = *reinterpret_cast<const bf16x8 *>(stage + gswz(wm * 96 + i * 32 + (lane & 31), ch));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            F.b[j] = *reinterpret_cast<const bf16x8 *>(stage + GSA + gswz(wn * 64 + j * 32 + (lane & 31), ch));
+        for (int j = 0; j < 4; ++j)
+            F.b[j] = *reinterpret_cast<const bf16x8 *>(stage + GSA + gswz(wn * 128 + j * 32 + (lane & 31), ch));
     };
     // step it: wait for block it's loads, barrier (every wave is done with
-    // block it - 1, whose stage takes block it + 1), four k-steps of 8 MFMAs
-    // with block it + 1's eight direct loads spread between them
+    // block it - 1, whose stage takes block it + 1), four k-steps of 12 MFMAs
+    // with block it + 1's ten direct loads spread between them
     auto kstep = [&](auto load_c, int it) __attribute__((always_inline)) {
         constexpr bool LOAD = decltype(load_c)::value;
         if constexpr (LOAD) wait_vmcnt<0>();
@@ -143,10 +145,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int s = 0; s < 4; ++s) {
             if (s < 3) read(fr[(s + 1) & 1], cur, s + 1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int ti = j / 2, tj = j % 2;
+            for (int j = 0; j < 12; ++j) {
+                const int ti = j / 4, tj = j % 4, i = 12 * s + j;
                 acc[ti][tj] = mfma32x32x16(fr[s & 1].a[ti], fr[s & 1].b[tj], acc[ti][tj]);
-                if (LOAD && j % 4 == 1) ld(2 * s + j / 4);
+                if (LOAD && i % 4 == 1 && i / 4 < GLOADS) ld(i / 4);
             }
         }
     };
@@ -154,24 +156,61 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int it = 1; it < nblk; ++it) kstep(std::true_type(), it);
     wait_vmcnt<0>();   // the repeated loads issued past the last block
 
-    // acc[ti][tj][e]: token m0 + 128 wm + 32 ti + 8 (e / 4) + 4 (lane / 32) + e % 4,
-    //                 feature n0 + 64 wn + 32 tj + lane % 32
-    const int nb = n0 + wn * 64 + (lane & 31);
+    // acc[ti][tj][e]: token m0 + 96 wm + 32 ti + 8 (e / 4) + 4 (lane / 32) + e % 4,
+    //                 feature n0 + 128 wn + 32 tj + lane % 32
+    // Per 32 x 32 tile, the epilogue's operands are all loaded before any of
+    // its results is stored, so the loads go out back to back.
+    const int nb = n0 + wn * 128 + (lane & 31);
+    constexpr bool NEED1 = EPI == EPI_RESID || EPI == EPI_ADD || EPI == EPI_ADD_RESID || EPI == EPI_GATE ||
+                           EPI == EPI_ACCUM;
+    constexpr bool NEED2 = EPI == EPI_ADD_RESID;
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
+    for (int ti = 0; ti < 3; ++ti) {
+        const int mb = m0 + wm * 96 + ti * 32 + 4 * (lane >> 5);
+        if constexpr (EPI == EPI_SWIGLU) {
+            // features 64 g + r and 64 g + 32 + r of the packed rows are column r of W1 and W3 in group g:
+            // tiles (0, 1) and (2, 3) of the wave
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = m0 + wm * 128 + ti * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if (m >= M) continue;
-            if constexpr (EPI == EPI_SWIGLU) {
-                // features 64 g + r and 64 g + 32 + r of the packed rows are column r of W1 and W3 in group g
-                const int f = (n0 + wn * 64) / 2 + (lane & 31);
-                if (f < N / 2) C[(int64_t)m * ldc + f] = from_f32<TOut>(swiglu(acc[ti][0][e], acc[ti][1][e]));
-            } else {
+            for (int e = 0; e < 16; ++e) {
+                const int m = mb + 8 * (e >> 2) + (e & 3);
+                if (m >= M) continue;
 #pragma unroll
-                for (int tj = 0; tj < 2; ++tj) {
-                    const int n = nb + 32 * tj;
-                    if (n < N) epi_apply<EPI, TOut>(acc[ti][tj][e], m, n, C, ldc, rho, D1, ldd1, D2, ldd2);
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int f = (n0 + wn * 128 + 64 * pr) / 2 + (lane & 31);
+                    if (f < N / 2)
+                        C[(int64_t)m * ldc + f] = from_f32<TOut>(swiglu(acc[ti][2 * pr][e], acc[ti][2 * pr + 1][e]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                const int n = nb + 32 * tj;
+                if (n >= N) continue;
+                float d1[16], d2[16];
+                if constexpr (NEED1) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int m = mb + 8 * (e >> 2) + (e & 3);
+                        const bool ok = m < M;
+                        if constexpr (EPI == EPI_ACCUM) d1[e] = ok ? to_f32(C[(int64_t)m * ldc + n]) : 0.f;
+                        else d1[e] = ok ? D1[(int64_t)m * ldd1 + n] : 0.f;
+                        if constexpr (NEED2) d2[e] = ok ? D2[(int64_t)m * ldd2 + n] : 0.f;
+                    }
+                }
+                const float r = (EPI == EPI_RESID || EPI == EPI_ADD_RESID) ? rho[n] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = mb + 8 * (e >> 2) + (e & 3);
+                    if (m >= M) continue;
+                    const float x = acc[ti][tj][e];
+                    float y;
+                    if constexpr (EPI == EPI_STORE) y = x;
+                    else if constexpr (EPI == EPI_ACCUM) y = d1[e] + x;
+                    else if constexpr (EPI == EPI_RESID) y = x + r * d1[e];
+                    else if constexpr (EPI == EPI_ADD) y = x + d1[e];
+                    else if constexpr (EPI == EPI_ADD_RESID) y = x + d1[e] + r * d2[e];
+                    else y = d1[e] / (1.f + expf(-x));   // EPI_GATE
+                    C[(int64_t)m * ldc + n] = from_f32<TOut>(y);
                 }
             }
         }
