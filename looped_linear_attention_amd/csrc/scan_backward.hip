@@ -443,9 +443,67 @@ __global__ __launch_bounds__(BC_THREADS) void k_bwd_carry(const float *__restric
 }
 
 // ---------------------------------------------------------------------------
-// per-chunk gradients: one workgroup per (b, h, chunk), all columns
+// per-chunk gradients: one workgroup (8 waves) per (b, h, chunk), on MFMA
 // ---------------------------------------------------------------------------
+// The columns j of S, dS', dO, dE are walked in blocks of 32.  Per block, wave
+// w (row group rg = w % 4: token rows 16 rg .., column half hc = w / 4):
+//   A. stage S and dS' of the block transposed ([j][i]) and as they are
+//      ([i][j]), and dO transposed ([j][r]), in LDS as bf16 hi/lo planes;
+//   B. K S, Q S, K dS' and P^T dO for its 16 x 16 tile on 16x16x32 MFMA, then
+//      E = V - diag(gamma) K S, dU = P^T dO + diag(c) K dS', its share of
+//      dgamma; E (beta-scaled, transposed; and as is), dU into LDS;
+//   C. U = T diag(beta) E for its tile, its share of dc; U and diag(c) U into LDS;
+//   D. accumulate dP += dO U^T, dTb += dU E^T (two 16 x 16 tiles each) and
+//      dQ += diag(gamma) dO S^T, dK += -diag(gamma) dE S^T + diag(c) U dS'^T
+//      (four 16-row x 16-column tiles each) in registers; the staging of A
+//      also sums S (.) dS' (each element once).
+// fp32 operands enter the MFMA as bf16 hi + lo (3 passes; 2 where one side is
+// an exact bf16 input).  After the blocks: dP and dTb into LDS (fp32), the
+// 64 x 64 steps on the VALU (dT, dN = -T^T dT T^T, dA, dbeta), then dQ +=
+// (Gam (.) dP) K and dK += (Gam (.) dP)^T Q + (Gam (.) dA + (Gam (.) dA)^T) K on
+// MFMA with K^T and Q^T from the carry operands, and the decay gradient.
 constexpr int BK_THREADS = 512;
+
+// 8 consecutive fp32 values (16-byte aligned) as bf16 hi and lo parts
+__device__ __forceinline__ void ld_split8(const float *p, bf16x8 &hi, bf16x8 &lo) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    bf16 h[8], l[8];
+    split_bf16<8>(x, h, l);
+    hi = pack8(h);
+    lo = pack8(l);
+}
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+    bf16 h[8], l[8];
+    split_bf16<8>(x, h, l);
+    hi = pack8(h);
+    lo = pack8(l);
+}
+// c += a.b with both sides as hi/lo parts (3 passes), or a exact (2 passes)
+__device__ __forceinline__ f32x4 mm3(const bf16x8 &ah, const bf16x8 &al, const bf16x8 &bh, const bf16x8 &bl,
+                                     f32x4 c) {
+    c = mfma16x16x32(ah, bh, c);
+    c = mfma16x16x32(ah, bl, c);
+    return mfma16x16x32(al, bh, c);
+}
+__device__ __forceinline__ f32x4 mm2(const bf16x8 &a, const bf16x8 &bh, const bf16x8 &bl, f32x4 c) {
+    c = mfma16x16x32(a, bh, c);
+    return mfma16x16x32(a, bl, c);
+}
+// ... or with b exact
+__device__ __forceinline__ f32x4 mm2b(const bf16x8 &ah, const bf16x8 &al, const bf16x8 &b, f32x4 c) {
+    c = mfma16x16x32(ah, b, c);
+    return mfma16x16x32(al, b, c);
+}
+// A fragment of an input row (K, Q): exact bf16, or fp32 split
+template <typename TIn>
+__device__ __forceinline__ void in_frag(const TIn *p, bf16x8 &hi, bf16x8 &lo) {
+    if constexpr (sizeof(TIn) == 2) {
+        hi = *reinterpret_cast<const bf16x8 *>(p);
+    } else {
+        ld_split8(reinterpret_cast<const float *>(p), hi, lo);
+    }
+}
 
 template <int D, typename TIn>
 __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
@@ -453,40 +511,44 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     const float *__restrict__ beta, const float *__restrict__ d_o, const float *__restrict__ dvin,
     const float *__restrict__ s_chunks, const float *__restrict__ ds_end, BwdMats bm, int L, int H, int Nc,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dalpha, float *__restrict__ dbeta) {
-    __shared__ TIn Ks[C][D], Qs[C][D];
-    __shared__ float As[C][C + 1], Ps[C][C + 1], Ts[C][C + 1], Gs[C][C + 1];   // Gs: Gam (lower incl)
-    // the column-block buffers (S and dS' blocks, then E, U, dO, dE, dU, K dS' of the block) while the
-    // columns are walked; afterwards the same memory holds dP and the dT / dA matrix
-    constexpr int BLK = 2 * D * 17 + 6 * C * 17, MAT = 2 * C * (C + 1);
-    __shared__ float scratch[BLK > MAT ? BLK : MAT];
-    float (*Sb)[17] = reinterpret_cast<float (*)[17]>(scratch);
-    float (*dSb)[17] = reinterpret_cast<float (*)[17]>(scratch + D * 17);
-    float (*Eb)[17] = reinterpret_cast<float (*)[17]>(scratch + 2 * D * 17);
-    float (*Ub)[17] = Eb + C, (*dOb)[17] = Eb + 2 * C, (*dEb)[17] = Eb + 3 * C, (*dUb)[17] = Eb + 4 * C,
-          (*KdSb)[17] = Eb + 5 * C;
-    float (*dPs)[C + 1] = reinterpret_cast<float (*)[C + 1]>(scratch);
-    float (*dXs)[C + 1] = reinterpret_cast<float (*)[C + 1]>(scratch + C * (C + 1));
+    constexpr bool F32 = sizeof(TIn) == 4;
+    constexpr int JB = 32, NB = D / JB, KSD = D / 32;
+    constexpr int SL = D + 8, ML = C + 8, JL = JB + 8;   // LDS row strides (bf16)
+    constexpr int QT = D / 32;                           // 16-column i tiles per wave in dQ, dK
+    // block phase: bf16 planes
+    constexpr int O_PT = 0, O_ST = O_PT + 2 * C * ML, O_DST = O_ST + 2 * JB * SL, O_DOT = O_DST + 2 * JB * SL,
+                  O_ET = O_DOT + 2 * JB * ML, O_EN = O_ET + 2 * JB * ML, O_UN = O_EN + 2 * C * JL,
+                  O_CU = O_UN + 2 * C * JL, O_DU = O_CU + 2 * C * JL, O_SN = O_DU + 2 * C * JL,
+                  O_DSN = O_SN + 2 * D * JL, BLK_ELEMS = O_DSN + 2 * D * JL;
+    // final phase: fp32 [64][65] matrices over the same memory
+    constexpr int FL = C + 1, MAT = C * FL, FIN_FLOATS = 6 * MAT;
+    constexpr int LDS_BYTES = (BLK_ELEMS * 2 > FIN_FLOATS * 4) ? BLK_ELEMS * 2 : FIN_FLOATS * 4;
+    __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+    bf16 *pl = reinterpret_cast<bf16 *>(smem);
+    float *fm = reinterpret_cast<float *>(smem);
+    float *Ts = fm, *As = fm + MAT, *Ps = fm + 2 * MAT, *Gs = fm + 3 * MAT, *dPs = fm + 4 * MAT, *dXs = fm + 5 * MAT;
     __shared__ double lgs[C];
-    __shared__ float gam[C], cr[C], bes[C], als[C], dgam[C], dcr[C], dbn[C], dlg[C], red[BK_THREADS / 64];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    __shared__ float gam[C], cr[C], bes[C], als[C], dgam2[2][C], dcr2[2][C], dbn[C], dlg[C], dbp[C], sdd[8];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 15, lg = lane >> 4;
+    const int rg = wave & 3, hc = wave >> 2;
     const int h = blockIdx.x % H, chunk = blockIdx.x / H, b = blockIdx.y;
     const int c0 = chunk * C, nvalid = min(C, L - c0);
     const int64_t tok0 = (int64_t)b * L + c0;
     const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
+    const int64_t rs = (int64_t)H * D;   // elements between consecutive tokens of q, k, v, dO, dE
+    const TIn *kb = k + (tok0 * H + h) * D, *qb = q + (tok0 * H + h) * D, *vb = v + (tok0 * H + h) * D;
+    const float *dob = d_o + (tok0 * H + h) * D, *deb = dvin + (tok0 * H + h) * D;
+    const float *Sg = s_chunks + cid * D * D, *dSg = ds_end + cid * D * D;
 
-    // K, Q tiles (rows past the end are zero), gates, and the chunk matrices of the backward prep
-    for (int n = t; n < C * D; n += BK_THREADS) {
-        const int r = n / D, i = n % D;
-        const bool ok = r < nvalid;
-        const int64_t off = ((tok0 + (ok ? r : 0)) * H + h) * D + i;
-        Ks[r][i] = ok ? k[off] : from_f32<TIn>(0.f);
-        Qs[r][i] = ok ? q[off] : from_f32<TIn>(0.f);
-    }
+    // P^T into LDS (split) and the chunk's scalars
     for (int n = t; n < C * C; n += BK_THREADS) {
-        const int r = n / C, i = n % C;
-        As[r][i] = bm.A[cid * C * C + n];
-        Ps[r][i] = bm.P[cid * C * C + n];
-        Ts[r][i] = bm.T[cid * C * C + n];
+        const int r = n / C, m = n % C;
+        const float x[2] = {bm.P[cid * C * C + n], 0.f};
+        bf16 hh[2], ll[2];
+        split_bf16<2>(x, hh, ll);
+        pl[O_PT + m * ML + r] = hh[0];
+        pl[O_PT + C * ML + m * ML + r] = ll[0];
     }
     if (t < C) {
         const bool ok = t < nvalid;
@@ -496,164 +558,276 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
         lgs[t] = bm.lg[cid * C + t];
         gam[t] = bm.gam[cid * C + t];
         cr[t] = bm.c[cid * C + t];
-        dgam[t] = 0.f;
-        dcr[t] = 0.f;
-    }
-    __syncthreads();
-    for (int n = t; n < C * C; n += BK_THREADS) {
-        const int r = n / C, i = n % C;
-        Gs[r][i] = i <= r ? (float)exp(lgs[r] - lgs[i]) : 0.f;
     }
     __syncthreads();
 
-    // accumulators in registers: dQ, dK rows r = t / 8, columns i = t % 8 + 8 a;
-    // dP, dTb rows r, columns m = t % 8 + 8 a
-    constexpr int QA = D / 8;
-    const int rr = t >> 3, cq = t & 7;
-    float dQa[QA], dKa[QA], dPa[8], dTa[8];
+    const int ra = 16 * rg + lr;                 // this lane's A row in the row-group products
+    const bool ra_ok = ra < nvalid;
+    f32x4 dPa[2], dTa[2], dQa[QT], dKa[QT];
 #pragma unroll
-    for (int a = 0; a < QA; ++a) dQa[a] = dKa[a] = 0.f;
+    for (int x = 0; x < 2; ++x) dPa[x] = dTa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int a = 0; a < 8; ++a) dPa[a] = dTa[a] = 0.f;
-    float dgC = 0.f;   // this thread's share of sum S (.) dS'
+    for (int x = 0; x < QT; ++x) dQa[x] = dKa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgacc[4] = {0.f, 0.f, 0.f, 0.f}, dcacc[4] = {0.f, 0.f, 0.f, 0.f}, sdacc = 0.f;
+    const bf16x8 z8 = {};
 
-    for (int jb = 0; jb < D / 16; ++jb) {
-        const int j0 = jb * 16;
-        for (int n = t; n < D * 16; n += BK_THREADS) {
-            const int i = n / 16, j = n % 16;
-            const int64_t off = (cid * D + i) * D + j0 + j;
-            Sb[i][j] = s_chunks[off];
-            dSb[i][j] = ds_end[off];
+    for (int jb = 0; jb < NB; ++jb) {
+        const int j0 = jb * JB;
+        // A. S, dS' transposed ([j][i]) and dO transposed ([j][r]), split
+        for (int n = t; n < D * (JB / 4); n += BK_THREADS) {
+            const int i = n / (JB / 4), qd = n % (JB / 4);
+            const float4 sv = *reinterpret_cast<const float4 *>(Sg + (int64_t)i * D + j0 + 4 * qd);
+            const float4 dv = *reinterpret_cast<const float4 *>(dSg + (int64_t)i * D + j0 + 4 * qd);
+            const float xs[4] = {sv.x, sv.y, sv.z, sv.w}, xd[4] = {dv.x, dv.y, dv.z, dv.w};
+            sdacc = fmaf(xs[0], xd[0], fmaf(xs[1], xd[1], fmaf(xs[2], xd[2], fmaf(xs[3], xd[3], sdacc))));
+            bf16 sh[4], sl[4], dh[4], dl[4];
+            split_bf16<4>(xs, sh, sl);
+            split_bf16<4>(xd, dh, dl);
+            *reinterpret_cast<bf16x4 *>(pl + O_SN + i * JL + 4 * qd) = pack4(sh);
+            *reinterpret_cast<bf16x4 *>(pl + O_SN + D * JL + i * JL + 4 * qd) = pack4(sl);
+            *reinterpret_cast<bf16x4 *>(pl + O_DSN + i * JL + 4 * qd) = pack4(dh);
+            *reinterpret_cast<bf16x4 *>(pl + O_DSN + D * JL + i * JL + 4 * qd) = pack4(dl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * qd + e;
+                pl[O_ST + j * SL + i] = sh[e];
+                pl[O_ST + JB * SL + j * SL + i] = sl[e];
+                pl[O_DST + j * SL + i] = dh[e];
+                pl[O_DST + JB * SL + j * SL + i] = dl[e];
+            }
         }
-        for (int n = t; n < C * 16; n += BK_THREADS) {
-            const int r = n / 16, j = n % 16;
-            const bool ok = r < nvalid;
-            const int64_t off = ((tok0 + (ok ? r : 0)) * H + h) * D + j0 + j;
-            dOb[r][j] = ok ? d_o[off] : 0.f;
-            dEb[r][j] = ok ? dvin[off] : 0.f;
-            Eb[r][j] = ok ? to_f32(v[off]) : 0.f;   // V for now; E below
+        for (int n = t; n < C * (JB / 4); n += BK_THREADS) {
+            const int r = n / (JB / 4), qd = n % (JB / 4);
+            float4 ov = {0.f, 0.f, 0.f, 0.f};
+            if (r < nvalid) ov = *reinterpret_cast<const float4 *>(dob + r * rs + j0 + 4 * qd);
+            const float xo[4] = {ov.x, ov.y, ov.z, ov.w};
+            bf16 oh[4], ol[4];
+            split_bf16<4>(xo, oh, ol);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pl[O_DOT + (4 * qd + e) * ML + r] = oh[e];
+                pl[O_DOT + JB * ML + (4 * qd + e) * ML + r] = ol[e];
+            }
         }
         __syncthreads();
-        // K S, Q S, K dS' (64 x 16): thread (r = t / 8, j = 2 (t % 8) + {0, 1})
-        {
-            const int r = rr;
-            float dg = 0.f;
+        // B. tile (rows 16 rg .., columns j0 + 16 hc ..): K S, Q S, K dS', P^T dO
+        const int jl = 16 * hc + lr;   // this lane's B column within the block
+        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = ks, kd = ks, pd = ks;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * cq + jj;
-                float ks = 0.f, qs = 0.f, kd = 0.f;
-                for (int i = 0; i < D; ++i) {
-                    const float kv = to_f32(Ks[r][i]), s = Sb[i][j];
-                    ks = fmaf(kv, s, ks);
-                    qs = fmaf(to_f32(Qs[r][i]), s, qs);
-                    kd = fmaf(kv, dSb[i][j], kd);
-                }
-                const float e = Eb[r][j] - gam[r] * ks;
-                dg += dOb[r][j] * qs - dEb[r][j] * ks;
-                Eb[r][j] = e;
-                KdSb[r][j] = kd;
+        for (int s = 0; s < KSD; ++s) {
+            const int kk = 32 * s + 8 * lg;
+            bf16x8 kh = z8, kl = z8, qh = z8, ql = z8;
+            if (ra_ok) {
+                in_frag<TIn>(kb + ra * rs + kk, kh, kl);
+                in_frag<TIn>(qb + ra * rs + kk, qh, ql);
             }
-            // row sums over the 8 threads of row r (consecutive lanes)
-#pragma unroll
-            for (int off = 1; off < 8; off <<= 1) dg += __shfl_xor(dg, off, 64);
-            if (cq == 0) dgam[r] += dg;
+            const bf16x8 sh = *reinterpret_cast<const bf16x8 *>(pl + O_ST + jl * SL + kk);
+            const bf16x8 sl = *reinterpret_cast<const bf16x8 *>(pl + O_ST + JB * SL + jl * SL + kk);
+            const bf16x8 dh = *reinterpret_cast<const bf16x8 *>(pl + O_DST + jl * SL + kk);
+            const bf16x8 dl = *reinterpret_cast<const bf16x8 *>(pl + O_DST + JB * SL + jl * SL + kk);
+            ks = mm2(kh, sh, sl, ks);
+            qs = mm2(qh, sh, sl, qs);
+            kd = mm2(kh, dh, dl, kd);
+            if constexpr (F32) {
+                ks = mfma16x16x32(kl, sh, ks);
+                qs = mfma16x16x32(ql, sh, qs);
+                kd = mfma16x16x32(kl, dh, kd);
+            }
         }
-        for (int n = t; n < D * 16; n += BK_THREADS) {
-            const int i = n / 16, j = n % 16;
-            dgC = fmaf(Sb[i][j], dSb[i][j], dgC);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int kk = 32 * s + 8 * lg;
+            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(pl + O_PT + ra * ML + kk);
+            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(pl + O_PT + C * ML + ra * ML + kk);
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(pl + O_DOT + jl * ML + kk);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(pl + O_DOT + JB * ML + jl * ML + kk);
+            pd = mm3(ah, al, bh, bl, pd);
+        }
+        // output element jj: row r = 16 rg + 4 lg + jj, column j = j0 + 16 hc + lr
+        {
+            const int jg = j0 + 16 * hc + lr;
+            float ev[4], bev[4], du[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * rg + 4 * lg + jj;
+                const bool ok = r < nvalid;
+                const float vv = ok ? to_f32(vb[r * rs + jg]) : 0.f;
+                const float od = ok ? dob[r * rs + jg] : 0.f, de = ok ? deb[r * rs + jg] : 0.f;
+                ev[jj] = vv - gam[r] * ks[jj];
+                bev[jj] = bes[r] * ev[jj];
+                du[jj] = pd[jj] + cr[r] * kd[jj];
+                dgacc[jj] = fmaf(od, qs[jj], fmaf(-de, ks[jj], dgacc[jj]));
+            }
+            bf16 eh[4], el[4];
+            split_bf16<4>(bev, eh, el);
+            const int m0 = 16 * rg + 4 * lg;
+            *reinterpret_cast<bf16x4 *>(pl + O_ET + jl * ML + m0) = pack4(eh);
+            *reinterpret_cast<bf16x4 *>(pl + O_ET + JB * ML + jl * ML + m0) = pack4(el);
+            bf16 nh[4], nl[4], uh[4], ul[4];
+            split_bf16<4>(ev, nh, nl);
+            split_bf16<4>(du, uh, ul);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                pl[O_EN + (m0 + jj) * JL + jl] = nh[jj];
+                pl[O_EN + C * JL + (m0 + jj) * JL + jl] = nl[jj];
+                pl[O_DU + (m0 + jj) * JL + jl] = uh[jj];
+                pl[O_DU + C * JL + (m0 + jj) * JL + jl] = ul[jj];
+            }
         }
         __syncthreads();
-        // U = T diag(beta) E; dU = P^T dO + diag(c) K dS'
+        // C. U = T (beta E) for the tile; dc; U and diag(c) U into LDS
         {
-            const int r = rr;
-            float dc = 0.f;
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * cq + jj;
-                float u = 0.f, du = 0.f;
-                for (int m = 0; m <= r; ++m) u = fmaf(Ts[r][m] * bes[m], Eb[m][j], u);
-                for (int m = r; m < C; ++m) du = fmaf(Ps[m][r], dOb[m][j], du);
-                du = fmaf(cr[r], KdSb[r][j], du);
-                Ub[r][j] = u;
-                dUb[r][j] = du;
-                dc = fmaf(u, KdSb[r][j], dc);
+            for (int s = 0; s < 2; ++s) {
+                const int kk = 32 * s + 8 * lg;
+                bf16x8 ah, al;
+                ld_split8(bm.T + cid * C * C + ra * C + kk, ah, al);
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(pl + O_ET + jl * ML + kk);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(pl + O_ET + JB * ML + jl * ML + kk);
+                u = mm3(ah, al, bh, bl, u);
             }
+            float uv[4], cu[4];
+            const int m0 = 16 * rg + 4 * lg;
 #pragma unroll
-            for (int off = 1; off < 8; off <<= 1) dc += __shfl_xor(dc, off, 64);
-            if (cq == 0) dcr[r] += dc;
+            for (int jj = 0; jj < 4; ++jj) {
+                uv[jj] = u[jj];
+                cu[jj] = cr[m0 + jj] * u[jj];
+                dcacc[jj] = fmaf(u[jj], kd[jj], dcacc[jj]);
+            }
+            bf16 uh[4], ul[4], ch[4], cl[4];
+            split_bf16<4>(uv, uh, ul);
+            split_bf16<4>(cu, ch, cl);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                pl[O_UN + (m0 + jj) * JL + jl] = uh[jj];
+                pl[O_UN + C * JL + (m0 + jj) * JL + jl] = ul[jj];
+                pl[O_CU + (m0 + jj) * JL + jl] = ch[jj];
+                pl[O_CU + C * JL + (m0 + jj) * JL + jl] = cl[jj];
+            }
         }
         __syncthreads();
-        // accumulate dP = dO U^T (lower incl), dTb = dU E^T, dQ, dK
+        // D. accumulate (k = the block's 32 columns j: one MFMA k-step)
         {
-            const int r = rr;
+            const int kk = 8 * lg;
+            // A rows ra: gamma dO, -gamma dE (fp32, split), dU, diag(c) U (LDS)
+            float od8[8] = {}, de8[8] = {};
+            if (ra_ok) {
+                const float4 o0 = *reinterpret_cast<const float4 *>(dob + ra * rs + j0 + kk);
+                const float4 o1 = *reinterpret_cast<const float4 *>(dob + ra * rs + j0 + kk + 4);
+                const float4 e0 = *reinterpret_cast<const float4 *>(deb + ra * rs + j0 + kk);
+                const float4 e1 = *reinterpret_cast<const float4 *>(deb + ra * rs + j0 + kk + 4);
+                const float og[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                const float eg[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                const int m = cq + 8 * a;
-                float p = 0.f, tb = 0.f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    p = fmaf(dOb[r][j], Ub[m][j], p);
-                    tb = fmaf(dUb[r][j], Eb[m][j], tb);
+                for (int e = 0; e < 8; ++e) {
+                    od8[e] = og[e];
+                    de8[e] = eg[e];
                 }
-                dPa[a] += p;
-                dTa[a] += tb;
             }
-            const float gr = gam[r], crr = cr[r];
+            bf16x8 oh, ol, goh, gol, geh, gel;
+            split8(od8, oh, ol);
+            {
+                float go[8], ge[8];
+                const float gr = gam[ra];
 #pragma unroll
-            for (int a = 0; a < QA; ++a) {
-                const int i = cq + 8 * a;
-                float aq = 0.f, ak = 0.f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    aq = fmaf(dOb[r][j], Sb[i][j], aq);
-                    ak = fmaf(crr * Ub[r][j], dSb[i][j], fmaf(-gr * dEb[r][j], Sb[i][j], ak));
+                for (int e = 0; e < 8; ++e) {
+                    go[e] = gr * od8[e];
+                    ge[e] = -gr * de8[e];
                 }
-                dQa[a] = fmaf(gr, aq, dQa[a]);
-                dKa[a] += ak;
+                split8(go, goh, gol);
+                split8(ge, geh, gel);
+            }
+            const bf16x8 duh = *reinterpret_cast<const bf16x8 *>(pl + O_DU + ra * JL + kk);
+            const bf16x8 dul = *reinterpret_cast<const bf16x8 *>(pl + O_DU + C * JL + ra * JL + kk);
+            const bf16x8 cuh = *reinterpret_cast<const bf16x8 *>(pl + O_CU + ra * JL + kk);
+            const bf16x8 cul = *reinterpret_cast<const bf16x8 *>(pl + O_CU + C * JL + ra * JL + kk);
+            // dP += dO U^T, dTb += dU E^T: m tiles 2 hc, 2 hc + 1
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int mrow = 16 * (2 * hc + x) + lr;
+                const bf16x8 ubh = *reinterpret_cast<const bf16x8 *>(pl + O_UN + mrow * JL + kk);
+                const bf16x8 ubl = *reinterpret_cast<const bf16x8 *>(pl + O_UN + C * JL + mrow * JL + kk);
+                const bf16x8 ebh = *reinterpret_cast<const bf16x8 *>(pl + O_EN + mrow * JL + kk);
+                const bf16x8 ebl = *reinterpret_cast<const bf16x8 *>(pl + O_EN + C * JL + mrow * JL + kk);
+                dPa[x] = mm3(oh, ol, ubh, ubl, dPa[x]);
+                dTa[x] = mm3(duh, dul, ebh, ebl, dTa[x]);
+            }
+            // dQ += (gamma dO) S^T, dK += (-gamma dE) S^T + (c U) dS'^T: i tiles QT hc ..
+#pragma unroll
+            for (int x = 0; x < QT; ++x) {
+                const int irow = 16 * (QT * hc + x) + lr;
+                const bf16x8 sh = *reinterpret_cast<const bf16x8 *>(pl + O_SN + irow * JL + kk);
+                const bf16x8 sl = *reinterpret_cast<const bf16x8 *>(pl + O_SN + D * JL + irow * JL + kk);
+                const bf16x8 dh = *reinterpret_cast<const bf16x8 *>(pl + O_DSN + irow * JL + kk);
+                const bf16x8 dl = *reinterpret_cast<const bf16x8 *>(pl + O_DSN + D * JL + irow * JL + kk);
+                dQa[x] = mm3(goh, gol, sh, sl, dQa[x]);
+                dKa[x] = mm3(geh, gel, sh, sl, dKa[x]);
+                dKa[x] = mm3(cuh, cul, dh, dl, dKa[x]);
             }
         }
-        __syncthreads();   // the next block restages the block buffers
+        __syncthreads();   // the next block restages every plane
     }
 
-    // ---- the chunk-matrix gradients (dP, then dTb -> dT -> Y = T^T dT -> dA, in the freed block memory) ----
+    // per-row sums of this wave's dgamma and dc shares (16 lanes of a row group hold one row each)
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        const int m = cq + 8 * a;
-        dPs[rr][m] = m <= rr ? dPa[a] : 0.f;
-        dXs[rr][m] = dTa[a];   // dTb for now
+    for (int jj = 0; jj < 4; ++jj) {
+        float g = dgacc[jj], cc = dcacc[jj];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            g += __shfl_xor(g, off, 64);
+            cc += __shfl_xor(cc, off, 64);
+        }
+        if (lr == 0) {
+            dgam2[hc][16 * rg + 4 * lg + jj] = g;
+            dcr2[hc][16 * rg + 4 * lg + jj] = cc;
+        }
     }
-    // the thread-local share of sum S (.) dS' to one value
     {
-        float v2 = dgC;
+        float v2 = sdacc;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) v2 += __shfl_xor(v2, off, 64);
-        if (lane == 0) red[wave] = v2;
+        if (lane == 0) sdd[wave] = v2;
     }
-    __syncthreads();
-    // dbeta part 1 (from Tb = T diag(beta)): sum_r dTb_rm T_rm; dT = dTb diag(beta) in place
-    float dbm = 0.f;
-    if (t < C) {
-        const int m = t;
-        for (int r = 0; r < C; ++r) dbm = fmaf(dXs[r][m], Ts[r][m], dbm);
-    }
-    __syncthreads();
+    // dP (lower incl) and dTb into LDS fp32; T, A, P, Gam for the 64 x 64 steps
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * rg + 4 * lg + jj, m = 16 * (2 * hc + x) + lr;
+            dPs[r * FL + m] = m <= r ? dPa[x][jj] : 0.f;
+            dXs[r * FL + m] = dTa[x][jj];
+        }
     for (int n = t; n < C * C; n += BK_THREADS) {
         const int r = n / C, m = n % C;
-        dXs[r][m] *= bes[m];
+        Ts[r * FL + m] = bm.T[cid * C * C + n];
+        As[r * FL + m] = bm.A[cid * C * C + n];
+        Ps[r * FL + m] = bm.P[cid * C * C + n];
+        Gs[r * FL + m] = m <= r ? (float)exp(lgs[r] - lgs[m]) : 0.f;
     }
     __syncthreads();
-    // Y = T^T dT (row rr, columns m = t % 8 + 8 a, in registers), then dN = -Y T^T (strict lower)
+    // dbeta part 1 (from Tb = T diag(beta)): sum_r dTb_rm T_rm
+    if (t < C) {
+        float s = 0.f;
+        for (int r = 0; r < C; ++r) s = fmaf(dXs[r * FL + t], Ts[r * FL + t], s);
+        dbp[t] = s;
+    }
+    __syncthreads();
+    for (int n = t; n < C * C; n += BK_THREADS) dXs[(n / C) * FL + n % C] *= bes[n % C];   // dT = dTb diag(beta)
+    __syncthreads();
+    // Y = T^T dT (8 elements per thread: row r = t / 8, columns m = t % 8 + 8 a)
+    const int rr = t >> 3, cq = t & 7;
     float Y[8];
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
         const int m = cq + 8 * a;
         float acc = 0.f;
-        for (int r = rr; r < C; ++r) acc = fmaf(Ts[r][rr], dXs[r][m], acc);   // T_r,rr nonzero for r >= rr
+        for (int r = rr; r < C; ++r) acc = fmaf(Ts[r * FL + rr], dXs[r * FL + m], acc);
         Y[a] = acc;
     }
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 8; ++a) dXs[rr][cq + 8 * a] = Y[a];
+    for (int a = 0; a < 8; ++a) dXs[rr * FL + cq + 8 * a] = Y[a];
     __syncthreads();
     // dN_ri = -sum_m Y_rm T_im (strict lower); dA = diag(beta) dN; dbeta part 2: sum_i dN_ri A_ri
     float dNr[8];
@@ -661,41 +835,55 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     for (int a = 0; a < 8; ++a) {
         const int i = cq + 8 * a;
         float acc = 0.f;
-        if (i < rr) {
-            for (int m = 0; m <= i; ++m) acc = fmaf(dXs[rr][m], Ts[i][m], acc);   // T_im is zero for m > i
-        }
+        if (i < rr)
+            for (int m = 0; m <= i; ++m) acc = fmaf(dXs[rr * FL + m], Ts[i * FL + m], acc);
         dNr[a] = -acc;
     }
     __syncthreads();
-    // dXs <- dA = diag(beta) dN (strict lower)
-#pragma unroll
-    for (int a = 0; a < 8; ++a) dXs[rr][cq + 8 * a] = bes[rr] * dNr[a];
     {
         float p2 = 0.f;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) p2 = fmaf(dNr[a], As[rr][cq + 8 * a], p2);
+        for (int a = 0; a < 8; ++a) {
+            dXs[rr * FL + cq + 8 * a] = bes[rr] * dNr[a];
+            p2 = fmaf(dNr[a], As[rr * FL + cq + 8 * a], p2);
+        }
 #pragma unroll
         for (int off = 1; off < 8; off <<= 1) p2 += __shfl_xor(p2, off, 64);
-        if (cq == 0) dbn[rr] = p2;   // dbeta of row rr through N = diag(beta) A
+        if (cq == 0) dbn[rr] = p2;
     }
     __syncthreads();
-    // dQ += (Gam (.) dP) K;  dK += (Gam (.) dP)^T Q + (Gam (.) dA) K + (Gam (.) dA)^T K
-    {
-        const int r = rr;
+    // dQ += (Gam (.) dP) K;  dK += (Gam (.) dP)^T Q + (Gam (.) dA + (Gam (.) dA)^T) K   (k = m, 64)
 #pragma unroll
-        for (int a = 0; a < QA; ++a) {
-            const int i = cq + 8 * a;
-            float aq = 0.f, ak = 0.f;
-            for (int m = 0; m < C; ++m) {
-                const float gpr = Gs[r][m];   // Gam_rm (zero for m > r)
-                const float gmr = Gs[m][r];   // Gam_mr (zero for r > m)
-                const float km = to_f32(Ks[m][i]);
-                aq = fmaf(gpr * dPs[r][m], km, aq);
-                ak = fmaf(gmr * dPs[m][r], to_f32(Qs[m][i]), ak);
-                ak = fmaf(gpr * dXs[r][m] + gmr * dXs[m][r], km, ak);
+    for (int s = 0; s < 2; ++s) {
+        const int kk = 32 * s + 8 * lg;
+        float xp[8], xpt[8], xa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int m = kk + e;
+            xp[e] = Gs[ra * FL + m] * dPs[ra * FL + m];
+            xpt[e] = Gs[m * FL + ra] * dPs[m * FL + ra];
+            xa[e] = Gs[ra * FL + m] * dXs[ra * FL + m] + Gs[m * FL + ra] * dXs[m * FL + ra];
+        }
+        bf16x8 ph, pl8, pth, ptl, ah, al;
+        split8(xp, ph, pl8);
+        split8(xpt, pth, ptl);
+        split8(xa, ah, al);
+#pragma unroll
+        for (int x = 0; x < QT; ++x) {
+            const int irow = 16 * (QT * hc + x) + lr;
+            const int64_t off = (cid * D + irow) * C + kk;
+            const bf16x8 kth = *reinterpret_cast<const bf16x8 *>(bm.Kth + off);
+            const bf16x8 qth = *reinterpret_cast<const bf16x8 *>(bm.Qth + off);
+            dQa[x] = mm2b(ph, pl8, kth, dQa[x]);
+            dKa[x] = mm2b(pth, ptl, qth, dKa[x]);
+            dKa[x] = mm2b(ah, al, kth, dKa[x]);
+            if constexpr (F32) {
+                const bf16x8 ktl = *reinterpret_cast<const bf16x8 *>(bm.Ktl + off);
+                const bf16x8 qtl = *reinterpret_cast<const bf16x8 *>(bm.Qtl + off);
+                dQa[x] = mfma16x16x32(ph, ktl, dQa[x]);
+                dKa[x] = mfma16x16x32(pth, qtl, dKa[x]);
+                dKa[x] = mfma16x16x32(ah, ktl, dKa[x]);
             }
-            dQa[a] += aq;
-            dKa[a] += ak;
         }
     }
     // The decay gradient.  gamma_r depends on log alpha_m for m <= r, Gam_ab for b < m <= a, c_r for
@@ -703,35 +891,47 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     //     dlog alpha_m = sum_{r >= m} gamma_r dgamma_r + sum_{a >= m > b} (A (.) dA + P (.) dP)_ab
     //                    + sum_{r < m} c_r dc_r + gamma_C dgamma_C,
     // each term a sum of the contributions that actually depend on alpha_m (no cancelling pairs).
+    // The middle sum as prefix sums: R[a][m] = sum_{b < m} (A (.) dA + P (.) dP)_ab row by row (one thread a
+    // per row, into the Gam matrix's memory, read for the last time above), then sum_{a >= m} R[a][m] per m.
+    __syncthreads();
+    float *Rs = Gs;
+    if (t < C) {
+        const int a = t;
+        float run = 0.f;
+        for (int m = 0; m < C; ++m) {
+            Rs[a * FL + m] = run;
+            run += As[a * FL + m] * dXs[a * FL + m] + Ps[a * FL + m] * dPs[a * FL + m];
+        }
+    }
+    __syncthreads();
     if (t < C) {
         const int m = t;
         float dgCt = 0.f;
-        for (int w = 0; w < BK_THREADS / 64; ++w) dgCt += red[w];
+        for (int w = 0; w < BK_THREADS / 64; ++w) dgCt += sdd[w];
         float s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        for (int r = m; r < C; ++r) s1 = fmaf(gam[r], dgam[r], s1);
-        for (int a = m; a < C; ++a)
-            for (int b2 = 0; b2 < m; ++b2) s2 += As[a][b2] * dXs[a][b2] + Ps[a][b2] * dPs[a][b2];
-        for (int r = 0; r < m; ++r) s3 = fmaf(cr[r], dcr[r], s3);
+        for (int r = m; r < C; ++r) s1 = fmaf(gam[r], dgam2[0][r] + dgam2[1][r], s1);
+        for (int a = m; a < C; ++a) s2 += Rs[a * FL + m];
+        for (int r = 0; r < m; ++r) s3 = fmaf(cr[r], dcr2[0][r] + dcr2[1][r], s3);
         dlg[m] = s1 + s2 + s3 + gam[C - 1] * dgCt;
     }
     __syncthreads();
-    // outputs
-    if (t < C) {
-        const int m = t;
-        if (m < nvalid) {
-            const int64_t gi = (tok0 + m) * H + h;
-            dalpha[gi] = dlg[m] / als[m];
-            dbeta[gi] = dbm + dbn[m];
-        }
+    if (t < C && t < nvalid) {
+        const int64_t gi = (tok0 + t) * H + h;
+        dalpha[gi] = dlg[t] / als[t];
+        dbeta[gi] = dbp[t] + dbn[t];
     }
-    if (rr < nvalid) {
-        const int64_t base = ((tok0 + rr) * H + h) * D;
+    // dQ, dK: element jj of lane (lr, lg) in tile x is row r = 16 rg + 4 lg + jj, column i = 16 (QT hc + x) + lr
 #pragma unroll
-        for (int a = 0; a < QA; ++a) {
-            dq[base + cq + 8 * a] = dQa[a];
-            dk[base + cq + 8 * a] = dKa[a];
+    for (int x = 0; x < QT; ++x)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * rg + 4 * lg + jj, i = 16 * (QT * hc + x) + lr;
+            if (r < nvalid) {
+                const int64_t o = ((tok0 + r) * H + h) * D + i;
+                dq[o] = dQa[x][jj];
+                dk[o] = dKa[x][jj];
+            }
         }
-    }
 }
 
 }  // namespace
