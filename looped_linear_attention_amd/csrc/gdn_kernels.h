@@ -125,9 +125,9 @@ hipError_t launch_lb_epilogue_grad(int M, int H, int D, float *Y, int64_t P, int
 int lb_drho_blocks(int M);
 hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp_f32, float *part, float *drho,
                           hipStream_t s);
-// dWT [d][P] to dWq, dWk [d][H D], dWv [d][H D], dwa, dwb [d][H].
-hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, int64_t P, int64_t qkvp, float *dWq, float *dWk,
-                            float *dWv, float *dwa, float *dwb, hipStream_t s);
+// dWT [d][P] (plus dWT2 when given) to dWq, dWk [d][H D], dWv [d][H D], dwa, dwb [d][H].
+hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, const float *dWT2, int64_t P, int64_t qkvp,
+                            float *dWq, float *dWk, float *dWv, float *dwa, float *dwb, hipStream_t s);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 
 // ---- products and transposes of the loop backward (gemm_nt.hip) ----
@@ -152,10 +152,16 @@ hipError_t launch_gemm_nt(int mode_a, int mode_b, int epi, const void *A, int64_
 // The tiled bf16 product (gemm_tile.hip): C[m][n] = epi(sum_k A[m][k] B[n][k])
 // with A2 / B2 the optional lo planes of an fp32 operand split into bf16 hi +
 // lo (null when the operand is bf16).  K a multiple of 64, lda, ldb multiples
-// of 8 and >= K; C fp32 or bf16 (EPI_ACCUM fp32 only).
+// of 8 and >= K; C fp32 or bf16 (EPI_ACCUM fp32 only).  With ksplit > 1 (store
+// or accumulate only) the k-blocks of all passes are divided into ksplit
+// contiguous ranges, range z's partial products going to C + z cstride.
 hipError_t launch_gemm_tile(int epi, bool out_f32, const bf16 *A, const bf16 *A2, int64_t lda, const bf16 *B,
                             const bf16 *B2, int64_t ldb, int M, int N, int K, void *C, int64_t ldc, const float *rho,
-                            const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s);
+                            const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s,
+                            int ksplit = 1, int64_t cstride = 0);
+// out = sum_z parts[z] (z < nparts, stride pstride) + rho[c] * add[r][c] (rho null: no term), n = rows * d.
+hipError_t launch_sum_parts(int64_t rows, int d, const float *parts, int nparts, int64_t pstride, const float *rho,
+                            const float *add, float *out, hipStream_t s);
 // x ~ hi + lo, both bf16, elementwise over n values (16-byte aligned).
 hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream_t s);
 // hi[c][r] + lo[c][r] ~ in[r][c] (fp32 in [R][ldi]), zero for R <= r < Rp.

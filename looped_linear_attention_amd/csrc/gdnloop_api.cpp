@@ -9,6 +9,7 @@
 //   -> chunk prep -> state carry with the residual fused into its output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -107,6 +108,10 @@ gdn_status check_loop_backward(const gdn_desc *d) {
         if ((p) && !aligned16(p)) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p);     \
     } while (0)
 
+// The loop backward's dY W product splits its k range into up to this many
+// partial sums when its tiles alone would leave CUs idle.
+constexpr int LB_DX_SPLIT = 4;
+
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
     size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, sc = 0, dse = 0, bm = 0;
@@ -116,6 +121,7 @@ struct Layout {
     // gradients, two dh buffers, the weight-gradient accumulator [d][P], rho partials
     size_t Y = 0, YT = 0, XT = 0, WT = 0, gq = 0, gk = 0, gv = 0, gal = 0, gbe = 0, dhA = 0, dhB = 0, dW = 0, part = 0;
     size_t Yhl = 0;   // bf16 workloads: dY as bf16 hi and lo planes (the transpose's planes reuse YT)
+    size_t Gp = 0;    // bf16 workloads: the split-k partial sums of dY W
     size_t total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
@@ -173,7 +179,8 @@ Layout layout(const gdn_desc *d, int op) {
         lo.gbe = take(tokens * d->H * 4);
         lo.dhA = take(tokens * d->d * 4);
         lo.dhB = take(tokens * d->d * 4);
-        lo.dW = take(d->d * P * 4);
+        lo.dW = take(d->d * P * 4 * (d->act == GDN_BF16 ? 2 : 1));   // bf16: two split-k halves
+        if (d->act == GDN_BF16) lo.Gp = take((size_t)LB_DX_SPLIT * tokens * d->d * 4);
         lo.part = take((size_t)lb_drho_blocks((int)tokens) * d->d * 4);
     }
     if (act) {
@@ -447,7 +454,11 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
 
     hipError_t e = launch_transpose(f32, f32, Wpack, d, P, d, WT, P, P, s);   // W^T [d][P]
     if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
-    if ((e = launch_fill_zero(dW, (int64_t)d * P, s)) != hipSuccess) return hip_fail(e, "fill launch");
+    if ((e = launch_fill_zero(dW, (int64_t)d * P * (f32 ? 1 : 2), s)) != hipSuccess) return hip_fail(e, "fill launch");
+    // bf16: dY W splits its k range so that its tiles fill the chip (partials summed with the residual), and
+    // x^T dY accumulates in two k halves (summed when unpacked)
+    const int dx_tiles = ((M + 383) / 384) * ((d + 255) / 256);
+    const int dx_split = std::min(LB_DX_SPLIT, std::max(1, (256 + dx_tiles - 1) / dx_tiles));
     for (int tau = T - 1; tau >= 0; --tau) {
         // loop tau + 1 of the forward: input h^(tau), incoming gradient dL/dh^(tau+1)
         const bool hp_f32 = f32 || tau > 0;
@@ -515,22 +526,32 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
             bf16 *Yh = (bf16 *)at(ws, lo.Yhl), *Yl = Yh + (int64_t)M * P;
             bf16 *YTh = (bf16 *)YT, *YTl = YTh + (int64_t)P * Mp;
             if ((e = launch_split((int64_t)M * P, Y, Yh, Yl, s)) != hipSuccess) return hip_fail(e, "split launch");
-            e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
-                return launch_gemm_tile(EPI_RESID, true, Yh, Yl, P, (const bf16 *)WT, nullptr, P, M, d, P, g_out, d,
-                                        rho + (int64_t)tau * d, g_in, d, nullptr, 0, s);
-            });
+            if (dx_split == 1) {
+                e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                    return launch_gemm_tile(EPI_RESID, true, Yh, Yl, P, (const bf16 *)WT, nullptr, P, M, d, P, g_out,
+                                            d, rho + (int64_t)tau * d, g_in, d, nullptr, 0, s);
+                });
+            } else {
+                float *Gp = (float *)at(ws, lo.Gp);
+                e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                    return launch_gemm_tile(EPI_STORE, true, Yh, Yl, P, (const bf16 *)WT, nullptr, P, M, d, P, Gp, d,
+                                            nullptr, nullptr, 0, nullptr, 0, s, dx_split, (int64_t)M * d);
+                });
+                if (e == hipSuccess)
+                    e = launch_sum_parts(M, d, Gp, dx_split, (int64_t)M * d, rho + (int64_t)tau * d, g_in, g_out, s);
+            }
             if (e != hipSuccess) return hip_fail(e, "input gradient launch");
             if ((e = launch_transpose(false, false, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess ||
                 (e = launch_transpose_split(Y, P, M, P, YTh, YTl, Mp, Mp, s)) != hipSuccess)
                 return hip_fail(e, "transpose launch");
             e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
                 return launch_gemm_tile(EPI_ACCUM, true, (const bf16 *)XT, nullptr, Mp, YTh, YTl, Mp, d, P, Mp, dW,
-                                        P, nullptr, nullptr, 0, nullptr, 0, s);
+                                        P, nullptr, nullptr, 0, nullptr, 0, s, 2, (int64_t)d * P);
             });
         }
         if (e != hipSuccess) return hip_fail(e, "weight gradient launch");
     }
-    e = launch_lb_unpack(d, H, D, dW, P, qkvp, dWq, dWk, dWv, dwa, dwb, s);
+    e = launch_lb_unpack(d, H, D, dW, f32 ? nullptr : dW + (int64_t)d * P, P, qkvp, dWq, dWk, dWv, dwa, dwb, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "weight gradient unpack launch");
 }
 

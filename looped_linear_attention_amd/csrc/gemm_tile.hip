@@ -69,9 +69,9 @@ __device__ __forceinline__ void block_bases(const Planes &P, int pass, int kb, c
 template <int EPI, typename TOut>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_tile(
     const bf16 *__restrict__ A, const bf16 *__restrict__ A2, int64_t lda, const bf16 *__restrict__ B,
-    const bf16 *__restrict__ B2, int64_t ldb, int M, int N, int K, int m_tiles, int n_tiles, TOut *__restrict__ C,
-    int64_t ldc, const float *__restrict__ rho, const float *__restrict__ D1, int64_t ldd1,
-    const float *__restrict__ D2, int64_t ldd2) {
+    const bf16 *__restrict__ B2, int64_t ldb, int M, int N, int K, int m_tiles, int n_tiles, int ksplit,
+    int64_t cstride, TOut *__restrict__ C, int64_t ldc, const float *__restrict__ rho, const float *__restrict__ D1,
+    int64_t ldd1, const float *__restrict__ D2, int64_t ldd2) {
     __shared__ __attribute__((aligned(16))) char smem[G_LDS];
     bf16 *stages = reinterpret_cast<bf16 *>(smem);
     const int t = threadIdx.x, lane = t & 63;
@@ -80,8 +80,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Workgroup ids go to the 8 XCDs round-robin; XCD x takes the tiles
     // x, x + 8, ... of the token-tile-major order, so one XCD's tiles share
     // token tiles (A rows) in its L2 as the features advance.
-    const int id = blockIdx.x;
+    // With ksplit > 1 the k-blocks (over all passes) are divided into ksplit
+    // contiguous ranges; range z's partial sums go to C + z cstride.
     const int ntot = m_tiles * n_tiles;
+    const int split = blockIdx.x / ntot, id = blockIdx.x % ntot;
+    C += (int64_t)split * cstride;
     const int tix = (ntot % 8 == 0) ? (id % 8) * (ntot / 8) + id / 8 : id;
     const int m_tile = tix / n_tiles, n_tile = tix % n_tiles;
     const int m0 = m_tile * GM, n0 = n_tile * GN;
@@ -89,9 +92,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const TileSrc src = tile_src(lane, wave, min(GM, M - m0), min(GN, N - n0), lda, ldb);
     Planes P{A + (int64_t)m0 * lda, A2 ? A2 + (int64_t)m0 * lda : nullptr, B + (int64_t)n0 * ldb,
              B2 ? B2 + (int64_t)n0 * ldb : nullptr};
-    const int nkb = K / GK, npass = 1 + (A2 != nullptr) + (B2 != nullptr), nblk = nkb * npass;
+    const int nkb = K / GK, npass = 1 + (A2 != nullptr) + (B2 != nullptr), nall = nkb * npass;
+    const int blk0 = (int)((int64_t)nall * split / ksplit), nblk = (int)((int64_t)nall * (split + 1) / ksplit) - blk0;
     auto issue = [&](int blk, bf16 *stage) __attribute__((always_inline)) {
-        const int b = min(blk, nblk - 1);
+        const int b = blk0 + min(blk, nblk - 1);
         const bf16 *ab, *bb;
         block_bases(P, b / nkb, b % nkb, ab, bb);
         return [=](int i) __attribute__((always_inline)) {
@@ -219,22 +223,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <int EPI, typename TOut>
 void tile_launch(const bf16 *A, const bf16 *A2, int64_t lda, const bf16 *B, const bf16 *B2, int64_t ldb, int M,
-                 int N, int K, TOut *C, int64_t ldc, const float *rho, const float *D1, int64_t ldd1, const float *D2,
-                 int64_t ldd2, hipStream_t s) {
+                 int N, int K, int ksplit, int64_t cstride, TOut *C, int64_t ldc, const float *rho, const float *D1,
+                 int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s) {
     const int mt = (M + GM - 1) / GM, nt = (N + GN - 1) / GN;
-    launch_kernel(k_gemm_tile<EPI, TOut>, dim3(mt * nt), dim3(512), 0, s, A, A2, lda, B, B2, ldb, M, N, K, mt, nt,
-                  C, ldc, rho, D1, ldd1, D2, ldd2);
+    launch_kernel(k_gemm_tile<EPI, TOut>, dim3(mt * nt * ksplit), dim3(512), 0, s, A, A2, lda, B, B2, ldb, M, N, K,
+                  mt, nt, ksplit, cstride, C, ldc, rho, D1, ldd1, D2, ldd2);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_tile(int epi, bool out_f32, const bf16 *A, const bf16 *A2, int64_t lda, const bf16 *B,
                             const bf16 *B2, int64_t ldb, int M, int N, int K, void *C, int64_t ldc, const float *rho,
-                            const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s) {
+                            const float *D1, int64_t ldd1, const float *D2, int64_t ldd2, hipStream_t s, int ksplit,
+                            int64_t cstride) {
     if (M <= 0 || N <= 0 || K <= 0 || K % GK || lda % 8 || ldb % 8 || lda < K || ldb < K) return hipErrorInvalidValue;
     if ((int64_t)GM * lda * 2 >= (int64_t(1) << 32) || (int64_t)GN * ldb * 2 >= (int64_t(1) << 32))
         return hipErrorInvalidValue;   // per-tile byte offsets are 32-bit
-    const int64_t tiles = (int64_t)((M + GM - 1) / GM) * ((N + GN - 1) / GN);
+    const int npass = 1 + (A2 != nullptr) + (B2 != nullptr);
+    if (ksplit < 1 || ksplit > (K / GK) * npass || (ksplit > 1 && epi != EPI_STORE && epi != EPI_ACCUM))
+        return hipErrorInvalidValue;   // a split sum takes no epilogue but store or accumulate
+    const int64_t tiles = (int64_t)((M + GM - 1) / GM) * ((N + GN - 1) / GN) * ksplit;
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
     const bool need_d1 = epi == EPI_RESID || epi == EPI_ADD || epi == EPI_ADD_RESID || epi == EPI_GATE;
     if ((need_d1 && !D1) || ((epi == EPI_RESID || epi == EPI_ADD_RESID) && !rho) || (epi == EPI_ADD_RESID && !D2))
@@ -242,14 +250,15 @@ hipError_t launch_gemm_tile(int epi, bool out_f32, const bf16 *A, const bf16 *A2
     if (epi == EPI_SWIGLU && N % 64) return hipErrorInvalidValue;
 #define TL(E)                                                                                                  \
     do {                                                                                                       \
-        if (out_f32) tile_launch<E, float>(A, A2, lda, B, B2, ldb, M, N, K, (float *)C, ldc, rho, D1, ldd1, D2, ldd2, s); \
-        else tile_launch<E, bf16>(A, A2, lda, B, B2, ldb, M, N, K, (bf16 *)C, ldc, rho, D1, ldd1, D2, ldd2, s);           \
+        if (out_f32) tile_launch<E, float>(A, A2, lda, B, B2, ldb, M, N, K, ksplit, cstride, (float *)C, ldc, rho, D1, ldd1, D2, ldd2, s); \
+        else tile_launch<E, bf16>(A, A2, lda, B, B2, ldb, M, N, K, ksplit, cstride, (bf16 *)C, ldc, rho, D1, ldd1, D2, ldd2, s);           \
     } while (0)
     switch (epi) {
         case EPI_STORE: TL(EPI_STORE); break;
         case EPI_ACCUM:
             if (!out_f32) return hipErrorInvalidValue;
-            tile_launch<EPI_ACCUM, float>(A, A2, lda, B, B2, ldb, M, N, K, (float *)C, ldc, rho, D1, ldd1, D2, ldd2, s);
+            tile_launch<EPI_ACCUM, float>(A, A2, lda, B, B2, ldb, M, N, K, ksplit, cstride, (float *)C, ldc, rho, D1,
+                                          ldd1, D2, ldd2, s);
             break;
         case EPI_RESID: TL(EPI_RESID); break;
         case EPI_ADD: TL(EPI_ADD); break;

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void k_lb_drho_sum(const float *__restrict__ p
 // layouts: dWq[c][j D + i] = dWT[c][3 D j + i], dWk at + D, dWv at + 2 D,
 // dwa[c][j] = dWT[c][qkvp + j], dwb[c][j] = dWT[c][qkvp + H + j].
 template <int D>
-__global__ __launch_bounds__(256) void k_lb_unpack(const float *__restrict__ dWT, int64_t P, int64_t qkvp, int d, int H,
+__global__ __launch_bounds__(256) void k_lb_unpack(const float *__restrict__ dWT, const float *__restrict__ dWT2,
+                                                   int64_t P, int64_t qkvp, int d, int H,
                                                    float *__restrict__ dWq, float *__restrict__ dWk,
                                                    float *__restrict__ dWv, float *__restrict__ dwa,
                                                    float *__restrict__ dwb) {
@@ -127,18 +128,30 @@ __global__ __launch_bounds__(256) void k_lb_unpack(const float *__restrict__ dWT
     const int64_t per_row = 3 * HD + 2 * H;
     if (idx >= (int64_t)d * per_row) return;
     const int64_t c = idx / per_row, w = idx % per_row;
-    const float *row = dWT + c * P;
+    const float *row = dWT + c * P, *row2 = dWT2 ? dWT2 + c * P : nullptr;
+    auto get = [&](int64_t col) { return row2 ? row[col] + row2[col] : row[col]; };
     if (w < 3 * HD) {
         const int64_t kind = w / HD, col = w % HD, j = col / D, i = col % D;
         float *dst = kind == 0 ? dWq : (kind == 1 ? dWk : dWv);
-        dst[c * HD + col] = row[3 * D * j + kind * D + i];
+        dst[c * HD + col] = get(3 * D * j + kind * D + i);
     } else if (w < 3 * HD + H) {
         const int64_t j = w - 3 * HD;
-        dwa[c * H + j] = row[qkvp + j];
+        dwa[c * H + j] = get(qkvp + j);
     } else {
         const int64_t j = w - 3 * HD - H;
-        dwb[c * H + j] = row[qkvp + H + j];
+        dwb[c * H + j] = get(qkvp + H + j);
     }
+}
+
+__global__ __launch_bounds__(256) void k_sum_parts(int64_t n, int d, const float *__restrict__ parts, int nparts,
+                                                   int64_t pstride, const float *__restrict__ rho,
+                                                   const float *__restrict__ add, float *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = parts[i];
+    for (int z = 1; z < nparts; ++z) acc += parts[(int64_t)z * pstride + i];
+    if (rho) acc = fmaf(rho[i % d], add[i], acc);
+    out[i] = acc;
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float *p, int64_t n) {
@@ -186,16 +199,25 @@ hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp
     return hipGetLastError();
 }
 
-hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, int64_t P, int64_t qkvp, float *dWq, float *dWk,
-                            float *dWv, float *dwa, float *dwb, hipStream_t s) {
+hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, const float *dWT2, int64_t P, int64_t qkvp,
+                            float *dWq, float *dWk, float *dWv, float *dwa, float *dwb, hipStream_t s) {
     const int64_t n = (int64_t)d * (3LL * H * D + 2 * H);
     const dim3 grid((unsigned)((n + 255) / 256));
     if (D == 128)
-        launch_kernel(k_lb_unpack<128>, grid, dim3(256), 0, s, dWT, P, qkvp, d, H, dWq, dWk, dWv, dwa, dwb);
+        launch_kernel(k_lb_unpack<128>, grid, dim3(256), 0, s, dWT, dWT2, P, qkvp, d, H, dWq, dWk, dWv, dwa, dwb);
     else if (D == 64)
-        launch_kernel(k_lb_unpack<64>, grid, dim3(256), 0, s, dWT, P, qkvp, d, H, dWq, dWk, dWv, dwa, dwb);
+        launch_kernel(k_lb_unpack<64>, grid, dim3(256), 0, s, dWT, dWT2, P, qkvp, d, H, dWq, dWk, dWv, dwa, dwb);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(int64_t rows, int d, const float *parts, int nparts, int64_t pstride, const float *rho,
+                            const float *add, float *out, hipStream_t s) {
+    const int64_t n = rows * d;
+    if (n <= 0) return hipSuccess;
+    launch_kernel(k_sum_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, d, parts, nparts, pstride, rho,
+                  add, out);
     return hipGetLastError();
 }
 

@@ -145,7 +145,8 @@ def test_workspace_sizes():
         xb = up(tok * d * 2) if act == gl.GDN_BF16 else 0   # the bf16 loop operand
         exp = (3 * up(tok * H * D * eb) + 2 * up(tok * H * 4) + xb + chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats)
                + up(tok * P * 4) + (up(tok * P * 4) if act == gl.GDN_BF16 else 0) + up(P * Mp * 4) + up(d * Mp * eb) + up(d * P * eb) + 3 * up(tok * H * D * 4)
-               + 2 * up(tok * H * 4) + 2 * up(tok * d * 4) + up(d * P * 4) + up(((tok + 127) // 128) * d * 4))
+               + 2 * up(tok * H * 4) + 2 * up(tok * d * 4) + up(d * P * 4 * (2 if act == gl.GDN_BF16 else 1))
+               + (up(4 * tok * d * 4) if act == gl.GDN_BF16 else 0) + up(((tok + 127) // 128) * d * 4))
         assert _ws_status(gl.make_desc(B, L, H, D, D, act=act), gl.GDN_OP_LOOP_BACKWARD) == (0, exp)
     st, _ = _ws_status(gl.make_desc(B, L, H, 128, 128, act=gl.GDN_F32), gl.GDN_OP_LOOP_BACKWARD)
     assert st == -3
