@@ -27,7 +27,7 @@ Printed (one JSON line on stdout):
   block           the headline workload through a one-block LT2 stack looped T times (gdn_block_loop_prefill);
   cpu_baseline    the oracle on a bounded sample of the headline workload, on the host's cores.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode]
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME,...] [--no-decode] [--only LEG]
                        [--no-act] [--no-block] [--no-backward] [--no-cpu-baseline]
        python bench.py --calib-copy          (plain 256 MiB device copy, for HBM counter calibration)
 Only one GPU is used: --gpus N with N > 1 exits with a message.
@@ -635,6 +635,9 @@ def main():
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--only", default="", choices=["", "act", "block", "scan_backward", "loop_backward", "decode",
+                                                   "loop_decode"],
+                    help="run one secondary leg alone and print its record (for profiling; no headline line)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -651,6 +654,16 @@ def main():
     import synth
     gl.load()
     w = synth.workload(args.workload)
+    if args.only:
+        legs = {"act": lambda: bench_act(args, torch, gl, synth, w),
+                "block": lambda: bench_block(args, torch, gl, synth, w.name),
+                "scan_backward": lambda: bench_backward(args, torch, gl, synth),
+                "loop_backward": lambda: bench_loop_backward(args, torch, gl, synth),
+                "decode": lambda: bench_decode(args, torch, gl, synth),
+                "loop_decode": lambda: bench_loop_decode(args, torch, gl, synth, synth.workload("decode_n64_s256"))}
+        log(f"{args.only} alone")
+        print(json.dumps({args.only: legs[args.only]()}))
+        return
     log(f"prefill: {w.name}, warmup {args.warmup}, steps {args.steps}")
     pf = bench_prefill(args, w, torch, gl, synth, args.warmup)
     head = prefill_record(w, pf)
