@@ -342,7 +342,7 @@ def bench_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     stages = {"fwd_prep": gl.GDN_STAGE_SCAN_PREP, "fwd_carry": gl.GDN_STAGE_SCAN_CARRY,
-              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_ops": gl.GDN_STAGE_BWD_OPS, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
+              "bwd_ops": gl.GDN_STAGE_BWD_OPS, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
               "bwd_chunk": gl.GDN_STAGE_BWD_CHUNK}
     timers = {k: gl.gdn_timer_create(v, n) for k, v in stages.items()}
     for t in timers.values():
@@ -448,7 +448,7 @@ def bench_loop_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     stages = {"gemm": gl.GDN_STAGE_BWD_GEMM, "fwd_prep": gl.GDN_STAGE_SCAN_PREP, "fwd_carry": gl.GDN_STAGE_SCAN_CARRY,
-              "bwd_prep": gl.GDN_STAGE_BWD_PREP, "bwd_ops": gl.GDN_STAGE_BWD_OPS, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
+              "bwd_ops": gl.GDN_STAGE_BWD_OPS, "bwd_carry": gl.GDN_STAGE_BWD_CARRY,
               "bwd_chunk": gl.GDN_STAGE_BWD_CHUNK}
     timers = {k: gl.gdn_timer_create(v, 3 * n * T) for k, v in stages.items()}
     for t in timers.values():
@@ -470,7 +470,7 @@ def bench_loop_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
     return {"workload": f"loop backward, {name} (B={B}, L={L}, H={H}, dk=dv={D}, d={d}, T={T}, {w.act} inputs)",
             "value": M / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
             "stages_ms_per_call": tot, "stages_avg_launch_us": {k: v * 1e3 for k, v in per.items()},
-            "gemm": {"bound": "mfma", "kernel": "k_gemm_nt", "achieved": gemm_ach, "peak": PEAK_BF16_TFLOPS,
+            "gemm": {"bound": "mfma", "kernel": "k_gemm_tile" if w.act == "bf16" else "k_gemm_nt", "achieved": gemm_ach, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": gemm_ach / PEAK_BF16_TFLOPS,
                      "note": "algorithmic 2MNK per product; fp32 operands run 2-3 bf16 passes"}}
 

@@ -367,23 +367,24 @@ const char *gdn_version(void);
 
 /* ---- optional device timing of one stage -------------------------------- */
 
-/* Stages that a timer can bracket (4 is not a stage: it named a separate
- * output pass that the carry now performs, and gdn_timer_create rejects it). */
+/* Stages that a timer can bracket.  4 and 8 are not stages, and
+ * gdn_timer_create rejects them: 4 named a separate output pass that the carry
+ * now performs, 8 a backward preparation whose matrices the forward's chunk
+ * preparation now writes. */
 enum { GDN_STAGE_PROJECT = 0, GDN_STAGE_SCAN_PREP = 1, GDN_STAGE_SCAN_CARRY = 2,
        GDN_STAGE_DECODE = 3, GDN_STAGE_GATES = 5, GDN_STAGE_BWD_CARRY = 6, GDN_STAGE_BWD_CHUNK = 7,
-       GDN_STAGE_BWD_PREP = 8, GDN_STAGE_BWD_GEMM = 9, GDN_STAGE_BWD_OPS = 10, GDN_STAGE_BLOCK_GEMM = 11 };
+       GDN_STAGE_BWD_GEMM = 9, GDN_STAGE_BWD_OPS = 10, GDN_STAGE_BLOCK_GEMM = 11 };
 /* GDN_STAGE_BLOCK_GEMM times the four products of an LT2 block around its
  * mixer (the gate with o, the output projection, the FFN's up and down
  * projections); the mixer's own launches keep their stages. */
 /* GDN_STAGE_BWD_GEMM times the three products of each loop of
  * gdn_loop_backward (the projections recomputed, the input gradient and the
  * weight gradient). */
-/* GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_OPS, GDN_STAGE_BWD_CARRY and
- * GDN_STAGE_BWD_CHUNK time the four kernels of the scan backward (in
- * gdn_scan_backward and in each loop of gdn_loop_backward) that follow its
- * forward recomputation
- * (whose prep and carry are timed as GDN_STAGE_SCAN_PREP and
- * GDN_STAGE_SCAN_CARRY). */
+/* GDN_STAGE_BWD_OPS, GDN_STAGE_BWD_CARRY and GDN_STAGE_BWD_CHUNK time the
+ * three kernels of the scan backward (in gdn_scan_backward and in each loop
+ * of gdn_loop_backward) that follow its forward recomputation, whose prep
+ * (which also forms the backward's chunk matrices) and carry are timed as
+ * GDN_STAGE_SCAN_PREP and GDN_STAGE_SCAN_CARRY. */
 /* GDN_STAGE_SCAN_CARRY times the carry kernel, which computes the chunk outputs
  * (and the loop residual) as well.  GDN_STAGE_PROJECT times the projection GEMM.  For bf16 inputs of 1024 or
  * more tokens the gates alpha/beta leave the GEMM's epilogue: gdn_project and

@@ -23,7 +23,7 @@ __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_OP_LOOP_PREFILL", "GDN_OP_LOOP_DECODE", "GDN_OP_SCAN_PREFILL", "GDN_OP_SCAN_DECODE",
     "GDN_OP_PROJECT", "GDN_OP_SCAN_BACKWARD", "GDN_OP_LOOP_PREFILL_ACT", "GDN_OP_LOOP_BACKWARD",
     "GDN_STAGE_PROJECT", "GDN_STAGE_SCAN_PREP", "GDN_STAGE_SCAN_CARRY", "GDN_STAGE_DECODE", "GDN_STAGE_GATES",
-    "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_PREP", "GDN_STAGE_BWD_GEMM", "GDN_STAGE_BWD_OPS",
+    "GDN_STAGE_BWD_CARRY", "GDN_STAGE_BWD_CHUNK", "GDN_STAGE_BWD_GEMM", "GDN_STAGE_BWD_OPS",
     "GDN_STAGE_BLOCK_GEMM", "GDN_WS_Q", "GDN_WS_K", "GDN_WS_V", "GDN_WS_ALPHA", "GDN_WS_BETA", "GDN_BWS_X1",
     "GDN_BWS_O", "GDN_BWS_Z", "GDN_BWS_H1", "GDN_BWS_X2", "GDN_BWS_U", "GdnError", "gdn_desc", "make_desc",
     "lib_path", "load", "EXPORTED", "workspace", "workspace_view", "block_workspace", "block_workspace_view",
@@ -39,7 +39,7 @@ GDN_F32, GDN_BF16 = 0, 1
 (GDN_OP_LOOP_PREFILL, GDN_OP_LOOP_DECODE, GDN_OP_SCAN_PREFILL, GDN_OP_SCAN_DECODE, GDN_OP_PROJECT, GDN_OP_SCAN_BACKWARD,
  GDN_OP_LOOP_PREFILL_ACT, GDN_OP_LOOP_BACKWARD) = range(8)
 GDN_STAGE_PROJECT, GDN_STAGE_SCAN_PREP, GDN_STAGE_SCAN_CARRY, GDN_STAGE_DECODE, GDN_STAGE_GATES = 0, 1, 2, 3, 5
-GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_PREP, GDN_STAGE_BWD_GEMM, GDN_STAGE_BWD_OPS = 6, 7, 8, 9, 10
+GDN_STAGE_BWD_CARRY, GDN_STAGE_BWD_CHUNK, GDN_STAGE_BWD_GEMM, GDN_STAGE_BWD_OPS = 6, 7, 9, 10
 GDN_STAGE_BLOCK_GEMM = 11
 GDN_WS_Q, GDN_WS_K, GDN_WS_V, GDN_WS_ALPHA, GDN_WS_BETA = range(5)
 GDN_BWS_X1, GDN_BWS_O, GDN_BWS_Z, GDN_BWS_H1, GDN_BWS_X2, GDN_BWS_U = range(16, 22)

@@ -61,12 +61,25 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
 hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
                         float *beta, float alpha_lo, hipStream_t s);
 
+// Chunk matrices that the backward pass takes from the forward preparation,
+// per chunk (regions of a bwd_mats_bytes block): T, P, A [64][64] fp32
+// row-major (A = strict_lower(Gam (.) K K^T), P = lower_incl(Gam (.) Q K^T),
+// both zero in the rows of tokens past the end of the sequence; T =
+// (I + diag(beta) A)^{-1}), the fp64 log-cumsum lg of alpha, gamma = e^lg and
+// c = e^(lg_last - lg) [64] fp32.
+struct PrepBwd {
+    float *T, *P, *A;
+    double *lg;
+    float *gam, *c;
+};
 // Chunk preparation: per (b, h, chunk) decay products, the UT-transform
-// inverse and the derived matrices W [D x 64], M [64 x 64], gamma [64].
+// inverse and the derived matrices W [D x 64], M [64 x 64], gamma [64]; with
+// bwd.T set, also the backward's chunk matrices.
 struct ChunkWs {
     float *W;    // per chunk: bf16 hi plane [D][64] then bf16 lo plane [D][64] (D*64*4 bytes)
     float *M;    // per chunk: bf16 hi plane [64][64] then bf16 lo plane [64][64]
     float *g;    // per chunk: gamma [64] fp32
+    PrepBwd bwd = {};
 };
 // Gates of the chunk preparation: alpha/beta [B*L, H], or (zp != nullptr) the
 // P partial pre-activations zp[P][2H][B*L] of the projection, summed in order
@@ -125,9 +138,10 @@ hipError_t launch_lb_epilogue_grad(int M, int H, int D, float *Y, int64_t P, int
 int lb_drho_blocks(int M);
 hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp_f32, float *part, float *drho,
                           hipStream_t s);
-// dWT [d][P] (plus dWT2 when given) to dWq, dWk [d][H D], dWv [d][H D], dwa, dwb [d][H].
-hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, const float *dWT2, int64_t P, int64_t qkvp,
-                            float *dWq, float *dWk, float *dWv, float *dwa, float *dwb, hipStream_t s);
+// dWT [d][P], the sum of nparts partial arrays pstride floats apart (added in
+// order), to dWq, dWk [d][H D], dWv [d][H D], dwa, dwb [d][H].
+hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, int nparts, int64_t pstride, int64_t P,
+                            int64_t qkvp, float *dWq, float *dWk, float *dWv, float *dwa, float *dwb, hipStream_t s);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 
 // ---- products and transposes of the loop backward (gemm_nt.hip) ----
@@ -187,10 +201,10 @@ hipError_t launch_act_rows(int M, const int *halt, int tau, int *rows, int *coun
 hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,
                              ChunkWs ws, const float *s_init, float *s_final, CarryOut out, hipStream_t s);
 
-// Backward of the chunkwise scan.  launch_bwd_prep forms per (b, h, chunk) T,
-// P, A, the log-cumsum of alpha, gamma and c in `mats` (bwd_mats_bytes for
-// B*H*Nc chunks of width D); launch_bwd_ops the reverse carry's operands from
-// them and dO: W^T = diag(beta) T^T diag(c) K (split bf16), K^T, Q^T (bf16) and
+// Backward of the chunkwise scan.  The forward preparation, given
+// bwd_prep_out(mats, B*H*Nc, D), forms per (b, h, chunk) T, P, A, the
+// log-cumsum of alpha, gamma and c in `mats` (bwd_mats_bytes for B*H*Nc chunks
+// of width D); launch_bwd_ops the reverse carry's operands from them and dO: W^T = diag(beta) T^T diag(c) K (split bf16), K^T, Q^T (bf16) and
 // M^T dO = diag(beta) T^T P^T dO (fp32).  The reverse carry walks the chunks of
 // each (b, h, 16-column slice) backwards on MFMA: dE = M^T dO + W^T dS'
 // (written to dv), dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dE,
@@ -199,8 +213,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
 // per (b, h, chunk) from the chunk-start states s_chunks and ds_end.  fp32
 // inputs need D = 64.
 size_t bwd_mats_bytes(int64_t chunks, int D);
-hipError_t launch_bwd_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *alpha,
-                           const float *beta, float *mats, hipStream_t s);
+PrepBwd bwd_prep_out(float *mats, int64_t chunks, int D);
 hipError_t launch_bwd_ops(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
                           const float *d_o, float *mats, hipStream_t s);
 hipError_t launch_bwd_carry(bool f32, int B, int L, int H, int D, const float *d_o, const float *d_sfinal,

@@ -108,9 +108,32 @@ gdn_status check_loop_backward(const gdn_desc *d) {
         if ((p) && !aligned16(p)) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p);     \
     } while (0)
 
-// The loop backward's dY W product splits its k range into up to this many
-// partial sums when its tiles alone would leave CUs idle.
-constexpr int LB_DX_SPLIT = 4;
+// The loop backward's products split their k range into partial sums when
+// their tiles alone would leave CUs idle (one 384 x 256 tile per CU at a time):
+// dY W into at most LB_DX_SPLIT (summed with the residual), x^T dY into at
+// most LB_DW_SPLIT accumulators (summed when unpacked).  The count minimises
+// the rounds of tiles per unit of work plus `cost` per extra partial sum (its
+// traffic, in rounds).  Sized for 256 CUs, so that workspace sizes do not
+// depend on the device.
+constexpr int LB_DX_SPLIT = 4, LB_DW_SPLIT = 3;
+static int lb_split(int64_t tiles, int max_split, double cost) {
+    int best = 1;
+    double best_c = 1e30;
+    for (int sp = 1; sp <= max_split; ++sp) {
+        const double c = (double)((tiles * sp + 255) / 256) / sp + cost * (sp - 1);
+        if (c < best_c - 1e-9) {
+            best_c = c;
+            best = sp;
+        }
+    }
+    return best;
+}
+static int lb_dx_split(int64_t tokens, int d) {
+    return lb_split(((tokens + 383) / 384) * ((d + 255) / 256), LB_DX_SPLIT, 0.025);
+}
+static int lb_dw_split(int d, int64_t P, bool f32) {
+    return f32 ? 1 : lb_split(((int64_t)(d + 383) / 384) * ((P + 255) / 256), LB_DW_SPLIT, 0.05);
+}
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
@@ -179,8 +202,9 @@ Layout layout(const gdn_desc *d, int op) {
         lo.gbe = take(tokens * d->H * 4);
         lo.dhA = take(tokens * d->d * 4);
         lo.dhB = take(tokens * d->d * 4);
-        lo.dW = take(d->d * P * 4 * (d->act == GDN_BF16 ? 2 : 1));   // bf16: two split-k halves
-        if (d->act == GDN_BF16) lo.Gp = take((size_t)LB_DX_SPLIT * tokens * d->d * 4);
+        lo.dW = take(d->d * P * 4 * lb_dw_split(d->d, P, d->act == GDN_F32));
+        const int dxs = lb_dx_split(tokens, d->d);
+        if (d->act == GDN_BF16 && dxs > 1) lo.Gp = take((size_t)dxs * tokens * d->d * 4);
         lo.part = take((size_t)lb_drho_blocks((int)tokens) * d->d * 4);
     }
     if (act) {
@@ -335,11 +359,14 @@ gdn_status gdn_project(const gdn_desc *desc, const void *x, const void *Wpack, v
     return e == hipSuccess ? GDN_OK : hip_fail(e, "projection launch");
 }
 
+// The chunk preparation and the carry.  With `bwd_mats` the preparation also
+// writes the chunk matrices of the backward pass there.
 static gdn_status scan_chunks(const gdn_desc *d, const void *q, const void *k, const void *v,
                               GateSrc gates, const float *s_init, float *s_final, CarryOut out, void *ws,
-                              const Layout &lo, hipStream_t s) {
+                              const Layout &lo, hipStream_t s, float *bwd_mats = nullptr) {
     const bool f32 = d->act == GDN_F32;
     ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g)};
+    if (bwd_mats) cw.bwd = bwd_prep_out(bwd_mats, (int64_t)d->B * d->H * ((d->L + 63) / 64), d->dk);
     hipError_t e = timed(GDN_STAGE_SCAN_PREP, s, [&] {
         return launch_scan_prep(f32, d->B, d->L, d->H, d->dk, q, k, gates, cw, s);
     });
@@ -390,17 +417,12 @@ gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k,
     const bool f32 = desc->act == GDN_F32;
     const int B = desc->B, L = desc->L, H = desc->H, D = desc->dk;
     // forward recomputation: the chunk matrices, then the state chain with the chunk-start states kept
-    float *sc = (float *)at(ws, lo.sc), *dse = (float *)at(ws, lo.dse);
+    float *sc = (float *)at(ws, lo.sc), *dse = (float *)at(ws, lo.dse), *bm = (float *)at(ws, lo.bm);
     CarryOut out{nullptr, nullptr, false, nullptr, nullptr, nullptr, sc};
     st = scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo, nullptr, nullptr}, s_init,
-                     nullptr, out, ws, lo, s);
+                     nullptr, out, ws, lo, s, bm);
     if (st != GDN_OK) return st;
-    float *bm = (float *)at(ws, lo.bm);
-    hipError_t e = timed(GDN_STAGE_BWD_PREP, s, [&] {
-        return launch_bwd_prep(f32, B, L, H, D, q, k, alpha, beta, bm, s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "backward prep launch");
-    e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, beta, d_o, bm, s); });
+    hipError_t e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, beta, d_o, bm, s); });
     if (e != hipSuccess) return hip_fail(e, "backward carry operands launch");
     e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
         return launch_bwd_carry(f32, B, L, H, D, d_o, d_sfinal, bm, dv, dse, ds_init, s);
@@ -454,11 +476,9 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
 
     hipError_t e = launch_transpose(f32, f32, Wpack, d, P, d, WT, P, P, s);   // W^T [d][P]
     if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
-    if ((e = launch_fill_zero(dW, (int64_t)d * P * (f32 ? 1 : 2), s)) != hipSuccess) return hip_fail(e, "fill launch");
-    // bf16: dY W splits its k range so that its tiles fill the chip (partials summed with the residual), and
-    // x^T dY accumulates in two k halves (summed when unpacked)
-    const int dx_tiles = ((M + 383) / 384) * ((d + 255) / 256);
-    const int dx_split = std::min(LB_DX_SPLIT, std::max(1, (256 + dx_tiles - 1) / dx_tiles));
+    // bf16: dY W and x^T dY split their k ranges so that their tiles fill the chip
+    const int dx_split = f32 ? 1 : lb_dx_split(M, d), dw_split = lb_dw_split(d, P, f32);
+    if ((e = launch_fill_zero(dW, (int64_t)d * P * dw_split, s)) != hipSuccess) return hip_fail(e, "fill launch");
     for (int tau = T - 1; tau >= 0; --tau) {
         // loop tau + 1 of the forward: input h^(tau), incoming gradient dL/dh^(tau+1)
         const bool hp_f32 = f32 || tau > 0;
@@ -488,10 +508,8 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         // partials the prep forms alpha and beta into their workspace regions, as in the forward
         CarryOut out{nullptr, nullptr, false, nullptr, nullptr, nullptr, sc};
         st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
-                         nullptr, nullptr, out, ws, lo, s);
+                         nullptr, nullptr, out, ws, lo, s, bm);
         if (st != GDN_OK) return st;
-        e = timed(GDN_STAGE_BWD_PREP, s, [&] { return launch_bwd_prep(f32, B, L, H, D, q, k, al, be, bm, s); });
-        if (e != hipSuccess) return hip_fail(e, "backward prep launch");
         e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, be, g_in, bm, s); });
         if (e != hipSuccess) return hip_fail(e, "backward carry operands launch");
         e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
@@ -546,12 +564,12 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
                 return hip_fail(e, "transpose launch");
             e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
                 return launch_gemm_tile(EPI_ACCUM, true, (const bf16 *)XT, nullptr, Mp, YTh, YTl, Mp, d, P, Mp, dW,
-                                        P, nullptr, nullptr, 0, nullptr, 0, s, 2, (int64_t)d * P);
+                                        P, nullptr, nullptr, 0, nullptr, 0, s, dw_split, (int64_t)d * P);
             });
         }
         if (e != hipSuccess) return hip_fail(e, "weight gradient launch");
     }
-    e = launch_lb_unpack(d, H, D, dW, f32 ? nullptr : dW + (int64_t)d * P, P, qkvp, dWq, dWk, dWv, dwa, dwb, s);
+    e = launch_lb_unpack(d, H, D, dW, dw_split, (int64_t)d * P, P, qkvp, dWq, dWk, dWv, dwa, dwb, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "weight gradient unpack launch");
 }
 
@@ -958,7 +976,8 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
 // ---- timers -------------------------------------------------------------------
 gdn_status gdn_timer_create(int stage, int capacity, gdn_timer **out) {
     if (!out) return fail(GDN_ERR_NULL, "out is NULL");
-    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BLOCK_GEMM || stage == 4 || capacity < 1 || capacity > (1 << 20))
+    if (stage < GDN_STAGE_PROJECT || stage > GDN_STAGE_BLOCK_GEMM || stage == 4 || stage == 8 || capacity < 1 ||
+        capacity > (1 << 20))
         return fail(GDN_ERR_SHAPE, "bad timer stage %d or capacity %d", stage, capacity);
     gdn_timer *t = new gdn_timer;
     t->stage = stage;

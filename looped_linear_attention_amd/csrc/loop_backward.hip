@@ -92,18 +92,47 @@ __global__ __launch_bounds__(256) void k_lb_epilogue_grad(float *Y, int64_t P, i
     }
 }
 
-// drho partials: part[rb][c] = sum over rows r of block rb (ROWS rows) of
-// dh[r][c] hp[r][c]; then drho[c] = sum over rb in order.
-constexpr int DR_ROWS = 128;
+// drho partials: part[rb][c] = sum over rows r of block rb (DR_ROWS rows, in
+// order) of dh[r][c] hp[r][c]; then drho[c] = sum over rb in order.  A thread
+// takes 4 adjacent columns (16-byte loads of dh) and issues the loads of 8
+// rows before it adds them up.
+constexpr int DR_ROWS = 32;
+template <typename TH> struct Quad;
+template <> struct Quad<float> {
+    __device__ static float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+};
+template <> struct Quad<bf16> {
+    __device__ static float4 load(const bf16 *p) {
+        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+        return float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+};
 template <typename TH>
 __global__ __launch_bounds__(256) void k_lb_drho_part(const float *__restrict__ dh, const TH *__restrict__ hp, int M,
                                                       int d, float *__restrict__ part) {
-    const int c = blockIdx.x * 256 + threadIdx.x, rb = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4, rb = blockIdx.y;
     if (c >= d) return;
-    const int r1 = min(M, (rb + 1) * DR_ROWS);
-    float acc = 0.f;
-    for (int r = rb * DR_ROWS; r < r1; ++r) acc = fmaf(dh[(int64_t)r * d + c], to_f32(hp[(int64_t)r * d + c]), acc);
-    part[(int64_t)rb * d + c] = acc;
+    const int r0 = rb * DR_ROWS, r1 = min(M, r0 + DR_ROWS);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = r0; r < r1; r += 8) {
+        float4 a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t o = (int64_t)min(r + u, r1 - 1) * d + c;
+            a[u] = *reinterpret_cast<const float4 *>(dh + o);
+            b[u] = Quad<TH>::load(hp + o);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (r + u < r1) {
+                acc.x = fmaf(a[u].x, b[u].x, acc.x);
+                acc.y = fmaf(a[u].y, b[u].y, acc.y);
+                acc.z = fmaf(a[u].z, b[u].z, acc.z);
+                acc.w = fmaf(a[u].w, b[u].w, acc.w);
+            }
+        }
+    }
+    *reinterpret_cast<float4 *>(part + (int64_t)rb * d + c) = acc;
 }
 __global__ __launch_bounds__(256) void k_lb_drho_sum(const float *__restrict__ part, int nrb, int d,
                                                      float *__restrict__ drho) {
@@ -118,7 +147,7 @@ __global__ __launch_bounds__(256) void k_lb_drho_sum(const float *__restrict__ p
 // layouts: dWq[c][j D + i] = dWT[c][3 D j + i], dWk at + D, dWv at + 2 D,
 // dwa[c][j] = dWT[c][qkvp + j], dwb[c][j] = dWT[c][qkvp + H + j].
 template <int D>
-__global__ __launch_bounds__(256) void k_lb_unpack(const float *__restrict__ dWT, const float *__restrict__ dWT2,
+__global__ __launch_bounds__(256) void k_lb_unpack(const float *__restrict__ dWT, int nparts, int64_t pstride,
                                                    int64_t P, int64_t qkvp, int d, int H,
                                                    float *__restrict__ dWq, float *__restrict__ dWk,
                                                    float *__restrict__ dWv, float *__restrict__ dwa,
@@ -128,8 +157,12 @@ __global__ __launch_bounds__(256) void k_lb_unpack(const float *__restrict__ dWT
     const int64_t per_row = 3 * HD + 2 * H;
     if (idx >= (int64_t)d * per_row) return;
     const int64_t c = idx / per_row, w = idx % per_row;
-    const float *row = dWT + c * P, *row2 = dWT2 ? dWT2 + c * P : nullptr;
-    auto get = [&](int64_t col) { return row2 ? row[col] + row2[col] : row[col]; };
+    const float *row = dWT + c * P;
+    auto get = [&](int64_t col) {   // the k-range partial sums, in order
+        float acc = row[col];
+        for (int z = 1; z < nparts; ++z) acc += row[(int64_t)z * pstride + col];
+        return acc;
+    };
     if (w < 3 * HD) {
         const int64_t kind = w / HD, col = w % HD, j = col / D, i = col % D;
         float *dst = kind == 0 ? dWq : (kind == 1 ? dWk : dWv);
@@ -189,8 +222,8 @@ int lb_drho_blocks(int M) { return (M + DR_ROWS - 1) / DR_ROWS; }
 hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp_f32, float *part, float *drho,
                           hipStream_t s) {
     const int nrb = lb_drho_blocks(M);
-    if (nrb > 65535) return hipErrorInvalidValue;
-    const dim3 g1((d + 255) / 256, nrb);
+    if (nrb > 65535 || d % 4) return hipErrorInvalidValue;
+    const dim3 g1((d / 4 + 255) / 256, nrb);
     if (hp_f32) launch_kernel(k_lb_drho_part<float>, g1, dim3(256), 0, s, dh, (const float *)hp, M, d, part);
     else launch_kernel(k_lb_drho_part<bf16>, g1, dim3(256), 0, s, dh, (const bf16 *)hp, M, d, part);
     hipError_t e = hipGetLastError();
@@ -199,14 +232,17 @@ hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp
     return hipGetLastError();
 }
 
-hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, const float *dWT2, int64_t P, int64_t qkvp,
-                            float *dWq, float *dWk, float *dWv, float *dwa, float *dwb, hipStream_t s) {
+hipError_t launch_lb_unpack(int d, int H, int D, const float *dWT, int nparts, int64_t pstride, int64_t P,
+                            int64_t qkvp, float *dWq, float *dWk, float *dWv, float *dwa, float *dwb, hipStream_t s) {
     const int64_t n = (int64_t)d * (3LL * H * D + 2 * H);
     const dim3 grid((unsigned)((n + 255) / 256));
+    if (nparts < 1) return hipErrorInvalidValue;
     if (D == 128)
-        launch_kernel(k_lb_unpack<128>, grid, dim3(256), 0, s, dWT, dWT2, P, qkvp, d, H, dWq, dWk, dWv, dwa, dwb);
+        launch_kernel(k_lb_unpack<128>, grid, dim3(256), 0, s, dWT, nparts, pstride, P, qkvp, d, H, dWq, dWk, dWv,
+                      dwa, dwb);
     else if (D == 64)
-        launch_kernel(k_lb_unpack<64>, grid, dim3(256), 0, s, dWT, dWT2, P, qkvp, d, H, dWq, dWk, dWv, dwa, dwb);
+        launch_kernel(k_lb_unpack<64>, grid, dim3(256), 0, s, dWT, nparts, pstride, P, qkvp, d, H, dWq, dWk, dWv,
+                      dwa, dwb);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -17,8 +17,9 @@
 //     dE = Tb^T dU = M^T dO + W^T dS'                       (= dV)
 //     dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dE
 // chunk after chunk in reverse (k_bwd_carry: sequential over chunks, parallel
-// over column slices of S, from the fp32 T, P, gamma, c that k_bwd_prep forms
-// per chunk), and per chunk, in parallel (k_bwd_chunk):
+// over column slices of S, from the fp32 T, P, gamma, c that the forward's
+// chunk preparation also writes when asked), and per chunk, in parallel
+// (k_bwd_chunk):
 //     dP  = lower_incl(dO U^T),  dTb = dU E^T,  dT = dTb diag(beta),
 //     dN  = strict_lower(-T^T dT T^T),  dA = diag(beta) dN
 //     dQ  = diag(gamma) dO S^T + (Gam (.) dP) K
@@ -33,7 +34,9 @@
 //     dgamma_r = sum_j dO_rj (Q S)_rj - dE_rj (K S)_rj,  dc_r = sum_j U_rj (K dS')_rj,
 //     dgamma_C = sum S (.) dS'.
 // Tokens past the end of a sequence are zero rows with alpha = 1, beta = 0,
-// so they contribute nothing.  Everything here is fp32 VALU arithmetic.
+// so they contribute nothing.  Products of the reverse carry and of the chunk
+// kernel run on 16x16x32 MFMA with fp32 operands split into bf16 hi + lo
+// (exact bf16 inputs are not split); the rest is fp32 VALU arithmetic.
 #include "gdn_device.h"
 #include "gdn_kernels.h"
 
@@ -78,89 +81,6 @@ BwdMats bwd_mats(float *base, int64_t chunks, int D) {
     m.Qtl = b + 5 * plane;
     m.MtdO = reinterpret_cast<float *>(b + 6 * plane);
     return m;
-}
-
-// ---------------------------------------------------------------------------
-// backward prep: one workgroup per (b, h, chunk)
-// ---------------------------------------------------------------------------
-constexpr int BP_THREADS = 256;
-
-template <int D, typename TIn>
-__global__ __launch_bounds__(BP_THREADS) void k_bwd_prep(const TIn *__restrict__ q, const TIn *__restrict__ k,
-                                                         const float *__restrict__ alpha,
-                                                         const float *__restrict__ beta, int L, int H, int Nc,
-                                                         BwdMats bm) {
-    __shared__ TIn Ks[C][D], Qs[C][D];
-    __shared__ float As[C][C + 1], bes[C];
-    __shared__ double lgs[C];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int h = blockIdx.x % H, chunk = blockIdx.x / H, b = blockIdx.y;
-    const int c0 = chunk * C, nvalid = min(C, L - c0);
-    const int64_t tok0 = (int64_t)b * L + c0;
-    const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
-    for (int n = t; n < C * D; n += BP_THREADS) {
-        const int r = n / D, i = n % D;
-        const bool ok = r < nvalid;
-        const int64_t off = ((tok0 + (ok ? r : 0)) * H + h) * D + i;
-        Ks[r][i] = ok ? k[off] : from_f32<TIn>(0.f);
-        Qs[r][i] = ok ? q[off] : from_f32<TIn>(0.f);
-    }
-    if (wave == 0) {
-        // log-cumsum of alpha in fp64 (tokens past the end: alpha = 1, beta = 0)
-        const bool ok = lane < nvalid;
-        const int64_t gi = (tok0 + (ok ? lane : 0)) * H + h;
-        const float a = ok ? alpha[gi] : 1.f;
-        bes[lane] = ok ? beta[gi] : 0.f;
-        double x = log((double)fmaxf(a, 1e-37f));
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        lgs[lane] = x;
-        const double last = __shfl(x, 63, 64);
-        bm.lg[cid * C + lane] = x;
-        bm.gam[cid * C + lane] = (float)exp(x);
-        bm.c[cid * C + lane] = (float)exp(last - x);
-    }
-    __syncthreads();
-    // A = strict_lower(Gam (.) K K^T), P = lower_incl(Gam (.) Q K^T)
-    float *Ag = bm.A + cid * C * C, *Pg = bm.P + cid * C * C, *Tg = bm.T + cid * C * C;
-    for (int n = t; n < C * C; n += BP_THREADS) {
-        const int r = n / C, i = n % C;
-        float kk = 0.f, qk = 0.f;
-        if (i <= r) {
-            for (int e = 0; e < D; ++e) {
-                const float ki = to_f32(Ks[i][e]);
-                kk = fmaf(to_f32(Ks[r][e]), ki, kk);
-                qk = fmaf(to_f32(Qs[r][e]), ki, qk);
-            }
-        }
-        const float gm = i <= r ? (float)exp(lgs[r] - lgs[i]) : 0.f;
-        const float av = i < r ? gm * kk : 0.f;
-        As[r][i] = av;
-        Ag[n] = av;
-        Pg[n] = i <= r ? gm * qk : 0.f;
-    }
-    __syncthreads();
-    // T = (I + diag(beta) A)^{-1}: column cc by forward substitution
-    if (t < C) {
-        const int cc = t;
-        float tcol[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float v = r == cc ? 1.f : 0.f;
-            if (r > cc) {
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < r; ++i)
-                    if (i >= cc) s = fmaf(As[r][i], tcol[i], s);
-                v = -bes[r] * s;
-            }
-            tcol[r] = v;
-            Tg[r * C + cc] = v;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -936,19 +856,9 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
 
 }  // namespace
 
-hipError_t launch_bwd_prep(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *alpha,
-                           const float *beta, float *mats, hipStream_t s) {
-    const int Nc = (L + C - 1) / C;
-    const dim3 grid((unsigned)(Nc * H), B);
-    const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc, D);
-#define BP(DD, T) launch_kernel((k_bwd_prep<DD, T>), grid, dim3(BP_THREADS), 0, s, (const T *)q, (const T *)k, alpha, beta, L, H, Nc, bm)
-    if (f32) {
-        if (D == 64) BP(64, float); else return hipErrorInvalidValue;
-    } else {
-        if (D == 128) BP(128, bf16); else BP(64, bf16);
-    }
-#undef BP
-    return hipGetLastError();
+PrepBwd bwd_prep_out(float *mats, int64_t chunks, int D) {
+    const BwdMats bm = bwd_mats(mats, chunks, D);
+    return PrepBwd{bm.T, bm.P, bm.A, bm.lg, bm.gam, bm.c};
 }
 
 hipError_t launch_bwd_ops(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,

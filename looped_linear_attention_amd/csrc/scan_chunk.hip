@@ -158,7 +158,10 @@ __device__ __forceinline__ f32x4 mma4s(const float (&a)[4], const float (&b)[4],
     return mfma16x16x16(pack4(al), pack4(bh), c);
 }
 
-template <int D, typename TIn, bool GP>
+// With BWO it also writes the chunk matrices that the backward pass takes (A,
+// P, T, the log-cumsum, gamma and c, fp32 row-major; A and P zero in the rows
+// of tokens past the end).
+template <int D, typename TIn, bool GP, bool BWO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_prep(const TIn *__restrict__ q,
                                                    const TIn *__restrict__ k,
                                                    const float *__restrict__ alpha,
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
                                                    float alpha_lo, int L, int H,
                                                    int Nc, float *__restrict__ wsW,
                                                    float *__restrict__ wsM,
-                                                   float *__restrict__ wsg) {
+                                                   float *__restrict__ wsg, PrepBwd bo) {
     constexpr bool F32 = In<TIn>::f32;
     constexpr int LT = C + 4;                // row stride (floats) of the 64x64 N and T tiles
     constexpr int KS = D / 32;               // k-steps of the D contractions
@@ -202,6 +205,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int h = blockIdx.x % H, chunk = blockIdx.x / H, b = blockIdx.y;
     const int c0 = chunk * C;
     const int64_t tok0 = (int64_t)b * L + c0;
+    const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
 
     // (1) K and Q tiles into LDS by direct loads of whole 1 KiB runs (rows past
     // the end of the sequence re-read the last row: beta = 0 makes their rows
@@ -261,6 +265,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         }
         lgs[lane] = x;
         bes[lane] = ok ? b_raw : 0.f;
+        if constexpr (BWO) {
+            const double xl = __shfl(x, 63, 64);
+            bo.lg[cid * C + lane] = x;
+            bo.gam[cid * C + lane] = (float)exp(x);
+            bo.c[cid * C + lane] = (float)exp(xl - x);
+        }
     }
     wait_vmcnt<0>();   // this wave's direct loads of the K and Q tiles landed
     __syncthreads();   // ... and the other waves'.
@@ -335,6 +345,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
                 const int m = 16 * tn + 4 * lg + j;                               // P[r_a][m]
                 const float gp = __expf((float)(lr_a - lm[tn][j]));
                 pv[tn][j] = (tn <= wave && m <= r_a) ? gp * kq[tn][j] : 0.f;
+                if constexpr (BWO)
+                    bo.A[cid * C * C + row * C + col] = (tn <= wave && col < row && row <= last) ? gn * kk[tn][j] : 0.f;
+            }
+            if constexpr (BWO) {
+                const bool ok = r_a <= last;
+                *reinterpret_cast<f32x4 *>(bo.P + cid * C * C + r_a * C + 16 * tn + 4 * lg) =
+                    f32x4{ok ? pv[tn][0] : 0.f, ok ? pv[tn][1] : 0.f, ok ? pv[tn][2] : 0.f, ok ? pv[tn][3] : 0.f};
             }
         }
     }
@@ -423,10 +440,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         Ts[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.f;
     }
     __syncthreads();
+    if constexpr (BWO) {   // T, row r = t / 4, 16 columns from 16 (t % 4)
+        const int r = t >> 2, c16 = 16 * (t & 3);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<float4 *>(bo.T + cid * C * C + r * C + c16 + 4 * u) =
+                *reinterpret_cast<const float4 *>(Ts + r * LT + c16 + 4 * u);
+    }
 
     // (6) Tb^T fragments, A operand over k = token m (carry slot order):
     // Tb[m][c] = T[m][c] beta_c; the W variant also carries gamma_C / gamma_m
-    const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
     bf16 *dW = reinterpret_cast<bf16 *>(wsW + cid * D * C);
     bf16 *dM = reinterpret_cast<bf16 *>(wsM + cid * C * C);
     const double lgC = lgs[C - 1];
@@ -1552,10 +1575,14 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
     if ((int64_t)Nc * H > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid((unsigned)(Nc * H), B);
     if (gs.zp && (f32 || gs.P < 1 || gs.P > 16)) return hipErrorInvalidValue;
-#define PREP(DD, T, GP)                                                                            \
-    launch_kernel((k_scan_prep<DD, T, GP>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,     \
+#define PREP1(DD, TT, GP, BW)                                                                       \
+    launch_kernel((k_scan_prep<DD, TT, GP, BW>), grid, dim3(256), 0, s, (const TT *)q, (const TT *)k, \
                   gs.alpha, gs.beta, gs.zp, gs.P, B * L, gs.alpha_out, gs.beta_out, gs.alpha_lo, L, H, Nc, \
-                  ws.W, ws.M, ws.g)
+                  ws.W, ws.M, ws.g, ws.bwd)
+#define PREP(DD, TT, GP)                                                                            \
+    do {                                                                                           \
+        if (ws.bwd.T) PREP1(DD, TT, GP, true); else PREP1(DD, TT, GP, false);                        \
+    } while (0)
     if (f32) {
         if (D == 128) PREP(128, float, false); else PREP(64, float, false);
     } else if (gs.zp) {
@@ -1564,6 +1591,7 @@ hipError_t launch_scan_prep(bool f32, int B, int L, int H, int D, const void *q,
         if (D == 128) PREP(128, bf16, false); else PREP(64, bf16, false);
     }
 #undef PREP
+#undef PREP1
     return hipGetLastError();
 }
 

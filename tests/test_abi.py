@@ -134,7 +134,18 @@ def test_workspace_sizes():
     # loop backward: the loop prefill's regions (q, k, v, alpha, beta, the bf16 operand; gate partials from 1024
     # tokens), the scan backward's, then the raw projections (and for bf16 their gradient as bf16 hi/lo planes)
     # [M][P] and their transpose [P][Mp] (Mp = M rounded up to 64), x^T [d][Mp] and W^T [d][P] in the activation
-    # dtype, the scan gradients, two dh buffers, the weight-gradient accumulator [d][P] and the rho partials
+    # dtype, the scan gradients, two dh buffers, the weight-gradient accumulators [d][P] (bf16: one per k-range
+    # split of x^T dY), the split-k partials of dY W (bf16, when split) and the rho partials (32-row blocks).
+    # A product with `tiles` 384 x 256 tiles splits its k range s ways, s in 1..smax minimising
+    # ceil(tiles s / 256) / s + cost (s - 1).
+    def split(tiles, smax, cost):
+        best, bc = 1, 1e30
+        for sp in range(1, smax + 1):
+            c = -(-tiles * sp // 256) / sp + cost * (sp - 1)
+            if c < bc - 1e-9:
+                best, bc = sp, c
+        return best
+
     for act, eb in [(gl.GDN_BF16, 2), (gl.GDN_F32, 4)]:
         B, L, H, D = 2, 130, 3, (128 if act == gl.GDN_BF16 else 64)
         d, tok, Nc = H * D, B * L, (L + 63) // 64
@@ -145,8 +156,12 @@ def test_workspace_sizes():
         xb = up(tok * d * 2) if act == gl.GDN_BF16 else 0   # the bf16 loop operand
         exp = (3 * up(tok * H * D * eb) + 2 * up(tok * H * 4) + xb + chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats)
                + up(tok * P * 4) + (up(tok * P * 4) if act == gl.GDN_BF16 else 0) + up(P * Mp * 4) + up(d * Mp * eb) + up(d * P * eb) + 3 * up(tok * H * D * 4)
-               + 2 * up(tok * H * 4) + 2 * up(tok * d * 4) + up(d * P * 4 * (2 if act == gl.GDN_BF16 else 1))
-               + (up(4 * tok * d * 4) if act == gl.GDN_BF16 else 0) + up(((tok + 127) // 128) * d * 4))
+               + 2 * up(tok * H * 4) + 2 * up(tok * d * 4))
+        bf = act == gl.GDN_BF16
+        dws = split(-(-d // 384) * -(-P // 256), 3, 0.05) if bf else 1
+        dxs = split(-(-tok // 384) * -(-d // 256), 4, 0.025)
+        assert dxs == 4 and dws == (3 if bf else 1)   # the small shape splits both products
+        exp += up(d * P * 4 * dws) + (up(dxs * tok * d * 4) if bf and dxs > 1 else 0) + up(((tok + 31) // 32) * d * 4)
         assert _ws_status(gl.make_desc(B, L, H, D, D, act=act), gl.GDN_OP_LOOP_BACKWARD) == (0, exp)
     st, _ = _ws_status(gl.make_desc(B, L, H, 128, 128, act=gl.GDN_F32), gl.GDN_OP_LOOP_BACKWARD)
     assert st == -3
@@ -253,6 +268,7 @@ def test_timer_validation(lib):
     h = ctypes.c_void_p()
     assert lib.gdn_timer_create(12, 4, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(4, 4, ctypes.byref(h)) == -2   # not a stage
+    assert lib.gdn_timer_create(8, 4, ctypes.byref(h)) == -2   # not a stage
     assert lib.gdn_timer_create(0, 0, ctypes.byref(h)) == -2
     assert lib.gdn_timer_create(0, 4, None) == -1
     assert lib.gdn_timer_attach(None) == -1
