@@ -66,11 +66,16 @@ hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *W
 // row-major (A = strict_lower(Gam (.) K K^T), P = lower_incl(Gam (.) Q K^T),
 // both zero in the rows of tokens past the end of the sequence; T =
 // (I + diag(beta) A)^{-1}), the fp64 log-cumsum lg of alpha, gamma = e^lg and
-// c = e^(lg_last - lg) [64] fp32.
+// c = e^(lg_last - lg) [64] fp32; W^T = diag(beta) T^T diag(c) K [64][D] as
+// bf16 hi and lo planes, K^T and Q^T [D][64] bf16 (fp32 inputs: hi and lo
+// planes; zero for tokens past the end) and M^T = diag(beta) T^T P^T [64][64]
+// fp32 (zero in the columns of tokens past the end).
 struct PrepBwd {
     float *T, *P, *A;
     double *lg;
     float *gam, *c;
+    bf16 *Wth, *Wtl, *Kth, *Ktl, *Qth, *Qtl;
+    float *Mt;
 };
 // Chunk preparation: per (b, h, chunk) decay products, the UT-transform
 // inverse and the derived matrices W [D x 64], M [64 x 64], gamma [64]; with
@@ -202,10 +207,10 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
                              ChunkWs ws, const float *s_init, float *s_final, CarryOut out, hipStream_t s);
 
 // Backward of the chunkwise scan.  The forward preparation, given
-// bwd_prep_out(mats, B*H*Nc, D), forms per (b, h, chunk) T, P, A, the
-// log-cumsum of alpha, gamma and c in `mats` (bwd_mats_bytes for B*H*Nc chunks
-// of width D); launch_bwd_ops the reverse carry's operands from them and dO: W^T = diag(beta) T^T diag(c) K (split bf16), K^T, Q^T (bf16) and
-// M^T dO = diag(beta) T^T P^T dO (fp32).  The reverse carry walks the chunks of
+// bwd_prep_out(mats, B*H*Nc, D), forms per (b, h, chunk) the matrices of
+// PrepBwd in `mats` (bwd_mats_bytes for B*H*Nc chunks of width D), and
+// launch_bwd_ops M^T dO = diag(beta) T^T P^T dO (fp32) from M^T and dO.  The
+// reverse carry walks the chunks of
 // each (b, h, 16-column slice) backwards on MFMA: dE = M^T dO + W^T dS'
 // (written to dv), dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dE,
 // with each chunk's dS' kept in ds_end [B, H, Nc, D, D] and ds_init given the
@@ -214,8 +219,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
 // inputs need D = 64.
 size_t bwd_mats_bytes(int64_t chunks, int D);
 PrepBwd bwd_prep_out(float *mats, int64_t chunks, int D);
-hipError_t launch_bwd_ops(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
-                          const float *d_o, float *mats, hipStream_t s);
+hipError_t launch_bwd_ops(int B, int L, int H, int D, const float *d_o, float *mats, hipStream_t s);
 hipError_t launch_bwd_carry(bool f32, int B, int L, int H, int D, const float *d_o, const float *d_sfinal,
                             float *mats, float *dv, float *ds_end, float *ds_init, hipStream_t s);
 hipError_t launch_bwd_chunk(bool f32, int B, int L, int H, int D, const void *q, const void *k, const void *v,

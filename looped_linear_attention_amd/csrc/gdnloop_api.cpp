@@ -422,7 +422,7 @@ gdn_status gdn_scan_backward(const gdn_desc *desc, const void *q, const void *k,
     st = scan_chunks(desc, q, k, v, GateSrc{alpha, beta, nullptr, 0, desc->alpha_lo, nullptr, nullptr}, s_init,
                      nullptr, out, ws, lo, s, bm);
     if (st != GDN_OK) return st;
-    hipError_t e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, beta, d_o, bm, s); });
+    hipError_t e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(B, L, H, D, d_o, bm, s); });
     if (e != hipSuccess) return hip_fail(e, "backward carry operands launch");
     e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
         return launch_bwd_carry(f32, B, L, H, D, d_o, d_sfinal, bm, dv, dse, ds_init, s);
@@ -510,7 +510,7 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         st = scan_chunks(desc, q, k, v, GateSrc{al, be, zp, lo.P, desc->alpha_lo, zp ? al : nullptr, zp ? be : nullptr},
                          nullptr, nullptr, out, ws, lo, s, bm);
         if (st != GDN_OK) return st;
-        e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(f32, B, L, H, D, q, k, be, g_in, bm, s); });
+        e = timed(GDN_STAGE_BWD_OPS, s, [&] { return launch_bwd_ops(B, L, H, D, g_in, bm, s); });
         if (e != hipSuccess) return hip_fail(e, "backward carry operands launch");
         e = timed(GDN_STAGE_BWD_CARRY, s, [&] {
             return launch_bwd_carry(f32, B, L, H, D, g_in, nullptr, bm, gv, dse, nullptr, s);

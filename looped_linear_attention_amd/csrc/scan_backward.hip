@@ -50,17 +50,19 @@ constexpr int C = 64;
 // log-cumsum lg [64] (fp64), gamma = e^lg and c = e^(lg_last - lg) [64]; and
 // the operands of the reverse carry: W^T = diag(beta) T^T diag(c) K [64][D]
 // as bf16 hi and lo planes, K^T and Q^T [D][64] as bf16 hi (and, for fp32
-// inputs, lo) planes, and M^T dO = diag(beta) T^T P^T dO [64][D] fp32.
+// inputs, lo) planes, M^T dO = diag(beta) T^T P^T dO [64][D] fp32, and
+// M^T = diag(beta) T^T P^T [64][64] fp32.  The forward's chunk preparation
+// writes all but M^T dO (k_bwd_ops).
 struct BwdMats {
     float *T, *P, *A;
     double *lg;
     float *gam, *c;
     bf16 *Wth, *Wtl, *Kth, *Ktl, *Qth, *Qtl;
-    float *MtdO;
+    float *MtdO, *Mt;
 };
 // bytes per chunk
 __host__ __device__ constexpr size_t bwd_mats_per_chunk(int D) {
-    return 3 * C * C * 4 + C * 8 + 2 * C * 4 + (size_t)6 * D * C * 2 + (size_t)C * D * 4;
+    return 4 * C * C * 4 + C * 8 + 2 * C * 4 + (size_t)6 * D * C * 2 + (size_t)C * D * 4;
 }
 // The regions of a BwdMats block for `chunks` chunks, each array for all chunks in turn.
 BwdMats bwd_mats(float *base, int64_t chunks, int D) {
@@ -80,100 +82,71 @@ BwdMats bwd_mats(float *base, int64_t chunks, int D) {
     m.Qth = b + 4 * plane;
     m.Qtl = b + 5 * plane;
     m.MtdO = reinterpret_cast<float *>(b + 6 * plane);
+    m.Mt = m.MtdO + chunks * C * D;
     return m;
 }
 
 // ---------------------------------------------------------------------------
-// carry operands: one workgroup per (b, h, chunk), in 32-column blocks
+// M^T dO: one workgroup (4 waves) per (b, h, chunk)
 // ---------------------------------------------------------------------------
-// W^T[m][i] = beta_m sum_{r >= m} T[r][m] c_r K[r][i], (P^T dO)[m][i] =
-// sum_{r >= m} P[r][m] dO[r][i], M^T dO[m][i] = beta_m sum_{r >= m} T[r][m]
-// (P^T dO)[r][i]; K^T and Q^T copied transposed.  Rows past the end of the
-// sequence are zero (beta = 0 there).
+// (M^T dO)[m][i] = sum_r M^T[m][r] dO[r][i] on 16x16x32 MFMA, both operands
+// fp32 split into bf16 hi + lo (3 passes).  dO is staged transposed ([i][r])
+// in LDS as the two bf16 planes; wave w forms output rows 16 w .. 16 w + 15.
+// Rows of dO past the end of the sequence are zero.
 constexpr int BO_THREADS = 256;
 
-template <int D, typename TIn>
-__global__ __launch_bounds__(BO_THREADS) void k_bwd_ops(const TIn *__restrict__ q, const TIn *__restrict__ k,
-                                                        const float *__restrict__ beta, const float *__restrict__ d_o,
-                                                        int L, int H, int Nc, BwdMats bm) {
-    constexpr bool SPLIT_KQ = sizeof(TIn) == 4;
-    __shared__ float Ts[C][C + 1], Ps[C][C + 1];
-    __shared__ float Kc[C][33], Kr[C][33], Qr[C][33], dOb[C][33], PdO[C][33];
-    __shared__ float bes[C];
-    const int t = threadIdx.x;
+template <int D>
+__global__ __launch_bounds__(BO_THREADS) void k_bwd_ops(const float *__restrict__ d_o, int L, int H, int Nc,
+                                                        BwdMats bm) {
+    constexpr int TL = C + 8;   // row stride (bf16) of the transposed planes: 16-byte aligned rows
+    __shared__ __attribute__((aligned(16))) bf16 dOh[D * TL], dOl[D * TL];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 15, lg = lane >> 4;
     const int h = blockIdx.x % H, chunk = blockIdx.x / H, b = blockIdx.y;
     const int c0 = chunk * C, nvalid = min(C, L - c0);
     const int64_t tok0 = (int64_t)b * L + c0;
     const int64_t cid = ((int64_t)b * H + h) * Nc + chunk;
-    for (int n = t; n < C * C; n += BO_THREADS) {
-        Ts[n / C][n % C] = bm.T[cid * C * C + n];
-        Ps[n / C][n % C] = bm.P[cid * C * C + n];
+    // token rows 2 rp, 2 rp + 1 and columns 4 q4 .. 4 q4 + 3 per item: one 4-byte LDS write per column and plane
+    for (int n = t; n < (C / 2) * (D / 4); n += BO_THREADS) {
+        const int rp = n / (D / 4), i4 = 4 * (n % (D / 4)), r = 2 * rp;
+        float4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+        if (r < nvalid) v0 = *reinterpret_cast<const float4 *>(d_o + ((tok0 + r) * H + h) * D + i4);
+        if (r + 1 < nvalid) v1 = *reinterpret_cast<const float4 *>(d_o + ((tok0 + r + 1) * H + h) * D + i4);
+        const float x[8] = {v0.x, v1.x, v0.y, v1.y, v0.z, v1.z, v0.w, v1.w};
+        bf16 hh[8], ll[8];
+        split_bf16<8>(x, hh, ll);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16 ph[2] = {hh[2 * e], hh[2 * e + 1]}, pl2[2] = {ll[2 * e], ll[2 * e + 1]};
+            __builtin_memcpy(dOh + (i4 + e) * TL + r, ph, 4);
+            __builtin_memcpy(dOl + (i4 + e) * TL + r, pl2, 4);
+        }
     }
-    if (t < C) bes[t] = t < nvalid ? beta[(tok0 + t) * H + h] : 0.f;
-    const int m = t >> 2, i8 = (t & 3) * 8;   // this thread's row and 8 columns of a block
-    for (int cb = 0; cb < D; cb += 32) {
-        __syncthreads();   // the previous block's readers are done
-        for (int n = t; n < C * 32; n += BO_THREADS) {
-            const int r = n >> 5, i = n & 31;
-            const bool ok = r < nvalid;
-            const int64_t off = ((tok0 + (ok ? r : 0)) * H + h) * D + cb + i;
-            const float kv = ok ? to_f32(k[off]) : 0.f;
-            Kr[r][i] = kv;
-            Kc[r][i] = kv * bm.c[cid * C + r];
-            Qr[r][i] = ok ? to_f32(q[off]) : 0.f;
-            dOb[r][i] = ok ? d_o[off] : 0.f;
-        }
-        __syncthreads();
-        float w[8] = {}, pd[8] = {};
-        for (int r = m; r < C; ++r) {
-            const float tr = Ts[r][m], pr = Ps[r][m];
+    // A fragments: M^T row 16 wave + lr, k = r = 32 s + 8 lg ..
+    bf16x8 ah[2], al[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                w[e] = fmaf(tr, Kc[r][i8 + e], w[e]);
-                pd[e] = fmaf(pr, dOb[r][i8 + e], pd[e]);
-            }
-        }
-        const float bm_ = bes[m];
-        {
-            float wv[8];
-            bf16 hi[8], lo[8];
+    for (int s = 0; s < 2; ++s) {
+        const float4 *src = reinterpret_cast<const float4 *>(bm.Mt + (cid * C + 16 * wave + lr) * C + 32 * s + 8 * lg);
+        const float4 a = src[0], c = src[1];
+        const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        bf16 hh[8], ll[8];
+        split_bf16<8>(x, hh, ll);
+        ah[s] = pack8(hh);
+        al[s] = pack8(ll);
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int ct = 0; ct < D / 16; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                wv[e] = bm_ * w[e];
-                PdO[m][i8 + e] = pd[e];
-            }
-            split_bf16<8>(wv, hi, lo);
-            const int64_t o = (cid * C + m) * D + cb + i8;
-            *reinterpret_cast<bf16x8 *>(bm.Wth + o) = pack8(hi);
-            *reinterpret_cast<bf16x8 *>(bm.Wtl + o) = pack8(lo);
+        for (int s = 0; s < 2; ++s) {
+            const int o = (16 * ct + lr) * TL + 32 * s + 8 * lg;
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(dOh + o), bl = *reinterpret_cast<const bf16x8 *>(dOl + o);
+            acc = mfma16x16x32(ah[s], bh, acc);
+            acc = mfma16x16x32(ah[s], bl, acc);
+            acc = mfma16x16x32(al[s], bh, acc);
         }
-        // K^T, Q^T of the block: [i][m]
-        for (int n = t; n < 32 * C; n += BO_THREADS) {
-            const int i = n >> 6, r = n & 63;
-            const int64_t o = (cid * D + cb + i) * C + r;
-            if constexpr (SPLIT_KQ) {
-                const float kv[2] = {Kr[r][i], Qr[r][i]};
-                bf16 hi[2], lo[2];
-                split_bf16<2>(kv, hi, lo);
-                bm.Kth[o] = hi[0];
-                bm.Ktl[o] = lo[0];
-                bm.Qth[o] = hi[1];
-                bm.Qtl[o] = lo[1];
-            } else {
-                bm.Kth[o] = (bf16)Kr[r][i];
-                bm.Qth[o] = (bf16)Qr[r][i];
-            }
-        }
-        __syncthreads();
-        float mo[8] = {};
-        for (int r = m; r < C; ++r) {
-            const float tr = Ts[r][m];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mo[e] = fmaf(tr, PdO[r][i8 + e], mo[e]);
-        }
-        float4 *dst = reinterpret_cast<float4 *>(bm.MtdO + (cid * C + m) * D + cb + i8);
-        dst[0] = float4{bm_ * mo[0], bm_ * mo[1], bm_ * mo[2], bm_ * mo[3]};
-        dst[1] = float4{bm_ * mo[4], bm_ * mo[5], bm_ * mo[6], bm_ * mo[7]};
+        for (int j = 0; j < 4; ++j) bm.MtdO[(cid * C + 16 * wave + 4 * lg + j) * D + 16 * ct + lr] = acc[j];
     }
 }
 
@@ -858,21 +831,16 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
 
 PrepBwd bwd_prep_out(float *mats, int64_t chunks, int D) {
     const BwdMats bm = bwd_mats(mats, chunks, D);
-    return PrepBwd{bm.T, bm.P, bm.A, bm.lg, bm.gam, bm.c};
+    return PrepBwd{bm.T, bm.P, bm.A, bm.lg, bm.gam, bm.c, bm.Wth, bm.Wtl, bm.Kth, bm.Ktl, bm.Qth, bm.Qtl, bm.Mt};
 }
 
-hipError_t launch_bwd_ops(bool f32, int B, int L, int H, int D, const void *q, const void *k, const float *beta,
-                          const float *d_o, float *mats, hipStream_t s) {
+hipError_t launch_bwd_ops(int B, int L, int H, int D, const float *d_o, float *mats, hipStream_t s) {
     const int Nc = (L + C - 1) / C;
     const dim3 grid((unsigned)(Nc * H), B);
     const BwdMats bm = bwd_mats(mats, (int64_t)B * H * Nc, D);
-#define BO(DD, T) launch_kernel((k_bwd_ops<DD, T>), grid, dim3(BO_THREADS), 0, s, (const T *)q, (const T *)k, beta, d_o, L, H, Nc, bm)
-    if (f32) {
-        if (D == 64) BO(64, float); else return hipErrorInvalidValue;
-    } else {
-        if (D == 128) BO(128, bf16); else BO(64, bf16);
-    }
-#undef BO
+    if (D == 128) launch_kernel(k_bwd_ops<128>, grid, dim3(BO_THREADS), 0, s, d_o, L, H, Nc, bm);
+    else if (D == 64) launch_kernel(k_bwd_ops<64>, grid, dim3(BO_THREADS), 0, s, d_o, L, H, Nc, bm);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

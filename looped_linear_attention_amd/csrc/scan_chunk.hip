@@ -159,8 +159,9 @@ __device__ __forceinline__ f32x4 mma4s(const float (&a)[4], const float (&b)[4],
 }
 
 // With BWO it also writes the chunk matrices that the backward pass takes (A,
-// P, T, the log-cumsum, gamma and c, fp32 row-major; A and P zero in the rows
-// of tokens past the end).
+// P, T, M^T fp32 row-major, the log-cumsum, gamma and c; A and P zero in the
+// rows, M^T in the columns of tokens past the end; W^T as bf16 hi and lo
+// planes; K^T and Q^T from the LDS tiles, zero past the end).
 template <int D, typename TIn, bool GP, bool BWO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_prep(const TIn *__restrict__ q,
                                                    const TIn *__restrict__ k,
@@ -274,6 +275,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
     wait_vmcnt<0>();   // this wave's direct loads of the K and Q tiles landed
     __syncthreads();   // ... and the other waves'.
+    if constexpr (BWO) {   // K^T, Q^T [D][64]: 8 consecutive tokens of one column per item
+        for (int u = t; u < D * (C / 8); u += 256) {
+            const int i = u / (C / 8), r0 = 8 * (u % (C / 8));
+            float kv[8], qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool ok = r0 + e <= last;
+                kv[e] = ok ? tile_elem<D, TIn>(Ks, r0 + e, i) : 0.f;
+                qv[e] = ok ? tile_elem<D, TIn>(Qs, r0 + e, i) : 0.f;
+            }
+            const int64_t o = (cid * D + i) * C + r0;
+            __bf16 kh[8], kl[8], qh[8], ql[8];
+            split_bf16(kv, kh, kl);
+            split_bf16(qv, qh, ql);
+            *reinterpret_cast<bf16x8 *>(bo.Kth + o) = pack8(kh);
+            *reinterpret_cast<bf16x8 *>(bo.Qth + o) = pack8(qh);
+            if constexpr (F32) {
+                *reinterpret_cast<bf16x8 *>(bo.Ktl + o) = pack8(kl);
+                *reinterpret_cast<bf16x8 *>(bo.Qtl + o) = pack8(ql);
+            }
+        }
+    }
 
     // (2) N = diag(beta) strict_lower(Gam (.) K K^T) for this wave's 16 rows;
     // P^T tiles (m-tile mt, r-tile wave) = Gam (.) K Q^T, m <= r, in registers
@@ -524,6 +547,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         for (int tt = 0; tt < NT; ++tt)
             store_pair(aw_acc[tt], dW + ((((int64_t)(wave * NT + tt) * 2 + s2) * 2) * 64 + lane) * 8);
         store_pair(am_acc, dM + ((((int64_t)wave * 2 + s2) * 2) * 64 + lane) * 8);
+        if constexpr (BWO) {
+            // W^T[c][i] and M^T[c][r] at rows c = 16 (2 s2 + h2) + 4 lg + j of the accumulator tiles
+            const int rr = 16 * wave + lr;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 16 * (2 * s2 + h2) + 4 * lg + j;
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const int i = RW * wave + 4 * NT * (lr >> 2) + 4 * tt + (lr & 3);
+                        const float x[2] = {aw_acc[tt][h2][j], 0.f};
+                        __bf16 xh[2], xl[2];
+                        split_bf16(x, xh, xl);
+                        bo.Wth[(cid * C + c) * D + i] = xh[0];
+                        bo.Wtl[(cid * C + c) * D + i] = xl[0];
+                    }
+                    bo.Mt[(cid * C + c) * C + rr] = rr <= last ? am_acc[h2][j] : 0.f;
+                }
+        }
     }
     // (9) gamma
     if (t < C) wsg[cid * C + t] = __expf((float)lgs[t]);

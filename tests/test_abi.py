@@ -124,9 +124,9 @@ def test_workspace_sizes():
     B, L, H, D = 2, 130, 3, 128
     Nc = (L + 63) // 64
     chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
-    # fp32 T, P, A; fp64 log-cumsum; gamma, c; the reverse carry's W^T (hi, lo), K^T, Q^T (hi, lo) bf16 planes
+    # fp32 T, P, A, M^T; fp64 log-cumsum; gamma, c; the reverse carry's W^T (hi, lo), K^T, Q^T (hi, lo) bf16 planes
     # [D][64] and M^T dO [64][D] fp32
-    mats = B * H * Nc * (3 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4 + 6 * D * 64 * 2 + 64 * D * 4)
+    mats = B * H * Nc * (4 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4 + 6 * D * 64 * 2 + 64 * D * 4)
     assert _ws_status(gl.make_desc(B, L, H, D, D), gl.GDN_OP_SCAN_BACKWARD) == (
         0, chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats))
     st, _ = _ws_status(gl.make_desc(B, L, H, D, D, act=gl.GDN_F32), gl.GDN_OP_SCAN_BACKWARD)
@@ -152,7 +152,7 @@ def test_workspace_sizes():
         P = (H * 3 * D + 127) // 128 * 128 + 128
         Mp = (tok + 63) // 64 * 64
         chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
-        mats = B * H * Nc * (3 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4 + 6 * D * 64 * 2 + 64 * D * 4)
+        mats = B * H * Nc * (4 * 64 * 64 * 4 + 64 * 8 + 2 * 64 * 4 + 6 * D * 64 * 2 + 64 * D * 4)
         xb = up(tok * d * 2) if act == gl.GDN_BF16 else 0   # the bf16 loop operand
         exp = (3 * up(tok * H * D * eb) + 2 * up(tok * H * 4) + xb + chunks + 2 * up(B * H * Nc * D * D * 4) + up(mats)
                + up(tok * P * 4) + (up(tok * P * 4) if act == gl.GDN_BF16 else 0) + up(P * Mp * 4) + up(d * Mp * eb) + up(d * P * eb) + 3 * up(tok * H * D * 4)
