@@ -23,8 +23,9 @@ __global__ __launch_bounds__(256) void k_act_init(float *R, int *halt, int M) {
 }
 
 // One wave per position: the dot product over d channels in a fixed order
-// (lane-strided partial sums, then a butterfly), so the decision is
-// deterministic.  Waves with no position return at once (no barriers here).
+// (each lane sums its 16-byte groups 4 l, 4 l + 256, ..., then a butterfly),
+// so the decision is deterministic.  d is a multiple of 4.  Waves with no
+// position return at once (no barriers here).
 __global__ __launch_bounds__(256) void k_act_halt(const float *__restrict__ h, const float *__restrict__ w, float b,
                                                   float thr, int d, int M, int tau, int T, float *__restrict__ R,
                                                   int *__restrict__ halt, int *__restrict__ halt_out,
@@ -34,7 +35,13 @@ __global__ __launch_bounds__(256) void k_act_halt(const float *__restrict__ h, c
     if (t >= M) return;
     const float *ht = h + t * d;
     float acc = 0.f;
-    for (int i = lane; i < d; i += 64) acc = fmaf(ht[i], w[i], acc);
+    for (int i = 4 * lane; i < d; i += 256) {
+        const float4 x = *reinterpret_cast<const float4 *>(ht + i), y = *reinterpret_cast<const float4 *>(w + i);
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        acc = fmaf(x.w, y.w, acc);
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (lane == 0) {
@@ -56,34 +63,39 @@ __global__ __launch_bounds__(256) void k_act_halt(const float *__restrict__ h, c
     }
 }
 
-// One workgroup: each thread takes a contiguous run of positions, counts the
-// ones that ran loop tau, and after a workgroup prefix sum of the counts writes
-// their indices in ascending order.
+// One workgroup of 16 waves: wave w takes a contiguous range of positions in
+// steps of 64 (one position per lane), counts the ones that ran loop tau with
+// ballots, and after an exclusive sum of the 16 counts writes their indices
+// in ascending order.
 __global__ __launch_bounds__(1024) void k_act_rows(const int *__restrict__ halt, int tau, int M,
                                                    int *__restrict__ rows, int *__restrict__ count) {
-    __shared__ int part[1024];
-    const int t = threadIdx.x;
-    const int64_t per = ((int64_t)M + 1023) / 1024;
-    const int64_t lo = min((int64_t)M, t * per), hi = min((int64_t)M, lo + per);
+    __shared__ int wsum[16];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int per = ((M + 15) / 16 + 63) / 64 * 64;
+    const int lo = min(M, wave * per), hi = min(M, lo + per);
+    auto ran = [&](int i) {
+        if (i >= hi) return false;
+        const int hv = halt[i];
+        return hv == 0 || hv == tau;
+    };
     int c = 0;
-    for (int64_t i = lo; i < hi; ++i) {
-        const int hv = halt[i];
-        c += (hv == 0 || hv == tau) ? 1 : 0;
-    }
-    part[t] = c;
+    for (int i0 = lo; i0 < hi; i0 += 64) c += __popcll(__ballot(ran(i0 + lane)));
+    if (lane == 0) wsum[wave] = c;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan, Hillis-Steele
-        const int y = t >= off ? part[t - off] : 0;
-        __syncthreads();
-        part[t] += y;
-        __syncthreads();
+    int o = 0;
+    for (int u = 0; u < wave; ++u) o += wsum[u];
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int i0 = lo; i0 < hi; i0 += 64) {
+        const bool r = ran(i0 + lane);
+        const unsigned long long m = __ballot(r);
+        if (r) rows[o + __popcll(m & below)] = i0 + lane;
+        o += __popcll(m);
     }
-    int o = part[t] - c;
-    for (int64_t i = lo; i < hi; ++i) {
-        const int hv = halt[i];
-        if (hv == 0 || hv == tau) rows[o++] = (int)i;
+    if (t == 0) {
+        int tot = 0;
+        for (int u = 0; u < 16; ++u) tot += wsum[u];
+        *count = tot;
     }
-    if (t == 1023) *count = part[1023];
 }
 
 }  // namespace
@@ -100,6 +112,7 @@ hipError_t launch_act_init(int M, float *R, int *halt, hipStream_t s) {
 
 hipError_t launch_act_halt(int M, int d, const float *h, const float *w, float b, float thr, int tau, int T, float *R,
                            int *halt, int *halt_out, float *ponder_out, hipStream_t s) {
+    if (d % 4) return hipErrorInvalidValue;
     launch_kernel(k_act_halt, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, h, w, b, thr, d, M, tau, T, R, halt,
                   halt_out, ponder_out);
     return hipGetLastError();

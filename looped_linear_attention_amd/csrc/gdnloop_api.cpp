@@ -874,8 +874,9 @@ static gdn_status loop_prefill_impl(const gdn_desc *desc, const void *h0, const 
         e = project(f32, M, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo, desc->norm_eps, zp, s,
                     compact ? act->rows : nullptr, compact ? act->rows_count : nullptr);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
+        // (no position has halted before the first loop's decision)
         CarryOut out{nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, hdst, (!f32 && !last) ? xbuf : nullptr,
-                     nullptr, act ? act->halt : nullptr};
+                     nullptr, (act && tau > 0) ? act->halt : nullptr};
         // with gate partials the prep forms alpha and beta and stores them in the
         // workspace's gate regions, where gdn_loop_prefill documents them
         gdn_status st = scan_chunks(desc, q, k, v,

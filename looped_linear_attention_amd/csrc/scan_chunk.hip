@@ -840,6 +840,7 @@ constexpr int PF_AHEAD = 3;
 // h_prev at the lane's 4 (token, column) cells of one output step
 struct OutIn {
     float hp[4];
+    int hf[4];   // halted flags of the rows (0 without halting)
 };
 
 template <int D, typename TIn, int RES, bool XN>
@@ -931,6 +932,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 in.hp[j] = 0.f;
+                in.hf[j] = halted ? halted[tokb + c0 + min(16 * ot + 4 * lg + j, last)] : 0;
                 if constexpr (RES != 0) {
                     const int64_t off = (tokb + c0 + min(16 * ot + 4 * lg + j, last)) * (int64_t)d + (int64_t)h * D + col;
                     if constexpr (RES == 2) in.hp[j] = (float)static_cast<const bf16 *>(h_prev)[off];
@@ -976,7 +978,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 if (c0 + r >= L) continue;
                 const float ov = gv[j] * qs[j] + me[j];
                 const int64_t row = tokb + c0 + r;
-                if (halted && halted[row] != 0) continue;   // a halted position keeps its state
+                if (in.hf[j] != 0) continue;   // a halted position keeps its state
                 if constexpr (RES == 0) {
                     if (o) o[(row * H + h) * D + col] = ov;
                 } else {
@@ -1473,9 +1475,13 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) rho_c[ct] = RES ? rho[h * D + col0 + 16 * ct + lr] : 0.f;
     float hp[2][4];
-    // h_prev of chunk cc (rows past the end of the sequence read the last row; never stored)
+    int hf[4];   // halted flags of the rows (0 without halting)
+    // h_prev of chunk cc and the rows' halted flags (rows past the end of the
+    // sequence read the last row; never stored)
     auto load_hp = [&](int cc) __attribute__((always_inline)) {
         const int c0 = cc * C, last = L - 1 - c0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hf[j] = halted ? halted[tokb + c0 + min(16 * ot + 4 * lg + j, last)] : 0;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -1578,7 +1584,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
                 if (c0 + r >= L) continue;
                 const float ov = gv[j] * qs[j] + mev[j];
                 const int64_t row = tokb + c0 + r;
-                if (halted && halted[row] != 0) continue;   // a halted position keeps its state
+                if (hf[j] != 0) continue;   // a halted position keeps its state
                 if constexpr (RES == 0) {
                     if (o) o[(row * H + h) * D + col] = ov;
                 } else {
