@@ -144,7 +144,7 @@ __device__ __forceinline__ int swz(int r, int ch) { return r * BK_BF + ((ch ^ sw
 // B tile (1024 chunks, same rule).  LDS chunk p holds row p / 8, logical chunk
 // (p % 8) ^ swz_key(row).  Only the first NA of the A loads are issued: with at
 // most 64 tokens (NA = 2) the rows they skip are all past M.
-template <int I0, int I1, int NA>
+template <int I0, int I1, int NA, int AE = A_ELEMS>
 __device__ __forceinline__ void gemm_issue(bf16 *stage, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int m0,
                                            int n0, int M, int K, int b_rows, int k0) {
@@ -162,7 +162,7 @@ __device__ __forceinline__ void gemm_issue(bf16 *stage, const bf16 *__restrict__
             const int r = p >> 3, ch = (p & 7) ^ swz_key(r);
             const int rr = min(r, b_rows - 1);   // gate tile: unused rows repeat a used one
             __builtin_amdgcn_global_load_lds(Wp + (int64_t)(n0 + rr) * K + k0 + ch * 8,
-                                             (lds_void *)(stage + A_ELEMS + base * 8), 16, 0, 0);
+                                             (lds_void *)(stage + AE + base * 8), 16, 0, 0);
         }
     }
 }
@@ -172,73 +172,97 @@ struct KFrags {
     bf16x8 a[BK_BF / 16][4], b[BK_BF / 16][2];
 };
 
+// AE: bf16 elements of the stage's A area; TMR: A tiles read (the A area of
+// AE = 64 x 64 holds rows 0 .. 63 only, read by every wave).
+template <int AE = A_ELEMS, int TMR = 4>
 __device__ __forceinline__ void read_frags_step(KFrags &F, const bf16 *stage, int s, int lane, int wm, int wn) {
-    const bf16 *Ab = stage, *Bb = stage + A_ELEMS;
+    const bf16 *Ab = stage, *Bb = stage + AE;
     const int ch = 2 * s + (lane >> 5);
+    const int wrow = AE == A_ELEMS ? wm * 128 : 0;
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
-        F.a[s][tm] = *reinterpret_cast<const bf16x8 *>(Ab + swz(wm * 128 + tm * 32 + (lane & 31), ch));
+    for (int tm = 0; tm < TMR; ++tm)
+        F.a[s][tm] = *reinterpret_cast<const bf16x8 *>(Ab + swz(wrow + tm * 32 + (lane & 31), ch));
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn)
         F.b[s][tn] = *reinterpret_cast<const bf16x8 *>(Bb + swz(wn * 64 + tn * 32 + (lane & 31), ch));
 }
 
-// The k-loop of one tile, software-pipelined over three LDS stages and two
+// The k-loop of one tile, software-pipelined over NST LDS stages and two
 // fragment register sets.  Iteration kb: wait until k-block kb+1 has landed
-// (kb+2's loads may stay in flight), barrier, then per k-step: issue a quarter
-// of k-block kb+3's direct loads (into the stage that held kb, whose fragments
-// were read during the previous iteration), read k-block kb+1's fragments into
-// the idle register set, and run k-block kb's MFMAs from the other set.  The
-// direct loads go out in small groups between MFMAs so that issuing them never
-// fills the memory pipeline's queue, which would stall the wave's MFMA issue.
-// Past the end the loads re-read the last k-block into a free stage, so every
-// iteration has the same shape.  GATE: only the 32-column MFMA tiles holding
-// used gate columns are computed (a wave-uniform condition).  NA < 8: only the
-// tile's first 32 NA token rows can be valid; the other A rows are neither loaded
-// nor multiplied (their outputs are never stored), and the wait counts follow
-// the NA + 4 loads per k-block.
+// (kb+2 .. kb+NST-1 may stay in flight), barrier, then per k-step: issue a
+// quarter of k-block kb+NST's direct loads (into the stage that held kb, whose
+// fragments were read during the previous iteration), read k-block kb+1's
+// fragments into the idle register set, and run k-block kb's MFMAs from the
+// other set.  The direct loads go out in small groups between MFMAs so that
+// issuing them never fills the memory pipeline's queue, which would stall the
+// wave's MFMA issue.  Past the end the loads re-read the last k-block into a
+// free stage, so every iteration has the same shape.  GATE: only the 32-column
+// MFMA tiles holding used gate columns are computed (a wave-uniform
+// condition).  NA < 8: only the tile's first 32 NA token rows can be valid; the
+// other A rows are neither loaded nor multiplied (their outputs are never
+// stored), and the wait counts follow the NA + 4 loads per k-block.  With
+// NA = 2 (at most 64 tokens) a stage holds only those 64 A rows and the B
+// tile (24 KB), so six stages fit where three full ones did: five k-blocks
+// in flight instead of two, for a tile that streams its weights with little
+// arithmetic per byte.
+template <int NA> struct KloopCfg {
+    static constexpr int AE = NA == 2 ? 64 * BK_BF : A_ELEMS;   // bf16 elements of a stage's A area
+    static constexpr int SE = AE + B_ELEMS;                       // bf16 elements per stage
+    static constexpr int NST = NA == 2 ? 6 : STAGES;
+};
+static_assert(KloopCfg<2>::NST * KloopCfg<2>::SE <= STAGES * STAGE_ELEMS, "the NA = 2 stages fit the LDS");
 template <bool GATE, int NA>
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int wm,
                                            int wn, int m0, int n0, int M, int K, int b_rows,
                                            int gate_cols) {
+    using CF = KloopCfg<NA>;
+    constexpr int NST = CF::NST, SE = CF::SE, AE = CF::AE;
     const int nkb = K / BK_BF;   // >= 1
     auto kblock = [&](int kb) { return min(kb, nkb - 1) * BK_BF; };
     constexpr int NL = NA + 4;          // direct loads per k-block
+    static_assert((NST - 1) * NL < 64, "the vector-memory counter holds 0..63");
     // 32-row A tiles a wave multiplies: each A load covers 8 rows in each of the
     // 4 waves, so NA loads cover the rows of NA tiles
     constexpr int TM = NA >= 8 ? 4 : NA;
-    static_assert(NA == 8 || NA <= 4, "NA < 8 covers rows of the first wave row (128 rows) only");
-    const bool rows_on = NA >= 8 || wm == 0;
-    gemm_issue<0, 12, NA>(stages, x, Wp, lane, wave, m0, n0, M, K, b_rows, 0);
-    gemm_issue<0, 12, NA>(stages + STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(1));
-    gemm_issue<0, 12, NA>(stages + 2 * STAGE_ELEMS, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(2));
-    wait_vmcnt<2 * NL>();   // k-block 0 landed
+    static_assert(NA == 8 || NA == 2, "NA < 8 covers rows 0 .. 63 of the tile only");
+    // NA = 2: the 64 rows are one row of waves' work, so the two rows of waves
+    // split each k-block instead: waves wm take its k-steps 2 wm and 2 wm + 1
+    // (partial sums added in the epilogue)
+    const bool rows_on = true;
+    auto mine = [&](int s) { return NA >= 8 || (s >> 1) == wm; };
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+        gemm_issue<0, 12, NA, AE>(stages + st * SE, x, Wp, lane, wave, m0, n0, M, K, b_rows, kblock(st));
+    wait_vmcnt<(NST - 1) * NL>();   // k-block 0 landed
     lds_barrier();
     const bool tn_on[2] = {!GATE || wn * 64 < gate_cols, !GATE || wn * 64 + 32 < gate_cols};
     KFrags f0, f1;
 #pragma unroll
-    for (int s = 0; s < BK_BF / 16; ++s) read_frags_step(f0, stages, s, lane, wm, wn);
+    for (int s = 0; s < BK_BF / 16; ++s)
+        if (mine(s)) read_frags_step<AE, TM>(f0, stages, s, lane, wm, wn);
 
     auto step = [&](int kb, const KFrags &cur, KFrags &nxt) __attribute__((always_inline)) {
-        wait_vmcnt<NL>();   // k-block kb+1 landed (kb+2's NL loads may remain)
+        wait_vmcnt<(NST - 2) * NL>();   // k-block kb+1 landed (kb+2 .. kb+NST-1 may remain)
         lds_barrier();      // ... for every wave; every wave has read k-block kb's fragments
-        bf16 *ld_stage = stages + (kb % STAGES) * STAGE_ELEMS;           // receives kb+3
-        const bf16 *rd_stage = stages + ((kb + 1) % STAGES) * STAGE_ELEMS;
-        const int k3 = kblock(kb + 3);
+        bf16 *ld_stage = stages + (kb % NST) * SE;           // receives kb+NST
+        const bf16 *rd_stage = stages + ((kb + 1) % NST) * SE;
+        const int kn = kblock(kb + NST);
 #pragma unroll
         for (int s = 0; s < BK_BF / 16; ++s) {
-            if (s == 0) gemm_issue<0, 3, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            if (s == 1) gemm_issue<3, 6, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            if (s == 2) gemm_issue<6, 9, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            if (s == 3) gemm_issue<9, 12, NA>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, k3);
-            read_frags_step(nxt, rd_stage, s, lane, wm, wn);
+            if (s == 0) gemm_issue<0, 3, NA, AE>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, kn);
+            if (s == 1) gemm_issue<3, 6, NA, AE>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, kn);
+            if (s == 2) gemm_issue<6, 9, NA, AE>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, kn);
+            if (s == 3) gemm_issue<9, 12, NA, AE>(ld_stage, x, Wp, lane, wave, m0, n0, M, K, b_rows, kn);
+            if (mine(s)) {
+                read_frags_step<AE, TM>(nxt, rd_stage, s, lane, wm, wn);
 #pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
-                if (tn_on[tn] && rows_on)
+                for (int tn = 0; tn < 2; ++tn)
+                    if (tn_on[tn] && rows_on)
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
-                        acc[tm][tn] = mfma32x32x16(cur.a[s][tm], cur.b[s][tn], acc[tm][tn]);
+                        for (int tm = 0; tm < TM; ++tm)
+                            acc[tm][tn] = mfma32x32x16(cur.a[s][tm], cur.b[s][tn], acc[tm][tn]);
+            }
         }
     };
     for (int kb = 0; kb < nkb; kb += 2) {
@@ -289,6 +313,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // epilogue in two 128-row halves through an fp32 tile in LDS (reuses the operand buffers)
     float *Cs = reinterpret_cast<float *>(smem);
     float *red = Cs + 128 * CS_LD;
+    if constexpr (NA == 2) {
+        // rows 0 .. 63: the k-step halves of the two rows of waves, added in the order wm = 0, 1; rows
+        // 64 .. 127 (never stored) zero
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if (wm == pass) {
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            if (pass == 1 && tm >= 2) continue;
+                            const int r = tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            const int c = wn * 64 + tn * 32 + (lane & 31);
+                            const float a = tm < 2 ? acc[tm][tn][e] : 0.f;
+                            Cs[r * CS_LD + c] = pass ? Cs[r * CS_LD + c] + a : a;
+                        }
+            }
+            __syncthreads();
+        }
+        proj_epilogue<D, 128, bf16>(Cs, red, m0, n0, M, H, q, k, v, alpha, beta, alpha_lo, eps);
+        return;
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         if (m0 + half * 128 >= M) break;   // no valid row in this half (uniform)
