@@ -838,12 +838,17 @@ constexpr int CARRY_THREADS = 576;
 constexpr int PF_AHEAD = 3;
 
 // h_prev at the lane's 4 (token, column) cells of one output step
+enum CarryExtra : int { XM_NONE = 0, XM_STATES = 1, XM_HALT = 2 };
+
 struct OutIn {
     float hp[4];
-    int hf[4];   // halted flags of the rows (0 without halting)
+    int hf[4];   // halted flags of the rows (XM_HALT)
 };
 
-template <int D, typename TIn, int RES, bool XN>
+// XM: what the carry does besides the scan: XM_NONE, XM_STATES (store each
+// chunk's start state for the backward pass) or XM_HALT (skip the outputs of
+// halted rows); each is compiled in only where it is used.
+template <int D, typename TIn, int RES, bool XN, int XM>
 __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc,
     const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
@@ -932,7 +937,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 in.hp[j] = 0.f;
-                in.hf[j] = halted ? halted[tokb + c0 + min(16 * ot + 4 * lg + j, last)] : 0;
+                if constexpr (XM == XM_HALT) in.hf[j] = halted[tokb + c0 + min(16 * ot + 4 * lg + j, last)];
                 if constexpr (RES != 0) {
                     const int64_t off = (tokb + c0 + min(16 * ot + 4 * lg + j, last)) * (int64_t)d + (int64_t)h * D + col;
                     if constexpr (RES == 2) in.hp[j] = (float)static_cast<const bf16 *>(h_prev)[off];
@@ -978,7 +983,8 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
                 if (c0 + r >= L) continue;
                 const float ov = gv[j] * qs[j] + me[j];
                 const int64_t row = tokb + c0 + r;
-                if (in.hf[j] != 0) continue;   // a halted position keeps its state
+                if constexpr (XM == XM_HALT)
+                    if (in.hf[j] != 0) continue;   // a halted position keeps its state
                 if constexpr (RES == 0) {
                     if (o) o[(row * H + h) * D + col] = ov;
                 } else {
@@ -1075,7 +1081,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
         const float *g_cur = ST == 0 ? g0_s : g1_s;
         const bf16x8 *w_cur = reinterpret_cast<const bf16x8 *>(ST == 0 ? w0_s : w1_s) + wave * NT * 4 * 64 + lane;
         lds_barrier();   // (B0) chunk cc's loads have landed; chunk cc-1's stage is free
-        if (s_chunks) {   // chunk-start states for the backward pass
+        if constexpr (XM == XM_STATES) {   // chunk-start states for the backward pass
             float *dst = s_chunks + (cidb + ccs) * D * D;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
@@ -1234,7 +1240,7 @@ struct CarryW {
     static_assert(VGW_INS + M_INS < 64, "the vector-memory counter holds 0..63");
 };
 
-template <int RES, bool XN>
+template <int RES, bool XN, int XM>
 __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v, int L, int H, int Nc,
     const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
@@ -1367,7 +1373,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
             const float *g_cur = ST == 0 ? g0_s : g1_s;
             const bf16x8 *w_cur = ST == 0 ? wf0 : wf1;
             lds_barrier();   // B0
-            if (s_chunks) {   // chunk-start states for the backward pass
+            if constexpr (XM == XM_STATES) {   // chunk-start states for the backward pass
                 float *dst = s_chunks + (cidb + ccs) * D * D;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
@@ -1475,13 +1481,14 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) rho_c[ct] = RES ? rho[h * D + col0 + 16 * ct + lr] : 0.f;
     float hp[2][4];
-    int hf[4];   // halted flags of the rows (0 without halting)
+    int hf[4];   // halted flags of the rows (XM_HALT)
     // h_prev of chunk cc and the rows' halted flags (rows past the end of the
     // sequence read the last row; never stored)
     auto load_hp = [&](int cc) __attribute__((always_inline)) {
         const int c0 = cc * C, last = L - 1 - c0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hf[j] = halted ? halted[tokb + c0 + min(16 * ot + 4 * lg + j, last)] : 0;
+        for (int j = 0; j < 4; ++j)
+            if constexpr (XM == XM_HALT) hf[j] = halted[tokb + c0 + min(16 * ot + 4 * lg + j, last)];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -1584,7 +1591,8 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
                 if (c0 + r >= L) continue;
                 const float ov = gv[j] * qs[j] + mev[j];
                 const int64_t row = tokb + c0 + r;
-                if (hf[j] != 0) continue;   // a halted position keeps its state
+                if constexpr (XM == XM_HALT)
+                    if (hf[j] != 0) continue;   // a halted position keeps its state
                 if constexpr (RES == 0) {
                     if (o) o[(row * H + h) * D + col] = ov;
                 } else {
@@ -1649,32 +1657,44 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
     const int Nc = (L + C - 1) / C;
     const int res = out.h_out == nullptr ? 0 : (out.h_prev_bf16 ? 2 : 1);
     const bool xn = out.h_out != nullptr && out.x_next != nullptr;
+    // chunk-start states only in the scan form, halting only with the loop residual
+    if ((out.s_chunks && (res != 0 || out.halted)) || (out.halted && res == 0)) return hipErrorInvalidValue;
+    const int xm = out.s_chunks ? XM_STATES : (out.halted ? XM_HALT : XM_NONE);
     // 32-column slices when 16-column ones would need more than one round of
     // workgroups (one workgroup per CU: each holds most of the CU's LDS).  A
     // 32-column chunk step takes nearly twice as long, so with one round of
     // 16-column workgroups those are faster.
     if (!f32 && D == 128 && (int64_t)B * H * (D / 16) > compute_units()) {
         const dim3 gridw(H, D / CarryW::SW, B);
-#define CARRYW(R, X)                                                                               \
-    launch_kernel((k_scan_carry_w<R, X>), gridw, dim3(CARRY_THREADS), 0, s, (const bf16 *)q, (const bf16 *)k, \
+#define CARRYW(R, X, XM)                                                                           \
+    launch_kernel((k_scan_carry_w<R, X, XM>), gridw, dim3(CARRY_THREADS), 0, s, (const bf16 *)q, (const bf16 *)k, \
                   (const bf16 *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
                   s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks, out.halted)
-        if (res == 0) CARRYW(0, false);
-        else if (res == 1) { if (xn) CARRYW(1, true); else CARRYW(1, false); }
-        else { if (xn) CARRYW(2, true); else CARRYW(2, false); }
+#define CARRYW_H(R, X)                                                                             \
+    do {                                                                                           \
+        if (xm == XM_HALT) CARRYW(R, X, XM_HALT); else CARRYW(R, X, XM_NONE);                      \
+    } while (0)
+        if (res == 0) { if (xm == XM_STATES) CARRYW(0, false, XM_STATES); else CARRYW(0, false, XM_NONE); }
+        else if (res == 1) { if (xn) CARRYW_H(1, true); else CARRYW_H(1, false); }
+        else { if (xn) CARRYW_H(2, true); else CARRYW_H(2, false); }
+#undef CARRYW_H
 #undef CARRYW
         return hipGetLastError();
     }
     dim3 grid(H, D / 16, B);
-#define CARRY(DD, T, R, X)                                                                         \
-    launch_kernel((k_scan_carry<DD, T, R, X>), grid, dim3(CARRY_THREADS), 0, s, (const T *)q, (const T *)k, \
+#define CARRY(DD, T, R, X, XM)                                                                     \
+    launch_kernel((k_scan_carry<DD, T, R, X, XM>), grid, dim3(CARRY_THREADS), 0, s, (const T *)q, (const T *)k, \
                   (const T *)v, L, H, Nc, (const float *)ws.W, (const float *)ws.M, (const float *)ws.g, \
                   s_init, s_final, out.o, out.h_prev, out.rho, out.h_out, out.x_next, out.s_chunks, out.halted)
+#define CARRY_H(DD, T, R, X)                                                                       \
+    do {                                                                                           \
+        if (xm == XM_HALT) CARRY(DD, T, R, X, XM_HALT); else CARRY(DD, T, R, X, XM_NONE);          \
+    } while (0)
 #define CARRY_R(DD, T)                                                                             \
     do {                                                                                           \
-        if (res == 0) CARRY(DD, T, 0, false);                                                      \
-        else if (res == 1) { if (xn) CARRY(DD, T, 1, true); else CARRY(DD, T, 1, false); }         \
-        else { if (xn) CARRY(DD, T, 2, true); else CARRY(DD, T, 2, false); }                       \
+        if (res == 0) { if (xm == XM_STATES) CARRY(DD, T, 0, false, XM_STATES); else CARRY(DD, T, 0, false, XM_NONE); } \
+        else if (res == 1) { if (xn) CARRY_H(DD, T, 1, true); else CARRY_H(DD, T, 1, false); }     \
+        else { if (xn) CARRY_H(DD, T, 2, true); else CARRY_H(DD, T, 2, false); }                   \
     } while (0)
     if (f32) {
         if (D == 128) CARRY_R(128, float); else CARRY_R(64, float);
@@ -1682,6 +1702,7 @@ hipError_t launch_scan_carry(bool f32, int B, int L, int H, int D, const void *q
         if (D == 128) CARRY_R(128, bf16); else CARRY_R(64, bf16);
     }
 #undef CARRY_R
+#undef CARRY_H
 #undef CARRY
     return hipGetLastError();
 }
