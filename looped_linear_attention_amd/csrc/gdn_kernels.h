@@ -53,11 +53,13 @@ bool project_separate_gates(bool f32, int M);
 int gate_partials(bool f32, int M, int d, int H);
 // With rows != nullptr (bf16 wide projection with gate partials only) only the
 // tokens rows[0 .. *rows_count) are projected (count read on the device); the
-// other tokens' q, k, v and gate partials stay as they are.
+// other tokens' q, k, v and gate partials stay as they are.  With yraw
+// (project_separate_gates inputs, no row list) the GEMM also stores the raw
+// fp32 projections of the q|k|v columns, before the norms, to yraw[M][ldy].
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
                           float eps, float *zp, hipStream_t s, const int *rows = nullptr,
-                          const int *rows_count = nullptr);
+                          const int *rows_count = nullptr, float *yraw = nullptr, int64_t ldy = 0);
 hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
                         float *beta, float alpha_lo, hipStream_t s);
 
@@ -135,10 +137,11 @@ hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t 
 // ---- token-local steps of the loop backward (loop_backward.hip) ----
 // x[i] = bf16(h[i]) (round to nearest even), n elements, 16-byte aligned.
 hipError_t launch_lb_round(int64_t n, const float *h, bf16 *x, hipStream_t s);
-// Y <- dL/dY from the scan gradients, in place.
+// Y <- dL/dY from the scan gradients, in place; the raw gates from Y's gate
+// columns, or with zp the sums of its nzp partials; dY's padding columns zero.
 hipError_t launch_lb_epilogue_grad(int M, int H, int D, float *Y, int64_t P, int64_t qkvp, float eps, float alpha_lo,
                                    const float *dq, const float *dk, const float *dv, const float *dalpha,
-                                   const float *dbeta, hipStream_t s);
+                                   const float *dbeta, const float *zp, int nzp, hipStream_t s);
 // drho[c] = sum_r dh[r][c] hp[r][c] through lb_drho_blocks(M) x d partials.
 int lb_drho_blocks(int M);
 hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp_f32, float *part, float *drho,

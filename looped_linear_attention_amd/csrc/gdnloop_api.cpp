@@ -256,9 +256,11 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
 // GEMM leaves the gates to it and does not write gate partials (zp).
 hipError_t project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
                    void *v, float *al, float *be, float alpha_lo, float eps, float *zp, hipStream_t s,
-                   const int *rows = nullptr, const int *rows_count = nullptr) {
+                   const int *rows = nullptr, const int *rows_count = nullptr, float *yraw = nullptr,
+                   int64_t ldy = 0) {
     hipError_t e = timed(GDN_STAGE_PROJECT, s, [&] {
-        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, zp, s, rows, rows_count);
+        return launch_project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, alpha_lo, eps, zp, s, rows, rows_count,
+                              yraw, ldy);
     });
     if (e == hipSuccess && !zp && project_separate_gates(f32, M))
         e = timed(GDN_STAGE_GATES, s, [&] { return launch_gates(M, d, H, D, x, Wpack, al, be, alpha_lo, s); });
@@ -478,7 +480,9 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
     if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
     // bf16: dY W and x^T dY split their k ranges so that their tiles fill the chip
     const int dx_split = f32 ? 1 : lb_dx_split(M, d), dw_split = lb_dw_split(d, P, f32);
-    if ((e = launch_fill_zero(dW, (int64_t)d * P * dw_split, s)) != hipSuccess) return hip_fail(e, "fill launch");
+    // (the first loop's x^T dY stores the accumulators, later loops add to them; the fp32 path accumulates
+    // from zero)
+    if (f32 && (e = launch_fill_zero(dW, (int64_t)d * P * dw_split, s)) != hipSuccess) return hip_fail(e, "fill launch");
     for (int tau = T - 1; tau >= 0; --tau) {
         // loop tau + 1 of the forward: input h^(tau), incoming gradient dL/dh^(tau+1)
         const bool hp_f32 = f32 || tau > 0;
@@ -493,17 +497,23 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
             if ((e = launch_lb_round(tokd, (const float *)hp, xb, s)) != hipSuccess) return hip_fail(e, "round launch");
             x = xb;
         }
-        e = project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo, desc->norm_eps, zp, s);
+        // the raw projections in fp32 (the normalisation's and the gates' gradients need them): from the
+        // projection GEMM itself where it forms the gate partials (the raw gates are their sums), else from
+        // one more product
+        const bool raw_in_gemm = zp != nullptr;
+        e = project(f32, M, d, H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo, desc->norm_eps, zp, s, nullptr,
+                    nullptr, raw_in_gemm ? Y : nullptr, P);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
-        // the raw projections in fp32 (the normalisation's and the gates' gradients need them)
-        e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
-            if (f32)
-                return launch_gemm_nt(OPND_F32_SPLIT, wmode, EPI_STORE, x, d, Wpack, d, M, P, d, Y, P, nullptr,
-                                      nullptr, 0, s);
-            return launch_gemm_tile(EPI_STORE, true, (const bf16 *)x, nullptr, d, (const bf16 *)Wpack, nullptr, d, M,
-                                    P, d, Y, P, nullptr, nullptr, 0, nullptr, 0, s);
-        });
-        if (e != hipSuccess) return hip_fail(e, "projection recompute launch");
+        if (!raw_in_gemm) {
+            e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
+                if (f32)
+                    return launch_gemm_nt(OPND_F32_SPLIT, wmode, EPI_STORE, x, d, Wpack, d, M, P, d, Y, P, nullptr,
+                                          nullptr, 0, s);
+                return launch_gemm_tile(EPI_STORE, true, (const bf16 *)x, nullptr, d, (const bf16 *)Wpack, nullptr,
+                                        d, M, P, d, Y, P, nullptr, nullptr, 0, nullptr, 0, s);
+            });
+            if (e != hipSuccess) return hip_fail(e, "projection recompute launch");
+        }
         // the scan backward from S = 0 with dO = dL/dh^(tau+1) (the mixer output is h's width); with gate
         // partials the prep forms alpha and beta into their workspace regions, as in the forward
         CarryOut out{nullptr, nullptr, false, nullptr, nullptr, nullptr, sc};
@@ -521,7 +531,8 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         });
         if (e != hipSuccess) return hip_fail(e, "backward chunk launch");
         // through the normalisation and the gates: Y <- dY
-        e = launch_lb_epilogue_grad(M, H, D, Y, P, qkvp, desc->norm_eps, desc->alpha_lo, gq, gk, gv, gal, gbe, s);
+        e = launch_lb_epilogue_grad(M, H, D, Y, P, qkvp, desc->norm_eps, desc->alpha_lo, gq, gk, gv, gal, gbe,
+                                    raw_in_gemm ? zp : nullptr, lo.P, s);
         if (e != hipSuccess) return hip_fail(e, "epilogue gradient launch");
         e = launch_lb_drho(M, d, g_in, hp, hp_f32, part, drho + (int64_t)tau * d, s);
         if (e != hipSuccess) return hip_fail(e, "rho gradient launch");
@@ -563,8 +574,9 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
                 (e = launch_transpose_split(Y, P, M, P, YTh, YTl, Mp, Mp, s)) != hipSuccess)
                 return hip_fail(e, "transpose launch");
             e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
-                return launch_gemm_tile(EPI_ACCUM, true, (const bf16 *)XT, nullptr, Mp, YTh, YTl, Mp, d, P, Mp, dW,
-                                        P, nullptr, nullptr, 0, nullptr, 0, s, dw_split, (int64_t)d * P);
+                return launch_gemm_tile(tau == T - 1 ? EPI_STORE : EPI_ACCUM, true, (const bf16 *)XT, nullptr, Mp,
+                                        YTh, YTl, Mp, d, P, Mp, dW, P, nullptr, nullptr, 0, nullptr, 0, s, dw_split,
+                                        (int64_t)d * P);
             });
         }
         if (e != hipSuccess) return hip_fail(e, "weight gradient launch");

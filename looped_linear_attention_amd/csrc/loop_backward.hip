@@ -34,13 +34,18 @@ __global__ __launch_bounds__(256) void k_lb_round(const float *__restrict__ h, b
 // The gradient of the epilogue, one wave per (token, head), written over the
 // raw projections Y [M][P] in place (packed order: head j's q|k|v at columns
 // 3 D j .., the gates at qkvp + j and qkvp + H + j); each lane reads its own
-// elements of Y before it writes them.
+// elements of Y before it writes them.  With zp the raw gate pre-activations
+// are the sums of the projection's nzp partials zp[p][2H][M] in the order
+// p = 0, 1, ... (as the chunk preparation forms them) rather than Y's gate
+// columns.  The padding columns of dY (between the q|k|v columns and qkvp,
+// and after the 2H gate columns) are set to zero.
 template <int D>
 __global__ __launch_bounds__(256) void k_lb_epilogue_grad(float *Y, int64_t P, int64_t qkvp, int M, int H, float eps,
                                                           float alpha_lo, const float *__restrict__ dq,
                                                           const float *__restrict__ dk, const float *__restrict__ dv,
                                                           const float *__restrict__ dalpha,
-                                                          const float *__restrict__ dbeta) {
+                                                          const float *__restrict__ dbeta,
+                                                          const float *__restrict__ zp, int nzp) {
     constexpr int E = D / 64;
     const int lane = threadIdx.x & 63;
     const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -86,10 +91,23 @@ __global__ __launch_bounds__(256) void k_lb_epilogue_grad(float *Y, int64_t P, i
     }
     if (lane == 0) {
         float *ya = Y + m * P + qkvp + j, *yb = Y + m * P + qkvp + H + j;
-        const float s = 1.f / (1.f + expf(*ya)), be = 1.f / (1.f + expf(-*yb));
+        float za = 0.f, zb = 0.f;
+        if (zp) {
+            for (int p = 0; p < nzp; ++p) {
+                za += zp[((int64_t)p * 2 * H + j) * M + m];
+                zb += zp[((int64_t)p * 2 * H + H + j) * M + m];
+            }
+        } else {
+            za = *ya;
+            zb = *yb;
+        }
+        const float s = 1.f / (1.f + expf(za)), be = 1.f / (1.f + expf(-zb));
         *ya = -dalpha[u] * (1.f - alpha_lo) * s * (1.f - s);
         *yb = dbeta[u] * be * (1.f - be);
     }
+    const int64_t qkv = (int64_t)H * 3 * D, pad1 = qkvp - qkv, pad2 = P - qkvp - 2 * H;
+    for (int64_t i = (int64_t)j * 64 + lane; i < pad1 + pad2; i += (int64_t)H * 64)
+        Y[m * P + (i < pad1 ? qkv + i : qkvp + 2 * H + (i - pad1))] = 0.f;
 }
 
 // drho partials: part[rb][c] = sum over rows r of block rb (DR_ROWS rows, in
@@ -134,13 +152,20 @@ __global__ __launch_bounds__(256) void k_lb_drho_part(const float *__restrict__ 
     }
     *reinterpret_cast<float4 *>(part + (int64_t)rb * d + c) = acc;
 }
+// 64 columns per workgroup: wave g sums the partials of row blocks
+// [g nrb / 4, (g + 1) nrb / 4) in order, then the four sums are added in the
+// order g = 0..3.
 __global__ __launch_bounds__(256) void k_lb_drho_sum(const float *__restrict__ part, int nrb, int d,
                                                      float *__restrict__ drho) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= d) return;
+    __shared__ float s4[4][64];
+    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
     float acc = 0.f;
-    for (int rb = 0; rb < nrb; ++rb) acc += part[(int64_t)rb * d + c];
-    drho[c] = acc;
+    if (c < d)
+        for (int rb = nrb * g / 4; rb < nrb * (g + 1) / 4; ++rb) acc += part[(int64_t)rb * d + c];
+    s4[g][lane] = acc;
+    __syncthreads();
+    if (g == 0 && c < d) drho[c] = ((s4[0][lane] + s4[1][lane]) + s4[2][lane]) + s4[3][lane];
 }
 
 // dWT [d][P] (the weight gradient in the orientation x^T dY) to the unpacked
@@ -203,15 +228,15 @@ hipError_t launch_lb_round(int64_t n, const float *h, bf16 *x, hipStream_t s) {
 
 hipError_t launch_lb_epilogue_grad(int M, int H, int D, float *Y, int64_t P, int64_t qkvp, float eps, float alpha_lo,
                                    const float *dq, const float *dk, const float *dv, const float *dalpha,
-                                   const float *dbeta, hipStream_t s) {
+                                   const float *dbeta, const float *zp, int nzp, hipStream_t s) {
     const int64_t units = (int64_t)M * H;
     const dim3 grid((unsigned)((units + 3) / 4));
     if (D == 128)
         launch_kernel(k_lb_epilogue_grad<128>, grid, dim3(256), 0, s, Y, P, qkvp, M, H, eps, alpha_lo, dq, dk, dv,
-                      dalpha, dbeta);
+                      dalpha, dbeta, zp, nzp);
     else if (D == 64)
         launch_kernel(k_lb_epilogue_grad<64>, grid, dim3(256), 0, s, Y, P, qkvp, M, H, eps, alpha_lo, dq, dk, dv,
-                      dalpha, dbeta);
+                      dalpha, dbeta, zp, nzp);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -228,7 +253,7 @@ hipError_t launch_lb_drho(int M, int d, const float *dh, const void *hp, bool hp
     else launch_kernel(k_lb_drho_part<bf16>, g1, dim3(256), 0, s, dh, (const bf16 *)hp, M, d, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_kernel(k_lb_drho_sum, dim3((d + 255) / 256), dim3(256), 0, s, (const float *)part, nrb, d, drho);
+    launch_kernel(k_lb_drho_sum, dim3((d + 63) / 64), dim3(256), 0, s, (const float *)part, nrb, d, drho);
     return hipGetLastError();
 }
 

@@ -562,11 +562,12 @@ __device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[3][4], char *s
 // (count in *rows_count, read on the device), gathered from x and scattered to
 // q, k, v and the gate partials; tiles past the count return at once.  M stays
 // the row stride of the gate partials.
-template <int D, bool GZ, bool ROWS>
+// RAW: also store the raw fp32 projections (yraw) before the epilogue.
+template <int D, bool GZ, bool ROWS, bool RAW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_proj_wide(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Wp, int M, int K, int H, int m_tiles, int n_tiles,
     bf16 *q, bf16 *k, bf16 *v, float eps, float *__restrict__ zp, const int *__restrict__ rows,
-    const int *__restrict__ rows_count) {
+    const int *__restrict__ rows_count, float *__restrict__ yraw, int64_t ldy) {
     __shared__ __attribute__((aligned(16))) char smem[W_LDS_MAIN];
     bf16 *stages = reinterpret_cast<bf16 *>(smem);
 
@@ -705,6 +706,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int it = 1; it < nkb; ++it) kstep(std::true_type(), it);
     wait_vmcnt<0>();   // the re-reads past the end land before LDS is reused
     __syncthreads();
+
+    if constexpr (RAW) {
+        // the raw fp32 projections before the epilogue (for the backward pass): yraw[token][packed row], the
+        // q|k|v rows only; a lane's four consecutive rows of a token as one 16-byte store
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int m = m0 + wt * 128 + tt * 32 + (lane & 31);
+            if (m < Mv) {
+                const int nl = n0 + wf * WCOLS + 4 * (lane >> 5);
+                float *yr = yraw + (int64_t)m * ldy + nl;
+#pragma unroll
+                for (int ft = 0; ft < 3; ++ft)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        if (nl + ft * 32 + 8 * g < qkv_rows)
+                            *reinterpret_cast<float4 *>(yr + ft * 32 + 8 * g) =
+                                float4{acc[ft][tt][4 * g], acc[ft][tt][4 * g + 1], acc[ft][tt][4 * g + 2],
+                                       acc[ft][tt][4 * g + 3]};
+            }
+        }
+    }
 
     switch (wf) {
         case 0: wide_epilogue<D, 0>(acc, smem, lane, wt, t, m0, n0, Mv, H, q, k, v, eps, ROWS ? rows : nullptr); break;
@@ -871,9 +893,11 @@ int gate_partials(bool f32, int M, int d, int H) {
 
 hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, const void *Wpack,
                           void *q, void *k, void *v, float *alpha, float *beta, float alpha_lo,
-                          float eps, float *zp, hipStream_t s, const int *rows, const int *rows_count) {
+                          float eps, float *zp, hipStream_t s, const int *rows, const int *rows_count,
+                          float *yraw, int64_t ldy) {
     if (rows && (f32 || !project_separate_gates(f32, M) || !zp || (int64_t)M * d * 2 >= (int64_t(1) << 32)))
         return hipErrorInvalidValue;
+    if (yraw && (rows || !project_separate_gates(f32, M) || ldy < H * 3 * D || ldy % 4)) return hipErrorInvalidValue;
     const int ntiles = (int)(packed_rows(H, D) / BN);
     if (f32) {
         dim3 grid(ntiles, (M + BM_F - 1) / BM_F);
@@ -887,16 +911,20 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
                                alpha, beta, alpha_lo, eps);
     } else if (project_separate_gates(f32, M)) {
         const int m_tiles = (M + WM - 1) / WM, n_tiles = (H * 3 * D + WN - 1) / WN;
-#define WIDE(DD, GZ, RW)                                                                           \
-    launch_kernel(k_proj_wide<DD, GZ, RW>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x, \
+#define WIDE(DD, GZ, RW, RAW)                                                                      \
+    launch_kernel(k_proj_wide<DD, GZ, RW, RAW>, dim3(m_tiles * n_tiles), dim3(512), 0, s, (const bf16 *)x, \
                   (const bf16 *)Wpack, M, d, H, m_tiles, n_tiles, (bf16 *)q, (bf16 *)k, (bf16 *)v, eps, zp, rows, \
-                  rows_count)
+                  rows_count, yraw, ldy)
         if (rows) {
-            if (D == 128) WIDE(128, true, true); else WIDE(64, true, true);
+            if (D == 128) WIDE(128, true, true, false); else WIDE(64, true, true, false);
+        } else if (zp && yraw) {
+            if (D == 128) WIDE(128, true, false, true); else WIDE(64, true, false, true);
         } else if (zp) {
-            if (D == 128) WIDE(128, true, false); else WIDE(64, true, false);
+            if (D == 128) WIDE(128, true, false, false); else WIDE(64, true, false, false);
+        } else if (yraw) {
+            if (D == 128) WIDE(128, false, false, true); else WIDE(64, false, false, true);
         } else {
-            if (D == 128) WIDE(128, false, false); else WIDE(64, false, false);
+            if (D == 128) WIDE(128, false, false, false); else WIDE(64, false, false, false);
         }
 #undef WIDE
     } else {
