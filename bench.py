@@ -465,7 +465,10 @@ def bench_loop_backward(args, torch, gl, synth, name="prefill_b1_l4096"):
         gl.gdn_timer_destroy(t)
     M = B * L
     P = (H * 3 * D + 127) // 128 * 128 + 128
-    gemm_flops = 3 * 2 * M * P * d     # per loop: projections recomputed, dY W, x^T dY (counted once each)
+    # per loop: dY W and x^T dY (counted once each), plus the raw projections recomputed where the projection
+    # GEMM does not store them itself (it does for bf16 inputs of >= 1024 tokens with 2H <= 32)
+    nprod = 2 if (w.act == "bf16" and M >= 1024 and 2 * H <= 32) else 3
+    gemm_flops = nprod * 2 * M * P * d
     gemm_ach = gemm_flops * T / (tot["gemm"] * 1e-3) / 1e12
     return {"workload": f"loop backward, {name} (B={B}, L={L}, H={H}, dk=dv={D}, d={d}, T={T}, {w.act} inputs)",
             "value": M / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
