@@ -184,11 +184,10 @@ hipError_t launch_gemm_tile(int epi, bool out_f32, const bf16 *A, const bf16 *A2
 // out = sum_z parts[z] (z < nparts, stride pstride) + rho[c] * add[r][c] (rho null: no term), n = rows * d.
 hipError_t launch_sum_parts(int64_t rows, int d, const float *parts, int nparts, int64_t pstride, const float *rho,
                             const float *add, float *out, hipStream_t s);
-// x ~ hi + lo, both bf16, elementwise over n values (16-byte aligned).
-hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream_t s);
-// hi[c][r] + lo[c][r] ~ in[r][c] (fp32 in [R][ldi]), zero for R <= r < Rp.
-hipError_t launch_transpose_split(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldo,
-                                  int Rp, hipStream_t s);
+// hi/lo [R][ldh] split planes of in [R][ldi] and, from the same read, the
+// transposed planes hiT/loT [Cc][ldo] (rows r < Rp, zero past R).
+hipError_t launch_split_both(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldh, bf16 *hiT,
+                             bf16 *loT, int64_t ldo, int Rp, hipStream_t s);
 // The same product with every epilogue of launch_gemm_tile (C fp32 or bf16);
 // operand pairs (split, split) and (bf16, bf16).
 hipError_t launch_gemm_nt_ex(int mode_a, int mode_b, int epi, bool out_f32, const void *A, int64_t lda, const void *B,

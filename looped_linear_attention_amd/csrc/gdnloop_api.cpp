@@ -554,7 +554,9 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
         } else {
             bf16 *Yh = (bf16 *)at(ws, lo.Yhl), *Yl = Yh + (int64_t)M * P;
             bf16 *YTh = (bf16 *)YT, *YTl = YTh + (int64_t)P * Mp;
-            if ((e = launch_split((int64_t)M * P, Y, Yh, Yl, s)) != hipSuccess) return hip_fail(e, "split launch");
+            // dY as bf16 hi/lo planes for dY W, and transposed for x^T dY, from one read
+            if ((e = launch_split_both(Y, P, M, P, Yh, Yl, P, YTh, YTl, Mp, Mp, s)) != hipSuccess)
+                return hip_fail(e, "split launch");
             if (dx_split == 1) {
                 e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
                     return launch_gemm_tile(EPI_RESID, true, Yh, Yl, P, (const bf16 *)WT, nullptr, P, M, d, P, g_out,
@@ -570,8 +572,7 @@ gdn_status gdn_loop_backward(const gdn_desc *desc, const void *h0, const void *W
                     e = launch_sum_parts(M, d, Gp, dx_split, (int64_t)M * d, rho + (int64_t)tau * d, g_in, g_out, s);
             }
             if (e != hipSuccess) return hip_fail(e, "input gradient launch");
-            if ((e = launch_transpose(false, false, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess ||
-                (e = launch_transpose_split(Y, P, M, P, YTh, YTl, Mp, Mp, s)) != hipSuccess)
+            if ((e = launch_transpose(false, false, x, d, M, d, XT, Mp, Mp, s)) != hipSuccess)
                 return hip_fail(e, "transpose launch");
             e = timed(GDN_STAGE_BWD_GEMM, s, [&] {
                 return launch_gemm_tile(tau == T - 1 ? EPI_STORE : EPI_ACCUM, true, (const bf16 *)XT, nullptr, Mp,

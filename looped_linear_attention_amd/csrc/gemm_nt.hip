@@ -191,16 +191,26 @@ __global__ __launch_bounds__(256) void k_transpose(const TI *__restrict__ in, in
     }
 }
 
-// hi[c][r] + lo[c][r] ~ in[r][c], the fp32 value split into two bf16 parts.
-__global__ __launch_bounds__(256) void k_transpose_split(const float *__restrict__ in, int64_t ldi, int R, int Cc,
-                                                         bf16 *__restrict__ hi, bf16 *__restrict__ lo, int64_t ldo,
-                                                         int Rp) {
+// Both at once from one read of in [R][ldi]: hi/lo [R][ldh] as they are (rows
+// r < R) and hiT/loT [Cc][ldo] transposed (r < Rp, zero past R).
+__global__ __launch_bounds__(256) void k_split_both(const float *__restrict__ in, int64_t ldi, int R, int Cc,
+                                                    bf16 *__restrict__ hi, bf16 *__restrict__ lo, int64_t ldh,
+                                                    bf16 *__restrict__ hiT, bf16 *__restrict__ loT, int64_t ldo,
+                                                    int Rp) {
     __shared__ float tile[64][65];
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = r0 + ty + 4 * i, c = c0 + tx;
-        tile[ty + 4 * i][tx] = (r < R && c < Cc) ? in[(int64_t)r * ldi + c] : 0.f;
+        const bool ok = r < R && c < Cc;
+        const float x[2] = {ok ? in[(int64_t)r * ldi + c] : 0.f, 0.f};
+        tile[ty + 4 * i][tx] = x[0];
+        if (ok) {
+            bf16 h[2], l[2];
+            split_bf16<2>(x, h, l);
+            hi[(int64_t)r * ldh + c] = h[0];
+            lo[(int64_t)r * ldh + c] = l[0];
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -210,30 +220,8 @@ __global__ __launch_bounds__(256) void k_transpose_split(const float *__restrict
             const float x[2] = {tile[tx][ty + 4 * i], 0.f};
             bf16 h[2], l[2];
             split_bf16<2>(x, h, l);
-            hi[(int64_t)c * ldo + r] = h[0];
-            lo[(int64_t)c * ldo + r] = l[0];
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void k_split(const float *__restrict__ x, bf16 *__restrict__ hi,
-                                               bf16 *__restrict__ lo, int64_t n) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= n) return;
-    if (i + 3 < n) {
-        const float4 v = *reinterpret_cast<const float4 *>(x + i);
-        const float a[4] = {v.x, v.y, v.z, v.w};
-        bf16 h[4], l[4];
-        split_bf16<4>(a, h, l);
-        *reinterpret_cast<bf16x4 *>(hi + i) = pack4(h);
-        *reinterpret_cast<bf16x4 *>(lo + i) = pack4(l);
-    } else {
-        for (int64_t j = i; j < n; ++j) {
-            const float a[2] = {x[j], 0.f};
-            bf16 h[2], l[2];
-            split_bf16<2>(a, h, l);
-            hi[j] = h[0];
-            lo[j] = l[0];
+            hiT[(int64_t)c * ldo + r] = h[0];
+            loT[(int64_t)c * ldo + r] = l[0];
         }
     }
 }
@@ -299,19 +287,12 @@ hipError_t launch_gemm_nt(int mode_a, int mode_b, int epi, const void *A, int64_
                              s);
 }
 
-hipError_t launch_split(int64_t n, const float *x, bf16 *hi, bf16 *lo, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    const int64_t groups = (n + 3) / 4;
-    launch_kernel(k_split, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, hi, lo, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose_split(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldo,
-                                  int Rp, hipStream_t s) {
+hipError_t launch_split_both(const float *in, int64_t ldi, int R, int Cc, bf16 *hi, bf16 *lo, int64_t ldh, bf16 *hiT,
+                             bf16 *loT, int64_t ldo, int Rp, hipStream_t s) {
     if (R < 0 || Cc <= 0 || Rp < R || (Rp + 63) / 64 > 65535) return hipErrorInvalidValue;
     if (Rp == 0) return hipSuccess;
-    launch_kernel(k_transpose_split, dim3((Cc + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s, in, ldi, R, Cc, hi, lo,
-                  ldo, Rp);
+    launch_kernel(k_split_both, dim3((Cc + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s, in, ldi, R, Cc, hi, lo, ldh,
+                  hiT, loT, ldo, Rp);
     return hipGetLastError();
 }
 
