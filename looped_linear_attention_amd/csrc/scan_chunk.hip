@@ -1223,6 +1223,13 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
 // and S_c after B0(cc+1), so each needs a single buffer; V, gamma and W have
 // two stages.  The producer's wait counts are the same every chunk (past the
 // last chunk it re-reads the last one into buffers nobody reads any more).
+
+// Chunks ahead of the output step that the 32-column carry's L2 prefetch touches.
+// This carry runs when the (sequence, head) pairs are many (at 4 x 16 of them each
+// XCD holds eight slice groups), and lines fetched further ahead are then evicted
+// from the XCD's L2 before use and fetched again.
+constexpr int PFW_AHEAD = 1;
+
 struct CarryW {
     static constexpr int D = 128;
     static constexpr int SW = 32;                    // columns of S per workgroup
@@ -1502,7 +1509,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
                 }
             }
     };
-    // L2 prefetch, PF_AHEAD chunks ahead: one load touching each 128-byte line of
+    // L2 prefetch, PFW_AHEAD chunks ahead: one load touching each 128-byte line of
     // that chunk's K, Q, V, W, M, h_prev and gamma for this head, the lines dealt
     // over the head's slice workgroups (which share an XCD's L2); the loaded word
     // is consumed two chunks later.
@@ -1517,7 +1524,7 @@ __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
         asm volatile("" ::"v"(pfv[P]));
         const int j = slice + G::NSL * (lane * 4 + ot);
         if (j < NL) {
-            const int cp = min(cc + PF_AHEAD, Nc - 1), c0p = cp * C;
+            const int cp = min(cc + PFW_AHEAD, Nc - 1), c0p = cp * C;
             const char *p;
             int jj = j;
             auto row_tok = [&](int r) { return tokb + min(c0p + r, L - 1); };
