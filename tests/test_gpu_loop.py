@@ -373,3 +373,30 @@ def test_loop_decode_n64_forced():
     for s in range(steps):
         say(f"    step {s}")
         _, states = check_forced_decode_step(w, x, Wp, dev(hs[s]), rho, states, N, TOL_BF16)
+
+
+@pytest.mark.parametrize("name", ["prefill_b1_l4096", "tiny_f32"])
+def test_loop_decode_batch_independent(name):
+    """Each sequence's projection, state step and residual do not depend on the batch around it: a call
+    on 64 sequences gives the same bits, in h_out and in every state, as four calls of 16."""
+    w = synth.workload(name)
+    N, part = 64, 16
+    say(f"[loop_decode] {name}: N={N} against {N // part} calls of {part}")
+    x = synth.prefill_inputs(w, L=N)
+    h_t = dev(x["h0"].reshape(-1, w.d)[:N].contiguous())
+    Wp = _pack(w, x)
+    rho = dev(x["rho"])
+    g = torch.Generator().manual_seed(5)
+    states0 = (0.05 * torch.randn(w.T, N, w.H, w.dk, w.dv, generator=g)).to("cuda")
+    s_all = states0.clone()
+    h_all, _, _ = _decode_call(w, Wp, w.T, h_t, rho, s_all, N)
+    h_part = torch.empty_like(h_all)
+    s_part = states0.clone()
+    for p0 in range(0, N, part):
+        st = s_part[:, p0:p0 + part].contiguous()
+        ho, _, _ = _decode_call(w, Wp, w.T, h_t[p0:p0 + part].contiguous(), rho, st, part)
+        h_part[p0:p0 + part] = ho
+        s_part[:, p0:p0 + part] = st
+    torch.cuda.synchronize()
+    assert torch.equal(h_all, h_part)
+    assert torch.equal(s_all, s_part)
