@@ -352,7 +352,7 @@ __global__ __launch_bounds__(BC_THREADS) void k_bwd_carry(const float *__restric
 //      also sums S (.) dS' (each element once).
 // fp32 operands enter the MFMA as bf16 hi + lo (3 passes; 2 where one side is
 // an exact bf16 input).  After the blocks: dP and dTb into LDS (fp32), the
-// 64 x 64 steps on the VALU (dT, dN = -T^T dT T^T, dA, dbeta), then dQ +=
+// 64 x 64 products Y = T^T dT and dN = -Y T^T on MFMA (3 passes), dA, dbeta, then dQ +=
 // (Gam (.) dP) K and dK += (Gam (.) dP)^T Q + (Gam (.) dA + (Gam (.) dA)^T) K on
 // MFMA with K^T and Q^T from the carry operands, and the decay gradient.
 constexpr int BK_THREADS = 512;
@@ -414,12 +414,13 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
                   O_CU = O_UN + 2 * C * JL, O_DU = O_CU + 2 * C * JL, O_SN = O_DU + 2 * C * JL,
                   O_DSN = O_SN + 2 * D * JL, BLK_ELEMS = O_DSN + 2 * D * JL;
     // final phase: fp32 [64][65] matrices over the same memory
-    constexpr int FL = C + 1, MAT = C * FL, FIN_FLOATS = 6 * MAT;
+    constexpr int FL = C + 1, MAT = C * FL, FIN_FLOATS = 6 * MAT + 10 * C;   // six matrices, then sum partials
     constexpr int LDS_BYTES = (BLK_ELEMS * 2 > FIN_FLOATS * 4) ? BLK_ELEMS * 2 : FIN_FLOATS * 4;
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
     bf16 *pl = reinterpret_cast<bf16 *>(smem);
     float *fm = reinterpret_cast<float *>(smem);
     float *Ts = fm, *As = fm + MAT, *Ps = fm + 2 * MAT, *Gs = fm + 3 * MAT, *dPs = fm + 4 * MAT, *dXs = fm + 5 * MAT;
+    float *part = fm + 6 * MAT, *part2 = part + 8 * C;   // [8][C] and [2][C] partial sums
     __shared__ double lgs[C];
     __shared__ float gam[C], cr[C], bes[C], als[C], dgam2[2][C], dcr2[2][C], dbn[C], dlg[C], dbp[C], sdd[8];
 
@@ -699,52 +700,92 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
         Gs[r * FL + m] = m <= r ? (float)exp(lgs[r] - lgs[m]) : 0.f;
     }
     __syncthreads();
-    // dbeta part 1 (from Tb = T diag(beta)): sum_r dTb_rm T_rm
-    if (t < C) {
-        float s = 0.f;
-        for (int r = 0; r < C; ++r) s = fmaf(dXs[r * FL + t], Ts[r * FL + t], s);
-        dbp[t] = s;
-    }
-    __syncthreads();
-    for (int n = t; n < C * C; n += BK_THREADS) dXs[(n / C) * FL + n % C] *= bes[n % C];   // dT = dTb diag(beta)
-    __syncthreads();
-    // Y = T^T dT (8 elements per thread: row r = t / 8, columns m = t % 8 + 8 a)
-    const int rr = t >> 3, cq = t & 7;
-    float Y[8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        const int m = cq + 8 * a;
-        float acc = 0.f;
-        for (int r = rr; r < C; ++r) acc = fmaf(Ts[r * FL + rr], dXs[r * FL + m], acc);
-        Y[a] = acc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < 8; ++a) dXs[rr * FL + cq + 8 * a] = Y[a];
-    __syncthreads();
-    // dN_ri = -sum_m Y_rm T_im (strict lower); dA = diag(beta) dN; dbeta part 2: sum_i dN_ri A_ri
-    float dNr[8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        const int i = cq + 8 * a;
-        float acc = 0.f;
-        if (i < rr)
-            for (int m = 0; m <= i; ++m) acc = fmaf(dXs[rr * FL + m], Ts[i * FL + m], acc);
-        dNr[a] = -acc;
-    }
-    __syncthreads();
+    // dbeta part 1 (from Tb = T diag(beta)): sum_r dTb_rm T_rm, over 8 row groups of 8
     {
-        float p2 = 0.f;
+        const int m = t & 63, g = t >> 6;
+        float sp = 0.f;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            dXs[rr * FL + cq + 8 * a] = bes[rr] * dNr[a];
-            p2 = fmaf(dNr[a], As[rr * FL + cq + 8 * a], p2);
+        for (int e = 0; e < 8; ++e) sp = fmaf(dXs[(8 * g + e) * FL + m], Ts[(8 * g + e) * FL + m], sp);
+        part[g * C + m] = sp;
+    }
+    // Y = T^T dT with dT = dTb diag(beta), on MFMA (3 passes).  Wave w: row tile w % 4 of Y,
+    // column tiles 2 (w / 4) + {0, 1}; T is lower triangular, so its zeros bound the sums.
+    const int yr = wave & 3, yc = 2 * (wave >> 2);
+    f32x4 yacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int kk = 32 * s + 8 * lg;
+        float a8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = Ts[(kk + e) * FL + 16 * yr + lr];
+        bf16x8 ah, al;
+        split8(a8, ah, al);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int m = 16 * (yc + x) + lr;
+            float b8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b8[e] = dXs[(kk + e) * FL + m] * bes[m];
+            bf16x8 bh, bl;
+            split8(b8, bh, bl);
+            yacc[x] = mm3(ah, al, bh, bl, yacc[x]);
         }
+    }
+    __syncthreads();   // dTb read by every wave; Y replaces it
+    if (t < C) {
+        float sp = 0.f;
 #pragma unroll
-        for (int off = 1; off < 8; off <<= 1) p2 += __shfl_xor(p2, off, 64);
-        if (cq == 0) dbn[rr] = p2;
+        for (int g = 0; g < 8; ++g) sp += part[g * C + t];
+        dbp[t] = sp;
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dXs[(16 * yr + 4 * lg + jj) * FL + 16 * (yc + x) + lr] = yacc[x][jj];
+    __syncthreads();
+    // dN = -(Y T^T) strictly below the diagonal (T's zeros bound the sums), same tiles;
+    // dA = diag(beta) dN; dbeta part 2: sum_i dN_ri A_ri
+    f32x4 nacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int kk = 32 * s + 8 * lg;
+        float a8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = dXs[(16 * yr + lr) * FL + kk + e];
+        bf16x8 ah, al;
+        split8(a8, ah, al);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int i = 16 * (yc + x) + lr;
+            float b8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b8[e] = Ts[i * FL + kk + e];
+            bf16x8 bh, bl;
+            split8(b8, bh, bl);
+            nacc[x] = mm3(ah, al, bh, bl, nacc[x]);
+        }
+    }
+    __syncthreads();   // Y read by every wave; dA replaces it
+    {
+        float p2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * yr + 4 * lg + jj, i = 16 * (yc + x) + lr;
+                const float dn = i < r ? -nacc[x][jj] : 0.f;
+                dXs[r * FL + i] = bes[r] * dn;
+                p2[jj] = fmaf(dn, As[r * FL + i], p2[jj]);
+            }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) p2[jj] += __shfl_xor(p2[jj], off, 64);
+            if (lr == 0) part2[(wave >> 2) * C + 16 * yr + 4 * lg + jj] = p2[jj];
+        }
     }
     __syncthreads();
+    if (t < C) dbn[t] = part2[t] + part2[C + t];
     // dQ += (Gam (.) dP) K;  dK += (Gam (.) dP)^T Q + (Gam (.) dA + (Gam (.) dA)^T) K   (k = m, 64)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -784,28 +825,64 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     //     dlog alpha_m = sum_{r >= m} gamma_r dgamma_r + sum_{a >= m > b} (A (.) dA + P (.) dP)_ab
     //                    + sum_{r < m} c_r dc_r + gamma_C dgamma_C,
     // each term a sum of the contributions that actually depend on alpha_m (no cancelling pairs).
-    // The middle sum as prefix sums: R[a][m] = sum_{b < m} (A (.) dA + P (.) dP)_ab row by row (one thread a
-    // per row, into the Gam matrix's memory, read for the last time above), then sum_{a >= m} R[a][m] per m.
+    // The middle sum as prefix sums: R[a][m] = sum_{b < m} (A (.) dA + P (.) dP)_ab by rows (into the Gam
+    // matrix's memory, read for the last time above), then sum_{a >= m} R[a][m] per m.
     __syncthreads();
     float *Rs = Gs;
-    if (t < C) {
-        const int a = t;
-        float run = 0.f;
-        for (int m = 0; m < C; ++m) {
-            Rs[a * FL + m] = run;
-            run += As[a * FL + m] * dXs[a * FL + m] + Ps[a * FL + m] * dPs[a * FL + m];
+    {
+        // row a by 8 threads of 8 columns: the row's exclusive prefix sums of Z = A (.) dA + P (.) dP
+        const int a = t >> 3, q = t & 7;
+        float z[8], tot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int m = 8 * q + e;
+            z[e] = As[a * FL + m] * dXs[a * FL + m] + Ps[a * FL + m] * dPs[a * FL + m];
+            tot += z[e];
+        }
+        float inc = tot;
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+            const float y = __shfl_up(inc, off, 8);
+            if (q >= off) inc += y;
+        }
+        float run = inc - tot;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            Rs[a * FL + 8 * q + e] = run;
+            run += z[e];
         }
     }
     __syncthreads();
+    {
+        // sum_{a >= m} R[a][m] over 8 row groups of 8
+        const int m = t & 63, g = t >> 6;
+        float sp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int a = 8 * g + e;
+            if (a >= m) sp += Rs[a * FL + m];
+        }
+        part[g * C + m] = sp;
+    }
+    __syncthreads();
     if (t < C) {
+        // wave 0, lane m: sum_{r >= m} gamma_r dgamma_r and sum_{r < m} c_r dc_r as scans over the lanes
         const int m = t;
+        float s2 = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) s2 += part[g * C + m];
         float dgCt = 0.f;
         for (int w = 0; w < BK_THREADS / 64; ++w) dgCt += sdd[w];
-        float s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        for (int r = m; r < C; ++r) s1 = fmaf(gam[r], dgam2[0][r] + dgam2[1][r], s1);
-        for (int a = m; a < C; ++a) s2 += Rs[a * FL + m];
-        for (int r = 0; r < m; ++r) s3 = fmaf(cr[r], dcr2[0][r] + dcr2[1][r], s3);
-        dlg[m] = s1 + s2 + s3 + gam[C - 1] * dgCt;
+        const float g1 = gam[m] * (dgam2[0][m] + dgam2[1][m]);
+        const float c3 = cr[m] * (dcr2[0][m] + dcr2[1][m]);
+        float s1 = g1, p3 = c3;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float yd = __shfl_down(s1, off, 64), yu = __shfl_up(p3, off, 64);
+            if (m + off < 64) s1 += yd;
+            if (m >= off) p3 += yu;
+        }
+        dlg[m] = s1 + s2 + (p3 - c3) + gam[C - 1] * dgCt;
     }
     __syncthreads();
     if (t < C && t < nvalid) {
