@@ -342,10 +342,13 @@ __global__ __launch_bounds__(BC_THREADS) void k_bwd_carry(const float *__restric
 // w (row group rg = w % 4: token rows 16 rg .., column half hc = w / 4):
 //   A. stage S and dS' of the block transposed ([j][i]) and as they are
 //      ([i][j]), and dO transposed ([j][r]), in LDS as bf16 hi/lo planes;
-//   B. K S, Q S, K dS' and P^T dO for its 16 x 16 tile on 16x16x32 MFMA, then
-//      E = V - diag(gamma) K S, dU = P^T dO + diag(c) K dS', its share of
-//      dgamma; E (beta-scaled, transposed; and as is), dU into LDS;
-//   C. U = T diag(beta) E for its tile, its share of dc; U and diag(c) U into LDS;
+//   B. K S, Q S, K dS' and P^T dO for its 16 x 16 tile on 16x16x32 MFMA, formed
+//      transposed (a lane holds four consecutive columns of one token, so the
+//      [token][column] planes take 8-byte stores), then E = V - diag(gamma) K S,
+//      dU = P^T dO + diag(c) K dS', its share of dgamma; E (beta-scaled,
+//      transposed; and as is), dU into LDS;
+//   C. U = T diag(beta) E for its tile (transposed likewise), its share of dc;
+//      U and diag(c) U into LDS;
 //   D. accumulate dP += dO U^T, dTb += dU E^T (two 16 x 16 tiles each) and
 //      dQ += diag(gamma) dO S^T, dK += -diag(gamma) dE S^T + diag(c) U dS'^T
 //      (four 16-row x 16-column tiles each) in registers; the staging of A
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     for (int x = 0; x < 2; ++x) dPa[x] = dTa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < QT; ++x) dQa[x] = dKa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dgacc[4] = {0.f, 0.f, 0.f, 0.f}, dcacc[4] = {0.f, 0.f, 0.f, 0.f}, sdacc = 0.f;
+    float dgacc = 0.f, dcacc = 0.f, sdacc = 0.f;   // this lane's token ra: its dgamma, dc shares
     const bf16x8 z8 = {};
 
     for (int jb = 0; jb < NB; ++jb) {
@@ -504,8 +507,9 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
             }
         }
         __syncthreads();
-        // B. tile (rows 16 rg .., columns j0 + 16 hc ..): K S, Q S, K dS', P^T dO
-        const int jl = 16 * hc + lr;   // this lane's B column within the block
+        // B. tile (columns j0 + 16 hc .., tokens 16 rg ..), formed transposed so that a lane holds four
+        // consecutive columns of one token: (K S)^T, (Q S)^T, (K dS')^T, (P^T dO)^T
+        const int jl = 16 * hc + lr;   // this lane's A row (a column j) within the block
         f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = ks, kd = ks, pd = ks;
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
@@ -519,86 +523,87 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
             const bf16x8 sl = *reinterpret_cast<const bf16x8 *>(pl + O_ST + JB * SL + jl * SL + kk);
             const bf16x8 dh = *reinterpret_cast<const bf16x8 *>(pl + O_DST + jl * SL + kk);
             const bf16x8 dl = *reinterpret_cast<const bf16x8 *>(pl + O_DST + JB * SL + jl * SL + kk);
-            ks = mm2(kh, sh, sl, ks);
-            qs = mm2(qh, sh, sl, qs);
-            kd = mm2(kh, dh, dl, kd);
+            ks = mm2b(sh, sl, kh, ks);
+            qs = mm2b(sh, sl, qh, qs);
+            kd = mm2b(dh, dl, kh, kd);
             if constexpr (F32) {
-                ks = mfma16x16x32(kl, sh, ks);
-                qs = mfma16x16x32(ql, sh, qs);
-                kd = mfma16x16x32(kl, dh, kd);
+                ks = mfma16x16x32(sh, kl, ks);
+                qs = mfma16x16x32(sh, ql, qs);
+                kd = mfma16x16x32(dh, kl, kd);
             }
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int kk = 32 * s + 8 * lg;
-            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(pl + O_PT + ra * ML + kk);
-            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(pl + O_PT + C * ML + ra * ML + kk);
-            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(pl + O_DOT + jl * ML + kk);
-            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(pl + O_DOT + JB * ML + jl * ML + kk);
+            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(pl + O_DOT + jl * ML + kk);
+            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(pl + O_DOT + JB * ML + jl * ML + kk);
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(pl + O_PT + ra * ML + kk);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(pl + O_PT + C * ML + ra * ML + kk);
             pd = mm3(ah, al, bh, bl, pd);
         }
-        // output element jj: row r = 16 rg + 4 lg + jj, column j = j0 + 16 hc + lr
+        // element jj: column j = j0 + jq + jj (jq = 16 hc + 4 lg), token r = ra
+        const int jq = 16 * hc + 4 * lg;
         {
-            const int jg = j0 + 16 * hc + lr;
+            float vv[4] = {0.f, 0.f, 0.f, 0.f}, od[4] = {0.f, 0.f, 0.f, 0.f}, de[4] = {0.f, 0.f, 0.f, 0.f};
+            if (ra_ok) {
+                const float4 o4 = *reinterpret_cast<const float4 *>(dob + ra * rs + j0 + jq);
+                const float4 e4 = *reinterpret_cast<const float4 *>(deb + ra * rs + j0 + jq);
+                od[0] = o4.x; od[1] = o4.y; od[2] = o4.z; od[3] = o4.w;
+                de[0] = e4.x; de[1] = e4.y; de[2] = e4.z; de[3] = e4.w;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) vv[jj] = to_f32(vb[ra * rs + j0 + jq + jj]);
+            }
+            const float gr = gam[ra], br = bes[ra], cg = cr[ra];
             float ev[4], bev[4], du[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * rg + 4 * lg + jj;
-                const bool ok = r < nvalid;
-                const float vv = ok ? to_f32(vb[r * rs + jg]) : 0.f;
-                const float od = ok ? dob[r * rs + jg] : 0.f, de = ok ? deb[r * rs + jg] : 0.f;
-                ev[jj] = vv - gam[r] * ks[jj];
-                bev[jj] = bes[r] * ev[jj];
-                du[jj] = pd[jj] + cr[r] * kd[jj];
-                dgacc[jj] = fmaf(od, qs[jj], fmaf(-de, ks[jj], dgacc[jj]));
+                ev[jj] = vv[jj] - gr * ks[jj];
+                bev[jj] = br * ev[jj];
+                du[jj] = pd[jj] + cg * kd[jj];
+                dgacc = fmaf(od[jj], qs[jj], fmaf(-de[jj], ks[jj], dgacc));
             }
-            bf16 eh[4], el[4];
+            bf16 eh[4], el[4], nh[4], nl[4], uh[4], ul[4];
             split_bf16<4>(bev, eh, el);
-            const int m0 = 16 * rg + 4 * lg;
-            *reinterpret_cast<bf16x4 *>(pl + O_ET + jl * ML + m0) = pack4(eh);
-            *reinterpret_cast<bf16x4 *>(pl + O_ET + JB * ML + jl * ML + m0) = pack4(el);
-            bf16 nh[4], nl[4], uh[4], ul[4];
             split_bf16<4>(ev, nh, nl);
             split_bf16<4>(du, uh, ul);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                pl[O_EN + (m0 + jj) * JL + jl] = nh[jj];
-                pl[O_EN + C * JL + (m0 + jj) * JL + jl] = nl[jj];
-                pl[O_DU + (m0 + jj) * JL + jl] = uh[jj];
-                pl[O_DU + C * JL + (m0 + jj) * JL + jl] = ul[jj];
+                pl[O_ET + (jq + jj) * ML + ra] = eh[jj];
+                pl[O_ET + JB * ML + (jq + jj) * ML + ra] = el[jj];
             }
+            *reinterpret_cast<bf16x4 *>(pl + O_EN + ra * JL + jq) = pack4(nh);
+            *reinterpret_cast<bf16x4 *>(pl + O_EN + C * JL + ra * JL + jq) = pack4(nl);
+            *reinterpret_cast<bf16x4 *>(pl + O_DU + ra * JL + jq) = pack4(uh);
+            *reinterpret_cast<bf16x4 *>(pl + O_DU + C * JL + ra * JL + jq) = pack4(ul);
         }
         __syncthreads();
-        // C. U = T (beta E) for the tile; dc; U and diag(c) U into LDS
+        // C. U^T = (diag(beta) E)^T T^T for the tile; dc; U and diag(c) U into LDS
         {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int kk = 32 * s + 8 * lg;
-                bf16x8 ah, al;
-                ld_split8(bm.T + cid * C * C + ra * C + kk, ah, al);
-                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(pl + O_ET + jl * ML + kk);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(pl + O_ET + JB * ML + jl * ML + kk);
+                bf16x8 bh, bl;
+                ld_split8(bm.T + cid * C * C + ra * C + kk, bh, bl);
+                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(pl + O_ET + jl * ML + kk);
+                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(pl + O_ET + JB * ML + jl * ML + kk);
                 u = mm3(ah, al, bh, bl, u);
             }
             float uv[4], cu[4];
-            const int m0 = 16 * rg + 4 * lg;
+            const float cg = cr[ra];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 uv[jj] = u[jj];
-                cu[jj] = cr[m0 + jj] * u[jj];
-                dcacc[jj] = fmaf(u[jj], kd[jj], dcacc[jj]);
+                cu[jj] = cg * u[jj];
+                dcacc = fmaf(u[jj], kd[jj], dcacc);
             }
             bf16 uh[4], ul[4], ch[4], cl[4];
             split_bf16<4>(uv, uh, ul);
             split_bf16<4>(cu, ch, cl);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                pl[O_UN + (m0 + jj) * JL + jl] = uh[jj];
-                pl[O_UN + C * JL + (m0 + jj) * JL + jl] = ul[jj];
-                pl[O_CU + (m0 + jj) * JL + jl] = ch[jj];
-                pl[O_CU + C * JL + (m0 + jj) * JL + jl] = cl[jj];
-            }
+            *reinterpret_cast<bf16x4 *>(pl + O_UN + ra * JL + jq) = pack4(uh);
+            *reinterpret_cast<bf16x4 *>(pl + O_UN + C * JL + ra * JL + jq) = pack4(ul);
+            *reinterpret_cast<bf16x4 *>(pl + O_CU + ra * JL + jq) = pack4(ch);
+            *reinterpret_cast<bf16x4 *>(pl + O_CU + C * JL + ra * JL + jq) = pack4(cl);
         }
         __syncthreads();
         // D. accumulate (k = the block's 32 columns j: one MFMA k-step)
@@ -663,18 +668,16 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
         __syncthreads();   // the next block restages every plane
     }
 
-    // per-row sums of this wave's dgamma and dc shares (16 lanes of a row group hold one row each)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        float g = dgacc[jj], cc = dcacc[jj];
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            g += __shfl_xor(g, off, 64);
-            cc += __shfl_xor(cc, off, 64);
-        }
-        if (lr == 0) {
-            dgam2[hc][16 * rg + 4 * lg + jj] = g;
-            dcr2[hc][16 * rg + 4 * lg + jj] = cc;
+    // per-token sums of this wave's dgamma and dc shares (the four lane groups lg hold token ra's columns)
+    {
+        float g = dgacc, cc = dcacc;
+        g += __shfl_xor(g, 16, 64);
+        cc += __shfl_xor(cc, 16, 64);
+        g += __shfl_xor(g, 32, 64);
+        cc += __shfl_xor(cc, 32, 64);
+        if (lg == 0) {
+            dgam2[hc][ra] = g;
+            dcr2[hc][ra] = cc;
         }
     }
     {
