@@ -411,6 +411,7 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     constexpr int JB = 32, NB = D / JB, KSD = D / 32;
     constexpr int SL = D + 8, ML = C + 8, JL = JB + 8;   // LDS row strides (bf16)
     constexpr int QT = D / 32;                           // 16-column i tiles per wave in dQ, dK
+    static_assert((D / 4) * (JB / 4) + (C / 4) * (JB / 4) <= BK_THREADS, "staging threads");
     // block phase: bf16 planes
     constexpr int O_PT = 0, O_ST = O_PT + 2 * C * ML, O_DST = O_ST + 2 * JB * SL, O_DOT = O_DST + 2 * JB * SL,
                   O_ET = O_DOT + 2 * JB * ML, O_EN = O_ET + 2 * JB * ML, O_UN = O_EN + 2 * C * JL,
@@ -438,14 +439,23 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
     const float *dob = d_o + (tok0 * H + h) * D, *deb = dvin + (tok0 * H + h) * D;
     const float *Sg = s_chunks + cid * D * D, *dSg = ds_end + cid * D * D;
 
-    // P^T into LDS (split) and the chunk's scalars
-    for (int n = t; n < C * C; n += BK_THREADS) {
-        const int r = n / C, m = n % C;
-        const float x[2] = {bm.P[cid * C * C + n], 0.f};
-        bf16 hh[2], ll[2];
-        split_bf16<2>(x, hh, ll);
-        pl[O_PT + m * ML + r] = hh[0];
-        pl[O_PT + C * ML + m * ML + r] = ll[0];
+    // P^T into LDS (split) and the chunk's scalars; P by 4 x 4 blocks (rows 4 r4 .., columns 4 m4 ..), so
+    // that each transposed row piece is one 8-byte store
+    if (t < (C / 4) * (C / 4)) {
+        const int r4 = (t & 7) + 8 * ((t >> 6) & 1), m4 = ((t >> 3) & 7) + 8 * (t >> 7);
+        float x[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float4 p4 = *reinterpret_cast<const float4 *>(bm.P + cid * C * C + (4 * r4 + rr) * C + 4 * m4);
+            x[0][rr] = p4.x; x[1][rr] = p4.y; x[2][rr] = p4.z; x[3][rr] = p4.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16 hh[4], ll[4];
+            split_bf16<4>(x[c], hh, ll);
+            *reinterpret_cast<bf16x4 *>(pl + O_PT + (4 * m4 + c) * ML + 4 * r4) = pack4(hh);
+            *reinterpret_cast<bf16x4 *>(pl + O_PT + C * ML + (4 * m4 + c) * ML + 4 * r4) = pack4(ll);
+        }
     }
     if (t < C) {
         const bool ok = t < nvalid;
@@ -470,40 +480,61 @@ __global__ __launch_bounds__(BK_THREADS) void k_bwd_chunk(
 
     for (int jb = 0; jb < NB; ++jb) {
         const int j0 = jb * JB;
-        // A. S, dS' transposed ([j][i]) and dO transposed ([j][r]), split
-        for (int n = t; n < D * (JB / 4); n += BK_THREADS) {
-            const int i = n / (JB / 4), qd = n % (JB / 4);
-            const float4 sv = *reinterpret_cast<const float4 *>(Sg + (int64_t)i * D + j0 + 4 * qd);
-            const float4 dv = *reinterpret_cast<const float4 *>(dSg + (int64_t)i * D + j0 + 4 * qd);
-            const float xs[4] = {sv.x, sv.y, sv.z, sv.w}, xd[4] = {dv.x, dv.y, dv.z, dv.w};
-            sdacc = fmaf(xs[0], xd[0], fmaf(xs[1], xd[1], fmaf(xs[2], xd[2], fmaf(xs[3], xd[3], sdacc))));
-            bf16 sh[4], sl[4], dh[4], dl[4];
-            split_bf16<4>(xs, sh, sl);
-            split_bf16<4>(xd, dh, dl);
-            *reinterpret_cast<bf16x4 *>(pl + O_SN + i * JL + 4 * qd) = pack4(sh);
-            *reinterpret_cast<bf16x4 *>(pl + O_SN + D * JL + i * JL + 4 * qd) = pack4(sl);
-            *reinterpret_cast<bf16x4 *>(pl + O_DSN + i * JL + 4 * qd) = pack4(dh);
-            *reinterpret_cast<bf16x4 *>(pl + O_DSN + D * JL + i * JL + 4 * qd) = pack4(dl);
+        // A. S, dS' as they are ([i][j]) and transposed ([j][i]), and dO transposed ([j][r]), split, by 4 x 4
+        // blocks (rows 4 i4 .., columns 4 qd ..): every plane row piece is one 8-byte store
+        if (t < (D / 4) * (JB / 4)) {
+            const int i4 = (t & 7) + 8 * (t >> 6), qd = (t >> 3) & 7;
+            float xs[4][4], xd[4][4];   // [column c][row rr]
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 4 * qd + e;
-                pl[O_ST + j * SL + i] = sh[e];
-                pl[O_ST + JB * SL + j * SL + i] = sl[e];
-                pl[O_DST + j * SL + i] = dh[e];
-                pl[O_DST + JB * SL + j * SL + i] = dl[e];
+            for (int rr = 0; rr < 4; ++rr) {
+                const int64_t o = (int64_t)(4 * i4 + rr) * D + j0 + 4 * qd;
+                const float4 sv = *reinterpret_cast<const float4 *>(Sg + o);
+                const float4 dv = *reinterpret_cast<const float4 *>(dSg + o);
+                const float sr[4] = {sv.x, sv.y, sv.z, sv.w}, dr[4] = {dv.x, dv.y, dv.z, dv.w};
+                bf16 sh[4], sl[4], dh[4], dl[4];
+                split_bf16<4>(sr, sh, sl);
+                split_bf16<4>(dr, dh, dl);
+                const int i = 4 * i4 + rr;
+                *reinterpret_cast<bf16x4 *>(pl + O_SN + i * JL + 4 * qd) = pack4(sh);
+                *reinterpret_cast<bf16x4 *>(pl + O_SN + D * JL + i * JL + 4 * qd) = pack4(sl);
+                *reinterpret_cast<bf16x4 *>(pl + O_DSN + i * JL + 4 * qd) = pack4(dh);
+                *reinterpret_cast<bf16x4 *>(pl + O_DSN + D * JL + i * JL + 4 * qd) = pack4(dl);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    xs[c][rr] = sr[c];
+                    xd[c][rr] = dr[c];
+                    sdacc = fmaf(sr[c], dr[c], sdacc);
+                }
             }
-        }
-        for (int n = t; n < C * (JB / 4); n += BK_THREADS) {
-            const int r = n / (JB / 4), qd = n % (JB / 4);
-            float4 ov = {0.f, 0.f, 0.f, 0.f};
-            if (r < nvalid) ov = *reinterpret_cast<const float4 *>(dob + r * rs + j0 + 4 * qd);
-            const float xo[4] = {ov.x, ov.y, ov.z, ov.w};
-            bf16 oh[4], ol[4];
-            split_bf16<4>(xo, oh, ol);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pl[O_DOT + (4 * qd + e) * ML + r] = oh[e];
-                pl[O_DOT + JB * ML + (4 * qd + e) * ML + r] = ol[e];
+            for (int c = 0; c < 4; ++c) {
+                bf16 sh[4], sl[4], dh[4], dl[4];
+                split_bf16<4>(xs[c], sh, sl);
+                split_bf16<4>(xd[c], dh, dl);
+                const int j = 4 * qd + c;
+                *reinterpret_cast<bf16x4 *>(pl + O_ST + j * SL + 4 * i4) = pack4(sh);
+                *reinterpret_cast<bf16x4 *>(pl + O_ST + JB * SL + j * SL + 4 * i4) = pack4(sl);
+                *reinterpret_cast<bf16x4 *>(pl + O_DST + j * SL + 4 * i4) = pack4(dh);
+                *reinterpret_cast<bf16x4 *>(pl + O_DST + JB * SL + j * SL + 4 * i4) = pack4(dl);
+            }
+        } else if (t >= BK_THREADS - (C / 4) * (JB / 4)) {
+            // dO of the block's columns, transposed, by 4 x 4 blocks (tokens 4 r4 .., columns 4 qd ..)
+            const int u = t - (BK_THREADS - (C / 4) * (JB / 4));
+            const int r4 = (u & 7) + 8 * (u >> 6), qd = (u >> 3) & 7;
+            float xo[4][4];   // [column c][token rr]
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 4 * r4 + rr;
+                float4 ov = {0.f, 0.f, 0.f, 0.f};
+                if (r < nvalid) ov = *reinterpret_cast<const float4 *>(dob + r * rs + j0 + 4 * qd);
+                xo[0][rr] = ov.x; xo[1][rr] = ov.y; xo[2][rr] = ov.z; xo[3][rr] = ov.w;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                bf16 oh[4], ol[4];
+                split_bf16<4>(xo[c], oh, ol);
+                *reinterpret_cast<bf16x4 *>(pl + O_DOT + (4 * qd + c) * ML + 4 * r4) = pack4(oh);
+                *reinterpret_cast<bf16x4 *>(pl + O_DOT + JB * ML + (4 * qd + c) * ML + 4 * r4) = pack4(ol);
             }
         }
         __syncthreads();
