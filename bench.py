@@ -182,18 +182,42 @@ def bench_prefill(args, w, torch, gl, synth, warmup):
             gl.gdn_timer_destroy(t)
         return ms_total, wall, per_stage
 
-    # The timed region carries dispatch events on every fifth projection GEMM launch only (each armed dispatch
-    # costs the GPU a few microseconds; 5 is coprime to the 4 loops, so the sample covers every loop evenly); the
-    # per-stage breakdown comes from a second pass with every launch of every stage armed.
-    stride = 5 if args.steps * w.T >= 20 else 1
-    ms_total, wall, timed_stages = timed_pass(["project"], stride)
-    _, _, per_stage = timed_pass(list(stages))
+    # Where gdn_loop_prefill runs this shape as a pipeline over pieces (its automatic setting), the step time is
+    # that of the pipelined call, timed with no dispatch events armed; the kernels then share the CUs, so their
+    # per-launch times and rooflines come from the same call run loop by loop (gdn_loop_prefill_set_pieces(-1)).
+    pipe = None
+    piece = gl.gdn_loop_prefill_pieces(desc)
+    if piece > 0:
+        ms_pipe, wall, _ = timed_pass([])
+        gl.gdn_loop_prefill_set_pieces(-1)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        per_seq, t0 = 0, 0
+        while t0 < w.L:   # the runs gdn_loop_prefill forms: a last run under 1024 tokens joins the one before
+            n = min(piece, w.L - t0)
+            t0 += n if w.L - (t0 + n) >= 1024 else w.L - t0
+            per_seq += 1
+        pipe = dict(ms_step=ms_pipe / args.steps, wall_s=wall, piece_tokens=piece, pieces_per_sequence=per_seq)
+    try:
+        # The timed region carries dispatch events on every fifth projection GEMM launch only (each armed
+        # dispatch costs the GPU a few microseconds; 5 is coprime to the 4 loops, so the sample covers every
+        # loop evenly); the per-stage breakdown comes from a second pass with every launch of every stage armed.
+        stride = 5 if args.steps * w.T >= 20 else 1
+        ms_total, wall, timed_stages = timed_pass(["project"], stride)
+        _, _, per_stage = timed_pass(list(stages))
+    finally:
+        gl.gdn_loop_prefill_set_pieces(0)
     per_stage["project"] = timed_stages["project"]
     ms_step = ms_total / args.steps
     tokens = w.B * w.L
     for v in per_stage.values():
         v["share"] = v["avg_ms"] * w.T / ms_step
-    return dict(ms_step=ms_step, wall_s=wall, tokens=tokens, per_stage=per_stage)
+    if pipe is None:
+        return dict(ms_step=ms_step, wall_s=wall, tokens=tokens, per_stage=per_stage)
+    return dict(ms_step=pipe["ms_step"], wall_s=pipe["wall_s"], tokens=tokens, per_stage=per_stage,
+                pipeline=dict(piece_tokens=pipe["piece_tokens"], pieces_per_sequence=pipe["pieces_per_sequence"],
+                              loop_by_loop_ms_per_step=ms_step))
 
 
 def bench_decode(args, torch, gl, synth):
@@ -612,6 +636,11 @@ def prefill_record(w, pf):
                        "stages": {k: {"avg_launch_us": v["avg_ms"] * 1e3, "share_of_step": v["share"]}
                                   for k, v in st.items()}},
     }
+    if "pipeline" in pf:
+        rec["pipeline"] = dict(pf["pipeline"], note=(
+            "the step runs as a pipeline over pieces of each sequence (one stream of projections and chunk preps, "
+            "a carry stream per loop); the kernel rooflines and stage times are those of the same call run loop "
+            "by loop, and the stage shares are of that call's step"))
     if "scan_carry" in st:
         bpl = carry_bytes_per_step(w) * tokens / w.T
         gbs = bpl / (st["scan_carry"]["avg_ms"] * 1e-3) / 1e9

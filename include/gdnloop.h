@@ -219,6 +219,42 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
                             const float *rho, float *h_out, float *states_out,
                             float *h_loops, void *ws, size_t ws_bytes, void *stream);
 
+/* How gdn_loop_prefill orders its work (a process-wide setting).
+ * Passage: LT2 Section 2 "LT2" paragraph: loop tau's projections of a token
+ * need only h^(tau-1) of that token, and its scan state needs only the tokens
+ * before it; so loop tau+1 can start on the first tokens of a prompt while
+ * loop tau is still scanning later ones (a wavefront over loops and pieces).
+ * With pieces, gdn_loop_prefill splits each sequence into runs of whole
+ * chunks of about `tokens` tokens (a multiple of 256, at least 1024; a last
+ * run shorter than 1024 joins the one before).  The projections and chunk
+ * preparations of all loops run on one internal stream and each loop's
+ * carries on another (three carry streams, shared round-robin beyond three
+ * loops); loop tau+1's projection of piece j waits (a stream wait on an
+ * event, never a spin) for loop tau's carry of piece j, so it runs on the CUs
+ * that the carries leave idle.  The call still orders against `stream` as one
+ * operation: its work starts after what was queued on `stream` before it,
+ * and what is queued there after it waits for all of it.  Every output is
+ * the same as in the loop-by-loop order up to the carry's slice width, which
+ * each launch chooses by its own workgroup count (the rounding of the
+ * state's sums can differ in the last bits).  Pieces apply to bf16 workloads
+ * of T >= 2 whose projection forms the gate partials (2H <= 32) and whose
+ * sequences give at least two pieces (L >= 2048, or B >= 2 with L >= 1024);
+ * gdn_workspace_bytes(GDN_OP_LOOP_PREFILL) includes the pieces' state buffer
+ * for those shapes whatever the setting.  Calls from several host threads on
+ * one device take turns while they enqueue.
+ *   tokens  -1: loop by loop always; 0 (the default): two pieces per
+ *           sequence where L >= 16384 and the whole call's carry would fill
+ *           at most half the CUs (one workgroup per sequence, head and
+ *           16-column slice); > 0: pieces of that many tokens wherever they
+ *           apply
+ * Errors: GDN_ERR_SHAPE for tokens < -1. */
+gdn_status gdn_loop_prefill_set_pieces(int tokens);
+
+/* The piece length gdn_loop_prefill would use for `desc` under the current
+ * setting (0: loop by loop).  Errors: the usual descriptor errors,
+ * GDN_ERR_NULL for a NULL `tokens`. */
+gdn_status gdn_loop_prefill_pieces(const gdn_desc *desc, int *tokens);
+
 /* T loops with per-token adaptive halting (ACT).
  * Passage: LT2 Appendix A: after loop tau a linear layer with a sigmoid gives
  * each position a halting probability p_t = sigmoid(w_halt . h_t^(tau) +

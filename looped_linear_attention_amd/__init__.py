@@ -29,6 +29,7 @@ __all__ = [
     "lib_path", "load", "EXPORTED", "workspace", "workspace_view", "block_workspace", "block_workspace_view",
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act",
+    "gdn_loop_prefill_set_pieces", "gdn_loop_prefill_pieces",
     "gdn_loop_decode", "gdn_loop_decode_noalloc", "gdn_loop_backward", "gdn_block_packed_bytes", "gdn_block_pack",
     "gdn_block_workspace_bytes", "gdn_block_workspace_region", "gdn_block_forward", "gdn_block_loop_prefill",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride",
@@ -48,6 +49,7 @@ GDN_BWS_X1, GDN_BWS_O, GDN_BWS_Z, GDN_BWS_H1, GDN_BWS_X2, GDN_BWS_U = range(16, 
 EXPORTED = [
     "gdn_weights_packed_bytes", "gdn_weights_pack", "gdn_workspace_bytes", "gdn_workspace_region", "gdn_project",
     "gdn_scan_prefill", "gdn_scan_backward", "gdn_scan_decode", "gdn_loop_prefill", "gdn_loop_prefill_act",
+    "gdn_loop_prefill_set_pieces", "gdn_loop_prefill_pieces",
     "gdn_loop_decode", "gdn_loop_decode_noalloc", "gdn_loop_backward", "gdn_block_packed_bytes", "gdn_block_pack",
     "gdn_block_workspace_bytes", "gdn_block_workspace_region", "gdn_block_forward", "gdn_block_loop_prefill",
     "gdn_status_string", "gdn_last_error", "gdn_version", "gdn_timer_create", "gdn_timer_set_stride",
@@ -106,6 +108,8 @@ def load():
         "gdn_loop_prefill": [D, P, P, P, P, P, P, P, S, P],
         "gdn_loop_decode": [D, P, P, P, P, P, P, S, P],
         "gdn_loop_prefill_act": [D, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, P, P, S, P],
+        "gdn_loop_prefill_set_pieces": [I],
+        "gdn_loop_prefill_pieces": [D, ctypes.POINTER(I)],
         "gdn_loop_decode_noalloc": [D, P, P, P, P, P, P],
         "gdn_loop_backward": [D] + [P] * 13 + [S, P],
         "gdn_block_packed_bytes": [D, I, ctypes.POINTER(S)],
@@ -382,6 +386,18 @@ def gdn_loop_prefill(desc, h0, Wpack, rho, h_out, states_out, h_loops, ws, strea
              optional=True),
         _ptr(h_loops, "h_loops", torch.float32, T * BL * d, optional=True), wp, wn,
         _stream(stream)))
+
+
+def gdn_loop_prefill_set_pieces(tokens: int) -> None:
+    """-1: loops one after another; 0: automatic; > 0: pieces of about that many tokens (process-wide)."""
+    _check(load().gdn_loop_prefill_set_pieces(int(tokens)))
+
+
+def gdn_loop_prefill_pieces(desc) -> int:
+    """Tokens per piece that gdn_loop_prefill would use for desc now (0: loop by loop)."""
+    n = ctypes.c_int()
+    _check(load().gdn_loop_prefill_pieces(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
 
 
 def gdn_loop_prefill_act(desc, h0, Wpack, rho, w_halt, b_halt, eps, h_out, halt_loop, ponder, ws, stream=None):

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -135,6 +136,29 @@ static int lb_dw_split(int d, int64_t P, bool f32) {
     return f32 ? 1 : lb_split(((int64_t)(d + 383) / 384) * ((P + 255) / 256), LB_DW_SPLIT, 0.05);
 }
 
+// ---- the loop prefill as a pipeline over pieces ------------------------------
+// A piece is one sequence's run of whole chunks (at least PIPE_MIN_PIECE
+// tokens, so that its projection takes the same wide GEMM as the whole call).
+// Every step of a loop is local to its piece except the state, which crosses
+// from piece to piece of a sequence; so loop tau+1 can project and scan piece
+// j as soon as loop tau has finished piece j, while loop tau goes on with
+// piece j+1.  The projections and chunk preps of all loops run on one stream,
+// each loop's carries on a stream of their own, so that the projection of the
+// next piece runs on the CUs that a carry leaves idle; the only waits are
+// stream waits on events, so no kernel ever spins on another.
+constexpr int PIPE_MIN_PIECE = 1024;
+constexpr int PIPE_AUTO_MIN_L = 16384;   // shortest sequence the automatic setting splits
+constexpr int PIPE_STREAMS = 4;
+int g_pipe_piece = 0;   // gdn_loop_prefill_set_pieces: 0 automatic, -1 off, > 0 tokens per piece
+
+// bf16 workloads of at least two loops whose projection forms the gate
+// partials (P > 0), with pieces to form: more than one sequence, or one
+// sequence of at least two pieces.
+bool pipeline_capable(const gdn_desc *d, int P) {
+    return d->act == GDN_BF16 && d->T >= 2 && P > 0 && d->L >= PIPE_MIN_PIECE &&
+           (d->B >= 2 || d->L >= 2 * PIPE_MIN_PIECE);
+}
+
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
     size_t q = 0, k = 0, v = 0, alpha = 0, beta = 0, zp = 0, W = 0, M = 0, g = 0, x = 0, sc = 0, dse = 0, bm = 0;
@@ -145,6 +169,7 @@ struct Layout {
     size_t Y = 0, YT = 0, XT = 0, WT = 0, gq = 0, gk = 0, gv = 0, gal = 0, gbe = 0, dhA = 0, dhB = 0, dW = 0, part = 0;
     size_t Yhl = 0;   // bf16 workloads: dY as bf16 hi and lo planes (the transpose's planes reuse YT)
     size_t Gp = 0;    // bf16 workloads: the split-k partial sums of dY W
+    size_t st = 0;    // the pipelined loop prefill: each (loop, sequence)'s state between pieces [T][B][H][D][D]
     size_t total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
@@ -213,6 +238,9 @@ Layout layout(const gdn_desc *d, int op) {
         lo.rows = take(tokens * 4);   // positions re-projected in the next loop, and their count
         lo.rows_count = take(4);
     }
+    // shapes the loop prefill can run as a pipeline of pieces (below) carry
+    // each (loop, sequence)'s state from one piece to the next through here
+    if (op == GDN_OP_LOOP_PREFILL && !act && pipeline_capable(d, lo.P)) lo.st = take((size_t)d->T * bh * D * D * 4);
     lo.total = off;
     return lo;
 }
@@ -365,7 +393,8 @@ gdn_status gdn_project(const gdn_desc *desc, const void *x, const void *Wpack, v
 // writes the chunk matrices of the backward pass there.
 static gdn_status scan_chunks(const gdn_desc *d, const void *q, const void *k, const void *v,
                               GateSrc gates, const float *s_init, float *s_final, CarryOut out, void *ws,
-                              const Layout &lo, hipStream_t s, float *bwd_mats = nullptr) {
+                              const Layout &lo, hipStream_t s, float *bwd_mats = nullptr,
+                              hipStream_t carry_stream = nullptr, hipEvent_t prep_done = nullptr) {
     const bool f32 = d->act == GDN_F32;
     ChunkWs cw{(float *)at(ws, lo.W), (float *)at(ws, lo.M), (float *)at(ws, lo.g)};
     if (bwd_mats) cw.bwd = bwd_prep_out(bwd_mats, (int64_t)d->B * d->H * ((d->L + 63) / 64), d->dk);
@@ -373,8 +402,15 @@ static gdn_status scan_chunks(const gdn_desc *d, const void *q, const void *k, c
         return launch_scan_prep(f32, d->B, d->L, d->H, d->dk, q, k, gates, cw, s);
     });
     if (e != hipSuccess) return hip_fail(e, "chunk prep launch");
-    e = timed(GDN_STAGE_SCAN_CARRY, s, [&] {
-        return launch_scan_carry(f32, d->B, d->L, d->H, d->dk, q, k, v, cw, s_init, s_final, out, s);
+    // the carry on a stream of its own (the pipelined loop prefill): it waits for the prep's event
+    hipStream_t cs = s;
+    if (carry_stream && carry_stream != s) {
+        if ((e = hipEventRecord(prep_done, s)) != hipSuccess || (e = hipStreamWaitEvent(carry_stream, prep_done, 0)) != hipSuccess)
+            return hip_fail(e, "carry stream wait");
+        cs = carry_stream;
+    }
+    e = timed(GDN_STAGE_SCAN_CARRY, cs, [&] {
+        return launch_scan_carry(f32, d->B, d->L, d->H, d->dk, q, k, v, cw, s_init, s_final, out, cs);
     });
     if (e != hipSuccess) return hip_fail(e, "carry launch");
     return GDN_OK;
@@ -912,6 +948,184 @@ static gdn_status loop_prefill_impl(const gdn_desc *desc, const void *h0, const 
     return GDN_OK;
 }
 
+// ---- the pipelined loop prefill ----------------------------------------------
+struct PipeRes {
+    hipStream_t st[PIPE_STREAMS] = {};
+    hipEvent_t fork = nullptr, done[PIPE_STREAMS] = {};
+    std::vector<hipEvent_t> ev;   // two per loop: the end of loop tau's carry of piece j in ev[2 tau + j % 2]
+    std::vector<hipEvent_t> evp;  // two per loop: the end of loop tau's chunk prep of piece j
+};
+std::mutex g_pipe_mu;   // one submission at a time: the streams and events are shared per device
+PipeRes g_pipe_res[64];
+
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Tokens per piece for this call (0: the loops run one after another).
+int pipe_piece_tokens(const gdn_desc *d, const Layout &lo) {
+    if (!lo.st || g_pipe_piece < 0) return 0;
+    int want = g_pipe_piece;
+    if (want == 0) {
+        // automatic: two pieces per sequence, where the whole call's carry would
+        // leave at least half the CUs idle (one 16-column slice workgroup per
+        // CU) and the sequences are long enough for the projection of one loop
+        // to hide behind the carry of another (measured on MI355X at 16 heads
+        // of 128: one sequence of 16384 tokens 3.55 -> 3.07 ms, of 32768 tokens
+        // 6.89 -> 5.79 ms; pieces of 4096 or 8192 gained less, and at 4096
+        // tokens, or where the carry fills the CUs, pieces lose)
+        if ((int64_t)d->B * d->H * (d->dk / 16) * 2 > device_cus() || d->L < PIPE_AUTO_MIN_L) return 0;
+        want = (d->L + 1) / 2;
+    }
+    want = std::max(PIPE_MIN_PIECE, (int)std::min<int64_t>(((int64_t)want + 255) / 256 * 256, INT32_MAX / 2));
+    if (want >= d->L && d->B == 1) return 0;   // a single piece: nothing to overlap
+    return std::min(want, d->L);
+}
+
+// Per-device streams (non-blocking, default priority) and events, made on
+// first use and kept until the process ends.
+hipError_t pipe_resources(int T, PipeRes **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    PipeRes &r = g_pipe_res[dev];
+    if (!r.fork) {
+        for (int i = 0; i < PIPE_STREAMS; ++i) {
+            if ((e = hipStreamCreateWithFlags(&r.st[i], hipStreamNonBlocking)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming)) != hipSuccess) return e;
+        }
+        if ((e = hipEventCreateWithFlags(&r.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    while ((int)r.ev.size() < 2 * T) {
+        hipEvent_t ev;
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
+        r.ev.push_back(ev);
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
+        r.evp.push_back(ev);
+    }
+    *out = &r;
+    return hipSuccess;
+}
+
+// The loops over pieces in wavefront order: step w issues piece w - tau of
+// every loop tau, so each event is recorded (host order) before the wait on
+// it, and any mapping of the streams onto hardware queues keeps the order of
+// the dependencies.  Edges: loop tau's projection of piece j waits for loop
+// tau-1's carry of piece j (its h rows and the q/k/v, gate-partial and chunk
+// sub-regions it overwrites); loop tau's carry of piece j waits for the prep
+// of piece j and follows its carry of piece j-1 on its stream (the state).  Within a piece the launches are those of the whole call
+// (projection with gate partials, chunk prep, carry with the loop residual)
+// on that piece's rows, its own gate-partial and chunk-matrix sub-regions, and
+// the state of the previous piece of its sequence as the carry's start.  The
+// arithmetic of every row is that of the whole call; only the carry's slice
+// width may differ (it is chosen by the workgroup count of each launch).
+static gdn_status loop_prefill_pipelined(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,
+                                         float *h_out, float *states_out, float *h_loops, void *ws, const Layout &lo,
+                                         hipStream_t s, int piece) {
+    const int B = desc->B, L = desc->L, H = desc->H, D = desc->dk, d = desc->d, T = desc->T;
+    const int64_t M = (int64_t)B * L, tokd = M * d, Nc = (L + CHUNK - 1) / CHUNK;
+    const int64_t state_elems = (int64_t)B * H * D * D, seq_state = (int64_t)H * D * D;
+    struct Piece { int b, t0, len; bool first, last; int64_t cu; };   // cu: chunk units (b, h, c) before it
+    std::vector<Piece> pieces;
+    for (int b = 0; b < B; ++b)
+        for (int t0 = 0; t0 < L;) {
+            int len = std::min(piece, L - t0);
+            if (L - (t0 + len) < PIPE_MIN_PIECE) len = L - t0;   // no short last piece
+            pieces.push_back(Piece{b, t0, len, t0 == 0, t0 + len == L, 0});
+            t0 += len;
+        }
+    int64_t cu = 0;
+    for (Piece &p : pieces) {
+        p.cu = cu;
+        cu += (int64_t)H * ((p.len + CHUNK - 1) / CHUNK);
+    }
+    if (cu != (int64_t)B * H * Nc) return fail(GDN_ERR_SHAPE, "pieces do not tile the chunks");
+
+    std::lock_guard<std::mutex> lock(g_pipe_mu);
+    PipeRes *r = nullptr;
+    hipError_t e = pipe_resources(T, &r);
+    if (e != hipSuccess) return hip_fail(e, "pipeline streams");
+    // stream 0: every projection and chunk prep, in submission order; streams
+    // 1 .. NC: the carries, loop tau's on stream 1 + tau % NC
+    const int NC = std::min(T, PIPE_STREAMS - 1), NS = NC + 1;
+    hipStream_t ps = r->st[0];
+    if ((e = hipEventRecord(r->fork, s)) != hipSuccess) return hip_fail(e, "pipeline fork");
+    for (int i = 0; i < NS; ++i)
+        if ((e = hipStreamWaitEvent(r->st[i], r->fork, 0)) != hipSuccess) return hip_fail(e, "pipeline fork");
+
+    const size_t ab = 2;   // bf16 activations
+    char *q = at(ws, lo.q), *k = at(ws, lo.k), *v = at(ws, lo.v);
+    float *al = (float *)at(ws, lo.alpha), *be = (float *)at(ws, lo.beta);
+    float *zp = (float *)at(ws, lo.zp), *stb = (float *)at(ws, lo.st);
+    bf16 *xbuf = (bf16 *)at(ws, lo.x);
+    const int npc = (int)pieces.size();
+    gdn_status st = GDN_OK;
+    for (int w = 0; w < npc + T - 1 && st == GDN_OK; ++w) {
+        for (int tau = 0; tau < T && st == GDN_OK; ++tau) {
+            const int j = w - tau;
+            if (j < 0 || j >= npc) continue;
+            const Piece &p = pieces[j];
+            hipStream_t cs = r->st[1 + tau % NC];
+            const bool last = tau == T - 1;
+            const int64_t tok0 = (int64_t)p.b * L + p.t0;   // first row of the piece
+            if (tau > 0 && (e = hipStreamWaitEvent(ps, r->ev[2 * (tau - 1) + j % 2], 0)) != hipSuccess) {
+                st = hip_fail(e, "pipeline wait");
+                break;
+            }
+            float *hdst = (h_loops ? h_loops + tau * tokd : h_out) + tok0 * d;
+            const void *x = tau == 0 ? (const void *)((const char *)h0 + tok0 * d * ab) : (const void *)(xbuf + tok0 * d);
+            const void *hprev = tau == 0 ? (const void *)((const char *)h0 + tok0 * d * ab)
+                                         : (const void *)((h_loops ? h_loops + (tau - 1) * tokd : h_out) + tok0 * d);
+            const int64_t qo = tok0 * H * D * ab;
+            float *zpp = zp + (int64_t)lo.P * 2 * H * tok0;   // the piece's partials [P][2H][len]
+            e = project(false, p.len, d, H, D, x, Wpack, q + qo, k + qo, v + qo, al + tok0 * H, be + tok0 * H,
+                        desc->alpha_lo, desc->norm_eps, zpp, ps);
+            if (e != hipSuccess) {
+                st = hip_fail(e, "projection launch");
+                break;
+            }
+            gdn_desc pd = *desc;
+            pd.B = 1;
+            pd.L = p.len;
+            Layout pl = lo;   // the piece's chunk matrices follow those of the pieces before it
+            pl.W = lo.W + (size_t)p.cu * D * CHUNK * 4;
+            pl.M = lo.M + (size_t)p.cu * CHUNK * CHUNK * 4;
+            pl.g = lo.g + (size_t)p.cu * CHUNK * 4;
+            float *sbuf = stb + ((int64_t)tau * B + p.b) * seq_state;
+            const float *s_init = p.first ? nullptr : sbuf;
+            float *s_final = p.last ? (states_out ? states_out + tau * state_elems + p.b * seq_state : nullptr) : sbuf;
+            CarryOut out{nullptr, hprev, tau == 0, rho + (int64_t)tau * d, hdst, last ? nullptr : xbuf + tok0 * d,
+                         nullptr, nullptr};
+            st = scan_chunks(&pd, q + qo, k + qo, v + qo,
+                             GateSrc{al + tok0 * H, be + tok0 * H, zpp, lo.P, desc->alpha_lo, al + tok0 * H,
+                                     be + tok0 * H},
+                             s_init, s_final, out, ws, pl, ps, nullptr, cs, r->evp[2 * tau + j % 2]);
+            if (st != GDN_OK) break;
+            if (!last && (e = hipEventRecord(r->ev[2 * tau + j % 2], cs)) != hipSuccess) st = hip_fail(e, "pipeline event");
+        }
+    }
+    // join (also after a failed launch, so that the caller's stream never runs ahead of work already queued)
+    for (int i = 0; i < NS; ++i) {
+        if ((e = hipEventRecord(r->done[i], r->st[i])) != hipSuccess) return st != GDN_OK ? st : hip_fail(e, "pipeline join");
+        if ((e = hipStreamWaitEvent(s, r->done[i], 0)) != hipSuccess) return st != GDN_OK ? st : hip_fail(e, "pipeline join");
+    }
+    if (st != GDN_OK) return st;
+    if (h_loops) {
+        e = hipMemcpyAsync(h_out, h_loops + (T - 1) * tokd, tokd * sizeof(float), hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "copy of h^(T)");
+    }
+    return GDN_OK;
+}
+
 gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wpack,
                             const float *rho, float *h_out, float *states_out, float *h_loops,
                             void *ws, size_t ws_bytes, void *stream) {
@@ -925,7 +1139,26 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
     if (!ws || ws_bytes < lo.total)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
     if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
+    const int piece = pipe_piece_tokens(desc, lo);
+    if (piece > 0)
+        return loop_prefill_pipelined(desc, h0, Wpack, rho, h_out, states_out, h_loops, ws, lo, (hipStream_t)stream,
+                                      piece);
     return loop_prefill_impl(desc, h0, Wpack, rho, h_out, states_out, h_loops, ws, lo, (hipStream_t)stream, nullptr);
+}
+
+gdn_status gdn_loop_prefill_set_pieces(int tokens) {
+    if (tokens < -1) return fail(GDN_ERR_SHAPE, "tokens per piece must be -1, 0 or positive (got %d)", tokens);
+    g_pipe_piece = tokens;
+    return GDN_OK;
+}
+
+gdn_status gdn_loop_prefill_pieces(const gdn_desc *desc, int *tokens) {
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if ((st = check_prefill_grid(desc)) != GDN_OK) return st;
+    if (!tokens) return fail(GDN_ERR_NULL, "tokens is NULL");
+    *tokens = pipe_piece_tokens(desc, layout(desc, GDN_OP_LOOP_PREFILL));
+    return GDN_OK;
 }
 
 gdn_status gdn_loop_prefill_act(const gdn_desc *desc, const void *h0, const void *Wpack, const float *rho,

@@ -851,8 +851,8 @@ struct OutIn {
 template <int D, typename TIn, int RES, bool XN, int XM>
 __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, int L, int H, int Nc,
-    const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
-    float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
+    const float *W, const float *__restrict__ M, const float *g, const float *s_init,
+    float *s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
     float *h_out, bf16 *x_next, float *__restrict__ s_chunks, const int *__restrict__ halted) {
     using G = CarryCfg<D, TIn>;
     constexpr int NT = G::NT, RW = G::RW, KW = G::KW, STG = G::STG;
@@ -1250,8 +1250,8 @@ struct CarryW {
 template <int RES, bool XN, int XM>
 __global__ __launch_bounds__(CARRY_THREADS) void k_scan_carry_w(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v, int L, int H, int Nc,
-    const float *W, const float *__restrict__ M, const float *g, const float *__restrict__ s_init,
-    float *__restrict__ s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
+    const float *W, const float *__restrict__ M, const float *g, const float *s_init,
+    float *s_final, float *__restrict__ o, const void *h_prev, const float *__restrict__ rho,
     float *h_out, bf16 *x_next, float *__restrict__ s_chunks, const int *__restrict__ halted) {
     using G = CarryW;
     using KT = KTile<128, bf16>;

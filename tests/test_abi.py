@@ -319,3 +319,59 @@ def test_block_sizes_and_rejections(lib):
                                       good, 1 << 40, None) == -2   # no layers
     st = lib.gdn_block_forward(ctypes.byref(desc), 256, good, good, ctypes.c_void_p(0x200000), good, 16, None)
     assert st == -4 and "workspace" in gl.gdn_last_error()
+
+
+def test_loop_prefill_pieces_setting():
+    """The process-wide piece setting of gdn_loop_prefill: -1 loop by loop, 0 automatic (two pieces per sequence
+    where L >= 16384 and the whole call's 16-column carry would fill at most half of the 256 CUs), > 0 pieces of
+    that many tokens rounded up to a multiple of 256 and at least 1024; a single piece of a single sequence runs
+    loop by loop; shapes the pieces do not apply to (fp32, T = 1, 2H > 32, sequences too short) always run loop
+    by loop."""
+    pieces = lambda *a, **k: gl.gdn_loop_prefill_pieces(gl.make_desc(*a, **k))
+    lib = gl.load()
+    assert lib.gdn_loop_prefill_set_pieces(-2) == -2
+    try:
+        gl.gdn_loop_prefill_set_pieces(0)
+        assert pieces(1, 32768, 16, 128, 128) == 16384    # 128 carry workgroups: two pieces
+        assert pieces(1, 16384, 16, 128, 128) == 8192
+        assert pieces(1, 20000, 16, 128, 128) == 10240    # half, rounded up to 256
+        assert pieces(1, 16383, 16, 128, 128) == 0        # shorter than 16384
+        assert pieces(1, 4096, 16, 128, 128) == 0
+        assert pieces(4, 32768, 16, 128, 128) == 0        # 512 carry workgroups: loop by loop
+        assert pieces(1, 32768, 16, 128, 128, T=1) == 0
+        assert pieces(1, 32768, 16, 128, 128, act=gl.GDN_F32) == 0
+        assert pieces(1, 32768, 17, 128, 128) == 0        # 2H > 32: gates not from the GEMM's partials
+        assert pieces(1, 2048, 16, 128, 128) == 0         # one piece
+        gl.gdn_loop_prefill_set_pieces(1000)
+        assert pieces(1, 4096, 16, 128, 128) == 1024
+        assert pieces(4, 8192, 16, 128, 128) == 1024
+        assert pieces(2, 1100, 16, 128, 128) == 1024      # one piece per sequence (the 76 left join it)
+        assert pieces(1, 1100, 16, 128, 128) == 0
+        gl.gdn_loop_prefill_set_pieces(5000)
+        assert pieces(1, 4096, 16, 128, 128) == 0         # longer than the sequence
+        assert pieces(3, 4096, 16, 128, 128) == 4096
+        gl.gdn_loop_prefill_set_pieces(-1)
+        assert pieces(1, 32768, 16, 128, 128) == 0
+    finally:
+        gl.gdn_loop_prefill_set_pieces(0)
+
+
+def test_loop_prefill_pieces_workspace():
+    """Shapes the pieces apply to add one state per (loop, sequence, head) [T][B][H][dk][dv] fp32 at the end of
+    the loop prefill's workspace, whatever the setting; the halting call's workspace does not have it."""
+    up = lambda x: (x + 255) // 256 * 256
+    for B, L in [(1, 2048), (2, 1024), (1, 4096)]:
+        H, D, T = 16, 128, 4
+        tok, Nc, P = B * L, (L + 63) // 64, (H * D + 127) // 128
+        chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+        base = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2) + up(P * 2 * H * tok * 4) + chunks
+        desc = gl.make_desc(B, L, H, D, D, T=T)
+        assert _ws_status(desc) == (0, base + up(T * B * H * D * D * 4))
+        act = base + 3 * up(tok * 4) + up(4)
+        assert _ws_status(desc, gl.GDN_OP_LOOP_PREFILL_ACT) == (0, act)
+    # one sequence of fewer than 2048 tokens: no pieces, no state buffer
+    B, L, H, D, T = 1, 2047, 16, 128, 4
+    tok, Nc, P = B * L, (L + 63) // 64, (H * D + 127) // 128
+    chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
+    base = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2) + up(P * 2 * H * tok * 4) + chunks
+    assert _ws_status(gl.make_desc(B, L, H, D, D, T=T)) == (0, base)

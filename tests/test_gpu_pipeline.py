@@ -1,0 +1,112 @@
+"""The loop prefill run as a pipeline over pieces (gdn_loop_prefill_set_pieces) against the same call run loop
+by loop.
+
+Every row's arithmetic is the same in both orders (the projection, the chunk preparation and the carry of a
+chunk see the same operands; the state crosses a piece boundary through fp32 memory unchanged), so where both
+orders take the same carry variant the outputs must agree bit for bit: h^(T), every h^(tau) and every loop's
+final state.  Where the whole call takes the 32-column carry and the pieces the 16-column one, the pipelined
+call is held to the oracle stage by stage at the fixed bf16 bar instead (check_forced_loops).
+"""
+import numpy as np
+import pytest
+import torch
+
+import looped_linear_attention_amd as gl
+import synth
+from helpers import say
+from test_gpu_loop import LoopRun, _pack, check_forced_loops
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def pieces():
+    """Sets the piece length for one test and restores the automatic setting afterwards."""
+    yield gl.gdn_loop_prefill_set_pieces
+    gl.gdn_loop_prefill_set_pieces(0)
+
+
+def _both(w, x, B, L, piece, set_pieces):
+    Wp = _pack(w, x)
+    set_pieces(-1)
+    ref = LoopRun(w, x, B, L, w.T, Wp=Wp)
+    set_pieces(piece)
+    assert gl.gdn_loop_prefill_pieces(ref.desc) > 0
+    run = LoopRun(w, x, B, L, w.T, Wp=Wp)
+    return ref, run
+
+
+@pytest.mark.parametrize("B,L,piece", [(1, 3772, 1024), (2, 1100, 1024), (1, 4096, 2048), (2, 2500, 1024)])
+def test_pieces_match_loop_by_loop(B, L, piece, pieces):
+    """16 heads of 128 (the 16-column carry in both orders): pieces of one sequence with a ragged last piece
+    (3772 = 1024 + 1024 + 1724 tokens, ending in a 60-token chunk), one piece per sequence, the automatic piece
+    length, and two sequences of two pieces each."""
+    w = synth.workload("prefill_b4_l8192")
+    say(f"[pipeline] B={B} L={L} pieces of {piece} against loop by loop")
+    x = synth.prefill_inputs(w, B=B, L=L)
+    ref, run = _both(w, x, B, L, piece, pieces)
+    assert torch.equal(run.h_out, ref.h_out)
+    assert torch.equal(run.loops, ref.loops)
+    assert torch.equal(run.states, ref.states)
+    # the documented regions hold loop T's operands in both orders
+    for a, b in zip(run.operands(), ref.operands()):
+        assert torch.equal(a, b)
+
+
+def test_pieces_repeat_bitwise(pieces):
+    """Back-to-back pipelined calls on one stream (the second reuses the streams and events of the first) give
+    the same bits."""
+    w = synth.workload("prefill_b1_l4096")
+    say("[pipeline] prefill_b1_l4096, three pipelined calls in a row")
+    x = synth.prefill_inputs(w)
+    pieces(1024)
+    Wp = _pack(w, x)
+    desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL)
+    h0, rho = x["h0"].to("cuda"), x["rho"].to("cuda")
+    outs = []
+    for _ in range(3):
+        h = torch.empty(w.B, w.L, w.d, device="cuda")
+        gl.gdn_loop_prefill(desc, h0, Wp, rho, h, None, None, ws)
+        outs.append(h)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    assert bool(torch.isfinite(outs[0]).all())
+
+
+def test_pieces_on_side_stream(pieces):
+    """A pipelined call on a non-default torch stream orders against that stream: work queued after it sees
+    its outputs (here a copy of h_out made on the same stream), and it starts after what was queued before
+    (h0 filled on that stream just before the call)."""
+    w = synth.workload("prefill_b1_l4096")
+    say("[pipeline] prefill_b1_l4096 on a side stream")
+    x = synth.prefill_inputs(w)
+    Wp = _pack(w, x)
+    desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    pieces(-1)
+    ref = LoopRun(w, x, w.B, w.L, w.T, Wp=Wp, keep=False).h_out
+    pieces(1024)
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL)
+    rho = x["rho"].to("cuda")
+    h0_src = x["h0"].to("cuda")
+    h0 = torch.zeros_like(h0_src)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        h0.copy_(h0_src)
+        h = torch.empty(w.B, w.L, w.d, device="cuda")
+        gl.gdn_loop_prefill(desc, h0, Wp, rho, h, None, None, ws, stream=s)
+        h_copy = h.clone()
+    s.synchronize()
+    assert torch.equal(h_copy, ref)
+
+
+def test_pieces_headline_shape_stage_forced(pieces):
+    """4 x 8192 tokens in pieces of 2048: the whole call takes the 32-column carry, the pieces the 16-column
+    one, so the pipelined call is checked against the oracle, stage by stage at 3e-3, on every token of two
+    heads (on different XCDs)."""
+    w = synth.workload("prefill_b4_l8192")
+    say("[pipeline] prefill_b4_l8192 in pieces of 2048, heads (3, 12), stage-forced")
+    pieces(2048)
+    # (the call with T = 1 runs loop by loop, on the 32-column carry: its h^(1) may differ in the last bits)
+    check_forced_loops(w, synth.prefill_inputs(w), w.B, w.L, heads=(3, 12), prefix_bitwise=False)
