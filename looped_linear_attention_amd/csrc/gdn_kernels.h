@@ -62,6 +62,16 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
                           const int *rows_count = nullptr, float *yraw = nullptr, int64_t ldy = 0);
 hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
                         float *beta, float alpha_lo, hipStream_t s);
+// The projection of at most 64 bf16 tokens (a decode step) split over the
+// channels: decode_k_splits(...) = S > 1 ranges whose fp32 partial products go
+// to part (decode_part_bytes bytes: [S][M][packed rows]) and are summed in a
+// second launch, in the fixed order 0 .. S-1, before the same epilogue as
+// launch_project.  S == 1: not split (use launch_project).
+int decode_k_splits(bool f32, int M, int d);
+size_t decode_part_bytes(bool f32, int M, int d, int H, int D);
+hipError_t launch_project_decode(int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
+                                 void *v, float *alpha, float *beta, float alpha_lo, float eps, float *part,
+                                 hipStream_t s);
 
 // Chunk matrices that the backward pass takes from the forward preparation,
 // per chunk (regions of a bwd_mats_bytes block): T, P, A [64][64] fp32

@@ -170,6 +170,7 @@ struct Layout {
     size_t Yhl = 0;   // bf16 workloads: dY as bf16 hi and lo planes (the transpose's planes reuse YT)
     size_t Gp = 0;    // bf16 workloads: the split-k partial sums of dY W
     size_t st = 0;    // the pipelined loop prefill: each (loop, sequence)'s state between pieces [T][B][H][D][D]
+    size_t dpart = 0; // the loop decode: partial products of the channel-split projection (0: not split)
     size_t total = 0;
     int P = 0;   // gate partials of the projection (0: alpha and beta directly)
 };
@@ -241,6 +242,10 @@ Layout layout(const gdn_desc *d, int op) {
     // shapes the loop prefill can run as a pipeline of pieces (below) carry
     // each (loop, sequence)'s state from one piece to the next through here
     if (op == GDN_OP_LOOP_PREFILL && !act && pipeline_capable(d, lo.P)) lo.st = take((size_t)d->T * bh * D * D * 4);
+    if (op == GDN_OP_LOOP_DECODE) {
+        const size_t pb = decode_part_bytes(d->act == GDN_F32, (int)tokens, d->d, d->H, (int)D);
+        if (pb) lo.dpart = take(pb);
+    }
     lo.total = off;
     return lo;
 }
@@ -1204,8 +1209,12 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
     bool hprev_bf16 = !f32;
     for (int tau = 0; tau < desc->T; ++tau) {
         const bool last = tau == desc->T - 1;
-        hipError_t e = project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                               desc->norm_eps, nullptr, s);
+        // at most 64 tokens: the projection split over the channels (two launches)
+        // (not stage-timed: a stage timer times single launches)
+        hipError_t e = lo.dpart ? launch_project_decode(N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
+                                                        desc->norm_eps, (float *)at(ws, lo.dpart), s)
+                                : project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
+                                          desc->norm_eps, nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         e = timed(GDN_STAGE_DECODE, s, [&] {
             return launch_decode(f32, N, desc->H, D, q, k, v, al, be, states + tau * state_elems,

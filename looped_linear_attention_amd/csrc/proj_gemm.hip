@@ -211,14 +211,16 @@ template <int NA> struct KloopCfg {
     static constexpr int NST = NA == 2 ? 6 : STAGES;
 };
 static_assert(KloopCfg<2>::NST * KloopCfg<2>::SE <= STAGES * STAGE_ELEMS, "the NA = 2 stages fit the LDS");
+// K is the row stride of x and Wp; the loop covers channels [0, Kn) of the
+// rows as given (a k-range split passes x and Wp advanced to its first channel).
 template <bool GATE, int NA>
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16 *stages, const bf16 *__restrict__ x,
                                            const bf16 *__restrict__ Wp, int lane, int wave, int wm,
                                            int wn, int m0, int n0, int M, int K, int b_rows,
-                                           int gate_cols) {
+                                           int gate_cols, int Kn) {
     using CF = KloopCfg<NA>;
     constexpr int NST = CF::NST, SE = CF::SE, AE = CF::AE;
-    const int nkb = K / BK_BF;   // >= 1
+    const int nkb = Kn / BK_BF;   // >= 1
     auto kblock = [&](int kb) { return min(kb, nkb - 1) * BK_BF; };
     constexpr int NL = NA + 4;          // direct loads per k-block
     static_assert((NST - 1) * NL < 64, "the vector-memory counter holds 0..63");
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    if (gate) gemm_kloop<true, NA>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
-    else gemm_kloop<false, NA>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols);
+    if (gate) gemm_kloop<true, NA>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols, K);
+    else gemm_kloop<false, NA>(acc, stages, x, Wp, lane, wave, wm, wn, m0, n0, M, K, b_rows, gate_cols, K);
     __syncthreads();   // all waves done reading the operand stages
 
     // epilogue in two 128-row halves through an fp32 tile in LDS (reuses the operand buffers)
@@ -357,6 +359,103 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                     eps);
         __syncthreads();
     }
+}
+
+// ---------------------------------------------------------------------------
+// decode-size projection (at most 64 tokens) split over the channels
+// ---------------------------------------------------------------------------
+// With at most 64 tokens the projection streams the 25 MB of packed weights
+// (d = 2048) with little arithmetic per byte, and one workgroup per 128-column
+// tile leaves 80% of the CUs idle.  k_proj_dpart splits the channels into S
+// equal ranges: workgroup (column tile j, range s) runs the 64-token k-loop of
+// k_proj_bf16 over its range and stores the fp32 tile to part[s][M][NP]
+// (NP = packed rows; only the M token rows).  k_proj_dsum adds the S partials
+// of each element in the order s = 0 .. S-1 (the same order every call) and
+// applies k_proj_bf16's epilogue (per-head norms of q and k, gates, bf16 pack).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_proj_dpart(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ Wp, int M, int K, int Kn, int H, int n_main, int NP,
+    float *__restrict__ part) {
+    constexpr int LDS_MAIN = STAGES * STAGE_ELEMS * 2;
+    __shared__ __attribute__((aligned(16))) char smem[LDS_MAIN];
+    bf16 *stages = reinterpret_cast<bf16 *>(smem);
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n_tile = blockIdx.x, s = blockIdx.y;
+    const bool gate = n_tile == n_main;
+    const int n0 = n_tile * BN, k0 = s * Kn;
+    const int gate_cols = 2 * H;
+    const int b_rows = gate ? ((gate_cols + 31) / 32) * 32 : BN;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    if (gate) gemm_kloop<true, 2>(acc, stages, x + k0, Wp + k0, lane, wave, wm, wn, 0, n0, M, K, b_rows, gate_cols, Kn);
+    else gemm_kloop<false, 2>(acc, stages, x + k0, Wp + k0, lane, wave, wm, wn, 0, n0, M, K, b_rows, gate_cols, Kn);
+    __syncthreads();   // all waves done reading the operand stages
+    // the two rows of waves hold the k-step halves of rows 0 .. 63: added in the order wm = 0, 1
+    float *Cs = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        if (wm == pass) {
+#pragma unroll
+            for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const int c = wn * 64 + tn * 32 + (lane & 31);
+                        Cs[r * CS_LD + c] = pass ? Cs[r * CS_LD + c] + acc[tm][tn][e] : acc[tm][tn][e];
+                    }
+        }
+        __syncthreads();
+    }
+    // rows 0 .. M-1 of the tile: 32 float4 per row
+    float *dst = part + (int64_t)s * M * NP + n0;
+    for (int idx = t; idx < M * (BN / 4); idx += 256) {
+        const int r = idx / (BN / 4), c4 = idx % (BN / 4);
+        const float *src = Cs + r * CS_LD + 4 * c4;
+        *reinterpret_cast<float4 *>(dst + (int64_t)r * NP + 4 * c4) = make_float4(src[0], src[1], src[2], src[3]);
+    }
+}
+
+// One workgroup per (column tile, 16 token rows): each thread adds the S
+// partials of 8 consecutive columns of one row (all S loads issued first).
+constexpr int DS_ROWS = 16;
+template <int D, int S>
+__global__ __launch_bounds__(256) void k_proj_dsum(const float *__restrict__ part, int M, int H, int NP, bf16 *q,
+                                                   bf16 *k, bf16 *v, float *alpha, float *beta, float alpha_lo,
+                                                   float eps) {
+    __shared__ __attribute__((aligned(16))) float Cs[DS_ROWS * CS_LD + 16 * DS_ROWS];
+    float *red = Cs + DS_ROWS * CS_LD;
+    const int t = threadIdx.x;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * DS_ROWS;
+    const int r = t >> 4, c = (t & 15) * 8;   // 16 threads per row, 8 columns each
+    float4 p[S][2];
+    const bool valid = m0 + r < M;
+    const float *src = part + (int64_t)min(m0 + r, M - 1) * NP + n0 + c;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        p[s][0] = *reinterpret_cast<const float4 *>(src + (int64_t)s * M * NP);
+        p[s][1] = *reinterpret_cast<const float4 *>(src + (int64_t)s * M * NP + 4);
+    }
+    float4 a0 = p[0][0], a1 = p[0][1];
+#pragma unroll
+    for (int s = 1; s < S; ++s) {
+        a0.x += p[s][0].x; a0.y += p[s][0].y; a0.z += p[s][0].z; a0.w += p[s][0].w;
+        a1.x += p[s][1].x; a1.y += p[s][1].y; a1.z += p[s][1].z; a1.w += p[s][1].w;
+    }
+    float *d = Cs + r * CS_LD + c;
+    const float z = valid ? 1.f : 0.f;   // rows past M: zero (never stored)
+    d[0] = a0.x * z; d[1] = a0.y * z; d[2] = a0.z * z; d[3] = a0.w * z;
+    d[4] = a1.x * z; d[5] = a1.y * z; d[6] = a1.z * z; d[7] = a1.w * z;
+    __syncthreads();
+    proj_epilogue<D, DS_ROWS, bf16>(Cs, red, m0, n0, M, H, q, k, v, alpha, beta, alpha_lo, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,6 +982,46 @@ hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *W
     else if (ng <= 4) GATES(4);
     else GATES(8);
 #undef GATES
+    return hipGetLastError();
+}
+
+int decode_k_splits(bool f32, int M, int d) {
+    if (f32 || M > 64 || d % BK_BF) return 1;
+    const int nkb = d / BK_BF;
+    for (int S = 4; S > 1; S /= 2)
+        if (nkb % S == 0) return S;
+    return 1;
+}
+
+size_t decode_part_bytes(bool f32, int M, int d, int H, int D) {
+    const int S = decode_k_splits(f32, M, d);
+    return S > 1 ? (size_t)S * M * packed_rows(H, D) * 4 : 0;
+}
+
+hipError_t launch_project_decode(int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
+                                 void *v, float *alpha, float *beta, float alpha_lo, float eps, float *part,
+                                 hipStream_t s) {
+    const int S = decode_k_splits(false, M, d);
+    if (S < 2 || !part || M < 1) return hipErrorInvalidValue;
+    const int n_main = (int)(qkv_rows_padded(H, D) / BN), NP = (int)packed_rows(H, D);
+    const dim3 grid1(n_main + 1, S);
+#define DPART(DD)                                                                                  \
+    launch_kernel(k_proj_dpart<DD>, grid1, dim3(256), 0, s, (const bf16 *)x, (const bf16 *)Wpack, M, d, d / S, H, \
+                  n_main, NP, part)
+    if (D == 128) DPART(128); else DPART(64);
+#undef DPART
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid2(n_main + 1, (M + DS_ROWS - 1) / DS_ROWS);
+#define DSUM(DD, SS)                                                                               \
+    launch_kernel(k_proj_dsum<DD, SS>, grid2, dim3(256), 0, s, (const float *)part, M, H, NP, (bf16 *)q, (bf16 *)k, \
+                  (bf16 *)v, alpha, beta, alpha_lo, eps)
+    if (S == 4) {
+        if (D == 128) DSUM(128, 4); else DSUM(64, 4);
+    } else {
+        if (D == 128) DSUM(128, 2); else DSUM(64, 2);
+    }
+#undef DSUM
     return hipGetLastError();
 }
 

@@ -375,3 +375,22 @@ def test_loop_prefill_pieces_workspace():
     chunks = up(B * H * Nc * D * 64 * 4) + up(B * H * Nc * 64 * 64 * 4) + up(B * H * Nc * 64 * 4)
     base = 3 * up(tok * H * D * 2) + 2 * up(tok * H * 4) + up(tok * H * D * 2) + up(P * 2 * H * tok * 4) + chunks
     assert _ws_status(gl.make_desc(B, L, H, D, D, T=T)) == (0, base)
+
+
+def test_decode_workspace_split_projection():
+    """A bf16 loop decode of at most 64 sequences splits its projection over S channel ranges (S = 4, 2 or 1:
+    the largest that divides the 64-channel blocks) and keeps the fp32 partial products [S][N][packed rows] at
+    the end of its workspace; fp32 workloads and more than 64 sequences do not."""
+    up = lambda x: (x + 255) // 256 * 256
+
+    def base(N, H, D, eb):
+        return 3 * up(N * H * D * eb) + 2 * up(N * H * 4) + (up(N * H * D * 2) if eb == 2 else 0)
+
+    for N, H, D, S in [(64, 16, 128, 4), (1, 1, 128, 2), (7, 20, 64, 4), (3, 3, 64, 1)]:
+        P = (H * 3 * D + 127) // 128 * 128 + 128
+        exp = base(N, H, D, 2) + (up(S * N * P * 4) if S > 1 else 0)
+        assert _ws_status(gl.make_desc(N, 1, H, D, D), gl.GDN_OP_LOOP_DECODE) == (0, exp)
+    assert _ws_status(gl.make_desc(65, 1, 16, 128, 128), gl.GDN_OP_LOOP_DECODE) == (0, base(65, 16, 128, 2))
+    assert _ws_status(gl.make_desc(8, 1, 2, 64, 64, act=gl.GDN_F32), gl.GDN_OP_LOOP_DECODE) == (0, base(8, 2, 64, 4))
+    # the no-allocation decode still takes 64 sequences of width 2048
+    assert _ws_status(gl.make_desc(64, 1, 16, 128, 128), gl.GDN_OP_LOOP_DECODE)[1] <= 8 << 20   # its 8 MiB scratch

@@ -402,3 +402,17 @@ def test_loop_decode_batch_independent(name):
     torch.cuda.synchronize()
     assert torch.equal(h_all, h_part)
     assert torch.equal(s_all, s_part)
+
+
+@pytest.mark.parametrize("H,D,N", [(1, 128, 5), (20, 64, 7), (16, 128, 1)])
+def test_loop_decode_split_projection_shapes(H, D, N):
+    """The decode projection split over the channels on other shapes: d = 128 (two channel ranges), twenty
+    heads of 64 (d = 1280, four ranges, 40 gate columns: a gate tile wider than 32), one sequence at d = 2048;
+    one generated token, every loop stage-forced at 3e-3."""
+    w = dataclasses.replace(synth.workload("prefill_b1_l4096"), name=f"bf16_h{H}_d{D}", H=H, dk=D, dv=D, d=H * D)
+    say(f"[loop_decode] split projection H={H} D={D} N={N}, stage-forced")
+    x = synth.prefill_inputs(w, L=N)
+    g = torch.Generator().manual_seed(7)
+    states = dev(torch.randn(w.T, N, H, D, D, generator=g) * 0.02)
+    Wp = _pack(w, x)
+    check_forced_decode_step(w, x, Wp, dev(x["h0"][0]), dev(x["rho"]), states, N, TOL_BF16)
