@@ -207,7 +207,7 @@ def bench_prefill(args, w, torch, gl, synth, warmup):
         ms_total, wall, timed_stages = timed_pass(["project"], stride)
         _, _, per_stage = timed_pass(list(stages))
     finally:
-        gl.gdn_loop_prefill_set_pieces(0)
+        gl.gdn_loop_prefill_set_pieces(args.pieces)
     per_stage["project"] = timed_stages["project"]
     ms_step = ms_total / args.steps
     tokens = w.B * w.L
@@ -667,6 +667,9 @@ def main():
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--pieces", type=int, default=0,
+                    help="gdn_loop_prefill_set_pieces for the prefill legs: 0 the library's automatic setting, -1 loop "
+                         "by loop (every launch covers the whole prompt; for counter runs), > 0 tokens per piece")
     ap.add_argument("--only", default="", choices=["", "act", "block", "scan_backward", "loop_backward", "decode",
                                                    "loop_decode"],
                     help="run one secondary leg alone and print its record (for profiling; no headline line)")
@@ -685,6 +688,7 @@ def main():
     import looped_linear_attention_amd as gl
     import synth
     gl.load()
+    gl.gdn_loop_prefill_set_pieces(args.pieces)
     w = synth.workload(args.workload)
     if args.only:
         legs = {"act": lambda: bench_act(args, torch, gl, synth, w),
