@@ -51,16 +51,22 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["proj_gemm.hip", "scan_chunk.hip", "decode.hip", "gdn_device.h"]
+# the source files each counter-measured kernel is built from: its counters (profiles/traffic.json) stand only
+# while these files' code is unchanged
+KERNEL_SOURCES = {
+    "k_proj_wide": ["proj_gemm.hip", "gdn_device.h"], "k_proj_dpart": ["proj_gemm.hip", "gdn_device.h"],
+    "k_scan_prep": ["scan_chunk.hip", "gdn_device.h"], "k_scan_carry": ["scan_chunk.hip", "gdn_device.h"],
+    "k_scan_carry_w": ["scan_chunk.hip", "gdn_device.h"], "k_decode": ["decode.hip", "gdn_device.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "looped_linear_attention_amd", "csrc", name)) as f:
             text = f.read()
         # code only: comments and blank lines do not change what the counters measured
@@ -129,7 +135,7 @@ def traffic_for(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     ent = data.get(f"{kernel}@{workload}")
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or kernel not in KERNEL_SOURCES or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 

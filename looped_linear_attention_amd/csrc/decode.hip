@@ -17,7 +17,21 @@ namespace gdn {
 
 namespace {
 
-template <int D, typename TIn>
+// Projection partials (the loop decode's channel-split projection, S > 0):
+// instead of reading q, k, v, alpha, beta, workgroup (n, h) adds its head's S
+// partial products part[s][n][NP] in the order s = 0 .. S-1, normalises q and k
+// (x / sqrt(sum x^2 + eps)), rounds q, k, v to bf16, forms the gates from their
+// pre-activations, stores all five to q_out .. beta_out (where the loop decode
+// documents them) and continues with those values.
+struct DecParts {
+    const float *part;   // [S][N][NP] or nullptr
+    int S, NP, gate_row; // gate_row: first packed row of the gate tile (wa rows, then wb rows)
+    float alpha_lo, eps;
+    bf16 *q_out, *k_out, *v_out;     // [N, H, D]
+    float *alpha_out, *beta_out;     // [N, H]
+};
+
+template <int D, typename TIn, bool PARTS>
 __global__ __launch_bounds__(256) void k_decode(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                 const TIn *__restrict__ v,
                                                 const float *__restrict__ alpha,
@@ -25,29 +39,101 @@ __global__ __launch_bounds__(256) void k_decode(const TIn *__restrict__ q, const
                                                 float *__restrict__ o, const void *h_prev,
                                                 int h_prev_bf16, const float *__restrict__ rho,
                                                 float *h_out, bf16 *x_next,
-                                                int H) {
+                                                int H, DecParts dp) {
     constexpr int CG = D / 4;       // float4 column groups
     constexpr int RG = 256 / CG;    // row groups
     constexpr int RPT = D / RG;     // rows per thread
     __shared__ float ks[D], qs[D], vs[D];
     __shared__ __attribute__((aligned(16))) float4 pa[RG][CG], pb[RG][CG];
     __shared__ float kq_s;
+    __shared__ float nred[2][4], gate_s[2];
 
     const int t = threadIdx.x;
     const int nh = blockIdx.x;  // n * H + h
     const int h = nh % H;
     const int64_t vec = (int64_t)nh * D;
-    if (t < D) {
-        ks[t] = to_f32(k[vec + t]);
-        qs[t] = to_f32(q[vec + t]);
-        vs[t] = to_f32(v[vec + t]);
-    }
-    const float al = alpha[nh], be = beta[nh];
     const int cg = t % CG, rg = t / CG;
     float4 *S = reinterpret_cast<float4 *>(states + (int64_t)nh * D * D);
     float4 sr[RPT];
 #pragma unroll
     for (int ii = 0; ii < RPT; ++ii) sr[ii] = S[(rg + RG * ii) * CG + cg];
+    float al, be;
+    if constexpr (PARTS) {
+        // threads 0 .. D-1: q, k, v of column t; thread D: the two gate pre-activations
+        const int64_t n = nh / H;
+        const float *pr = dp.part + n * dp.NP;
+        const int64_t sstride = (int64_t)(gridDim.x / H) * dp.NP;
+        float qv = 0.f, kv = 0.f, vv = 0.f;
+        if (t < D) {
+            const float *c = pr + (int64_t)h * 3 * D + t;
+            float pq[8], pk[8], pv[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s < dp.S) {
+                    pq[s] = c[s * sstride];
+                    pk[s] = c[s * sstride + D];
+                    pv[s] = c[s * sstride + 2 * D];
+                }
+            qv = pq[0], kv = pk[0], vv = pv[0];
+#pragma unroll
+            for (int s = 1; s < 8; ++s)
+                if (s < dp.S) {
+                    qv += pq[s];
+                    kv += pk[s];
+                    vv += pv[s];
+                }
+            // per-head sums of squares: in-wave, then across the D / 64 waves
+            float sq = qv * qv, sk = kv * kv;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                sq += __shfl_xor(sq, off, 64);
+                sk += __shfl_xor(sk, off, 64);
+            }
+            if ((t & 63) == 0) {
+                nred[0][t >> 6] = sq;
+                nred[1][t >> 6] = sk;
+            }
+        } else if (t == D) {
+            float za = 0.f, zb = 0.f;
+            for (int s = 0; s < dp.S; ++s) {
+                za += pr[s * sstride + dp.gate_row + h];
+                zb += pr[s * sstride + dp.gate_row + H + h];
+            }
+            gate_s[0] = dp.alpha_lo + (1.f - dp.alpha_lo) / (1.f + expf(za));
+            gate_s[1] = 1.f / (1.f + expf(-zb));
+        }
+        __syncthreads();
+        if (t < D) {
+            float tq = 0.f, tk = 0.f;
+#pragma unroll
+            for (int w = 0; w < D / 64; ++w) {
+                tq += nred[0][w];
+                tk += nred[1][w];
+            }
+            const bf16 qb = (bf16)(qv * (1.f / sqrtf(tq + dp.eps))), kb = (bf16)(kv * (1.f / sqrtf(tk + dp.eps)));
+            const bf16 vb = (bf16)vv;
+            dp.q_out[vec + t] = qb;
+            dp.k_out[vec + t] = kb;
+            dp.v_out[vec + t] = vb;
+            qs[t] = (float)qb;
+            ks[t] = (float)kb;
+            vs[t] = (float)vb;
+        }
+        al = gate_s[0];
+        be = gate_s[1];
+        if (t == 0) {
+            dp.alpha_out[nh] = al;
+            dp.beta_out[nh] = be;
+        }
+    } else {
+        if (t < D) {
+            ks[t] = to_f32(k[vec + t]);
+            qs[t] = to_f32(q[vec + t]);
+            vs[t] = to_f32(v[vec + t]);
+        }
+        al = alpha[nh];
+        be = beta[nh];
+    }
     __syncthreads();
     if (t < 64) {
         float p = 0.f;
@@ -117,16 +203,23 @@ __global__ __launch_bounds__(256) void k_decode(const TIn *__restrict__ q, const
 hipError_t launch_decode(bool f32, int N, int H, int D, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, float *states, float *o,
                          const void *h_prev, bool h_prev_bf16, const float *rho, float *h_out,
-                         bf16 *x_next, hipStream_t s) {
+                         bf16 *x_next, hipStream_t s, const float *part, int S, float alpha_lo, float eps) {
     dim3 grid((unsigned)((int64_t)N * H));
-#define DEC(DD, T)                                                                                 \
-    launch_kernel((k_decode<DD, T>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,      \
+    if (part && (f32 || S < 1 || S > 8)) return hipErrorInvalidValue;
+    // with partials, q .. beta are where the step's operands are stored (nothing is read from them)
+    const DecParts dp{part, S, (int)packed_rows(H, D), (int)qkv_rows_padded(H, D), alpha_lo, eps,
+                      part ? (bf16 *)q : nullptr, part ? (bf16 *)k : nullptr, part ? (bf16 *)v : nullptr,
+                      part ? (float *)alpha : nullptr, part ? (float *)beta : nullptr};
+#define DEC(DD, T, PS)                                                                             \
+    launch_kernel((k_decode<DD, T, PS>), grid, dim3(256), 0, s, (const T *)q, (const T *)k,  \
                        (const T *)v, alpha, beta, states, o, h_prev, h_prev_bf16 ? 1 : 0, rho,    \
-                       h_out, x_next, H)
+                       h_out, x_next, H, dp)
     if (f32) {
-        if (D == 128) DEC(128, float); else DEC(64, float);
+        if (D == 128) DEC(128, float, false); else DEC(64, float, false);
+    } else if (part) {
+        if (D == 128) DEC(128, bf16, true); else DEC(64, bf16, true);
     } else {
-        if (D == 128) DEC(128, bf16); else DEC(64, bf16);
+        if (D == 128) DEC(128, bf16, false); else DEC(64, bf16, false);
     }
 #undef DEC
     return hipGetLastError();

@@ -63,15 +63,13 @@ hipError_t launch_project(bool f32, int M, int d, int H, int D, const void *x, c
 hipError_t launch_gates(int M, int d, int H, int D, const void *x, const void *Wpack, float *alpha,
                         float *beta, float alpha_lo, hipStream_t s);
 // The projection of at most 64 bf16 tokens (a decode step) split over the
-// channels: decode_k_splits(...) = S > 1 ranges whose fp32 partial products go
-// to part (decode_part_bytes bytes: [S][M][packed rows]) and are summed in a
-// second launch, in the fixed order 0 .. S-1, before the same epilogue as
-// launch_project.  S == 1: not split (use launch_project).
+// channels: decode_k_splits(...) = S > 1 ranges whose fp32 partial products
+// (no epilogue) go to part (decode_part_bytes bytes: [S][M][packed rows]);
+// launch_decode with part sums them.  S == 1: not split (use launch_project).
 int decode_k_splits(bool f32, int M, int d);
 size_t decode_part_bytes(bool f32, int M, int d, int H, int D);
-hipError_t launch_project_decode(int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
-                                 void *v, float *alpha, float *beta, float alpha_lo, float eps, float *part,
-                                 hipStream_t s);
+hipError_t launch_project_decode_parts(int M, int d, int H, int D, const void *x, const void *Wpack, float *part,
+                                       hipStream_t s);
 
 // Chunk matrices that the backward pass takes from the forward preparation,
 // per chunk (regions of a bwd_mats_bytes block): T, P, A [64][64] fp32
@@ -240,10 +238,15 @@ hipError_t launch_bwd_chunk(bool f32, int B, int L, int H, int D, const void *q,
                             float *dalpha, float *dbeta, hipStream_t s);
 
 // One recurrent token per sequence; states updated in place.  With
-// h_out != nullptr the loop residual is applied as in CarryOut.
+// h_out != nullptr the loop residual is applied as in CarryOut.  With part
+// (bf16 only; the S channel-range partials of launch_project_decode_parts) the
+// step forms its own q, k, v and gates from the partials (added in the order
+// 0 .. S-1, q and k normalised with eps, q/k/v rounded to bf16) and stores
+// them to q, k, v, alpha, beta instead of reading them.
 hipError_t launch_decode(bool f32, int N, int H, int D, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, float *states, float *o,
                          const void *h_prev, bool h_prev_bf16, const float *rho, float *h_out,
-                         bf16 *x_next, hipStream_t s);
+                         bf16 *x_next, hipStream_t s, const float *part = nullptr, int S = 0,
+                         float alpha_lo = 0.f, float eps = 0.f);
 
 }  // namespace gdn

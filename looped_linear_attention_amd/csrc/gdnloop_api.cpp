@@ -1209,17 +1209,19 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
     bool hprev_bf16 = !f32;
     for (int tau = 0; tau < desc->T; ++tau) {
         const bool last = tau == desc->T - 1;
-        // at most 64 tokens: the projection split over the channels (two launches)
+        // at most 64 bf16 tokens: the projection split over the channels into
+        // partial products, which the decode step itself sums and normalises
         // (not stage-timed: a stage timer times single launches)
-        hipError_t e = lo.dpart ? launch_project_decode(N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                                                        desc->norm_eps, (float *)at(ws, lo.dpart), s)
-                                : project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
-                                          desc->norm_eps, nullptr, s);
+        float *part = lo.dpart ? (float *)at(ws, lo.dpart) : nullptr;
+        hipError_t e = part ? launch_project_decode_parts(N, d, desc->H, D, x, Wpack, part, s)
+                            : project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
+                                      desc->norm_eps, nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "projection launch");
         e = timed(GDN_STAGE_DECODE, s, [&] {
             return launch_decode(f32, N, desc->H, D, q, k, v, al, be, states + tau * state_elems,
                                  nullptr, hprev, hprev_bf16, rho + (int64_t)tau * d, h_out,
-                                 (!f32 && !last) ? xbuf : nullptr, s);
+                                 (!f32 && !last) ? xbuf : nullptr, s, part, part ? decode_k_splits(f32, N, d) : 0,
+                                 desc->alpha_lo, desc->norm_eps);
         });
         if (e != hipSuccess) return hip_fail(e, "decode launch");
         hprev = h_out;

@@ -369,9 +369,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // tile leaves 80% of the CUs idle.  k_proj_dpart splits the channels into S
 // equal ranges: workgroup (column tile j, range s) runs the 64-token k-loop of
 // k_proj_bf16 over its range and stores the fp32 tile to part[s][M][NP]
-// (NP = packed rows; only the M token rows).  k_proj_dsum adds the S partials
-// of each element in the order s = 0 .. S-1 (the same order every call) and
-// applies k_proj_bf16's epilogue (per-head norms of q and k, gates, bf16 pack).
+// (NP = packed rows; only the M token rows).  The decode step that consumes
+// them (k_decode with partials) adds the S partials of each element in the
+// order s = 0 .. S-1 and applies the epilogue itself (per-head norms of q and
+// k, gates, bf16 rounding): each of its workgroups owns one (sequence, head).
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_proj_dpart(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Wp, int M, int K, int Kn, int H, int n_main, int NP,
@@ -422,40 +423,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float *src = Cs + r * CS_LD + 4 * c4;
         *reinterpret_cast<float4 *>(dst + (int64_t)r * NP + 4 * c4) = make_float4(src[0], src[1], src[2], src[3]);
     }
-}
-
-// One workgroup per (column tile, 16 token rows): each thread adds the S
-// partials of 8 consecutive columns of one row (all S loads issued first).
-constexpr int DS_ROWS = 16;
-template <int D, int S>
-__global__ __launch_bounds__(256) void k_proj_dsum(const float *__restrict__ part, int M, int H, int NP, bf16 *q,
-                                                   bf16 *k, bf16 *v, float *alpha, float *beta, float alpha_lo,
-                                                   float eps) {
-    __shared__ __attribute__((aligned(16))) float Cs[DS_ROWS * CS_LD + 16 * DS_ROWS];
-    float *red = Cs + DS_ROWS * CS_LD;
-    const int t = threadIdx.x;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * DS_ROWS;
-    const int r = t >> 4, c = (t & 15) * 8;   // 16 threads per row, 8 columns each
-    float4 p[S][2];
-    const bool valid = m0 + r < M;
-    const float *src = part + (int64_t)min(m0 + r, M - 1) * NP + n0 + c;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        p[s][0] = *reinterpret_cast<const float4 *>(src + (int64_t)s * M * NP);
-        p[s][1] = *reinterpret_cast<const float4 *>(src + (int64_t)s * M * NP + 4);
-    }
-    float4 a0 = p[0][0], a1 = p[0][1];
-#pragma unroll
-    for (int s = 1; s < S; ++s) {
-        a0.x += p[s][0].x; a0.y += p[s][0].y; a0.z += p[s][0].z; a0.w += p[s][0].w;
-        a1.x += p[s][1].x; a1.y += p[s][1].y; a1.z += p[s][1].z; a1.w += p[s][1].w;
-    }
-    float *d = Cs + r * CS_LD + c;
-    const float z = valid ? 1.f : 0.f;   // rows past M: zero (never stored)
-    d[0] = a0.x * z; d[1] = a0.y * z; d[2] = a0.z * z; d[3] = a0.w * z;
-    d[4] = a1.x * z; d[5] = a1.y * z; d[6] = a1.z * z; d[7] = a1.w * z;
-    __syncthreads();
-    proj_epilogue<D, DS_ROWS, bf16>(Cs, red, m0, n0, M, H, q, k, v, alpha, beta, alpha_lo, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -998,9 +965,8 @@ size_t decode_part_bytes(bool f32, int M, int d, int H, int D) {
     return S > 1 ? (size_t)S * M * packed_rows(H, D) * 4 : 0;
 }
 
-hipError_t launch_project_decode(int M, int d, int H, int D, const void *x, const void *Wpack, void *q, void *k,
-                                 void *v, float *alpha, float *beta, float alpha_lo, float eps, float *part,
-                                 hipStream_t s) {
+hipError_t launch_project_decode_parts(int M, int d, int H, int D, const void *x, const void *Wpack, float *part,
+                                       hipStream_t s) {
     const int S = decode_k_splits(false, M, d);
     if (S < 2 || !part || M < 1) return hipErrorInvalidValue;
     const int n_main = (int)(qkv_rows_padded(H, D) / BN), NP = (int)packed_rows(H, D);
@@ -1010,18 +976,6 @@ hipError_t launch_project_decode(int M, int d, int H, int D, const void *x, cons
                   n_main, NP, part)
     if (D == 128) DPART(128); else DPART(64);
 #undef DPART
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 grid2(n_main + 1, (M + DS_ROWS - 1) / DS_ROWS);
-#define DSUM(DD, SS)                                                                               \
-    launch_kernel(k_proj_dsum<DD, SS>, grid2, dim3(256), 0, s, (const float *)part, M, H, NP, (bf16 *)q, (bf16 *)k, \
-                  (bf16 *)v, alpha, beta, alpha_lo, eps)
-    if (S == 4) {
-        if (D == 128) DSUM(128, 4); else DSUM(64, 4);
-    } else {
-        if (D == 128) DSUM(128, 2); else DSUM(64, 2);
-    }
-#undef DSUM
     return hipGetLastError();
 }
 
