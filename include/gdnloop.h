@@ -290,7 +290,12 @@ gdn_status gdn_loop_prefill_act(const gdn_desc *desc, const void *h0, const void
  *   rho [T, d]                   device fp32
  *   states [T, B, H, dk, dv]     device fp32, in/out (loop tau advances its own)
  *   h_out [B, d]                 device fp32, written (h^(T) of the token)
- *   ws, ws_bytes                 gdn_workspace_bytes(LOOP_DECODE) */
+ *   ws, ws_bytes                 gdn_workspace_bytes(LOOP_DECODE); for at most 64
+ *                                bf16 sequences its last region holds the
+ *                                projection's partial products (the projection
+ *                                split over the channels), and a workspace of
+ *                                the size without that region runs the
+ *                                projection unsplit */
 gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wpack,
                            const float *rho, float *states, float *h_out,
                            void *ws, size_t ws_bytes, void *stream);

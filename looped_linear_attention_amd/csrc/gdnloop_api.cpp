@@ -1194,8 +1194,12 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
     REQUIRE_PTR(h_t); REQUIRE_PTR(Wpack); REQUIRE_PTR(rho); REQUIRE_PTR(states); REQUIRE_PTR(h_out);
     if ((const void *)h_out == h_t) return fail(GDN_ERR_SHAPE, "h_out may not alias h_t");
     const Layout lo = layout(desc, GDN_OP_LOOP_DECODE);
-    if (!ws || ws_bytes < lo.total)
-        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", lo.total, ws_bytes);
+    // the projection's partials are the last region: a workspace that holds
+    // everything before them runs the step with the projection unsplit
+    const bool split = lo.dpart && ws && ws_bytes >= lo.total;
+    const size_t need = lo.dpart ? lo.dpart : lo.total;
+    if (!ws || ws_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (!aligned16(ws)) return fail(GDN_ERR_ALIGN, "ws is not 16-byte aligned");
 
     const hipStream_t s = (hipStream_t)stream;
@@ -1212,7 +1216,7 @@ gdn_status gdn_loop_decode(const gdn_desc *desc, const void *h_t, const void *Wp
         // at most 64 bf16 tokens: the projection split over the channels into
         // partial products, which the decode step itself sums and normalises
         // (not stage-timed: a stage timer times single launches)
-        float *part = lo.dpart ? (float *)at(ws, lo.dpart) : nullptr;
+        float *part = split ? (float *)at(ws, lo.dpart) : nullptr;
         hipError_t e = part ? launch_project_decode_parts(N, d, desc->H, D, x, Wpack, part, s)
                             : project(f32, N, d, desc->H, D, x, Wpack, q, k, v, al, be, desc->alpha_lo,
                                       desc->norm_eps, nullptr, s);

@@ -54,6 +54,10 @@ extern "C" gdn_status gdn_loop_decode_noalloc(const gdn_desc *desc, const void *
     size_t need = 0;
     gdn_status st = gdn_workspace_bytes(desc, GDN_OP_LOOP_DECODE, &need);
     if (st != GDN_OK) return st;
+    // a step whose channel-split projection partials do not fit runs unsplit
+    // (gdn_loop_decode takes a workspace without that last region)
+    const size_t part = gdn::decode_part_bytes(desc->act == GDN_F32, desc->B, desc->d, desc->H, desc->dk);
+    if (part) need -= (part + 255) / 256 * 256;
     if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
         return (gdn_status)gdn::set_last_error(
             GDN_ERR_WORKSPACE, "gdn_loop_decode_noalloc: the step needs more scratch than the library's "

@@ -288,10 +288,12 @@ def test_loop_prefill_zero_values_closed_form():
 # ---------------------------------------------------------------------------
 # looped decode
 # ---------------------------------------------------------------------------
-def _decode_call(w, Wp, T, h_t, rho, states, N):
-    """gdn_loop_decode with T loops on poisoned output and workspace; returns (h_out, desc, ws)."""
+def _decode_call(w, Wp, T, h_t, rho, states, N, ws_short=0):
+    """gdn_loop_decode with T loops on poisoned output and workspace (ws_short bytes smaller than
+    gdn_workspace_bytes reports); returns (h_out, desc, ws)."""
     desc = gl.make_desc(N, 1, w.H, w.dk, w.dv, T=T, act=w.act, alpha_lo=w.alpha_lo)
-    ws = poison_(gl.workspace(desc, gl.GDN_OP_LOOP_DECODE))
+    ws = poison_(torch.empty(gl.gdn_workspace_bytes(desc, gl.GDN_OP_LOOP_DECODE) - ws_short, dtype=torch.uint8,
+                             device="cuda"))
     ho, hb = padded((N, w.d))
     gl.gdn_loop_decode(desc, h_t, Wp, rho[:T].contiguous(), states, ho, ws)
     torch.cuda.synchronize()
@@ -299,7 +301,7 @@ def _decode_call(w, Wp, T, h_t, rho, states, N):
     return ho, desc, ws
 
 
-def check_forced_decode_step(w, x, Wp, h_t, rho, states_before, N, tol):
+def check_forced_decode_step(w, x, Wp, h_t, rho, states_before, N, tol, ws_short=0):
     """One generated token per sequence, each loop stage-forced: the GPU's h^(tau-1) of the token and its
     loop-tau state before the step are the inputs on both sides (gdn_loop_decode with T = tau on a copy of
     the states gives h^(tau) and leaves loop tau's projections in the workspace).  Returns the GPU's
@@ -310,7 +312,7 @@ def check_forced_decode_step(w, x, Wp, h_t, rho, states_before, N, tol):
     h_prev = h_t.cpu().double().numpy()
     for tau in range(1, w.T + 1):
         st = states_before[:tau].clone()
-        ho, desc, ws = _decode_call(w, Wp, tau, h_t, rho, st, N)
+        ho, desc, ws = _decode_call(w, Wp, tau, h_t, rho, st, N, ws_short)
         ops = [gl.workspace_view(ws, desc, gl.GDN_OP_LOOP_DECODE, r).cpu()
                for r in (gl.GDN_WS_Q, gl.GDN_WS_K, gl.GDN_WS_V, gl.GDN_WS_ALPHA, gl.GDN_WS_BETA)]
         x_in = oracle.round_bf16(h_prev) if w.act == "bf16" else h_prev
@@ -324,7 +326,7 @@ def check_forced_decode_step(w, x, Wp, h_t, rho, states_before, N, tol):
         assert eh <= tol and es <= tol
         h_prev = ho.cpu().double().numpy()
     states = states_before.clone()
-    ho, _, _ = _decode_call(w, Wp, w.T, h_t, rho, states, N)
+    ho, _, _ = _decode_call(w, Wp, w.T, h_t, rho, states, N, ws_short)
     assert torch.equal(ho.cpu().double(), torch.from_numpy(h_prev))   # the T-loop call equals its forced loops
     return ho, states
 
@@ -416,3 +418,35 @@ def test_loop_decode_split_projection_shapes(H, D, N):
     states = dev(torch.randn(w.T, N, H, D, D, generator=g) * 0.02)
     Wp = _pack(w, x)
     check_forced_decode_step(w, x, Wp, dev(x["h0"][0]), dev(x["rho"]), states, N, TOL_BF16)
+
+
+def test_loop_decode_workspace_without_partials():
+    """A decode workspace without the projection's partials region (the last one) runs the projection unsplit:
+    one step stage-forced at 3e-3 (64 sequences, 16 heads of 128); a workspace one region smaller still is
+    refused.  gdn_loop_decode_noalloc at a width whose partials would not fit its 8 MiB scratch (32 heads of 128,
+    64 sequences) runs unsplit too and gives the same bits as gdn_loop_decode on the smaller workspace."""
+    up = lambda n: (n + 255) // 256 * 256
+    for H, N in [(16, 64), (32, 64)]:
+        w = dataclasses.replace(synth.workload("prefill_b1_l4096"), name=f"bf16_h{H}", H=H, d=H * 128)
+        say(f"[loop_decode] H={H} N={N}, workspace without the partials region")
+        x = synth.prefill_inputs(w, L=N)
+        Wp = _pack(w, x)
+        desc = gl.make_desc(N, 1, H, 128, 128, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+        full = gl.gdn_workspace_bytes(desc, gl.GDN_OP_LOOP_DECODE)
+        short = up(4 * N * ((H * 3 * 128 + 127) // 128 * 128 + 128) * 4)
+        g = torch.Generator().manual_seed(5)
+        st0 = dev(torch.randn(w.T, N, H, 128, 128, generator=g) * 0.02)
+        h_t, rho = dev(x["h0"][0]), dev(x["rho"])
+        with pytest.raises(gl.GdnError):
+            gl.gdn_loop_decode(desc, h_t, Wp, rho, st0.clone(), torch.empty(N, w.d, device="cuda"),
+                               torch.empty(full - short - 256, dtype=torch.uint8, device="cuda"))
+        if H == 16:
+            check_forced_decode_step(w, x, Wp, h_t, rho, st0, N, TOL_BF16, ws_short=short)
+            continue
+        assert full > 8 << 20 >= full - short
+        ho_ws, _, _ = _decode_call(w, Wp, w.T, h_t, rho, st_ws := st0.clone(), N, short)
+        st = st0.clone()
+        ho = torch.empty(N, w.d, device="cuda")
+        gl.gdn_loop_decode_noalloc(desc, h_t, Wp, rho, st, ho)
+        torch.cuda.synchronize()
+        assert torch.equal(ho, ho_ws) and torch.equal(st, st_ws)
