@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -149,7 +150,7 @@ static int lb_dw_split(int d, int64_t P, bool f32) {
 constexpr int PIPE_MIN_PIECE = 1024;
 constexpr int PIPE_AUTO_MIN_L = 16384;   // shortest sequence the automatic setting splits
 constexpr int PIPE_STREAMS = 4;
-int g_pipe_piece = 0;   // gdn_loop_prefill_set_pieces: 0 automatic, -1 off, > 0 tokens per piece
+std::atomic<int> g_pipe_piece{0};   // gdn_loop_prefill_set_pieces: 0 automatic, -1 off, > 0 tokens per piece
 
 // bf16 workloads of at least two loops whose projection forms the gate
 // partials (P > 0), with pieces to form: more than one sequence, or one
@@ -977,8 +978,8 @@ int device_cus() {
 
 // Tokens per piece for this call (0: the loops run one after another).
 int pipe_piece_tokens(const gdn_desc *d, const Layout &lo) {
-    if (!lo.st || g_pipe_piece < 0) return 0;
-    int want = g_pipe_piece;
+    int want = g_pipe_piece.load(std::memory_order_relaxed);
+    if (!lo.st || want < 0) return 0;
     if (want == 0) {
         // automatic: two pieces per sequence, where the whole call's carry would
         // leave at least half the CUs idle (one 16-column slice workgroup per
@@ -1153,7 +1154,7 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
 
 gdn_status gdn_loop_prefill_set_pieces(int tokens) {
     if (tokens < -1) return fail(GDN_ERR_SHAPE, "tokens per piece must be -1, 0 or positive (got %d)", tokens);
-    g_pipe_piece = tokens;
+    g_pipe_piece.store(tokens, std::memory_order_relaxed);
     return GDN_OK;
 }
 
