@@ -110,3 +110,19 @@ def test_pieces_headline_shape_stage_forced(pieces):
     pieces(2048)
     # (the call with T = 1 runs loop by loop, on the 32-column carry: its h^(1) may differ in the last bits)
     check_forced_loops(w, synth.prefill_inputs(w), w.B, w.L, heads=(3, 12), prefix_bitwise=False)
+
+
+@pytest.mark.parametrize("T,H,D,L,piece", [(5, 16, 128, 2500, 1024), (2, 16, 128, 4096, 2048), (4, 16, 64, 3000, 1024),
+                                           (3, 8, 128, 2100, 1024)])
+def test_pieces_other_loop_counts_and_heads(T, H, D, L, piece, pieces):
+    """More loops than carry streams (T = 5: loops 1 and 4 share one), two loops, heads of 64 and eight heads: the
+    pipelined call against the same call loop by loop, bit for bit (both take the 16-column carry)."""
+    import dataclasses
+    w = dataclasses.replace(synth.workload("prefill_b1_l4096"), name=f"bf16_t{T}_h{H}_d{D}", T=T, H=H, dk=D, dv=D,
+                            d=H * D)
+    say(f"[pipeline] T={T} H={H} D={D} L={L} pieces of {piece} against loop by loop")
+    x = synth.prefill_inputs(w, L=L)
+    ref, run = _both(w, x, 1, L, piece, pieces)
+    assert torch.equal(run.h_out, ref.h_out)
+    assert torch.equal(run.loops, ref.loops)
+    assert torch.equal(run.states, ref.states)
