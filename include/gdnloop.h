@@ -251,8 +251,9 @@ gdn_status gdn_loop_prefill(const gdn_desc *desc, const void *h0, const void *Wp
 gdn_status gdn_loop_prefill_set_pieces(int tokens);
 
 /* The piece length gdn_loop_prefill would use for `desc` under the current
- * setting (0: loop by loop).  Errors: the usual descriptor errors,
- * GDN_ERR_NULL for a NULL `tokens`. */
+ * setting (0: loop by loop).  Passage: as gdn_loop_prefill_set_pieces (LT2
+ * Section 2 "LT2" paragraph).  Host only, nothing enqueued.  Errors: the
+ * usual descriptor errors, GDN_ERR_NULL for a NULL `tokens`. */
 gdn_status gdn_loop_prefill_pieces(const gdn_desc *desc, int *tokens);
 
 /* T loops with per-token adaptive halting (ACT).
