@@ -126,3 +126,69 @@ def test_pieces_other_loop_counts_and_heads(T, H, D, L, piece, pieces):
     assert torch.equal(run.h_out, ref.h_out)
     assert torch.equal(run.loops, ref.loops)
     assert torch.equal(run.states, ref.states)
+
+
+def test_pieces_two_host_threads(pieces):
+    """Two host threads issue pipelined calls at the same time, each on its own stream with its own workspace and
+    outputs (the library's shared streams and events are taken in turn while a call enqueues): both results equal
+    the same call run alone, bit for bit."""
+    import threading
+    w = synth.workload("prefill_b1_l4096")
+    say("[pipeline] two host threads, pieces of 1024")
+    x = synth.prefill_inputs(w)
+    Wp = _pack(w, x)
+    desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    pieces(1024)
+    h0, rho = x["h0"].to("cuda"), x["rho"].to("cuda")
+    ref = torch.empty(w.B, w.L, w.d, device="cuda")
+    gl.gdn_loop_prefill(desc, h0, Wp, rho, ref, None, None, gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL))
+    torch.cuda.synchronize()
+    outs, errors = [None, None], []
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL) for _ in range(2)]
+    hs = [torch.empty(w.B, w.L, w.d, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+
+    def work(i):
+        try:
+            torch.cuda.set_device(0)
+            for _ in range(3):
+                gl.gdn_loop_prefill(desc, h0, Wp, rho, hs[i], None, None, wss[i], stream=streams[i])
+            streams[i].synchronize()
+            outs[i] = hs[i].clone()
+        except Exception as e:   # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], ref) and torch.equal(outs[1], ref)
+
+
+def test_pieces_stage_timers(pieces):
+    """The stage timers record the pipelined call's launches (on the library's own streams): one projection, prep
+    and carry per loop and piece."""
+    w = synth.workload("prefill_b1_l4096")
+    say("[pipeline] stage timers on a pipelined call")
+    x = synth.prefill_inputs(w)
+    Wp = _pack(w, x)
+    desc = gl.make_desc(w.B, w.L, w.H, w.dk, w.dv, T=w.T, act=w.act, alpha_lo=w.alpha_lo)
+    pieces(1024)
+    ws = gl.workspace(desc, gl.GDN_OP_LOOP_PREFILL)
+    h = torch.empty(w.B, w.L, w.d, device="cuda")
+    h0, rho = x["h0"].to("cuda"), x["rho"].to("cuda")
+    stages = (gl.GDN_STAGE_PROJECT, gl.GDN_STAGE_SCAN_PREP, gl.GDN_STAGE_SCAN_CARRY)
+    timers = [gl.gdn_timer_create(s, 64) for s in stages]
+    for t in timers:
+        gl.gdn_timer_attach(t)
+    gl.gdn_loop_prefill(desc, h0, Wp, rho, h, None, None, ws)
+    torch.cuda.synchronize()
+    gl.gdn_timer_detach()
+    for t in timers:
+        n, ms = gl.gdn_timer_read(t)
+        gl.gdn_timer_destroy(t)
+        assert n == w.T * 4 and ms > 0   # four pieces of 1024 tokens per loop
