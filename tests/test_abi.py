@@ -394,3 +394,20 @@ def test_decode_workspace_split_projection():
     assert _ws_status(gl.make_desc(8, 1, 2, 64, 64, act=gl.GDN_F32), gl.GDN_OP_LOOP_DECODE) == (0, base(8, 2, 64, 4))
     # the no-allocation decode still takes 64 sequences of width 2048
     assert _ws_status(gl.make_desc(64, 1, 16, 128, 128), gl.GDN_OP_LOOP_DECODE)[1] <= 8 << 20   # its 8 MiB scratch
+
+
+def test_new_workspace_minimums_rejected_before_launch(lib):
+    """On the host, before anything is enqueued: a loop decode workspace one byte short of the size without the
+    projection-partials region (the size at which the projection runs unsplit) is refused, as is a pipelined-shape
+    loop prefill workspace one byte short of the size with the pieces' state region."""
+    up = lambda n: (n + 255) // 256 * 256
+    o = [ctypes.c_void_p(0x100000 + 0x1000 * i) for i in range(8)]
+    desc = gl.make_desc(64, 1, 16, 128, 128)
+    full = _ws_status(desc, gl.GDN_OP_LOOP_DECODE)[1]
+    unsplit = full - up(4 * 64 * (16 * 3 * 128 + 128) * 4)
+    st = lib.gdn_loop_decode(ctypes.byref(desc), o[0], o[1], o[2], o[3], o[4], o[5], unsplit - 1, None)
+    assert st == -4 and f"{unsplit} bytes" in gl.gdn_last_error()
+    desc = gl.make_desc(1, 32768, 16, 128, 128)
+    full = _ws_status(desc)[1]
+    st = lib.gdn_loop_prefill(ctypes.byref(desc), o[0], o[1], o[2], o[3], None, None, o[5], full - 1, None)
+    assert st == -4 and f"{full} bytes" in gl.gdn_last_error()
